@@ -1,0 +1,343 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-MoE expert layer (2-bit routed experts) on one MI355X.
+
+A step is one full pass of the layer's hot path on one batch: router
+(logits, top-k, grouping), shared expert, routed expert FFN (gate/up +
+SwiGLU + down) and the weighted combine.  The headline workload is decode of
+one token through one DeepSeek-V3-class layer (H=7168, I=2048, 256 experts,
+top-8, bf16 shared expert); the reported value is whole-step algorithmic
+bytes / step time in GB/s.  The weights of the timed steps rotate over
+several copies at distinct addresses, as a model cycles through its layers,
+so they do not stay in the on-chip caches.
+
+Prints one JSON line (rank 0, one GPU).  Extra workloads (batched decode,
+prefill) are reported inside it under "workloads" as context.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer decode GB/s (% HBM peak) + prefill tokens/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+CACHE = os.environ.get("MOE_CACHE_DIR", "/tmp/moe_layer_cache")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha1()
+    d = os.path.join(ROOT, "bit_quantized_routed_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:12]
+
+
+# ------------------------------------------------------------------ algorithmic work
+def layer_bytes(cfg, n_active, T):
+    """Bytes the method must move for one step: weights of the active experts,
+    the shared expert and the router, plus x in and y out."""
+    import bit_quantized_routed_amd as M
+    H, I, E, sh = cfg["hidden"], cfg["inter"], cfg["n_experts"], cfg["sh_inter"]
+    per_expert = 2 * M.q2_packed_bytes(cfg["fmt_gate_up"], I, H) + M.q2_packed_bytes(cfg["fmt_down"], H, I)
+    xb = 2 if cfg["x_dtype"] == "bf16" else 4
+    return n_active * per_expert + 3 * sh * H * 2 + E * H * 4 + T * H * xb + T * H * 4
+
+
+def kernel_bytes(cfg, n_active, T, name):
+    """Algorithmic bytes of one launch of the named FFN kernel."""
+    import bit_quantized_routed_amd as M
+    H, I, k, sh = cfg["hidden"], cfg["inter"], cfg["top_k"], cfg["sh_inter"]
+    xb = 2 if cfg["x_dtype"] == "bf16" else 4
+    rows = T * k + (T if sh else 0)
+    if name.endswith("gateup"):
+        hb = 4 if "decode" in name else 2
+        return n_active * 2 * M.q2_packed_bytes(cfg["fmt_gate_up"], I, H) + 2 * sh * H * 2 + T * H * xb + rows * I * hb
+    if name.endswith("down"):
+        hb = 4 if "decode" in name else 2
+        return n_active * M.q2_packed_bytes(cfg["fmt_down"], H, I) + sh * H * 2 + rows * I * hb + rows * H * 4
+    return None
+
+
+def layer_flops(cfg, T):
+    H, I, E, k, sh = cfg["hidden"], cfg["inter"], cfg["n_experts"], cfg["top_k"], cfg["sh_inter"]
+    return 6.0 * H * I * T * k + 6.0 * H * sh * T + 2.0 * T * E * H
+
+
+def kernel_flops(cfg, T, name):
+    H, I, k, sh = cfg["hidden"], cfg["inter"], cfg["top_k"], cfg["sh_inter"]
+    if name.endswith("gateup"):
+        return 4.0 * H * (I * T * k + sh * T)
+    if name.endswith("down"):
+        return 2.0 * H * (I * T * k + sh * T)
+    return None
+
+
+# ------------------------------------------------------------------ GPU timing
+class Stepper:
+    def __init__(self, wl, cfg, decode):
+        import torch
+        import bit_quantized_routed_amd as M
+        self.M, self.torch = M, torch
+        self.wl, self.cfg, self.decode = wl, cfg, decode
+        self.x, self.act = wl.tokens(cfg)
+        self.T = self.x.shape[0]
+        self.bias = wl.bias(cfg)
+        c = wl.cfg
+        self.r = M.Routing(self.T, c["top_k"], c["n_experts"])
+        self.y = torch.empty((self.T, c["hidden"]), device="cuda")
+        self.ws_route = wl.layer.workspace(self.T, M.PATH_ROUTE)
+        self.ws_ffn = wl.layer.workspace(self.T, M.PATH_DECODE if decode else M.PATH_PREFILL)
+        self.stream = torch.cuda.current_stream()
+        self.i = 0
+
+    def step(self, prof_route=None, prof_ffn=None):
+        M = self.M
+        layer = self.wl.layers[self.i % len(self.wl.layers)]
+        self.i += 1
+        M.route(layer, self.x, self.act, self.T, self.bias, self.r, self.ws_route, self.stream, prof_route)
+        f = M.ffn_decode if self.decode else M.ffn_prefill
+        f(layer, self.x, self.act, self.T, self.r, self.y, self.ws_ffn, self.stream, prof_ffn)
+
+    def n_active(self):
+        import numpy as np
+        off = self.r.offsets.cpu().numpy()
+        return int((np.diff(off) > 0).sum())
+
+    def kernel_times(self, reps=5):
+        """Average duration (ms) of every launch of one step, by name."""
+        torch, M = self.torch, self.M
+        out = {}
+        for which in ("route", "ffn"):
+            k = 0
+            while True:
+                times = []
+                name = None
+                for _ in range(reps):
+                    p = M.Profile(k, 0, None, None, None)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(); e1.record()
+                    p.ev_start, p.ev_stop = e0.cuda_event, e1.cuda_event
+                    self.step(p if which == "route" else None, p if which == "ffn" else None)
+                    torch.cuda.synchronize()
+                    n = p.n_launches
+                    if k >= n:
+                        break
+                    name = p.name.decode()
+                    times.append(e0.elapsed_time(e1))
+                if name is None:
+                    break
+                out[name] = (which, k, sum(times) / len(times))
+                k += 1
+        return out
+
+    def timed(self, steps, warmup, dominant=None):
+        """ms per step over `steps` steps; with `dominant` = (which, index), also the
+        average duration of that launch, bracketed by events inside the timed region."""
+        torch, M = self.torch, self.M
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        pairs = []
+        profs = []
+        if dominant:
+            for _ in range(steps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(); e1.record()          # materialise the events
+                pairs.append((e0, e1))
+                p = M.Profile(dominant[1], 0, e0.cuda_event, e1.cuda_event, None)
+                profs.append(p)
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            p = profs[i] if dominant else None
+            self.step(p if dominant and dominant[0] == "route" else None,
+                      p if dominant and dominant[0] == "ffn" else None)
+        stop.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        ms = start.elapsed_time(stop) / steps
+        kms = sum(a.elapsed_time(b) for a, b in pairs) / steps if dominant else None
+        return ms, kms, wall
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(cfg, nbytes):
+    """The oracle, untuned, on the host cores: one full step of the workload
+    (route + dequantize the needed experts + FFN + combine), timed after its own
+    quantization (which is excluded)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import synthetic as S
+    from oracle import formats as F
+    from oracle import moe_ref as R
+
+    x, kind = S.tokens(cfg)
+    xf = S.bf16_to_f32(x) if kind == "bf16" else x
+    wr, b = S.router_weight(cfg), S.logit_bias(cfg)
+    idx0, _, _ = R.route(xf, wr, cfg["top_k"], b)
+    cb = S.codebook()
+    H, I = cfg["hidden"], cfg["inter"]
+    packed = {}
+    for e in np.unique(idx0):
+        packed[int(e)] = [F.pack(fmt, S.expert_weight(cfg, which, int(e)), cb)
+                          for which, fmt in (("gate", cfg["fmt_gate_up"]), ("up", cfg["fmt_gate_up"]),
+                                             ("down", cfg["fmt_down"]))]
+    sh = tuple(S.bf16_to_f32(S.shared_weight_bf16(cfg, n)) for n in ("gate", "up", "down")) if cfg["sh_inter"] else None
+    t0 = time.perf_counter()
+    idx, w, _ = R.route(xf, wr, cfg["top_k"], b)
+    R.group(idx, cfg["n_experts"])
+    ex = {}
+    for e in np.unique(idx):
+        p = packed[int(e)]
+        ex[int(e)] = (F.unpack(cfg["fmt_gate_up"], p[0], I, H, cb), F.unpack(cfg["fmt_gate_up"], p[1], I, H, cb),
+                      F.unpack(cfg["fmt_down"], p[2], H, I, cb))
+    R.moe_layer(xf, idx, w, ex, sh)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": "one full %s step (T=%d): fp64 route, numpy dequant of the %d selected experts, fp64 FFN "
+                      "and combine; %.2f s" % (cfg["name"], cfg["T"], len(ex), dt)}
+
+
+# ------------------------------------------------------------------ traffic (rocprofv3 --pmc)
+def read_traffic(kernel, workload):
+    """Per-launch HBM bytes from the committed counter summary, if it was taken
+    on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.md" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    h = re.search(r"kernel_source_hash:\s*(\w+)", txt)
+    if not m or not h or h.group(1) != kernel_source_hash():
+        return None
+    return float(m.group(1))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode1")
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--extra", default="decode32,prefill2048",
+                    help="comma-separated extra workloads reported as context ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the layer's multi-GPU sharding is a design, not "
+              "built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synthetic as S
+    import workload as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = S.config(args.workload)
+    decode = args.workload.startswith("decode")
+    log("building layer (%s), %d replicas" % (args.workload, args.replicas))
+    t0 = time.time()
+    wl = W.Workload(cfg, cache_dir=CACHE, progress=True, replicas=args.replicas)
+    log("layer ready in %.0f s" % (time.time() - t0))
+
+    st = Stepper(wl, cfg, decode)
+    st.step()
+    torch.cuda.synchronize()
+    n_active = st.n_active()
+    kt = st.kernel_times()
+    dom_name = max(kt, key=lambda n: kt[n][2])
+    which, kidx, _ = kt[dom_name]
+    log("per-kernel ms: " + ", ".join("%s=%.4f" % (n, v[2]) for n, v in kt.items()))
+    ms, kms, wall = st.timed(args.steps, args.warmup, (which, kidx))
+    T = st.T
+    nbytes = layer_bytes(cfg, n_active, T)
+    value = nbytes / (ms * 1e-3) / 1e9
+
+    if decode:
+        kb = kernel_bytes(cfg, n_active, T, dom_name)
+        ach = kb / (kms * 1e-3) / 1e9 if kb else None
+        roof = {"bound": "hbm", "kernel": dom_name, "achieved": round(ach, 1) if ach else None,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4) if ach else None,
+                "traffic": read_traffic(dom_name, args.workload), "algorithmic_bytes": kb,
+                "avg_launch_ms": round(kms, 5)}
+    else:
+        kf = kernel_flops(cfg, T, dom_name)
+        ach = kf / (kms * 1e-3) / 1e12 if kf else None
+        roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(ach, 1) if ach else None,
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4) if ach else None,
+                "traffic": read_traffic(dom_name, args.workload), "algorithmic_flops": kf,
+                "avg_launch_ms": round(kms, 5)}
+
+    workloads = {}
+    for name in [w for w in args.extra.split(",") if w and w != args.workload]:
+        c2 = S.config(name)
+        dec2 = name.startswith("decode")
+        if (c2["fmt_gate_up"], c2["fmt_down"]) != (cfg["fmt_gate_up"], cfg["fmt_down"]):
+            log("skip %s (different formats)" % name)
+            continue
+        s2 = Stepper(wl, c2, dec2)
+        s2.step()
+        torch.cuda.synchronize()
+        na2 = s2.n_active()
+        steps2 = args.steps if dec2 else max(5, args.steps // 10)
+        ms2, _, _ = s2.timed(steps2, max(2, args.warmup // 4))
+        if dec2:
+            b2 = layer_bytes(c2, na2, s2.T)
+            gbs = b2 / (ms2 * 1e-3) / 1e9
+            workloads[name] = {"ms_per_step": round(ms2, 4), "GB/s": round(gbs, 1),
+                               "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "active_experts": na2, "T": s2.T}
+        else:
+            fl = layer_flops(c2, s2.T)
+            tf = fl / (ms2 * 1e-3) / 1e12
+            workloads[name] = {"ms_per_step": round(ms2, 4), "tokens/s": round(s2.T / (ms2 * 1e-3), 1),
+                               "TFLOP/s": round(tf, 1), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4), "T": s2.T}
+        log("%s: %s" % (name, workloads[name]))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (cpu_baseline)")
+        cpu = cpu_baseline(cfg, nbytes)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s" if decode else "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "T": T, "hidden": cfg["hidden"], "inter": cfg["inter"],
+                   "experts": cfg["n_experts"], "top_k": cfg["top_k"], "shared_inter": cfg["sh_inter"],
+                   "formats": "gate/up %s, down %s, shared bf16" % (
+                       {1: "CB2", 3: "Q4_K"}[cfg["fmt_gate_up"]], {2: "Q2_K", 3: "Q4_K"}[cfg["fmt_down"]]),
+                   "active_experts": n_active, "algorithmic_bytes": nbytes, "weight_replicas": args.replicas},
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4) if decode else None,
+        "wall_ms_per_step": round(wall, 5),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels_ms": {n: round(v[2], 5) for n, v in kt.items()},
+        "kernel_source_hash": kernel_source_hash(),
+        "workloads": workloads,
+    }
+    if not decode:
+        out["value"] = round(T / (ms * 1e-3), 1)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,209 @@
+"""Routed-MoE expert layer with 2-bit routed experts on one MI355X (gfx950).
+
+Thin ctypes binding over the C-ABI library ``libmoe.so`` (``include/moe.h``).
+Every step of the layer runs in the library's HIP kernels; this module only
+marshals arguments (device pointers from PyTorch tensors, the caller's HIP
+stream) and raises on a non-zero status.  There is no CPU fallback: if the
+library is missing, loading fails loudly.
+
+Names follow the C ABI: ``moe_route``, ``moe_expert_ffn_decode``,
+``moe_expert_ffn_prefill``, ``q2_pack``, ``q2_unpack``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "libmoe.so")
+
+FMT_CB2, FMT_Q2K, FMT_Q4K, FMT_BF16 = 1, 2, 3, 4
+ACT_F32, ACT_BF16 = 0, 1
+PATH_ROUTE, PATH_DECODE, PATH_PREFILL = 0, 1, 2
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
+          -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
+BLOCK_BYTES = {FMT_CB2: 38, FMT_Q2K: 84, FMT_Q4K: 144}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__("%s: %s (%s)" % (where, STATUS.get(status, status), detail))
+        self.status = status
+
+
+class Layer(ctypes.Structure):
+    """struct moe_layer (host struct of device pointers)."""
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("fmt_gate_up", ctypes.c_int32), ("fmt_down", ctypes.c_int32),
+                ("sh_inter", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("codebook", ctypes.c_void_p),
+                ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p),
+                ("w_router", ctypes.c_void_p)]
+
+
+class Profile(ctypes.Structure):
+    """struct moe_profile: bracket launch number `kernel` with two hipEvents."""
+    _fields_ = [("kernel", ctypes.c_int32), ("n_launches", ctypes.c_int32),
+                ("ev_start", ctypes.c_void_p), ("ev_stop", ctypes.c_void_p),
+                ("name", ctypes.c_char_p)]
+
+
+_lib = None
+EXPORTS = ["moe_route", "moe_expert_ffn_decode", "moe_expert_ffn_prefill", "q2_pack", "q2_unpack",
+           "q2_packed_bytes", "moe_workspace_bytes", "moe_status_str", "moe_last_error"]
+
+
+def lib():
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libmoe.so not built at %s; run `python -m bit_quantized_routed_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lp, pp = ctypes.POINTER(Layer), ctypes.POINTER(Profile)
+    L.moe_route.argtypes = [lp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, pp]
+    L.moe_route.restype = i32
+    for f in (L.moe_expert_ffn_decode, L.moe_expert_ffn_prefill):
+        f.argtypes = [lp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, pp]
+        f.restype = i32
+    L.q2_pack.argtypes = [i32, vp, i64, i32, vp, vp]
+    L.q2_pack.restype = i32
+    L.q2_unpack.argtypes = [i32, vp, i64, i32, vp, vp, vp]
+    L.q2_unpack.restype = i32
+    L.q2_packed_bytes.argtypes = [i32, i64, i32]
+    L.q2_packed_bytes.restype = sz
+    L.moe_workspace_bytes.argtypes = [lp, i32, i32]
+    L.moe_workspace_bytes.restype = sz
+    L.moe_status_str.argtypes = [i32]
+    L.moe_status_str.restype = ctypes.c_char_p
+    L.moe_last_error.argtypes = []
+    L.moe_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise MoeError(rc, where, lib().moe_last_error().decode())
+
+
+def _ptr(t):
+    """Device (or host numpy) pointer of a tensor/array, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------------ helpers
+def q2_packed_bytes(fmt: int, rows: int, K: int) -> int:
+    return int(lib().q2_packed_bytes(fmt, rows, K))
+
+
+def workspace_bytes(layer: Layer, T: int, path: int) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(layer), T, path))
+
+
+# ------------------------------------------------------------------ entry points
+def q2_pack(fmt: int, w: np.ndarray, codebook: np.ndarray | None = None) -> np.ndarray:
+    """Host quantizer: fp32 [rows, K] -> packed uint8 bytes."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, K = w.shape
+    out = np.empty(q2_packed_bytes(fmt, rows, K), np.uint8)
+    cb = None if codebook is None else np.ascontiguousarray(codebook, dtype=np.int8)
+    _check(lib().q2_pack(fmt, w.ctypes.data, rows, K, _ptr(cb), out.ctypes.data), "q2_pack")
+    return out
+
+
+def q2_unpack(fmt: int, packed, rows: int, K: int, codebook, out, stream=None):
+    """Device dequantizer: packed (uint8 device) -> out (fp32 device [rows, K])."""
+    _check(lib().q2_unpack(fmt, _ptr(packed), rows, K, _ptr(codebook), _ptr(out), _stream(stream)), "q2_unpack")
+
+
+def moe_route(layer: Layer, x, act: int, T: int, bias, topk_idx, topk_w, offsets, perm, inv, ws,
+              stream=None, prof: Profile | None = None):
+    _check(lib().moe_route(ctypes.byref(layer), _ptr(x), act, T, _ptr(bias), _ptr(topk_idx), _ptr(topk_w),
+                           _ptr(offsets), _ptr(perm), _ptr(inv), _ptr(ws), ws.numel() * ws.element_size(),
+                           _stream(stream), None if prof is None else ctypes.byref(prof)), "moe_route")
+
+
+def _ffn(fn, name, layer, x, act, T, topk_idx, topk_w, offsets, perm, inv, y, ws, stream, prof):
+    _check(fn(ctypes.byref(layer), _ptr(x), act, T, _ptr(topk_idx), _ptr(topk_w), _ptr(offsets), _ptr(perm),
+              _ptr(inv), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream),
+              None if prof is None else ctypes.byref(prof)), name)
+
+
+def moe_expert_ffn_decode(layer, x, act, T, topk_idx, topk_w, offsets, perm, inv, y, ws, stream=None, prof=None):
+    _ffn(lib().moe_expert_ffn_decode, "moe_expert_ffn_decode", layer, x, act, T, topk_idx, topk_w, offsets,
+         perm, inv, y, ws, stream, prof)
+
+
+def moe_expert_ffn_prefill(layer, x, act, T, topk_idx, topk_w, offsets, perm, inv, y, ws, stream=None, prof=None):
+    _ffn(lib().moe_expert_ffn_prefill, "moe_expert_ffn_prefill", layer, x, act, T, topk_idx, topk_w, offsets,
+         perm, inv, y, ws, stream, prof)
+
+
+# ------------------------------------------------------------------ device layer
+class DeviceLayer:
+    """Device-resident weights of one layer plus the moe_layer struct over them.
+
+    Holds torch tensors (device memory) so the pointers stay valid; all
+    arithmetic happens in the library.
+    """
+
+    def __init__(self, hidden, inter, n_experts, top_k, fmt_gate_up, fmt_down, w_gate, w_up, w_down,
+                 codebook, w_router, sh_gate=None, sh_up=None, sh_down=None, sh_inter=0):
+        self.tensors = [w_gate, w_up, w_down, codebook, w_router, sh_gate, sh_up, sh_down]
+        self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
+        self.sh_inter = sh_inter
+        self.c = Layer(hidden, inter, n_experts, top_k, fmt_gate_up, fmt_down, sh_inter, 0,
+                       _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(codebook),
+                       _ptr(sh_gate), _ptr(sh_up), _ptr(sh_down), _ptr(w_router))
+
+    def workspace(self, T: int, path: int, device="cuda"):
+        import torch
+        n = max(workspace_bytes(self.c, T, path), 256)
+        return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+class Routing:
+    """Device routing buffers for T tokens."""
+
+    def __init__(self, T, k, E, device="cuda"):
+        import torch
+        self.T = T
+        self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=device)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=device)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=device)
+        self.perm = torch.empty(T * k, dtype=torch.int32, device=device)
+        self.inv = torch.empty(T * k, dtype=torch.int32, device=device)
+
+
+def route(dl: DeviceLayer, x, act, T, bias, r: Routing, ws, stream=None, prof=None):
+    moe_route(dl.c, x, act, T, bias, r.topk_idx, r.topk_w, r.offsets, r.perm, r.inv, ws, stream, prof)
+
+
+def ffn_decode(dl: DeviceLayer, x, act, T, r: Routing, y, ws, stream=None, prof=None):
+    moe_expert_ffn_decode(dl.c, x, act, T, r.topk_idx, r.topk_w, r.offsets, r.perm, r.inv, y, ws, stream, prof)
+
+
+def ffn_prefill(dl: DeviceLayer, x, act, T, r: Routing, y, ws, stream=None, prof=None):
+    moe_expert_ffn_prefill(dl.c, x, act, T, r.topk_idx, r.topk_w, r.offsets, r.perm, r.inv, y, ws, stream, prof)

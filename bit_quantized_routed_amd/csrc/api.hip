@@ -1,0 +1,329 @@
+// C ABI of the routed-MoE expert layer (see include/moe.h): host-side argument
+// validation, workspace carving and the kernel launch sequences.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+#include "moe.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+// Records the caller's events around launch number `prof->kernel`.
+struct Prof {
+    moe_profile *p;
+    hipStream_t s;
+    int n = 0;
+    bool before(const char *name)
+    {
+        if (p && p->kernel == n) {
+            p->name = name;
+            if (hipEventRecord((hipEvent_t)p->ev_start, s) != hipSuccess) return false;
+        }
+        return true;
+    }
+    bool after()
+    {
+        if (p && p->kernel == n && hipEventRecord((hipEvent_t)p->ev_stop, s) != hipSuccess) return false;
+        ++n;
+        if (p) p->n_launches = n;
+        return true;
+    }
+};
+
+bool fmt_ok(int f) { return f == MOE_FMT_CB2 || f == MOE_FMT_Q2K || f == MOE_FMT_Q4K; }
+int bbytes(int f) { return f == MOE_FMT_CB2 ? 38 : f == MOE_FMT_Q2K ? 84 : f == MOE_FMT_Q4K ? 144 : 0; }
+int nblocks(int K) { return (K + 255) / 256; }
+
+int check_router(const moe_layer *L)
+{
+    if (!L) return fail(MOE_ERR_INVALID_ARG, "layer is NULL");
+    if (L->hidden < 8 || L->hidden % 8) return fail(MOE_ERR_INVALID_ARG, "hidden=%d must be a positive multiple of 8", L->hidden);
+    if (L->n_experts < 1 || L->n_experts > 1024) return fail(MOE_ERR_INVALID_ARG, "n_experts=%d outside [1,1024]", L->n_experts);
+    if (L->top_k < 1 || L->top_k > L->n_experts) return fail(MOE_ERR_INVALID_ARG, "top_k=%d outside [1,n_experts]", L->top_k);
+    if (!L->w_router) return fail(MOE_ERR_INVALID_ARG, "w_router is NULL");
+    return MOE_OK;
+}
+
+int check_layer(const moe_layer *L)
+{
+    int rc = check_router(L);
+    if (rc) return rc;
+    if (L->inter < 8 || L->inter % 8) return fail(MOE_ERR_INVALID_ARG, "inter=%d must be a positive multiple of 8", L->inter);
+    if (L->fmt_gate_up != MOE_FMT_CB2 && L->fmt_gate_up != MOE_FMT_Q4K)
+        return fail(MOE_ERR_INVALID_ARG, "fmt_gate_up=%d must be CB2 or Q4K", L->fmt_gate_up);
+    if (L->fmt_down != MOE_FMT_Q2K && L->fmt_down != MOE_FMT_Q4K)
+        return fail(MOE_ERR_INVALID_ARG, "fmt_down=%d must be Q2K or Q4K", L->fmt_down);
+    if (!L->w_gate || !L->w_up || !L->w_down) return fail(MOE_ERR_INVALID_ARG, "routed expert weights are NULL");
+    if (L->fmt_gate_up == MOE_FMT_CB2 && !L->codebook) return fail(MOE_ERR_INVALID_ARG, "CB2 needs a codebook");
+    if (L->sh_inter < 0) return fail(MOE_ERR_INVALID_ARG, "sh_inter=%d < 0", L->sh_inter);
+    if (L->sh_inter > 0) {
+        if (!L->sh_gate || !L->sh_up || !L->sh_down) return fail(MOE_ERR_INVALID_ARG, "shared expert weights are NULL");
+        if (L->sh_inter % 256 || L->hidden % 256)
+            return fail(MOE_ERR_INVALID_ARG, "shared expert needs sh_inter and hidden multiples of 256");
+    }
+    return MOE_OK;
+}
+
+struct RouteWs {
+    double *logits;
+    int32_t *rank, *tile_counts;
+    size_t bytes;
+};
+
+bool route_small(const moe_layer *L, int T) { return T <= 64 && T * L->top_k <= 2048; }
+
+RouteWs route_ws(const moe_layer *L, int T, char *base)
+{
+    RouteWs w{};
+    size_t off = 0;
+    const size_t E = L->n_experts, k = L->top_k;
+    w.logits = (double *)(base + off);
+    off = align_up(off + (size_t)T * E * sizeof(double));
+    if (!route_small(L, T)) {
+        w.rank = (int32_t *)(base + off);
+        off = align_up(off + (size_t)T * k * sizeof(int32_t));
+        w.tile_counts = (int32_t *)(base + off);
+        off = align_up(off + (size_t)((T + 63) / 64) * E * sizeof(int32_t));
+    }
+    w.bytes = off;
+    return w;
+}
+
+struct FfnWs {
+    int32_t *sched;
+    void *h;
+    float *O;
+    size_t bytes;
+    int hstride;
+};
+
+FfnWs ffn_ws(const moe_layer *L, int T, bool prefill, char *base)
+{
+    FfnWs w{};
+    const int has_sh = L->sh_inter > 0;
+    const int BM = prefill ? PRE_BM : DEC_BM;
+    const size_t rows = (size_t)T * L->top_k + (has_sh ? T : 0);
+    w.hstride = std::max(L->inter, L->sh_inter);
+    size_t off = 0;
+    w.sched = (int32_t *)(base + off);
+    off = align_up(off + (1 + 2 * (size_t)ffn_max_tiles(T, L->top_k, L->n_experts, has_sh, BM)) * sizeof(int32_t));
+    w.h = base + off;
+    off = align_up(off + rows * w.hstride * (prefill ? 2 : 4));
+    w.O = (float *)(base + off);
+    off = align_up(off + rows * (size_t)L->hidden * sizeof(float));
+    w.bytes = off;
+    return w;
+}
+
+int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t *topk_idx, const float *topk_w,
+               const int32_t *offsets, const int32_t *perm, const int32_t *inv, float *y, void *ws,
+               size_t ws_bytes, void *stream, moe_profile *prof, bool prefill)
+{
+    int rc = check_layer(L);
+    if (rc) return rc;
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d < 0", T);
+    if (act != MOE_ACT_F32 && act != MOE_ACT_BF16) return fail(MOE_ERR_INVALID_ARG, "act=%d unknown", act);
+    if (prof) prof->n_launches = 0;
+    if (T == 0) return MOE_OK;
+    if ((int64_t)T * L->top_k > (1 << 30)) return fail(MOE_ERR_INVALID_ARG, "T*k too large");
+    if (!x || !topk_idx || !topk_w || !offsets || !perm || !inv || !y) return fail(MOE_ERR_INVALID_ARG, "NULL tensor argument");
+    if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+    if (prefill) {
+        if (act != MOE_ACT_BF16) return fail(MOE_ERR_INVALID_ARG, "prefill needs bf16 activations");
+    } else {
+        if (L->fmt_gate_up != MOE_FMT_CB2 || L->fmt_down != MOE_FMT_Q2K)
+            return fail(MOE_ERR_UNSUPPORTED, "decode supports CB2 gate/up with Q2K down");
+    }
+    FfnWs w = ffn_ws(L, T, prefill, (char *)ws);
+    if (ws_bytes < w.bytes) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.bytes);
+
+    hipStream_t s = (hipStream_t)stream;
+    Prof pr{prof, s};
+    const int H = L->hidden, I = L->inter, E = L->n_experts, k = L->top_k, Ish = L->sh_inter;
+    const int has_sh = Ish > 0;
+    const int BM = prefill ? PRE_BM : DEC_BM;
+
+    if (!pr.before("ffn_schedule")) return hip_fail(hipGetLastError(), "event record");
+    launch_ffn_schedule(offsets, T, k, E, has_sh, BM, w.sched, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "ffn_schedule launch");
+    if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+
+    FfnPass up{};
+    up.T = T; up.k = k; up.E = E;
+    up.offsets = offsets; up.perm = perm;
+    up.fmt = L->fmt_gate_up;
+    up.w0 = (const uint8_t *)L->w_gate; up.w1 = (const uint8_t *)L->w_up;
+    up.w_row_bytes = (int64_t)nblocks(H) * bbytes(L->fmt_gate_up);
+    up.w_expert_bytes = up.w_row_bytes * I;
+    up.s0 = (const uint16_t *)L->sh_gate; up.s1 = (const uint16_t *)L->sh_up;
+    up.codebook = L->codebook;
+    up.K = H; up.N = I; up.Ksh = H; up.Nsh = has_sh ? Ish : 0;
+    up.act = x; up.act_f32 = act == MOE_ACT_F32; up.act_by_token = 1; up.act_stride = H;
+    up.out = w.h; up.out_f32 = prefill ? 0 : 1; up.out_stride = w.hstride;
+    up.sched = w.sched;
+
+    FfnPass dn = up;
+    dn.fmt = L->fmt_down;
+    dn.w0 = (const uint8_t *)L->w_down; dn.w1 = nullptr;
+    dn.w_row_bytes = (int64_t)nblocks(I) * bbytes(L->fmt_down);
+    dn.w_expert_bytes = dn.w_row_bytes * H;
+    dn.s0 = (const uint16_t *)L->sh_down; dn.s1 = nullptr;
+    dn.K = I; dn.N = H; dn.Ksh = Ish; dn.Nsh = has_sh ? H : 0;
+    dn.act = w.h; dn.act_f32 = prefill ? 0 : 1; dn.act_by_token = 0; dn.act_stride = w.hstride;
+    dn.out = w.O; dn.out_f32 = 1; dn.out_stride = H;
+
+    const char *nm_up = prefill ? "ffn_prefill_gateup" : "ffn_decode_gateup";
+    const char *nm_dn = prefill ? "ffn_prefill_down" : "ffn_decode_down";
+    if (!pr.before(nm_up)) return hip_fail(hipGetLastError(), "event record");
+    e = prefill ? launch_ffn_prefill(up, true, s) : launch_ffn_decode(up, true, s);
+    if (e != hipSuccess) return hip_fail(e, nm_up);
+    if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+
+    if (!pr.before(nm_dn)) return hip_fail(hipGetLastError(), "event record");
+    e = prefill ? launch_ffn_prefill(dn, false, s) : launch_ffn_decode(dn, false, s);
+    if (e != hipSuccess) return hip_fail(e, nm_dn);
+    if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+
+    if (!pr.before("combine")) return hip_fail(hipGetLastError(), "event record");
+    launch_combine(w.O, inv, topk_w, T, k, H, has_sh, y, s);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_str(int status)
+{
+    switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+    }
+}
+
+const char *moe_last_error(void) { return g_err.c_str(); }
+
+size_t q2_packed_bytes(int fmt, int64_t rows, int K)
+{
+    if (!fmt_ok(fmt) || rows < 0 || K < 1) return 0;
+    return (size_t)rows * nblocks(K) * bbytes(fmt);
+}
+
+size_t moe_workspace_bytes(const moe_layer *L, int T, int path)
+{
+    if (T < 0) return 0;
+    if (path == MOE_PATH_ROUTE) {
+        if (check_router(L)) return 0;
+        return route_ws(L, T, nullptr).bytes;
+    }
+    if (path != MOE_PATH_DECODE && path != MOE_PATH_PREFILL) return 0;
+    if (check_layer(L)) return 0;
+    return ffn_ws(L, T, path == MOE_PATH_PREFILL, nullptr).bytes;
+}
+
+int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bias, int32_t *topk_idx,
+              float *topk_w, int32_t *offsets, int32_t *perm, int32_t *inv, void *ws, size_t ws_bytes,
+              void *stream, moe_profile *prof)
+{
+    int rc = check_router(L);
+    if (rc) return rc;
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d < 0", T);
+    if (act != MOE_ACT_F32 && act != MOE_ACT_BF16) return fail(MOE_ERR_INVALID_ARG, "act=%d unknown", act);
+    if (prof) prof->n_launches = 0;
+    if (T == 0) return MOE_OK;
+    if ((int64_t)T * L->top_k > (1 << 30)) return fail(MOE_ERR_INVALID_ARG, "T*k too large");
+    if (!x || !topk_idx || !topk_w || !offsets || !perm || !inv) return fail(MOE_ERR_INVALID_ARG, "NULL tensor argument");
+    if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+    RouteWs w = route_ws(L, T, (char *)ws);
+    if (ws_bytes < w.bytes) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.bytes);
+
+    hipStream_t s = (hipStream_t)stream;
+    Prof pr{prof, s};
+    const int H = L->hidden, E = L->n_experts, k = L->top_k;
+    hipError_t e;
+#define MOE_LAUNCH(name, call)                                                     \
+    do {                                                                           \
+        if (!pr.before(name)) return hip_fail(hipGetLastError(), "event record");  \
+        call;                                                                      \
+        e = hipGetLastError();                                                     \
+        if (e != hipSuccess) return hip_fail(e, name);                             \
+        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");       \
+    } while (0)
+
+    MOE_LAUNCH("route_logits", launch_route_logits(x, act == MOE_ACT_BF16, L->w_router, bias, T, H, E, w.logits, s));
+    if (route_small(L, T)) {
+        MOE_LAUNCH("route_select_small", launch_route_select_small(w.logits, T, E, k, topk_idx, topk_w, offsets, perm, inv, s));
+    } else {
+        MOE_LAUNCH("route_topk", launch_route_topk(w.logits, T, E, k, topk_idx, topk_w, s));
+        MOE_LAUNCH("route_rank", launch_route_rank(topk_idx, T, E, k, w.rank, w.tile_counts, s));
+        MOE_LAUNCH("route_scan", launch_route_scan(T, E, k, w.tile_counts, offsets, s));
+        MOE_LAUNCH("route_scatter", launch_route_scatter(topk_idx, w.rank, w.tile_counts, offsets, T, E, k, perm, inv, s));
+    }
+#undef MOE_LAUNCH
+    return MOE_OK;
+}
+
+int moe_expert_ffn_decode(const moe_layer *L, const void *x, int act, int T, const int32_t *topk_idx,
+                          const float *topk_w, const int32_t *offsets, const int32_t *perm, const int32_t *inv,
+                          float *y, void *ws, size_t ws_bytes, void *stream, moe_profile *prof)
+{
+    return ffn_common(L, x, act, T, topk_idx, topk_w, offsets, perm, inv, y, ws, ws_bytes, stream, prof, false);
+}
+
+int moe_expert_ffn_prefill(const moe_layer *L, const void *x, int act, int T, const int32_t *topk_idx,
+                           const float *topk_w, const int32_t *offsets, const int32_t *perm, const int32_t *inv,
+                           float *y, void *ws, size_t ws_bytes, void *stream, moe_profile *prof)
+{
+    return ffn_common(L, x, act, T, topk_idx, topk_w, offsets, perm, inv, y, ws, ws_bytes, stream, prof, true);
+}
+
+int q2_unpack(int fmt, const void *packed_dev, int64_t rows, int K, const int8_t *codebook_dev, float *out_dev,
+              void *stream)
+{
+    if (!fmt_ok(fmt)) return fail(MOE_ERR_INVALID_ARG, "fmt=%d unknown", fmt);
+    if (rows < 0 || K < 1) return fail(MOE_ERR_INVALID_ARG, "rows=%lld K=%d", (long long)rows, K);
+    if (rows == 0) return MOE_OK;
+    if (!packed_dev || !out_dev) return fail(MOE_ERR_INVALID_ARG, "NULL tensor argument");
+    if (fmt == MOE_FMT_CB2 && !codebook_dev) return fail(MOE_ERR_INVALID_ARG, "CB2 needs a codebook");
+    if (rows * nblocks(K) * 8 > ((int64_t)1 << 40)) return fail(MOE_ERR_INVALID_ARG, "too large");
+    hipError_t e = launch_unpack(fmt, (const uint8_t *)packed_dev, rows, K, codebook_dev, out_dev, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "q2_unpack launch");
+    return MOE_OK;
+}
+
+}  // extern "C"

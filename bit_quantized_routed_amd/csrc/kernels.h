@@ -1,0 +1,63 @@
+// Host-side launchers of the gfx950 kernels (all asynchronous on stream s).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ------------------------------------------------------------------ router
+void launch_route_logits(const void *x, bool xbf16, const float *wr, const float *bias, int T, int H, int E,
+                         double *logits, hipStream_t s);
+void launch_route_select_small(const double *logits, int T, int E, int k, int32_t *topk_idx, float *topk_w,
+                               int32_t *offsets, int32_t *perm, int32_t *inv, hipStream_t s);
+void launch_route_topk(const double *logits, int T, int E, int k, int32_t *topk_idx, float *topk_w,
+                       hipStream_t s);
+void launch_route_rank(const int32_t *topk_idx, int T, int E, int k, int32_t *rank, int32_t *tile_counts,
+                       hipStream_t s);
+void launch_route_scan(int T, int E, int k, int32_t *tile_counts, int32_t *offsets, hipStream_t s);
+void launch_route_scatter(const int32_t *topk_idx, const int32_t *rank, const int32_t *tile_base,
+                          const int32_t *offsets, int T, int E, int k, int32_t *perm, int32_t *inv,
+                          hipStream_t s);
+
+// ------------------------------------------------------------------ FFN
+// One grouped GEMM pass over the routed experts (groups 0..E-1) and the
+// shared expert (group E).  Rows of group g are "positions": routed expert e
+// owns positions offsets[e]..offsets[e+1]-1 (in perm order); the shared
+// expert owns positions T*k .. T*k+T-1 (token t at T*k+t).
+struct FfnPass {
+    int T, k, E;
+    const int32_t *offsets, *perm;
+    int fmt;                          // routed format
+    const uint8_t *w0, *w1;           // routed gate,up (gate/up pass) or down,null
+    int64_t w_expert_bytes;           // bytes of one expert's matrix
+    int64_t w_row_bytes;              // bytes of one packed row
+    const uint16_t *s0, *s1;          // shared expert bf16 matrices (or null)
+    const int8_t *codebook;           // CB2 codebook (device)
+    int K, N;                         // routed: reduction length, output rows
+    int Ksh, Nsh;                     // shared: reduction length, output rows (Nsh = 0: none)
+    const void *act;                  // activations
+    int act_f32;                      // 1: fp32 elements, 0: bf16
+    int act_by_token;                 // 1: gate/up (row = token of the position), 0: down (row = position)
+    int64_t act_stride;               // elements per activation row
+    void *out;                        // output rows by position
+    int out_f32;                      // 1: fp32 output, 0: bf16 (RNE)
+    int64_t out_stride;               // elements per output row
+    const int32_t *sched;             // [0] = tile count, then (group, m0) pairs
+};
+
+int ffn_max_tiles(int T, int k, int E, int has_shared, int BM);
+void launch_ffn_schedule(const int32_t *offsets, int T, int k, int E, int has_shared, int BM,
+                         int32_t *sched, hipStream_t s);
+// decode (exact codes, fp32 accumulation); returns hipSuccess or an error
+hipError_t launch_ffn_decode(const FfnPass &p, bool gateup, hipStream_t s);
+// prefill (bf16-rounded weights, bf16 MFMA)
+hipError_t launch_ffn_prefill(const FfnPass &p, bool gateup, hipStream_t s);
+void launch_combine(const float *O, const int32_t *inv, const float *topk_w, int T, int k, int H,
+                    int has_shared, float *y, hipStream_t s);
+hipError_t launch_unpack(int fmt, const uint8_t *packed, int64_t rows, int K, const int8_t *codebook,
+                         float *out, hipStream_t s);
+
+constexpr int DEC_BM = 16, DEC_BN = 16;
+constexpr int PRE_BM = 64, PRE_BN = 64;
+
+}  // namespace moe

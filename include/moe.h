@@ -1,0 +1,201 @@
+/*
+ * moe.h -- C ABI of the routed-MoE expert layer with 2-bit routed experts,
+ * for one AMD Instinct MI355X (gfx950).
+ *
+ * The layer (one MoE FFN of a DeepSeek-V3/V4-class model) is
+ *
+ *   y[t] = FFN_sh(x_t) + sum_{j<k} w[t,j] * FFN_{e(t,j)}(x_t),
+ *   FFN_e(x) = W_down,e ( silu(W_gate,e x) * (W_up,e x) ),
+ *
+ * where only the routed experts are quantized: gate/up in a 2-bit codebook
+ * format (CB2), down in Q2_K (or all three in Q4_K); the shared expert and the
+ * router stay unquantized.  This split follows the pages: "DwarfStar" README
+ * and the "ds4" README mirror, sections on model weights (only routed experts
+ * quantized, up/gate IQ2_XXS, down Q2_K, everything else unchanged); deep-dive
+ * article on DwarfStar, section 3.4.3 (quantization tree; router kept at high
+ * precision).  The pages give no bit layout; the block layouts are defined
+ * below and are this library's own.
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are HIP device memory owned by the caller.  The library
+ *    allocates nothing: scratch comes from the caller's workspace `ws`,
+ *    sized with moe_workspace_bytes().  Host pointers are marked "host".
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and never synchronise or read device data back to the host.
+ *  - Arguments are validated on the host before any HIP call; a bad argument
+ *    returns a negative moe_status and launches nothing.  A failed launch
+ *    returns MOE_ERR_HIP; moe_last_error() gives the detail for the calling
+ *    thread.  No entry point aborts or throws.
+ *  - T == 0 returns MOE_OK without launching.
+ *  - Non-finite inputs are caller error: results are then unspecified but
+ *    every access stays in bounds.
+ *  - Calls on one stream run in order; calls on different streams that share
+ *    a workspace or an output race.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ status */
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,   /* null pointer, bad size, k > E, ...          */
+    MOE_ERR_UNSUPPORTED = -2,   /* valid but not implemented (format / path)   */
+    MOE_ERR_WORKSPACE = -3,     /* ws_bytes smaller than moe_workspace_bytes() */
+    MOE_ERR_HIP = -4            /* a HIP launch or runtime call failed         */
+};
+
+/* ------------------------------------------------------------ formats
+ * A quantized matrix [rows][K] is stored row by row; each row holds
+ * nb = ceil(K/256) blocks of 256 consecutive weights (a row whose K is not a
+ * multiple of 256 is zero-padded).  Little-endian fields:
+ *
+ * MOE_FMT_CB2  38 B/block: [0:2) fp16 d | [2:6) eight 4-bit sub-block scales,
+ *   s_j in bits 4*(j%2).. of byte 2+j/2 | [6:38) 32 one-byte codebook indices,
+ *   one per group of 8 weights.  w[8g+i] = d * s_{g/4} * C[idx_g][i], with C
+ *   a caller-supplied int8 codebook [256][8] of values in {-3,-1,1,3}.
+ * MOE_FMT_Q2K  84 B/block: [0:2) fp16 d | [2:4) fp16 dmin | [4:20) byte j =
+ *   sc_j | m_j<<4 for 16 sub-blocks of 16 | [20:84) 2-bit q_i in bits
+ *   2*(i%4) of byte i/4.  w_i = d*sc_j*q_i - dmin*m_j, j = i/16.
+ * MOE_FMT_Q4K 144 B/block: [0:2) d | [2:4) dmin | [4:16) sixteen 6-bit
+ *   fields at bits 6n..6n+5 of one little-endian 96-bit stream (n<8: sc_n,
+ *   n>=8: m_{n-8}) | [16:144) 4-bit q_i in bits 4*(i%2) of byte i/2.
+ *   w_i = d*sc_j*q_i - dmin*m_j, j = i/32.
+ * MOE_FMT_BF16 plain row-major bf16 (the shared expert), no blocks.
+ *
+ * Every dequantized value is exact in fp32 (products need at most 21
+ * significant bits; the min term is subtracted with one rounding). */
+enum moe_format { MOE_FMT_CB2 = 1, MOE_FMT_Q2K = 2, MOE_FMT_Q4K = 3, MOE_FMT_BF16 = 4 };
+
+/* activation element type of x */
+enum moe_act { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 };
+
+/* workspace query paths */
+enum moe_path { MOE_PATH_ROUTE = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 };
+
+/* One MoE layer.  The struct itself lives in host memory; every pointer in
+ * it is device memory.
+ *   hidden (H), inter (I), n_experts (E), top_k (k): 1 <= k <= E <= 1024,
+ *     H % 8 == 0, I % 8 == 0.
+ *   fmt_gate_up: MOE_FMT_CB2 or MOE_FMT_Q4K; fmt_down: MOE_FMT_Q2K or MOE_FMT_Q4K.
+ *   w_gate, w_up: [E][I rows][ceil(H/256) blocks]; w_down: [E][H rows][ceil(I/256)
+ *     blocks]; experts stored back to back with no gaps.
+ *   codebook: int8 [256][8] (CB2 only, else may be NULL).
+ *   sh_inter: intermediate size of the bf16 shared expert, 0 if there is none
+ *     (then sh_* are ignored); sh_gate, sh_up: [sh_inter][H] bf16; sh_down:
+ *     [H][sh_inter] bf16; sh_inter % 256 == 0 and H % 256 == 0 when present.
+ *   w_router: fp32 [E][H]. */
+typedef struct moe_layer {
+    int32_t hidden, inter, n_experts, top_k;
+    int32_t fmt_gate_up, fmt_down;
+    int32_t sh_inter, reserved0;
+    const void *w_gate, *w_up, *w_down;
+    const int8_t *codebook;
+    const void *sh_gate, *sh_up, *sh_down;
+    const float *w_router;
+} moe_layer;
+
+/* Optional per-kernel timing.  When `prof` is non-NULL and prof->kernel is
+ * the 0-based index of one of the kernel launches a call makes, the library
+ * records hipEvent_t prof->ev_start immediately before that launch and
+ * prof->ev_stop immediately after it, on the call's stream; it always stores
+ * the number of launches the call made in prof->n_launches and the kernel's
+ * name in prof->name.  Events are created and destroyed by the caller. */
+typedef struct moe_profile {
+    int32_t kernel;
+    int32_t n_launches;
+    void *ev_start, *ev_stop;
+    const char *name;
+} moe_profile;
+
+/* ------------------------------------------------------------ routing
+ * moe_route: router scores, top-k selection and grouping (device side).
+ *   l[t,e] = sum_h x[t,h]*W_r[e,h] + bias[e]      (accumulated in fp64)
+ *   topk_idx[t,0..k) = the k largest l[t,:], descending, ties to the lower e
+ *   topk_w[t,j] = s_j / sum_j' s_j',  s = 1/(1+exp(-l))   (fp64, stored fp32)
+ *   offsets[E+1]: exclusive prefix sum of per-expert assignment counts
+ *   perm[T*k]: assignment ids a = t*k+j sorted by (expert, token)
+ *   inv[T*k]: inv[a] = position of a in perm
+ * The router is kept at full precision, as the pages do (deep-dive article,
+ * section 3.4.3; section 9.2 on routing quality); the function (sigmoid,
+ * top-k, renormalised weights) is the workload's definition.
+ * x: [T][H] of type `act` (device).  bias: fp32 [E] or NULL.  All outputs are
+ * device arrays of the sizes shown.  Launches: logits, then either one fused
+ * small-T select/group kernel (T <= 64) or top-k, rank, scan and scatter. */
+int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bias,
+              int32_t *topk_idx, float *topk_w, int32_t *offsets, int32_t *perm, int32_t *inv,
+              void *ws, size_t ws_bytes, void *stream, moe_profile *prof);
+
+/* ------------------------------------------------------------ expert FFN
+ * Both compute y [T][H] fp32 (overwritten) = shared expert + routing-weighted
+ * sum of the k routed expert FFNs (SwiGLU), from the routing that moe_route
+ * produced.  Inputs as in moe_route.
+ *
+ * moe_expert_ffn_decode -- fp32-accurate path meant for small T (any T works):
+ *   weights applied exactly (integer codes in bf16 MFMA with fp32 block
+ *   rescale), activations exact (bf16) or split into two bf16 terms (fp32),
+ *   fp32 accumulation, intermediate h in fp32.  Relative L2 error against an
+ *   exact evaluation is far below 1e-4.  Formats: CB2/Q2K routed, BF16 shared.
+ *   Launches: schedule, gate/up+SwiGLU, down, combine.
+ * moe_expert_ffn_prefill -- bf16 MFMA path for any T: x must be bf16;
+ *   dequantized weights rounded to bf16 (RNE) in LDS; fp32 accumulation;
+ *   h rounded to bf16; down output and combine in fp32.  Relative L2 error
+ *   below 5e-3.  Formats: CB2/Q4K gate/up, Q2K/Q4K down, BF16 shared.
+ *   Launches: schedule, gate/up+SwiGLU, down, combine. */
+int moe_expert_ffn_decode(const moe_layer *L, const void *x, int act, int T,
+                          const int32_t *topk_idx, const float *topk_w, const int32_t *offsets,
+                          const int32_t *perm, const int32_t *inv, float *y,
+                          void *ws, size_t ws_bytes, void *stream, moe_profile *prof);
+int moe_expert_ffn_prefill(const moe_layer *L, const void *x, int act, int T,
+                           const int32_t *topk_idx, const float *topk_w, const int32_t *offsets,
+                           const int32_t *perm, const int32_t *inv, float *y,
+                           void *ws, size_t ws_bytes, void *stream, moe_profile *prof);
+
+/* ------------------------------------------------------------ pack / unpack
+ * q2_pack (host): quantize a row-major fp32 matrix w_host [rows][K] into
+ * out_host (q2_packed_bytes(fmt, rows, K) bytes).  fmt: CB2 (needs
+ * codebook_host int8 [256][8]), Q2K or Q4K.  Quantizer (fp32 arithmetic,
+ * round-half-to-even everywhere, fp16 conversion RNE):
+ *   Q2_K / Q4_K, per sub-block j (16 / 32 weights): lo = min(0, min w),
+ *     hi = max w, scale_j = (hi-lo)/L, mn_j = -lo (L = 3 / 15); per block
+ *     d = fp16(max scale_j / S), dmin = fp16(max mn_j / S) (S = 15 / 63);
+ *     sc_j = rint(scale_j/d), m_j = rint(mn_j/dmin) clamped to [0,S] (0 if
+ *     the divisor is 0); q_i = rint((w_i + dmin*m_j)/(d*sc_j)) clamped to
+ *     [0,L] (0 if d*sc_j == 0).
+ *   CB2, per sub-block j of 32: sigma_j = max|w|/3; d = fp16(max sigma_j/15);
+ *     s_j = rint(sigma_j/d) clamped to [0,15]; per group of 8 with
+ *     step = d*s_j > 0: t_i = rint(w_i/step*4096), idx = argmin over the
+ *     codebook of the integer distance sum_i (t_i - 4096*C[idx][i])^2, lowest
+ *     index on ties (0 when step == 0).
+ * Rows are spread over at most 16 host threads; the bytes do not depend on the thread
+ * count.  Returns MOE_OK or MOE_ERR_INVALID_ARG. */
+int q2_pack(int fmt, const float *w_host, int64_t rows, int K, const int8_t *codebook_host,
+            void *out_host);
+
+/* q2_unpack (device): dequantize packed_dev [rows][nb blocks] to out_dev fp32
+ * [rows][K] (padding dropped), bit-exact with the definitions above.
+ * codebook_dev: int8 [256][8] device array for CB2, else ignored. */
+int q2_unpack(int fmt, const void *packed_dev, int64_t rows, int K, const int8_t *codebook_dev,
+              float *out_dev, void *stream);
+
+/* ------------------------------------------------------------ helpers */
+/* bytes of a packed [rows][K] matrix; 0 for an unknown format */
+size_t q2_packed_bytes(int fmt, int64_t rows, int K);
+/* workspace bytes for a call of the given path (MOE_PATH_*) with T tokens;
+ * 0 if L is invalid.  Sizes grow linearly with T. */
+size_t moe_workspace_bytes(const moe_layer *L, int T, int path);
+/* static text for a status code */
+const char *moe_status_str(int status);
+/* detail of the last error on the calling thread ("" if none) */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,138 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library must load and export every function include/moe.h declares;
+argument validation must return the documented status before any HIP call;
+q2_pack must write exactly the oracle's bytes.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_quantized_routed_amd as M
+import synthetic as S
+from oracle import formats as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CB = S.codebook()
+FAKE = 0x1000            # never dereferenced: every call below fails validation first
+
+
+def test_exports_every_declared_function():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    declared = set(re.findall(r"^(?:int|size_t|const char \*)\s*(\w+)\s*\(", src, flags=re.M))
+    assert {"moe_route", "moe_expert_ffn_decode", "moe_expert_ffn_prefill", "q2_pack", "q2_unpack"} <= declared
+    L = M.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert declared == set(M.EXPORTS)
+
+
+def _layer(**kw):
+    base = dict(hidden=256, inter=128, n_experts=8, top_k=2, fmt_gate_up=1, fmt_down=2, sh_inter=0, reserved0=0,
+                w_gate=FAKE, w_up=FAKE, w_down=FAKE, codebook=FAKE, sh_gate=None, sh_up=None, sh_down=None,
+                w_router=FAKE)
+    base.update(kw)
+    return M.Layer(**base)
+
+
+def _route(L, T=4, act=1, ws_bytes=1 << 30, ws=FAKE, out=FAKE):
+    return M.lib().moe_route(ctypes.byref(L) if L is not None else None, FAKE, act, T, None, out, out, out, out,
+                             out, ws, ws_bytes, None, None)
+
+
+def _ffn(fn, L, T=4, act=1, ws_bytes=1 << 30, ws=FAKE, out=FAKE):
+    return fn(ctypes.byref(L) if L is not None else None, FAKE, act, T, out, out, out, out, out, out, ws,
+              ws_bytes, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(top_k=0), -1), (dict(top_k=9), -1), (dict(n_experts=2000, top_k=2), -1), (dict(hidden=100), -1),
+    (dict(w_router=None), -1)])
+def test_route_validation(kw, code):
+    assert _route(_layer(**kw)) == code
+    assert M.lib().moe_last_error()
+
+
+def test_route_validation_misc():
+    L = _layer()
+    assert _route(None) == -1
+    assert _route(L, T=-1) == -1
+    assert _route(L, act=7) == -1
+    assert _route(L, out=None) == -1
+    assert _route(L, ws=None) == -1
+    assert _route(L, ws_bytes=10) == -3
+    assert _route(L, T=0, ws=None, out=None) == 0          # T == 0: no launch, OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(fmt_gate_up=2), -1), (dict(fmt_down=1), -1), (dict(inter=100), -1), (dict(w_down=None), -1),
+    (dict(codebook=None), -1), (dict(sh_inter=128, sh_gate=FAKE, sh_up=FAKE, sh_down=FAKE), -1),
+    (dict(sh_inter=256), -1), (dict(sh_inter=-1), -1)])
+def test_ffn_validation(kw, code):
+    for fn in (M.lib().moe_expert_ffn_decode, M.lib().moe_expert_ffn_prefill):
+        assert _ffn(fn, _layer(**kw)) == code
+
+
+def test_ffn_validation_misc():
+    dec, pre = M.lib().moe_expert_ffn_decode, M.lib().moe_expert_ffn_prefill
+    L = _layer()
+    assert _ffn(pre, L, act=0) == -1                           # prefill needs bf16 activations
+    assert _ffn(dec, _layer(fmt_gate_up=3, fmt_down=3)) == -2  # decode: CB2/Q2K only
+    assert _ffn(dec, L, ws_bytes=100) == -3
+    assert _ffn(pre, L, ws_bytes=100) == -3
+    assert _ffn(dec, L, T=-2) == -1
+    assert _ffn(dec, L, T=0, ws=None, out=None) == 0
+    assert _ffn(pre, L, out=None) == -1
+
+
+def test_unpack_validation():
+    U = M.lib().q2_unpack
+    assert U(9, FAKE, 4, 256, FAKE, FAKE, None) == -1
+    assert U(1, FAKE, 4, 256, None, FAKE, None) == -1          # CB2 needs a codebook
+    assert U(2, None, 4, 256, None, FAKE, None) == -1
+    assert U(2, FAKE, -1, 256, None, FAKE, None) == -1
+    assert U(2, FAKE, 0, 256, None, None, None) == 0
+
+
+def test_sizes():
+    assert M.q2_packed_bytes(1, 2048, 7168) == F.packed_bytes(F.CB2, 2048, 7168)
+    assert M.q2_packed_bytes(2, 7168, 2048) == F.packed_bytes(F.Q2K, 7168, 2048)
+    assert M.q2_packed_bytes(3, 7, 300) == F.packed_bytes(F.Q4K, 7, 300)
+    assert M.q2_packed_bytes(4, 7, 300) == 0
+    L = _layer()
+    for path in (0, 1, 2):
+        a, b = M.workspace_bytes(L, 4, path), M.workspace_bytes(L, 400, path)
+        assert 0 < a < b
+    assert M.workspace_bytes(_layer(top_k=0), 4, 1) == 0
+    assert [M.lib().moe_status_str(c).decode() for c in (0, -1, -2, -3, -4)] == [
+        "ok", "invalid argument", "unsupported", "workspace too small", "HIP error"]
+
+
+@pytest.mark.parametrize("fmt", [F.CB2, F.Q2K, F.Q4K])
+@pytest.mark.parametrize("shape", [(1, 256), (7, 100), (33, 384), (5, 1000)])
+def test_pack_matches_oracle_bytes(fmt, shape):
+    rng = np.random.default_rng(hash((fmt, shape)) % 2**32)
+    w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    assert np.array_equal(M.q2_pack(fmt, w, CB), F.pack(fmt, w, CB))
+
+
+def test_pack_matches_oracle_on_workload_rows():
+    cfg = S.config("decode1")
+    for which, fmt in (("gate", F.CB2), ("down", F.Q2K), ("down", F.Q4K), ("up", F.Q4K)):
+        w = S.expert_weight(cfg, which, 17)[:96]
+        assert np.array_equal(M.q2_pack(fmt, w, CB), F.pack(fmt, w, CB)), which
+
+
+def test_pack_edge_values():
+    # zeros, a constant row, all-negative and all-positive sub-blocks, a huge outlier
+    rows = np.zeros((6, 256), np.float32)
+    rows[1] = 0.5
+    rows[2] = -np.abs(np.linspace(0.01, 0.3, 256, dtype=np.float32))
+    rows[3] = np.abs(np.linspace(0.01, 0.3, 256, dtype=np.float32))
+    rows[4, 7] = 30.0
+    rows[5] = np.tile(np.array([1e-6, -2e-6], np.float32), 128)
+    for fmt in (F.CB2, F.Q2K, F.Q4K):
+        assert np.array_equal(M.q2_pack(fmt, rows, CB), F.pack(fmt, rows, CB)), fmt

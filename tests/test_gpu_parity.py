@@ -1,0 +1,247 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars: routing indices, offsets, perm, inv and dequantized weights bit-exact;
+routing weights within 2 fp32 ulps (fp64 sums in a different order);
+layer output relative L2 <= 1e-4 on the decode path and <= 5e-3 on the
+prefill path.  Small and mid-size cases compare every element; the full-size
+workloads (the benchmark's launch configuration) compare routing in full and
+the output on sampled tokens, which the oracle evaluates one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_routed_amd as M
+import synthetic as S
+import workload as W
+from oracle import formats as F
+from oracle import moe_ref as R
+from gpu_common import CACHE, need_gpu, oracle_experts, oracle_routing, oracle_shared, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+DEC_TOL, PRE_TOL = 1e-4, 5e-3
+
+MID = dict(hidden=512, inter=384, n_experts=16, top_k=4, sh_inter=256, x_dtype="bf16", skew=False,
+           fmt_gate_up=S.FMT_CB2, fmt_down=S.FMT_Q2K, name="mid")
+
+
+def mid(T, index, **kw):
+    c = dict(MID, T=T, index=index)
+    c.update(kw)
+    return c
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+    print("[gpu] libmoe:", M.LIB_PATH, flush=True)
+
+
+# ------------------------------------------------------------------ unpack
+@pytest.mark.parametrize("fmt", [F.CB2, F.Q2K, F.Q4K])
+@pytest.mark.parametrize("rows,K", [(1, 256), (5, 100), (19, 640), (64, 7168), (64, 2048)])
+def test_unpack_bit_exact(fmt, rows, K):
+    rng = np.random.default_rng(rows * 1000 + K + fmt)
+    w = (rng.standard_normal((rows, K)) * 0.02).astype(np.float32)
+    cb = S.codebook()
+    p = F.pack(fmt, w, cb)
+    ref = F.unpack(fmt, p, rows, K, cb)
+    out = torch.full((rows, K), float("nan"), device="cuda")
+    M.q2_unpack(fmt, torch.from_numpy(p).cuda(), rows, K, torch.from_numpy(cb).cuda(), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------ helpers
+def run_route(wl, cfg, T=None):
+    x, act = wl.tokens(cfg, T)
+    T = x.shape[0]
+    c = wl.cfg
+    r = M.Routing(T, c["top_k"], c["n_experts"])
+    ws = wl.layer.workspace(T, M.PATH_ROUTE)
+    M.route(wl.layer, x, act, T, wl.bias(cfg), r, ws)
+    torch.cuda.synchronize()
+    return x, act, r
+
+
+def check_route(r, idx, w, off, perm, inv):
+    assert np.array_equal(r.topk_idx.cpu().numpy(), idx)
+    assert np.array_equal(r.offsets.cpu().numpy(), off)
+    assert np.array_equal(r.perm.cpu().numpy(), perm)
+    assert np.array_equal(r.inv.cpu().numpy(), inv)
+    gw = r.topk_w.cpu().numpy()
+    assert np.allclose(gw, w, rtol=2.4e-7, atol=0), np.abs(gw - w).max()
+
+
+def run_ffn(wl, x, act, r, decode, T=None):
+    T = x.shape[0] if T is None else T
+    y = torch.full((x.shape[0], wl.cfg["hidden"]), float("nan"), device="cuda")
+    ws = wl.layer.workspace(T, M.PATH_DECODE if decode else M.PATH_PREFILL)
+    (M.ffn_decode if decode else M.ffn_prefill)(wl.layer, x, act, T, r, y, ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def full_reference(cfg, T=None):
+    x, idx, w, l, off, perm, inv = oracle_routing(cfg, T)
+    ex = oracle_experts(cfg, np.unique(idx))
+    y = R.moe_layer(x, idx, w, ex, oracle_shared(cfg))
+    return y, (idx, w, off, perm, inv)
+
+
+# ------------------------------------------------------------------ small / mid, every element
+SMALL = [
+    ("tiny", S.config("tiny")),
+    ("mid_T37", mid(37, 11)),
+    ("mid_T1", mid(1, 12)),
+    ("mid_T64_skew", mid(64, 13, skew=True)),
+    ("mid_T300", mid(300, 14)),
+    ("mid_allexperts", mid(9, 15, top_k=16, n_experts=16)),
+    ("mid_f32x", mid(20, 16, x_dtype="f32")),
+]
+
+
+@pytest.fixture(scope="module")
+def small_cases():
+    return {}
+
+
+def _case(small_cases, name, cfg):
+    if name not in small_cases:
+        wl = W.Workload(cfg)
+        y, routing = full_reference(cfg)
+        small_cases[name] = (wl, y, routing)
+    return small_cases[name]
+
+
+@pytest.mark.parametrize("name,cfg", SMALL, ids=[n for n, _ in SMALL])
+def test_route_small(small_cases, name, cfg):
+    wl, _, routing = _case(small_cases, name, cfg)
+    _, _, r = run_route(wl, cfg)
+    check_route(r, *routing)
+
+
+@pytest.mark.parametrize("name,cfg", SMALL, ids=[n for n, _ in SMALL])
+def test_decode_small(small_cases, name, cfg):
+    wl, yref, _ = _case(small_cases, name, cfg)
+    x, act, r = run_route(wl, cfg)
+    y = run_ffn(wl, x, act, r, decode=True)
+    err = rel_l2(y, yref)
+    print("[decode] %s rel_l2=%.3e" % (name, err))
+    assert err <= DEC_TOL
+
+
+@pytest.mark.parametrize("name,cfg", [c for c in SMALL if c[1]["x_dtype"] == "bf16"] +
+                         [("tiny_bf16", S.config("tiny", x_dtype="bf16")),
+                          ("mid_q4k", mid(150, 17, fmt_gate_up=S.FMT_Q4K, fmt_down=S.FMT_Q4K)),
+                          ("mid_q4k_T1", mid(1, 18, fmt_gate_up=S.FMT_Q4K, fmt_down=S.FMT_Q4K))],
+                         ids=lambda v: v if isinstance(v, str) else "")
+def test_prefill_small(small_cases, name, cfg):
+    wl, yref, routing = _case(small_cases, name, cfg)
+    x, act, r = run_route(wl, cfg)
+    check_route(r, *routing)
+    y = run_ffn(wl, x, act, r, decode=False)
+    err = rel_l2(y, yref)
+    print("[prefill] %s rel_l2=%.3e" % (name, err))
+    assert err <= PRE_TOL
+
+
+def test_route_ties_go_to_lower_index():
+    cfg = mid(40, 19)
+    wl = W.Workload(cfg)
+    wr = S.router_weight(cfg)
+    wr[9] = wr[3]
+    wr[12] = wr[3]
+    wl.layer.tensors[4].copy_(torch.from_numpy(wr))
+    x, act = wl.tokens(cfg)
+    r = M.Routing(40, cfg["top_k"], cfg["n_experts"])
+    M.route(wl.layer, x, act, 40, None, r, wl.layer.workspace(40, M.PATH_ROUTE))
+    torch.cuda.synchronize()
+    xf = S.bf16_to_f32(S.tokens(cfg)[0])
+    idx, w, _ = R.route(xf, wr, cfg["top_k"])
+    assert np.array_equal(r.topk_idx.cpu().numpy(), idx)
+    got = r.topk_idx.cpu().numpy()
+    for t in range(40):
+        row = got[t].tolist()
+        if 3 in row and 9 in row:
+            assert row.index(3) < row.index(9)
+
+
+def test_T0_is_a_noop():
+    cfg = mid(4, 20)
+    wl = W.Workload(cfg)
+    x, act = wl.tokens(cfg)
+    r = M.Routing(4, cfg["top_k"], cfg["n_experts"])
+    y = torch.full((4, cfg["hidden"]), 7.0, device="cuda")
+    ws = wl.layer.workspace(4, M.PATH_PREFILL)
+    M.route(wl.layer, x, act, 0, None, r, wl.layer.workspace(4, M.PATH_ROUTE))
+    M.ffn_decode(wl.layer, x, act, 0, r, y, ws)
+    M.ffn_prefill(wl.layer, x, act, 0, r, y, ws)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
+def test_decode_batch_invariance():
+    """Each token's decode output is the same whether it is computed alone or
+    in a batch of 24 (the pages require batched decode rows to return exactly
+    the logits of running each session alone -- "Part 5: serving layer",
+    section 6)."""
+    cfg = mid(24, 21, skew=True)
+    wl = W.Workload(cfg)
+    x, act, r = run_route(wl, cfg)
+    yb = run_ffn(wl, x, act, r, decode=True)
+    for t in (0, 5, 23):
+        xt = x[t:t + 1].contiguous()
+        r1 = M.Routing(1, cfg["top_k"], cfg["n_experts"])
+        M.route(wl.layer, xt, act, 1, None, r1, wl.layer.workspace(1, M.PATH_ROUTE))
+        y1 = run_ffn(wl, xt, act, r1, decode=True)
+        assert np.array_equal(y1[0].view(np.uint32), yb[t].view(np.uint32)), t
+
+
+# ------------------------------------------------------------------ full-size workloads
+@pytest.fixture(scope="module")
+def big():
+    return W.Workload(S.config("decode1"), cache_dir=CACHE, progress=True)
+
+
+@pytest.fixture(scope="module")
+def big_q4k():
+    return W.Workload(S.config("prefill8192_q4k"), cache_dir=CACHE, progress=True)
+
+
+def sampled_check(wl, cfg, decode, n_sample):
+    x, act, r = run_route(wl, cfg)
+    xf, idx, w, l, off, perm, inv = oracle_routing(cfg)
+    check_route(r, idx, w, off, perm, inv)
+    y = run_ffn(wl, x, act, r, decode=decode)
+    T = x.shape[0]
+    rng = np.random.default_rng(T)
+    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=min(n_sample, T), replace=False)]))[:n_sample + 1]
+    ex = oracle_experts(cfg, np.unique(idx[toks]), lib_packed=wl.packed)
+    yref = R.moe_layer(xf[toks], idx[toks], w[toks], ex, oracle_shared(cfg))
+    err = rel_l2(y[toks], yref)
+    print("[%s] %s tokens=%s rel_l2=%.3e" % ("decode" if decode else "prefill", cfg["name"], toks.tolist(), err))
+    assert np.all(np.isfinite(y))
+    return err
+
+
+def test_full_decode1(big):
+    assert sampled_check(big, S.config("decode1"), True, 1) <= DEC_TOL
+
+
+def test_full_decode32(big):
+    assert sampled_check(big, S.config("decode32"), True, 3) <= DEC_TOL
+
+
+def test_full_prefill2048(big):
+    assert sampled_check(big, S.config("prefill2048"), False, 2) <= PRE_TOL
+
+
+def test_full_prefill8192(big):
+    assert sampled_check(big, S.config("prefill8192"), False, 2) <= PRE_TOL
+
+
+def test_full_prefill8192_q4k(big_q4k):
+    assert sampled_check(big_q4k, S.config("prefill8192_q4k"), False, 2) <= PRE_TOL
