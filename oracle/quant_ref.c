@@ -67,7 +67,6 @@ float ref_f16_bits_to_f32(uint16_t h)
     return (float)(s ? -v : v);
 }
 
-static float round_f16(float f) { return ref_f16_bits_to_f32(ref_f32_to_f16_bits(f)); }
 
 static void put_f16(uint8_t *p, uint16_t h) { p[0] = (uint8_t)(h & 0xff); p[1] = (uint8_t)(h >> 8); }
 

@@ -195,7 +195,7 @@ def test_decode_batch_invariance():
     for t in (0, 5, 23):
         xt = x[t:t + 1].contiguous()
         r1 = M.Routing(1, cfg["top_k"], cfg["n_experts"])
-        M.route(wl.layer, xt, act, 1, None, r1, wl.layer.workspace(1, M.PATH_ROUTE))
+        M.route(wl.layer, xt, act, 1, wl.bias(cfg), r1, wl.layer.workspace(1, M.PATH_ROUTE))
         y1 = run_ffn(wl, xt, act, r1, decode=True)
         assert np.array_equal(y1[0].view(np.uint32), yb[t].view(np.uint32)), t
 
