@@ -144,34 +144,37 @@ class Stepper:
         return out
 
     def timed(self, steps, warmup, dominant=None):
-        """ms per step over `steps` steps; with `dominant` = (which, index), also the
-        average duration of that launch, bracketed by events inside the timed region."""
+        """ms per step over `steps` steps with nothing but the layer's launches on
+        the stream; with `dominant` = (which, index), a second run of `steps` steps
+        brackets that launch with HIP events on the layer's stream and returns its
+        average duration (the events themselves slow the step a little, so that
+        run does not give ms per step)."""
         torch, M = self.torch, self.M
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        pairs = []
-        profs = []
-        if dominant:
-            for _ in range(steps):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(); e1.record()          # materialise the events
-                pairs.append((e0, e1))
-                p = M.Profile(dominant[1], 0, e0.cuda_event, e1.cuda_event, None)
-                profs.append(p)
-        torch.cuda.synchronize()
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         start.record()
-        for i in range(steps):
-            p = profs[i] if dominant else None
-            self.step(p if dominant and dominant[0] == "route" else None,
-                      p if dominant and dominant[0] == "ffn" else None)
+        for _ in range(steps):
+            self.step()
         stop.record()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3 / steps
         ms = start.elapsed_time(stop) / steps
-        kms = sum(a.elapsed_time(b) for a, b in pairs) / steps if dominant else None
+        if not dominant:
+            return ms, None, wall
+        pairs, profs = [], []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(); e1.record()              # materialise the events
+            pairs.append((e0, e1))
+            profs.append(M.Profile(dominant[1], 0, e0.cuda_event, e1.cuda_event, None))
+        torch.cuda.synchronize()
+        for i in range(steps):
+            self.step(profs[i] if dominant[0] == "route" else None, profs[i] if dominant[0] == "ffn" else None)
+        torch.cuda.synchronize()
+        kms = sum(a.elapsed_time(b) for a, b in pairs) / steps
         return ms, kms, wall
 
 

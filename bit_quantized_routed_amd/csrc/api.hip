@@ -92,11 +92,12 @@ int check_layer(const moe_layer *L)
 }
 
 struct RouteWs {
-    double *logits;
+    double *logits;          // fused path: [NC][T][E] partial logits (chunk 0 ends as the logits)
     int32_t *rank, *tile_counts;
     size_t bytes;
 };
 
+bool route_fused(const moe_layer *L, int T) { return T <= 64 && L->top_k <= 64; }
 bool route_small(const moe_layer *L, int T) { return T <= 64 && T * L->top_k <= 2048; }
 
 RouteWs route_ws(const moe_layer *L, int T, char *base)
@@ -105,8 +106,9 @@ RouteWs route_ws(const moe_layer *L, int T, char *base)
     size_t off = 0;
     const size_t E = L->n_experts, k = L->top_k;
     w.logits = (double *)(base + off);
-    off = align_up(off + (size_t)T * E * sizeof(double));
-    if (!route_small(L, T)) {
+    const size_t nc = route_fused(L, T) ? (size_t)route_decode_chunks(T, L->hidden) : 1;
+    off = align_up(off + nc * (size_t)T * E * sizeof(double));
+    if (!route_fused(L, T) && !route_small(L, T)) {
         w.rank = (int32_t *)(base + off);
         off = align_up(off + (size_t)T * k * sizeof(int32_t));
         w.tile_counts = (int32_t *)(base + off);
@@ -122,7 +124,17 @@ struct FfnWs {
     float *O;
     size_t bytes;
     int hstride;
+    // single-token decode
+    bool single;
+    float *part_sh, *O_sh;
+    uint16_t *h_hi, *h_lo, *X;
 };
+
+bool dec_single(const moe_layer *L, int T, bool prefill)
+{
+    if (prefill || L->fmt_gate_up != MOE_FMT_CB2 || L->fmt_down != MOE_FMT_Q2K) return false;
+    return dec_single_ok(T, L->hidden, L->inter, L->sh_inter, L->top_k, nblocks(L->hidden) * 38);
+}
 
 FfnWs ffn_ws(const moe_layer *L, int T, bool prefill, char *base)
 {
@@ -132,6 +144,24 @@ FfnWs ffn_ws(const moe_layer *L, int T, bool prefill, char *base)
     const size_t rows = (size_t)T * L->top_k + (has_sh ? T : 0);
     w.hstride = std::max(L->inter, L->sh_inter);
     size_t off = 0;
+    w.single = dec_single(L, T, prefill);
+    if (w.single) {
+        const size_t k = L->top_k, H = L->hidden, Ish = L->sh_inter, nbI = nblocks(L->inter);
+        w.part_sh = (float *)(base + off);
+        off = align_up(off + 4 * 2 * Ish * sizeof(float));
+        w.h_hi = (uint16_t *)(base + off);
+        off = align_up(off + (k + 1) * w.hstride * 2);
+        w.h_lo = (uint16_t *)(base + off);
+        off = align_up(off + (k + 1) * w.hstride * 2);
+        w.X = (uint16_t *)(base + off);
+        off = align_up(off + k * nbI * 32 * 2);
+        w.O = (float *)(base + off);
+        off = align_up(off + k * H * sizeof(float));
+        w.O_sh = (float *)(base + off);
+        off = align_up(off + (Ish / 512) * H * sizeof(float));
+        w.bytes = off;
+        return w;
+    }
     w.sched = (int32_t *)(base + off);
     off = align_up(off + (1 + 2 * (size_t)ffn_max_tiles(T, L->top_k, L->n_experts, has_sh, BM)) * sizeof(int32_t));
     w.h = base + off;
@@ -169,6 +199,36 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
     const int H = L->hidden, I = L->inter, E = L->n_experts, k = L->top_k, Ish = L->sh_inter;
     const int has_sh = Ish > 0;
     const int BM = prefill ? PRE_BM : DEC_BM;
+
+    if (w.single) {
+        DecPass d{};
+        d.T = T; d.k = k; d.E = E; d.H = H; d.I = I; d.Ish = Ish; d.nbI = nblocks(I);
+        d.topk_idx = topk_idx; d.offsets = offsets; d.inv = inv; d.topk_w = topk_w;
+        d.wg = (const uint8_t *)L->w_gate; d.wu = (const uint8_t *)L->w_up; d.wd = (const uint8_t *)L->w_down;
+        d.gu_row_bytes = nblocks(H) * 38;
+        d.gu_expert_bytes = (int64_t)d.gu_row_bytes * I;
+        d.d_row_bytes = nblocks(I) * 84;
+        d.d_expert_bytes = (int64_t)d.d_row_bytes * H;
+        d.sg = (const uint16_t *)L->sh_gate; d.su = (const uint16_t *)L->sh_up; d.sd = (const uint16_t *)L->sh_down;
+        d.codebook = L->codebook;
+        d.x = x; d.x_f32 = act == MOE_ACT_F32;
+        d.h_hi = w.h_hi; d.h_lo = w.h_lo; d.hstride = w.hstride; d.X = w.X;
+        d.part_sh = w.part_sh;
+        d.O = w.O; d.O_sh = w.O_sh; d.y = y;
+        if (!pr.before("dec_gateup")) return hip_fail(hipGetLastError(), "event record");
+        hipError_t e = launch_dec_gateup(d, s);
+        if (e != hipSuccess) return hip_fail(e, "dec_gateup launch");
+        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+        if (!pr.before("dec_down")) return hip_fail(hipGetLastError(), "event record");
+        e = launch_dec_down(d, s);
+        if (e != hipSuccess) return hip_fail(e, "dec_down launch");
+        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+        if (!pr.before("dec_combine")) return hip_fail(hipGetLastError(), "event record");
+        e = launch_dec_combine(d, s);
+        if (e != hipSuccess) return hip_fail(e, "dec_combine launch");
+        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+        return MOE_OK;
+    }
 
     if (!pr.before("ffn_schedule")) return hip_fail(hipGetLastError(), "event record");
     launch_ffn_schedule(offsets, T, k, E, has_sh, BM, w.sched, s);
@@ -285,6 +345,12 @@ int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bi
         if (!pr.after()) return hip_fail(hipGetLastError(), "event record");       \
     } while (0)
 
+    if (route_fused(L, T)) {
+        MOE_LAUNCH("route_partial", launch_route_partial(x, act == MOE_ACT_BF16, L->w_router, T, H, E, w.logits, s));
+        MOE_LAUNCH("route_select", launch_route_select(w.logits, bias, T, H, E, k, topk_idx, topk_w, offsets, perm,
+                                                       inv, s));
+        return MOE_OK;
+    }
     MOE_LAUNCH("route_logits", launch_route_logits(x, act == MOE_ACT_BF16, L->w_router, bias, T, H, E, w.logits, s));
     if (route_small(L, T)) {
         MOE_LAUNCH("route_select_small", launch_route_select_small(w.logits, T, E, k, topk_idx, topk_w, offsets, perm, inv, s));

@@ -57,6 +57,39 @@ void launch_combine(const float *O, const int32_t *inv, const float *topk_w, int
 hipError_t launch_unpack(int fmt, const uint8_t *packed, int64_t rows, int K, const int8_t *codebook,
                          float *out, hipStream_t s);
 
+// single-token decode (T = 1), see decode.hip
+struct DecPass {
+    int T, k, E, H, I, Ish, nbI;
+    const int32_t *topk_idx, *offsets, *inv;
+    const float *topk_w;
+    const uint8_t *wg, *wu, *wd;                 // routed CB2 gate, up; Q2_K down
+    int64_t gu_expert_bytes, d_expert_bytes;
+    int gu_row_bytes, d_row_bytes;
+    const uint16_t *sg, *su, *sd;                // shared expert bf16 (Ish == 0: none)
+    const int8_t *codebook;
+    const void *x;
+    int x_f32;
+    uint16_t *h_hi, *h_lo;                       // [k+1][hstride]
+    int hstride;
+    uint16_t *X;                                 // [k][nbI][32] Q2_K min-term sums (hi 16, lo 16)
+    float *part_sh;                              // [4][2][Ish] shared gate/up partial sums (K quarters)
+    float *O;                                    // [k][H]
+    float *O_sh;                                 // [Ish/512][H]
+    float *y;                                    // [H]
+};
+bool dec_single_ok(int T, int H, int I, int Ish, int k, int gu_row_bytes);
+hipError_t launch_dec_gateup(const DecPass &p, hipStream_t s);
+hipError_t launch_dec_down(const DecPass &p, hipStream_t s);
+hipError_t launch_dec_combine(const DecPass &p, hipStream_t s);
+
+// small-T router (T <= 64, k <= 64, E <= 1024): partial logits, then one
+// work-group selects and groups
+int route_decode_chunks(int T, int H);
+void launch_route_partial(const void *x, bool xbf16, const float *wr, int T, int H, int E, double *part,
+                          hipStream_t s);
+void launch_route_select(const double *part, const float *bias, int T, int H, int E, int k, int32_t *topk_idx,
+                         float *topk_w, int32_t *offsets, int32_t *perm, int32_t *inv, hipStream_t s);
+
 constexpr int DEC_BM = 16, DEC_BN = 16;
 constexpr int PRE_BM = 64, PRE_BN = 64;
 

@@ -11,6 +11,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace moe {
 
 // ---------------------------------------------------------------- logits
@@ -318,6 +320,274 @@ void launch_route_scatter(const int32_t *topk_idx, const int32_t *rank, const in
                           const int32_t *offsets, int T, int E, int k, int32_t *perm, int32_t *inv, hipStream_t s)
 {
     route_scatter<<<(T * k + 255) / 256, 256, 0, s>>>(topk_idx, rank, tile_base, offsets, T, E, k, perm, inv);
+}
+
+}  // namespace moe
+
+// ============================================================================
+// Small-T router (T <= 64, k <= 64, E <= 1024) in two launches.
+//
+// route_partial: every wave computes fp64 partial logits for EW experts x TB
+// tokens over one H chunk (16-byte loads of W_r rows, 8-byte loads of bf16 x,
+// all loads of a batch issued before the arithmetic) and writes
+// partial[c][t][e].  Selection: a work-group per token sums the chunks in
+// order and ranks the experts; T == 1 then groups in the same work-group,
+// otherwise one more work-group builds offsets, perm and inv.  Every expert's logit is summed in the same order, so equal rows of
+// W_r give equal logits and ties resolve to the lower index exactly as in a
+// sequential evaluation.  (A single launch that lets its last work-group do
+// the selection needs a device-scope release/acquire in every work-group;
+// on this chip those write back and invalidate the L2 of each XCD and cost
+// far more than the second launch.)
+// ============================================================================
+namespace moe {
+
+template <int EW, int TB, bool XBF16>
+__global__ __launch_bounds__(256) void route_partial(const void *x, const float *wr, int T, int H, int E, int NC,
+                                                     int HC, double *part)
+{
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n_eg = E / EW, n_tg = (T + TB - 1) / TB;
+    const int item = blockIdx.x * 4 + wave;
+    if (item >= n_eg * n_tg * NC) return;
+    const int c = item % NC;
+    const int tg = (item / NC) % n_tg;
+    const int eg = item / (NC * n_tg);
+    const int t0 = tg * TB, nt = min(TB, T - t0);
+    const int h_begin = c * HC, h_end = min(H, h_begin + HC);
+    double acc[EW][TB];
+#pragma unroll
+    for (int a = 0; a < EW; ++a)
+#pragma unroll
+        for (int b = 0; b < TB; ++b) acc[a][b] = 0.0;
+    // batches of SB steps of 256 h: every load of a batch is issued before any use
+    constexpr int SB = TB == 1 ? 8 : 2;
+    for (int h0 = h_begin + 4 * lane; h0 < h_end; h0 += 256 * SB) {
+        f32x4 w4[SB][EW];
+        uint2 xb[SB][TB];
+        f32x4 xf[SB][TB];
+#pragma unroll
+        for (int st = 0; st < SB; ++st) {
+            const int h = h0 + 256 * st;
+            if (h < h_end) {
+#pragma unroll
+                for (int a = 0; a < EW; ++a) w4[st][a] = *(const f32x4 *)&wr[(size_t)(eg * EW + a) * H + h];
+#pragma unroll
+                for (int b = 0; b < TB; ++b)
+                    if (b < nt) {
+                        if (XBF16) xb[st][b] = *(const uint2 *)&((const uint16_t *)x)[(size_t)(t0 + b) * H + h];
+                        else xf[st][b] = *(const f32x4 *)&((const float *)x)[(size_t)(t0 + b) * H + h];
+                    }
+            }
+        }
+#pragma unroll
+        for (int st = 0; st < SB; ++st) {
+            if (h0 + 256 * st >= h_end) break;
+#pragma unroll
+            for (int b = 0; b < TB; ++b) {
+                if (b < nt) {
+                    double xv[4];
+                    if (XBF16) {
+                        const uint2 u = xb[st][b];
+                        xv[0] = bf16_bits_to_f32(u.x & 0xffffu); xv[1] = bf16_bits_to_f32(u.x >> 16);
+                        xv[2] = bf16_bits_to_f32(u.y & 0xffffu); xv[3] = bf16_bits_to_f32(u.y >> 16);
+                    } else {
+                        const f32x4 f = xf[st][b];
+                        xv[0] = f.x; xv[1] = f.y; xv[2] = f.z; xv[3] = f.w;
+                    }
+#pragma unroll
+                    for (int a = 0; a < EW; ++a)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[a][b] = fma(xv[q], (double)w4[st][a][q], acc[a][b]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int a = 0; a < EW; ++a)
+#pragma unroll
+        for (int b = 0; b < TB; ++b) {
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) acc[a][b] += __shfl_xor(acc[a][b], off, 64);
+        }
+#pragma unroll
+    for (int a = 0; a < EW; ++a)
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+            if (lane == a * TB + b && b < nt) part[((size_t)c * T + t0 + b) * E + eg * EW + a] = acc[a][b];
+}
+
+// Exact top-k of one token by rank counting: thread e counts the experts that
+// beat it (larger logit, or equal logit and lower index); rank < k selects it.
+// The ranks are a permutation of 0..E-1 (no NaN reaches here), so exactly k
+// distinct experts are selected.
+// All threads read the same logit at a time (LDS broadcast).  Writes the
+// selections in rank order and their normalised sigmoid weights.  256 threads.
+__device__ void rank_topk(const double *lg, int E, int k, int32_t *idx_out, float *w_out, int32_t *sel_e,
+                          double *sel_l)
+{
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += 256) {
+        const double le = lg[e];
+        int r = 0;
+        int f = 0;
+        for (; f + 4 <= E; f += 4) {
+            const double l0 = lg[f], l1 = lg[f + 1], l2 = lg[f + 2], l3 = lg[f + 3];
+            r += (l0 > le) || (l0 == le && f < e);
+            r += (l1 > le) || (l1 == le && f + 1 < e);
+            r += (l2 > le) || (l2 == le && f + 2 < e);
+            r += (l3 > le) || (l3 == le && f + 3 < e);
+        }
+        for (; f < E; ++f) r += (lg[f] > le) || (lg[f] == le && f < e);
+        if (r < k) { sel_e[r] = e; sel_l[r] = le; }
+    }
+    __syncthreads();
+    if (tid < 64) {
+        // weights: sigmoid of the selected logits over their sum (fp64)
+        double s = 0.0;
+        for (int j = tid; j < k; j += 64) s += 1.0 / (1.0 + exp(-sel_l[j]));
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+        for (int j = tid; j < k; j += 64) {
+            idx_out[j] = sel_e[j];
+            w_out[j] = (float)((1.0 / (1.0 + exp(-sel_l[j]))) / s);
+        }
+    }
+}
+
+__device__ __forceinline__ void token_logits(const double *part, const float *bias, int T, int E, int NC, int t,
+                                             double *lg)
+{
+    for (int e = threadIdx.x; e < E; e += 256) {
+        double v = part[(size_t)t * E + e];
+        for (int c = 1; c < NC; ++c) v += part[((size_t)c * T + t) * E + e];
+        if (bias) v += (double)bias[e];
+        lg[e] = v != v ? -INFINITY : v;   // NaN ranks below every number, so ranks stay a permutation
+    }
+    __syncthreads();
+}
+
+// counts, offsets, perm and inv from the selections (T <= 64); 256 threads
+__device__ void group_small(const int32_t *sidx, int T, int E, int k, int32_t *offsets, int32_t *perm, int32_t *inv,
+                            uint32_t *mask, int32_t *cnt)
+{
+    const int tid = threadIdx.x;
+    for (int i = tid; i < 2 * E; i += 256) mask[i] = 0;
+    __syncthreads();
+    for (int a = tid; a < T * k; a += 256) {
+        const int t = a / k, e = sidx[a];
+        atomicOr(&mask[2 * e + (t >> 5)], 1u << (t & 31));
+    }
+    __syncthreads();
+    int local[4], run = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = 4 * tid + i;
+        local[i] = e < E ? __popc(mask[2 * e]) + __popc(mask[2 * e + 1]) : 0;
+        run += local[i];
+    }
+    cnt[tid] = run;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const int v = tid >= off ? cnt[tid - off] : 0;
+        __syncthreads();
+        cnt[tid] += v;
+        __syncthreads();
+    }
+    int base = cnt[tid] - run;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = 4 * tid + i;
+        if (e < E) { cnt[e] = base; offsets[e] = base; }
+        base += local[i];
+    }
+    if (tid == 255) offsets[E] = base;
+    __syncthreads();
+    for (int a = tid; a < T * k; a += 256) {
+        const int t = a / k, e = sidx[a];
+        const uint64_t m = (uint64_t)mask[2 * e] | ((uint64_t)mask[2 * e + 1] << 32);
+        const uint64_t below = t ? ((1ull << t) - 1ull) : 0ull;
+        const int pos = cnt[e] + __popcll(m & below);
+        perm[pos] = a;
+        inv[a] = pos;
+    }
+}
+
+// T == 1: selection and grouping in one work-group
+__global__ __launch_bounds__(256) void route_select_one(const double *part, const float *bias, int E, int k, int NC,
+                                                        int32_t *topk_idx, float *topk_w, int32_t *offsets,
+                                                        int32_t *perm, int32_t *inv)
+{
+    __shared__ double lg[1024];
+    __shared__ double sel_l[64];
+    __shared__ int32_t sel_e[64];
+    __shared__ uint32_t mask[2 * 1024];
+    __shared__ int32_t cnt[1024];
+    token_logits(part, bias, 1, E, NC, 0, lg);
+    rank_topk(lg, E, k, topk_idx, topk_w, sel_e, sel_l);
+    __syncthreads();
+    group_small(sel_e, 1, E, k, offsets, perm, inv, mask, cnt);
+}
+
+// 1 < T <= 64: one work-group per token selects ...
+__global__ __launch_bounds__(256) void route_select_tok(const double *part, const float *bias, int T, int E, int k,
+                                                        int NC, int32_t *topk_idx, float *topk_w)
+{
+    __shared__ double lg[1024];
+    __shared__ double sel_l[64];
+    __shared__ int32_t sel_e[64];
+    const int t = blockIdx.x;
+    token_logits(part, bias, T, E, NC, t, lg);
+    rank_topk(lg, E, k, topk_idx + (size_t)t * k, topk_w + (size_t)t * k, sel_e, sel_l);
+}
+
+// ... and one work-group groups them
+__global__ __launch_bounds__(256) void route_group_small(const int32_t *topk_idx, int T, int E, int k,
+                                                         int32_t *offsets, int32_t *perm, int32_t *inv)
+{
+    __shared__ int32_t sidx[64 * 64];
+    __shared__ uint32_t mask[2 * 1024];
+    __shared__ int32_t cnt[1024];
+    for (int a = threadIdx.x; a < T * k; a += 256) sidx[a] = topk_idx[a];
+    __syncthreads();
+    group_small(sidx, T, E, k, offsets, perm, inv, mask, cnt);
+}
+
+int route_decode_chunks(int T, int H)
+{
+    // enough waves to spread the W_r stream over the chip at small T; the
+    // split depends on H only, so a token's logits do not depend on T
+    (void)T;
+    const int steps = (H + 255) / 256;
+    return std::min(4, steps);
+}
+
+void launch_route_partial(const void *x, bool xbf16, const float *wr, int T, int H, int E, double *part, hipStream_t s)
+{
+    const int NC = route_decode_chunks(T, H);
+    const int steps = (H + 255) / 256;
+    const int HC = ((steps + NC - 1) / NC) * 256;
+    const int EW = (T > 8 && E % 4 == 0) ? 4 : 1;
+    const int TB = T <= 2 ? 1 : 8;
+    const int items = (E / EW) * ((T + TB - 1) / TB) * NC;
+    const int grid = (items + 3) / 4;
+#define MOE_RP(ew, tb, xb) route_partial<ew, tb, xb><<<grid, 256, 0, s>>>(x, wr, T, H, E, NC, HC, part)
+    if (EW == 4) { if (xbf16) MOE_RP(4, 8, true); else MOE_RP(4, 8, false); }
+    else if (TB == 8) { if (xbf16) MOE_RP(1, 8, true); else MOE_RP(1, 8, false); }
+    else { if (xbf16) MOE_RP(1, 1, true); else MOE_RP(1, 1, false); }
+#undef MOE_RP
+}
+
+void launch_route_select(const double *part, const float *bias, int T, int H, int E, int k, int32_t *topk_idx,
+                         float *topk_w, int32_t *offsets, int32_t *perm, int32_t *inv, hipStream_t s)
+{
+    const int NC = route_decode_chunks(T, H);
+    if (T == 1) {
+        route_select_one<<<1, 256, 0, s>>>(part, bias, E, k, NC, topk_idx, topk_w, offsets, perm, inv);
+    } else {
+        route_select_tok<<<T, 256, 0, s>>>(part, bias, T, E, k, NC, topk_idx, topk_w);
+        route_group_small<<<1, 256, 0, s>>>(topk_idx, T, E, k, offsets, perm, inv);
+    }
 }
 
 }  // namespace moe

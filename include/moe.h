@@ -126,8 +126,9 @@ typedef struct moe_profile {
  * section 3.4.3; section 9.2 on routing quality); the function (sigmoid,
  * top-k, renormalised weights) is the workload's definition.
  * x: [T][H] of type `act` (device).  bias: fp32 [E] or NULL.  All outputs are
- * device arrays of the sizes shown.  Launches: logits, then either one fused
- * small-T select/group kernel (T <= 64) or top-k, rank, scan and scatter. */
+ * device arrays of the sizes shown.  Launches: for T <= 64 and k <= 64 fp64
+ * partial logits, then one work-group that selects and groups; otherwise
+ * logits, then top-k, rank, scan and scatter. */
 int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bias,
               int32_t *topk_idx, float *topk_w, int32_t *offsets, int32_t *perm, int32_t *inv,
               void *ws, size_t ws_bytes, void *stream, moe_profile *prof);
@@ -140,9 +141,12 @@ int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bi
  * moe_expert_ffn_decode -- fp32-accurate path meant for small T (any T works):
  *   weights applied exactly (integer codes in bf16 MFMA with fp32 block
  *   rescale), activations exact (bf16) or split into two bf16 terms (fp32),
- *   fp32 accumulation, intermediate h in fp32.  Relative L2 error against an
- *   exact evaluation is far below 1e-4.  Formats: CB2/Q2K routed, BF16 shared.
- *   Launches: schedule, gate/up+SwiGLU, down, combine.
+ *   fp32 accumulation, intermediate h in fp32 (single-token path: h held as
+ *   two bf16 terms).  Relative L2 error against an exact evaluation is far
+ *   below 1e-4.  Formats: CB2/Q2K routed, BF16 shared.  Launches: for T = 1
+ *   (with H % 512 == 0, I % 256 == 0, I <= 2048, sh_inter % 512 == 0, k <= 64)
+ *   gate/up+SwiGLU, down, combine; otherwise schedule, gate/up+SwiGLU, down,
+ *   combine.
  * moe_expert_ffn_prefill -- bf16 MFMA path for any T: x must be bf16;
  *   dequantized weights rounded to bf16 (RNE) in LDS; fp32 accumulation;
  *   h rounded to bf16; down output and combine in fp32.  Relative L2 error

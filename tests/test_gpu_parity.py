@@ -100,6 +100,11 @@ SMALL = [
     ("mid_T300", mid(300, 14)),
     ("mid_allexperts", mid(9, 15, top_k=16, n_experts=16)),
     ("mid_f32x", mid(20, 16, x_dtype="f32")),
+    # single-token decode path: H % 512 == 0, I % 256 == 0, shared I % 512 == 0
+    ("one_T1", mid(1, 22, hidden=1024, inter=512, sh_inter=512)),
+    ("one_T1_f32x", mid(1, 23, hidden=1024, inter=512, sh_inter=512, x_dtype="f32")),
+    ("one_T1_noshared", mid(1, 24, hidden=1024, inter=768, sh_inter=0)),
+    ("one_T1_k16", mid(1, 25, hidden=512, inter=256, sh_inter=512, n_experts=32, top_k=16)),
 ]
 
 
@@ -181,6 +186,27 @@ def test_T0_is_a_noop():
     M.ffn_prefill(wl.layer, x, act, 0, r, y, ws)
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
+
+
+@pytest.mark.parametrize("name,cfg", [c for c in SMALL if c[1]["T"] == 1], ids=lambda v: v if isinstance(v, str) else "")
+def test_repeated_calls_reuse_workspace(small_cases, name, cfg):
+    """Three calls on one workspace give bit-identical results (no state is
+    carried between calls)."""
+    wl, _, _ = _case(small_cases, name, cfg)
+    x, act = wl.tokens(cfg)
+    T = x.shape[0]
+    r = M.Routing(T, cfg["top_k"], cfg["n_experts"])
+    ws_r = wl.layer.workspace(T, M.PATH_ROUTE)
+    ws_f = wl.layer.workspace(T, M.PATH_DECODE)
+    outs = []
+    for _ in range(3):
+        y = torch.full((T, cfg["hidden"]), float("nan"), device="cuda")
+        M.route(wl.layer, x, act, T, wl.bias(cfg), r, ws_r)
+        M.ffn_decode(wl.layer, x, act, T, r, y, ws_f)
+        torch.cuda.synchronize()
+        outs.append(y.cpu().numpy())
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
 
 
 def test_decode_batch_invariance():
