@@ -127,16 +127,21 @@ struct FfnWs {
     // single-token decode
     bool single;
     float *part_sh, *O_sh;
-    uint16_t *h_hi, *h_lo, *X;
+    uint16_t *h_hi, *h_lo;
+    float *X;
 };
 
-bool dec_single(const moe_layer *L, int T, bool prefill)
+// single-token decode kernels apply: T == 1, CB2/Q2K, shapes they support
+bool dec_single(const moe_layer *L, int T, bool prefill, bool x_f32)
 {
     if (prefill || L->fmt_gate_up != MOE_FMT_CB2 || L->fmt_down != MOE_FMT_Q2K) return false;
-    return dec_single_ok(T, L->hidden, L->inter, L->sh_inter, L->top_k, nblocks(L->hidden) * 38);
+    return dec_single_ok(T, L->hidden, L->inter, L->sh_inter, L->top_k, nblocks(L->hidden) * 38, x_f32);
 }
 
-FfnWs ffn_ws(const moe_layer *L, int T, bool prefill, char *base)
+// Workspace carving.  `single` selects the single-token layout; the size a
+// caller must provide (moe_workspace_bytes) is the larger of the layouts the
+// call may take, since the choice also depends on the activation type.
+FfnWs ffn_ws(const moe_layer *L, int T, bool prefill, bool single, char *base)
 {
     FfnWs w{};
     const int has_sh = L->sh_inter > 0;
@@ -144,17 +149,17 @@ FfnWs ffn_ws(const moe_layer *L, int T, bool prefill, char *base)
     const size_t rows = (size_t)T * L->top_k + (has_sh ? T : 0);
     w.hstride = std::max(L->inter, L->sh_inter);
     size_t off = 0;
-    w.single = dec_single(L, T, prefill);
+    w.single = single;
     if (w.single) {
         const size_t k = L->top_k, H = L->hidden, Ish = L->sh_inter, nbI = nblocks(L->inter);
         w.part_sh = (float *)(base + off);
-        off = align_up(off + 4 * 2 * Ish * sizeof(float));
+        off = align_up(off + DEC_SH_KQ * 2 * Ish * sizeof(float));
         w.h_hi = (uint16_t *)(base + off);
-        off = align_up(off + (k + 1) * w.hstride * 2);
+        off = align_up(off + k * w.hstride * 2);
         w.h_lo = (uint16_t *)(base + off);
-        off = align_up(off + (k + 1) * w.hstride * 2);
-        w.X = (uint16_t *)(base + off);
-        off = align_up(off + k * nbI * 32 * 2);
+        off = align_up(off + k * w.hstride * 2);
+        w.X = (float *)(base + off);
+        off = align_up(off + k * nbI * 16 * sizeof(float));
         w.O = (float *)(base + off);
         off = align_up(off + k * H * sizeof(float));
         w.O_sh = (float *)(base + off);
@@ -170,6 +175,14 @@ FfnWs ffn_ws(const moe_layer *L, int T, bool prefill, char *base)
     off = align_up(off + rows * (size_t)L->hidden * sizeof(float));
     w.bytes = off;
     return w;
+}
+
+size_t ffn_ws_bytes(const moe_layer *L, int T, bool prefill)
+{
+    size_t b = ffn_ws(L, T, prefill, false, nullptr).bytes;
+    for (int xf = 0; xf < 2; ++xf)
+        if (dec_single(L, T, prefill, xf)) b = std::max(b, ffn_ws(L, T, prefill, true, nullptr).bytes);
+    return b;
 }
 
 int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t *topk_idx, const float *topk_w,
@@ -191,8 +204,9 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
         if (L->fmt_gate_up != MOE_FMT_CB2 || L->fmt_down != MOE_FMT_Q2K)
             return fail(MOE_ERR_UNSUPPORTED, "decode supports CB2 gate/up with Q2K down");
     }
-    FfnWs w = ffn_ws(L, T, prefill, (char *)ws);
-    if (ws_bytes < w.bytes) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.bytes);
+    const size_t need = ffn_ws_bytes(L, T, prefill);
+    if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    FfnWs w = ffn_ws(L, T, prefill, dec_single(L, T, prefill, act == MOE_ACT_F32), (char *)ws);
 
     hipStream_t s = (hipStream_t)stream;
     Prof pr{prof, s};
@@ -215,6 +229,7 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
         d.h_hi = w.h_hi; d.h_lo = w.h_lo; d.hstride = w.hstride; d.X = w.X;
         d.part_sh = w.part_sh;
         d.O = w.O; d.O_sh = w.O_sh; d.y = y;
+        dec_plan(d);
         if (!pr.before("dec_gateup")) return hip_fail(hipGetLastError(), "event record");
         hipError_t e = launch_dec_gateup(d, s);
         if (e != hipSuccess) return hip_fail(e, "dec_gateup launch");
@@ -313,7 +328,7 @@ size_t moe_workspace_bytes(const moe_layer *L, int T, int path)
     }
     if (path != MOE_PATH_DECODE && path != MOE_PATH_PREFILL) return 0;
     if (check_layer(L)) return 0;
-    return ffn_ws(L, T, path == MOE_PATH_PREFILL, nullptr).bytes;
+    return ffn_ws_bytes(L, T, path == MOE_PATH_PREFILL);
 }
 
 int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bias, int32_t *topk_idx,

@@ -1,55 +1,55 @@
 // Single-token decode (T = 1): the memory-bound case the pages describe for
 // decode, where every routed weight is read once per token step while compute
-// idles ("Part 5: 服务层", section 6).  Two launches after the router:
+// idles ("Part 5: 服务层", section 6).  Three launches after the router:
 //
-//   dec_gateup: each routed 16-row tile of one expert is one contiguous byte
-//     range (gate and up, 2 x 16 x 1064 B at H = 7168); a work-group loads it
-//     whole with 16-byte loads, all in flight, then eight waves split K.
-//     Codebook entries are exact bf16 MFMA operands; the fp32 sub-block
-//     scale d*s_j multiplies each 32-wide partial sum.  The epilogue writes
-//     h = silu(g)*u as two bf16 terms (hi + lo, relative error below 2^-17)
-//     and, per 16-row sub-block, the sums of h that Q2_K's min term needs.
-//     The bf16 shared expert runs as four K quarters that write partial sums.
-//   dec_down: 64 output rows per work-group and group; Q2_K codes become
-//     exact bf16 values sc*q through a 32 KB LDS table indexed by (sc, code
-//     byte); the block scale d and the min term dmin * sum_j m_j X_j apply to
-//     the fp32 sums of each 256-wide block.  The shared expert's work-groups
-//     first add the four gate/up quarters (in order) and form their slice of h.
-//   dec_combine: y = sum of the shared expert's K parts + the routed outputs
-//     weighted in top-k order.
+//   dec1_gateup: gate/up GEMVs + SwiGLU.  One persistent work-group per
+//     resident slot; each takes one role.  Shared-expert units are 16 bf16
+//     rows x one K eighth, loaded straight into MFMA B registers.  Routed
+//     units are 32 rows of gate and 32 of up of one selected expert
+//     (2 x 32 x 1064 B at H = 7168, two contiguous byte ranges), staged
+//     through LDS because the 38-byte blocks are only 2-byte aligned.  While
+//     one unit is computed the next unit's bytes are already in flight.
+//     Codebook entries are exact bf16 MFMA operands; the fp32 sub-block scale
+//     d*s_j multiplies each 32-wide partial sum.  h = silu(g)*u is stored as
+//     two bf16 terms (hi + lo, relative error below 2^-17) with the per-16
+//     sums Q2_K's min term needs; the shared expert stores fp32 partial sums
+//     of its K eighths.
+//   dec1_down: persistent again.  A unit is 128 output rows (16 per wave, each
+//     wave over the whole K) of one selected expert's Q2_K down, or of one
+//     512-wide K part of the bf16 shared down.  Q2_K codes become exact bf16
+//     values sc*q through a 32 KB LDS table indexed by (sc, code byte); the
+//     block scale d and the min term dmin * sum_j m_j X_j apply to the fp32
+//     sums of each 256-wide block.
+//   dec1_combine: y = the shared expert's K parts in order + the routed
+//     outputs weighted in top-k order.
 //
-// Work-groups of one launch never wait for each other: on this chip a
-// device-scope release/acquire writes back and invalidates the L2 of an XCD,
-// so results pass between work-groups only across launches.
+// Each codebook lookup reads a 16-byte LDS entry for 1.19 bytes of weights,
+// so a CU streams routed gate/up more slowly than bf16 rows; the role split
+// gives the routed role proportionally more work-groups.  Routed buffers are
+// indexed by top-k slot j (h, X, O), so no kernel needs the grouping arrays at
+// T = 1.  Activation terms (x or h as hi + lo bf16) enter as rows 0 and 1 of
+// the MFMA A operand, so one MFMA covers both.  Work-groups of one launch
+// never wait for each other: results pass between work-groups only across
+// launches.
 #include <algorithm>
+#include <atomic>
 
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int DD_ROWS = 64;        // output rows per down work-group
-constexpr int DD_KPART = 512;      // shared-expert K part of the down pass
-
-// ---------------------------------------------------------------- helpers
-// With one token, the k selected experts sit at positions sorted by expert
-// id: slot s is the expert of stable rank s among topk_idx[0..k) (rank = number
-// of smaller ids plus equal ids earlier in the list, a permutation of 0..k-1
-// even if a corrupt routing repeated an expert).  All threads call it.
-__device__ __forceinline__ int rank_expert(const int32_t *topk_idx, int k, int slot, int *lds)
-{
-    if ((int)threadIdx.x < k) lds[threadIdx.x] = topk_idx[threadIdx.x];
-    __syncthreads();
-    int g = -1;
-    for (int j = 0; j < k; ++j) {
-        const int ej = lds[j];
-        int rank = 0;
-        for (int i = 0; i < k; ++i) rank += (lds[i] < ej) || (i < j && lds[i] == ej);
-        if (rank == slot) g = ej;
-    }
-    __syncthreads();
-    return g;
-}
+constexpr int D1_THREADS = 512;
+constexpr int GU_ROWS = 32;        // rows of a routed gate/up unit (two 16-row halves)
+constexpr int GU_MAXL = 9;         // u32x4 per thread of a routed gate/up unit (2 * 32 * rb <= 512 * 9 * 16 B)
+constexpr int SH_KQ = DEC_SH_KQ;   // K parts of the shared gate/up
+constexpr int SH_MAXS = 4;         // shared gate/up K steps (of 32) per wave and unit
+constexpr int DN_ROWS = 128;       // output rows of a down unit (16 per wave)
+constexpr int DN_KPART = 512;      // K part of a shared down unit
+constexpr int DN_MAXB = 8;         // Q2_K blocks per row of a routed down unit (I <= 2048)
+constexpr int DN_STAGE = 4;        // h staging slots per thread: k * (I/256) * 32 <= 512 * 4
+constexpr int CB_COPIES = 8;       // interleaved codebook copies in LDS (no bank conflicts)
+constexpr size_t LDS_MAX = 160 * 1024;
 
 __device__ __forceinline__ void split_bf16(float v, uint32_t &hi, uint32_t &lo)
 {
@@ -62,337 +62,380 @@ __device__ __forceinline__ u32x4 pack8(const uint32_t h[8])
     return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
 }
 
-// h for 16 feature rows r0.. of one position, from the fp32 gate/up sums
-// g[16], u[16]; with `routed`, also the sub-block sum for Q2_K's min term.
-// Threads 0..15 (one wave) do the work.
-__device__ __forceinline__ void finalize_h(const DecPass &p, int64_t pos, int r0, int ncols, bool routed,
-                                           const float *g, const float *u)
+// A operand of one token's activation terms: row 0 = hi, row 1 = lo (when
+// there are two terms), other rows zero.  Lane (fr, fc) supplies 8 values at k.
+template <bool TWO>
+__device__ __forceinline__ bf16x8 act_rows(const uint16_t *hi, const uint16_t *lo, int k, int fr)
 {
-    const int tid = threadIdx.x;
-    if (tid < 16) {
-        const int n = r0 + tid;
-        const float gv = g[tid], uv = u[tid];
-        const float h = n < ncols ? gv / (1.0f + expf(-gv)) * uv : 0.f;
-        uint32_t hi, lo;
-        split_bf16(h, hi, lo);
-        if (n < ncols) {
-            p.h_hi[pos * p.hstride + n] = (uint16_t)hi;
-            p.h_lo[pos * p.hstride + n] = (uint16_t)lo;
-        }
-        if (routed) {
-            float s = h;                            // rows r0..r0+15 = one 16-wide sub-block of down's K
+    bf16x8 a = {};
+    if (fr == 0) a = *(const bf16x8 *)&hi[k];
+    else if (TWO && fr == 1) a = *(const bf16x8 *)&lo[k];
+    return a;
+}
+
+// The eight A fragments k0, k0 + step, ... of one block for rows 0 (and 1 with
+// two terms), read in one masked region.  Rows 2..15 of A only feed rows 2..15
+// of D, which no caller reads, so they are left as they are.
+template <bool TWO>
+__device__ __forceinline__ void act_block(const uint16_t *row, int k0, int step, int fr, bf16x8 (&a)[8])
+{
+    if (fr < (TWO ? 2 : 1)) {
 #pragma unroll
-            for (int off = 8; off > 0; off >>= 1) s += __shfl_xor(s, off, 16);
-            if (tid == 0) {
-                uint32_t shi, slo;
-                split_bf16(s, shi, slo);
-                uint16_t *xr = p.X + (pos * p.nbI + (r0 >> 8)) * 32;
-                xr[(r0 & 255) >> 4] = (uint16_t)shi;
-                xr[16 + ((r0 & 255) >> 4)] = (uint16_t)slo;
-            }
-        }
+        for (int m = 0; m < 8; ++m) a[m] = *(const bf16x8 *)&row[k0 + step * m];
     }
 }
 
-// ============================================================== gate / up
-constexpr int DG_KQ = 4;           // shared-expert K quarters
+__device__ __forceinline__ int clamp_expert(int g, int E) { return min(max(g, 0), E - 1); }
 
+// ============================================================== gate / up
+// Work-groups [0, gu_sh_wg) take shared-expert units u = wg, wg + gu_sh_wg, ...;
+// the others take routed units the same way.
 template <bool XF32>
-__global__ __launch_bounds__(512) void dec_gateup_kernel(DecPass p)
+__global__ __launch_bounds__(D1_THREADS) void dec1_gateup_kernel(DecPass p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
-    __shared__ float gsum[16], usum[16];
-    __shared__ int kidx[64];
+    __shared__ int kid[64];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int fr = lane & 15, fc = lane >> 4;
-    const int n_sh_items = p.Ish > 0 ? (p.Ish / 16) * DG_KQ : 0;
-    int item = blockIdx.x;
+    const int H = p.H;
+    uint16_t *xh = (uint16_t *)dsm;                               // [H]
+    uint16_t *xl = xh + H;                                        // [H] (fp32 x only)
+    float *red = (float *)(dsm + (XF32 ? 4 : 2) * (size_t)H);     // [8 waves][2][16]
+    uint16_t *cbt = (uint16_t *)(red + 256);                      // [256][8 copies][8] bf16 codewords
+    uint8_t *wt = (uint8_t *)(cbt + 256 * CB_COPIES * 8);         // [2][32][rb]
 
-    if (item < n_sh_items) {
-        // ---------------------------------------------- shared expert, one K quarter
-        const int rt = item / DG_KQ, q = item % DG_KQ;
-        const int r0 = rt * 16;
-        const int KQ = p.H / DG_KQ, k0 = q * KQ;
-        const int nsteps = KQ / 32;
-        uint16_t *xh = (uint16_t *)dsm;             // [KQ] hi
-        uint16_t *xl = xh + KQ;                     // [KQ] lo (fp32 x only)
-        float *red = (float *)(dsm + 4 * KQ);       // [8 waves][2][64*4]
-        // B fragments straight from HBM: wave w takes K steps w, w+8, ...
-        constexpr int MAXS = 9;
-        u32x4 bg[MAXS], bu[MAXS];
-        const uint16_t *rg = p.sg + (int64_t)(r0 + fr) * p.H + k0 + 8 * fc;
-        const uint16_t *ru = p.su + (int64_t)(r0 + fr) * p.H + k0 + 8 * fc;
+    const bool shared_role = (int)blockIdx.x < p.gu_sh_wg;
+    const int n_units = shared_role ? (p.Ish / 16) * SH_KQ : p.k * (p.I / GU_ROWS);
+    const int G = shared_role ? p.gu_sh_wg : p.gu_rt_wg;
+    int u = shared_role ? (int)blockIdx.x : (int)blockIdx.x - p.gu_sh_wg;
+    if (u >= n_units) return;                                     // uniform over the work-group
+
+    // ---- x (hi, and lo for fp32 x) into LDS once
+    for (int i = tid; i < H / 8; i += D1_THREADS) {
+        if (XF32) {
+            const float *src = (const float *)p.x + 8 * i;
+            uint32_t h[8], l[8];
 #pragma unroll
-        for (int j = 0; j < MAXS; ++j) {
-            const int st = wave + 8 * j;
-            if (st < nsteps) {
-                bg[j] = *(const u32x4 *)(rg + 32 * st);
-                bu[j] = *(const u32x4 *)(ru + 32 * st);
-            }
+            for (int e = 0; e < 8; ++e) split_bf16(src[e], h[e], l[e]);
+            *(u32x4 *)&xh[8 * i] = pack8(h);
+            *(u32x4 *)&xl[8 * i] = pack8(l);
+        } else {
+            *(u32x4 *)&xh[8 * i] = *(const u32x4 *)((const uint16_t *)p.x + 8 * i);
         }
-        for (int i = tid; i < KQ / 8; i += 512) {
-            if (XF32) {
-                const float *src = (const float *)p.x + k0 + 8 * i;
-                uint32_t h[8], l[8];
+    }
+
+    if (shared_role) {
+        // ---------------------------------------------- shared expert
+        const int KQ = H / SH_KQ, nsteps = KQ / 32;
+        // two register buffers in turn: unit u+G loads into one while unit u
+        // computes from the other (no copies, so no early waits on the loads)
+        u32x4 ga[SH_MAXS], ua[SH_MAXS], gb[SH_MAXS], ub[SH_MAXS];
+        auto load = [&](int uu, u32x4 (&G4)[SH_MAXS], u32x4 (&U4)[SH_MAXS]) {
+            const int r0 = (uu / SH_KQ) * 16, k0 = (uu % SH_KQ) * KQ;
+            const uint16_t *rg = p.sg + (int64_t)(r0 + fr) * H + k0 + 8 * fc;
+            const uint16_t *ru = p.su + (int64_t)(r0 + fr) * H + k0 + 8 * fc;
+            // unconditional loads (steps past the end re-read the last one and
+            // are never used): a load under a branch makes the compiler wait for it
 #pragma unroll
-                for (int e = 0; e < 8; ++e) split_bf16(src[e], h[e], l[e]);
-                *(u32x4 *)&xh[8 * i] = pack8(h);
-                *(u32x4 *)&xl[8 * i] = pack8(l);
-            } else {
-                *(u32x4 *)&xh[8 * i] = *(const u32x4 *)((const uint16_t *)p.x + k0 + 8 * i);
+            for (int j = 0; j < SH_MAXS; ++j) {
+                const int st = min(wave + 8 * j, nsteps - 1);
+                G4[j] = *(const u32x4 *)(rg + 32 * st);
+                U4[j] = *(const u32x4 *)(ru + 32 * st);
             }
-        }
-        __syncthreads();
-        f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+        };
+        auto unit = [&](int uu, const u32x4 (&G4)[SH_MAXS], const u32x4 (&U4)[SH_MAXS]) {
+            const int r0 = (uu / SH_KQ) * 16, q = uu % SH_KQ, k0 = q * KQ;
+            f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+            // every step consumes its registers (steps past the end with a zero
+            // A operand): a register left unread on some path keeps its load
+            // pending there, and the next load into it would wait for it
 #pragma unroll
-        for (int j = 0; j < MAXS; ++j) {
-            const int st = wave + 8 * j;
-            if (st >= nsteps) break;
-            const int k = 32 * st + 8 * fc;
-            bf16x8 a = {};
-            if (fr == 0) a = *(const bf16x8 *)&xh[k];          // A row 0 = the token
-            const bf16x8 Bg = __builtin_bit_cast(bf16x8, bg[j]), Bu = __builtin_bit_cast(bf16x8, bu[j]);
-            ag = mfma16x16x32(a, Bg, ag);
-            au = mfma16x16x32(a, Bu, au);
-            if (XF32) {
-                bf16x8 al = {};
-                if (fr == 0) al = *(const bf16x8 *)&xl[k];
-                ag = mfma16x16x32(al, Bg, ag);
-                au = mfma16x16x32(al, Bu, au);
+            for (int j = 0; j < SH_MAXS; ++j) {
+                const int st = wave + 8 * j;
+                bf16x8 a = act_rows<XF32>(xh, xl, k0 + 32 * min(st, nsteps - 1) + 8 * fc, fr);
+                if (st >= nsteps) a = bf16x8{};
+                ag = mfma16x16x32(a, __builtin_bit_cast(bf16x8, G4[j]), ag);
+                au = mfma16x16x32(a, __builtin_bit_cast(bf16x8, U4[j]), au);
             }
-        }
-        // D element (slot 0, feature fr) sits in lane fr (fc = 0), element 0
-        if (fc == 0) { red[(wave * 2 + 0) * 16 + fr] = ag[0]; red[(wave * 2 + 1) * 16 + fr] = au[0]; }
-        __syncthreads();
-        if (tid < 16) {
-            float g = 0.f, u = 0.f;
+            // D[0][n] (x hi) and D[1][n] (x lo) of feature n sit in lane n, elements 0 and 1
+            if (fc == 0) {
+                red[(wave * 2 + 0) * 16 + fr] = XF32 ? ag[0] + ag[1] : ag[0];
+                red[(wave * 2 + 1) * 16 + fr] = XF32 ? au[0] + au[1] : au[0];
+            }
+            __syncthreads();
+            if (tid < 32) {
+                const int m = tid >> 4, n = tid & 15;
+                float sum = 0.f;
 #pragma unroll
-            for (int w = 0; w < 8; ++w) { g += red[(w * 2 + 0) * 16 + tid]; u += red[(w * 2 + 1) * 16 + tid]; }
-            p.part_sh[(int64_t)(q * 2 + 0) * p.Ish + r0 + tid] = g;
-            p.part_sh[(int64_t)(q * 2 + 1) * p.Ish + r0 + tid] = u;
+                for (int w = 0; w < 8; ++w) sum += red[(w * 2 + m) * 16 + n];
+                p.part_sh[(int64_t)(q * 2 + m) * p.Ish + r0 + n] = sum;
+            }
+            __syncthreads();
+        };
+        // the prefetch is unconditional (the last unit re-reads its own bytes,
+        // which the L2 still holds): a load under a branch makes every later
+        // wait assume the shorter path and wait for the prefetch as well
+        load(u, ga, ua);
+        __syncthreads();                                          // x staged
+        for (;;) {
+            load(u + G < n_units ? u + G : u, gb, ub);
+            unit(u, ga, ua);
+            u += G;
+            if (u >= n_units) break;
+            load(u + G < n_units ? u + G : u, ga, ua);
+            unit(u, gb, ub);
+            u += G;
+            if (u >= n_units) break;
         }
         return;
     }
 
-    // -------------------------------------------------- routed expert tile
-    item -= n_sh_items;
-    const int n_rt = p.I / 16;
-    const int slot = item / n_rt, rt = item % n_rt;
-    const int g = rank_expert(p.topk_idx, p.k, slot, kidx);
-    if (g < 0 || g >= p.E) return;
-    const int64_t pos = min(max(p.offsets[g], 0), p.k - 1);
-    const int r0 = rt * 16;
+    // -------------------------------------------------- routed experts
+    const int n_rt = p.I / GU_ROWS;
     const int rb = p.gu_row_bytes;
-    uint8_t *wt = dsm;                                   // [2][16][rb]
-    uint16_t *xh = (uint16_t *)(dsm + 32 * rb);          // [H] hi
-    uint16_t *cbt = xh + p.H;                            // [256][8] bf16 codewords
-    {
-        const int n16 = rb;                              // 16 rows * rb bytes / 16
-        const u32x4 *sg4 = (const u32x4 *)(p.wg + (int64_t)g * p.gu_expert_bytes + (int64_t)r0 * rb);
-        const u32x4 *su4 = (const u32x4 *)(p.wu + (int64_t)g * p.gu_expert_bytes + (int64_t)r0 * rb);
-        constexpr int MAXL = 5;                          // 2 * n16 <= 2560
-        u32x4 buf[MAXL];
-#pragma unroll
-        for (int j = 0; j < MAXL; ++j) {
-            const int i = tid + 512 * j;
-            if (i < n16) buf[j] = sg4[i];
-            else if (i < 2 * n16) buf[j] = su4[i - n16];
-        }
-        for (int i = tid; i < p.H / 8; i += 512) {
-            u32x4 v;
-            if (XF32) {
-                const float *src = (const float *)p.x + 8 * i;
-                uint32_t h[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) h[e] = f32_to_bf16_rne(src[e]);
-                v = pack8(h);
-            } else {
-                v = *(const u32x4 *)((const uint16_t *)p.x + 8 * i);
-            }
-            *(u32x4 *)&xh[8 * i] = v;
-        }
-        for (int i = tid; i < 256 * 8; i += 512) cbt[i] = (uint16_t)f32_to_bf16_exact((float)p.codebook[i]);
-#pragma unroll
-        for (int j = 0; j < MAXL; ++j) {
-            const int i = tid + 512 * j;
-            if (i < 2 * n16) *(u32x4 *)(wt + 16 * i) = buf[j];
-        }
+    const int n32 = 2 * rb;                                       // u32x4 per 32-row tile of one matrix
+    if (tid < p.k) kid[tid] = clamp_expert(p.topk_idx[tid], p.E);
+    // the codebook is held in CB_COPIES interleaved copies (entry e, copy c at
+    // 16 * (e * CB_COPIES + c) bytes); lane l reads copy l % CB_COPIES, so the
+    // eight lanes the LDS serves together always hit eight different bank
+    // groups, whatever entries they look up
+    for (int i = tid; i < 256 * CB_COPIES * 8; i += D1_THREADS) {
+        const int e = i / (CB_COPIES * 8), v = i % 8;
+        cbt[i] = (uint16_t)f32_to_bf16_exact((float)p.codebook[8 * e + v]);
     }
-    __syncthreads();
+    __syncthreads();                                              // x, codebook, expert ids staged
+    // one register buffer: the next unit is in flight while this one is
+    // computed from LDS
+    u32x4 buf[GU_MAXL];
+    auto load = [&](int uu) {
+        const int slot = uu / n_rt, rt = uu % n_rt;
+        const int64_t off = (int64_t)kid[slot] * p.gu_expert_bytes + (int64_t)rt * GU_ROWS * rb;
+        const u32x4 *sg4 = (const u32x4 *)(p.wg + off);
+        const u32x4 *su4 = (const u32x4 *)(p.wu + off);
+        // unconditional loads; indices past the unit re-read its last chunk
+#pragma unroll
+        for (int j = 0; j < GU_MAXL; ++j) {
+            const int i = tid + D1_THREADS * j;
+            buf[j] = i < n32 ? sg4[i] : su4[min(i - n32, n32 - 1)];
+        }
+    };
     const int nbH = rb / 38;
-    const int b0 = (nbH * wave) / 8, b1 = (nbH * (wave + 1)) / 8;
-    f32x4 acc_g = {0.f, 0.f, 0.f, 0.f}, acc_u = {0.f, 0.f, 0.f, 0.f};
-    const uint8_t *rowg = wt + fr * rb, *rowu = wt + 16 * rb + fr * rb;
-    for (int b = b0; b < b1; ++b) {
+    const int half = wave >> 2, kq = wave & 3;
+    const int cbc = lane % CB_COPIES;                             // this lane's codebook copy
+    const uint16_t *xa = XF32 && (fr & 1) ? xl : xh;             // this lane's A row (rows 0, 1 used)
+    const int b0 = (nbH * kq) / 4, b1 = (nbH * (kq + 1)) / 4;
+    const uint8_t *rowg = wt + (16 * half + fr) * rb, *rowu = wt + (GU_ROWS + 16 * half + fr) * rb;
+    // per block: raw header words and this lane's eight index bytes of gate and up
+    struct Hdr { uint32_t dg, du, sg, su; int ig[8], iu[8]; };
+    auto read_hdr = [&](int b, Hdr &h) {
         const uint8_t *bkg = rowg + 38 * b, *bku = rowu + 38 * b;
-        const float dg = f16_bits_to_f32(bkg[0] | (bkg[1] << 8));
-        const float du = f16_bits_to_f32(bku[0] | (bku[1] << 8));
+        h.dg = *(const uint16_t *)bkg;
+        h.du = *(const uint16_t *)bku;
+        h.sg = *(const uint16_t *)(bkg + 2) | ((uint32_t)*(const uint16_t *)(bkg + 4) << 16);
+        h.su = *(const uint16_t *)(bku + 2) | ((uint32_t)*(const uint16_t *)(bku + 4) << 16);
+#pragma unroll
+        for (int sb = 0; sb < 8; ++sb) { h.ig[sb] = bkg[6 + 4 * sb + fc]; h.iu[sb] = bku[6 + 4 * sb + fc]; }
+    };
+    // codebook entries, A rows and MFMAs of block b from its header
+    auto block = [&](int b, const Hdr &h, float &acc_g, float &acc_u) {
+        bf16x8 Bg[8], Bu[8];
 #pragma unroll
         for (int sb = 0; sb < 8; ++sb) {
-            const int sgv = (bkg[2 + (sb >> 1)] >> (4 * (sb & 1))) & 15;
-            const int suv = (bku[2 + (sb >> 1)] >> (4 * (sb & 1))) & 15;
-            const bf16x8 Bg = *(const bf16x8 *)&cbt[8 * bkg[6 + 4 * sb + fc]];
-            const bf16x8 Bu = *(const bf16x8 *)&cbt[8 * bku[6 + 4 * sb + fc]];
-            const int k = 256 * b + 32 * sb + 8 * fc;
-            bf16x8 a = {};
-            if (fr == 0) a = *(const bf16x8 *)&xh[k];
-            f32x4 Pg = mfma16x16x32(a, Bg, f32x4{0.f, 0.f, 0.f, 0.f});
-            f32x4 Pu = mfma16x16x32(a, Bu, f32x4{0.f, 0.f, 0.f, 0.f});
-            if (XF32) {
-                uint32_t lo[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                if (fr == 0) {
-                    const float *src = (const float *)p.x + k;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        uint32_t hi;
-                        split_bf16(src[e], hi, lo[e]);
-                    }
-                }
-                const bf16x8 al = __builtin_bit_cast(bf16x8, pack8(lo));
-                Pg = mfma16x16x32(al, Bg, Pg);
-                Pu = mfma16x16x32(al, Bu, Pu);
-            }
-            // D columns are features: this lane's column is feature fr, whose
-            // block and sub-block scale this lane read itself
-            acc_g += (dg * (float)sgv) * Pg;
-            acc_u += (du * (float)suv) * Pu;
+            Bg[sb] = *(const bf16x8 *)&cbt[8 * (h.ig[sb] * CB_COPIES + cbc)];
+            Bu[sb] = *(const bf16x8 *)&cbt[8 * (h.iu[sb] * CB_COPIES + cbc)];
         }
-    }
-    __syncthreads();                                     // wt is reused for the reduction
-    float *red = (float *)wt;                            // [8 waves][2][16]
-    if (fc == 0) { red[(wave * 2 + 0) * 16 + fr] = acc_g[0]; red[(wave * 2 + 1) * 16 + fr] = acc_u[0]; }
-    __syncthreads();
-    if (tid < 16) {
-        float gg = 0.f, uu = 0.f;
+        bf16x8 a[8];
+        act_block<XF32>(xa, 256 * b + 8 * fc, 32, fr, a);
+        const float dg = f16_bits_to_f32(h.dg), du = f16_bits_to_f32(h.du);
 #pragma unroll
-        for (int w = 0; w < 8; ++w) { gg += red[(w * 2 + 0) * 16 + tid]; uu += red[(w * 2 + 1) * 16 + tid]; }
-        gsum[tid] = gg;
-        usum[tid] = uu;
-    }
-    __syncthreads();
-    finalize_h(p, pos, r0, p.I, true, gsum, usum);
-}
-
-// ============================================================== down + combine
-// 512 threads: wave w owns output rows 16*(w&3).. of the tile and the K half
-// w>>2; the two halves are added in a fixed order before the write.
-__global__ __launch_bounds__(512) void dec_down_kernel(DecPass p)
-{
-    extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
-    __shared__ float red[4][16];
-    __shared__ int kidx[64];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int fr = lane & 15, fc = lane >> 4;
-    const int rg = wave & 3, kh = wave >> 2;
-    const int n_ot = (p.H + DD_ROWS - 1) / DD_ROWS;
-    const int KPD = p.Ish > 0 ? p.Ish / DD_KPART : 0;
-    const int n_sh_items = n_ot * KPD;
-    int item = blockIdx.x;
-    const bool sh = item < n_sh_items;
-    int ot, part = 0, g = -1;
-    if (sh) {
-        ot = item / KPD;
-        part = item % KPD;
-    } else {
-        item -= n_sh_items;
-        const int slot = item / n_ot;
-        ot = item % n_ot;
-        g = rank_expert(p.topk_idx, p.k, slot, kidx);
-        if (g < 0 || g >= p.E) return;
-    }
-    const int row = ot * DD_ROWS + 16 * rg + fr;       // this lane's output feature
-    const bool row_ok = row < p.H;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    int64_t pos = 0;
-
-    if (sh) {
-        // ---------------------------------------------- shared expert K part
-        const int k0 = part * DD_KPART;
-        uint16_t *hh = (uint16_t *)dsm, *hl = hh + DD_KPART;
-        u32x4 bw[8];                                    // K steps 8*kh .. 8*kh+7 of 32
-        const uint16_t *rw = p.sd + (int64_t)(row_ok ? row : 0) * p.Ish + k0 + 8 * fc;
+        for (int sb = 0; sb < 8; ++sb) {
+            const f32x4 Pg = mfma16x16x32(a[sb], Bg[sb], f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 Pu = mfma16x16x32(a[sb], Bu[sb], f32x4{0.f, 0.f, 0.f, 0.f});
+            // column fr is feature r0+16*half+fr, whose block and sub-block scale this lane read
+            acc_g += (dg * (float)((h.sg >> (4 * sb)) & 15)) * (XF32 ? Pg[0] + Pg[1] : Pg[0]);
+            acc_u += (du * (float)((h.su >> (4 * sb)) & 15)) * (XF32 ? Pu[0] + Pu[1] : Pu[0]);
+        }
+    };
+    load(u);
+    for (;;) {
+        __syncthreads();                                          // previous unit done with wt and red
+        // unconditional stores: lanes past the unit loaded the unit's last chunk
+        // and write those same bytes again
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-            bw[s] = row_ok ? *(const u32x4 *)(rw + 32 * (8 * kh + s)) : u32x4{0, 0, 0, 0};
-        // this part's slice of the shared expert's h: add the gate/up quarters
-        // in order, then silu(g) * u, split into two bf16 terms
-        for (int i = tid; i < DD_KPART; i += 512) {
-            float g = 0.f, u = 0.f;
-#pragma unroll
-            for (int q = 0; q < DG_KQ; ++q) {
-                g += p.part_sh[(int64_t)(q * 2 + 0) * p.Ish + k0 + i];
-                u += p.part_sh[(int64_t)(q * 2 + 1) * p.Ish + k0 + i];
+        for (int j = 0; j < GU_MAXL; ++j) {
+            const int i = min(tid + D1_THREADS * j, 2 * n32 - 1);
+            *(u32x4 *)(wt + 16 * i) = buf[j];
+        }
+        __syncthreads();
+        const int un = u + G;
+        load(un < n_units ? un : u);                              // next unit in flight (unconditional)
+        const int slot = u / n_rt, r0 = (u % n_rt) * GU_ROWS;
+        float acc_g = 0.f, acc_u = 0.f;
+        // two-stage pipeline over the wave's blocks: the header and index
+        // bytes of the next block are read while this block's codebook
+        // entries are looked up and its MFMAs run
+        // (a wave whose K quarter holds no block, at small H, skips this)
+        if (b0 < b1) {
+            Hdr h0, h1;
+            read_hdr(b0, h0);
+            for (int b = b0;;) {
+                read_hdr(min(b + 1, b1 - 1), h1);
+                block(b, h0, acc_g, acc_u);
+                if (++b >= b1) break;
+                read_hdr(min(b + 1, b1 - 1), h0);
+                block(b, h1, acc_g, acc_u);
+                if (++b >= b1) break;
             }
-            const float h = g / (1.0f + expf(-g)) * u;
+        }
+        if (fc == 0) { red[(wave * 2 + 0) * 16 + fr] = acc_g; red[(wave * 2 + 1) * 16 + fr] = acc_u; }
+        __syncthreads();
+        if (tid < 32) {
+            const int hf = tid >> 4, n = tid & 15;
+            float gg = 0.f, uv = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                gg += red[((hf * 4 + q) * 2 + 0) * 16 + n];
+                uv += red[((hf * 4 + q) * 2 + 1) * 16 + n];
+            }
+            const int r = r0 + 16 * hf + n;
+            const float h = gg / (1.0f + expf(-gg)) * uv;
             uint32_t hi, lo;
             split_bf16(h, hi, lo);
-            hh[i] = (uint16_t)hi;
-            hl[i] = (uint16_t)lo;
-        }
-        __syncthreads();
+            p.h_hi[(int64_t)slot * p.hstride + r] = (uint16_t)hi;
+            p.h_lo[(int64_t)slot * p.hstride + r] = (uint16_t)lo;
+            // the 16 rows of a half are one 16-wide sub-block of down's K: its sum feeds the min term
+            float sum = h;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int k = 32 * (8 * kh + s) + 8 * fc;
-            bf16x8 ah = {}, al = {};
-            if (fr == 0) {
-                ah = *(const bf16x8 *)&hh[k];
-                al = *(const bf16x8 *)&hl[k];
+            for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
+            if (n == 0) p.X[((int64_t)slot * p.nbI + (r >> 8)) * 16 + ((r & 255) >> 4)] = sum;
+        }
+        if (un >= n_units) break;
+        u = un;
+    }
+}
+
+// ============================================================== down
+// Wave w computes output rows 16w.. of the unit's 128 over the whole K, so no
+// reduction between waves is needed.  Each work-group takes a contiguous range
+// of units, so the LDS copy of the activation (one slot's h, or one K part of
+// the shared h) changes rarely.
+__global__ __launch_bounds__(D1_THREADS) void dec1_down_kernel(DecPass p)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+    __shared__ int kid[64];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int fr = lane & 15, fc = lane >> 4;
+    const int H = p.H;
+    const int n_ot = (H + DN_ROWS - 1) / DN_ROWS;
+    const bool shared_role = (int)blockIdx.x < p.dn_sh_wg;
+    const int G = shared_role ? p.dn_sh_wg : p.dn_rt_wg;
+    const int w = shared_role ? (int)blockIdx.x : (int)blockIdx.x - p.dn_sh_wg;
+    const int n_units = shared_role ? n_ot * (p.Ish / DN_KPART) : p.k * n_ot;
+    const int u_begin = (int)(((int64_t)n_units * w) / G), u_end = (int)(((int64_t)n_units * (w + 1)) / G);
+    if (u_begin >= u_end) return;                                  // uniform over the work-group
+
+    if (shared_role) {
+        // ---------------------------------------------- shared expert K parts
+        uint16_t *hh = (uint16_t *)dsm, *hl = hh + DN_KPART;
+        u32x4 wa[16], wb[16];                                      // two buffers in turn
+        auto load = [&](int uu, u32x4 (&W4)[16]) {
+            const int part = uu / n_ot, row = min((uu % n_ot) * DN_ROWS + 16 * wave + fr, H - 1);
+            const uint16_t *rw = p.sd + (int64_t)row * p.Ish + part * DN_KPART + 8 * fc;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) W4[s] = *(const u32x4 *)(rw + 32 * s);
+        };
+        int cur_part = -1;
+        auto unit = [&](int uu, const u32x4 (&W4)[16]) {
+            const int part = uu / n_ot, ot = uu % n_ot;
+            if (part != cur_part) {
+                // this part's slice of the shared h: add the gate/up K parts in
+                // order, then silu(g) * u, split into two bf16 terms
+                __syncthreads();
+                const int k0 = part * DN_KPART;
+                for (int i = tid; i < DN_KPART; i += D1_THREADS) {
+                    float g = 0.f, uv = 0.f;
+#pragma unroll
+                    for (int q = 0; q < SH_KQ; ++q) {
+                        g += p.part_sh[(int64_t)(q * 2 + 0) * p.Ish + k0 + i];
+                        uv += p.part_sh[(int64_t)(q * 2 + 1) * p.Ish + k0 + i];
+                    }
+                    const float h = g / (1.0f + expf(-g)) * uv;
+                    uint32_t hi, lo;
+                    split_bf16(h, hi, lo);
+                    hh[i] = (uint16_t)hi;
+                    hl[i] = (uint16_t)lo;
+                }
+                __syncthreads();
+                cur_part = part;
             }
-            const bf16x8 B = __builtin_bit_cast(bf16x8, bw[s]);
-            acc = mfma16x16x32(ah, B, acc);
-            acc = mfma16x16x32(al, B, acc);
-        }
-    } else {
-        // ---------------------------------------------- routed Q2_K rows
-        pos = min(max(p.offsets[g], 0), p.k - 1);
-        const int nb = p.nbI;
-        const int nbh = (nb + 1) / 2;
-        const int bb0 = kh * nbh, bb1 = min(nb, bb0 + nbh);
-        uint16_t *tab = (uint16_t *)dsm;                  // [16 sc][256 bytes][4]
-        uint16_t *hh = tab + 16 * 256 * 4;                // [nb*256] hi
-        uint16_t *hl = hh + nb * 256;                     // [nb*256] lo
-        uint16_t *xm = hl + nb * 256;                     // [nb][32]
-        const uint8_t *wrow = p.wd + (int64_t)g * p.d_expert_bytes + (int64_t)(row_ok ? row : 0) * p.d_row_bytes;
-        constexpr int MAXB = 4;
-        u32x4 codes[MAXB], scl[MAXB];
-        uint32_t dd[MAXB];
+            f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < MAXB; ++j) {
-            const int b = bb0 + j;
-            if (b < bb1 && row_ok) {
-                const uint8_t *blk = wrow + 84 * b;
-                codes[j] = *(const u32x4 *)(blk + 20 + 16 * fc);
-                scl[j] = *(const u32x4 *)(blk + 4);
-                dd[j] = *(const uint32_t *)blk;
-            } else {
-                codes[j] = u32x4{0, 0, 0, 0};
-                scl[j] = u32x4{0, 0, 0, 0};
-                dd[j] = 0;
+            for (int s = 0; s < 16; ++s) {
+                const bf16x8 a = act_rows<true>(hh, hl, 32 * s + 8 * fc, fr);
+                P = mfma16x16x32(a, __builtin_bit_cast(bf16x8, W4[s]), P);
             }
+            const int row = ot * DN_ROWS + 16 * wave + fr;
+            if (fc == 0 && row < H) p.O_sh[(int64_t)part * H + row] = P[0] + P[1];
+        };
+        load(u_begin, wa);
+        for (int u = u_begin;;) {                                  // unconditional prefetch, as above
+            load(min(u + 1, u_end - 1), wb);
+            unit(u, wa);
+            if (++u >= u_end) break;
+            load(min(u + 1, u_end - 1), wa);
+            unit(u, wb);
+            if (++u >= u_end) break;
         }
-        for (int i = tid; i < 16 * 256; i += 512) {
-            const int sc = i >> 8, byte = i & 255;
-            uint32_t v[4];
+        return;
+    }
+
+    // -------------------------------------------------- routed Q2_K rows
+    const int nb = p.nbI;
+    // every slot's h (hi, lo) and min-term sums are staged once, so no load
+    // of the unit loop has to wait behind a staging load
+    uint16_t *tab = (uint16_t *)dsm;                               // [16 sc][256 bytes][4]
+    uint16_t *hh = tab + 16 * 256 * 4;                             // [k][nb*256] hi
+    uint16_t *hl = hh + p.k * nb * 256;                            // [k][nb*256] lo
+    float *xm = (float *)(hl + p.k * nb * 256);                    // [k][nb][16] sub-block sums of h
+    if (tid < p.k) kid[tid] = clamp_expert(p.topk_idx[tid], p.E);
+    __syncthreads();
+    // two register buffers in turn, per block: this lane's 16 code bytes, the
+    // sc|m bytes of its four sub-blocks, and d|dmin.  While one unit is
+    // computed, the next is in flight.
+    u32x4 ca[DN_MAXB], cb[DN_MAXB];
+    uint32_t sa[DN_MAXB], sb[DN_MAXB], da[DN_MAXB], db[DN_MAXB];
+    // unconditional loads (rows past H and blocks past nb re-read valid bytes
+    // that are never used): a load under a branch makes the compiler wait for it
+    auto load = [&](int uu, u32x4 (&C4)[DN_MAXB], uint32_t (&S4)[DN_MAXB], uint32_t (&D4)[DN_MAXB]) {
+        const int slot = uu / n_ot, row = min((uu % n_ot) * DN_ROWS + 16 * wave + fr, H - 1);
+        const uint8_t *wrow = p.wd + (int64_t)kid[slot] * p.d_expert_bytes + (int64_t)row * p.d_row_bytes;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] = f32_to_bf16_exact((float)(sc * ((byte >> (2 * t)) & 3)));
-            *(uint2 *)&tab[4 * i] = uint2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
+        for (int b = 0; b < DN_MAXB; ++b) {
+            const uint8_t *blk = wrow + 84 * min(b, nb - 1);
+            C4[b] = *(const u32x4 *)(blk + 20 + 16 * fc);
+            S4[b] = *(const uint32_t *)(blk + 4 + 4 * fc);
+            D4[b] = *(const uint32_t *)blk;
         }
-        for (int i = tid; i < nb * 32; i += 512) {
-            *(u32x4 *)&hh[8 * i] = *(const u32x4 *)(p.h_hi + pos * p.hstride + 8 * i);
-            *(u32x4 *)&hl[8 * i] = *(const u32x4 *)(p.h_lo + pos * p.hstride + 8 * i);
-            xm[i] = p.X[pos * nb * 32 + i];
-        }
-        __syncthreads();
+    };
+    const uint16_t *arow = (fr & 1) ? hl : hh;                      // this lane's A row (rows 0, 1 used)
+    auto unit = [&](int uu, const u32x4 (&C4)[DN_MAXB], const uint32_t (&S4)[DN_MAXB], const uint32_t (&D4)[DN_MAXB]) {
+        const int slot = uu / n_ot, ot = uu % n_ot;
+        const uint16_t *sa_row = arow + slot * nb * 256;
+        const float *sx = xm + slot * nb * 16;
+        float acc = 0.f, accm = 0.f;
+        // every block consumes its registers; blocks past nb (re-reads of the
+        // last block) read in-range LDS and add zero
 #pragma unroll
-        for (int j = 0; j < MAXB; ++j) {
-            const int b = bb0 + j;
-            if (b >= bb1) break;
+        for (int bl = 0; bl < DN_MAXB; ++bl) {
+            const int b = min(bl, nb - 1);
             // lane (fr, fc) owns K positions [64 fc, 64 fc + 64) of block b, i.e.
             // sub-blocks 4fc..4fc+3 and code bytes 16fc..16fc+15
-            const uint32_t cw[4] = {codes[j].x, codes[j].y, codes[j].z, codes[j].w};
-            const uint32_t sw[4] = {scl[j].x, scl[j].y, scl[j].z, scl[j].w};
-            const uint32_t scw = sw[fc];
-            f32x4 P = {0.f, 0.f, 0.f, 0.f};
+            const uint32_t cw[4] = {C4[bl].x, C4[bl].y, C4[bl].z, C4[bl].w};
+            const uint32_t scw = S4[bl];
+            // all LDS reads of the block (A rows, 16 table entries) go out before its MFMAs
+            bf16x8 a[8];
+            act_block<true>(sa_row, 256 * b + 64 * fc, 8, fr, a);
+            u32x4 Bq[8];
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const int sc = (scw >> (8 * (m >> 1))) & 15;
@@ -400,97 +443,186 @@ __global__ __launch_bounds__(512) void dec_down_kernel(DecPass p)
                 const int by0 = (word >> (16 * (m & 1))) & 255, by1 = (word >> (16 * (m & 1) + 8)) & 255;
                 const uint2 t0 = *(const uint2 *)&tab[4 * (sc * 256 + by0)];
                 const uint2 t1 = *(const uint2 *)&tab[4 * (sc * 256 + by1)];
-                const bf16x8 B = __builtin_bit_cast(bf16x8, u32x4{t0.x, t0.y, t1.x, t1.y});
-                const int k = 256 * b + 64 * fc + 8 * m;
-                bf16x8 ah = {}, al = {};
-                if (fr == 0) {
-                    ah = *(const bf16x8 *)&hh[k];
-                    al = *(const bf16x8 *)&hl[k];
-                }
-                P = mfma16x16x32(ah, B, P);
-                P = mfma16x16x32(al, B, P);
+                Bq[m] = u32x4{t0.x, t0.y, t1.x, t1.y};
             }
-            // min term over the block's 16 sub-blocks: k-slots 0..15 carry X_hi
-            // with m_0..15, slots 16..31 carry X_lo with the same m
-            uint32_t mv[4];
-            {
-                const uint32_t w0 = sw[2 * (fc & 1)], w1 = sw[2 * (fc & 1) + 1];
+            f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const uint32_t w = q ? w1 : w0;
-                    mv[2 * q] = f32_to_bf16_exact((float)((w >> 4) & 15)) |
-                                (f32_to_bf16_exact((float)((w >> 12) & 15)) << 16);
-                    mv[2 * q + 1] = f32_to_bf16_exact((float)((w >> 20) & 15)) |
-                                    (f32_to_bf16_exact((float)((w >> 28) & 15)) << 16);
-                }
-            }
-            bf16x8 xa = {};
-            if (fr == 0) xa = *(const bf16x8 *)&xm[b * 32 + 8 * fc];
-            const f32x4 Mt = mfma16x16x32(xa, __builtin_bit_cast(bf16x8, u32x4{mv[0], mv[1], mv[2], mv[3]}),
-                                          f32x4{0.f, 0.f, 0.f, 0.f});
-            // this lane's D column is its own feature `row`, whose d and dmin it read
-            const float d = f16_bits_to_f32(dd[j] & 0xffffu), dmin = f16_bits_to_f32(dd[j] >> 16);
-            acc += d * P - dmin * Mt;
+            for (int m = 0; m < 8; ++m) P = mfma16x16x32(a[m], __builtin_bit_cast(bf16x8, Bq[m]), P);
+            // min term of this lane's four sub-blocks: sum_j m_j X_j (fp32)
+            const f32x4 xv = *(const f32x4 *)&sx[b * 16 + 4 * fc];
+            float mt = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mt += (float)((scw >> (8 * i + 4)) & 15) * xv[i];
+            // column fr of D is this lane's own feature, whose d and dmin it read;
+            // rows 0 and 1 (h hi and lo) sit in lanes with fc == 0
+            const float d = f16_bits_to_f32(D4[bl] & 0xffffu), dmin = f16_bits_to_f32(D4[bl] >> 16);
+            acc += bl < nb ? d * (P[0] + P[1]) : 0.f;
+            accm += bl < nb ? dmin * mt : 0.f;
         }
+        // the four lanes of a feature hold its min term in four parts
+        accm += __shfl_xor(accm, 16, 64);
+        accm += __shfl_xor(accm, 32, 64);
+        const int row = ot * DN_ROWS + 16 * wave + fr;
+        if (fc == 0 && row < H) p.O[(int64_t)slot * H + row] = acc - accm;
+    };
+    // the first unit's weights go out first; the h staging and the table build
+    // overlap with them (the staging loads are waited for on their own before
+    // the barrier, which also covers the weight loads issued ahead of them)
+    // h staging loads go out first (into registers), then the first unit's
+    // weights; the LDS stores then wait for the staging loads only
+    u32x4 shh[DN_STAGE], shl[DN_STAGE];
+    float sxm[DN_STAGE];
+    const int nst = p.k * nb * 32;
+#pragma unroll
+    for (int j = 0; j < DN_STAGE; ++j) {
+        const int i = min(tid + D1_THREADS * j, nst - 1);
+        const int slot = i / (nb * 32), c = i % (nb * 32);
+        shh[j] = *(const u32x4 *)(p.h_hi + (int64_t)slot * p.hstride + 8 * c);
+        shl[j] = *(const u32x4 *)(p.h_lo + (int64_t)slot * p.hstride + 8 * c);
+        sxm[j] = p.X[min(i, p.k * nb * 16 - 1)];
     }
-    // add the two K halves in a fixed order: slot 0 of feature fr is lane fr, v = 0
-    if (kh == 1 && fc == 0) red[rg][fr] = acc[0];
+    load(u_begin, ca, sa, da);
+    for (int i = tid; i < 16 * 256; i += D1_THREADS) {
+        const int sc = i >> 8, byte = i & 255;
+        uint32_t v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = f32_to_bf16_exact((float)(sc * ((byte >> (2 * t)) & 3)));
+        *(uint2 *)&tab[4 * i] = uint2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
+    }
+    // unconditional stores (indices past the end rewrite the last entry with its own value)
+#pragma unroll
+    for (int j = 0; j < DN_STAGE; ++j) {
+        const int i = min(tid + D1_THREADS * j, nst - 1);
+        *(u32x4 *)&hh[8 * i] = shh[j];
+        *(u32x4 *)&hl[8 * i] = shl[j];
+        xm[min(i, p.k * nb * 16 - 1)] = sxm[j];
+    }
     __syncthreads();
-    if (kh == 0 && fc == 0 && row_ok) {
-        const float v = acc[0] + red[rg][fr];
-        if (sh) p.O_sh[(int64_t)part * p.H + row] = v;
-        else p.O[pos * p.H + row] = v;
+    for (int u = u_begin;;) {                                      // unconditional prefetch, as above
+        load(min(u + 1, u_end - 1), cb, sb, db);
+        unit(u, ca, sa, da);
+        if (++u >= u_end) break;
+        load(min(u + 1, u_end - 1), ca, sa, da);
+        unit(u, cb, sb, db);
+        if (++u >= u_end) break;
     }
-
 }
 
 // y = the shared expert's K parts in order, then the routed outputs in top-k order
-__global__ __launch_bounds__(256) void dec_combine_kernel(DecPass p)
+__global__ __launch_bounds__(256) void dec1_combine_kernel(DecPass p)
 {
     const int n = blockIdx.x * 256 + threadIdx.x;
     if (n >= p.H) return;
-    const int KPD = p.Ish > 0 ? p.Ish / DD_KPART : 0;
+    const int KPD = p.Ish / DN_KPART;
     float y = 0.f;
     for (int q = 0; q < KPD; ++q) y += p.O_sh[(int64_t)q * p.H + n];
-    for (int j = 0; j < p.k; ++j) {
-        const int ps = min(max(p.inv[j], 0), p.k - 1);
-        y += p.topk_w[j] * p.O[(int64_t)ps * p.H + n];
-    }
+    for (int j = 0; j < p.k; ++j) y += p.topk_w[j] * p.O[(int64_t)j * p.H + n];
     p.y[n] = y;
 }
 
 // ============================================================== launchers
-size_t dec_single_lds_gateup(int H, int gu_row_bytes) { return 32 * (size_t)gu_row_bytes + 2 * (size_t)H + 4096; }
+namespace {
 
-bool dec_single_ok(int T, int H, int I, int Ish, int k, int gu_row_bytes)
+int cu_count()
 {
-    return T == 1 && k <= 64 && H % 512 == 0 && (Ish == 0 || Ish % DD_KPART == 0) && I % 256 == 0 &&
-           I / 256 <= 8 && gu_row_bytes * 2 <= 2560 && H / DG_KQ / 32 <= 8 * 9 &&
-           dec_single_lds_gateup(H, gu_row_bytes) <= 64 * 1024;
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+        n = 256;
+    return n;
+}
+
+size_t lds_gateup(int H, int gu_row_bytes, bool xf32)
+{
+    return (size_t)(xf32 ? 4 : 2) * H + 256 * sizeof(float) + 256 * CB_COPIES * 16 + 2 * GU_ROWS * (size_t)gu_row_bytes;
+}
+
+size_t lds_down(int nbI, int k) { return 16 * 256 * 4 * 2 + (size_t)k * (2 * (size_t)nbI * 256 * 2 + (size_t)nbI * 32 * 2); }
+
+// Resident work-groups per CU for a kernel at a dynamic LDS size; also lifts
+// the kernel's dynamic LDS limit to that size.  Cached per kernel.
+template <typename K>
+int resident(K kernel, size_t lds, std::atomic<uint64_t> &cache)
+{
+    const uint64_t c = cache.load(std::memory_order_relaxed);
+    if (c && (c >> 32) == lds) return (int)(c & 0xffffffffu);
+    (void)hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, D1_THREADS, lds) != hipSuccess || n < 1) n = 1;
+    cache.store(((uint64_t)lds << 32) | (uint32_t)n, std::memory_order_relaxed);
+    return n;
+}
+
+std::atomic<uint64_t> occ_gu_bf16{0}, occ_gu_f32{0}, occ_dn{0};
+
+// Split G work-groups between two roles with n_a units of cost c_a and n_b
+// units of cost c_b, minimising the larger per-work-group load.
+void split_roles(int n_a, double c_a, int n_b, double c_b, int G, int &g_a, int &g_b)
+{
+    if (n_a == 0 || G < 2) { g_a = 0; g_b = std::max(1, std::min(n_b, G)); return; }
+    if (n_b == 0) { g_a = std::min(n_a, G); g_b = 0; return; }
+    double best = 1e300;
+    g_a = 1;
+    for (int a = 1; a < G; ++a) {
+        const double la = ((n_a + a - 1) / a) * c_a, lb = ((n_b + (G - a) - 1) / (G - a)) * c_b;
+        const double l = std::max(la, lb);
+        if (l < best) { best = l; g_a = a; }
+    }
+    g_b = G - g_a;
+    g_a = std::min(g_a, n_a);
+    g_b = std::min(g_b, n_b);
+}
+
+// Time per byte of a routed unit relative to a bf16 shared-expert unit, as
+// measured per work-group on the MI355X: a codebook unit is bound by its LDS
+// table reads (16 bytes per 1.19 bytes of weights), a Q2_K unit by its LDS
+// table reads and VALU work.  The role split gives each role work in
+// proportion to these costs.
+constexpr double CB2_COST = 3.1;
+constexpr double Q2K_COST = 1.55;
+
+}  // namespace
+
+bool dec_single_ok(int T, int H, int I, int Ish, int k, int gu_row_bytes, bool x_f32)
+{
+    return T == 1 && k <= 64 && H % 512 == 0 && (Ish == 0 || Ish % DN_KPART == 0) && I % 256 == 0 &&
+           I / 256 <= DN_MAXB && k * (I / 256) * 32 <= D1_THREADS * DN_STAGE && 4 * gu_row_bytes <= D1_THREADS * GU_MAXL && H / SH_KQ / 32 <= 8 * SH_MAXS &&
+           lds_gateup(H, gu_row_bytes, x_f32) <= LDS_MAX && lds_down(I / 256, k) <= LDS_MAX;
+}
+
+void dec_plan(DecPass &p)
+{
+    const int ncu = cu_count();
+    const size_t lgu = lds_gateup(p.H, p.gu_row_bytes, p.x_f32);
+    const int occ_gu = p.x_f32 ? resident(dec1_gateup_kernel<true>, lgu, occ_gu_f32)
+                               : resident(dec1_gateup_kernel<false>, lgu, occ_gu_bf16);
+    const int occ_d = resident(dec1_down_kernel, lds_down(p.nbI, p.k), occ_dn);
+    split_roles((p.Ish / 16) * SH_KQ, 16.0 * (p.H / SH_KQ) * 2 * 2, p.k * (p.I / GU_ROWS),
+                CB2_COST * 2.0 * GU_ROWS * p.gu_row_bytes, occ_gu * ncu, p.gu_sh_wg, p.gu_rt_wg);
+    const int n_ot = (p.H + DN_ROWS - 1) / DN_ROWS;
+    split_roles(n_ot * (p.Ish / DN_KPART), (double)DN_ROWS * DN_KPART * 2, p.k * n_ot,
+                Q2K_COST * DN_ROWS * p.d_row_bytes, occ_d * ncu, p.dn_sh_wg, p.dn_rt_wg);
 }
 
 hipError_t launch_dec_gateup(const DecPass &p, hipStream_t s)
 {
-    const int grid = (p.Ish > 0 ? (p.Ish / 16) * DG_KQ : 0) + p.k * (p.I / 16);
-    const size_t lds = dec_single_lds_gateup(p.H, p.gu_row_bytes);
-    if (p.x_f32) dec_gateup_kernel<true><<<grid, 512, lds, s>>>(p);
-    else dec_gateup_kernel<false><<<grid, 512, lds, s>>>(p);
+    const int grid = p.gu_sh_wg + p.gu_rt_wg;
+    const size_t lds = lds_gateup(p.H, p.gu_row_bytes, p.x_f32);
+    if (p.x_f32) dec1_gateup_kernel<true><<<grid, D1_THREADS, lds, s>>>(p);
+    else dec1_gateup_kernel<false><<<grid, D1_THREADS, lds, s>>>(p);
     return hipGetLastError();
 }
 
 hipError_t launch_dec_down(const DecPass &p, hipStream_t s)
 {
-    const int n_ot = (p.H + DD_ROWS - 1) / DD_ROWS;
-    const int KPD = p.Ish > 0 ? p.Ish / DD_KPART : 0;
-    const int grid = n_ot * KPD + p.k * n_ot;
-    const size_t lds = 16 * 256 * 4 * 2 + 2 * (size_t)p.nbI * 256 * 2 + (size_t)p.nbI * 32 * 2;
-    dec_down_kernel<<<grid, 512, lds, s>>>(p);
+    const int grid = p.dn_sh_wg + p.dn_rt_wg;
+    dec1_down_kernel<<<grid, D1_THREADS, lds_down(p.nbI, p.k), s>>>(p);
     return hipGetLastError();
 }
 
 hipError_t launch_dec_combine(const DecPass &p, hipStream_t s)
 {
-    dec_combine_kernel<<<(p.H + 255) / 256, 256, 0, s>>>(p);
+    dec1_combine_kernel<<<(p.H + 255) / 256, 256, 0, s>>>(p);
     return hipGetLastError();
 }
 

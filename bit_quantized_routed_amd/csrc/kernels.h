@@ -69,15 +69,19 @@ struct DecPass {
     const int8_t *codebook;
     const void *x;
     int x_f32;
-    uint16_t *h_hi, *h_lo;                       // [k+1][hstride]
+    uint16_t *h_hi, *h_lo;                       // [k][hstride] by top-k slot
     int hstride;
-    uint16_t *X;                                 // [k][nbI][32] Q2_K min-term sums (hi 16, lo 16)
-    float *part_sh;                              // [4][2][Ish] shared gate/up partial sums (K quarters)
-    float *O;                                    // [k][H]
+    float *X;                                    // [k][nbI][16] Q2_K min-term sums of h per 16-wide sub-block
+    float *part_sh;                              // [DEC_SH_KQ][2][Ish] shared gate/up partial sums (K parts)
+    float *O;                                    // [k][H] by top-k slot
     float *O_sh;                                 // [Ish/512][H]
     float *y;                                    // [H]
+    int gu_sh_wg, gu_rt_wg;                      // gate/up work-groups: shared, routed role
+    int dn_sh_wg, dn_rt_wg;                      // down work-groups: shared, routed role
 };
-bool dec_single_ok(int T, int H, int I, int Ish, int k, int gu_row_bytes);
+constexpr int DEC_SH_KQ = 8;                     // K parts of the single-token shared gate/up (part_sh)
+bool dec_single_ok(int T, int H, int I, int Ish, int k, int gu_row_bytes, bool x_f32);
+void dec_plan(DecPass &p);                       // fills the work-group split
 hipError_t launch_dec_gateup(const DecPass &p, hipStream_t s);
 hipError_t launch_dec_down(const DecPass &p, hipStream_t s);
 hipError_t launch_dec_combine(const DecPass &p, hipStream_t s);

@@ -513,20 +513,114 @@ __device__ void group_small(const int32_t *sidx, int T, int E, int k, int32_t *o
     }
 }
 
-// T == 1: selection and grouping in one work-group
-__global__ __launch_bounds__(256) void route_select_one(const double *part, const float *bias, int E, int k, int NC,
-                                                        int32_t *topk_idx, float *topk_w, int32_t *offsets,
-                                                        int32_t *perm, int32_t *inv)
+// One step of a wave-wide arg-max over (logit descending, expert ascending):
+// take the partner lane's candidate (DPP permutation CTRL) if it is better.
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(double &bv, int &be)
 {
-    __shared__ double lg[1024];
-    __shared__ double sel_l[64];
-    __shared__ int32_t sel_e[64];
-    __shared__ uint32_t mask[2 * 1024];
-    __shared__ int32_t cnt[1024];
-    token_logits(part, bias, 1, E, NC, 0, lg);
-    rank_topk(lg, E, k, topk_idx, topk_w, sel_e, sel_l);
-    __syncthreads();
-    group_small(sel_e, 1, E, k, offsets, perm, inv, mask, cnt);
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(bv), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(bv), CTRL, 0xF, 0xF, false);
+    const int oe = __builtin_amdgcn_mov_dpp(be, CTRL, 0xF, 0xF, false);
+    const double ov = __hiloint2double(hi, lo);
+    if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+}
+
+// Wave-wide arg-max: the four DPP steps (swap neighbours, swap pairs, mirror
+// the half-rows, mirror the rows) leave each 16-lane row's best in every lane
+// of the row; the four row results are then compared in lane order.
+__device__ __forceinline__ void wave_argmax(double &bv, int &be)
+{
+    argmax_dpp<0xB1>(bv, be);       // quad_perm [1,0,3,2]
+    argmax_dpp<0x4E>(bv, be);       // quad_perm [2,3,0,1]
+    argmax_dpp<0x141>(bv, be);      // row_half_mirror
+    argmax_dpp<0x140>(bv, be);      // row_mirror
+    double cv = 0.0;
+    int ce = 0x7fffffff;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int lo = __builtin_amdgcn_readlane(__double2loint(bv), 16 * r);
+        const int hi = __builtin_amdgcn_readlane(__double2hiint(bv), 16 * r);
+        const int re = __builtin_amdgcn_readlane(be, 16 * r);
+        const double rv = __hiloint2double(hi, lo);
+        if (ce == 0x7fffffff || rv > cv || (rv == cv && re < ce)) { cv = rv; ce = re; }
+    }
+    bv = cv;
+    be = ce;
+}
+
+// T == 1: one wave selects and groups.  Lane l holds experts l, l+64, ...;
+// k rounds of a wave-wide arg-max over (logit descending, expert ascending)
+// pick k distinct experts in top-k order.  The grouping of one token is the
+// selection sorted by expert id: offsets come from ballots of the taken
+// flags, and the position of slot j is the number of selected ids below its
+// own.  No LDS, no barriers.
+__global__ __launch_bounds__(64) void route_select_one(const double *part, const float *bias, int E, int k, int NC,
+                                                       int32_t *topk_idx, float *topk_w, int32_t *offsets,
+                                                       int32_t *perm, int32_t *inv)
+{
+    constexpr int MAXPL = 16;                     // E <= 1024
+    const int lane = threadIdx.x;
+    double v[MAXPL];
+#pragma unroll
+    for (int i = 0; i < MAXPL; ++i) {
+        const int e = lane + 64 * i;
+        double s = -INFINITY;
+        if (64 * i < E && e < E) {
+            // all chunk loads go out together (NC <= 4), then add in chunk order
+            double c4[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) c4[c] = c < NC ? part[(size_t)c * E + e] : 0.0;
+            const double bv = bias ? (double)bias[e] : 0.0;
+            s = c4[0];
+#pragma unroll
+            for (int c = 1; c < 4; ++c) if (c < NC) s += c4[c];
+            if (bias) s += bv;
+            if (s != s) s = -INFINITY;            // NaN ranks below every number
+        }
+        v[i] = s;
+    }
+    uint32_t taken = 0;
+    int my_e = 0;
+    double my_l = 0.0;
+    for (int j = 0; j < k; ++j) {
+        double bv = -INFINITY;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < MAXPL; ++i) {
+            if (64 * i >= E) break;
+            const int e = lane + 64 * i;
+            // e grows with i, so a strict '>' keeps the lowest expert among equals
+            if (e < E && !((taken >> i) & 1u) && (be == 0x7fffffff || v[i] > bv)) { bv = v[i]; be = e; }
+        }
+        wave_argmax(bv, be);
+        if ((be & 63) == lane && be < E) taken |= 1u << (be >> 6);
+        if (lane == j) { my_e = be; my_l = bv; }
+    }
+    // weights: sigmoid of the selected logits over their sum (fp64)
+    double sg = lane < k ? 1.0 / (1.0 + exp(-my_l)) : 0.0;
+    double ssum = sg;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ssum += __shfl_xor(ssum, off, 64);
+    // grouping
+    int below = 0;
+    for (int i = 0; i < k; ++i) below += __shfl(my_e, i, 64) < my_e;
+    if (lane < k) {
+        topk_idx[lane] = my_e;
+        topk_w[lane] = (float)(sg / ssum);
+        perm[below] = lane;
+        inv[lane] = below;
+    }
+    int base = 0;
+    const uint64_t lower = lane ? ((1ull << lane) - 1ull) : 0ull;
+#pragma unroll
+    for (int i = 0; i < MAXPL; ++i) {
+        if (64 * i >= E) break;
+        const uint64_t m = __ballot((taken >> i) & 1u);
+        const int e = lane + 64 * i;
+        if (e < E) offsets[e] = base + __popcll(m & lower);
+        base += __popcll(m);
+    }
+    if (lane == 0) offsets[E] = base;
 }
 
 // 1 < T <= 64: one work-group per token selects ...
@@ -583,7 +677,7 @@ void launch_route_select(const double *part, const float *bias, int T, int H, in
 {
     const int NC = route_decode_chunks(T, H);
     if (T == 1) {
-        route_select_one<<<1, 256, 0, s>>>(part, bias, E, k, NC, topk_idx, topk_w, offsets, perm, inv);
+        route_select_one<<<1, 64, 0, s>>>(part, bias, E, k, NC, topk_idx, topk_w, offsets, perm, inv);
     } else {
         route_select_tok<<<T, 256, 0, s>>>(part, bias, T, E, k, NC, topk_idx, topk_w);
         route_group_small<<<1, 256, 0, s>>>(topk_idx, T, E, k, offsets, perm, inv);
