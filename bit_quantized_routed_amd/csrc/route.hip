@@ -113,6 +113,76 @@ __global__ __launch_bounds__(256) void route_logits_tiled(const void *x, const f
         }
 }
 
+// Large T on the fp64 matrix cores: a 32-token x 64-expert tile per
+// work-group, H staged through LDS in chunks of 32 as fp64 (x and W_r widened
+// exactly); each wave owns 16 experts and both 16-token halves, and
+// accumulates with v_mfma_f64_16x16x4f64 (fp64 products and sums).  Rows of
+// the LDS tiles are padded to 33 doubles so the 16 lanes of one read hit 16
+// different bank pairs.  Needs H % 32 == 0.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+template <bool XBF16>
+__global__ __launch_bounds__(256) void route_logits_mfma(const void *x, const float *wr, const float *bias, int T,
+                                                          int H, int E, double *logits)
+{
+    constexpr int TT = 32, TE = 64, HC = 32, LD = HC + 1;
+    __shared__ double xs[TT][LD];
+    __shared__ double ws[TE][LD];
+    const int t0 = blockIdx.x * TT, e0 = blockIdx.y * TE;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int fr = lane & 15, fk = lane >> 4;
+    f64x4 acc[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
+    // staging maps: x -> 4 elements per thread (rows 0..31), W -> 8 per thread (rows 0..63)
+    const int xr = tid >> 3, xk = (tid & 7) * 4;
+    const int wrow = tid >> 2, wk = (tid & 3) * 8;
+    const bool xok = t0 + xr < T, wok = e0 + wrow < E;
+    for (int h0 = 0; h0 < H; h0 += HC) {
+        double xv[4], wv[8];
+        if (XBF16) {
+            uint2 u = xok ? *(const uint2 *)((const uint16_t *)x + (size_t)(t0 + xr) * H + h0 + xk) : uint2{0, 0};
+            xv[0] = bf16_bits_to_f32(u.x & 0xffffu); xv[1] = bf16_bits_to_f32(u.x >> 16);
+            xv[2] = bf16_bits_to_f32(u.y & 0xffffu); xv[3] = bf16_bits_to_f32(u.y >> 16);
+        } else {
+            const f32x4 f = xok ? *(const f32x4 *)((const float *)x + (size_t)(t0 + xr) * H + h0 + xk)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+            xv[0] = f.x; xv[1] = f.y; xv[2] = f.z; xv[3] = f.w;
+        }
+        {
+            const f32x4 a = wok ? *(const f32x4 *)&wr[(size_t)(e0 + wrow) * H + h0 + wk] : f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 b = wok ? *(const f32x4 *)&wr[(size_t)(e0 + wrow) * H + h0 + wk + 4] : f32x4{0.f, 0.f, 0.f, 0.f};
+            wv[0] = a.x; wv[1] = a.y; wv[2] = a.z; wv[3] = a.w; wv[4] = b.x; wv[5] = b.y; wv[6] = b.z; wv[7] = b.w;
+        }
+        __syncthreads();                                   // previous chunk consumed
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xs[xr][xk + i] = xv[i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ws[wrow][wk + i] = wv[i];
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < HC / 4; ++kk) {
+            // A: lane (fr, fk) holds x[token fr][h 4kk + fk]; B: W_r[expert fr][h 4kk + fk]
+            const double b = ws[wave * 16 + fr][4 * kk + fk];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[mt * 16 + fr][4 * kk + fk], b, acc[mt], 0, 0, 0);
+        }
+    }
+    // D: lane (fr, fk) holds rows fk + 4i (tokens) of column fr (expert); the
+    // fp64 16x16x4 result interleaves rows across lane groups, unlike the
+    // fp32-output shapes
+    const int e = e0 + wave * 16 + fr;
+    if (e < E) {
+        const double bv = bias ? (double)bias[e] : 0.0;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = t0 + mt * 16 + fk + 4 * i;
+                if (t < T) logits[(size_t)t * E + e] = acc[mt][i] + bv;
+            }
+    }
+}
+
 // ---------------------------------------------------------------- top-k
 // One wave selects the k best experts of one token: k rounds of a wave-wide
 // arg-max over (logit desc, expert asc).  Each lane holds experts lane+64*i.
@@ -287,6 +357,10 @@ void launch_route_logits(const void *x, bool xbf16, const float *wr, const float
         dim3 grid(E, (T + 7) / 8);
         if (xbf16) route_logits_small<true><<<grid, 64, 0, s>>>(x, wr, bias, T, H, E, logits);
         else route_logits_small<false><<<grid, 64, 0, s>>>(x, wr, bias, T, H, E, logits);
+    } else if (H % 32 == 0) {
+        dim3 grid((T + 31) / 32, (E + 63) / 64);
+        if (xbf16) route_logits_mfma<true><<<grid, 256, 0, s>>>(x, wr, bias, T, H, E, logits);
+        else route_logits_mfma<false><<<grid, 256, 0, s>>>(x, wr, bias, T, H, E, logits);
     } else {
         dim3 grid((T + 63) / 64, (E + 63) / 64);
         if (xbf16) route_logits_tiled<true><<<grid, 256, 0, s>>>(x, wr, bias, T, H, E, logits);
