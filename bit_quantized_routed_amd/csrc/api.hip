@@ -245,12 +245,6 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
         return MOE_OK;
     }
 
-    if (!pr.before("ffn_schedule")) return hip_fail(hipGetLastError(), "event record");
-    launch_ffn_schedule(offsets, T, k, E, has_sh, BM, w.sched, s);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "ffn_schedule launch");
-    if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
-
     FfnPass up{};
     up.T = T; up.k = k; up.E = E;
     up.offsets = offsets; up.perm = perm;
@@ -275,15 +269,24 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
     dn.act = w.h; dn.act_f32 = prefill ? 0 : 1; dn.act_by_token = 0; dn.act_stride = w.hstride;
     dn.out = w.O; dn.out_f32 = 1; dn.out_stride = H;
 
+    // prefill: in-register dequantization kernels when every K is a multiple of 256
+    const bool np = prefill && np_prefill_ok(up) && np_prefill_ok(dn);
+    const int sched_bm = np ? NP_BM : BM;
+    if (!pr.before("ffn_schedule")) return hip_fail(hipGetLastError(), "event record");
+    launch_ffn_schedule(offsets, T, k, E, has_sh, sched_bm, w.sched, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "ffn_schedule launch");
+    if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+
     const char *nm_up = prefill ? "ffn_prefill_gateup" : "ffn_decode_gateup";
     const char *nm_dn = prefill ? "ffn_prefill_down" : "ffn_decode_down";
     if (!pr.before(nm_up)) return hip_fail(hipGetLastError(), "event record");
-    e = prefill ? launch_ffn_prefill(up, true, s) : launch_ffn_decode(up, true, s);
+    e = np ? launch_np_prefill(up, true, s) : prefill ? launch_ffn_prefill(up, true, s) : launch_ffn_decode(up, true, s);
     if (e != hipSuccess) return hip_fail(e, nm_up);
     if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
 
     if (!pr.before(nm_dn)) return hip_fail(hipGetLastError(), "event record");
-    e = prefill ? launch_ffn_prefill(dn, false, s) : launch_ffn_decode(dn, false, s);
+    e = np ? launch_np_prefill(dn, false, s) : prefill ? launch_ffn_prefill(dn, false, s) : launch_ffn_decode(dn, false, s);
     if (e != hipSuccess) return hip_fail(e, nm_dn);
     if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
 

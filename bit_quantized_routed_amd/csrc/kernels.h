@@ -97,4 +97,10 @@ void launch_route_select(const double *part, const float *bias, int T, int H, in
 constexpr int DEC_BM = 16, DEC_BN = 16;
 constexpr int PRE_BM = 64, PRE_BN = 64;
 
+// prefill grouped GEMMs with in-register dequantization (K multiples of 256,
+// bf16 activations); tiles of NP_BM rows
+constexpr int NP_BM = 96;
+bool np_prefill_ok(const FfnPass &p);
+hipError_t launch_np_prefill(const FfnPass &p, bool gateup, hipStream_t s);
+
 }  // namespace moe

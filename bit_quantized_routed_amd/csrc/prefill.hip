@@ -1,0 +1,717 @@
+// Prefill expert FFN on gfx950: grouped GEMMs over the token rows routed to
+// each expert, with the 2-bit (or 4-bit) routed weights dequantized in
+// registers on their way into the matrix cores.
+//
+// Only the routed experts are quantized (gate/up in the 2-bit codebook
+// format, down in Q2_K, Q4_K as the wide variant); the shared expert stays
+// bf16 ("DwarfStar" README, section on model weights; deep-dive article,
+// section 3.4.3).  Prefill is the compute-bound side of the layer, so the
+// weights are expanded once per work-group straight into MFMA operands and
+// never pass through LDS as bf16.
+//
+// Tiling.  A tile is up to 96 rows (positions) of one group (expert, or the
+// shared expert as group E); a work-group of 8 waves owns one tile and one
+// slice of output columns.  Every wave covers all rows of the tile and its own
+// 64 GEMM columns (gate/up: 32 gate + the 32 matching up columns; down: 64
+// output features), so each weight is dequantized by exactly one lane.  The
+// activations of the tile are staged through LDS in half-blocks of 128 K,
+// double-buffered; row fragments beyond the tile's valid rows are skipped.
+//
+// K order.  Within each 256-weight block, MFMA step s (0..7) gives the lanes
+// of column group fc (0..3) the 8-weight group 8*fc + s, so each lane walks
+// 64 consecutive weights of its row across the block; the activations are
+// read with the same permutation, which leaves every dot product unchanged.
+//
+// Dequantization into bf16 operands (the weights are rounded to bf16, RNE):
+//   CB2   w = d*s_j*C, C in {-3,-1,1,3}: a 4-value pool {+-d s_j, +-3 d s_j}
+//         per lane and sub-block, and per-codeword byte selectors (a 256-entry
+//         LDS table) pick each packed pair with one v_perm.
+//   Q2_K  w = d*sc_j*q - dmin*m_j, q in 0..3: the same scheme with the pool of
+//         the four levels and selectors indexed by the code byte.
+//   Q4_K  16 levels: byte -> fp32 convert, one fma and a packed bf16 convert.
+// Work-groups are mapped to tiles XCD by XCD, so all column slices of a tile
+// (which share its activations) run on the same XCD and its L2.
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int NP_THREADS = 512;
+constexpr int NP_MF = NP_BM / 16;                  // row fragments per tile
+static_assert(NP_MF == 6, "np_dispatch instantiates 1..6 row fragments");
+constexpr int NP_COPIES = 8;                       // selector-table copies (bank spread)
+constexpr int NP_TAB_CB2 = 256 * NP_COPIES * 16;   // bytes
+constexpr int NP_TAB_Q2K = 256 * NP_COPIES * 8;
+
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{lo, hi}, bf16x2v));
+}
+
+// bytes of {hi:lo} picked by the four selector bytes (0..3: lo, 4..7: hi)
+__device__ __forceinline__ uint32_t vperm(uint32_t hi, uint32_t lo, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ float ubyte(uint32_t v, int i) { return (float)((v >> (8 * i)) & 0xffu); }
+
+struct NpTile {
+    int g, row0, nvalid, Ng, Kg, n0;
+    bool sh;
+};
+
+// Work-group -> (tile, column slice).  Work-groups are dispatched to the 8
+// XCDs round-robin; tile tau goes to XCD tau % 8 and its S slices run there
+// back to back.  Returns false (uniformly) when the work-group has no work.
+__device__ __forceinline__ bool np_tile(const FfnPass &p, int S, int wg_cols, NpTile &t)
+{
+    const int f = blockIdx.x, q = f >> 3;
+    const int tau = (q / S) * 8 + (f & 7), slice = q % S;
+    if (tau >= p.sched[0]) return false;
+    t.g = p.sched[1 + 2 * tau];
+    const int m0 = p.sched[2 + 2 * tau];
+    t.sh = t.g == p.E;
+    t.Ng = t.sh ? p.Nsh : p.N;
+    t.Kg = t.sh ? p.Ksh : p.K;
+    t.n0 = slice * wg_cols;
+    if (t.n0 >= t.Ng) return false;
+    const int Tk = p.T * p.k;
+    int pb, pe;
+    if (t.sh) { pb = Tk; pe = Tk + p.T; }
+    else { pb = min(max(p.offsets[t.g], 0), Tk); pe = min(max(p.offsets[t.g + 1], pb), Tk); }
+    t.row0 = pb + m0;
+    t.nvalid = min(NP_BM, pe - t.row0);
+    return t.nvalid > 0;
+}
+
+__device__ __forceinline__ int64_t np_act_row(const FfnPass &p, const NpTile &t, int i)
+{
+    const int pos = t.row0 + i;
+    if (!p.act_by_token) return pos;
+    if (t.sh) return pos - p.T * p.k;
+    const int tok = p.perm[pos] / p.k;
+    return min(max(tok, 0), p.T - 1);              // in bounds even for corrupt routing
+}
+
+// Selector tables.  CB2: entry idx holds, for each packed pair (C_2i, C_2i+1)
+// of codeword idx, the byte selector into the pool {lo: bf16(ds) | bf16(3ds),
+// hi: the same with the signs flipped}.  Q2_K: entry `byte` holds the two
+// selectors of its four 2-bit codes into the pool {lo: v0 | v1, hi: v2 | v3}.
+__device__ __forceinline__ uint32_t cb2_pos(int c)
+{
+    return (c < 0 ? 4u : 0u) + ((c == 3 || c == -3) ? 2u : 0u);
+}
+
+template <int FMT>
+__device__ __forceinline__ void np_build_table(const FfnPass &p, uint32_t *tab)
+{
+    if constexpr (FMT == FMT_CB2) {
+        for (int e = threadIdx.x; e < 256 * 4; e += NP_THREADS) {
+            const int idx = e >> 2, i = e & 3;
+            const uint32_t b0 = cb2_pos(p.codebook[8 * idx + 2 * i]), b1 = cb2_pos(p.codebook[8 * idx + 2 * i + 1]);
+            const uint32_t sel = b0 | ((b0 + 1) << 8) | (b1 << 16) | ((b1 + 1) << 24);
+#pragma unroll
+            for (int c = 0; c < NP_COPIES; ++c) tab[(idx * NP_COPIES + c) * 4 + i] = sel;
+        }
+    } else if constexpr (FMT == FMT_Q2K) {
+        for (int e = threadIdx.x; e < 256 * 2; e += NP_THREADS) {
+            const int byte = e >> 1, i = e & 1;
+            const uint32_t q0 = (byte >> (4 * i)) & 3, q1 = (byte >> (4 * i + 2)) & 3;
+            const uint32_t sel = (2 * q0) | ((2 * q0 + 1) << 8) | ((2 * q1) << 16) | ((2 * q1 + 1) << 24);
+#pragma unroll
+            for (int c = 0; c < NP_COPIES; ++c) tab[(byte * NP_COPIES + c) * 2 + i] = sel;
+        }
+    }
+}
+
+// Raw weight bytes of one lane and one column fragment for one half-block
+// (MFMA steps 4h..4h+3 of block b).
+struct RawCB2 { uint32_t d, sc, ix; };               // d, scale byte pair, 4 indices
+struct RawQ2K { uint32_t dd, scw, c0, c1; };         // d|dmin, 4 scale bytes, 16 codes
+struct RawQ4K { uint32_t dd, s0, s1, s2; u32x4 c; }; // d|dmin, 12 scale bytes, 32 codes
+struct RawBF16 { uint32_t unused; };                 // bf16 streams per MFMA step
+
+template <int FMT> struct RawOf;
+template <> struct RawOf<FMT_CB2> { using T = RawCB2; };
+template <> struct RawOf<FMT_Q2K> { using T = RawQ2K; };
+template <> struct RawOf<FMT_Q4K> { using T = RawQ4K; };
+template <> struct RawOf<FMT_BF16> { using T = RawBF16; };
+
+__device__ __forceinline__ uint32_t ld_u32_unaligned(const uint8_t *p)
+{
+    uint32_t v;
+    __builtin_memcpy(&v, p, 4);
+    return v;
+}
+
+// half-block hs = 2 b + h of the row
+template <int FMT>
+__device__ __forceinline__ void raw_load(const uint8_t *row, int hs, int fc, typename RawOf<FMT>::T &r)
+{
+    const int b = hs >> 1, h = hs & 1;
+    if constexpr (FMT == FMT_CB2) {
+        const uint8_t *blk = row + (int64_t)b * 38;
+        r.d = ld_u16(blk);
+        r.sc = ld_u16(blk + 2 + 2 * (fc >> 1));
+        r.ix = ld_u32_unaligned(blk + 6 + 8 * fc + 4 * h);      // 2-byte aligned
+    } else if constexpr (FMT == FMT_Q2K) {
+        const uint8_t *blk = row + (int64_t)b * 84;
+        r.dd = *(const uint32_t *)blk;
+        r.scw = *(const uint32_t *)(blk + 4 + 4 * fc);
+        const uint2 c = *(const uint2 *)(blk + 20 + 16 * fc + 8 * h);
+        r.c0 = c.x;
+        r.c1 = c.y;
+    } else if constexpr (FMT == FMT_Q4K) {
+        const uint8_t *blk = row + (int64_t)b * 144;
+        r.dd = *(const uint32_t *)blk;
+        r.s0 = *(const uint32_t *)(blk + 4);
+        r.s1 = *(const uint32_t *)(blk + 8);
+        r.s2 = *(const uint32_t *)(blk + 12);
+        r.c = *(const u32x4 *)(blk + 16 + 32 * fc + 16 * h);
+    }
+}
+
+// Per-half-block dequantization state of one lane and fragment.
+struct Pool { uint32_t lo[2], hi[2]; float mul, off; };
+
+template <int FMT>
+__device__ __forceinline__ void pool_prep(const typename RawOf<FMT>::T &r, int h, int fc, Pool &P)
+{
+    if constexpr (FMT == FMT_CB2) {
+        // sub-block 2 fc + h: nibble h of scale byte 2 + fc
+        const uint32_t s = (r.sc >> (8 * (fc & 1) + 4 * h)) & 15u;
+        const float ds = f16_bits_to_f32(r.d) * (float)s;        // exact (11 x 4 bits)
+        P.lo[0] = pk_bf16(ds, 3.0f * ds);
+        P.hi[0] = P.lo[0] ^ 0x80008000u;
+    } else if constexpr (FMT == FMT_Q2K) {
+        // sub-blocks 4 fc + 2 h + u, u = 0, 1 (each two MFMA steps)
+        const float d = f16_bits_to_f32(r.dd & 0xffffu), dmin = f16_bits_to_f32(r.dd >> 16);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const uint32_t sm = (r.scw >> (8 * (2 * h + u))) & 0xffu;
+            const float mul = d * (float)(sm & 15u), off = dmin * (float)(sm >> 4);
+            P.lo[u] = pk_bf16(-off, mul - off);
+            P.hi[u] = pk_bf16(2.0f * mul - off, 3.0f * mul - off);
+        }
+    } else if constexpr (FMT == FMT_Q4K) {
+        // sub-block 2 fc + h; 6-bit fields sc_0..7, m_0..7 in a 96-bit stream
+        const int j = 2 * fc + h;
+        const uint64_t lo64 = (uint64_t)r.s0 | ((uint64_t)r.s1 << 32);
+        const uint64_t hi64 = (uint64_t)r.s1 | ((uint64_t)r.s2 << 32);
+        const int bsc = 6 * j, bm = 6 * (8 + j);
+        const uint32_t sc = (uint32_t)(bsc < 32 ? lo64 >> bsc : hi64 >> (bsc - 32)) & 63u;
+        const uint32_t m = (uint32_t)(hi64 >> (bm - 32)) & 63u;
+        P.mul = f16_bits_to_f32(r.dd & 0xffffu) * (float)sc;
+        P.off = f16_bits_to_f32(r.dd >> 16) * (float)m;
+    }
+}
+
+// B fragment (8 bf16 = 4 dwords) of MFMA step s4 of the half-block.
+template <int FMT>
+__device__ __forceinline__ void bfrag(const typename RawOf<FMT>::T &r, const Pool &P, int s4,
+                                      const uint32_t *tab, int copy, uint32_t out[4])
+{
+    if constexpr (FMT == FMT_CB2) {
+        const uint32_t idx = (r.ix >> (8 * s4)) & 0xffu;
+        const u32x4 sel = *(const u32x4 *)&tab[(idx * NP_COPIES + copy) * 4];
+        out[0] = vperm(P.hi[0], P.lo[0], sel.x);
+        out[1] = vperm(P.hi[0], P.lo[0], sel.y);
+        out[2] = vperm(P.hi[0], P.lo[0], sel.z);
+        out[3] = vperm(P.hi[0], P.lo[0], sel.w);
+    } else if constexpr (FMT == FMT_Q2K) {
+        const uint32_t cw = s4 < 2 ? r.c0 : r.c1;
+        const uint32_t b0 = (cw >> (16 * (s4 & 1))) & 0xffu, b1 = (cw >> (16 * (s4 & 1) + 8)) & 0xffu;
+        const uint2 s0 = *(const uint2 *)&tab[(b0 * NP_COPIES + copy) * 2];
+        const uint2 s1 = *(const uint2 *)&tab[(b1 * NP_COPIES + copy) * 2];
+        const int u = s4 >> 1;
+        out[0] = vperm(P.hi[u], P.lo[u], s0.x);
+        out[1] = vperm(P.hi[u], P.lo[u], s0.y);
+        out[2] = vperm(P.hi[u], P.lo[u], s1.x);
+        out[3] = vperm(P.hi[u], P.lo[u], s1.y);
+    } else if constexpr (FMT == FMT_Q4K) {
+        const uint32_t cw = r.c[s4];
+        const uint32_t lo = cw & 0x0f0f0f0fu, hi = (cw >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            out[i] = pk_bf16(__builtin_fmaf(P.mul, ubyte(lo, i), -P.off), __builtin_fmaf(P.mul, ubyte(hi, i), -P.off));
+    }
+}
+
+__device__ __forceinline__ float np_silu_mul(float g, float u)
+{
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt vmcnt(n) with the other counters left free
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(N | (7 << 4) | (15 << 8));
+}
+
+// Activation stages: 3 LDS buffers of 96 rows x 128 bf16 (256 B per row,
+// 16-B chunks XOR-swizzled by the row so that a column read of 16 rows hits
+// all banks).  Logical chunk c of a stage row holds K offsets
+// 64 (c >> 2) + 32 h + 8 (c & 3) of block b; the lanes fill the stages with
+// direct global -> LDS loads, wave w filling rows 16w..16w+15 (its own row
+// fragment), two half-blocks ahead of use.
+constexpr int NP_ABUF = NP_BM * 256;               // bytes per stage
+constexpr int NP_NBUF = 3;
+
+template <bool GATEUP, int NMF>
+__device__ __forceinline__ void np_epilogue(const FfnPass &p, const NpTile &t, const f32x4 (&acc)[NMF][4])
+{
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int fr = lane & 15, fc = lane >> 4;
+    // D lane (fr, fc) holds rows 4 fc + v of column fr
+#pragma unroll
+    for (int mf = 0; mf < NMF; ++mf) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = mf * 16 + 4 * fc + v;
+            if (i >= t.nvalid) continue;
+            const int64_t pos = t.row0 + i;
+            if (GATEUP) {
+#pragma unroll
+                for (int nf = 0; nf < 2; ++nf) {
+                    const int n = t.n0 + wave * 32 + nf * 16 + fr;
+                    if (n < t.Ng) {
+                        const float hv = np_silu_mul(acc[mf][nf][v], acc[mf][nf + 2][v]);
+                        ((uint16_t *)p.out)[pos * p.out_stride + n] = (uint16_t)(pk_bf16(hv, 0.f) & 0xffffu);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int nf = 0; nf < 4; ++nf) {
+                    const int n = t.n0 + wave * 64 + nf * 16 + fr;
+                    if (n < t.Ng) ((float *)p.out)[pos * p.out_stride + n] = acc[mf][nf][v];
+                }
+            }
+        }
+    }
+}
+
+template <int FMT, bool GATEUP, int NMF>
+__device__ __forceinline__ void np_body(const FfnPass &p, const NpTile &t, uint8_t *As, const uint32_t *tab)
+{
+    using Raw = typename RawOf<FMT>::T;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int fr = lane & 15, fc = lane >> 4, copy = lane & (NP_COPIES - 1);
+    const int nb = t.Kg >> 8;
+    const int nhs = 2 * nb;
+
+    // ---- direct-to-LDS activation loads of this lane (4 per stage)
+    const bool astage = wave < NMF;
+    // element offsets (activation tensors hold < 2^31 elements)
+    uint32_t asrc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * wave + 4 * i + (lane >> 4);
+        const int c = (lane & 15) ^ (r & 15);
+        asrc[i] = (uint32_t)(np_act_row(p, t, min(r, t.nvalid - 1)) * p.act_stride) + 64 * (c >> 2) + 8 * (c & 3);
+    }
+    const uint16_t *act = (const uint16_t *)p.act;
+    auto a_issue = [&](int hs, int buf) {
+        if (astage) {
+            const uint32_t koff = 256 * (hs >> 1) + 32 * (hs & 1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_global_load_lds((const void *)(act + (asrc[i] + koff)),
+                                                 (lds_void *)(As + buf * NP_ABUF + (16 * wave + 4 * i) * 256),
+                                                 16, 0, 0);
+        }
+    };
+    // A fragment read offsets (bytes within a stage) of MFMA step s4: row fr,
+    // logical chunk 4 fc + s4
+    int aoff[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) aoff[s4] = fr * 256 + (((4 * fc + s4) ^ fr) << 4);
+
+    // ---- weight rows of this lane's four column fragments
+    // byte offsets inside one expert's matrix (< 2^32 bytes) from per-tile bases
+    const uint8_t *wb0, *wb1;
+    if (FMT == FMT_BF16) { wb0 = (const uint8_t *)p.s0; wb1 = (const uint8_t *)p.s1; }
+    else {
+        wb0 = p.w0 + (int64_t)t.g * p.w_expert_bytes;
+        wb1 = GATEUP ? p.w1 + (int64_t)t.g * p.w_expert_bytes : wb0;
+    }
+    uint32_t wo[4];
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf) {
+        int col;
+        if (GATEUP) col = t.n0 + wave * 32 + (nf & 1) * 16 + fr;
+        else col = t.n0 + wave * 64 + nf * 16 + fr;
+        col = min(col, t.Ng - 1);
+        wo[nf] = FMT == FMT_BF16 ? (uint32_t)col * (uint32_t)t.Kg * 2u + 128u * fc : (uint32_t)col * (uint32_t)p.w_row_bytes;
+    }
+    auto wrow = [&](int nf) -> const uint8_t * { return (GATEUP && nf >= 2 ? wb1 : wb0) + wo[nf]; };
+
+    f32x4 acc[NMF][4];
+#pragma unroll
+    for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    Raw raw[2][4];                                   // [half parity][fragment], ping-pong
+    u32x4 bw[2][4];                                  // bf16: [step parity][fragment]
+    const int nks = 8 * nb;
+    auto bw_load = [&](int ks, int par) {
+        ks = min(ks, nks - 1);
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf)
+            bw[par][nf] = *(const u32x4 *)(wrow(nf) + 512 * (ks >> 3) + 16 * (ks & 7));
+    };
+
+    // ---- prologue: weights of unit 0, activation stages 0 and 1
+    if constexpr (FMT == FMT_BF16) bw_load(0, 0);
+    else {
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) raw_load<FMT>(wrow(nf), 0, fc, raw[0][nf]);
+    }
+    a_issue(0, 0);
+    a_issue(min(1, nhs - 1), 1);
+    wait_vm<4>();
+    __builtin_amdgcn_s_barrier();
+
+    int buf = 0;                                     // stage hs lives in buffer hs % 3
+    for (int b = 0; b < nb; ++b) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int hs = 2 * b + h;
+            // weights of the next half-block first, then the activation stage two ahead
+            if constexpr (FMT != FMT_BF16) {
+#pragma unroll
+                for (int nf = 0; nf < 4; ++nf) raw_load<FMT>(wrow(nf), min(hs + 1, nhs - 1), fc, raw[h ^ 1][nf]);
+            }
+            {
+                const int b2 = buf == 0 ? 2 : buf - 1;          // (hs + 2) % 3
+                a_issue(min(hs + 2, nhs - 1), b2);
+            }
+            Pool P[4];
+            if constexpr (FMT != FMT_BF16) {
+#pragma unroll
+                for (int nf = 0; nf < 4; ++nf) pool_prep<FMT>(raw[h][nf], h, fc, P[nf]);
+            }
+            const uint8_t *ab = As + buf * NP_ABUF;
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                bf16x8 a[NMF];
+#pragma unroll
+                for (int mf = 0; mf < NMF; ++mf) a[mf] = *(const bf16x8 *)(ab + aoff[s4] + mf * 4096);
+                bf16x8 bq[4];
+                if constexpr (FMT == FMT_BF16) {
+                    const int ks = 8 * b + 4 * h + s4;
+                    bw_load(ks + 1, (s4 + 1) & 1);
+#pragma unroll
+                    for (int nf = 0; nf < 4; ++nf) bq[nf] = __builtin_bit_cast(bf16x8, bw[s4 & 1][nf]);
+                } else {
+#pragma unroll
+                    for (int nf = 0; nf < 4; ++nf) {
+                        uint32_t o[4];
+                        bfrag<FMT>(raw[h][nf], P[nf], s4, tab, copy, o);
+                        bq[nf] = __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
+                    }
+                }
+#pragma unroll
+                for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+                    for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma16x16x32(a[mf], bq[nf], acc[mf][nf]);
+            }
+            // stage hs + 1 (issued one step ago) has landed once at most the
+            // loads issued in this step are outstanding: the 4 activation
+            // loads of stage hs + 2 are this wave's last memory loads, except
+            // in the bf16 body, which streams 4 more after them
+            if constexpr (FMT == FMT_BF16) wait_vm<8>();
+            else wait_vm<4>();
+            __builtin_amdgcn_s_barrier();
+            buf = buf == 2 ? 0 : buf + 1;
+        }
+    }
+
+    np_epilogue<GATEUP, NMF>(p, t, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Routed CB2 / Q2_K body.  Weights stream from HBM as small scattered reads
+// (each lane reads a few bytes of its own row), so they are prefetched a
+// whole block ahead: the bytes of block b + 1 are requested at the start of
+// block b, after that half-block's activation loads, and are only needed two
+// half-blocks later.  Vector-memory loads complete in order, so the
+// activation loads (one half-block ahead, staged through registers into the
+// swizzled LDS layout) never force the weight loads issued after them.
+struct BlkCB2 { uint32_t d, sc, i0, i1; };            // d, scale byte pair, 8 indices
+struct BlkQ2K { uint32_t dd, scw; uint2 c0, c1; };    // d|dmin, 4 scale bytes, 2 x 16 codes
+template <int FMT> struct BlkOf;
+template <> struct BlkOf<FMT_CB2> { using T = BlkCB2; };
+template <> struct BlkOf<FMT_Q2K> { using T = BlkQ2K; };
+
+// the part of block b that half h of the previous block requests (Q2_K
+// splits its codes so that only half of them are in flight at a time)
+template <int FMT>
+__device__ __forceinline__ void blk_load(const uint8_t *row, int b, int h, int fc, typename BlkOf<FMT>::T &r)
+{
+    if constexpr (FMT == FMT_CB2) {
+        if (h == 0) {
+            const uint8_t *blk = row + (int64_t)b * 38;
+            r.d = ld_u16(blk);
+            r.sc = ld_u16(blk + 2 + 2 * (fc >> 1));
+            r.i0 = ld_u32_unaligned(blk + 6 + 8 * fc);           // 2-byte aligned
+            r.i1 = ld_u32_unaligned(blk + 10 + 8 * fc);
+        }
+    } else {
+        const uint8_t *blk = row + (int64_t)b * 84;
+        if (h == 0) {
+            r.dd = *(const uint32_t *)blk;
+            r.scw = *(const uint32_t *)(blk + 4 + 4 * fc);
+            r.c0 = *(const uint2 *)(blk + 20 + 16 * fc);
+        } else {
+            r.c1 = *(const uint2 *)(blk + 28 + 16 * fc);
+        }
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void blk_pool(const typename BlkOf<FMT>::T &r, int h, int fc, Pool &P)
+{
+    if constexpr (FMT == FMT_CB2) {
+        RawCB2 x{r.d, r.sc, 0u};
+        pool_prep<FMT_CB2>(x, h, fc, P);
+    } else {
+        RawQ2K x{r.dd, r.scw, 0u, 0u};
+        pool_prep<FMT_Q2K>(x, h, fc, P);
+    }
+}
+
+__device__ __forceinline__ void q2k_pool(const BlkQ2K &r, int h, int u, Pool &P)
+{
+    const float d = f16_bits_to_f32(r.dd & 0xffffu), dmin = f16_bits_to_f32(r.dd >> 16);
+    const uint32_t sm = (r.scw >> (8 * (2 * h + u))) & 0xffu;
+    const float mul = d * (float)(sm & 15u), off = dmin * (float)(sm >> 4);
+    P.lo[u] = pk_bf16(-off, mul - off);
+    P.hi[u] = pk_bf16(2.0f * mul - off, 3.0f * mul - off);
+}
+
+template <int FMT>
+__device__ __forceinline__ void blk_frag(const typename BlkOf<FMT>::T &r, const Pool &P, int h, int s4,
+                                         const uint32_t *tab, int copy, uint32_t out[4])
+{
+    if constexpr (FMT == FMT_CB2) {
+        RawCB2 x{r.d, r.sc, h == 0 ? r.i0 : r.i1};
+        bfrag<FMT_CB2>(x, P, s4, tab, copy, out);
+    } else {
+        const uint2 c = h == 0 ? r.c0 : r.c1;
+        RawQ2K x{r.dd, r.scw, c.x, c.y};
+        bfrag<FMT_Q2K>(x, P, s4, tab, copy, out);
+    }
+}
+
+template <int FMT, bool GATEUP, int NMF>
+__device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uint8_t *As, const uint32_t *tab)
+{
+    using Blk = typename BlkOf<FMT>::T;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int fr = lane & 15, fc = lane >> 4, copy = lane & (NP_COPIES - 1);
+    const int nb = t.Kg >> 8;                        // even (checked on the host)
+    const int nhs = 2 * nb;
+
+    // ---- activation staging: 16-B chunk ci = tid + 512 j of a stage is row
+    // ci >> 4, physical chunk ci & 15 (logical chunk (ci & 15) ^ (row & 15))
+    uint32_t aoffs[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int ci = tid + NP_THREADS * j, r = ci >> 4;
+        const int c = (ci & 15) ^ (r & 15);
+        aoffs[j] = (uint32_t)(np_act_row(p, t, min(r, t.nvalid - 1)) * p.act_stride) + 64 * (c >> 2) + 8 * (c & 3);
+    }
+    const uint16_t *act = (const uint16_t *)p.act;
+    u32x4 av[3];
+    auto a_load = [&](int hs) {
+        const uint32_t koff = 256 * (hs >> 1) + 32 * (hs & 1);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) av[j] = *(const u32x4 *)(act + (aoffs[j] + koff));
+    };
+    auto a_store = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) *(u32x4 *)(As + buf * NP_ABUF + (tid + NP_THREADS * j) * 16) = av[j];
+    };
+    int aoff[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) aoff[s4] = fr * 256 + (((4 * fc + s4) ^ fr) << 4);
+
+    // ---- weight rows of this lane's four column fragments
+    const uint8_t *wb0 = p.w0 + (int64_t)t.g * p.w_expert_bytes;
+    const uint8_t *wb1 = GATEUP ? p.w1 + (int64_t)t.g * p.w_expert_bytes : wb0;
+    uint32_t wo[4];
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf) {
+        int col;
+        if (GATEUP) col = t.n0 + wave * 32 + (nf & 1) * 16 + fr;
+        else col = t.n0 + wave * 64 + nf * 16 + fr;
+        wo[nf] = (uint32_t)min(col, t.Ng - 1) * (uint32_t)p.w_row_bytes;
+    }
+    auto wrow = [&](int nf) -> const uint8_t * { return (GATEUP && nf >= 2 ? wb1 : wb0) + wo[nf]; };
+
+    f32x4 acc[NMF][4];
+#pragma unroll
+    for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    Blk blk[2][4];                                   // [block parity][fragment]
+    a_load(0);
+#pragma unroll
+    for (int nf = 0; nf < 4; ++nf) {
+        blk_load<FMT>(wrow(nf), 0, 0, fc, blk[0][nf]);
+        blk_load<FMT>(wrow(nf), 0, 1, fc, blk[0][nf]);
+    }
+    a_store(0);
+    __syncthreads();
+
+    for (int b = 0; b < nb; b += 2) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int bb = b + q;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int hs = 2 * bb + h;
+                a_load(min(hs + 1, nhs - 1));
+                // keep the weight loads behind this step's activation loads
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int nf = 0; nf < 4; ++nf) blk_load<FMT>(wrow(nf), min(bb + 1, nb - 1), h, fc, blk[q ^ 1][nf]);
+                Pool P[4];
+                if constexpr (FMT == FMT_CB2) {
+#pragma unroll
+                    for (int nf = 0; nf < 4; ++nf) blk_pool<FMT>(blk[q][nf], h, fc, P[nf]);
+                }
+                const uint8_t *ab = As + h * NP_ABUF;
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    if constexpr (FMT == FMT_Q2K) {
+                        // the pool of sub-block 4 fc + 2 h + s4 / 2, built when first needed
+                        if ((s4 & 1) == 0) {
+#pragma unroll
+                            for (int nf = 0; nf < 4; ++nf) q2k_pool(blk[q][nf], h, s4 >> 1, P[nf]);
+                        }
+                    }
+                    bf16x8 a[NMF];
+#pragma unroll
+                    for (int mf = 0; mf < NMF; ++mf) a[mf] = *(const bf16x8 *)(ab + aoff[s4] + mf * 4096);
+                    bf16x8 bq[4];
+#pragma unroll
+                    for (int nf = 0; nf < 4; ++nf) {
+                        uint32_t o[4];
+                        blk_frag<FMT>(blk[q][nf], P[nf], h, s4, tab, copy, o);
+                        bq[nf] = __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
+                    }
+#pragma unroll
+                    for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+                        for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma16x16x32(a[mf], bq[nf], acc[mf][nf]);
+                }
+                a_store(h ^ 1);
+                __syncthreads();
+            }
+        }
+    }
+    np_epilogue<GATEUP, NMF>(p, t, acc);
+}
+
+template <int FMT, bool GATEUP>
+__device__ __forceinline__ void np_dispatch(const FfnPass &p, const NpTile &t, uint8_t *As, const uint32_t *tab)
+{
+    if constexpr (FMT == FMT_CB2 || FMT == FMT_Q2K) {
+        switch ((t.nvalid + 15) >> 4) {
+        case 1: np_body_r<FMT, GATEUP, 1>(p, t, As, tab); break;
+        case 2: np_body_r<FMT, GATEUP, 2>(p, t, As, tab); break;
+        case 3: np_body_r<FMT, GATEUP, 3>(p, t, As, tab); break;
+        case 4: np_body_r<FMT, GATEUP, 4>(p, t, As, tab); break;
+        case 5: np_body_r<FMT, GATEUP, 5>(p, t, As, tab); break;
+        default: np_body_r<FMT, GATEUP, 6>(p, t, As, tab); break;
+        }
+    } else {
+        switch ((t.nvalid + 15) >> 4) {
+        case 1: np_body<FMT, GATEUP, 1>(p, t, As, tab); break;
+        case 2: np_body<FMT, GATEUP, 2>(p, t, As, tab); break;
+        case 3: np_body<FMT, GATEUP, 3>(p, t, As, tab); break;
+        case 4: np_body<FMT, GATEUP, 4>(p, t, As, tab); break;
+        case 5: np_body<FMT, GATEUP, 5>(p, t, As, tab); break;
+        default: np_body<FMT, GATEUP, 6>(p, t, As, tab); break;
+        }
+    }
+}
+
+template <int FMT> constexpr int np_tab_bytes() { return FMT == FMT_CB2 ? NP_TAB_CB2 : FMT == FMT_Q2K ? NP_TAB_Q2K : 0; }
+template <int FMT> constexpr int np_lds_bytes() { return NP_NBUF * NP_ABUF + np_tab_bytes<FMT>(); }
+
+template <int FMT, bool GATEUP>
+__global__ __launch_bounds__(NP_THREADS) void np_kernel(FfnPass p, int S)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t np_smem[];
+    NpTile t;
+    if (!np_tile(p, S, GATEUP ? 256 : 512, t)) return;
+    uint8_t *As = np_smem;
+    uint32_t *tab = (uint32_t *)(np_smem + NP_NBUF * NP_ABUF);
+    if (t.sh) {
+        np_dispatch<FMT_BF16, GATEUP>(p, t, As, tab);
+    } else {
+        np_build_table<FMT>(p, tab);
+        __syncthreads();
+        np_dispatch<FMT, GATEUP>(p, t, As, tab);
+    }
+}
+
+template <int FMT, bool GATEUP>
+hipError_t np_launch(const FfnPass &p, hipStream_t s)
+{
+    constexpr int lds = np_lds_bytes<FMT>();
+    static bool attr = false;
+    if (!attr) {
+        const hipError_t e = hipFuncSetAttribute((const void *)np_kernel<FMT, GATEUP>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    const int wg_cols = GATEUP ? 256 : 512;
+    const int S = (std::max(p.N, p.Nsh) + wg_cols - 1) / wg_cols;
+    const int tiles = ffn_max_tiles(p.T, p.k, p.E, p.Nsh > 0, NP_BM);
+    const int64_t grid = (int64_t)((tiles + 7) / 8) * 8 * S;
+    np_kernel<FMT, GATEUP><<<dim3((unsigned)grid), NP_THREADS, lds, s>>>(p, S);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool np_prefill_ok(const FfnPass &p)
+{
+    if (p.act_f32) return false;
+    if (p.K % (2 * QK) || p.K < 2 * QK) return false;   // routed blocks run in pairs
+    if (p.Nsh > 0 && (p.Ksh % QK || p.Ksh < QK)) return false;
+    return true;
+}
+
+hipError_t launch_np_prefill(const FfnPass &p, bool gateup, hipStream_t s)
+{
+    if (!np_prefill_ok(p) || p.out_f32 == gateup) return hipErrorInvalidValue;
+    if (gateup) {
+        if (p.fmt == FMT_CB2) return np_launch<FMT_CB2, true>(p, s);
+        if (p.fmt == FMT_Q4K) return np_launch<FMT_Q4K, true>(p, s);
+    } else {
+        if (p.fmt == FMT_Q2K) return np_launch<FMT_Q2K, false>(p, s);
+        if (p.fmt == FMT_Q4K) return np_launch<FMT_Q4K, false>(p, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace moe
