@@ -273,7 +273,7 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
     const bool np = prefill && np_prefill_ok(up) && np_prefill_ok(dn);
     const int sched_bm = np ? NP_BM : BM;
     if (!pr.before("ffn_schedule")) return hip_fail(hipGetLastError(), "event record");
-    launch_ffn_schedule(offsets, T, k, E, has_sh, sched_bm, w.sched, s);
+    launch_ffn_schedule(offsets, T, k, E, has_sh, sched_bm, w.sched, s, np ? NP_BM_SH : sched_bm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "ffn_schedule launch");
     if (!pr.after()) return hip_fail(hipGetLastError(), "event record");

@@ -22,16 +22,17 @@
 namespace moe {
 
 // ============================================================== schedule
-int ffn_max_tiles(int T, int k, int E, int has_shared, int BM)
+int ffn_max_tiles(int T, int k, int E, int has_shared, int BM, int BMsh)
 {
+    if (BMsh <= 0) BMsh = BM;
     const int64_t tk = (int64_t)T * k;
     const int64_t routed = (tk + BM - 1) / BM + std::min<int64_t>(E, tk);
-    const int64_t sh = has_shared ? (T + BM - 1) / BM : 0;
+    const int64_t sh = has_shared ? (T + BMsh - 1) / BMsh : 0;
     return (int)(routed + sh);
 }
 
 __global__ __launch_bounds__(1024) void ffn_schedule(const int32_t *offsets, int T, int k, int E, int has_shared,
-                                                     int BM, int max_tiles, int32_t *sched)
+                                                     int BM, int BMsh, int max_tiles, int32_t *sched)
 {
     __shared__ int32_t part[1024];
     const int tid = threadIdx.x;
@@ -46,7 +47,8 @@ __global__ __launch_bounds__(1024) void ffn_schedule(const int32_t *offsets, int
             // caller-supplied offsets array cannot push tiles out of range
             const int Tk = T * k;
             const int n = g == E ? T : min(max(offsets[g + 1], 0), Tk) - min(max(offsets[g], 0), Tk);
-            cnt[i] = n > 0 ? (n + BM - 1) / BM : 0;
+            const int bm = g == E ? BMsh : BM;
+            cnt[i] = n > 0 ? (n + bm - 1) / bm : 0;
             mine += cnt[i];
         }
     }
@@ -63,9 +65,10 @@ __global__ __launch_bounds__(1024) void ffn_schedule(const int32_t *offsets, int
         const int o = tid * per + i;
         if (o < G) {
             const int g = has_shared ? (o == 0 ? E : o - 1) : o;
+            const int bm = g == E ? BMsh : BM;
             for (int c = 0; c < cnt[i] && start + c < max_tiles; ++c) {
                 sched[1 + 2 * (start + c)] = g;
-                sched[2 + 2 * (start + c)] = c * BM;
+                sched[2 + 2 * (start + c)] = c * bm;
             }
             start += cnt[i];
         }
@@ -74,9 +77,11 @@ __global__ __launch_bounds__(1024) void ffn_schedule(const int32_t *offsets, int
 }
 
 void launch_ffn_schedule(const int32_t *offsets, int T, int k, int E, int has_shared, int BM, int32_t *sched,
-                         hipStream_t s)
+                         hipStream_t s, int BMsh)
 {
-    ffn_schedule<<<1, 1024, 0, s>>>(offsets, T, k, E, has_shared, BM, ffn_max_tiles(T, k, E, has_shared, BM), sched);
+    if (BMsh <= 0) BMsh = BM;
+    ffn_schedule<<<1, 1024, 0, s>>>(offsets, T, k, E, has_shared, BM, BMsh, ffn_max_tiles(T, k, E, has_shared, BM, BMsh),
+                                    sched);
 }
 
 // ============================================================== tile helpers

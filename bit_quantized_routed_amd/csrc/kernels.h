@@ -45,9 +45,10 @@ struct FfnPass {
     const int32_t *sched;             // [0] = tile count, then (group, m0) pairs
 };
 
-int ffn_max_tiles(int T, int k, int E, int has_shared, int BM);
+// tiles of BM rows per routed group and BMsh (<= 0: BM) for the shared group
+int ffn_max_tiles(int T, int k, int E, int has_shared, int BM, int BMsh = 0);
 void launch_ffn_schedule(const int32_t *offsets, int T, int k, int E, int has_shared, int BM,
-                         int32_t *sched, hipStream_t s);
+                         int32_t *sched, hipStream_t s, int BMsh = 0);
 // decode (exact codes, fp32 accumulation); returns hipSuccess or an error
 hipError_t launch_ffn_decode(const FfnPass &p, bool gateup, hipStream_t s);
 // prefill (bf16-rounded weights, bf16 MFMA)
@@ -99,7 +100,7 @@ constexpr int PRE_BM = 64, PRE_BN = 64;
 
 // prefill grouped GEMMs with in-register dequantization (K multiples of 256,
 // bf16 activations); tiles of NP_BM rows
-constexpr int NP_BM = 96;
+constexpr int NP_BM = 96, NP_BM_SH = 80;
 bool np_prefill_ok(const FfnPass &p);
 hipError_t launch_np_prefill(const FfnPass &p, bool gateup, hipStream_t s);
 

@@ -17,10 +17,13 @@
 // activations of the tile are staged through LDS in half-blocks of 128 K,
 // double-buffered; row fragments beyond the tile's valid rows are skipped.
 //
-// K order.  Within each 256-weight block, MFMA step s (0..7) gives the lanes
-// of column group fc (0..3) the 8-weight group 8*fc + s, so each lane walks
-// 64 consecutive weights of its row across the block; the activations are
-// read with the same permutation, which leaves every dot product unchanged.
+// K order.  Within each 256-weight block of a packed format, MFMA step s
+// (0..7) gives the lanes of column group fc (0..3) the 8-weight group
+// 8*fc + s, so each lane walks 64 consecutive weights of its row across the
+// block and reads its packed bytes once per block; the activations are read
+// with the same permutation, which leaves every dot product unchanged.  The
+// bf16 shared expert keeps the natural order (step s covers K 32s..32s+31),
+// where the 4 lanes of a row read 64 contiguous bytes per step.
 //
 // Dequantization into bf16 operands (the weights are rounded to bf16, RNE):
 //   CB2   w = d*s_j*C, C in {-3,-1,1,3}: a 4-value pool {+-d s_j, +-3 d s_j}
@@ -42,7 +45,7 @@ namespace {
 
 constexpr int NP_THREADS = 512;
 constexpr int NP_MF = NP_BM / 16;                  // row fragments per tile
-static_assert(NP_MF == 6, "np_dispatch instantiates 1..6 row fragments");
+static_assert(NP_MF == 6 && NP_BM_SH == 80, "the dispatch switches instantiate 1..6 (routed) and 1..5 (shared) row fragments");
 constexpr int NP_COPIES = 8;                       // selector-table copies (bank spread)
 constexpr int NP_TAB_CB2 = 256 * NP_COPIES * 16;   // bytes
 constexpr int NP_TAB_Q2K = 256 * NP_COPIES * 8;
@@ -88,7 +91,7 @@ __device__ __forceinline__ bool np_tile(const FfnPass &p, int S, int wg_cols, Np
     if (t.sh) { pb = Tk; pe = Tk + p.T; }
     else { pb = min(max(p.offsets[t.g], 0), Tk); pe = min(max(p.offsets[t.g + 1], pb), Tk); }
     t.row0 = pb + m0;
-    t.nvalid = min(NP_BM, pe - t.row0);
+    t.nvalid = min(t.sh ? NP_BM_SH : NP_BM, pe - t.row0);
     return t.nvalid > 0;
 }
 
@@ -250,24 +253,13 @@ __device__ __forceinline__ float np_silu_mul(float g, float u)
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt vmcnt(n) with the other counters left free
-template <int N>
-__device__ __forceinline__ void wait_vm()
-{
-    static_assert(N < 16, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt(N | (7 << 4) | (15 << 8));
-}
-
-// Activation stages: 3 LDS buffers of 96 rows x 128 bf16 (256 B per row,
+// Activation stages: 2 LDS buffers of 96 rows x 128 bf16 (256 B per row,
 // 16-B chunks XOR-swizzled by the row so that a column read of 16 rows hits
-// all banks).  Logical chunk c of a stage row holds K offsets
-// 64 (c >> 2) + 32 h + 8 (c & 3) of block b; the lanes fill the stages with
-// direct global -> LDS loads, wave w filling rows 16w..16w+15 (its own row
-// fragment), two half-blocks ahead of use.
+// all banks).  Logical chunk c of the stage of half-block h of block b holds
+// K offsets 64 (c >> 2) + 32 h + 8 (c & 3) (packed formats) or 128 h + 8 c
+// (bf16).
 constexpr int NP_ABUF = NP_BM * 256;               // bytes per stage
-constexpr int NP_NBUF = 3;
+constexpr int NP_NBUF = 2;
 
 template <bool GATEUP, int NMF>
 __device__ __forceinline__ void np_epilogue(const FfnPass &p, const NpTile &t, const f32x4 (&acc)[NMF][4])
@@ -300,146 +292,6 @@ __device__ __forceinline__ void np_epilogue(const FfnPass &p, const NpTile &t, c
             }
         }
     }
-}
-
-template <int FMT, bool GATEUP, int NMF>
-__device__ __forceinline__ void np_body(const FfnPass &p, const NpTile &t, uint8_t *As, const uint32_t *tab)
-{
-    using Raw = typename RawOf<FMT>::T;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int fr = lane & 15, fc = lane >> 4, copy = lane & (NP_COPIES - 1);
-    const int nb = t.Kg >> 8;
-    const int nhs = 2 * nb;
-
-    // ---- direct-to-LDS activation loads of this lane (4 per stage)
-    const bool astage = wave < NMF;
-    // element offsets (activation tensors hold < 2^31 elements)
-    uint32_t asrc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 16 * wave + 4 * i + (lane >> 4);
-        const int c = (lane & 15) ^ (r & 15);
-        asrc[i] = (uint32_t)(np_act_row(p, t, min(r, t.nvalid - 1)) * p.act_stride) + 64 * (c >> 2) + 8 * (c & 3);
-    }
-    const uint16_t *act = (const uint16_t *)p.act;
-    auto a_issue = [&](int hs, int buf) {
-        if (astage) {
-            const uint32_t koff = 256 * (hs >> 1) + 32 * (hs & 1);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                __builtin_amdgcn_global_load_lds((const void *)(act + (asrc[i] + koff)),
-                                                 (lds_void *)(As + buf * NP_ABUF + (16 * wave + 4 * i) * 256),
-                                                 16, 0, 0);
-        }
-    };
-    // A fragment read offsets (bytes within a stage) of MFMA step s4: row fr,
-    // logical chunk 4 fc + s4
-    int aoff[4];
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) aoff[s4] = fr * 256 + (((4 * fc + s4) ^ fr) << 4);
-
-    // ---- weight rows of this lane's four column fragments
-    // byte offsets inside one expert's matrix (< 2^32 bytes) from per-tile bases
-    const uint8_t *wb0, *wb1;
-    if (FMT == FMT_BF16) { wb0 = (const uint8_t *)p.s0; wb1 = (const uint8_t *)p.s1; }
-    else {
-        wb0 = p.w0 + (int64_t)t.g * p.w_expert_bytes;
-        wb1 = GATEUP ? p.w1 + (int64_t)t.g * p.w_expert_bytes : wb0;
-    }
-    uint32_t wo[4];
-#pragma unroll
-    for (int nf = 0; nf < 4; ++nf) {
-        int col;
-        if (GATEUP) col = t.n0 + wave * 32 + (nf & 1) * 16 + fr;
-        else col = t.n0 + wave * 64 + nf * 16 + fr;
-        col = min(col, t.Ng - 1);
-        wo[nf] = FMT == FMT_BF16 ? (uint32_t)col * (uint32_t)t.Kg * 2u + 128u * fc : (uint32_t)col * (uint32_t)p.w_row_bytes;
-    }
-    auto wrow = [&](int nf) -> const uint8_t * { return (GATEUP && nf >= 2 ? wb1 : wb0) + wo[nf]; };
-
-    f32x4 acc[NMF][4];
-#pragma unroll
-    for (int mf = 0; mf < NMF; ++mf)
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    Raw raw[2][4];                                   // [half parity][fragment], ping-pong
-    u32x4 bw[2][4];                                  // bf16: [step parity][fragment]
-    const int nks = 8 * nb;
-    auto bw_load = [&](int ks, int par) {
-        ks = min(ks, nks - 1);
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf)
-            bw[par][nf] = *(const u32x4 *)(wrow(nf) + 512 * (ks >> 3) + 16 * (ks & 7));
-    };
-
-    // ---- prologue: weights of unit 0, activation stages 0 and 1
-    if constexpr (FMT == FMT_BF16) bw_load(0, 0);
-    else {
-#pragma unroll
-        for (int nf = 0; nf < 4; ++nf) raw_load<FMT>(wrow(nf), 0, fc, raw[0][nf]);
-    }
-    a_issue(0, 0);
-    a_issue(min(1, nhs - 1), 1);
-    wait_vm<4>();
-    __builtin_amdgcn_s_barrier();
-
-    int buf = 0;                                     // stage hs lives in buffer hs % 3
-    for (int b = 0; b < nb; ++b) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int hs = 2 * b + h;
-            // weights of the next half-block first, then the activation stage two ahead
-            if constexpr (FMT != FMT_BF16) {
-#pragma unroll
-                for (int nf = 0; nf < 4; ++nf) raw_load<FMT>(wrow(nf), min(hs + 1, nhs - 1), fc, raw[h ^ 1][nf]);
-            }
-            {
-                const int b2 = buf == 0 ? 2 : buf - 1;          // (hs + 2) % 3
-                a_issue(min(hs + 2, nhs - 1), b2);
-            }
-            Pool P[4];
-            if constexpr (FMT != FMT_BF16) {
-#pragma unroll
-                for (int nf = 0; nf < 4; ++nf) pool_prep<FMT>(raw[h][nf], h, fc, P[nf]);
-            }
-            const uint8_t *ab = As + buf * NP_ABUF;
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                bf16x8 a[NMF];
-#pragma unroll
-                for (int mf = 0; mf < NMF; ++mf) a[mf] = *(const bf16x8 *)(ab + aoff[s4] + mf * 4096);
-                bf16x8 bq[4];
-                if constexpr (FMT == FMT_BF16) {
-                    const int ks = 8 * b + 4 * h + s4;
-                    bw_load(ks + 1, (s4 + 1) & 1);
-#pragma unroll
-                    for (int nf = 0; nf < 4; ++nf) bq[nf] = __builtin_bit_cast(bf16x8, bw[s4 & 1][nf]);
-                } else {
-#pragma unroll
-                    for (int nf = 0; nf < 4; ++nf) {
-                        uint32_t o[4];
-                        bfrag<FMT>(raw[h][nf], P[nf], s4, tab, copy, o);
-                        bq[nf] = __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
-                    }
-                }
-#pragma unroll
-                for (int mf = 0; mf < NMF; ++mf)
-#pragma unroll
-                    for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma16x16x32(a[mf], bq[nf], acc[mf][nf]);
-            }
-            // stage hs + 1 (issued one step ago) has landed once at most the
-            // loads issued in this step are outstanding: the 4 activation
-            // loads of stage hs + 2 are this wave's last memory loads, except
-            // in the bf16 body, which streams 4 more after them
-            if constexpr (FMT == FMT_BF16) wait_vm<8>();
-            else wait_vm<4>();
-            __builtin_amdgcn_s_barrier();
-            buf = buf == 2 ? 0 : buf + 1;
-        }
-    }
-
-    np_epilogue<GATEUP, NMF>(p, t, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -519,7 +371,15 @@ __device__ __forceinline__ void blk_frag(const typename BlkOf<FMT>::T &r, const 
 template <int FMT, bool GATEUP, int NMF>
 __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uint8_t *As, const uint32_t *tab)
 {
-    using Blk = typename BlkOf<FMT>::T;
+    // per-format weight staging: CB2/Q2_K whole blocks (two sets), Q4_K
+    // half-blocks (two sets), bf16 one MFMA step at a time (a ring of four)
+    constexpr bool BLK = FMT == FMT_CB2 || FMT == FMT_Q2K;
+    using Blk = typename BlkOf<BLK ? FMT : FMT_CB2>::T;
+    // bf16 weights use the natural K order (MFMA step s of a block covers K
+    // 32 s .. 32 s + 31, lane group fc its 8-wide slice), so the 4 lanes of a
+    // row read 64 contiguous bytes per step; the packed formats use the
+    // block-walking order (one small read per block)
+    constexpr bool NAT = FMT == FMT_BF16;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int fr = lane & 15, fc = lane >> 4, copy = lane & (NP_COPIES - 1);
     const int nb = t.Kg >> 8;                        // even (checked on the host)
@@ -532,12 +392,13 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
     for (int j = 0; j < 3; ++j) {
         const int ci = tid + NP_THREADS * j, r = ci >> 4;
         const int c = (ci & 15) ^ (r & 15);
-        aoffs[j] = (uint32_t)(np_act_row(p, t, min(r, t.nvalid - 1)) * p.act_stride) + 64 * (c >> 2) + 8 * (c & 3);
+        aoffs[j] = (uint32_t)(np_act_row(p, t, min(r, t.nvalid - 1)) * p.act_stride) +
+                   (NAT ? 8 * c : 64 * (c >> 2) + 8 * (c & 3));
     }
     const uint16_t *act = (const uint16_t *)p.act;
     u32x4 av[3];
     auto a_load = [&](int hs) {
-        const uint32_t koff = 256 * (hs >> 1) + 32 * (hs & 1);
+        const uint32_t koff = 256 * (hs >> 1) + (NAT ? 128 : 32) * (hs & 1);
 #pragma unroll
         for (int j = 0; j < 3; ++j) av[j] = *(const u32x4 *)(act + (aoffs[j] + koff));
     };
@@ -547,18 +408,24 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
     };
     int aoff[4];
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) aoff[s4] = fr * 256 + (((4 * fc + s4) ^ fr) << 4);
+    for (int s4 = 0; s4 < 4; ++s4) aoff[s4] = fr * 256 + (((NAT ? 4 * s4 + fc : 4 * fc + s4) ^ fr) << 4);
 
-    // ---- weight rows of this lane's four column fragments
-    const uint8_t *wb0 = p.w0 + (int64_t)t.g * p.w_expert_bytes;
-    const uint8_t *wb1 = GATEUP ? p.w1 + (int64_t)t.g * p.w_expert_bytes : wb0;
+    // ---- weight rows of this lane's four column fragments (byte offsets
+    // inside one expert's matrix, < 2^32, from per-tile bases)
+    const uint8_t *wb0, *wb1;
+    if (FMT == FMT_BF16) { wb0 = (const uint8_t *)p.s0; wb1 = (const uint8_t *)p.s1; }
+    else {
+        wb0 = p.w0 + (int64_t)t.g * p.w_expert_bytes;
+        wb1 = GATEUP ? p.w1 + (int64_t)t.g * p.w_expert_bytes : wb0;
+    }
     uint32_t wo[4];
 #pragma unroll
     for (int nf = 0; nf < 4; ++nf) {
         int col;
         if (GATEUP) col = t.n0 + wave * 32 + (nf & 1) * 16 + fr;
         else col = t.n0 + wave * 64 + nf * 16 + fr;
-        wo[nf] = (uint32_t)min(col, t.Ng - 1) * (uint32_t)p.w_row_bytes;
+        col = min(col, t.Ng - 1);
+        wo[nf] = FMT == FMT_BF16 ? (uint32_t)col * (uint32_t)t.Kg * 2u + 16u * fc : (uint32_t)col * (uint32_t)p.w_row_bytes;
     }
     auto wrow = [&](int nf) -> const uint8_t * { return (GATEUP && nf >= 2 ? wb1 : wb0) + wo[nf]; };
 
@@ -568,12 +435,29 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    Blk blk[2][4];                                   // [block parity][fragment]
-    a_load(0);
+    Blk blk[2][4];                                   // CB2/Q2_K: [block parity][fragment]
+    RawQ4K r4[2][4];                                 // Q4_K: [half parity][fragment]
+    u32x4 bw[4][4];                                  // bf16: [step mod 4][fragment]
+    const int nks = 8 * nb;
+    auto bw_load = [&](int ks) {
+        const int kc = min(ks, nks - 1);
 #pragma unroll
-    for (int nf = 0; nf < 4; ++nf) {
-        blk_load<FMT>(wrow(nf), 0, 0, fc, blk[0][nf]);
-        blk_load<FMT>(wrow(nf), 0, 1, fc, blk[0][nf]);
+        for (int nf = 0; nf < 4; ++nf) bw[ks & 3][nf] = *(const u32x4 *)(wrow(nf) + 512 * (kc >> 3) + 64 * (kc & 7));
+    };
+    a_load(0);
+    if constexpr (BLK) {
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) {
+            blk_load<FMT>(wrow(nf), 0, 0, fc, blk[0][nf]);
+            blk_load<FMT>(wrow(nf), 0, 1, fc, blk[0][nf]);
+        }
+    } else if constexpr (FMT == FMT_Q4K) {
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) raw_load<FMT_Q4K>(wrow(nf), 0, fc, r4[0][nf]);
+    } else {
+        bw_load(0);
+        bw_load(1);
+        bw_load(2);
     }
     a_store(0);
     __syncthreads();
@@ -588,12 +472,20 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
                 a_load(min(hs + 1, nhs - 1));
                 // keep the weight loads behind this step's activation loads
                 __builtin_amdgcn_sched_barrier(0);
+                if constexpr (BLK) {
 #pragma unroll
-                for (int nf = 0; nf < 4; ++nf) blk_load<FMT>(wrow(nf), min(bb + 1, nb - 1), h, fc, blk[q ^ 1][nf]);
+                    for (int nf = 0; nf < 4; ++nf) blk_load<FMT>(wrow(nf), min(bb + 1, nb - 1), h, fc, blk[q ^ 1][nf]);
+                } else if constexpr (FMT == FMT_Q4K) {
+#pragma unroll
+                    for (int nf = 0; nf < 4; ++nf) raw_load<FMT_Q4K>(wrow(nf), min(hs + 1, nhs - 1), fc, r4[h ^ 1][nf]);
+                }
                 Pool P[4];
                 if constexpr (FMT == FMT_CB2) {
 #pragma unroll
                     for (int nf = 0; nf < 4; ++nf) blk_pool<FMT>(blk[q][nf], h, fc, P[nf]);
+                } else if constexpr (FMT == FMT_Q4K) {
+#pragma unroll
+                    for (int nf = 0; nf < 4; ++nf) pool_prep<FMT_Q4K>(r4[h][nf], h, fc, P[nf]);
                 }
                 const uint8_t *ab = As + h * NP_ABUF;
 #pragma unroll
@@ -609,11 +501,19 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
 #pragma unroll
                     for (int mf = 0; mf < NMF; ++mf) a[mf] = *(const bf16x8 *)(ab + aoff[s4] + mf * 4096);
                     bf16x8 bq[4];
+                    if constexpr (FMT == FMT_BF16) {
+                        const int ks = 8 * bb + 4 * h + s4;
+                        bw_load(ks + 3);                             // ring slot (s4 + 3) & 3
 #pragma unroll
-                    for (int nf = 0; nf < 4; ++nf) {
-                        uint32_t o[4];
-                        blk_frag<FMT>(blk[q][nf], P[nf], h, s4, tab, copy, o);
-                        bq[nf] = __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
+                        for (int nf = 0; nf < 4; ++nf) bq[nf] = __builtin_bit_cast(bf16x8, bw[s4][nf]);
+                    } else {
+#pragma unroll
+                        for (int nf = 0; nf < 4; ++nf) {
+                            uint32_t o[4];
+                            if constexpr (BLK) blk_frag<FMT>(blk[q][nf], P[nf], h, s4, tab, copy, o);
+                            else bfrag<FMT_Q4K>(r4[h][nf], P[nf], s4, tab, copy, o);
+                            bq[nf] = __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
+                        }
                     }
 #pragma unroll
                     for (int mf = 0; mf < NMF; ++mf)
@@ -631,24 +531,13 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
 template <int FMT, bool GATEUP>
 __device__ __forceinline__ void np_dispatch(const FfnPass &p, const NpTile &t, uint8_t *As, const uint32_t *tab)
 {
-    if constexpr (FMT == FMT_CB2 || FMT == FMT_Q2K) {
-        switch ((t.nvalid + 15) >> 4) {
-        case 1: np_body_r<FMT, GATEUP, 1>(p, t, As, tab); break;
-        case 2: np_body_r<FMT, GATEUP, 2>(p, t, As, tab); break;
-        case 3: np_body_r<FMT, GATEUP, 3>(p, t, As, tab); break;
-        case 4: np_body_r<FMT, GATEUP, 4>(p, t, As, tab); break;
-        case 5: np_body_r<FMT, GATEUP, 5>(p, t, As, tab); break;
-        default: np_body_r<FMT, GATEUP, 6>(p, t, As, tab); break;
-        }
-    } else {
-        switch ((t.nvalid + 15) >> 4) {
-        case 1: np_body<FMT, GATEUP, 1>(p, t, As, tab); break;
-        case 2: np_body<FMT, GATEUP, 2>(p, t, As, tab); break;
-        case 3: np_body<FMT, GATEUP, 3>(p, t, As, tab); break;
-        case 4: np_body<FMT, GATEUP, 4>(p, t, As, tab); break;
-        case 5: np_body<FMT, GATEUP, 5>(p, t, As, tab); break;
-        default: np_body<FMT, GATEUP, 6>(p, t, As, tab); break;
-        }
+    switch ((t.nvalid + 15) >> 4) {
+    case 1: np_body_r<FMT, GATEUP, 1>(p, t, As, tab); break;
+    case 2: np_body_r<FMT, GATEUP, 2>(p, t, As, tab); break;
+    case 3: np_body_r<FMT, GATEUP, 3>(p, t, As, tab); break;
+    case 4: np_body_r<FMT, GATEUP, 4>(p, t, As, tab); break;
+    case 5: np_body_r<FMT, GATEUP, 5>(p, t, As, tab); break;
+    default: np_body_r<FMT, GATEUP, 6>(p, t, As, tab); break;
     }
 }
 
@@ -664,7 +553,15 @@ __global__ __launch_bounds__(NP_THREADS) void np_kernel(FfnPass p, int S)
     uint8_t *As = np_smem;
     uint32_t *tab = (uint32_t *)(np_smem + NP_NBUF * NP_ABUF);
     if (t.sh) {
-        np_dispatch<FMT_BF16, GATEUP>(p, t, As, tab);
+        // shared-expert tiles are at most 80 rows: the bf16 weight ring and
+        // six row fragments would not fit the register budget together
+        switch ((t.nvalid + 15) >> 4) {
+        case 1: np_body_r<FMT_BF16, GATEUP, 1>(p, t, As, tab); break;
+        case 2: np_body_r<FMT_BF16, GATEUP, 2>(p, t, As, tab); break;
+        case 3: np_body_r<FMT_BF16, GATEUP, 3>(p, t, As, tab); break;
+        case 4: np_body_r<FMT_BF16, GATEUP, 4>(p, t, As, tab); break;
+        default: np_body_r<FMT_BF16, GATEUP, 5>(p, t, As, tab); break;
+        }
     } else {
         np_build_table<FMT>(p, tab);
         __syncthreads();
@@ -685,7 +582,7 @@ hipError_t np_launch(const FfnPass &p, hipStream_t s)
     }
     const int wg_cols = GATEUP ? 256 : 512;
     const int S = (std::max(p.N, p.Nsh) + wg_cols - 1) / wg_cols;
-    const int tiles = ffn_max_tiles(p.T, p.k, p.E, p.Nsh > 0, NP_BM);
+    const int tiles = ffn_max_tiles(p.T, p.k, p.E, p.Nsh > 0, NP_BM, NP_BM_SH);
     const int64_t grid = (int64_t)((tiles + 7) / 8) * 8 * S;
     np_kernel<FMT, GATEUP><<<dim3((unsigned)grid), NP_THREADS, lds, s>>>(p, S);
     return hipGetLastError();
@@ -697,7 +594,7 @@ bool np_prefill_ok(const FfnPass &p)
 {
     if (p.act_f32) return false;
     if (p.K % (2 * QK) || p.K < 2 * QK) return false;   // routed blocks run in pairs
-    if (p.Nsh > 0 && (p.Ksh % QK || p.Ksh < QK)) return false;
+    if (p.Nsh > 0 && (p.Ksh % (2 * QK) || p.Ksh < 2 * QK)) return false;
     return true;
 }
 
