@@ -36,13 +36,38 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+# sources that define each timed kernel (plus the shared headers)
+_KERNEL_SOURCES = {"dec_": ["decode.hip"], "route_": ["route.hip"], "ffn_prefill_": ["prefill.hip", "ffn.hip"],
+                   "ffn_schedule": ["ffn.hip"], "combine": ["ffn.hip"]}
+
+
+def kernel_source_hash(kernel: str | None = None) -> str:
+    """Hash of the sources of one kernel (all of csrc/ when kernel is None)."""
     h = hashlib.sha1()
     d = os.path.join(ROOT, "bit_quantized_routed_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(d, f), "rb").read())
+    files = sorted(f for f in os.listdir(d) if f.endswith((".hip", ".h")))
+    if kernel is not None:
+        for prefix, own in _KERNEL_SOURCES.items():
+            if kernel.startswith(prefix):
+                files = sorted(own + ["common.h", "kernels.h"])
+                break
+    for f in files:
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:12]
+
+
+def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):
+    """Plain device-to-device copy of known size, for scaling the HBM byte
+    counters (FETCH_SIZE / WRITE_SIZE) taken under rocprofv3."""
+    import torch
+    x = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "reps": reps, "read_bytes_per_copy": nbytes,
+                      "write_bytes_per_copy": nbytes}), flush=True)
 
 
 # ------------------------------------------------------------------ algorithmic work
@@ -228,7 +253,7 @@ def read_traffic(kernel, workload):
     txt = open(path).read()
     m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
     h = re.search(r"kernel_source_hash:\s*(\w+)", txt)
-    if not m or not h or h.group(1) != kernel_source_hash():
+    if not m or not h or h.group(1) != kernel_source_hash(kernel):
         return None
     return float(m.group(1))
 
@@ -243,6 +268,8 @@ def main():
     ap.add_argument("--extra", default="decode32,prefill2048",
                     help="comma-separated extra workloads reported as context ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy 5 times (counter calibration under rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the layer's multi-GPU sharding is a design, not "
@@ -254,6 +281,9 @@ def main():
     import workload as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     cfg = S.config(args.workload)
     decode = args.workload.startswith("decode")
     log("building layer (%s), %d replicas" % (args.workload, args.replicas))
