@@ -271,7 +271,8 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
 
     // prefill: in-register dequantization kernels when every K is a multiple of 256
     const bool np = prefill && np_prefill_ok(up) && np_prefill_ok(dn);
-    const int sched_bm = np ? NP_BM : BM;
+    const bool npd = !prefill && np_decode_ok(up) && np_decode_ok(dn);
+    const int sched_bm = np ? NP_BM : npd ? NP_BM_DEC : BM;
     if (!pr.before("ffn_schedule")) return hip_fail(hipGetLastError(), "event record");
     launch_ffn_schedule(offsets, T, k, E, has_sh, sched_bm, w.sched, s, np ? NP_BM_SH : sched_bm);
     hipError_t e = hipGetLastError();
@@ -281,12 +282,14 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
     const char *nm_up = prefill ? "ffn_prefill_gateup" : "ffn_decode_gateup";
     const char *nm_dn = prefill ? "ffn_prefill_down" : "ffn_decode_down";
     if (!pr.before(nm_up)) return hip_fail(hipGetLastError(), "event record");
-    e = np ? launch_np_prefill(up, true, s) : prefill ? launch_ffn_prefill(up, true, s) : launch_ffn_decode(up, true, s);
+    e = np ? launch_np_prefill(up, true, s) : npd ? launch_np_decode(up, true, s)
+           : prefill ? launch_ffn_prefill(up, true, s) : launch_ffn_decode(up, true, s);
     if (e != hipSuccess) return hip_fail(e, nm_up);
     if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
 
     if (!pr.before(nm_dn)) return hip_fail(hipGetLastError(), "event record");
-    e = np ? launch_np_prefill(dn, false, s) : prefill ? launch_ffn_prefill(dn, false, s) : launch_ffn_decode(dn, false, s);
+    e = np ? launch_np_prefill(dn, false, s) : npd ? launch_np_decode(dn, false, s)
+           : prefill ? launch_ffn_prefill(dn, false, s) : launch_ffn_decode(dn, false, s);
     if (e != hipSuccess) return hip_fail(e, nm_dn);
     if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
 

@@ -103,5 +103,10 @@ constexpr int PRE_BM = 64, PRE_BN = 64;
 constexpr int NP_BM = 96, NP_BM_SH = 80;
 bool np_prefill_ok(const FfnPass &p);
 hipError_t launch_np_prefill(const FfnPass &p, bool gateup, hipStream_t s);
+// the same GEMMs at decode precision (exact weights, fp32 h), tiles of
+// NP_BM_DEC rows, for batched decode (T > 1)
+constexpr int NP_BM_DEC = 32;
+bool np_decode_ok(const FfnPass &p);
+hipError_t launch_np_decode(const FfnPass &p, bool gateup, hipStream_t s);
 
 }  // namespace moe

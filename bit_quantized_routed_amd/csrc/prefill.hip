@@ -74,7 +74,7 @@ struct NpTile {
 // Work-group -> (tile, column slice).  Work-groups are dispatched to the 8
 // XCDs round-robin; tile tau goes to XCD tau % 8 and its S slices run there
 // back to back.  Returns false (uniformly) when the work-group has no work.
-__device__ __forceinline__ bool np_tile(const FfnPass &p, int S, int wg_cols, NpTile &t)
+__device__ __forceinline__ bool np_tile(const FfnPass &p, int S, int wg_cols, int bm, int bm_sh, NpTile &t)
 {
     const int f = blockIdx.x, q = f >> 3;
     const int tau = (q / S) * 8 + (f & 7), slice = q % S;
@@ -91,7 +91,7 @@ __device__ __forceinline__ bool np_tile(const FfnPass &p, int S, int wg_cols, Np
     if (t.sh) { pb = Tk; pe = Tk + p.T; }
     else { pb = min(max(p.offsets[t.g], 0), Tk); pe = min(max(p.offsets[t.g + 1], pb), Tk); }
     t.row0 = pb + m0;
-    t.nvalid = min(t.sh ? NP_BM_SH : NP_BM, pe - t.row0);
+    t.nvalid = min(t.sh ? bm_sh : bm, pe - t.row0);
     return t.nvalid > 0;
 }
 
@@ -183,15 +183,18 @@ __device__ __forceinline__ void raw_load(const uint8_t *row, int hs, int fc, typ
 }
 
 // Per-half-block dequantization state of one lane and fragment.
-struct Pool { uint32_t lo[2], hi[2]; float mul, off; };
+struct Pool { uint32_t lo[2], hi[2], mv[2]; float mul, off; };
 
-template <int FMT>
+// DEC (decode): exact integer codes -- CB2 {+-s, +-3s}, Q2_K {0, sc, 2sc, 3sc}
+// and the sub-block min m as a separate operand -- whose block scales d
+// (and dmin) are applied to each block's fp32 sums.
+template <int FMT, bool DEC = false>
 __device__ __forceinline__ void pool_prep(const typename RawOf<FMT>::T &r, int h, int fc, Pool &P)
 {
     if constexpr (FMT == FMT_CB2) {
         // sub-block 2 fc + h: nibble h of scale byte 2 + fc
         const uint32_t s = (r.sc >> (8 * (fc & 1) + 4 * h)) & 15u;
-        const float ds = f16_bits_to_f32(r.d) * (float)s;        // exact (11 x 4 bits)
+        const float ds = DEC ? (float)s : f16_bits_to_f32(r.d) * (float)s;   // exact (11 x 4 bits)
         P.lo[0] = pk_bf16(ds, 3.0f * ds);
         P.hi[0] = P.lo[0] ^ 0x80008000u;
     } else if constexpr (FMT == FMT_Q2K) {
@@ -261,7 +264,7 @@ __device__ __forceinline__ float np_silu_mul(float g, float u)
 constexpr int NP_ABUF = NP_BM * 256;               // bytes per stage
 constexpr int NP_NBUF = 2;
 
-template <bool GATEUP, int NMF>
+template <bool GATEUP, int NMF, bool DEC>
 __device__ __forceinline__ void np_epilogue(const FfnPass &p, const NpTile &t, const f32x4 (&acc)[NMF][4])
 {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -280,7 +283,8 @@ __device__ __forceinline__ void np_epilogue(const FfnPass &p, const NpTile &t, c
                     const int n = t.n0 + wave * 32 + nf * 16 + fr;
                     if (n < t.Ng) {
                         const float hv = np_silu_mul(acc[mf][nf][v], acc[mf][nf + 2][v]);
-                        ((uint16_t *)p.out)[pos * p.out_stride + n] = (uint16_t)(pk_bf16(hv, 0.f) & 0xffffu);
+                        if (DEC) ((float *)p.out)[pos * p.out_stride + n] = hv;
+                        else ((uint16_t *)p.out)[pos * p.out_stride + n] = (uint16_t)(pk_bf16(hv, 0.f) & 0xffffu);
                     }
                 }
             } else {
@@ -333,25 +337,33 @@ __device__ __forceinline__ void blk_load(const uint8_t *row, int b, int h, int f
     }
 }
 
-template <int FMT>
+template <int FMT, bool DEC>
 __device__ __forceinline__ void blk_pool(const typename BlkOf<FMT>::T &r, int h, int fc, Pool &P)
 {
     if constexpr (FMT == FMT_CB2) {
         RawCB2 x{r.d, r.sc, 0u};
-        pool_prep<FMT_CB2>(x, h, fc, P);
+        pool_prep<FMT_CB2, DEC>(x, h, fc, P);
     } else {
         RawQ2K x{r.dd, r.scw, 0u, 0u};
-        pool_prep<FMT_Q2K>(x, h, fc, P);
+        pool_prep<FMT_Q2K, DEC>(x, h, fc, P);
     }
 }
 
+template <bool DEC>
 __device__ __forceinline__ void q2k_pool(const BlkQ2K &r, int h, int u, Pool &P)
 {
-    const float d = f16_bits_to_f32(r.dd & 0xffffu), dmin = f16_bits_to_f32(r.dd >> 16);
     const uint32_t sm = (r.scw >> (8 * (2 * h + u))) & 0xffu;
-    const float mul = d * (float)(sm & 15u), off = dmin * (float)(sm >> 4);
-    P.lo[u] = pk_bf16(-off, mul - off);
-    P.hi[u] = pk_bf16(2.0f * mul - off, 3.0f * mul - off);
+    if (DEC) {
+        const float sc = (float)(sm & 15u), m = (float)(sm >> 4);
+        P.lo[u] = pk_bf16(0.0f, sc);
+        P.hi[u] = pk_bf16(2.0f * sc, 3.0f * sc);
+        P.mv[u] = pk_bf16(m, m);
+    } else {
+        const float d = f16_bits_to_f32(r.dd & 0xffffu), dmin = f16_bits_to_f32(r.dd >> 16);
+        const float mul = d * (float)(sm & 15u), off = dmin * (float)(sm >> 4);
+        P.lo[u] = pk_bf16(-off, mul - off);
+        P.hi[u] = pk_bf16(2.0f * mul - off, 3.0f * mul - off);
+    }
 }
 
 template <int FMT>
@@ -368,7 +380,9 @@ __device__ __forceinline__ void blk_frag(const typename BlkOf<FMT>::T &r, const 
     }
 }
 
-template <int FMT, bool GATEUP, int NMF>
+// DEC: decode precision (exact weights, see pool_prep); TWO: fp32 activations
+// entered as two bf16 terms (hi, lo), each its own MFMA.
+template <int FMT, bool GATEUP, int NMF, bool DEC, bool TWO>
 __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uint8_t *As, const uint32_t *tab)
 {
     // per-format weight staging: CB2/Q2_K whole blocks (two sets), Q4_K
@@ -386,25 +400,46 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
     const int nhs = 2 * nb;
 
     // ---- activation staging: 16-B chunk ci = tid + 512 j of a stage is row
-    // ci >> 4, physical chunk ci & 15 (logical chunk (ci & 15) ^ (row & 15))
-    uint32_t aoffs[3];
+    // ci >> 4, physical chunk ci & 15 (logical chunk (ci & 15) ^ (row & 15));
+    // fp32 activations are split into hi and lo bf16 stages
+    constexpr int NCH = (DEC ? NP_BM_DEC : NP_BM) * 16 / NP_THREADS;
+    uint32_t aoffs[NCH];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
+    for (int j = 0; j < NCH; ++j) {
         const int ci = tid + NP_THREADS * j, r = ci >> 4;
         const int c = (ci & 15) ^ (r & 15);
         aoffs[j] = (uint32_t)(np_act_row(p, t, min(r, t.nvalid - 1)) * p.act_stride) +
                    (NAT ? 8 * c : 64 * (c >> 2) + 8 * (c & 3));
     }
-    const uint16_t *act = (const uint16_t *)p.act;
-    u32x4 av[3];
+    u32x4 av[NCH], avl[TWO ? NCH : 1];
     auto a_load = [&](int hs) {
         const uint32_t koff = 256 * (hs >> 1) + (NAT ? 128 : 32) * (hs & 1);
 #pragma unroll
-        for (int j = 0; j < 3; ++j) av[j] = *(const u32x4 *)(act + (aoffs[j] + koff));
+        for (int j = 0; j < NCH; ++j) {
+            if constexpr (TWO) {
+                const f32x4 *src = (const f32x4 *)((const float *)p.act + (aoffs[j] + koff));
+                const f32x4 v0 = src[0], v1 = src[1];
+                const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hi[e] = pk_bf16(v[2 * e], v[2 * e + 1]);
+                    lo[e] = pk_bf16(v[2 * e] - __uint_as_float(hi[e] << 16),
+                                    v[2 * e + 1] - __uint_as_float(hi[e] & 0xffff0000u));
+                }
+                av[j] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+                avl[j] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+            } else {
+                av[j] = *(const u32x4 *)((const uint16_t *)p.act + (aoffs[j] + koff));
+            }
+        }
     };
     auto a_store = [&](int buf) {
 #pragma unroll
-        for (int j = 0; j < 3; ++j) *(u32x4 *)(As + buf * NP_ABUF + (tid + NP_THREADS * j) * 16) = av[j];
+        for (int j = 0; j < NCH; ++j) {
+            *(u32x4 *)(As + buf * NP_ABUF + (tid + NP_THREADS * j) * 16) = av[j];
+            if constexpr (TWO) *(u32x4 *)(As + (NP_NBUF + buf) * NP_ABUF + (tid + NP_THREADS * j) * 16) = avl[j];
+        }
     };
     int aoff[4];
 #pragma unroll
@@ -429,11 +464,19 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
     }
     auto wrow = [&](int nf) -> const uint8_t * { return (GATEUP && nf >= 2 ? wb1 : wb0) + wo[nf]; };
 
-    f32x4 acc[NMF][4];
+    // DEC with packed weights: each block's sums (P1: codes, P2: Q2_K min
+    // operand) are scaled by the block's d (and dmin) into acc
+    constexpr bool PBLK = DEC && FMT != FMT_BF16;
+    constexpr bool PMIN = DEC && FMT == FMT_Q2K;
+    f32x4 acc[NMF][4], P1[PBLK ? NMF : 1][4], P2[PMIN ? NMF : 1][4];
 #pragma unroll
     for (int mf = 0; mf < NMF; ++mf)
 #pragma unroll
         for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mf = 0; mf < (PBLK ? NMF : 1); ++mf)
+#pragma unroll
+        for (int nf = 0; nf < 4; ++nf) P1[mf][nf] = P2[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     Blk blk[2][4];                                   // CB2/Q2_K: [block parity][fragment]
     RawQ4K r4[2][4];                                 // Q4_K: [half parity][fragment]
@@ -482,24 +525,27 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
                 Pool P[4];
                 if constexpr (FMT == FMT_CB2) {
 #pragma unroll
-                    for (int nf = 0; nf < 4; ++nf) blk_pool<FMT>(blk[q][nf], h, fc, P[nf]);
+                    for (int nf = 0; nf < 4; ++nf) blk_pool<FMT, DEC>(blk[q][nf], h, fc, P[nf]);
                 } else if constexpr (FMT == FMT_Q4K) {
 #pragma unroll
                     for (int nf = 0; nf < 4; ++nf) pool_prep<FMT_Q4K>(r4[h][nf], h, fc, P[nf]);
                 }
-                const uint8_t *ab = As + h * NP_ABUF;
+                const uint8_t *ab = As + h * NP_ABUF, *abl = As + (NP_NBUF + h) * NP_ABUF;
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4) {
                     if constexpr (FMT == FMT_Q2K) {
                         // the pool of sub-block 4 fc + 2 h + s4 / 2, built when first needed
                         if ((s4 & 1) == 0) {
 #pragma unroll
-                            for (int nf = 0; nf < 4; ++nf) q2k_pool(blk[q][nf], h, s4 >> 1, P[nf]);
+                            for (int nf = 0; nf < 4; ++nf) q2k_pool<DEC>(blk[q][nf], h, s4 >> 1, P[nf]);
                         }
                     }
-                    bf16x8 a[NMF];
+                    bf16x8 a[NMF], al[TWO ? NMF : 1];
 #pragma unroll
-                    for (int mf = 0; mf < NMF; ++mf) a[mf] = *(const bf16x8 *)(ab + aoff[s4] + mf * 4096);
+                    for (int mf = 0; mf < NMF; ++mf) {
+                        a[mf] = *(const bf16x8 *)(ab + aoff[s4] + mf * 4096);
+                        if constexpr (TWO) al[mf] = *(const bf16x8 *)(abl + aoff[s4] + mf * 4096);
+                    }
                     bf16x8 bq[4];
                     if constexpr (FMT == FMT_BF16) {
                         const int ks = 8 * bb + 4 * h + s4;
@@ -518,73 +564,113 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
 #pragma unroll
                     for (int mf = 0; mf < NMF; ++mf)
 #pragma unroll
-                        for (int nf = 0; nf < 4; ++nf) acc[mf][nf] = mfma16x16x32(a[mf], bq[nf], acc[mf][nf]);
+                        for (int nf = 0; nf < 4; ++nf) {
+                            if constexpr (PBLK) {
+                                P1[mf][nf] = mfma16x16x32(a[mf], bq[nf], P1[mf][nf]);
+                                if constexpr (TWO) P1[mf][nf] = mfma16x16x32(al[mf], bq[nf], P1[mf][nf]);
+                                if constexpr (PMIN) {
+                                    const uint32_t mv = P[nf].mv[s4 >> 1];
+                                    const bf16x8 bm = __builtin_bit_cast(bf16x8, u32x4{mv, mv, mv, mv});
+                                    P2[mf][nf] = mfma16x16x32(a[mf], bm, P2[mf][nf]);
+                                    if constexpr (TWO) P2[mf][nf] = mfma16x16x32(al[mf], bm, P2[mf][nf]);
+                                }
+                            } else {
+                                acc[mf][nf] = mfma16x16x32(a[mf], bq[nf], acc[mf][nf]);
+                                if constexpr (TWO) acc[mf][nf] = mfma16x16x32(al[mf], bq[nf], acc[mf][nf]);
+                            }
+                        }
+                }
+                if constexpr (PBLK) {
+                    if (h == 1) {
+                        // block bb done: its sums times this lane's column scales
+#pragma unroll
+                        for (int nf = 0; nf < 4; ++nf) {
+                            float d, dmin = 0.f;
+                            if constexpr (FMT == FMT_CB2) d = f16_bits_to_f32(blk[q][nf].d);
+                            else {
+                                d = f16_bits_to_f32(blk[q][nf].dd & 0xffffu);
+                                dmin = f16_bits_to_f32(blk[q][nf].dd >> 16);
+                            }
+#pragma unroll
+                            for (int mf = 0; mf < NMF; ++mf) {
+                                acc[mf][nf] += d * P1[mf][nf];
+                                if constexpr (PMIN) acc[mf][nf] -= dmin * P2[mf][nf];
+                                P1[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+                                if constexpr (PMIN) P2[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+                            }
+                        }
+                    }
                 }
                 a_store(h ^ 1);
                 __syncthreads();
             }
         }
     }
-    np_epilogue<GATEUP, NMF>(p, t, acc);
+    np_epilogue<GATEUP, NMF, DEC>(p, t, acc);
 }
 
-template <int FMT, bool GATEUP>
+// decode tiles are at most 32 rows (2 fragments), prefill tiles 96 (6)
+template <int FMT, bool GATEUP, bool DEC, bool TWO, int MAXF>
 __device__ __forceinline__ void np_dispatch(const FfnPass &p, const NpTile &t, uint8_t *As, const uint32_t *tab)
 {
-    switch ((t.nvalid + 15) >> 4) {
-    case 1: np_body_r<FMT, GATEUP, 1>(p, t, As, tab); break;
-    case 2: np_body_r<FMT, GATEUP, 2>(p, t, As, tab); break;
-    case 3: np_body_r<FMT, GATEUP, 3>(p, t, As, tab); break;
-    case 4: np_body_r<FMT, GATEUP, 4>(p, t, As, tab); break;
-    case 5: np_body_r<FMT, GATEUP, 5>(p, t, As, tab); break;
-    default: np_body_r<FMT, GATEUP, 6>(p, t, As, tab); break;
+    const int nmf = (t.nvalid + 15) >> 4;
+    if constexpr (MAXF <= 2) {
+        if (nmf <= 1) np_body_r<FMT, GATEUP, 1, DEC, TWO>(p, t, As, tab);
+        else np_body_r<FMT, GATEUP, 2, DEC, TWO>(p, t, As, tab);
+    } else {
+        switch (nmf) {
+        case 1: np_body_r<FMT, GATEUP, 1, DEC, TWO>(p, t, As, tab); break;
+        case 2: np_body_r<FMT, GATEUP, 2, DEC, TWO>(p, t, As, tab); break;
+        case 3: np_body_r<FMT, GATEUP, 3, DEC, TWO>(p, t, As, tab); break;
+        case 4: np_body_r<FMT, GATEUP, 4, DEC, TWO>(p, t, As, tab); break;
+        case 5: np_body_r<FMT, GATEUP, 5, DEC, TWO>(p, t, As, tab); break;
+        default:
+            if constexpr (MAXF >= 6) np_body_r<FMT, GATEUP, 6, DEC, TWO>(p, t, As, tab);
+            else np_body_r<FMT, GATEUP, 5, DEC, TWO>(p, t, As, tab);
+            break;
+        }
     }
 }
 
 template <int FMT> constexpr int np_tab_bytes() { return FMT == FMT_CB2 ? NP_TAB_CB2 : FMT == FMT_Q2K ? NP_TAB_Q2K : 0; }
-template <int FMT> constexpr int np_lds_bytes() { return NP_NBUF * NP_ABUF + np_tab_bytes<FMT>(); }
+template <int FMT, bool TWO> constexpr int np_lds_bytes() { return (TWO ? 2 : 1) * NP_NBUF * NP_ABUF + np_tab_bytes<FMT>(); }
 
-template <int FMT, bool GATEUP>
+template <int FMT, bool GATEUP, bool DEC, bool TWO>
 __global__ __launch_bounds__(NP_THREADS) void np_kernel(FfnPass p, int S)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t np_smem[];
     NpTile t;
-    if (!np_tile(p, S, GATEUP ? 256 : 512, t)) return;
+    if (!np_tile(p, S, GATEUP ? 256 : 512, DEC ? NP_BM_DEC : NP_BM, DEC ? NP_BM_DEC : NP_BM_SH, t)) return;
     uint8_t *As = np_smem;
-    uint32_t *tab = (uint32_t *)(np_smem + NP_NBUF * NP_ABUF);
+    uint32_t *tab = (uint32_t *)(np_smem + (TWO ? 2 : 1) * NP_NBUF * NP_ABUF);
     if (t.sh) {
         // shared-expert tiles are at most 80 rows: the bf16 weight ring and
         // six row fragments would not fit the register budget together
-        switch ((t.nvalid + 15) >> 4) {
-        case 1: np_body_r<FMT_BF16, GATEUP, 1>(p, t, As, tab); break;
-        case 2: np_body_r<FMT_BF16, GATEUP, 2>(p, t, As, tab); break;
-        case 3: np_body_r<FMT_BF16, GATEUP, 3>(p, t, As, tab); break;
-        case 4: np_body_r<FMT_BF16, GATEUP, 4>(p, t, As, tab); break;
-        default: np_body_r<FMT_BF16, GATEUP, 5>(p, t, As, tab); break;
-        }
+        np_dispatch<FMT_BF16, GATEUP, DEC, TWO, DEC ? 2 : 5>(p, t, As, tab);
     } else {
         np_build_table<FMT>(p, tab);
         __syncthreads();
-        np_dispatch<FMT, GATEUP>(p, t, As, tab);
+        np_dispatch<FMT, GATEUP, DEC, TWO, DEC ? 2 : 6>(p, t, As, tab);
     }
 }
 
-template <int FMT, bool GATEUP>
+template <int FMT, bool GATEUP, bool DEC, bool TWO>
 hipError_t np_launch(const FfnPass &p, hipStream_t s)
 {
-    constexpr int lds = np_lds_bytes<FMT>();
+    constexpr int lds = np_lds_bytes<FMT, TWO>();
     static bool attr = false;
     if (!attr) {
-        const hipError_t e = hipFuncSetAttribute((const void *)np_kernel<FMT, GATEUP>,
+        const hipError_t e = hipFuncSetAttribute((const void *)np_kernel<FMT, GATEUP, DEC, TWO>,
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         attr = true;
     }
     const int wg_cols = GATEUP ? 256 : 512;
     const int S = (std::max(p.N, p.Nsh) + wg_cols - 1) / wg_cols;
-    const int tiles = ffn_max_tiles(p.T, p.k, p.E, p.Nsh > 0, NP_BM, NP_BM_SH);
+    const int tiles = DEC ? ffn_max_tiles(p.T, p.k, p.E, p.Nsh > 0, NP_BM_DEC, NP_BM_DEC)
+                          : ffn_max_tiles(p.T, p.k, p.E, p.Nsh > 0, NP_BM, NP_BM_SH);
     const int64_t grid = (int64_t)((tiles + 7) / 8) * 8 * S;
-    np_kernel<FMT, GATEUP><<<dim3((unsigned)grid), NP_THREADS, lds, s>>>(p, S);
+    np_kernel<FMT, GATEUP, DEC, TWO><<<dim3((unsigned)grid), NP_THREADS, lds, s>>>(p, S);
     return hipGetLastError();
 }
 
@@ -602,12 +688,30 @@ hipError_t launch_np_prefill(const FfnPass &p, bool gateup, hipStream_t s)
 {
     if (!np_prefill_ok(p) || p.out_f32 == gateup) return hipErrorInvalidValue;
     if (gateup) {
-        if (p.fmt == FMT_CB2) return np_launch<FMT_CB2, true>(p, s);
-        if (p.fmt == FMT_Q4K) return np_launch<FMT_Q4K, true>(p, s);
+        if (p.fmt == FMT_CB2) return np_launch<FMT_CB2, true, false, false>(p, s);
+        if (p.fmt == FMT_Q4K) return np_launch<FMT_Q4K, true, false, false>(p, s);
     } else {
-        if (p.fmt == FMT_Q2K) return np_launch<FMT_Q2K, false>(p, s);
-        if (p.fmt == FMT_Q4K) return np_launch<FMT_Q4K, false>(p, s);
+        if (p.fmt == FMT_Q2K) return np_launch<FMT_Q2K, false, false, false>(p, s);
+        if (p.fmt == FMT_Q4K) return np_launch<FMT_Q4K, false, false, false>(p, s);
     }
+    return hipErrorInvalidValue;
+}
+
+bool np_decode_ok(const FfnPass &p)
+{
+    if (p.K % (2 * QK) || p.K < 2 * QK) return false;
+    if (p.Nsh > 0 && (p.Ksh % (2 * QK) || p.Ksh < 2 * QK)) return false;
+    return p.out_f32 && (p.fmt == FMT_CB2 || p.fmt == FMT_Q2K);
+}
+
+hipError_t launch_np_decode(const FfnPass &p, bool gateup, hipStream_t s)
+{
+    if (!np_decode_ok(p)) return hipErrorInvalidValue;
+    if (gateup && p.fmt == FMT_CB2) {
+        if (p.act_f32) return np_launch<FMT_CB2, true, true, true>(p, s);
+        return np_launch<FMT_CB2, true, true, false>(p, s);
+    }
+    if (!gateup && p.fmt == FMT_Q2K && p.act_f32) return np_launch<FMT_Q2K, false, true, true>(p, s);
     return hipErrorInvalidValue;
 }
 

@@ -105,6 +105,10 @@ SMALL = [
     ("one_T1_f32x", mid(1, 23, hidden=1024, inter=512, sh_inter=512, x_dtype="f32")),
     ("one_T1_noshared", mid(1, 24, hidden=1024, inter=768, sh_inter=0)),
     ("one_T1_k16", mid(1, 25, hidden=512, inter=256, sh_inter=512, n_experts=32, top_k=16)),
+    # batched decode through the grouped GEMMs (every K a multiple of 512)
+    ("gemm_T37", mid(37, 26, hidden=1024, inter=512, sh_inter=512)),
+    ("gemm_T20_f32x", mid(20, 27, hidden=1024, inter=512, sh_inter=512, x_dtype="f32")),
+    ("gemm_T9_noshared", mid(9, 28, hidden=1024, inter=512, sh_inter=0)),
 ]
 
 
@@ -224,6 +228,21 @@ def test_decode_batch_invariance():
         M.route(wl.layer, xt, act, 1, wl.bias(cfg), r1, wl.layer.workspace(1, M.PATH_ROUTE))
         y1 = run_ffn(wl, xt, act, r1, decode=True)
         assert np.array_equal(y1[0].view(np.uint32), yb[t].view(np.uint32)), t
+
+
+def test_decode_batch_invariance_gemm():
+    """The same for the grouped-GEMM decode path (T >= 2): a token's output
+    does not depend on which other tokens share its call or its row tiles."""
+    cfg = mid(24, 29, hidden=1024, inter=512, sh_inter=512, skew=True)
+    wl = W.Workload(cfg)
+    x, act, r = run_route(wl, cfg)
+    yb = run_ffn(wl, x, act, r, decode=True)
+    for t in (0, 5, 22):
+        xt = x[t:t + 2].contiguous()
+        r2 = M.Routing(2, cfg["top_k"], cfg["n_experts"])
+        M.route(wl.layer, xt, act, 2, wl.bias(cfg), r2, wl.layer.workspace(2, M.PATH_ROUTE))
+        y2 = run_ffn(wl, xt, act, r2, decode=True)
+        assert np.array_equal(y2.view(np.uint32), yb[t:t + 2].view(np.uint32)), t
 
 
 # ------------------------------------------------------------------ full-size workloads
