@@ -127,6 +127,8 @@ struct FfnWs {
     // single-token decode
     bool single;
     float *part_sh, *O_sh;
+    float *sh_part;                   // batched decode: shared-expert K-part partial sums
+    int ks_gu, ks_dn;                 // its K parts for gate/up and down (0: not split)
     uint16_t *h_hi, *h_lo;
     float *X;
 };
@@ -167,8 +169,19 @@ FfnWs ffn_ws(const moe_layer *L, int T, bool prefill, bool single, char *base)
         w.bytes = off;
         return w;
     }
+    // batched decode splits the shared expert over K in parts of 512
+    if (!prefill && has_sh) {
+        w.ks_gu = std::max(1, L->hidden / 512);
+        w.ks_dn = std::max(1, L->sh_inter / 512);
+    }
+    int tiles = ffn_max_tiles(T, L->top_k, L->n_experts, has_sh, BM);
+    if (!prefill)
+        tiles = std::max(tiles, ffn_max_tiles(T, L->top_k, L->n_experts, has_sh, NP_BM_DEC, NP_BM_DEC,
+                                              std::max(w.ks_gu, w.ks_dn)));
     w.sched = (int32_t *)(base + off);
-    off = align_up(off + (1 + 2 * (size_t)ffn_max_tiles(T, L->top_k, L->n_experts, has_sh, BM)) * sizeof(int32_t));
+    off = align_up(off + (1 + 2 * (size_t)tiles) * sizeof(int32_t));
+    w.sh_part = (float *)(base + off);
+    off = align_up(off + std::max((size_t)w.ks_gu * 2 * T * L->sh_inter, (size_t)w.ks_dn * T * L->hidden) * sizeof(float));
     w.h = base + off;
     off = align_up(off + rows * w.hstride * (prefill ? 2 : 4));
     w.O = (float *)(base + off);
@@ -273,8 +286,16 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
     const bool np = prefill && np_prefill_ok(up) && np_prefill_ok(dn);
     const bool npd = !prefill && np_decode_ok(up) && np_decode_ok(dn);
     const int sched_bm = np ? NP_BM : npd ? NP_BM_DEC : BM;
+    // batched decode: the shared expert's few rows are spread over K parts so
+    // that its work-groups stream no more than a routed tile's
+    const bool split = npd && has_sh && H % 512 == 0 && Ish % 512 == 0;
+    if (split) {
+        up.sh_parts = w.ks_gu; up.sh_part_out = w.sh_part;
+        dn.sh_parts = w.ks_dn; dn.sh_part_out = w.sh_part;
+    }
     if (!pr.before("ffn_schedule")) return hip_fail(hipGetLastError(), "event record");
-    launch_ffn_schedule(offsets, T, k, E, has_sh, sched_bm, w.sched, s, np ? NP_BM_SH : sched_bm);
+    launch_ffn_schedule(offsets, T, k, E, has_sh, sched_bm, w.sched, s, np ? NP_BM_SH : sched_bm,
+                        split ? std::max(w.ks_gu, w.ks_dn) : 1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "ffn_schedule launch");
     if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
@@ -286,6 +307,13 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
            : prefill ? launch_ffn_prefill(up, true, s) : launch_ffn_decode(up, true, s);
     if (e != hipSuccess) return hip_fail(e, nm_up);
     if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+    if (split) {
+        if (!pr.before("sh_finalize")) return hip_fail(hipGetLastError(), "event record");
+        launch_sh_finalize(w.sh_part, w.ks_gu, T, Ish, T * k, nullptr, (float *)w.h, w.hstride, s);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "sh_finalize launch");
+        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+    }
 
     if (!pr.before(nm_dn)) return hip_fail(hipGetLastError(), "event record");
     e = np ? launch_np_prefill(dn, false, s) : npd ? launch_np_decode(dn, false, s)
@@ -294,7 +322,8 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
     if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
 
     if (!pr.before("combine")) return hip_fail(hipGetLastError(), "event record");
-    launch_combine(w.O, inv, topk_w, T, k, H, has_sh, y, s);
+    launch_combine(w.O, inv, topk_w, T, k, H, has_sh ? (split ? w.ks_dn : 1) : 0,
+                   split ? w.sh_part : w.O + (size_t)T * k * H, y, s);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     if (!pr.after()) return hip_fail(hipGetLastError(), "event record");

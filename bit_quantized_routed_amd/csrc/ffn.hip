@@ -22,17 +22,17 @@
 namespace moe {
 
 // ============================================================== schedule
-int ffn_max_tiles(int T, int k, int E, int has_shared, int BM, int BMsh)
+int ffn_max_tiles(int T, int k, int E, int has_shared, int BM, int BMsh, int KSsh)
 {
     if (BMsh <= 0) BMsh = BM;
     const int64_t tk = (int64_t)T * k;
     const int64_t routed = (tk + BM - 1) / BM + std::min<int64_t>(E, tk);
-    const int64_t sh = has_shared ? (T + BMsh - 1) / BMsh : 0;
+    const int64_t sh = has_shared ? (int64_t)((T + BMsh - 1) / BMsh) * std::max(KSsh, 1) : 0;
     return (int)(routed + sh);
 }
 
 __global__ __launch_bounds__(1024) void ffn_schedule(const int32_t *offsets, int T, int k, int E, int has_shared,
-                                                     int BM, int BMsh, int max_tiles, int32_t *sched)
+                                                     int BM, int BMsh, int KSsh, int max_tiles, int32_t *sched)
 {
     __shared__ int32_t part[1024];
     const int tid = threadIdx.x;
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(1024) void ffn_schedule(const int32_t *offsets, int
             const int Tk = T * k;
             const int n = g == E ? T : min(max(offsets[g + 1], 0), Tk) - min(max(offsets[g], 0), Tk);
             const int bm = g == E ? BMsh : BM;
-            cnt[i] = n > 0 ? (n + bm - 1) / bm : 0;
+            cnt[i] = n > 0 ? ((n + bm - 1) / bm) * (g == E ? KSsh : 1) : 0;
             mine += cnt[i];
         }
     }
@@ -65,10 +65,11 @@ __global__ __launch_bounds__(1024) void ffn_schedule(const int32_t *offsets, int
         const int o = tid * per + i;
         if (o < G) {
             const int g = has_shared ? (o == 0 ? E : o - 1) : o;
-            const int bm = g == E ? BMsh : BM;
+            const int bm = g == E ? BMsh : BM, ks = g == E ? KSsh : 1;
+            // shared K parts of one row tile are consecutive: group id E + part
             for (int c = 0; c < cnt[i] && start + c < max_tiles; ++c) {
-                sched[1 + 2 * (start + c)] = g;
-                sched[2 + 2 * (start + c)] = c * bm;
+                sched[1 + 2 * (start + c)] = g + c % ks;
+                sched[2 + 2 * (start + c)] = (c / ks) * bm;
             }
             start += cnt[i];
         }
@@ -77,11 +78,38 @@ __global__ __launch_bounds__(1024) void ffn_schedule(const int32_t *offsets, int
 }
 
 void launch_ffn_schedule(const int32_t *offsets, int T, int k, int E, int has_shared, int BM, int32_t *sched,
-                         hipStream_t s, int BMsh)
+                         hipStream_t s, int BMsh, int KSsh)
 {
     if (BMsh <= 0) BMsh = BM;
-    ffn_schedule<<<1, 1024, 0, s>>>(offsets, T, k, E, has_shared, BM, BMsh, ffn_max_tiles(T, k, E, has_shared, BM, BMsh),
-                                    sched);
+    KSsh = std::max(KSsh, 1);
+    ffn_schedule<<<1, 1024, 0, s>>>(offsets, T, k, E, has_shared, BM, BMsh, KSsh,
+                                    ffn_max_tiles(T, k, E, has_shared, BM, BMsh, KSsh), sched);
+}
+
+// h of the shared rows (positions Tk + t) from the K-part partial sums of g
+// and u, added in part order
+__global__ __launch_bounds__(256) void sh_finalize_kernel(const float *part, int KS, int T, int I, int Tk,
+                                                          uint16_t *h_bf16, float *h_f32, int hstride)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)T * I) return;
+    const int t = (int)(i / I), n = (int)(i % I);
+    float g = 0.f, u = 0.f;
+    for (int q = 0; q < KS; ++q) {
+        g += part[(((int64_t)q * 2 + 0) * T + t) * I + n];
+        u += part[(((int64_t)q * 2 + 1) * T + t) * I + n];
+    }
+    const float h = g / (1.0f + expf(-g)) * u;
+    const int64_t o = (int64_t)(Tk + t) * hstride + n;
+    if (h_f32) h_f32[o] = h;
+    else h_bf16[o] = (uint16_t)f32_to_bf16_rne(h);
+}
+
+void launch_sh_finalize(const float *part, int KS, int T, int I, int Tk, uint16_t *h_bf16, float *h_f32, int hstride,
+                        hipStream_t s)
+{
+    const int64_t n = (int64_t)T * I;
+    sh_finalize_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, KS, T, I, Tk, h_bf16, h_f32, hstride);
 }
 
 // ============================================================== tile helpers
@@ -502,16 +530,18 @@ hipError_t launch_ffn_prefill(const FfnPass &p, bool gateup, hipStream_t s)
 }
 
 // ============================================================== combine
-// y[t] = O[shared row of t] + sum_{j<k} w[t,j] * O[inv[t*k+j]], j in top-k
-// order; fp32, four features per thread.  Atomic-free: each output element is
-// written by exactly one thread.
+// y[t] = shared(t) + sum_{j<k} w[t,j] * O[inv[t*k+j]], j in top-k order, with
+// shared(t) = sum_q sh[q][t] over the shared expert's K parts in order (one
+// part: its O rows); fp32, four features per thread.  Atomic-free: each
+// output element is written by exactly one thread.
 __global__ __launch_bounds__(256) void combine_kernel(const float *O, const int32_t *inv, const float *topk_w,
-                                                      int T, int k, int H, int has_shared, float *y)
+                                                      int T, int k, int H, int sh_parts, const float *sh, float *y)
 {
     const int t = blockIdx.x;
     const int Tk = T * k;
     for (int n = 4 * threadIdx.x; n < H; n += 4 * 256) {
-        f32x4 acc = has_shared ? *(const f32x4 *)&O[(int64_t)(Tk + t) * H + n] : f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < sh_parts; ++q) acc += *(const f32x4 *)&sh[((int64_t)q * T + t) * H + n];
         for (int j = 0; j < k; ++j) {
             const float w = topk_w[t * k + j];
             const int pos = min(max(inv[t * k + j], 0), Tk - 1);
@@ -522,10 +552,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *O, const int3
     }
 }
 
-void launch_combine(const float *O, const int32_t *inv, const float *topk_w, int T, int k, int H, int has_shared,
-                    float *y, hipStream_t s)
+void launch_combine(const float *O, const int32_t *inv, const float *topk_w, int T, int k, int H, int sh_parts,
+                    const float *sh, float *y, hipStream_t s)
 {
-    combine_kernel<<<T, 256, 0, s>>>(O, inv, topk_w, T, k, H, has_shared, y);
+    combine_kernel<<<T, 256, 0, s>>>(O, inv, topk_w, T, k, H, sh_parts, sh, y);
 }
 
 // ============================================================== unpack

@@ -43,18 +43,29 @@ struct FfnPass {
     int out_f32;                      // 1: fp32 output, 0: bf16 (RNE)
     int64_t out_stride;               // elements per output row
     const int32_t *sched;             // [0] = tile count, then (group, m0) pairs
+    // shared expert split over K (batched decode): tiles of group E + q take
+    // K part q of sh_parts; with sh_part_out set they write fp32 partial sums
+    // there (gate/up: [q][2][T][Nsh] g and u; down: [q][T][Nsh]) instead of out
+    int sh_parts;                     // 0 or 1: one part
+    float *sh_part_out;               // null: shared rows go to out like the others
 };
 
-// tiles of BM rows per routed group and BMsh (<= 0: BM) for the shared group
-int ffn_max_tiles(int T, int k, int E, int has_shared, int BM, int BMsh = 0);
+// tiles of BM rows per routed group and BMsh (<= 0: BM) for the shared group,
+// each shared row tile repeated for KSsh K parts (group ids E .. E+KSsh-1)
+int ffn_max_tiles(int T, int k, int E, int has_shared, int BM, int BMsh = 0, int KSsh = 1);
 void launch_ffn_schedule(const int32_t *offsets, int T, int k, int E, int has_shared, int BM,
-                         int32_t *sched, hipStream_t s, int BMsh = 0);
+                         int32_t *sched, hipStream_t s, int BMsh = 0, int KSsh = 1);
+// h of the shared rows from K-part partial sums: silu(sum g) * sum u
+void launch_sh_finalize(const float *part, int KS, int T, int I, int Tk, uint16_t *h_bf16, float *h_f32, int hstride,
+                        hipStream_t s);
 // decode (exact codes, fp32 accumulation); returns hipSuccess or an error
 hipError_t launch_ffn_decode(const FfnPass &p, bool gateup, hipStream_t s);
 // prefill (bf16-rounded weights, bf16 MFMA)
 hipError_t launch_ffn_prefill(const FfnPass &p, bool gateup, hipStream_t s);
+// sh_parts > 0: the shared expert's output is the sum of sh_parts slices
+// [q][T][H] at sh (fixed order); 0: no shared expert
 void launch_combine(const float *O, const int32_t *inv, const float *topk_w, int T, int k, int H,
-                    int has_shared, float *y, hipStream_t s);
+                    int sh_parts, const float *sh, float *y, hipStream_t s);
 hipError_t launch_unpack(int fmt, const uint8_t *packed, int64_t rows, int K, const int8_t *codebook,
                          float *out, hipStream_t s);
 

@@ -68,6 +68,7 @@ __device__ __forceinline__ float ubyte(uint32_t v, int i) { return (float)((v >>
 
 struct NpTile {
     int g, row0, nvalid, Ng, Kg, n0;
+    int part, k0, Kfull;              // shared expert: K part, its first K, full K
     bool sh;
 };
 
@@ -81,9 +82,14 @@ __device__ __forceinline__ bool np_tile(const FfnPass &p, int S, int wg_cols, in
     if (tau >= p.sched[0]) return false;
     t.g = p.sched[1 + 2 * tau];
     const int m0 = p.sched[2 + 2 * tau];
-    t.sh = t.g == p.E;
+    t.sh = t.g >= p.E;                              // shared expert, K part g - E
+    const int ks = max(p.sh_parts, 1);
+    t.part = t.sh ? t.g - p.E : 0;
+    if (t.part >= ks) return false;                 // a part of the other pass
     t.Ng = t.sh ? p.Nsh : p.N;
-    t.Kg = t.sh ? p.Ksh : p.K;
+    t.Kfull = t.sh ? p.Ksh : p.K;
+    t.Kg = t.sh ? p.Ksh / ks : p.K;
+    t.k0 = t.part * t.Kg;
     t.n0 = slice * wg_cols;
     if (t.n0 >= t.Ng) return false;
     const int Tk = p.T * p.k;
@@ -270,6 +276,33 @@ __device__ __forceinline__ void np_epilogue(const FfnPass &p, const NpTile &t, c
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int fr = lane & 15, fc = lane >> 4;
     // D lane (fr, fc) holds rows 4 fc + v of column fr
+    if (t.sh && p.sh_part_out) {
+        // one K part of the shared expert: fp32 partial sums (gate/up: g and
+        // u, SwiGLU after all parts are added)
+        const int Tk = p.T * p.k;
+#pragma unroll
+        for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int i = mf * 16 + 4 * fc + v;
+                if (i >= t.nvalid) continue;
+                const int64_t tt = t.row0 + i - Tk;
+#pragma unroll
+                for (int nf = 0; nf < 4; ++nf) {
+                    int n;
+                    int64_t o;
+                    if (GATEUP) {
+                        n = t.n0 + wave * 32 + (nf & 1) * 16 + fr;
+                        o = (((int64_t)t.part * 2 + (nf >> 1)) * p.T + tt) * t.Ng + n;
+                    } else {
+                        n = t.n0 + wave * 64 + nf * 16 + fr;
+                        o = ((int64_t)t.part * p.T + tt) * t.Ng + n;
+                    }
+                    if (n < t.Ng) p.sh_part_out[o] = acc[mf][nf][v];
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int mf = 0; mf < NMF; ++mf) {
 #pragma unroll
@@ -408,7 +441,7 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
     for (int j = 0; j < NCH; ++j) {
         const int ci = tid + NP_THREADS * j, r = ci >> 4;
         const int c = (ci & 15) ^ (r & 15);
-        aoffs[j] = (uint32_t)(np_act_row(p, t, min(r, t.nvalid - 1)) * p.act_stride) +
+        aoffs[j] = (uint32_t)(np_act_row(p, t, min(r, t.nvalid - 1)) * p.act_stride) + t.k0 +
                    (NAT ? 8 * c : 64 * (c >> 2) + 8 * (c & 3));
     }
     u32x4 av[NCH], avl[TWO ? NCH : 1];
@@ -460,7 +493,8 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
         if (GATEUP) col = t.n0 + wave * 32 + (nf & 1) * 16 + fr;
         else col = t.n0 + wave * 64 + nf * 16 + fr;
         col = min(col, t.Ng - 1);
-        wo[nf] = FMT == FMT_BF16 ? (uint32_t)col * (uint32_t)t.Kg * 2u + 16u * fc : (uint32_t)col * (uint32_t)p.w_row_bytes;
+        wo[nf] = FMT == FMT_BF16 ? (uint32_t)col * (uint32_t)t.Kfull * 2u + 2u * t.k0 + 16u * fc
+                                 : (uint32_t)col * (uint32_t)p.w_row_bytes;
     }
     auto wrow = [&](int nf) -> const uint8_t * { return (GATEUP && nf >= 2 ? wb1 : wb0) + wo[nf]; };
 
