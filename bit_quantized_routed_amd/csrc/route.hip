@@ -628,11 +628,11 @@ __device__ __forceinline__ void wave_argmax(double &bv, int &be)
 // selection sorted by expert id: offsets come from ballots of the taken
 // flags, and the position of slot j is the number of selected ids below its
 // own.  No LDS, no barriers.
+template <int MAXPL>                              // experts per lane: E <= 64 * MAXPL
 __global__ __launch_bounds__(64) void route_select_one(const double *part, const float *bias, int E, int k, int NC,
                                                        int32_t *topk_idx, float *topk_w, int32_t *offsets,
                                                        int32_t *perm, int32_t *inv)
 {
-    constexpr int MAXPL = 16;                     // E <= 1024
     const int lane = threadIdx.x;
     double v[MAXPL];
 #pragma unroll
@@ -751,7 +751,11 @@ void launch_route_select(const double *part, const float *bias, int T, int H, in
 {
     const int NC = route_decode_chunks(T, H);
     if (T == 1) {
-        route_select_one<<<1, 64, 0, s>>>(part, bias, E, k, NC, topk_idx, topk_w, offsets, perm, inv);
+        if (E <= 64) route_select_one<1><<<1, 64, 0, s>>>(part, bias, E, k, NC, topk_idx, topk_w, offsets, perm, inv);
+        else if (E <= 128) route_select_one<2><<<1, 64, 0, s>>>(part, bias, E, k, NC, topk_idx, topk_w, offsets, perm, inv);
+        else if (E <= 256) route_select_one<4><<<1, 64, 0, s>>>(part, bias, E, k, NC, topk_idx, topk_w, offsets, perm, inv);
+        else if (E <= 512) route_select_one<8><<<1, 64, 0, s>>>(part, bias, E, k, NC, topk_idx, topk_w, offsets, perm, inv);
+        else route_select_one<16><<<1, 64, 0, s>>>(part, bias, E, k, NC, topk_idx, topk_w, offsets, perm, inv);
     } else {
         route_select_tok<<<T, 256, 0, s>>>(part, bias, T, E, k, NC, topk_idx, topk_w);
         route_group_small<<<1, 256, 0, s>>>(topk_idx, T, E, k, offsets, perm, inv);
