@@ -82,6 +82,9 @@ int check_layer(const moe_layer *L)
         return fail(MOE_ERR_INVALID_ARG, "fmt_down=%d must be Q2K or Q4K", L->fmt_down);
     if (!L->w_gate || !L->w_up || !L->w_down) return fail(MOE_ERR_INVALID_ARG, "routed expert weights are NULL");
     if (L->fmt_gate_up == MOE_FMT_CB2 && !L->codebook) return fail(MOE_ERR_INVALID_ARG, "CB2 needs a codebook");
+    for (const void *ptr : {L->w_gate, L->w_up, L->w_down, (const void *)L->codebook, L->sh_gate, L->sh_up,
+                            L->sh_down, (const void *)L->w_router})
+        if ((uintptr_t)ptr % 16) return fail(MOE_ERR_INVALID_ARG, "layer pointer %p is not 16-byte aligned", ptr);
     if (L->sh_inter < 0) return fail(MOE_ERR_INVALID_ARG, "sh_inter=%d < 0", L->sh_inter);
     if (L->sh_inter > 0) {
         if (!L->sh_gate || !L->sh_up || !L->sh_down) return fail(MOE_ERR_INVALID_ARG, "shared expert weights are NULL");

@@ -48,7 +48,11 @@ constexpr int DN_ROWS = 128;       // output rows of a down unit (16 per wave)
 constexpr int DN_KPART = 512;      // K part of a shared down unit
 constexpr int DN_MAXB = 8;         // Q2_K blocks per row of a routed down unit (I <= 2048)
 constexpr int DN_STAGE = 4;        // h staging slots per thread: k * (I/256) * 32 <= 512 * 4
-constexpr int CB_COPIES = 8;       // interleaved codebook copies in LDS (no bank conflicts)
+// Interleaved codebook copies in LDS: lane l reads copy l % copies, so the
+// lanes the LDS serves together for a 16-byte read hit distinct bank groups
+// whatever entries they look up (sixteen copies measured faster than eight;
+// fp32 x leaves room for eight only).
+__host__ __device__ constexpr int cb_copies(bool xf32) { return xf32 ? 8 : 16; }
 constexpr size_t LDS_MAX = 160 * 1024;
 
 __device__ __forceinline__ void split_bf16(float v, uint32_t &hi, uint32_t &lo)
@@ -101,8 +105,9 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_gateup_kernel(DecPass p)
     uint16_t *xh = (uint16_t *)dsm;                               // [H]
     uint16_t *xl = xh + H;                                        // [H] (fp32 x only)
     float *red = (float *)(dsm + (XF32 ? 4 : 2) * (size_t)H);     // [8 waves][2][16]
-    uint16_t *cbt = (uint16_t *)(red + 256);                      // [256][8 copies][8] bf16 codewords
-    uint8_t *wt = (uint8_t *)(cbt + 256 * CB_COPIES * 8);         // [2][32][rb]
+    constexpr int NCOP = cb_copies(XF32);
+    uint16_t *cbt = (uint16_t *)(red + 256);                      // [256][NCOP copies][8] bf16 codewords
+    uint8_t *wt = (uint8_t *)(cbt + 256 * NCOP * 8);              // [2][32][rb]
 
     const bool shared_role = (int)blockIdx.x < p.gu_sh_wg;
     const int n_units = shared_role ? (p.Ish / 16) * SH_KQ : p.k * (p.I / GU_ROWS);
@@ -195,13 +200,15 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_gateup_kernel(DecPass p)
     const int rb = p.gu_row_bytes;
     const int n32 = 2 * rb;                                       // u32x4 per 32-row tile of one matrix
     if (tid < p.k) kid[tid] = clamp_expert(p.topk_idx[tid], p.E);
-    // the codebook is held in CB_COPIES interleaved copies (entry e, copy c at
-    // 16 * (e * CB_COPIES + c) bytes); lane l reads copy l % CB_COPIES, so the
-    // eight lanes the LDS serves together always hit eight different bank
-    // groups, whatever entries they look up
-    for (int i = tid; i < 256 * CB_COPIES * 8; i += D1_THREADS) {
-        const int e = i / (CB_COPIES * 8), v = i % 8;
-        cbt[i] = (uint16_t)f32_to_bf16_exact((float)p.codebook[8 * e + v]);
+    // the codebook in NCOP interleaved copies: entry e, copy c at
+    // 16 * (e * NCOP + c) bytes (one 8-byte load per entry and copy)
+    for (int i = tid; i < 256 * NCOP; i += D1_THREADS) {
+        const int e = i / NCOP;
+        const uint64_t cw = *(const uint64_t *)(p.codebook + 8 * e);
+        uint32_t h[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) h[v] = f32_to_bf16_exact((float)(int8_t)(cw >> (8 * v)));
+        *(u32x4 *)&cbt[8 * i] = pack8(h);
     }
     __syncthreads();                                              // x, codebook, expert ids staged
     // one register buffer: the next unit is in flight while this one is
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_gateup_kernel(DecPass p)
     };
     const int nbH = rb / 38;
     const int half = wave >> 2, kq = wave & 3;
-    const int cbc = lane % CB_COPIES;                             // this lane's codebook copy
+    const int cbc = lane % NCOP;                                  // this lane's codebook copy
     const uint16_t *xa = XF32 && (fr & 1) ? xl : xh;             // this lane's A row (rows 0, 1 used)
     const int b0 = (nbH * kq) / 4, b1 = (nbH * (kq + 1)) / 4;
     const uint8_t *rowg = wt + (16 * half + fr) * rb, *rowu = wt + (GU_ROWS + 16 * half + fr) * rb;
@@ -241,20 +248,33 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_gateup_kernel(DecPass p)
         bf16x8 Bg[8], Bu[8];
 #pragma unroll
         for (int sb = 0; sb < 8; ++sb) {
-            Bg[sb] = *(const bf16x8 *)&cbt[8 * (h.ig[sb] * CB_COPIES + cbc)];
-            Bu[sb] = *(const bf16x8 *)&cbt[8 * (h.iu[sb] * CB_COPIES + cbc)];
+            // index bytes are below 256 (the loads zero-extend; the loop-carried
+            // copies lose that fact, and the mask it would cost is per lookup)
+            __builtin_assume((unsigned)h.ig[sb] < 256u && (unsigned)h.iu[sb] < 256u);
+            Bg[sb] = *(const bf16x8 *)&cbt[8 * (h.ig[sb] * NCOP + cbc)];
+            Bu[sb] = *(const bf16x8 *)&cbt[8 * (h.iu[sb] * NCOP + cbc)];
         }
         bf16x8 a[8];
         act_block<XF32>(xa, 256 * b + 8 * fc, 32, fr, a);
-        const float dg = f16_bits_to_f32(h.dg), du = f16_bits_to_f32(h.du);
+        // the eight 4-bit sub-block scales spread over bytes: even sub-blocks
+        // in one word, odd ones in another, each byte converted by one
+        // instruction
+        const uint32_t sge = h.sg & 0x0F0F0F0Fu, sgo = (h.sg >> 4) & 0x0F0F0F0Fu;
+        const uint32_t sue = h.su & 0x0F0F0F0Fu, suo = (h.su >> 4) & 0x0F0F0F0Fu;
+        float bg = 0.f, bu = 0.f;
 #pragma unroll
         for (int sb = 0; sb < 8; ++sb) {
             const f32x4 Pg = mfma16x16x32(a[sb], Bg[sb], f32x4{0.f, 0.f, 0.f, 0.f});
             const f32x4 Pu = mfma16x16x32(a[sb], Bu[sb], f32x4{0.f, 0.f, 0.f, 0.f});
             // column fr is feature r0+16*half+fr, whose block and sub-block scale this lane read
-            acc_g += (dg * (float)((h.sg >> (4 * sb)) & 15)) * (XF32 ? Pg[0] + Pg[1] : Pg[0]);
-            acc_u += (du * (float)((h.su >> (4 * sb)) & 15)) * (XF32 ? Pu[0] + Pu[1] : Pu[0]);
+            const float sg = (float)(((sb & 1 ? sgo : sge) >> (8 * (sb >> 1))) & 0xffu);
+            const float su = (float)(((sb & 1 ? suo : sue) >> (8 * (sb >> 1))) & 0xffu);
+            bg += sg * (XF32 ? Pg[0] + Pg[1] : Pg[0]);
+            bu += su * (XF32 ? Pu[0] + Pu[1] : Pu[0]);
         }
+        // the block scale d once per block
+        acc_g += f16_bits_to_f32(h.dg) * bg;
+        acc_u += f16_bits_to_f32(h.du) * bu;
     };
     load(u);
     for (;;) {
@@ -534,7 +554,8 @@ int cu_count()
 
 size_t lds_gateup(int H, int gu_row_bytes, bool xf32)
 {
-    return (size_t)(xf32 ? 4 : 2) * H + 256 * sizeof(float) + 256 * CB_COPIES * 16 + 2 * GU_ROWS * (size_t)gu_row_bytes;
+    return (size_t)(xf32 ? 4 : 2) * H + 256 * sizeof(float) + 256 * cb_copies(xf32) * 16 +
+           2 * GU_ROWS * (size_t)gu_row_bytes;
 }
 
 size_t lds_down(int nbI, int k) { return 16 * 256 * 4 * 2 + (size_t)k * (2 * (size_t)nbI * 256 * 2 + (size_t)nbI * 32 * 2); }
@@ -578,7 +599,7 @@ void split_roles(int n_a, double c_a, int n_b, double c_b, int G, int &g_a, int 
 // table reads (16 bytes per 1.19 bytes of weights), a Q2_K unit by its LDS
 // table reads and VALU work.  The role split gives each role work in
 // proportion to these costs.
-constexpr double CB2_COST = 3.1;
+constexpr double CB2_COST = 2.9;
 constexpr double Q2K_COST = 1.55;
 
 }  // namespace

@@ -90,7 +90,9 @@ enum moe_path { MOE_PATH_ROUTE = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 };
  *   sh_inter: intermediate size of the bf16 shared expert, 0 if there is none
  *     (then sh_* are ignored); sh_gate, sh_up: [sh_inter][H] bf16; sh_down:
  *     [H][sh_inter] bf16; sh_inter % 256 == 0 and H % 256 == 0 when present.
- *   w_router: fp32 [E][H]. */
+ *   w_router: fp32 [E][H].
+ *   Every pointer must be 16-byte aligned (device allocations are); the
+ *   kernels read weights and the codebook in 8- and 16-byte pieces. */
 typedef struct moe_layer {
     int32_t hidden, inter, n_experts, top_k;
     int32_t fmt_gate_up, fmt_down;
