@@ -214,6 +214,8 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
     if ((int64_t)T * L->top_k > (1 << 30)) return fail(MOE_ERR_INVALID_ARG, "T*k too large");
     if (!x || !topk_idx || !topk_w || !offsets || !perm || !inv || !y) return fail(MOE_ERR_INVALID_ARG, "NULL tensor argument");
     if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+    if ((uintptr_t)x % 16 || (uintptr_t)y % 16 || (uintptr_t)ws % 16)
+        return fail(MOE_ERR_INVALID_ARG, "x, y and the workspace must be 16-byte aligned");
     if (prefill) {
         if (act != MOE_ACT_BF16) return fail(MOE_ERR_INVALID_ARG, "prefill needs bf16 activations");
     } else {

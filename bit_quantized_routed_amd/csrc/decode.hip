@@ -529,15 +529,37 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_down_kernel(DecPass p)
 }
 
 // y = the shared expert's K parts in order, then the routed outputs in top-k order
-__global__ __launch_bounds__(256) void dec1_combine_kernel(DecPass p)
+__global__ __launch_bounds__(64) void dec1_combine_kernel(DecPass p)
 {
-    const int n = blockIdx.x * 256 + threadIdx.x;
+    // four outputs per lane; every load of a lane is issued before the first
+    // sum (indices clamped, the extra terms masked), so the kernel waits for
+    // one memory latency rather than one per term
+    const int n = 4 * (blockIdx.x * 64 + threadIdx.x);
     if (n >= p.H) return;
     const int KPD = p.Ish / DN_KPART;
-    float y = 0.f;
-    for (int q = 0; q < KPD; ++q) y += p.O_sh[(int64_t)q * p.H + n];
-    for (int j = 0; j < p.k; ++j) y += p.topk_w[j] * p.O[(int64_t)j * p.H + n];
-    p.y[n] = y;
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    for (int q0 = 0; q0 < KPD; q0 += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = *(const f32x4 *)&p.O_sh[(int64_t)min(q0 + i, KPD - 1) * p.H + n];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (q0 + i < KPD) y += v[i];
+    }
+    for (int j0 = 0; j0 < p.k; j0 += 8) {
+        f32x4 v[8];
+        float w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = min(j0 + i, p.k - 1);
+            v[i] = *(const f32x4 *)&p.O[(int64_t)j * p.H + n];
+            w[i] = p.topk_w[j];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (j0 + i < p.k) y += w[i] * v[i];
+    }
+    *(f32x4 *)&p.y[n] = y;
 }
 
 // ============================================================== launchers
@@ -643,7 +665,7 @@ hipError_t launch_dec_down(const DecPass &p, hipStream_t s)
 
 hipError_t launch_dec_combine(const DecPass &p, hipStream_t s)
 {
-    dec1_combine_kernel<<<(p.H + 255) / 256, 256, 0, s>>>(p);
+    dec1_combine_kernel<<<(p.H / 4 + 63) / 64, 64, 0, s>>>(p);
     return hipGetLastError();
 }
 

@@ -587,39 +587,57 @@ __device__ void group_small(const int32_t *sidx, int T, int E, int k, int32_t *o
     }
 }
 
-// One step of a wave-wide arg-max over (logit descending, expert ascending):
-// take the partner lane's candidate (DPP permutation CTRL) if it is better.
+// Wave-wide reductions by DPP: four steps (swap neighbours, swap pairs,
+// mirror the half-rows, mirror the rows) leave each 16-lane row's result in
+// every lane of the row; the four row results are read from lanes 0, 16, 32,
+// 48.  Straight-line code: no exec-mask branches between the steps.
 template <int CTRL>
-__device__ __forceinline__ void argmax_dpp(double &bv, int &be)
+__device__ __forceinline__ double dpp_f64(double v)
 {
-    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(bv), CTRL, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(bv), CTRL, 0xF, 0xF, false);
-    const int oe = __builtin_amdgcn_mov_dpp(be, CTRL, 0xF, 0xF, false);
-    const double ov = __hiloint2double(hi, lo);
-    if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xF, 0xF, false);
+    return __hiloint2double(hi, lo);
 }
 
-// Wave-wide arg-max: the four DPP steps (swap neighbours, swap pairs, mirror
-// the half-rows, mirror the rows) leave each 16-lane row's best in every lane
-// of the row; the four row results are then compared in lane order.
+__device__ __forceinline__ double readlane_f64(double v, int l)
+{
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                            __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+
+// largest value of the wave (no NaN among the inputs)
+__device__ __forceinline__ double wave_max_f64(double v)
+{
+    v = fmax(v, dpp_f64<0xB1>(v));      // quad_perm [1,0,3,2]
+    v = fmax(v, dpp_f64<0x4E>(v));      // quad_perm [2,3,0,1]
+    v = fmax(v, dpp_f64<0x141>(v));     // row_half_mirror
+    v = fmax(v, dpp_f64<0x140>(v));     // row_mirror
+    return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)), fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
+
+__device__ __forceinline__ int wave_min_i32(int v)
+{
+    v = min(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));
+    v = min(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));
+    v = min(v, __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false));
+    v = min(v, __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false));
+    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// Wave-wide arg-max over (value descending, expert ascending): the largest
+// value, then the lowest expert among the lanes holding it (a ballot names the
+// lane when only one does, the usual case; equal values take a min-reduction).
+// Lanes without a candidate hold (-inf, INT_MAX).  Returns uniform values.
 __device__ __forceinline__ void wave_argmax(double &bv, int &be)
 {
-    argmax_dpp<0xB1>(bv, be);       // quad_perm [1,0,3,2]
-    argmax_dpp<0x4E>(bv, be);       // quad_perm [2,3,0,1]
-    argmax_dpp<0x141>(bv, be);      // row_half_mirror
-    argmax_dpp<0x140>(bv, be);      // row_mirror
-    double cv = 0.0;
-    int ce = 0x7fffffff;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int lo = __builtin_amdgcn_readlane(__double2loint(bv), 16 * r);
-        const int hi = __builtin_amdgcn_readlane(__double2hiint(bv), 16 * r);
-        const int re = __builtin_amdgcn_readlane(be, 16 * r);
-        const double rv = __hiloint2double(hi, lo);
-        if (ce == 0x7fffffff || rv > cv || (rv == cv && re < ce)) { cv = rv; ce = re; }
-    }
-    bv = cv;
-    be = ce;
+    const double m = wave_max_f64(bv);
+    const uint64_t tie = __ballot(bv == m);
+    int e;
+    if (__popcll(tie) == 1) e = __builtin_amdgcn_readlane(be, __ffsll((unsigned long long)tie) - 1);
+    else e = wave_min_i32(bv == m ? be : 0x7fffffff);
+    bv = m;
+    be = e;
 }
 
 // T == 1: one wave selects and groups.  Lane l holds experts l, l+64, ...;
@@ -675,9 +693,16 @@ __global__ __launch_bounds__(64) void route_select_one(const double *part, const
     double ssum = sg;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ssum += __shfl_xor(ssum, off, 64);
-    // grouping
+    // grouping: one ballot of the taken flags per slot gives both the
+    // offsets and, for slot j's expert, the number of selected experts below it
+    uint64_t mk[MAXPL];
+#pragma unroll
+    for (int i = 0; i < MAXPL; ++i) mk[i] = 64 * i < E ? __ballot((taken >> i) & 1u) : 0ull;
+    const int es = my_e >> 6, el = my_e & 63;
     int below = 0;
-    for (int i = 0; i < k; ++i) below += __shfl(my_e, i, 64) < my_e;
+#pragma unroll
+    for (int i = 0; i < MAXPL; ++i)
+        below += i < es ? __popcll(mk[i]) : i == es ? __popcll(mk[i] & ((1ull << el) - 1ull)) : 0;
     if (lane < k) {
         topk_idx[lane] = my_e;
         topk_w[lane] = (float)(sg / ssum);
@@ -685,14 +710,13 @@ __global__ __launch_bounds__(64) void route_select_one(const double *part, const
         inv[lane] = below;
     }
     int base = 0;
-    const uint64_t lower = lane ? ((1ull << lane) - 1ull) : 0ull;
+    const uint64_t lower = (1ull << lane) - 1ull;
 #pragma unroll
     for (int i = 0; i < MAXPL; ++i) {
         if (64 * i >= E) break;
-        const uint64_t m = __ballot((taken >> i) & 1u);
         const int e = lane + 64 * i;
-        if (e < E) offsets[e] = base + __popcll(m & lower);
-        base += __popcll(m);
+        if (e < E) offsets[e] = base + __popcll(mk[i] & lower);
+        base += __popcll(mk[i]);
     }
     if (lane == 0) offsets[E] = base;
 }

@@ -138,7 +138,8 @@ int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bi
 /* ------------------------------------------------------------ expert FFN
  * Both compute y [T][H] fp32 (overwritten) = shared expert + routing-weighted
  * sum of the k routed expert FFNs (SwiGLU), from the routing that moe_route
- * produced.  Inputs as in moe_route.
+ * produced.  Inputs as in moe_route; x, y and ws must be 16-byte aligned
+ * (MOE_ERR_INVALID_ARG otherwise).
  *
  * moe_expert_ffn_decode -- fp32-accurate path meant for small T (any T works):
  *   weights applied exactly (integer codes in bf16 MFMA with fp32 block
