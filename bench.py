@@ -56,6 +56,45 @@ def kernel_source_hash(kernel: str | None = None) -> str:
     return h.hexdigest()[:12]
 
 
+def machine_ceilings():
+    """What this machine sustains, measured with the library's probe kernels: the
+    best streaming-read rate over a few launch shapes (1 GiB, read 5 times)
+    and a bf16 MFMA loop filling every CU."""
+    import torch
+    import bit_quantized_routed_amd as M
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    best_gbs, best_grid = 0.0, None
+    for grid in (256, 512, 1024):
+        sink = torch.empty(grid * 512 * 4, dtype=torch.int32, device="cuda")
+        M.probe_stream_read(buf, grid, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            M.probe_stream_read(buf, grid, sink)
+        e1.record()
+        e1.synchronize()
+        gbs = 5 * buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        if gbs > best_gbs:
+            best_gbs, best_grid = gbs, grid
+    del buf
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    grid, iters = 4 * n_cu, 4000
+    sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    tf = {}
+    for shape, name, fl in ((0, "16x16x32", 16384), (1, "32x32x16", 32768)):
+        M.probe_mfma_loop(shape, grid, 10, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        M.probe_mfma_loop(shape, grid, iters, sink)
+        e1.record()
+        e1.synchronize()
+        tf[name] = round(grid * 4 * iters * 8 * fl / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    return {"stream_read_GBps": round(best_gbs, 1), "stream_read_grid": best_grid,
+            "mfma_bf16_TFLOPs": max(tf.values()), "mfma_bf16_TFLOPs_by_shape": tf,
+            "probe": "moe_probe_stream_read / moe_probe_mfma_loop"}
+
+
 def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5):
     """Plain device-to-device copy of known size, for scaling the HBM byte
     counters (FETCH_SIZE / WRITE_SIZE) taken under rocprofv3."""
@@ -344,6 +383,12 @@ def main():
                                "TFLOP/s": round(tf, 1), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4), "T": s2.T}
         log("%s: %s" % (name, workloads[name]))
 
+    ceil = machine_ceilings()
+    log("machine ceilings: %s" % ceil)
+    meas = ceil["stream_read_GBps"] if decode else ceil["mfma_bf16_TFLOPs"]
+    roof["measured_peak"] = meas
+    roof["frac_of_measured"] = round(roof["achieved"] / meas, 4) if roof["achieved"] and meas else None
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (cpu_baseline)")
@@ -364,6 +409,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels_ms": {n: round(v[2], 5) for n, v in kt.items()},
+        "machine_ceilings": ceil,
         "kernel_source_hash": kernel_source_hash(),
         "workloads": workloads,
     }

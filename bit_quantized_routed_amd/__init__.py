@@ -54,7 +54,8 @@ class Profile(ctypes.Structure):
 
 _lib = None
 EXPORTS = ["moe_route", "moe_expert_ffn_decode", "moe_expert_ffn_prefill", "q2_pack", "q2_unpack",
-           "q2_packed_bytes", "moe_workspace_bytes", "moe_status_str", "moe_last_error"]
+           "q2_packed_bytes", "moe_workspace_bytes", "moe_status_str", "moe_last_error",
+           "moe_probe_stream_read", "moe_probe_mfma_loop"]
 
 
 def lib():
@@ -84,6 +85,10 @@ def lib():
     L.moe_status_str.restype = ctypes.c_char_p
     L.moe_last_error.argtypes = []
     L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_probe_stream_read.argtypes = [vp, sz, i32, vp, vp]
+    L.moe_probe_stream_read.restype = i32
+    L.moe_probe_mfma_loop.argtypes = [i32, i32, i32, vp, vp]
+    L.moe_probe_mfma_loop.restype = i32
     _lib = L
     return L
 
@@ -136,6 +141,18 @@ def q2_pack(fmt: int, w: np.ndarray, codebook: np.ndarray | None = None) -> np.n
 def q2_unpack(fmt: int, packed, rows: int, K: int, codebook, out, stream=None):
     """Device dequantizer: packed (uint8 device) -> out (fp32 device [rows, K])."""
     _check(lib().q2_unpack(fmt, _ptr(packed), rows, K, _ptr(codebook), _ptr(out), _stream(stream)), "q2_unpack")
+
+
+def probe_stream_read(buf, grid: int, sink, stream=None):
+    """Machine-ceiling probe: read every byte of buf (uint8 device) once."""
+    _check(lib().moe_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), grid, _ptr(sink),
+                                       _stream(stream)), "moe_probe_stream_read")
+
+
+def probe_mfma_loop(shape: int, grid: int, iters: int, sink, stream=None):
+    """Machine-ceiling probe: grid*4*iters*8*(16384 or 32768) flop of bf16 MFMA
+    (shape 0: 16x16x32, shape 1: 32x32x16)."""
+    _check(lib().moe_probe_mfma_loop(shape, grid, iters, _ptr(sink), _stream(stream)), "moe_probe_mfma_loop")
 
 
 def moe_route(layer: Layer, x, act: int, T: int, bias, topk_idx, topk_w, offsets, perm, inv, ws,

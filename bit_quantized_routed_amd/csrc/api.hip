@@ -9,6 +9,7 @@
 
 #include "kernels.h"
 #include "moe.h"
+#include "moe_probe.h"
 
 using namespace moe;
 
@@ -444,6 +445,28 @@ int q2_unpack(int fmt, const void *packed_dev, int64_t rows, int K, const int8_t
     if (rows * nblocks(K) * 8 > ((int64_t)1 << 40)) return fail(MOE_ERR_INVALID_ARG, "too large");
     hipError_t e = launch_unpack(fmt, (const uint8_t *)packed_dev, rows, K, codebook_dev, out_dev, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "q2_unpack launch");
+    return MOE_OK;
+}
+
+int moe_probe_stream_read(const void *buf, size_t bytes, int grid, void *sink, void *stream)
+{
+    if (!buf || !sink) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+    if (bytes == 0 || bytes % 16 || (uintptr_t)buf % 16 || (uintptr_t)sink % 16)
+        return fail(MOE_ERR_INVALID_ARG, "bytes=%zu and both pointers must be 16-byte multiples", bytes);
+    if (grid < 1 || grid > 65536) return fail(MOE_ERR_INVALID_ARG, "grid=%d outside [1, 65536]", grid);
+    hipError_t e = launch_probe_stream(buf, bytes, grid, sink, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_probe_stream_read launch");
+    return MOE_OK;
+}
+
+int moe_probe_mfma_loop(int shape, int grid, int iters, float *sink, void *stream)
+{
+    if (!sink) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+    if (shape != 0 && shape != 1) return fail(MOE_ERR_INVALID_ARG, "shape=%d must be 0 or 1", shape);
+    if (grid < 1 || grid > 65536 || iters < 1 || iters > (1 << 24))
+        return fail(MOE_ERR_INVALID_ARG, "grid=%d or iters=%d out of range", grid, iters);
+    hipError_t e = launch_probe_mfma(shape, grid, iters, sink, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "moe_probe_mfma_loop launch");
     return MOE_OK;
 }
 

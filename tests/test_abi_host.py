@@ -21,7 +21,7 @@ FAKE = 0x1000            # never dereferenced: every call below fails validation
 
 
 def test_exports_every_declared_function():
-    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = "".join(open(os.path.join(ROOT, "include", h)).read() for h in sorted(os.listdir(os.path.join(ROOT, "include"))))
     declared = set(re.findall(r"^(?:int|size_t|const char \*)\s*(\w+)\s*\(", src, flags=re.M))
     assert {"moe_route", "moe_expert_ffn_decode", "moe_expert_ffn_prefill", "q2_pack", "q2_unpack"} <= declared
     L = M.lib()
@@ -136,3 +136,14 @@ def test_pack_edge_values():
     rows[5] = np.tile(np.array([1e-6, -2e-6], np.float32), 128)
     for fmt in (F.CB2, F.Q2K, F.Q4K):
         assert np.array_equal(M.q2_pack(fmt, rows, CB), F.pack(fmt, rows, CB)), fmt
+
+
+def test_probe_argument_checks():
+    L = M.lib()
+    assert L.moe_probe_stream_read(None, 16, 1, FAKE, None) == -1
+    assert L.moe_probe_stream_read(FAKE, 15, 1, FAKE, None) == -1
+    assert L.moe_probe_stream_read(FAKE, 16, 0, FAKE, None) == -1
+    assert L.moe_probe_mfma_loop(0, 0, 1, FAKE, None) == -1
+    assert L.moe_probe_mfma_loop(0, 1, 0, FAKE, None) == -1
+    assert L.moe_probe_mfma_loop(0, 1, 1, None, None) == -1
+    assert L.moe_probe_mfma_loop(2, 1, 1, FAKE, None) == -1
