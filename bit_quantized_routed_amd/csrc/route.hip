@@ -114,57 +114,71 @@ __global__ __launch_bounds__(256) void route_logits_tiled(const void *x, const f
 }
 
 // Large T on the fp64 matrix cores: a 32-token x 64-expert tile per
-// work-group, H staged through LDS in chunks of 32 as fp64 (x and W_r widened
+// work-group, H staged through LDS in chunks of 64 as fp64 (x and W_r widened
 // exactly); each wave owns 16 experts and both 16-token halves, and
-// accumulates with v_mfma_f64_16x16x4f64 (fp64 products and sums).  Rows of
-// the LDS tiles are padded to 33 doubles so the 16 lanes of one read hit 16
-// different bank pairs.  Needs H % 32 == 0.
+// accumulates with v_mfma_f64_16x16x4f64 (fp64 products and sums).  The raw
+// values of chunk c + 1 are loaded into registers while chunk c is computed,
+// so the loads' latency is hidden behind the MFMAs.  Rows of the LDS tiles are
+// padded to 65 doubles so the 16 lanes of one read hit 16 different bank
+// pairs.  Needs H % 64 == 0.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 template <bool XBF16>
 __global__ __launch_bounds__(256) void route_logits_mfma(const void *x, const float *wr, const float *bias, int T,
                                                           int H, int E, double *logits)
 {
-    constexpr int TT = 32, TE = 64, HC = 32, LD = HC + 1;
+    constexpr int TT = 32, TE = 64, HC = 64, LD = HC + 1;
     __shared__ double xs[TT][LD];
     __shared__ double ws[TE][LD];
     const int t0 = blockIdx.x * TT, e0 = blockIdx.y * TE;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int fr = lane & 15, fk = lane >> 4;
-    f64x4 acc[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
-    // staging maps: x -> 4 elements per thread (rows 0..31), W -> 8 per thread (rows 0..63)
-    const int xr = tid >> 3, xk = (tid & 7) * 4;
-    const int wrow = tid >> 2, wk = (tid & 3) * 8;
+    // four independent accumulator sets per token half (K steps kk mod 4):
+    // one wave per SIMD, so the matrix pipe needs several chains in flight
+    f64x4 acc[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[mt][c] = f64x4{0.0, 0.0, 0.0, 0.0};
+    // staging maps: x -> 8 elements per thread (rows 0..31), W -> 16 per thread (rows 0..63)
+    const int xr = tid >> 3, xk = (tid & 7) * 8;
+    const int wrow = tid >> 2, wk = (tid & 3) * 16;
     const bool xok = t0 + xr < T, wok = e0 + wrow < E;
+    // rows past T or E load row 0 of the tile's block (in bounds) and stage zeros
+    const size_t xoff = (size_t)(xok ? t0 + xr : 0) * H + xk, woff = (size_t)(wok ? e0 + wrow : 0) * H + wk;
+    u32x4 xraw[XBF16 ? 1 : 2];
+    f32x4 wraw[4];
+    auto gload = [&](int h0) {
+        if (XBF16) xraw[0] = *(const u32x4 *)((const uint16_t *)x + xoff + h0);
+        else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) xraw[i] = *(const u32x4 *)((const float *)x + xoff + h0 + 4 * i);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wraw[i] = *(const f32x4 *)&wr[woff + h0 + 4 * i];
+    };
+    gload(0);
     for (int h0 = 0; h0 < H; h0 += HC) {
-        double xv[4], wv[8];
-        if (XBF16) {
-            uint2 u = xok ? *(const uint2 *)((const uint16_t *)x + (size_t)(t0 + xr) * H + h0 + xk) : uint2{0, 0};
-            xv[0] = bf16_bits_to_f32(u.x & 0xffffu); xv[1] = bf16_bits_to_f32(u.x >> 16);
-            xv[2] = bf16_bits_to_f32(u.y & 0xffffu); xv[3] = bf16_bits_to_f32(u.y >> 16);
-        } else {
-            const f32x4 f = xok ? *(const f32x4 *)((const float *)x + (size_t)(t0 + xr) * H + h0 + xk)
-                                : f32x4{0.f, 0.f, 0.f, 0.f};
-            xv[0] = f.x; xv[1] = f.y; xv[2] = f.z; xv[3] = f.w;
-        }
-        {
-            const f32x4 a = wok ? *(const f32x4 *)&wr[(size_t)(e0 + wrow) * H + h0 + wk] : f32x4{0.f, 0.f, 0.f, 0.f};
-            const f32x4 b = wok ? *(const f32x4 *)&wr[(size_t)(e0 + wrow) * H + h0 + wk + 4] : f32x4{0.f, 0.f, 0.f, 0.f};
-            wv[0] = a.x; wv[1] = a.y; wv[2] = a.z; wv[3] = a.w; wv[4] = b.x; wv[5] = b.y; wv[6] = b.z; wv[7] = b.w;
-        }
         __syncthreads();                                   // previous chunk consumed
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xs[xr][xk + i] = xv[i];
+        for (int i = 0; i < 8; ++i) {
+            double v;
+            if (XBF16) v = (double)bf16_bits_to_f32((xraw[0][i >> 1] >> (16 * (i & 1))) & 0xffffu);
+            else v = (double)__uint_as_float(xraw[i >> 2][i & 3]);
+            xs[xr][xk + i] = xok ? v : 0.0;
+        }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ws[wrow][wk + i] = wv[i];
+        for (int i = 0; i < 16; ++i) ws[wrow][wk + i] = wok ? (double)wraw[i >> 2][i & 3] : 0.0;
         __syncthreads();
+        gload(min(h0 + HC, H - HC));                       // next chunk in flight (the last re-reads its own)
 #pragma unroll
         for (int kk = 0; kk < HC / 4; ++kk) {
             // A: lane (fr, fk) holds x[token fr][h 4kk + fk]; B: W_r[expert fr][h 4kk + fk]
             const double b = ws[wave * 16 + fr][4 * kk + fk];
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
-                acc[mt] = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[mt * 16 + fr][4 * kk + fk], b, acc[mt], 0, 0, 0);
+                acc[mt][kk & 3] = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[mt * 16 + fr][4 * kk + fk], b, acc[mt][kk & 3],
+                                                                      0, 0, 0);
         }
     }
     // D: lane (fr, fk) holds rows fk + 4i (tokens) of column fr (expert); the
@@ -178,7 +192,8 @@ __global__ __launch_bounds__(256) void route_logits_mfma(const void *x, const fl
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = t0 + mt * 16 + fk + 4 * i;
-                if (t < T) logits[(size_t)t * E + e] = acc[mt][i] + bv;
+                const double l = (acc[mt][0][i] + acc[mt][1][i]) + (acc[mt][2][i] + acc[mt][3][i]);
+                if (t < T) logits[(size_t)t * E + e] = l + bv;
             }
     }
 }
@@ -357,7 +372,7 @@ void launch_route_logits(const void *x, bool xbf16, const float *wr, const float
         dim3 grid(E, (T + 7) / 8);
         if (xbf16) route_logits_small<true><<<grid, 64, 0, s>>>(x, wr, bias, T, H, E, logits);
         else route_logits_small<false><<<grid, 64, 0, s>>>(x, wr, bias, T, H, E, logits);
-    } else if (H % 32 == 0) {
+    } else if (H % 64 == 0) {
         dim3 grid((T + 31) / 32, (E + 63) / 64);
         if (xbf16) route_logits_mfma<true><<<grid, 256, 0, s>>>(x, wr, bias, T, H, E, logits);
         else route_logits_mfma<false><<<grid, 256, 0, s>>>(x, wr, bias, T, H, E, logits);
