@@ -65,18 +65,19 @@ def machine_ceilings():
     buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
     best_gbs, best_grid = 0.0, None
-    for grid in (256, 512, 1024):
-        sink = torch.empty(grid * 512 * 4, dtype=torch.int32, device="cuda")
-        M.probe_stream_read(buf, grid, sink)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(5):
-            M.probe_stream_read(buf, grid, sink)
-        e1.record()
-        e1.synchronize()
-        gbs = 5 * buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
-        if gbs > best_gbs:
-            best_gbs, best_grid = gbs, grid
+    for nt in (False, True):
+        for grid in (256, 512, 1024, 2048):
+            sink = torch.empty(grid * 512 * 4, dtype=torch.int32, device="cuda")
+            M.probe_stream_read(buf, grid, sink, nt)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                M.probe_stream_read(buf, grid, sink, nt)
+            e1.record()
+            e1.synchronize()
+            gbs = 5 * buf.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            if gbs > best_gbs:
+                best_gbs, best_grid = gbs, "%d%s" % (grid, " nontemporal" if nt else "")
     del buf
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     grid, iters = 4 * n_cu, 4000

@@ -85,7 +85,7 @@ def lib():
     L.moe_status_str.restype = ctypes.c_char_p
     L.moe_last_error.argtypes = []
     L.moe_last_error.restype = ctypes.c_char_p
-    L.moe_probe_stream_read.argtypes = [vp, sz, i32, vp, vp]
+    L.moe_probe_stream_read.argtypes = [vp, sz, i32, i32, vp, vp]
     L.moe_probe_stream_read.restype = i32
     L.moe_probe_mfma_loop.argtypes = [i32, i32, i32, vp, vp]
     L.moe_probe_mfma_loop.restype = i32
@@ -143,10 +143,10 @@ def q2_unpack(fmt: int, packed, rows: int, K: int, codebook, out, stream=None):
     _check(lib().q2_unpack(fmt, _ptr(packed), rows, K, _ptr(codebook), _ptr(out), _stream(stream)), "q2_unpack")
 
 
-def probe_stream_read(buf, grid: int, sink, stream=None):
+def probe_stream_read(buf, grid: int, sink, nontemporal: bool = False, stream=None):
     """Machine-ceiling probe: read every byte of buf (uint8 device) once."""
-    _check(lib().moe_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), grid, _ptr(sink),
-                                       _stream(stream)), "moe_probe_stream_read")
+    _check(lib().moe_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), grid, int(nontemporal),
+                                       _ptr(sink), _stream(stream)), "moe_probe_stream_read")
 
 
 def probe_mfma_loop(shape: int, grid: int, iters: int, sink, stream=None):

@@ -448,13 +448,13 @@ int q2_unpack(int fmt, const void *packed_dev, int64_t rows, int K, const int8_t
     return MOE_OK;
 }
 
-int moe_probe_stream_read(const void *buf, size_t bytes, int grid, void *sink, void *stream)
+int moe_probe_stream_read(const void *buf, size_t bytes, int grid, int nontemporal, void *sink, void *stream)
 {
     if (!buf || !sink) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
     if (bytes == 0 || bytes % 16 || (uintptr_t)buf % 16 || (uintptr_t)sink % 16)
         return fail(MOE_ERR_INVALID_ARG, "bytes=%zu and both pointers must be 16-byte multiples", bytes);
     if (grid < 1 || grid > 65536) return fail(MOE_ERR_INVALID_ARG, "grid=%d outside [1, 65536]", grid);
-    hipError_t e = launch_probe_stream(buf, bytes, grid, sink, (hipStream_t)stream);
+    hipError_t e = launch_probe_stream(buf, bytes, grid, nontemporal, sink, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "moe_probe_stream_read launch");
     return MOE_OK;
 }

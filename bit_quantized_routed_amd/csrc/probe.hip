@@ -10,6 +10,8 @@ namespace {
 constexpr int PR_THREADS = 512;
 constexpr int PR_DEPTH = 4;        // 16-byte loads in flight per thread
 
+// NT: non-temporal loads (streamed data marked for early eviction)
+template <bool NT>
 __global__ __launch_bounds__(PR_THREADS) void probe_stream_kernel(const u32x4 *p, size_t n, u32x4 *sink)
 {
     const size_t T = (size_t)gridDim.x * PR_THREADS, g = (size_t)blockIdx.x * PR_THREADS + threadIdx.x;
@@ -19,7 +21,9 @@ __global__ __launch_bounds__(PR_THREADS) void probe_stream_kernel(const u32x4 *p
 #pragma unroll
         for (int j = 0; j < PR_DEPTH; ++j) {
             const size_t i = b + (size_t)j * T;
-            v[j] = i < n ? p[i] : u32x4{0u, 0u, 0u, 0u};
+            const size_t ic = i < n ? i : n - 1;
+            v[j] = NT ? __builtin_nontemporal_load(&p[ic]) : p[ic];
+            if (i >= n) v[j] = u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int j = 0; j < PR_DEPTH; ++j) acc ^= v[j];
@@ -73,9 +77,10 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float *sink)
 
 }  // namespace
 
-hipError_t launch_probe_stream(const void *buf, size_t bytes, int grid, void *sink, hipStream_t s)
+hipError_t launch_probe_stream(const void *buf, size_t bytes, int grid, int nontemporal, void *sink, hipStream_t s)
 {
-    probe_stream_kernel<<<grid, PR_THREADS, 0, s>>>((const u32x4 *)buf, bytes / 16, (u32x4 *)sink);
+    if (nontemporal) probe_stream_kernel<true><<<grid, PR_THREADS, 0, s>>>((const u32x4 *)buf, bytes / 16, (u32x4 *)sink);
+    else probe_stream_kernel<false><<<grid, PR_THREADS, 0, s>>>((const u32x4 *)buf, bytes / 16, (u32x4 *)sink);
     return hipGetLastError();
 }
 

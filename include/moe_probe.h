@@ -8,9 +8,10 @@
  *
  * moe_probe_stream_read: `grid` work-groups of 512 threads read every byte of
  *   buf once (device, 16-byte aligned, bytes a positive multiple of 16) in
- *   16-byte loads, four per thread in flight; each thread XORs what it read
- *   into sink[thread] (device, grid * 512 * 16 bytes) so no load can be
- *   dropped.  Bytes read = `bytes`.
+ *   16-byte loads, four per thread in flight (non-temporal loads when
+ *   `nontemporal` is non-zero); each thread XORs what it read into
+ *   sink[thread] (device, grid * 512 * 16 bytes) so no load can be dropped.
+ *   Bytes read = `bytes`.
  * moe_probe_mfma_loop: `grid` work-groups of 256 threads; every wave runs
  *   `iters` rounds of 8 independent bf16 MFMAs -- shape 0:
  *   v_mfma_f32_16x16x32_bf16 (16384 flop each), shape 1:
@@ -31,7 +32,7 @@
 extern "C" {
 #endif
 
-int moe_probe_stream_read(const void *buf, size_t bytes, int grid, void *sink, void *stream);
+int moe_probe_stream_read(const void *buf, size_t bytes, int grid, int nontemporal, void *sink, void *stream);
 int moe_probe_mfma_loop(int shape, int grid, int iters, float *sink, void *stream);
 
 #ifdef __cplusplus

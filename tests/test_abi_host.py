@@ -140,9 +140,9 @@ def test_pack_edge_values():
 
 def test_probe_argument_checks():
     L = M.lib()
-    assert L.moe_probe_stream_read(None, 16, 1, FAKE, None) == -1
-    assert L.moe_probe_stream_read(FAKE, 15, 1, FAKE, None) == -1
-    assert L.moe_probe_stream_read(FAKE, 16, 0, FAKE, None) == -1
+    assert L.moe_probe_stream_read(None, 16, 1, 0, FAKE, None) == -1
+    assert L.moe_probe_stream_read(FAKE, 15, 1, 0, FAKE, None) == -1
+    assert L.moe_probe_stream_read(FAKE, 16, 0, 1, FAKE, None) == -1
     assert L.moe_probe_mfma_loop(0, 0, 1, FAKE, None) == -1
     assert L.moe_probe_mfma_loop(0, 1, 0, FAKE, None) == -1
     assert L.moe_probe_mfma_loop(0, 1, 1, None, None) == -1

@@ -21,12 +21,13 @@ def test_stream_probe_reads_every_word():
     host = np.random.default_rng(5).integers(0, 2**32, size=n, dtype=np.uint64).astype(np.uint32)
     buf = torch.from_numpy(host.view(np.uint8)).cuda()
     for grid in (1, 7, 256):
-        sink = torch.zeros(grid * 512 * 4, dtype=torch.int32, device="cuda")
-        M.probe_stream_read(buf, grid, sink)
-        torch.cuda.synchronize()
-        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32).reshape(-1, 4), axis=0)
-        want = np.bitwise_xor.reduce(host.reshape(-1, 4), axis=0)
-        assert np.array_equal(got, want), grid
+        for nt in (False, True):
+            sink = torch.zeros(grid * 512 * 4, dtype=torch.int32, device="cuda")
+            M.probe_stream_read(buf, grid, sink, nt)
+            torch.cuda.synchronize()
+            got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32).reshape(-1, 4), axis=0)
+            want = np.bitwise_xor.reduce(host.reshape(-1, 4), axis=0)
+            assert np.array_equal(got, want), (grid, nt)
 
 
 @pytest.mark.parametrize("shape,elems,kdim", [(0, 4, 32), (1, 16, 16)])
