@@ -8,6 +8,7 @@
 #include <string>
 
 #include "kernels.h"
+#include "probe.h"
 #include "moe.h"
 #include "moe_probe.h"
 

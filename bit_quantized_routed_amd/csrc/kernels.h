@@ -120,8 +120,4 @@ constexpr int NP_BM_DEC = 32;
 bool np_decode_ok(const FfnPass &p);
 hipError_t launch_np_decode(const FfnPass &p, bool gateup, hipStream_t s);
 
-// machine ceilings (moe_probe.h)
-hipError_t launch_probe_stream(const void *buf, size_t bytes, int grid, int nontemporal, void *sink, hipStream_t s);
-hipError_t launch_probe_mfma(int shape, int grid, int iters, float *sink, hipStream_t s);
-
 }  // namespace moe

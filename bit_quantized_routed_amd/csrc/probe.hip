@@ -1,7 +1,7 @@
 // Machine ceilings for the benchmark (see include/moe_probe.h): a streaming
 // HBM read and a bf16 MFMA loop, measured on the box the kernels run on.
 #include "common.h"
-#include "kernels.h"
+#include "probe.h"
 
 namespace moe {
 
