@@ -196,8 +196,9 @@ class DeviceLayer:
                        _ptr(sh_gate), _ptr(sh_up), _ptr(sh_down), _ptr(w_router))
 
     def workspace(self, T: int, path: int, device="cuda"):
-        """A workspace for `path` at T tokens.  Allocated zeroed: its first bytes
-        hold arrival counters that must start at zero (calls leave them zero)."""
+        """A workspace for `path` at T tokens (the library needs no particular
+        initial contents; zeroed so that nothing reads stale data from earlier
+        tests)."""
         import torch
         n = max(workspace_bytes(self.c, T, path), 256)
         return torch.zeros(n, dtype=torch.uint8, device=device)
