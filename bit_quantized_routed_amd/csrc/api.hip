@@ -8,6 +8,7 @@
 #include <string>
 
 #include "kernels.h"
+#include "route.h"
 #include "probe.h"
 #include "moe.h"
 #include "moe_probe.h"
@@ -111,7 +112,8 @@ RouteWs route_ws(const moe_layer *L, int T, char *base)
     size_t off = 0;
     const size_t E = L->n_experts, k = L->top_k;
     w.logits = (double *)(base + off);
-    const size_t nc = route_fused(L, T) ? (size_t)route_decode_chunks(T, L->hidden) : 1;
+    const size_t nc = route_fused(L, T) ? (size_t)route_decode_chunks(T, L->hidden)
+                                        : (size_t)route_logits_parts(T, L->hidden);
     off = align_up(off + nc * (size_t)T * E * sizeof(double));
     if (!route_fused(L, T) && !route_small(L, T)) {
         w.rank = (int32_t *)(base + off);
@@ -412,7 +414,7 @@ int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bi
     if (route_small(L, T)) {
         MOE_LAUNCH("route_select_small", launch_route_select_small(w.logits, T, E, k, topk_idx, topk_w, offsets, perm, inv, s));
     } else {
-        MOE_LAUNCH("route_topk", launch_route_topk(w.logits, T, E, k, topk_idx, topk_w, s));
+        MOE_LAUNCH("route_topk", launch_route_topk(w.logits, bias, T, H, E, k, topk_idx, topk_w, s));
         MOE_LAUNCH("route_rank", launch_route_rank(topk_idx, T, E, k, w.rank, w.tile_counts, s));
         MOE_LAUNCH("route_scan", launch_route_scan(T, E, k, w.tile_counts, offsets, s));
         MOE_LAUNCH("route_scatter", launch_route_scatter(topk_idx, w.rank, w.tile_counts, offsets, T, E, k, perm, inv, s));

@@ -9,7 +9,7 @@
 // is a counting sort whose ranks come from per-expert token bitmasks, so the
 // result does not depend on thread timing.
 #include "common.h"
-#include "kernels.h"
+#include "route.h"
 
 #include <algorithm>
 
@@ -113,41 +113,39 @@ __global__ __launch_bounds__(256) void route_logits_tiled(const void *x, const f
         }
 }
 
-// Large T on the fp64 matrix cores: a 32-token x 64-expert tile per
-// work-group, H staged through LDS in chunks of 64 as fp64 (x and W_r widened
-// exactly); each wave owns 16 experts and both 16-token halves, and
-// accumulates with v_mfma_f64_16x16x4f64 (fp64 products and sums).  The raw
-// values of chunk c + 1 are loaded into registers while chunk c is computed,
-// so the loads' latency is hidden behind the MFMAs.  Rows of the LDS tiles are
-// padded to 65 doubles so the 16 lanes of one read hit 16 different bank
-// pairs.  Needs H % 64 == 0.
+// Large T on the fp64 matrix cores: a 64-token x 64-expert tile and one of
+// ROUTE_KPARTS halves of H per work-group, written as partial logits
+// [part][T][E] that the top-k kernel adds in part order.  Bigger token tiles
+// read W_r fewer times (T/64 instead of T/32 passes over its 7.34 MB); the K
+// split keeps the work-group count.  H is staged through LDS in chunks of 32
+// as fp64 (x and W_r widened exactly); each wave owns 16 experts and the
+// four 16-token quarters (four independent v_mfma_f64_16x16x4f64 chains),
+// and the raw values of chunk c + 1 are loaded into registers while chunk c
+// is computed.  Rows of the LDS tiles are padded to 33 doubles so the 16
+// lanes of one read hit 16 different bank pairs.  Needs H % 64 == 0.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 template <bool XBF16>
-__global__ __launch_bounds__(256) void route_logits_mfma(const void *x, const float *wr, const float *bias, int T,
-                                                          int H, int E, double *logits)
+__global__ __launch_bounds__(256) void route_logits_mfma(const void *x, const float *wr, int T, int H, int E,
+                                                          double *part)
 {
-    constexpr int TT = 32, TE = 64, HC = 64, LD = HC + 1;
+    constexpr int TT = 64, TE = 64, HC = 32, LD = HC + 1;
     __shared__ double xs[TT][LD];
     __shared__ double ws[TE][LD];
-    const int t0 = blockIdx.x * TT, e0 = blockIdx.y * TE;
+    const int t0 = blockIdx.x * TT, e0 = blockIdx.y * TE, kp = blockIdx.z;
+    const int HP = H / ROUTE_KPARTS, hb = kp * HP;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int fr = lane & 15, fk = lane >> 4;
-    // four independent accumulator sets per token half (K steps kk mod 4):
-    // one wave per SIMD, so the matrix pipe needs several chains in flight
-    f64x4 acc[2][4];
+    f64x4 acc[4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[mt][c] = f64x4{0.0, 0.0, 0.0, 0.0};
-    // staging maps: x -> 8 elements per thread (rows 0..31), W -> 16 per thread (rows 0..63)
-    const int xr = tid >> 3, xk = (tid & 7) * 8;
-    const int wrow = tid >> 2, wk = (tid & 3) * 16;
-    const bool xok = t0 + xr < T, wok = e0 + wrow < E;
-    // rows past T or E load row 0 of the tile's block (in bounds) and stage zeros
-    const size_t xoff = (size_t)(xok ? t0 + xr : 0) * H + xk, woff = (size_t)(wok ? e0 + wrow : 0) * H + wk;
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = f64x4{0.0, 0.0, 0.0, 0.0};
+    // staging maps: 8 x values and 8 W_r values per thread (64 rows x 32 each)
+    const int sr = tid >> 2, sk = (tid & 3) * 8;
+    const bool xok = t0 + sr < T, wok = e0 + sr < E;
+    // rows past T or E load row 0 (in bounds) and stage zeros
+    const size_t xoff = (size_t)(xok ? t0 + sr : 0) * H + hb + sk, woff = (size_t)(wok ? e0 + sr : 0) * H + hb + sk;
     u32x4 xraw[XBF16 ? 1 : 2];
-    f32x4 wraw[4];
+    f32x4 wraw[2];
     auto gload = [&](int h0) {
         if (XBF16) xraw[0] = *(const u32x4 *)((const uint16_t *)x + xoff + h0);
         else {
@@ -155,30 +153,28 @@ __global__ __launch_bounds__(256) void route_logits_mfma(const void *x, const fl
             for (int i = 0; i < 2; ++i) xraw[i] = *(const u32x4 *)((const float *)x + xoff + h0 + 4 * i);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wraw[i] = *(const f32x4 *)&wr[woff + h0 + 4 * i];
+        for (int i = 0; i < 2; ++i) wraw[i] = *(const f32x4 *)&wr[woff + h0 + 4 * i];
     };
     gload(0);
-    for (int h0 = 0; h0 < H; h0 += HC) {
+    for (int h0 = 0; h0 < HP; h0 += HC) {
         __syncthreads();                                   // previous chunk consumed
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             double v;
             if (XBF16) v = (double)bf16_bits_to_f32((xraw[0][i >> 1] >> (16 * (i & 1))) & 0xffffu);
             else v = (double)__uint_as_float(xraw[i >> 2][i & 3]);
-            xs[xr][xk + i] = xok ? v : 0.0;
+            xs[sr][sk + i] = xok ? v : 0.0;
+            ws[sr][sk + i] = wok ? (double)wraw[i >> 2][i & 3] : 0.0;
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ws[wrow][wk + i] = wok ? (double)wraw[i >> 2][i & 3] : 0.0;
         __syncthreads();
-        gload(min(h0 + HC, H - HC));                       // next chunk in flight (the last re-reads its own)
+        gload(min(h0 + HC, HP - HC));                      // next chunk in flight (the last re-reads its own)
 #pragma unroll
         for (int kk = 0; kk < HC / 4; ++kk) {
             // A: lane (fr, fk) holds x[token fr][h 4kk + fk]; B: W_r[expert fr][h 4kk + fk]
             const double b = ws[wave * 16 + fr][4 * kk + fk];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-                acc[mt][kk & 3] = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[mt * 16 + fr][4 * kk + fk], b, acc[mt][kk & 3],
-                                                                      0, 0, 0);
+            for (int mt = 0; mt < 4; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_f64_16x16x4f64(xs[mt * 16 + fr][4 * kk + fk], b, acc[mt], 0, 0, 0);
         }
     }
     // D: lane (fr, fk) holds rows fk + 4i (tokens) of column fr (expert); the
@@ -186,14 +182,12 @@ __global__ __launch_bounds__(256) void route_logits_mfma(const void *x, const fl
     // fp32-output shapes
     const int e = e0 + wave * 16 + fr;
     if (e < E) {
-        const double bv = bias ? (double)bias[e] : 0.0;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = t0 + mt * 16 + fk + 4 * i;
-                const double l = (acc[mt][0][i] + acc[mt][1][i]) + (acc[mt][2][i] + acc[mt][3][i]);
-                if (t < T) logits[(size_t)t * E + e] = l + bv;
+                if (t < T) part[((size_t)kp * T + t) * E + e] = acc[mt][i];
             }
     }
 }
@@ -201,16 +195,26 @@ __global__ __launch_bounds__(256) void route_logits_mfma(const void *x, const fl
 // ---------------------------------------------------------------- top-k
 // One wave selects the k best experts of one token: k rounds of a wave-wide
 // arg-max over (logit desc, expert asc).  Each lane holds experts lane+64*i.
+// l: the token's logits, or its first partial-logit row when nparts > 1 (the
+// parts, pstride apart, are added in part order, then the bias)
 __device__ __forceinline__ void wave_topk(const double *l, int E, int k, int lane, int32_t *idx_out,
-                                          float *w_out, int32_t *idx_lds)
+                                          float *w_out, int32_t *idx_lds, int nparts = 1, size_t pstride = 0,
+                                          const float *bias = nullptr)
 {
     constexpr int MAXPL = 16;                    // E <= 1024
+    // the same sum wherever a logit is needed (selection and normalisation)
+    auto logit = [&](int e) {
+        double s = l[e];
+        for (int c = 1; c < nparts; ++c) s += l[c * pstride + e];
+        if (bias) s += (double)bias[e];
+        return s;
+    };
     double v[MAXPL];
     uint32_t taken = 0;
 #pragma unroll
     for (int i = 0; i < MAXPL; ++i) {
         const int e = lane + 64 * i;
-        v[i] = e < E ? l[e] : -INFINITY;
+        v[i] = e < E ? logit(e) : -INFINITY;
     }
     double ssum = 0.0;
     for (int j = 0; j < k; ++j) {
@@ -242,19 +246,20 @@ __device__ __forceinline__ void wave_topk(const double *l, int E, int k, int lan
     if (lane == 0) {
         for (int j = 0; j < k; ++j) {
             const int e = idx_out[j];
-            const double s = 1.0 / (1.0 + exp(-l[e]));
+            const double s = 1.0 / (1.0 + exp(-logit(e)));
             w_out[j] = (float)(s / ssum);
         }
     }
 }
 
-__global__ __launch_bounds__(256) void route_topk(const double *logits, int T, int E, int k,
-                                                  int32_t *topk_idx, float *topk_w)
+__global__ __launch_bounds__(256) void route_topk(const double *logits, const float *bias, int nparts, int T,
+                                                  int E, int k, int32_t *topk_idx, float *topk_w)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
-    wave_topk(logits + (size_t)t * E, E, k, lane, topk_idx + (size_t)t * k, topk_w + (size_t)t * k, nullptr);
+    wave_topk(logits + (size_t)t * E, E, k, lane, topk_idx + (size_t)t * k, topk_w + (size_t)t * k, nullptr,
+              nparts, (size_t)T * E, bias);
 }
 
 // ---------------------------------------------------------------- grouping
@@ -372,10 +377,10 @@ void launch_route_logits(const void *x, bool xbf16, const float *wr, const float
         dim3 grid(E, (T + 7) / 8);
         if (xbf16) route_logits_small<true><<<grid, 64, 0, s>>>(x, wr, bias, T, H, E, logits);
         else route_logits_small<false><<<grid, 64, 0, s>>>(x, wr, bias, T, H, E, logits);
-    } else if (H % 64 == 0) {
-        dim3 grid((T + 31) / 32, (E + 63) / 64);
-        if (xbf16) route_logits_mfma<true><<<grid, 256, 0, s>>>(x, wr, bias, T, H, E, logits);
-        else route_logits_mfma<false><<<grid, 256, 0, s>>>(x, wr, bias, T, H, E, logits);
+    } else if (route_logits_parts(T, H) > 1) {
+        dim3 grid((T + 63) / 64, (E + 63) / 64, ROUTE_KPARTS);
+        if (xbf16) route_logits_mfma<true><<<grid, 256, 0, s>>>(x, wr, T, H, E, logits);
+        else route_logits_mfma<false><<<grid, 256, 0, s>>>(x, wr, T, H, E, logits);
     } else {
         dim3 grid((T + 63) / 64, (E + 63) / 64);
         if (xbf16) route_logits_tiled<true><<<grid, 256, 0, s>>>(x, wr, bias, T, H, E, logits);
@@ -389,10 +394,16 @@ void launch_route_select_small(const double *logits, int T, int E, int k, int32_
     route_select_small<<<1, 256, 0, s>>>(logits, T, E, k, topk_idx, topk_w, offsets, perm, inv);
 }
 
-void launch_route_topk(const double *logits, int T, int E, int k, int32_t *topk_idx, float *topk_w, hipStream_t s)
+void launch_route_topk(const double *logits, const float *bias, int T, int H, int E, int k, int32_t *topk_idx,
+                       float *topk_w, hipStream_t s)
 {
-    route_topk<<<(T + 3) / 4, 256, 0, s>>>(logits, T, E, k, topk_idx, topk_w);
+    // the fp64 MFMA logits leave partial sums without the bias; the other
+    // logits kernels leave finished logits
+    const int np = route_logits_parts(T, H);
+    route_topk<<<(T + 3) / 4, 256, 0, s>>>(logits, np > 1 ? bias : nullptr, np, T, E, k, topk_idx, topk_w);
 }
+
+int route_logits_parts(int T, int H) { return T > 64 && H % 64 == 0 ? ROUTE_KPARTS : 1; }
 
 void launch_route_rank(const int32_t *topk_idx, int T, int E, int k, int32_t *rank, int32_t *tile_counts,
                        hipStream_t s)
