@@ -290,3 +290,31 @@ def test_full_prefill8192(big):
 
 def test_full_prefill8192_q4k(big_q4k):
     assert sampled_check(big_q4k, S.config("prefill8192_q4k"), False, 2) <= PRE_TOL
+
+
+# ------------------------------------------------------------------ router shapes
+# Router alone (the expert weights are never read by moe_route): every
+# selection-kernel specialisation at T = 1 (experts per lane 1, 2, 4, 8, 16),
+# the fp64 MFMA logits with token and expert tails and a bias, and the plain
+# tiled logits when H is not a multiple of 64.
+@pytest.mark.parametrize("T,E,k,H,bias", [(1, 100, 6, 512, False), (1, 500, 8, 768, True), (1, 1000, 12, 256, False),
+                                          (1, 64, 64, 512, False), (130, 300, 8, 640, True), (100, 40, 5, 352, False),
+                                          (70, 1024, 3, 128, True)],
+                         ids=["T1_E100", "T1_E500_bias", "T1_E1000", "T1_k_eq_E", "T130_E300_bias", "T100_H352",
+                              "T70_E1024_bias"])
+def test_route_shapes(T, E, k, H, bias):
+    rng = np.random.default_rng(T * 7919 + E * 31 + k)
+    wr = (rng.standard_normal((E, H)) * 0.02).astype(np.float32)
+    xb = S.bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    b = (rng.standard_normal(E) * 0.01).astype(np.float32) if bias else None
+    dummy = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    cb = torch.from_numpy(S.codebook()).cuda()
+    dl = M.DeviceLayer(H, 256, E, k, S.FMT_CB2, S.FMT_Q2K, dummy, dummy, dummy, cb, torch.from_numpy(wr).cuda())
+    r = M.Routing(T, k, E)
+    x = torch.from_numpy(xb.view(np.int16)).cuda()
+    bt = torch.from_numpy(b).cuda() if bias else None
+    M.route(dl, x, M.ACT_BF16, T, bt, r, dl.workspace(T, M.PATH_ROUTE))
+    torch.cuda.synchronize()
+    idx, w, _ = R.route(S.bf16_to_f32(xb), wr, k, b)
+    off, perm, inv = R.group(idx, E)
+    check_route(r, idx, w, off, perm, inv)
