@@ -643,6 +643,236 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
     np_epilogue<GATEUP, NMF, DEC>(p, t, acc);
 }
 
+// ---------------------------------------------------------------------------
+// Prefill down-projection body for routed tiles on v_mfma_f32_32x32x16_bf16
+// (measured on the MI355X at almost twice the rate of the 16x16x32 shape).
+// Same tiling as above (96-row tiles, 8 waves, 64 GEMM columns per wave) with
+// 32-row fragments and two 32-column fragments per wave.  Lane l supplies
+// column (or row, for A) l % 32 and K group kg = l / 32 of each MFMA step
+// (K = 16).  K order inside a 256-weight block: step 8h + s (half h,
+// s = 0..7) gives lane half kg the 8-weight group 16 kg + 8 h + s, so each
+// lane walks 128 consecutive weights of its row per block; the activations
+// are staged with the same permutation.  D element v of lane l is row
+// 8 (v / 4) + 4 kg + v % 4, column l % 32.  Gate/up passes and the shared
+// expert stay on the 16x16x32 bodies, which measured faster for them.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// one lane's bytes of one Q2_K block or one Q4_K half-block
+struct C32Q2K { uint32_t dd; uint2 sc; uint2 c[4]; };
+struct C32Q4K { uint32_t dd, s0, s1, s2; u32x4 c[2]; };
+template <int FMT> struct C32Of { using T = C32Q2K; };
+template <> struct C32Of<FMT_Q4K> { using T = C32Q4K; };
+
+// Q2_K: b is the block, h the half of this lane's 32 code bytes.  Q4_K: b is
+// the half-block (h unused).
+template <int FMT>
+__device__ __forceinline__ void c32_load(const uint8_t *row, int b, int h, int kg, typename C32Of<FMT>::T &r)
+{
+    if constexpr (FMT == FMT_Q2K) {
+        const uint8_t *blk = row + (int64_t)b * 84;
+        if (h == 0) {
+            r.dd = *(const uint32_t *)blk;
+            r.sc = *(const uint2 *)(blk + 4 + 8 * kg);
+            r.c[0] = *(const uint2 *)(blk + 20 + 32 * kg);
+            r.c[1] = *(const uint2 *)(blk + 28 + 32 * kg);
+        } else {
+            r.c[2] = *(const uint2 *)(blk + 36 + 32 * kg);
+            r.c[3] = *(const uint2 *)(blk + 44 + 32 * kg);
+        }
+    } else {
+        const uint8_t *blk = row + (int64_t)(b >> 1) * 144;
+        r.dd = *(const uint32_t *)blk;
+        r.s0 = *(const uint32_t *)(blk + 4);
+        r.s1 = *(const uint32_t *)(blk + 8);
+        r.s2 = *(const uint32_t *)(blk + 12);
+        r.c[0] = *(const u32x4 *)(blk + 16 + 64 * kg + 32 * (b & 1));
+        r.c[1] = *(const u32x4 *)(blk + 32 + 64 * kg + 32 * (b & 1));
+    }
+}
+
+template <int FMT, int NMF>
+__device__ __forceinline__ void np_body32_down(const FfnPass &p, const NpTile &t, uint8_t *As, const uint32_t *tab)
+{
+    static_assert(FMT == FMT_Q2K || FMT == FMT_Q4K, "routed down formats");
+    using Raw = typename C32Of<FMT>::T;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int c32 = lane & 31, kg = lane >> 5, copy = lane & (NP_COPIES - 1);
+    const int nb = t.Kg >> 8;                        // even (checked on the host)
+    const int nhs = 2 * nb;
+
+    // ---- activation staging: 16-byte chunks, swizzled as in the 16x16x32
+    // body; chunk c of a row holds K 128 (c / 8) + 8 (c % 8) .. + 7 of the
+    // half-block, so a lane half reads its 8 consecutive groups
+    constexpr int NCH = NP_BM * 16 / NP_THREADS;
+    uint32_t aoffs[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        const int ci = tid + NP_THREADS * j, r = ci >> 4;
+        const int c = (ci & 15) ^ (r & 15);
+        aoffs[j] = (uint32_t)(np_act_row(p, t, min(r, t.nvalid - 1)) * p.act_stride) + t.k0 + 128 * (c >> 3) + 8 * (c & 7);
+    }
+    u32x4 av[NCH];
+    auto a_load = [&](int hs) {
+        const uint32_t koff = 256 * (hs >> 1) + 64 * (hs & 1);
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) av[j] = *(const u32x4 *)((const uint16_t *)p.act + (aoffs[j] + koff));
+    };
+    auto a_store = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) *(u32x4 *)(As + buf * NP_ABUF + (tid + NP_THREADS * j) * 16) = av[j];
+    };
+    int aoff[8];
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) aoff[s8] = c32 * 256 + (((8 * kg + s8) ^ (c32 & 15)) << 4);
+
+    // ---- weight rows of this lane's two column fragments
+    const uint8_t *wb = p.w0 + (int64_t)t.g * p.w_expert_bytes;
+    const uint8_t *wr[2];
+#pragma unroll
+    for (int cf = 0; cf < 2; ++cf) {
+        const int col = min(t.n0 + wave * 64 + cf * 32 + c32, t.Ng - 1);
+        wr[cf] = wb + (int64_t)col * p.w_row_bytes;
+    }
+
+    f32x16 acc[NMF][2];
+#pragma unroll
+    for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+        for (int cf = 0; cf < 2; ++cf)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[mf][cf][v] = 0.f;
+
+    Raw blk[2][2];                                   // Q2_K: [block parity][fragment]; Q4_K: [half parity][fragment]
+    a_load(0);
+#pragma unroll
+    for (int cf = 0; cf < 2; ++cf) {
+        c32_load<FMT>(wr[cf], 0, 0, kg, blk[0][cf]);
+        if constexpr (FMT == FMT_Q2K) c32_load<FMT>(wr[cf], 0, 1, kg, blk[0][cf]);
+    }
+    a_store(0);
+    __syncthreads();
+
+    for (int b = 0; b < nb; b += 2) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int bb = b + q;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int hs = 2 * bb + h;
+                a_load(min(hs + 1, nhs - 1));
+                // keep the weight loads behind this step's activation loads
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int cf = 0; cf < 2; ++cf) {
+                    if constexpr (FMT == FMT_Q2K) c32_load<FMT>(wr[cf], min(bb + 1, nb - 1), h, kg, blk[q ^ 1][cf]);
+                    else c32_load<FMT>(wr[cf], min(hs + 1, nhs - 1), 0, kg, blk[h ^ 1][cf]);
+                }
+                // per-fragment dequantization state of this half: Q2_K four
+                // sub-block pools, Q4_K two (mul, off) pairs
+                uint32_t plo[2][4], phi[2][4];
+                float pmul[2][2], poff[2][2];
+#pragma unroll
+                for (int cf = 0; cf < 2; ++cf) {
+                    if constexpr (FMT == FMT_Q2K) {
+                        const float d = f16_bits_to_f32(blk[q][cf].dd & 0xffffu), dmin = f16_bits_to_f32(blk[q][cf].dd >> 16);
+                        const uint32_t sw = h ? blk[q][cf].sc.y : blk[q][cf].sc.x;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const uint32_t sm = (sw >> (8 * u)) & 0xffu;
+                            const float mul = d * (float)(sm & 15u), off = dmin * (float)(sm >> 4);
+                            plo[cf][u] = pk_bf16(-off, mul - off);
+                            phi[cf][u] = pk_bf16(2.0f * mul - off, 3.0f * mul - off);
+                        }
+                    } else {
+                        const Raw &r = blk[h][cf];
+                        const uint64_t lo64 = (uint64_t)r.s0 | ((uint64_t)r.s1 << 32);
+                        const uint64_t hi64 = (uint64_t)r.s1 | ((uint64_t)r.s2 << 32);
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const int j = 4 * kg + 2 * h + u;
+                            const int bsc = 6 * j, bm = 6 * (8 + j);
+                            const uint32_t sc = (uint32_t)(bsc < 32 ? lo64 >> bsc : hi64 >> (bsc - 32)) & 63u;
+                            const uint32_t m = (uint32_t)(hi64 >> (bm - 32)) & 63u;
+                            pmul[cf][u] = f16_bits_to_f32(r.dd & 0xffffu) * (float)sc;
+                            poff[cf][u] = f16_bits_to_f32(r.dd >> 16) * (float)m;
+                        }
+                    }
+                }
+                const uint8_t *ab = As + h * NP_ABUF;
+#pragma unroll
+                for (int s8 = 0; s8 < 8; ++s8) {
+                    bf16x8 a[NMF];
+#pragma unroll
+                    for (int mf = 0; mf < NMF; ++mf) a[mf] = *(const bf16x8 *)(ab + aoff[s8] + mf * 8192);
+                    bf16x8 bq[2];
+#pragma unroll
+                    for (int cf = 0; cf < 2; ++cf) {
+                        uint32_t o[4];
+                        if constexpr (FMT == FMT_Q2K) {
+                            // code bytes 16 h + 2 s8, +1 of this lane's 32; sub-block 4 h + s8 / 2
+                            const uint2 cw2 = blk[q][cf].c[2 * h + (s8 >> 2)];
+                            const uint32_t cw = (s8 & 2) ? cw2.y : cw2.x;
+                            const uint32_t b0 = (cw >> (16 * (s8 & 1))) & 0xffu, b1 = (cw >> (16 * (s8 & 1) + 8)) & 0xffu;
+                            const uint2 t0 = *(const uint2 *)&tab[(b0 * NP_COPIES + copy) * 2];
+                            const uint2 t1 = *(const uint2 *)&tab[(b1 * NP_COPIES + copy) * 2];
+                            const int u = s8 >> 1;
+                            o[0] = vperm(phi[cf][u], plo[cf][u], t0.x);
+                            o[1] = vperm(phi[cf][u], plo[cf][u], t0.y);
+                            o[2] = vperm(phi[cf][u], plo[cf][u], t1.x);
+                            o[3] = vperm(phi[cf][u], plo[cf][u], t1.y);
+                        } else {
+                            // code dword s8 of this half's eight; sub-block 2 h + s8 / 4
+                            const uint32_t cw = blk[h][cf].c[s8 >> 2][s8 & 3];
+                            const uint32_t lo = cw & 0x0f0f0f0fu, hi = (cw >> 4) & 0x0f0f0f0fu;
+                            const int u = s8 >> 2;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                o[i] = pk_bf16(__builtin_fmaf(pmul[cf][u], ubyte(lo, i), -poff[cf][u]),
+                                               __builtin_fmaf(pmul[cf][u], ubyte(hi, i), -poff[cf][u]));
+                        }
+                        bq[cf] = __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
+                    }
+#pragma unroll
+                    for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+                        for (int cf = 0; cf < 2; ++cf) acc[mf][cf] = mfma32x32x16(a[mf], bq[cf], acc[mf][cf]);
+                }
+                a_store(h ^ 1);
+                __syncthreads();
+            }
+        }
+    }
+
+    // ---- epilogue: fp32 rows of the down output
+#pragma unroll
+    for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int i = mf * 32 + 8 * (v >> 2) + 4 * kg + (v & 3);
+            if (i >= t.nvalid) continue;
+            const int64_t pos = t.row0 + i;
+#pragma unroll
+            for (int cf = 0; cf < 2; ++cf) {
+                const int n = t.n0 + wave * 64 + cf * 32 + c32;
+                if (n < t.Ng) ((float *)p.out)[pos * p.out_stride + n] = acc[mf][cf][v];
+            }
+        }
+}
+
+template <int FMT>
+__device__ __forceinline__ void np_dispatch32_down(const FfnPass &p, const NpTile &t, uint8_t *As, const uint32_t *tab)
+{
+    const int nmf = (t.nvalid + 31) >> 5;
+    if (nmf <= 1) np_body32_down<FMT, 1>(p, t, As, tab);
+    else if (nmf == 2) np_body32_down<FMT, 2>(p, t, As, tab);
+    else np_body32_down<FMT, 3>(p, t, As, tab);
+}
+
 // decode tiles are at most 32 rows (2 fragments), prefill tiles 96 (6)
 template <int FMT, bool GATEUP, bool DEC, bool TWO, int MAXF>
 __device__ __forceinline__ void np_dispatch(const FfnPass &p, const NpTile &t, uint8_t *As, const uint32_t *tab)
@@ -684,7 +914,10 @@ __global__ __launch_bounds__(NP_THREADS) void np_kernel(FfnPass p, int S)
     } else {
         np_build_table<FMT>(p, tab);
         __syncthreads();
-        np_dispatch<FMT, GATEUP, DEC, TWO, DEC ? 2 : 6>(p, t, As, tab);
+        if constexpr (!DEC && !TWO && !GATEUP && (FMT == FMT_Q2K || FMT == FMT_Q4K))
+            np_dispatch32_down<FMT>(p, t, As, tab);
+        else
+            np_dispatch<FMT, GATEUP, DEC, TWO, DEC ? 2 : 6>(p, t, As, tab);
     }
 }
 
