@@ -37,7 +37,7 @@ def log(msg):
 
 
 # sources that define each timed kernel (plus the shared headers)
-_KERNEL_SOURCES = {"dec_": ["decode.hip"], "route_": ["route.hip"], "ffn_prefill_": ["prefill.hip", "ffn.hip"],
+_KERNEL_SOURCES = {"dec_": ["decode.hip", "decode.h"], "route_": ["route.hip"], "ffn_prefill_": ["prefill.hip", "ffn.hip"],
                    "ffn_schedule": ["ffn.hip"], "combine": ["ffn.hip"]}
 
 

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <string>
 
+#include "decode.h"
 #include "kernels.h"
 #include "route.h"
 #include "probe.h"
@@ -136,8 +137,8 @@ struct FfnWs {
     float *part_sh, *O_sh;
     float *sh_part;                   // batched decode: shared-expert K-part partial sums
     int ks_gu, ks_dn;                 // its K parts for gate/up and down (0: not split)
-    uint16_t *h_hi, *h_lo;
-    float *X;
+    float *part_rt;
+    int nkc;
 };
 
 // single-token decode kernels apply: T == 1, CB2/Q2K, shapes they support
@@ -160,15 +161,12 @@ FfnWs ffn_ws(const moe_layer *L, int T, bool prefill, bool single, char *base)
     size_t off = 0;
     w.single = single;
     if (w.single) {
-        const size_t k = L->top_k, H = L->hidden, Ish = L->sh_inter, nbI = nblocks(L->inter);
+        const size_t k = L->top_k, H = L->hidden, Ish = L->sh_inter;
         w.part_sh = (float *)(base + off);
         off = align_up(off + DEC_SH_KQ * 2 * Ish * sizeof(float));
-        w.h_hi = (uint16_t *)(base + off);
-        off = align_up(off + k * w.hstride * 2);
-        w.h_lo = (uint16_t *)(base + off);
-        off = align_up(off + k * w.hstride * 2);
-        w.X = (float *)(base + off);
-        off = align_up(off + k * nbI * 16 * sizeof(float));
+        w.nkc = (int)((H + 256 * DEC_LUT_KB - 1) / (256 * DEC_LUT_KB));
+        w.part_rt = (float *)(base + off);
+        off = align_up(off + (size_t)w.nkc * k * 2 * L->inter * sizeof(float));
         w.O = (float *)(base + off);
         off = align_up(off + k * H * sizeof(float));
         w.O_sh = (float *)(base + off);
@@ -248,7 +246,7 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
         d.sg = (const uint16_t *)L->sh_gate; d.su = (const uint16_t *)L->sh_up; d.sd = (const uint16_t *)L->sh_down;
         d.codebook = L->codebook;
         d.x = x; d.x_f32 = act == MOE_ACT_F32;
-        d.h_hi = w.h_hi; d.h_lo = w.h_lo; d.hstride = w.hstride; d.X = w.X;
+        d.nkc = w.nkc; d.part_rt = w.part_rt;
         d.part_sh = w.part_sh;
         d.O = w.O; d.O_sh = w.O_sh; d.y = y;
         dec_plan(d);

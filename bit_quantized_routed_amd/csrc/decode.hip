@@ -35,25 +35,21 @@
 #include <atomic>
 
 #include "common.h"
+#include "decode.h"
 #include "kernels.h"
 
 namespace moe {
 
 constexpr int D1_THREADS = 512;
-constexpr int GU_ROWS = 32;        // rows of a routed gate/up unit (two 16-row halves)
-constexpr int GU_MAXL = 9;         // u32x4 per thread of a routed gate/up unit (2 * 32 * rb <= 512 * 9 * 16 B)
 constexpr int SH_KQ = DEC_SH_KQ;   // K parts of the shared gate/up
 constexpr int SH_MAXS = 4;         // shared gate/up K steps (of 32) per wave and unit
 constexpr int DN_ROWS = 128;       // output rows of a down unit (16 per wave)
 constexpr int DN_KPART = 512;      // K part of a shared down unit
 constexpr int DN_MAXB = 8;         // Q2_K blocks per row of a routed down unit (I <= 2048)
-constexpr int DN_STAGE = 4;        // h staging slots per thread: k * (I/256) * 32 <= 512 * 4
-// Interleaved codebook copies in LDS: lane l reads copy l % copies, so the
-// lanes the LDS serves together for a 16-byte read hit distinct bank groups
-// whatever entries they look up (sixteen copies measured faster than eight;
-// fp32 x leaves room for eight only).
-__host__ __device__ constexpr int cb_copies(bool xf32) { return xf32 ? 8 : 16; }
+constexpr int DN_MAXKC = 8;        // K chunks of the routed gate/up tables (H <= 8192)
 constexpr size_t LDS_MAX = 160 * 1024;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ void split_bf16(float v, uint32_t &hi, uint32_t &lo)
 {
@@ -102,38 +98,32 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_gateup_kernel(DecPass p)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int fr = lane & 15, fc = lane >> 4;
     const int H = p.H;
-    uint16_t *xh = (uint16_t *)dsm;                               // [H]
-    uint16_t *xl = xh + H;                                        // [H] (fp32 x only)
-    float *red = (float *)(dsm + (XF32 ? 4 : 2) * (size_t)H);     // [8 waves][2][16]
-    constexpr int NCOP = cb_copies(XF32);
-    uint16_t *cbt = (uint16_t *)(red + 256);                      // [256][NCOP copies][8] bf16 codewords
-    uint8_t *wt = (uint8_t *)(cbt + 256 * NCOP * 8);              // [2][32][rb]
 
     const bool shared_role = (int)blockIdx.x < p.gu_sh_wg;
-    const int n_units = shared_role ? (p.Ish / 16) * SH_KQ : p.k * (p.I / GU_ROWS);
     const int G = shared_role ? p.gu_sh_wg : p.gu_rt_wg;
     int u = shared_role ? (int)blockIdx.x : (int)blockIdx.x - p.gu_sh_wg;
-    if (u >= n_units) return;                                     // uniform over the work-group
-
-    // ---- x (hi, and lo for fp32 x) into LDS once
-    for (int i = tid; i < H / 8; i += D1_THREADS) {
-        if (XF32) {
-            const float *src = (const float *)p.x + 8 * i;
-            uint32_t h[8], l[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) split_bf16(src[e], h[e], l[e]);
-            *(u32x4 *)&xh[8 * i] = pack8(h);
-            *(u32x4 *)&xl[8 * i] = pack8(l);
-        } else {
-            *(u32x4 *)&xh[8 * i] = *(const u32x4 *)((const uint16_t *)p.x + 8 * i);
-        }
-    }
 
     if (shared_role) {
         // ---------------------------------------------- shared expert
+        const int n_units = (p.Ish / 16) * SH_KQ;
+        if (u >= n_units) return;                                 // uniform over the work-group
+        uint16_t *xh = (uint16_t *)dsm;                           // [H]
+        uint16_t *xl = xh + H;                                    // [H] (fp32 x only)
+        float *red = (float *)(dsm + (XF32 ? 4 : 2) * (size_t)H); // [8 waves][2][16]
+        // x (hi, and lo for fp32 x) into LDS once
+        for (int i = tid; i < H / 8; i += D1_THREADS) {
+            if (XF32) {
+                const float *src = (const float *)p.x + 8 * i;
+                uint32_t h[8], l[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) split_bf16(src[e], h[e], l[e]);
+                *(u32x4 *)&xh[8 * i] = pack8(h);
+                *(u32x4 *)&xl[8 * i] = pack8(l);
+            } else {
+                *(u32x4 *)&xh[8 * i] = *(const u32x4 *)((const uint16_t *)p.x + 8 * i);
+            }
+        }
         const int KQ = H / SH_KQ, nsteps = KQ / 32;
-        // two register buffers in turn: unit u+G loads into one while unit u
-        // computes from the other (no copies, so no early waits on the loads)
         u32x4 ga[SH_MAXS], ua[SH_MAXS], gb[SH_MAXS], ub[SH_MAXS];
         auto load = [&](int uu, u32x4 (&G4)[SH_MAXS], u32x4 (&U4)[SH_MAXS]) {
             const int r0 = (uu / SH_KQ) * 16, k0 = (uu % SH_KQ) * KQ;
@@ -196,141 +186,143 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_gateup_kernel(DecPass p)
     }
 
     // -------------------------------------------------- routed experts
-    const int n_rt = p.I / GU_ROWS;
-    const int rb = p.gu_row_bytes;
-    const int n32 = 2 * rb;                                       // u32x4 per 32-row tile of one matrix
+    // Work-group r owns K chunk kc = r % nkc (DEC_LUT_KB blocks of 256) and
+    // takes the tiles r / nkc, r / nkc + R, ... (R = work-groups per chunk).
+    // Tile t is 128 features of one top-k slot, their gate and up rows.  The
+    // work-group first builds the chunk's table T[g][c] = sum_v C[c][v]
+    // x[8g + v] for its 32 * DEC_LUT_KB groups g and all 256 codewords c, one
+    // MFMA per 32 x 32 tile (K = 16: x hi in K 0..7, x lo in K 8..15, the
+    // codeword in both); then each 8-weight group of a row costs one 4-byte LDS
+    // read.  Wave w reads block w % 4 of the chunk from the gate (w < 4) or up
+    // rows of features 64 i + lane (i = 0, 1) of the tile, straight into
+    // registers.  The block sums of a row meet in LDS and one fp32 partial per
+    // row and chunk goes to part_rt; the down launch adds them in chunk order.
+    const int nkc = p.nkc, R = G / nkc;
+    const int kc = u % nkc, j0 = u / nkc;
+    if (j0 >= R) return;                                          // uniform over the work-group
+    const int nbH = H >> 8, rb = p.gu_row_bytes;
+    const int kb = min(DEC_LUT_KB, nbH - DEC_LUT_KB * kc);        // blocks in this chunk (2 or 4: H % 512 == 0)
+    float *tab = (float *)dsm;                                    // [32 * DEC_LUT_KB groups][256 codewords]
+    float *red = tab + 32 * DEC_LUT_KB * 256;                     // [2][4 blocks][256 rows]
     if (tid < p.k) kid[tid] = clamp_expert(p.topk_idx[tid], p.E);
-    // the codebook in NCOP interleaved copies: entry e, copy c at
-    // 16 * (e * NCOP + c) bytes (one 8-byte load per entry and copy)
-    for (int i = tid; i < 256 * NCOP; i += D1_THREADS) {
-        const int e = i / NCOP;
-        const uint64_t cw = *(const uint64_t *)(p.codebook + 8 * e);
-        uint32_t h[8];
+    __syncthreads();                                              // expert ids staged
+    // this wave's block of the chunk; waves past a short chunk re-read its
+    // last block and their sums are not added.  Blocks start 2-byte aligned
+    // (rows are 4-byte aligned): the 40-byte window from the aligned address
+    // at or below the block covers it, and stays in the row (a block at a
+    // dword boundary is never the last one, since every row has an even
+    // number of blocks).
+    const int bw = wave & 3, hr = wave >> 2;
+    const int B = DEC_LUT_KB * kc + min(bw, kb - 1);
+    const int boff = (38 * B) & ~3;
+    const bool odd = __builtin_amdgcn_readfirstlane(B & 1);
+    const float *tb = tab + 32 * 256 * min(bw, kb - 1);
+    const int nft = p.I / 128, ntile = p.k * nft;
+    const uint8_t *wmat = hr ? p.wu : p.wg;
+    auto rowp = [&](int t, int i) -> const uint32_t * {
+        const int s = t / nft, f = 128 * (t - s * nft) + 64 * i + lane;
+        return (const uint32_t *)(wmat + (int64_t)kid[s] * p.gu_expert_bytes + (int64_t)f * rb + boff);
+    };
+    uint32_t wa[2][10], wb2[2][10];
+    auto load = [&](int t, uint32_t (&W)[2][10]) {
 #pragma unroll
-        for (int v = 0; v < 8; ++v) h[v] = f32_to_bf16_exact((float)(int8_t)(cw >> (8 * v)));
-        *(u32x4 *)&cbt[8 * i] = pack8(h);
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t *src = rowp(t, i);
+#pragma unroll
+            for (int e = 0; e < 10; ++e) W[i][e] = src[e];
+        }
+    };
+    // the first tile loads while the table is built
+    int t = j0;
+    load(t, wa);
+    {
+        // wave w: codewords 32 w .. 32 w + 31 against each 32-group tile
+        const int c = 32 * wave + (lane & 31), hl = lane >> 5;
+        const uint64_t cw = *(const uint64_t *)(p.codebook + 8 * c);
+        uint32_t cb[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) cb[v] = f32_to_bf16_exact((float)(int8_t)(cw >> (8 * v)));
+        const bf16x8 Bc = __builtin_bit_cast(bf16x8, pack8(cb));
+        for (int gt = 0; gt < kb; ++gt) {
+            const int k = 256 * (DEC_LUT_KB * kc + gt) + 8 * (lane & 31);
+            bf16x8 A = {};
+            if (XF32) {
+                const f32x4 v0 = *(const f32x4 *)((const float *)p.x + k), v1 = *(const f32x4 *)((const float *)p.x + k + 4);
+                const float xv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                uint32_t h8[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    uint32_t hi, lo;
+                    split_bf16(xv[e], hi, lo);
+                    h8[e] = hl ? lo : hi;
+                }
+                A = __builtin_bit_cast(bf16x8, pack8(h8));
+            } else if (hl == 0) {
+                A = *(const bf16x8 *)((const uint16_t *)p.x + k);
+            }
+            f32x16 D = {};
+            D = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bc, D, 0, 0, 0);
+            // D element v of lane l: group 8 (v / 4) + 4 (l / 32) + v % 4 of the tile, codeword c
+#pragma unroll
+            for (int v = 0; v < 16; ++v) tab[(32 * gt + 8 * (v >> 2) + 4 * hl + (v & 3)) * 256 + c] = D[v];
+        }
     }
-    __syncthreads();                                              // x, codebook, expert ids staged
-    // one register buffer: the next unit is in flight while this one is
-    // computed from LDS
-    u32x4 buf[GU_MAXL];
-    auto load = [&](int uu) {
-        const int slot = uu / n_rt, rt = uu % n_rt;
-        const int64_t off = (int64_t)kid[slot] * p.gu_expert_bytes + (int64_t)rt * GU_ROWS * rb;
-        const u32x4 *sg4 = (const u32x4 *)(p.wg + off);
-        const u32x4 *su4 = (const u32x4 *)(p.wu + off);
-        // unconditional loads; indices past the unit re-read its last chunk
+    // one row's block: sum over sub-blocks of s_j * (four table entries), times d
+    auto task = [&](const uint32_t (&W)[10], auto sh2) -> float {
+        constexpr bool SH2 = decltype(sh2)::value;
+        uint32_t d16, sc, ix[8];
+        if constexpr (SH2) {
+            d16 = W[0] >> 16;
+            sc = W[1];
 #pragma unroll
-        for (int j = 0; j < GU_MAXL; ++j) {
-            const int i = tid + D1_THREADS * j;
-            buf[j] = i < n32 ? sg4[i] : su4[min(i - n32, n32 - 1)];
+            for (int m = 0; m < 8; ++m) ix[m] = W[2 + m];
+        } else {
+            d16 = W[0] & 0xffffu;
+            sc = __builtin_amdgcn_alignbyte(W[1], W[0], 2);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) ix[m] = __builtin_amdgcn_alignbyte(W[2 + m], W[1 + m], 2);
         }
-    };
-    const int nbH = rb / 38;
-    const int half = wave >> 2, kq = wave & 3;
-    const int cbc = lane % NCOP;                                  // this lane's codebook copy
-    const uint16_t *xa = XF32 && (fr & 1) ? xl : xh;             // this lane's A row (rows 0, 1 used)
-    const int b0 = (nbH * kq) / 4, b1 = (nbH * (kq + 1)) / 4;
-    const uint8_t *rowg = wt + (16 * half + fr) * rb, *rowu = wt + (GU_ROWS + 16 * half + fr) * rb;
-    // per block: raw header words and this lane's eight index bytes of gate and up
-    struct Hdr { uint32_t dg, du, sg, su; int ig[8], iu[8]; };
-    auto read_hdr = [&](int b, Hdr &h) {
-        const uint8_t *bkg = rowg + 38 * b, *bku = rowu + 38 * b;
-        h.dg = *(const uint16_t *)bkg;
-        h.du = *(const uint16_t *)bku;
-        h.sg = *(const uint16_t *)(bkg + 2) | ((uint32_t)*(const uint16_t *)(bkg + 4) << 16);
-        h.su = *(const uint16_t *)(bku + 2) | ((uint32_t)*(const uint16_t *)(bku + 4) << 16);
-#pragma unroll
-        for (int sb = 0; sb < 8; ++sb) { h.ig[sb] = bkg[6 + 4 * sb + fc]; h.iu[sb] = bku[6 + 4 * sb + fc]; }
-    };
-    // codebook entries, A rows and MFMAs of block b from its header
-    auto block = [&](int b, const Hdr &h, float &acc_g, float &acc_u) {
-        bf16x8 Bg[8], Bu[8];
+        float acc = 0.f;
 #pragma unroll
         for (int sb = 0; sb < 8; ++sb) {
-            // index bytes are below 256 (the loads zero-extend; the loop-carried
-            // copies lose that fact, and the mask it would cost is per lookup)
-            __builtin_assume((unsigned)h.ig[sb] < 256u && (unsigned)h.iu[sb] < 256u);
-            Bg[sb] = *(const bf16x8 *)&cbt[8 * (h.ig[sb] * NCOP + cbc)];
-            Bu[sb] = *(const bf16x8 *)&cbt[8 * (h.iu[sb] * NCOP + cbc)];
+            const uint32_t w = ix[sb];
+            const float *t4 = tb + 4 * sb * 256;
+            const float tv = (t4[w & 255u] + t4[256 + ((w >> 8) & 255u)]) + (t4[512 + ((w >> 16) & 255u)] + t4[768 + (w >> 24)]);
+            acc += (float)((sc >> (4 * sb)) & 15u) * tv;
         }
-        bf16x8 a[8];
-        act_block<XF32>(xa, 256 * b + 8 * fc, 32, fr, a);
-        // the eight 4-bit sub-block scales spread over bytes: even sub-blocks
-        // in one word, odd ones in another, each byte converted by one
-        // instruction
-        const uint32_t sge = h.sg & 0x0F0F0F0Fu, sgo = (h.sg >> 4) & 0x0F0F0F0Fu;
-        const uint32_t sue = h.su & 0x0F0F0F0Fu, suo = (h.su >> 4) & 0x0F0F0F0Fu;
-        float bg = 0.f, bu = 0.f;
-#pragma unroll
-        for (int sb = 0; sb < 8; ++sb) {
-            const f32x4 Pg = mfma16x16x32(a[sb], Bg[sb], f32x4{0.f, 0.f, 0.f, 0.f});
-            const f32x4 Pu = mfma16x16x32(a[sb], Bu[sb], f32x4{0.f, 0.f, 0.f, 0.f});
-            // column fr is feature r0+16*half+fr, whose block and sub-block scale this lane read
-            const float sg = (float)(((sb & 1 ? sgo : sge) >> (8 * (sb >> 1))) & 0xffu);
-            const float su = (float)(((sb & 1 ? suo : sue) >> (8 * (sb >> 1))) & 0xffu);
-            bg += sg * (XF32 ? Pg[0] + Pg[1] : Pg[0]);
-            bu += su * (XF32 ? Pu[0] + Pu[1] : Pu[0]);
-        }
-        // the block scale d once per block
-        acc_g += f16_bits_to_f32(h.dg) * bg;
-        acc_u += f16_bits_to_f32(h.du) * bu;
+        return f16_bits_to_f32(d16) * acc;
     };
-    load(u);
-    for (;;) {
-        __syncthreads();                                          // previous unit done with wt and red
-        // unconditional stores: lanes past the unit loaded the unit's last chunk
-        // and write those same bytes again
-#pragma unroll
-        for (int j = 0; j < GU_MAXL; ++j) {
-            const int i = min(tid + D1_THREADS * j, 2 * n32 - 1);
-            *(u32x4 *)(wt + 16 * i) = buf[j];
-        }
+    const int64_t cstride = (int64_t)2 * p.k * p.I;               // one K chunk of part_rt
+    auto tile = [&](int tt, int buf, const uint32_t (&W)[2][10]) {
+        float a0, a1;
+        if (odd) { a0 = task(W[0], std::true_type{}); a1 = task(W[1], std::true_type{}); }
+        else { a0 = task(W[0], std::false_type{}); a1 = task(W[1], std::false_type{}); }
+        float *rr = red + (buf * 4 + bw) * 256 + 128 * hr + lane;
+        rr[0] = a0;
+        rr[64] = a1;
         __syncthreads();
-        const int un = u + G;
-        load(un < n_units ? un : u);                              // next unit in flight (unconditional)
-        const int slot = u / n_rt, r0 = (u % n_rt) * GU_ROWS;
-        float acc_g = 0.f, acc_u = 0.f;
-        // two-stage pipeline over the wave's blocks: the header and index
-        // bytes of the next block are read while this block's codebook
-        // entries are looked up and its MFMAs run
-        // (a wave whose K quarter holds no block, at small H, skips this)
-        if (b0 < b1) {
-            Hdr h0, h1;
-            read_hdr(b0, h0);
-            for (int b = b0;;) {
-                read_hdr(min(b + 1, b1 - 1), h1);
-                block(b, h0, acc_g, acc_u);
-                if (++b >= b1) break;
-                read_hdr(min(b + 1, b1 - 1), h0);
-                block(b, h1, acc_g, acc_u);
-                if (++b >= b1) break;
-            }
+        if (tid < 256) {
+            const int s = tt / nft, f0 = 128 * (tt - s * nft);
+            const float *rs = red + buf * 4 * 256 + tid;
+            float sum = rs[0];
+            for (int b = 1; b < kb; ++b) sum += rs[256 * b];
+            p.part_rt[kc * cstride + (int64_t)(2 * s + (tid >> 7)) * p.I + f0 + (tid & 127)] = sum;
         }
-        if (fc == 0) { red[(wave * 2 + 0) * 16 + fr] = acc_g; red[(wave * 2 + 1) * 16 + fr] = acc_u; }
-        __syncthreads();
-        if (tid < 32) {
-            const int hf = tid >> 4, n = tid & 15;
-            float gg = 0.f, uv = 0.f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                gg += red[((hf * 4 + q) * 2 + 0) * 16 + n];
-                uv += red[((hf * 4 + q) * 2 + 1) * 16 + n];
-            }
-            const int r = r0 + 16 * hf + n;
-            const float h = gg / (1.0f + expf(-gg)) * uv;
-            uint32_t hi, lo;
-            split_bf16(h, hi, lo);
-            p.h_hi[(int64_t)slot * p.hstride + r] = (uint16_t)hi;
-            p.h_lo[(int64_t)slot * p.hstride + r] = (uint16_t)lo;
-            // the 16 rows of a half are one 16-wide sub-block of down's K: its sum feeds the min term
-            float sum = h;
-#pragma unroll
-            for (int off = 8; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 16);
-            if (n == 0) p.X[((int64_t)slot * p.nbI + (r >> 8)) * 16 + ((r & 255) >> 4)] = sum;
-        }
-        if (un >= n_units) break;
-        u = un;
+    };
+    __syncthreads();                                              // table staged
+    // two register buffers in turn: the next tile is in flight while this one
+    // is computed.  The prefetch is unconditional (the last tile re-reads its
+    // own rows); the two LDS buffers of block sums alternate, so one barrier
+    // per tile suffices.
+    for (int buf = 0;;) {
+        load(t + R < ntile ? t + R : t, wb2);
+        tile(t, buf, wa);
+        buf ^= 1;
+        if ((t += R) >= ntile) break;
+        load(t + R < ntile ? t + R : t, wa);
+        tile(t, buf, wb2);
+        buf ^= 1;
+        if ((t += R) >= ntile) break;
     }
 }
 
@@ -485,22 +477,8 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_down_kernel(DecPass p)
         const int row = ot * DN_ROWS + 16 * wave + fr;
         if (fc == 0 && row < H) p.O[(int64_t)slot * H + row] = acc - accm;
     };
-    // the first unit's weights go out first; the h staging and the table build
-    // overlap with them (the staging loads are waited for on their own before
-    // the barrier, which also covers the weight loads issued ahead of them)
-    // h staging loads go out first (into registers), then the first unit's
-    // weights; the LDS stores then wait for the staging loads only
-    u32x4 shh[DN_STAGE], shl[DN_STAGE];
-    float sxm[DN_STAGE];
-    const int nst = p.k * nb * 32;
-#pragma unroll
-    for (int j = 0; j < DN_STAGE; ++j) {
-        const int i = min(tid + D1_THREADS * j, nst - 1);
-        const int slot = i / (nb * 32), c = i % (nb * 32);
-        shh[j] = *(const u32x4 *)(p.h_hi + (int64_t)slot * p.hstride + 8 * c);
-        shl[j] = *(const u32x4 *)(p.h_lo + (int64_t)slot * p.hstride + 8 * c);
-        sxm[j] = p.X[min(i, p.k * nb * 16 - 1)];
-    }
+    // the first unit's weights go out first; the code table is built and h is
+    // formed while they are in flight
     load(u_begin, ca, sa, da);
     for (int i = tid; i < 16 * 256; i += D1_THREADS) {
         const int sc = i >> 8, byte = i & 255;
@@ -509,13 +487,45 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_down_kernel(DecPass p)
         for (int t = 0; t < 4; ++t) v[t] = f32_to_bf16_exact((float)(sc * ((byte >> (2 * t)) & 3)));
         *(uint2 *)&tab[4 * i] = uint2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
     }
-    // unconditional stores (indices past the end rewrite the last entry with its own value)
+    // h of the slots this work-group's units use: the gate and up partial sums
+    // of the K chunks added in chunk order, then silu(g) * u as two bf16 terms,
+    // and the per-16 sums of h for the min term.  Four features per thread and
+    // pass; I % 256 == 0 keeps whole waves in or out of a pass (the four lanes
+    // of a 16-wide sub-block are adjacent).
+    {
+        const int I = p.I, s0 = u_begin / n_ot, s1 = (u_end - 1) / n_ot;
+        const int nq = (s1 - s0 + 1) * (I / 4);
+        const int64_t cstride = (int64_t)2 * p.k * I;             // one K chunk of part_rt
+        for (int q0 = 0; q0 < nq; q0 += D1_THREADS) {
+            const int q = q0 + tid;
+            if (q >= nq) break;                                    // uniform over each wave
+            const int slot = s0 + q / (I / 4), f = 4 * (q % (I / 4));
+            const float *pg = p.part_rt + (int64_t)2 * slot * I + f;
+            f32x4 gv[DN_MAXKC], uv[DN_MAXKC];
 #pragma unroll
-    for (int j = 0; j < DN_STAGE; ++j) {
-        const int i = min(tid + D1_THREADS * j, nst - 1);
-        *(u32x4 *)&hh[8 * i] = shh[j];
-        *(u32x4 *)&hl[8 * i] = shl[j];
-        xm[min(i, p.k * nb * 16 - 1)] = sxm[j];
+            for (int c = 0; c < DN_MAXKC; ++c) {
+                const int64_t o = cstride * min(c, p.nkc - 1);
+                gv[c] = *(const f32x4 *)(pg + o);
+                uv[c] = *(const f32x4 *)(pg + o + I);
+            }
+            f32x4 g = gv[0], uu = uv[0];
+#pragma unroll
+            for (int c = 1; c < DN_MAXKC; ++c)
+                if (c < p.nkc) { g += gv[c]; uu += uv[c]; }
+            uint32_t hi[4], lo[4];
+            float hs = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float h = g[e] / (1.0f + expf(-g[e])) * uu[e];
+                split_bf16(h, hi[e], lo[e]);
+                hs += h;
+            }
+            *(uint2 *)&hh[slot * I + f] = uint2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+            *(uint2 *)&hl[slot * I + f] = uint2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+            hs += __shfl_xor(hs, 1, 64);
+            hs += __shfl_xor(hs, 2, 64);
+            if ((lane & 3) == 0) xm[slot * nb * 16 + (f >> 4)] = hs;
+        }
     }
     __syncthreads();
     for (int u = u_begin;;) {                                      // unconditional prefetch, as above
@@ -574,10 +584,13 @@ int cu_count()
     return n;
 }
 
-size_t lds_gateup(int H, int gu_row_bytes, bool xf32)
+// shared role: x (one or two bf16 terms) and the wave sums; routed role: the
+// chunk's table and the two buffers of block sums.  One launch, so the larger.
+size_t lds_gateup(int H, bool xf32)
 {
-    return (size_t)(xf32 ? 4 : 2) * H + 256 * sizeof(float) + 256 * cb_copies(xf32) * 16 +
-           2 * GU_ROWS * (size_t)gu_row_bytes;
+    const size_t sh = (size_t)(xf32 ? 4 : 2) * H + 256 * sizeof(float);
+    const size_t rt = (32 * DEC_LUT_KB * 256 + 2 * 4 * 256) * sizeof(float);
+    return std::max(sh, rt);
 }
 
 size_t lds_down(int nbI, int k) { return 16 * 256 * 4 * 2 + (size_t)k * (2 * (size_t)nbI * 256 * 2 + (size_t)nbI * 32 * 2); }
@@ -617,31 +630,36 @@ void split_roles(int n_a, double c_a, int n_b, double c_b, int G, int &g_a, int 
 }
 
 // Time per byte of a routed unit relative to a bf16 shared-expert unit, as
-// measured per work-group on the MI355X: a codebook unit is bound by its LDS
-// table reads (16 bytes per 1.19 bytes of weights), a Q2_K unit by its LDS
-// table reads and VALU work.  The role split gives each role work in
-// proportion to these costs.
-constexpr double CB2_COST = 2.9;
+// measured per work-group on the MI355X: a codebook tile is bound by its LDS
+// table reads (one 4-byte read per 8 weights) and its rows' strided bytes, a
+// Q2_K unit by its LDS table reads and VALU work.  The role split gives each
+// role work in proportion to these costs.
+constexpr double CB2_COST = 2.0;
 constexpr double Q2K_COST = 1.55;
 
 }  // namespace
 
 bool dec_single_ok(int T, int H, int I, int Ish, int k, int gu_row_bytes, bool x_f32)
 {
-    return T == 1 && k <= 64 && H % 512 == 0 && (Ish == 0 || Ish % DN_KPART == 0) && I % 256 == 0 &&
-           I / 256 <= DN_MAXB && k * (I / 256) * 32 <= D1_THREADS * DN_STAGE && 4 * gu_row_bytes <= D1_THREADS * GU_MAXL && H / SH_KQ / 32 <= 8 * SH_MAXS &&
-           lds_gateup(H, gu_row_bytes, x_f32) <= LDS_MAX && lds_down(I / 256, k) <= LDS_MAX;
+    return T == 1 && k <= 64 && H % 512 == 0 && H <= 256 * DEC_LUT_KB * DN_MAXKC && (Ish == 0 || Ish % DN_KPART == 0) &&
+           I % 256 == 0 && I / 256 <= DN_MAXB && gu_row_bytes == 38 * (H / 256) && H / SH_KQ / 32 <= 8 * SH_MAXS &&
+           lds_gateup(H, x_f32) <= LDS_MAX && lds_down(I / 256, k) <= LDS_MAX;
 }
 
 void dec_plan(DecPass &p)
 {
     const int ncu = cu_count();
-    const size_t lgu = lds_gateup(p.H, p.gu_row_bytes, p.x_f32);
+    const size_t lgu = lds_gateup(p.H, p.x_f32);
     const int occ_gu = p.x_f32 ? resident(dec1_gateup_kernel<true>, lgu, occ_gu_f32)
                                : resident(dec1_gateup_kernel<false>, lgu, occ_gu_bf16);
     const int occ_d = resident(dec1_down_kernel, lds_down(p.nbI, p.k), occ_dn);
-    split_roles((p.Ish / 16) * SH_KQ, 16.0 * (p.H / SH_KQ) * 2 * 2, p.k * (p.I / GU_ROWS),
-                CB2_COST * 2.0 * GU_ROWS * p.gu_row_bytes, occ_gu * ncu, p.gu_sh_wg, p.gu_rt_wg);
+    // routed gate/up: work-groups in whole multiples of the K chunk count
+    const int n_sh = (p.Ish / 16) * SH_KQ, ntile = p.k * p.I / 128, G = occ_gu * ncu;
+    int g_sh = 0, g_rt = 0;
+    split_roles(n_sh, 16.0 * (p.H / SH_KQ) * 2 * 2, p.nkc * ntile, CB2_COST * 256.0 * DEC_LUT_KB * 38, G, g_sh, g_rt);
+    const int R = std::max(1, std::min(ntile, (g_rt + p.nkc / 2) / p.nkc));
+    p.gu_rt_wg = R * p.nkc;
+    p.gu_sh_wg = n_sh ? std::max(1, std::min(n_sh, G - p.gu_rt_wg)) : 0;
     const int n_ot = (p.H + DN_ROWS - 1) / DN_ROWS;
     split_roles(n_ot * (p.Ish / DN_KPART), (double)DN_ROWS * DN_KPART * 2, p.k * n_ot,
                 Q2K_COST * DN_ROWS * p.d_row_bytes, occ_d * ncu, p.dn_sh_wg, p.dn_rt_wg);
@@ -650,7 +668,7 @@ void dec_plan(DecPass &p)
 hipError_t launch_dec_gateup(const DecPass &p, hipStream_t s)
 {
     const int grid = p.gu_sh_wg + p.gu_rt_wg;
-    const size_t lds = lds_gateup(p.H, p.gu_row_bytes, p.x_f32);
+    const size_t lds = lds_gateup(p.H, p.x_f32);
     if (p.x_f32) dec1_gateup_kernel<true><<<grid, D1_THREADS, lds, s>>>(p);
     else dec1_gateup_kernel<false><<<grid, D1_THREADS, lds, s>>>(p);
     return hipGetLastError();

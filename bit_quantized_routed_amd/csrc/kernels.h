@@ -55,35 +55,6 @@ void launch_combine(const float *O, const int32_t *inv, const float *topk_w, int
 hipError_t launch_unpack(int fmt, const uint8_t *packed, int64_t rows, int K, const int8_t *codebook,
                          float *out, hipStream_t s);
 
-// single-token decode (T = 1), see decode.hip
-struct DecPass {
-    int T, k, E, H, I, Ish, nbI;
-    const int32_t *topk_idx, *offsets, *inv;
-    const float *topk_w;
-    const uint8_t *wg, *wu, *wd;                 // routed CB2 gate, up; Q2_K down
-    int64_t gu_expert_bytes, d_expert_bytes;
-    int gu_row_bytes, d_row_bytes;
-    const uint16_t *sg, *su, *sd;                // shared expert bf16 (Ish == 0: none)
-    const int8_t *codebook;
-    const void *x;
-    int x_f32;
-    uint16_t *h_hi, *h_lo;                       // [k][hstride] by top-k slot
-    int hstride;
-    float *X;                                    // [k][nbI][16] Q2_K min-term sums of h per 16-wide sub-block
-    float *part_sh;                              // [DEC_SH_KQ][2][Ish] shared gate/up partial sums (K parts)
-    float *O;                                    // [k][H] by top-k slot
-    float *O_sh;                                 // [Ish/512][H]
-    float *y;                                    // [H]
-    int gu_sh_wg, gu_rt_wg;                      // gate/up work-groups: shared, routed role
-    int dn_sh_wg, dn_rt_wg;                      // down work-groups: shared, routed role
-};
-constexpr int DEC_SH_KQ = 8;                     // K parts of the single-token shared gate/up (part_sh)
-bool dec_single_ok(int T, int H, int I, int Ish, int k, int gu_row_bytes, bool x_f32);
-void dec_plan(DecPass &p);                       // fills the work-group split
-hipError_t launch_dec_gateup(const DecPass &p, hipStream_t s);
-hipError_t launch_dec_down(const DecPass &p, hipStream_t s);
-hipError_t launch_dec_combine(const DecPass &p, hipStream_t s);
-
 constexpr int DEC_BM = 16, DEC_BN = 16;
 constexpr int PRE_BM = 64, PRE_BN = 64;
 
