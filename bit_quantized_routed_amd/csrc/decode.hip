@@ -477,8 +477,49 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_down_kernel(DecPass p)
         const int row = ot * DN_ROWS + 16 * wave + fr;
         if (fc == 0 && row < H) p.O[(int64_t)slot * H + row] = acc - accm;
     };
-    // the first unit's weights go out first; the code table is built and h is
-    // formed while they are in flight
+    // h of the slots this work-group's units use: the gate and up partial sums
+    // of the K chunks added in chunk order, then silu(g) * u as two bf16 terms,
+    // and the per-16 sums of h for the min term.  Four features per thread and
+    // pass; I % 256 == 0 keeps whole waves in or out of a pass (the four lanes
+    // of a 16-wide sub-block are adjacent).  The first pass's partials go out
+    // before the first unit's weights, so waiting for them waits for nothing
+    // else; the code table is built while both are in flight.
+    const int I = p.I, s0 = u_begin / n_ot, s1 = (u_end - 1) / n_ot;
+    const int nq = (s1 - s0 + 1) * (I / 4);
+    const int64_t cstride = (int64_t)2 * p.k * I;                 // one K chunk of part_rt
+    f32x4 gv[DN_MAXKC], uv[DN_MAXKC];
+    auto h_load = [&](int q) {
+        const int slot = s0 + q / (I / 4), f = 4 * (q % (I / 4));
+        const float *pg = p.part_rt + (int64_t)2 * slot * I + f;
+#pragma unroll
+        for (int c = 0; c < DN_MAXKC; ++c) {
+            const int64_t o = cstride * min(c, p.nkc - 1);
+            gv[c] = *(const f32x4 *)(pg + o);
+            uv[c] = *(const f32x4 *)(pg + o + I);
+        }
+    };
+    auto h_form = [&](int q) {
+        const int slot = s0 + q / (I / 4), f = 4 * (q % (I / 4));
+        f32x4 g = gv[0], uu = uv[0];
+#pragma unroll
+        for (int c = 1; c < DN_MAXKC; ++c)
+            if (c < p.nkc) { g += gv[c]; uu += uv[c]; }
+        uint32_t hi[4], lo[4];
+        float hs = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float h = g[e] / (1.0f + expf(-g[e])) * uu[e];
+            split_bf16(h, hi[e], lo[e]);
+            hs += h;
+        }
+        *(uint2 *)&hh[slot * I + f] = uint2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+        *(uint2 *)&hl[slot * I + f] = uint2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+        hs += __shfl_xor(hs, 1, 64);
+        hs += __shfl_xor(hs, 2, 64);
+        if ((lane & 3) == 0) xm[slot * nb * 16 + (f >> 4)] = hs;
+    };
+    // pass 0 covers quads [0, 512): nq >= I / 4 >= 64, so at least wave 0 is in it
+    h_load(min(tid, nq - 1));
     load(u_begin, ca, sa, da);
     for (int i = tid; i < 16 * 256; i += D1_THREADS) {
         const int sc = i >> 8, byte = i & 255;
@@ -487,45 +528,12 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_down_kernel(DecPass p)
         for (int t = 0; t < 4; ++t) v[t] = f32_to_bf16_exact((float)(sc * ((byte >> (2 * t)) & 3)));
         *(uint2 *)&tab[4 * i] = uint2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
     }
-    // h of the slots this work-group's units use: the gate and up partial sums
-    // of the K chunks added in chunk order, then silu(g) * u as two bf16 terms,
-    // and the per-16 sums of h for the min term.  Four features per thread and
-    // pass; I % 256 == 0 keeps whole waves in or out of a pass (the four lanes
-    // of a 16-wide sub-block are adjacent).
-    {
-        const int I = p.I, s0 = u_begin / n_ot, s1 = (u_end - 1) / n_ot;
-        const int nq = (s1 - s0 + 1) * (I / 4);
-        const int64_t cstride = (int64_t)2 * p.k * I;             // one K chunk of part_rt
-        for (int q0 = 0; q0 < nq; q0 += D1_THREADS) {
-            const int q = q0 + tid;
-            if (q >= nq) break;                                    // uniform over each wave
-            const int slot = s0 + q / (I / 4), f = 4 * (q % (I / 4));
-            const float *pg = p.part_rt + (int64_t)2 * slot * I + f;
-            f32x4 gv[DN_MAXKC], uv[DN_MAXKC];
-#pragma unroll
-            for (int c = 0; c < DN_MAXKC; ++c) {
-                const int64_t o = cstride * min(c, p.nkc - 1);
-                gv[c] = *(const f32x4 *)(pg + o);
-                uv[c] = *(const f32x4 *)(pg + o + I);
-            }
-            f32x4 g = gv[0], uu = uv[0];
-#pragma unroll
-            for (int c = 1; c < DN_MAXKC; ++c)
-                if (c < p.nkc) { g += gv[c]; uu += uv[c]; }
-            uint32_t hi[4], lo[4];
-            float hs = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float h = g[e] / (1.0f + expf(-g[e])) * uu[e];
-                split_bf16(h, hi[e], lo[e]);
-                hs += h;
-            }
-            *(uint2 *)&hh[slot * I + f] = uint2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
-            *(uint2 *)&hl[slot * I + f] = uint2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
-            hs += __shfl_xor(hs, 1, 64);
-            hs += __shfl_xor(hs, 2, 64);
-            if ((lane & 3) == 0) xm[slot * nb * 16 + (f >> 4)] = hs;
-        }
+    if (tid < nq) h_form(tid);                                     // uniform over each wave
+    for (int q0 = D1_THREADS; q0 < nq; q0 += D1_THREADS) {
+        const int q = q0 + tid;
+        if (q >= nq) break;                                        // uniform over each wave
+        h_load(q);
+        h_form(q);
     }
     __syncthreads();
     for (int u = u_begin;;) {                                      // unconditional prefetch, as above
