@@ -2,35 +2,34 @@
 // decode, where every routed weight is read once per token step while compute
 // idles ("Part 5: 服务层", section 6).  Three launches after the router:
 //
-//   dec1_gateup: gate/up GEMVs + SwiGLU.  One persistent work-group per
-//     resident slot; each takes one role.  Shared-expert units are 16 bf16
-//     rows x one K eighth, loaded straight into MFMA B registers.  Routed
-//     units are 32 rows of gate and 32 of up of one selected expert
-//     (2 x 32 x 1064 B at H = 7168, two contiguous byte ranges), staged
-//     through LDS because the 38-byte blocks are only 2-byte aligned.  While
-//     one unit is computed the next unit's bytes are already in flight.
-//     Codebook entries are exact bf16 MFMA operands; the fp32 sub-block scale
-//     d*s_j multiplies each 32-wide partial sum.  h = silu(g)*u is stored as
-//     two bf16 terms (hi + lo, relative error below 2^-17) with the per-16
-//     sums Q2_K's min term needs; the shared expert stores fp32 partial sums
-//     of its K eighths.
-//   dec1_down: persistent again.  A unit is 128 output rows (16 per wave, each
-//     wave over the whole K) of one selected expert's Q2_K down, or of one
-//     512-wide K part of the bf16 shared down.  Q2_K codes become exact bf16
-//     values sc*q through a 32 KB LDS table indexed by (sc, code byte); the
-//     block scale d and the min term dmin * sum_j m_j X_j apply to the fp32
-//     sums of each 256-wide block.
+//   dec1_gateup: gate/up GEMVs.  One persistent work-group per resident slot;
+//     each takes one role.  Shared-expert units are 16 bf16 rows x one K
+//     eighth, loaded straight into MFMA B registers, x as the A operand.  The
+//     routed role is a table lookup: a work-group owns one 1024-wide K chunk,
+//     builds T[g][c] = codeword c . x[8g .. 8g+7] for the chunk's 128 groups
+//     and all 256 codewords once (fp32, from MFMA with exact operands), then
+//     streams row tiles of the selected experts through it, one 4-byte LDS
+//     read per 8 weights, with the fp32 sub-block scale s_j and block scale d
+//     applied to the sums.  It writes one fp32 partial per row and chunk; the
+//     shared expert writes fp32 partial sums of its K eighths.
+//   dec1_down: persistent again.  A routed work-group first forms h = silu(g)
+//     * u for the slots of its units from the gate/up chunk partials (added
+//     in chunk order) as two bf16 terms (hi + lo, relative error below 2^-17)
+//     with the per-16 sums Q2_K's min term needs.  A unit is 128 output rows
+//     (16 per wave, each wave over the whole K) of one selected expert's Q2_K
+//     down, or of one 512-wide K part of the bf16 shared down.  Q2_K codes
+//     become exact bf16 values sc*q through a 32 KB LDS table indexed by (sc,
+//     code byte); the block scale d and the min term dmin * sum_j m_j X_j
+//     apply to the fp32 sums of each 256-wide block.
 //   dec1_combine: y = the shared expert's K parts in order + the routed
 //     outputs weighted in top-k order.
 //
-// Each codebook lookup reads a 16-byte LDS entry for 1.19 bytes of weights,
-// so a CU streams routed gate/up more slowly than bf16 rows; the role split
-// gives the routed role proportionally more work-groups.  Routed buffers are
-// indexed by top-k slot j (h, X, O), so no kernel needs the grouping arrays at
-// T = 1.  Activation terms (x or h as hi + lo bf16) enter as rows 0 and 1 of
-// the MFMA A operand, so one MFMA covers both.  Work-groups of one launch
-// never wait for each other: results pass between work-groups only across
-// launches.
+// The role split gives each role work-groups in proportion to its measured
+// cost per byte.  Routed buffers are indexed by top-k slot j (partials, O),
+// so no kernel needs the grouping arrays at T = 1.  Activation terms (x or h
+// as hi + lo bf16) enter as rows 0 and 1 of an MFMA A operand, so one MFMA
+// covers both.  Work-groups of one launch never wait for each other: results
+// pass between work-groups only across launches.
 #include <algorithm>
 #include <atomic>
 
