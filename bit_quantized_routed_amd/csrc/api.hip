@@ -299,6 +299,7 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
     if (split) {
         up.sh_parts = w.ks_gu; up.sh_part_out = w.sh_part;
         dn.sh_parts = w.ks_dn; dn.sh_part_out = w.sh_part;
+        up.sched_parts = dn.sched_parts = std::max(w.ks_gu, w.ks_dn);
     }
     if (!pr.before("ffn_schedule")) return hip_fail(hipGetLastError(), "event record");
     launch_ffn_schedule(offsets, T, k, E, has_sh, sched_bm, w.sched, s, np ? NP_BM_SH : sched_bm,

@@ -34,6 +34,8 @@ struct FfnPass {
     // there (gate/up: [q][2][T][Nsh] g and u; down: [q][T][Nsh]) instead of out
     int sh_parts;                     // 0 or 1: one part
     float *sh_part_out;               // null: shared rows go to out like the others
+    int sched_parts;                  // shared K parts the schedule was built with (>= sh_parts; 0 or 1: one);
+                                      // the launch grid covers every tile of that schedule
 };
 
 // tiles of BM rows per routed group and BMsh (<= 0: BM) for the shared group,

@@ -934,8 +934,11 @@ hipError_t np_launch(const FfnPass &p, hipStream_t s)
     }
     const int wg_cols = GATEUP ? 256 : 512;
     const int S = (std::max(p.N, p.Nsh) + wg_cols - 1) / wg_cols;
-    const int tiles = DEC ? ffn_max_tiles(p.T, p.k, p.E, p.Nsh > 0, NP_BM_DEC, NP_BM_DEC)
-                          : ffn_max_tiles(p.T, p.k, p.E, p.Nsh > 0, NP_BM, NP_BM_SH);
+    // every tile the schedule can hold, the shared expert's K parts included
+    // (both passes read one schedule built with the larger part count)
+    const int ks = std::max(p.sched_parts, 1);
+    const int tiles = DEC ? ffn_max_tiles(p.T, p.k, p.E, p.Nsh > 0, NP_BM_DEC, NP_BM_DEC, ks)
+                          : ffn_max_tiles(p.T, p.k, p.E, p.Nsh > 0, NP_BM, NP_BM_SH, ks);
     const int64_t grid = (int64_t)((tiles + 7) / 8) * 8 * S;
     np_kernel<FMT, GATEUP, DEC, TWO><<<dim3((unsigned)grid), NP_THREADS, lds, s>>>(p, S);
     return hipGetLastError();

@@ -280,6 +280,13 @@ def test_full_decode32(big):
     assert sampled_check(big, S.config("decode32"), True, 3) <= DEC_TOL
 
 
+@pytest.mark.parametrize("T", [2, 3, 4, 6])
+def test_full_decode_small_batches(big, T):
+    """Batched decode at the full layer shape for the smallest batches (one or
+    two rows per selected expert, the shared expert in one row tile)."""
+    assert sampled_check(big, S.config("decode32", T=T), True, 1) <= DEC_TOL
+
+
 def test_full_prefill2048(big):
     assert sampled_check(big, S.config("prefill2048"), False, 2) <= PRE_TOL
 
