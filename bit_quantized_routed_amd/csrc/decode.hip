@@ -642,7 +642,7 @@ void split_roles(int n_a, double c_a, int n_b, double c_b, int G, int &g_a, int 
 // Q2_K unit by its LDS table reads and VALU work.  The role split gives each
 // role work in proportion to these costs.
 constexpr double CB2_COST = 2.0;
-constexpr double Q2K_COST = 1.55;
+constexpr double Q2K_COST = 2.5;
 
 }  // namespace
 
