@@ -298,6 +298,53 @@ def read_traffic(kernel, workload):
     return float(m.group(1))
 
 
+SWEEP_T = (1, 2, 4, 8, 16, 24, 32, 48, 64)
+
+
+def sweep(args):
+    """Decode (fp32-accurate) and prefill (bf16 MFMA) paths on the full layer at
+    T = SWEEP_T tokens, Zipf-skewed routing as in decode32: time per step of each,
+    the decode path's algorithmic GB/s, the first T at which prefill is faster,
+    and how far each token's decode output in the batch is from the same token
+    decoded alone (max |difference| relative to max |y|; 0 means bit-identical)."""
+    import torch
+    import synthetic as S
+    import workload as W
+    import bit_quantized_routed_amd as M
+    base = S.config("decode32")
+    wl = W.Workload(base, cache_dir=CACHE, progress=True, replicas=args.replicas)
+    rows = []
+    for T in SWEEP_T:
+        c = S.config("decode32", T=T)
+        row = {"T": T}
+        ys = {}
+        for mode in ("decode", "prefill"):
+            st = Stepper(wl, c, mode == "decode")
+            st.step()
+            torch.cuda.synchronize()
+            if mode == "decode":
+                ys["batch"] = st.y.clone()
+                row["active_experts"] = st.n_active()
+            ms, _, _ = st.timed(args.steps, args.warmup)
+            row[mode + "_ms"] = round(ms, 5)
+        # token 0 alone, on replica 0 as in the batch's first step
+        one = Stepper(wl, S.config("decode32", T=1), True)
+        xb, _ = wl.tokens(c)
+        one.x = xb[:1].contiguous()
+        one.step()
+        torch.cuda.synchronize()
+        d = (one.y[0] - ys["batch"][0]).abs().max().item()
+        row["token0_alone_vs_batch"] = d / max(ys["batch"][0].abs().max().item(), 1e-30)
+        row["decode_GBps"] = round(layer_bytes(c, row["active_experts"], T) / (row["decode_ms"] * 1e-3) / 1e9, 1)
+        row["faster"] = "prefill" if row["prefill_ms"] < row["decode_ms"] else "decode"
+        log("sweep T=%d: %s" % (T, row))
+        rows.append(row)
+    cross = next((r["T"] for r in rows if r["faster"] == "prefill"), None)
+    print(json.dumps({"sweep": "decode vs prefill path, full layer (H=7168, I=2048, E=256, k=8, bf16 shared), "
+                               "Zipf-skewed routing", "steps": args.steps, "warmup": args.warmup,
+                      "rows": rows, "crossover_T": cross}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -308,6 +355,9 @@ def main():
     ap.add_argument("--extra", default="decode32,prefill2048",
                     help="comma-separated extra workloads reported as context ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only the micro-batch sweep: decode and prefill paths at T = 1..64 on the full layer "
+                         "(Zipf-skewed routing), with the crossover T; one JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy 5 times (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -323,6 +373,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.sweep:
+        sweep(args)
         return
     cfg = S.config(args.workload)
     decode = args.workload.startswith("decode")

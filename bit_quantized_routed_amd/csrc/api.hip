@@ -141,11 +141,17 @@ struct FfnWs {
     int nkc;
 };
 
-// single-token decode kernels apply: T == 1, CB2/Q2K, shapes they support
+// Decode batches of up to DEC_TOKENWISE_MAX tokens run the single-token
+// kernels once per token (measured faster than the grouped GEMMs there, since
+// almost every assignment is a distinct expert), so such a token's result does
+// not depend on the batch it came in.  They apply for CB2/Q2K and the shapes
+// the single-token kernels support.
+constexpr int DEC_TOKENWISE_MAX = 4;
 bool dec_single(const moe_layer *L, int T, bool prefill, bool x_f32)
 {
-    if (prefill || L->fmt_gate_up != MOE_FMT_CB2 || L->fmt_down != MOE_FMT_Q2K) return false;
-    return dec_single_ok(T, L->hidden, L->inter, L->sh_inter, L->top_k, nblocks(L->hidden) * 38, x_f32);
+    if (prefill || T < 1 || T > DEC_TOKENWISE_MAX) return false;
+    if (L->fmt_gate_up != MOE_FMT_CB2 || L->fmt_down != MOE_FMT_Q2K) return false;
+    return dec_single_ok(1, L->hidden, L->inter, L->sh_inter, L->top_k, nblocks(L->hidden) * 38, x_f32);
 }
 
 // Workspace carving.  `single` selects the single-token layout; the size a
@@ -199,7 +205,7 @@ size_t ffn_ws_bytes(const moe_layer *L, int T, bool prefill)
 {
     size_t b = ffn_ws(L, T, prefill, false, nullptr).bytes;
     for (int xf = 0; xf < 2; ++xf)
-        if (dec_single(L, T, prefill, xf)) b = std::max(b, ffn_ws(L, T, prefill, true, nullptr).bytes);
+        if (dec_single(L, T, prefill, xf)) b = std::max(b, ffn_ws(L, 1, prefill, true, nullptr).bytes);
     return b;
 }
 
@@ -226,7 +232,8 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
     }
     const size_t need = ffn_ws_bytes(L, T, prefill);
     if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-    FfnWs w = ffn_ws(L, T, prefill, dec_single(L, T, prefill, act == MOE_ACT_F32), (char *)ws);
+    const bool single = dec_single(L, T, prefill, act == MOE_ACT_F32);
+    FfnWs w = ffn_ws(L, single ? 1 : T, prefill, single, (char *)ws);
 
     hipStream_t s = (hipStream_t)stream;
     Prof pr{prof, s};
@@ -236,7 +243,7 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
 
     if (w.single) {
         DecPass d{};
-        d.T = T; d.k = k; d.E = E; d.H = H; d.I = I; d.Ish = Ish; d.nbI = nblocks(I);
+        d.T = 1; d.k = k; d.E = E; d.H = H; d.I = I; d.Ish = Ish; d.nbI = nblocks(I);
         d.topk_idx = topk_idx; d.offsets = offsets; d.inv = inv; d.topk_w = topk_w;
         d.wg = (const uint8_t *)L->w_gate; d.wu = (const uint8_t *)L->w_up; d.wd = (const uint8_t *)L->w_down;
         d.gu_row_bytes = nblocks(H) * 38;
@@ -250,18 +257,25 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
         d.part_sh = w.part_sh;
         d.O = w.O; d.O_sh = w.O_sh; d.y = y;
         dec_plan(d);
-        if (!pr.before("dec_gateup")) return hip_fail(hipGetLastError(), "event record");
-        hipError_t e = launch_dec_gateup(d, s);
-        if (e != hipSuccess) return hip_fail(e, "dec_gateup launch");
-        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
-        if (!pr.before("dec_down")) return hip_fail(hipGetLastError(), "event record");
-        e = launch_dec_down(d, s);
-        if (e != hipSuccess) return hip_fail(e, "dec_down launch");
-        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
-        if (!pr.before("dec_combine")) return hip_fail(hipGetLastError(), "event record");
-        e = launch_dec_combine(d, s);
-        if (e != hipSuccess) return hip_fail(e, "dec_combine launch");
-        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+        const size_t xrow = (size_t)H * (act == MOE_ACT_F32 ? 4 : 2);
+        for (int t = 0; t < T; ++t) {                              // one token at a time, in order
+            d.x = (const char *)x + t * xrow;
+            d.topk_idx = topk_idx + (size_t)t * k;
+            d.topk_w = topk_w + (size_t)t * k;
+            d.y = y + (size_t)t * H;
+            if (!pr.before("dec_gateup")) return hip_fail(hipGetLastError(), "event record");
+            hipError_t e = launch_dec_gateup(d, s);
+            if (e != hipSuccess) return hip_fail(e, "dec_gateup launch");
+            if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+            if (!pr.before("dec_down")) return hip_fail(hipGetLastError(), "event record");
+            e = launch_dec_down(d, s);
+            if (e != hipSuccess) return hip_fail(e, "dec_down launch");
+            if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+            if (!pr.before("dec_combine")) return hip_fail(hipGetLastError(), "event record");
+            e = launch_dec_combine(d, s);
+            if (e != hipSuccess) return hip_fail(e, "dec_combine launch");
+            if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+        }
         return MOE_OK;
     }
 

@@ -148,9 +148,11 @@ int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bi
  *   bf16 terms (fp32), fp32 accumulation, intermediate h in fp32
  *   (single-token path: h held as two bf16 terms).  Relative L2 error against
  *   an exact evaluation is far below 1e-4.  Formats: CB2/Q2K routed, BF16
- *   shared.  Launches: for T = 1 (with H % 512 == 0, H <= 8192, I % 256 == 0,
- *   I <= 2048, sh_inter % 512 == 0, k <= 64) gate/up, down (SwiGLU as it
- *   forms h), combine; otherwise schedule, gate/up+SwiGLU, down, combine.
+ *   shared.  Launches: for T <= 4 (with H % 512 == 0, H <= 8192, I % 256 ==
+ *   0, I <= 2048, sh_inter % 512 == 0, k <= 64) per token, in order: gate/up,
+ *   down (SwiGLU as it forms h), combine -- so such a token's y does not
+ *   depend on the other tokens of the call; otherwise schedule,
+ *   gate/up+SwiGLU, down, combine.
  * moe_expert_ffn_prefill -- bf16 MFMA path for any T: x must be bf16;
  *   dequantized weights rounded to bf16 (RNE) in LDS; fp32 accumulation;
  *   h rounded to bf16; down output and combine in fp32.  Relative L2 error

@@ -237,12 +237,13 @@ def test_decode_batch_invariance_gemm():
     wl = W.Workload(cfg)
     x, act, r = run_route(wl, cfg)
     yb = run_ffn(wl, x, act, r, decode=True)
-    for t in (0, 5, 22):
-        xt = x[t:t + 2].contiguous()
-        r2 = M.Routing(2, cfg["top_k"], cfg["n_experts"])
-        M.route(wl.layer, xt, act, 2, wl.bias(cfg), r2, wl.layer.workspace(2, M.PATH_ROUTE))
-        y2 = run_ffn(wl, xt, act, r2, decode=True)
-        assert np.array_equal(y2.view(np.uint32), yb[t:t + 2].view(np.uint32)), t
+    # sub-batches of 6 tokens: above the size that runs token by token
+    for t in (0, 5, 18):
+        xt = x[t:t + 6].contiguous()
+        r6 = M.Routing(6, cfg["top_k"], cfg["n_experts"])
+        M.route(wl.layer, xt, act, 6, wl.bias(cfg), r6, wl.layer.workspace(6, M.PATH_ROUTE))
+        y6 = run_ffn(wl, xt, act, r6, decode=True)
+        assert np.array_equal(y6.view(np.uint32), yb[t:t + 6].view(np.uint32)), t
 
 
 # ------------------------------------------------------------------ full-size workloads
@@ -285,6 +286,20 @@ def test_full_decode_small_batches(big, T):
     """Batched decode at the full layer shape for the smallest batches (one or
     two rows per selected expert, the shared expert in one row tile)."""
     assert sampled_check(big, S.config("decode32", T=T), True, 1) <= DEC_TOL
+
+
+def test_full_decode_tokenwise_bit_identical(big):
+    """Decode batches of up to four tokens run the single-token kernels token by
+    token, so each token's y is bit-identical to decoding it alone."""
+    cfg = S.config("decode32", T=4)
+    x, act, r = run_route(big, cfg)
+    yb = run_ffn(big, x, act, r, decode=True)
+    for t in (0, 3):
+        xt = x[t:t + 1].contiguous()
+        r1 = M.Routing(1, cfg["top_k"], cfg["n_experts"])
+        M.route(big.layer, xt, act, 1, big.bias(cfg), r1, big.layer.workspace(1, M.PATH_ROUTE))
+        y1 = run_ffn(big, xt, act, r1, decode=True)
+        assert np.array_equal(y1[0].view(np.uint32), yb[t].view(np.uint32)), t
 
 
 def test_full_prefill2048(big):
