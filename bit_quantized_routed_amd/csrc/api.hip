@@ -227,8 +227,11 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
     if (prefill) {
         if (act != MOE_ACT_BF16) return fail(MOE_ERR_INVALID_ARG, "prefill needs bf16 activations");
     } else {
-        if (L->fmt_gate_up != MOE_FMT_CB2 || L->fmt_down != MOE_FMT_Q2K)
-            return fail(MOE_ERR_UNSUPPORTED, "decode supports CB2 gate/up with Q2K down");
+        // Q4_K runs on the grouped-GEMM decode kernels only: every K a multiple of 512
+        const bool cb2q2k = L->fmt_gate_up == MOE_FMT_CB2 && L->fmt_down == MOE_FMT_Q2K;
+        const bool gemm = L->hidden % 512 == 0 && L->inter % 512 == 0 && (L->sh_inter == 0 || L->sh_inter % 512 == 0);
+        if (!cb2q2k && !gemm)
+            return fail(MOE_ERR_UNSUPPORTED, "decode with Q4K needs hidden, inter and sh_inter multiples of 512");
     }
     const size_t need = ffn_ws_bytes(L, T, prefill);
     if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);

@@ -221,8 +221,31 @@ __device__ __forceinline__ void pool_prep(const typename RawOf<FMT>::T &r, int h
         const int bsc = 6 * j, bm = 6 * (8 + j);
         const uint32_t sc = (uint32_t)(bsc < 32 ? lo64 >> bsc : hi64 >> (bsc - 32)) & 63u;
         const uint32_t m = (uint32_t)(hi64 >> (bm - 32)) & 63u;
-        P.mul = f16_bits_to_f32(r.dd & 0xffffu) * (float)sc;
-        P.off = f16_bits_to_f32(r.dd >> 16) * (float)m;
+        if (DEC) {
+            // exact integers: sc (codes enter as sc*q, split in two bf16 terms)
+            // and the min operand m
+            P.mul = (float)sc;
+            P.off = (float)m;
+            P.mv[0] = P.mv[1] = pk_bf16((float)m, (float)m);
+        } else {
+            P.mul = f16_bits_to_f32(r.dd & 0xffffu) * (float)sc;
+            P.off = f16_bits_to_f32(r.dd >> 16) * (float)m;
+        }
+    }
+}
+
+// Q4_K decode operands of MFMA step s4: sc * q (integers up to 63 * 15 = 945)
+// as hi = bf16(sc * q) plus lo = sc * q - hi (an integer of magnitude <= 2),
+// both exact, so the two MFMAs sum the exact products.
+__device__ __forceinline__ void bfrag_q4k_dec(const RawQ4K &r, const Pool &P, int s4, uint32_t hi[4], uint32_t lo[4])
+{
+    const uint32_t cw = r.c[s4];
+    const uint32_t cl = cw & 0x0f0f0f0fu, ch = (cw >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float v0 = P.mul * ubyte(cl, i), v1 = P.mul * ubyte(ch, i);
+        hi[i] = pk_bf16(v0, v1);
+        lo[i] = pk_bf16(v0 - __uint_as_float(hi[i] << 16), v1 - __uint_as_float(hi[i] & 0xffff0000u));
     }
 }
 
@@ -501,7 +524,8 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
     // DEC with packed weights: each block's sums (P1: codes, P2: Q2_K min
     // operand) are scaled by the block's d (and dmin) into acc
     constexpr bool PBLK = DEC && FMT != FMT_BF16;
-    constexpr bool PMIN = DEC && FMT == FMT_Q2K;
+    constexpr bool PMIN = DEC && (FMT == FMT_Q2K || FMT == FMT_Q4K);
+    constexpr bool Q4D = DEC && FMT == FMT_Q4K;     // two exact B terms per step
     f32x4 acc[NMF][4], P1[PBLK ? NMF : 1][4], P2[PMIN ? NMF : 1][4];
 #pragma unroll
     for (int mf = 0; mf < NMF; ++mf)
@@ -562,7 +586,7 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
                     for (int nf = 0; nf < 4; ++nf) blk_pool<FMT, DEC>(blk[q][nf], h, fc, P[nf]);
                 } else if constexpr (FMT == FMT_Q4K) {
 #pragma unroll
-                    for (int nf = 0; nf < 4; ++nf) pool_prep<FMT_Q4K>(r4[h][nf], h, fc, P[nf]);
+                    for (int nf = 0; nf < 4; ++nf) pool_prep<FMT_Q4K, DEC>(r4[h][nf], h, fc, P[nf]);
                 }
                 const uint8_t *ab = As + h * NP_ABUF, *abl = As + (NP_NBUF + h) * NP_ABUF;
 #pragma unroll
@@ -580,8 +604,16 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
                         a[mf] = *(const bf16x8 *)(ab + aoff[s4] + mf * 4096);
                         if constexpr (TWO) al[mf] = *(const bf16x8 *)(abl + aoff[s4] + mf * 4096);
                     }
-                    bf16x8 bq[4];
-                    if constexpr (FMT == FMT_BF16) {
+                    bf16x8 bq[4], bql[Q4D ? 4 : 1];
+                    if constexpr (Q4D) {
+#pragma unroll
+                        for (int nf = 0; nf < 4; ++nf) {
+                            uint32_t oh[4], ol[4];
+                            bfrag_q4k_dec(r4[h][nf], P[nf], s4, oh, ol);
+                            bq[nf] = __builtin_bit_cast(bf16x8, u32x4{oh[0], oh[1], oh[2], oh[3]});
+                            bql[nf] = __builtin_bit_cast(bf16x8, u32x4{ol[0], ol[1], ol[2], ol[3]});
+                        }
+                    } else if constexpr (FMT == FMT_BF16) {
                         const int ks = 8 * bb + 4 * h + s4;
                         bw_load(ks + 3);                             // ring slot (s4 + 3) & 3
 #pragma unroll
@@ -602,6 +634,10 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
                             if constexpr (PBLK) {
                                 P1[mf][nf] = mfma16x16x32(a[mf], bq[nf], P1[mf][nf]);
                                 if constexpr (TWO) P1[mf][nf] = mfma16x16x32(al[mf], bq[nf], P1[mf][nf]);
+                                if constexpr (Q4D) {
+                                    P1[mf][nf] = mfma16x16x32(a[mf], bql[nf], P1[mf][nf]);
+                                    if constexpr (TWO) P1[mf][nf] = mfma16x16x32(al[mf], bql[nf], P1[mf][nf]);
+                                }
                                 if constexpr (PMIN) {
                                     const uint32_t mv = P[nf].mv[s4 >> 1];
                                     const bf16x8 bm = __builtin_bit_cast(bf16x8, u32x4{mv, mv, mv, mv});
@@ -621,7 +657,10 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
                         for (int nf = 0; nf < 4; ++nf) {
                             float d, dmin = 0.f;
                             if constexpr (FMT == FMT_CB2) d = f16_bits_to_f32(blk[q][nf].d);
-                            else {
+                            else if constexpr (FMT == FMT_Q4K) {
+                                d = f16_bits_to_f32(r4[h][nf].dd & 0xffffu);
+                                dmin = f16_bits_to_f32(r4[h][nf].dd >> 16);
+                            } else {
                                 d = f16_bits_to_f32(blk[q][nf].dd & 0xffffu);
                                 dmin = f16_bits_to_f32(blk[q][nf].dd >> 16);
                             }
@@ -971,7 +1010,7 @@ bool np_decode_ok(const FfnPass &p)
 {
     if (p.K % (2 * QK) || p.K < 2 * QK) return false;
     if (p.Nsh > 0 && (p.Ksh % (2 * QK) || p.Ksh < 2 * QK)) return false;
-    return p.out_f32 && (p.fmt == FMT_CB2 || p.fmt == FMT_Q2K);
+    return p.out_f32 && (p.fmt == FMT_CB2 || p.fmt == FMT_Q2K || p.fmt == FMT_Q4K);
 }
 
 hipError_t launch_np_decode(const FfnPass &p, bool gateup, hipStream_t s)
@@ -981,7 +1020,12 @@ hipError_t launch_np_decode(const FfnPass &p, bool gateup, hipStream_t s)
         if (p.act_f32) return np_launch<FMT_CB2, true, true, true>(p, s);
         return np_launch<FMT_CB2, true, true, false>(p, s);
     }
+    if (gateup && p.fmt == FMT_Q4K) {
+        if (p.act_f32) return np_launch<FMT_Q4K, true, true, true>(p, s);
+        return np_launch<FMT_Q4K, true, true, false>(p, s);
+    }
     if (!gateup && p.fmt == FMT_Q2K && p.act_f32) return np_launch<FMT_Q2K, false, true, true>(p, s);
+    if (!gateup && p.fmt == FMT_Q4K && p.act_f32) return np_launch<FMT_Q4K, false, true, true>(p, s);
     return hipErrorInvalidValue;
 }
 

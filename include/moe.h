@@ -147,8 +147,10 @@ int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bi
  *   products; fp32 block rescale), activations exact (bf16) or split into two
  *   bf16 terms (fp32), fp32 accumulation, intermediate h in fp32
  *   (single-token path: h held as two bf16 terms).  Relative L2 error against
- *   an exact evaluation is far below 1e-4.  Formats: CB2/Q2K routed, BF16
- *   shared.  Launches: for T <= 4 (with H % 512 == 0, H <= 8192, I % 256 ==
+ *   an exact evaluation is far below 1e-4.  Formats: CB2 or Q4K gate/up, Q2K
+ *   or Q4K down, BF16 shared; Q4K needs hidden, inter and sh_inter multiples of
+ *   512 (MOE_ERR_UNSUPPORTED otherwise; Q4K codes enter as sc*q split exactly
+ *   into two bf16 terms).  Launches: for T <= 4 (with H % 512 == 0, H <= 8192, I % 256 ==
  *   0, I <= 2048, sh_inter % 512 == 0, k <= 64) per token, in order: gate/up,
  *   down (SwiGLU as it forms h), combine -- so such a token's y does not
  *   depend on the other tokens of the call; otherwise schedule,

@@ -157,6 +157,35 @@ def test_prefill_small(small_cases, name, cfg):
     assert err <= PRE_TOL
 
 
+Q4D = dict(hidden=1024, inter=512, sh_inter=512, fmt_gate_up=S.FMT_Q4K, fmt_down=S.FMT_Q4K)
+
+
+@pytest.mark.parametrize("name,cfg", [("q4k_dec_T1", mid(1, 31, **Q4D)),
+                                      ("q4k_dec_T5", mid(5, 32, **Q4D)),
+                                      ("q4k_dec_T40_f32", mid(40, 33, x_dtype="f32", **Q4D)),
+                                      ("q4k_dec_T70_skew", mid(70, 34, skew=True, **Q4D))],
+                         ids=lambda v: v if isinstance(v, str) else "")
+def test_decode_q4k(small_cases, name, cfg):
+    """Decode precision with Q4_K gate/up and down (exact sc*q in two bf16 terms,
+    the min term apart, d and dmin per block)."""
+    wl, yref, routing = _case(small_cases, name, cfg)
+    x, act, r = run_route(wl, cfg)
+    check_route(r, *routing)
+    y = run_ffn(wl, x, act, r, decode=True)
+    err = rel_l2(y, yref)
+    print("[decode] %s rel_l2=%.3e" % (name, err))
+    assert err <= DEC_TOL
+
+
+def test_decode_q4k_needs_512_multiples(small_cases):
+    """Q4_K decode on a shape whose K is not a multiple of 512 is refused."""
+    cfg = mid(8, 35, fmt_gate_up=S.FMT_Q4K, fmt_down=S.FMT_Q4K)     # inter 384
+    wl = W.Workload(cfg)
+    x, act, r = run_route(wl, cfg)
+    with pytest.raises(RuntimeError, match="unsupported|Q4K"):
+        run_ffn(wl, x, act, r, decode=True)
+
+
 def test_route_ties_go_to_lower_index():
     cfg = mid(40, 19)
     wl = W.Workload(cfg)
@@ -300,6 +329,10 @@ def test_full_decode_tokenwise_bit_identical(big):
         M.route(big.layer, xt, act, 1, big.bias(cfg), r1, big.layer.workspace(1, M.PATH_ROUTE))
         y1 = run_ffn(big, xt, act, r1, decode=True)
         assert np.array_equal(y1[0].view(np.uint32), yb[t].view(np.uint32)), t
+
+
+def test_full_decode32_q4k(big_q4k):
+    assert sampled_check(big_q4k, S.config("prefill8192_q4k", T=32), True, 2) <= DEC_TOL
 
 
 def test_full_prefill2048(big):
