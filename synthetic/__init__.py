@@ -15,6 +15,7 @@ no shapes, so the shapes are the stated workload definitions):
   prefill2048  same layer                 T=2048  unskewed logits
   prefill8192  same layer                 T=8192  Zipf-skewed logits
   prefill8192_q4k  as prefill8192 with all three routed projections in Q4_K
+  decode32_q4k     as decode32 with all three routed projections in Q4_K
 
 Every tensor comes from its own child stream of one layer seed
 (``numpy.random.default_rng([seed, tag, index])``), so one expert can be
@@ -56,6 +57,8 @@ CONFIGS = {
                         fmt_gate_up=FMT_CB2, fmt_down=FMT_Q2K, index=4),
     "prefill8192_q4k": dict(_BIG, T=8192, x_dtype="bf16", skew=True,
                             fmt_gate_up=FMT_Q4K, fmt_down=FMT_Q4K, index=4),
+    "decode32_q4k": dict(_BIG, T=32, x_dtype="bf16", skew=True,
+                         fmt_gate_up=FMT_Q4K, fmt_down=FMT_Q4K, index=4),
 }
 
 _GOLDEN = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
