@@ -127,6 +127,9 @@ def kernel_bytes(cfg, n_active, T, name):
     H, I, k, sh = cfg["hidden"], cfg["inter"], cfg["top_k"], cfg["sh_inter"]
     xb = 2 if cfg["x_dtype"] == "bf16" else 4
     rows = T * k + (T if sh else 0)
+    if name == "dec_down_fused":
+        # every selected expert's down and the shared down, h in (fp32), y out
+        return n_active * M.q2_packed_bytes(cfg["fmt_down"], H, I) + sh * H * 2 + rows * I * 4 + T * H * 4
     if name.endswith("gateup"):
         hb = 4 if "decode" in name else 2
         return n_active * 2 * M.q2_packed_bytes(cfg["fmt_gate_up"], I, H) + 2 * sh * H * 2 + T * H * xb + rows * I * hb

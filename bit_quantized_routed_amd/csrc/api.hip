@@ -139,6 +139,8 @@ struct FfnWs {
     int ks_gu, ks_dn;                 // its K parts for gate/up and down (0: not split)
     float *part_rt;
     int nkc;
+    uint16_t *h_hi, *h_lo, *sh_hi, *sh_lo;
+    float *X;
 };
 
 // Decode batches of up to DEC_TOKENWISE_MAX tokens run the single-token
@@ -173,6 +175,18 @@ FfnWs ffn_ws(const moe_layer *L, int T, bool prefill, bool single, char *base)
         w.nkc = (int)((H + 256 * DEC_LUT_KB - 1) / (256 * DEC_LUT_KB));
         w.part_rt = (float *)(base + off);
         off = align_up(off + (size_t)w.nkc * k * 2 * L->inter * sizeof(float));
+        // h formed once for the fused down: routed (two bf16 terms, per-16 sums), shared
+        const size_t nbI = nblocks(L->inter);
+        w.h_hi = (uint16_t *)(base + off);
+        off = align_up(off + k * w.hstride * 2);
+        w.h_lo = (uint16_t *)(base + off);
+        off = align_up(off + k * w.hstride * 2);
+        w.X = (float *)(base + off);
+        off = align_up(off + k * nbI * 16 * sizeof(float));
+        w.sh_hi = (uint16_t *)(base + off);
+        off = align_up(off + Ish * 2);
+        w.sh_lo = (uint16_t *)(base + off);
+        off = align_up(off + Ish * 2);
         w.O = (float *)(base + off);
         off = align_up(off + k * H * sizeof(float));
         w.O_sh = (float *)(base + off);
@@ -257,6 +271,8 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
         d.codebook = L->codebook;
         d.x = x; d.x_f32 = act == MOE_ACT_F32;
         d.nkc = w.nkc; d.part_rt = w.part_rt;
+        d.h_hi = w.h_hi; d.h_lo = w.h_lo; d.hstride = w.hstride; d.X = w.X; d.sh_hi = w.sh_hi; d.sh_lo = w.sh_lo;
+        d.fused = dec_fused_ok(k, I, Ish);
         d.part_sh = w.part_sh;
         d.O = w.O; d.O_sh = w.O_sh; d.y = y;
         dec_plan(d);
@@ -270,6 +286,18 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
             hipError_t e = launch_dec_gateup(d, s);
             if (e != hipSuccess) return hip_fail(e, "dec_gateup launch");
             if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+            if (d.fused) {
+                // h once, then every slot and the shared expert straight into y
+                if (!pr.before("dec_hform")) return hip_fail(hipGetLastError(), "event record");
+                e = launch_dec_hform(d, s);
+                if (e != hipSuccess) return hip_fail(e, "dec_hform launch");
+                if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+                if (!pr.before("dec_down_fused")) return hip_fail(hipGetLastError(), "event record");
+                e = launch_dec_down_fused(d, s);
+                if (e != hipSuccess) return hip_fail(e, "dec_down_fused launch");
+                if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+                continue;
+            }
             if (!pr.before("dec_down")) return hip_fail(hipGetLastError(), "event record");
             e = launch_dec_down(d, s);
             if (e != hipSuccess) return hip_fail(e, "dec_down launch");

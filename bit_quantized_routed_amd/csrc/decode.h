@@ -19,6 +19,11 @@ struct DecPass {
     int nkc;                                     // K chunks of the routed gate/up tables
     float *part_rt;                              // [nkc][k][2][I] routed gate/up partial sums by K chunk
     float *part_sh;                              // [DEC_SH_KQ][2][Ish] shared gate/up partial sums (K parts)
+    uint16_t *h_hi, *h_lo;                       // [k][hstride] routed h as two bf16 terms (fused down)
+    int hstride;
+    float *X;                                    // [k][nbI][16] per-16 sums of h (Q2_K min term; fused down)
+    uint16_t *sh_hi, *sh_lo;                     // [Ish] shared h as two bf16 terms (fused down)
+    int fused;                                   // 1: h formed once, then one down launch writes y
     float *O;                                    // [k][H] by top-k slot
     float *O_sh;                                 // [Ish/512][H]
     float *y;                                    // [H]
@@ -32,5 +37,10 @@ void dec_plan(DecPass &p);                       // fills the work-group split
 hipError_t launch_dec_gateup(const DecPass &p, hipStream_t s);
 hipError_t launch_dec_down(const DecPass &p, hipStream_t s);
 hipError_t launch_dec_combine(const DecPass &p, hipStream_t s);
+// the fused down (k <= 8, I <= 2048, sh_inter <= 2048): h formed once, then
+// y from every slot and the shared expert in one launch (no combine)
+bool dec_fused_ok(int k, int I, int Ish);
+hipError_t launch_dec_hform(const DecPass &p, hipStream_t s);
+hipError_t launch_dec_down_fused(const DecPass &p, hipStream_t s);
 
 }  // namespace moe

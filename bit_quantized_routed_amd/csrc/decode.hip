@@ -579,6 +579,232 @@ __global__ __launch_bounds__(64) void dec1_combine_kernel(DecPass p)
     *(f32x4 *)&p.y[n] = y;
 }
 
+// ============================================================== fused down
+// For k <= DF_MAXK slots, I <= 2048 and sh_inter <= 2048, h is formed once
+// (dec1_hform) and one launch computes y (dec1_down_fused).  Work-group wg
+// owns output rows DF_ROWS wg .. + DF_ROWS - 1; wave w takes the 16-row half
+// w % 2 of them for the routed slots w / 2 + 4 i (i < DF_SPW, j < k; output
+// weighted by w_j) and the shared expert's K quarter w / 2, so every CU streams
+// bf16 shared rows while it looks up Q2_K codes.  All of a wave's weight bytes
+// are requested before it computes.  The eight wave sums of a row meet in LDS
+// and are added in wave order.
+constexpr int DF_ROWS = 32;
+constexpr int DF_MAXK = 8;
+constexpr int DF_SPW = DF_MAXK / 4;              // routed slots per wave
+constexpr int DF_SHS = 2048 / 4 / 32;            // shared K steps per wave (sh_inter <= 2048)
+constexpr int DF_ST = DF_MAXK * 2048 / 8 / D1_THREADS;   // staged 8-element chunks of h per thread
+constexpr int DF_SX = (DF_MAXK * 8 * 16 + D1_THREADS - 1) / D1_THREADS;  // staged per-16 sums per thread
+
+// Routed h of every slot (chunk partials added in chunk order) and shared h
+// (K parts added in order): silu(g) * u as hi + lo bf16 terms, and the
+// per-16 sums of routed h for the Q2_K min term.  Four features per thread;
+// I % 256 == 0 and sh_inter % 512 == 0 keep whole waves on one side.
+__global__ __launch_bounds__(256) void dec1_hform_kernel(DecPass p)
+{
+    const int q = blockIdx.x * 256 + threadIdx.x, lane = threadIdx.x & 63;
+    const int I = p.I, nq_rt = p.k * (I / 4);
+    if (q >= nq_rt + p.Ish / 4) return;                            // uniform over each wave
+    f32x4 g, uu;
+    int slot = 0, f;
+    if (q < nq_rt) {
+        slot = q / (I / 4);
+        f = 4 * (q % (I / 4));
+        const int64_t cstride = (int64_t)2 * p.k * I;
+        const float *pg = p.part_rt + (int64_t)2 * slot * I + f;
+        f32x4 gv[DN_MAXKC], uv[DN_MAXKC];
+#pragma unroll
+        for (int c = 0; c < DN_MAXKC; ++c) {
+            const int64_t o = cstride * min(c, p.nkc - 1);
+            gv[c] = *(const f32x4 *)(pg + o);
+            uv[c] = *(const f32x4 *)(pg + o + I);
+        }
+        g = gv[0];
+        uu = uv[0];
+#pragma unroll
+        for (int c = 1; c < DN_MAXKC; ++c)
+            if (c < p.nkc) { g += gv[c]; uu += uv[c]; }
+    } else {
+        f = 4 * (q - nq_rt);
+        f32x4 gv[SH_KQ], uv[SH_KQ];
+#pragma unroll
+        for (int c = 0; c < SH_KQ; ++c) {
+            gv[c] = *(const f32x4 *)&p.part_sh[(int64_t)(2 * c) * p.Ish + f];
+            uv[c] = *(const f32x4 *)&p.part_sh[(int64_t)(2 * c + 1) * p.Ish + f];
+        }
+        g = gv[0];
+        uu = uv[0];
+#pragma unroll
+        for (int c = 1; c < SH_KQ; ++c) { g += gv[c]; uu += uv[c]; }
+    }
+    uint32_t hi[4], lo[4];
+    float hs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float h = g[e] / (1.0f + expf(-g[e])) * uu[e];
+        split_bf16(h, hi[e], lo[e]);
+        hs += h;
+    }
+    const uint2 vh = uint2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+    const uint2 vl = uint2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+    if (q < nq_rt) {
+        *(uint2 *)&p.h_hi[(int64_t)slot * p.hstride + f] = vh;
+        *(uint2 *)&p.h_lo[(int64_t)slot * p.hstride + f] = vl;
+        hs += __shfl_xor(hs, 1, 64);
+        hs += __shfl_xor(hs, 2, 64);
+        if ((lane & 3) == 0) p.X[((int64_t)slot * p.nbI + (f >> 8)) * 16 + ((f & 255) >> 4)] = hs;
+    } else {
+        *(uint2 *)&p.sh_hi[f] = vh;
+        *(uint2 *)&p.sh_lo[f] = vl;
+    }
+}
+
+__global__ __launch_bounds__(D1_THREADS) void dec1_down_fused_kernel(DecPass p)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+    __shared__ int kid[64];
+    __shared__ float wsum[8][16];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int fr = lane & 15, fc = lane >> 4;
+    const int nb = p.nbI, I = p.I, k = p.k, Ish = p.Ish;
+    uint16_t *tab = (uint16_t *)dsm;                               // [16 sc][256 bytes][4]
+    uint16_t *hh = tab + 16 * 256 * 4;                             // [k][I] routed h hi
+    uint16_t *hl = hh + k * I;                                     // [k][I] lo
+    float *xm = (float *)(hl + k * I);                             // [k][nb][16]
+    uint16_t *sh = (uint16_t *)(xm + k * nb * 16);                 // [Ish] shared h hi
+    uint16_t *sl = sh + Ish;                                       // [Ish] lo
+    if (tid < k) kid[tid] = clamp_expert(p.topk_idx[tid], p.E);
+    __syncthreads();                                               // expert ids
+    // h (every slot), its per-16 sums and shared h: loaded into registers
+    // before any weight byte is requested, so that storing them into LDS
+    // waits for these loads only (the load counter retires in order)
+    const int nch = k * I / 8, nxm = k * nb * 16, nsc = Ish / 8;
+    u32x4 rhh[DF_ST], rhl[DF_ST], rsh, rsl;
+    float rxm[DF_SX];
+#pragma unroll
+    for (int j = 0; j < DF_ST; ++j) {
+        const int i = min(tid + D1_THREADS * j, nch - 1), slot = i / (I / 8), c = i % (I / 8);
+        rhh[j] = *(const u32x4 *)(p.h_hi + (int64_t)slot * p.hstride + 8 * c);
+        rhl[j] = *(const u32x4 *)(p.h_lo + (int64_t)slot * p.hstride + 8 * c);
+    }
+#pragma unroll
+    for (int j = 0; j < DF_SX; ++j) rxm[j] = p.X[min(tid + D1_THREADS * j, nxm - 1)];
+    if (Ish > 0) {
+        rsh = *(const u32x4 *)(p.sh_hi + 8 * min(tid, nsc - 1));
+        rsl = *(const u32x4 *)(p.sh_lo + 8 * min(tid, nsc - 1));
+    }
+    const int hg = wave & 1, wp = wave >> 1;
+    const int row = DF_ROWS * blockIdx.x + 16 * hg + fr;           // < H (H % 512 == 0)
+    // this wave's weight bytes, all requested up front (unconditional loads:
+    // slots past k re-read slot k - 1, blocks past nb the last block, steps
+    // past the quarter its last step; none of those are used)
+    u32x4 C[DF_SPW][DN_MAXB];
+    uint32_t Sc[DF_SPW][DN_MAXB], Dd[DF_SPW][DN_MAXB];
+#pragma unroll
+    for (int i = 0; i < DF_SPW; ++i) {
+        const int j = min(wp + 4 * i, k - 1);
+        const uint8_t *wrow = p.wd + (int64_t)kid[j] * p.d_expert_bytes + (int64_t)row * p.d_row_bytes;
+#pragma unroll
+        for (int b = 0; b < DN_MAXB; ++b) {
+            const uint8_t *blk = wrow + 84 * min(b, nb - 1);
+            C[i][b] = *(const u32x4 *)(blk + 20 + 16 * fc);
+            Sc[i][b] = *(const uint32_t *)(blk + 4 + 4 * fc);
+            Dd[i][b] = *(const uint32_t *)blk;
+        }
+    }
+    const int KQs = Ish / 4, nsh = KQs / 32, kq0 = wp * KQs;
+    u32x4 Wsh[DF_SHS];
+    if (Ish > 0) {
+#pragma unroll
+        for (int s = 0; s < DF_SHS; ++s)
+            Wsh[s] = *(const u32x4 *)(p.sd + (int64_t)row * Ish + kq0 + 32 * min(s, nsh - 1) + 8 * fc);
+    }
+    // the code table, then the staged values (indices past the end rewrite
+    // the last element with its own value)
+    for (int i = tid; i < 16 * 256; i += D1_THREADS) {
+        const int sc = i >> 8, byte = i & 255;
+        uint32_t v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = f32_to_bf16_exact((float)(sc * ((byte >> (2 * t)) & 3)));
+        *(uint2 *)&tab[4 * i] = uint2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
+    }
+#pragma unroll
+    for (int j = 0; j < DF_ST; ++j) {
+        const int i = min(tid + D1_THREADS * j, nch - 1);
+        *(u32x4 *)&hh[8 * i] = rhh[j];
+        *(u32x4 *)&hl[8 * i] = rhl[j];
+    }
+#pragma unroll
+    for (int j = 0; j < DF_SX; ++j) xm[min(tid + D1_THREADS * j, nxm - 1)] = rxm[j];
+    if (Ish > 0) {
+        *(u32x4 *)&sh[8 * min(tid, nsc - 1)] = rsh;
+        *(u32x4 *)&sl[8 * min(tid, nsc - 1)] = rsl;
+    }
+    __syncthreads();                                               // h, X, shared h, table staged
+
+    float yv = 0.f;                                                // this lane's row (lanes fc == 0)
+    float ysh = 0.f;
+    if (Ish > 0) {
+        f32x4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < DF_SHS; ++st) {
+            bf16x8 a = act_rows<true>(sh, sl, kq0 + 32 * min(st, nsh - 1) + 8 * fc, fr);
+            if (st >= nsh) a = bf16x8{};
+            P = mfma16x16x32(a, __builtin_bit_cast(bf16x8, Wsh[st]), P);
+        }
+        ysh = P[0] + P[1];
+    }
+    const uint16_t *hrow = (fr & 1) ? hl : hh;                     // A rows 0, 1: h hi, lo
+#pragma unroll
+    for (int i = 0; i < DF_SPW; ++i) {
+        const int j = wp + 4 * i;
+        if (j >= k) break;                                         // uniform over the wave
+        const uint16_t *sa_row = hrow + j * I;
+        const float *sx = xm + j * nb * 16;
+        float acc = 0.f, accm = 0.f;
+#pragma unroll
+        for (int bl = 0; bl < DN_MAXB; ++bl) {
+            const int b = min(bl, nb - 1);
+            const uint32_t cw[4] = {C[i][bl].x, C[i][bl].y, C[i][bl].z, C[i][bl].w};
+            const uint32_t scw = Sc[i][bl];
+            bf16x8 a[8];
+            act_block<true>(sa_row, 256 * b + 64 * fc, 8, fr, a);
+            u32x4 Bq[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int sc = (scw >> (8 * (m >> 1))) & 15;
+                const uint32_t word = cw[m >> 1];
+                const int by0 = (word >> (16 * (m & 1))) & 255, by1 = (word >> (16 * (m & 1) + 8)) & 255;
+                const uint2 t0 = *(const uint2 *)&tab[4 * (sc * 256 + by0)];
+                const uint2 t1 = *(const uint2 *)&tab[4 * (sc * 256 + by1)];
+                Bq[m] = u32x4{t0.x, t0.y, t1.x, t1.y};
+            }
+            f32x4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 8; ++m) P = mfma16x16x32(a[m], __builtin_bit_cast(bf16x8, Bq[m]), P);
+            const f32x4 xv = *(const f32x4 *)&sx[b * 16 + 4 * fc];
+            float mt = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mt += (float)((scw >> (8 * e + 4)) & 15) * xv[e];
+            const float d = f16_bits_to_f32(Dd[i][bl] & 0xffffu), dmin = f16_bits_to_f32(Dd[i][bl] >> 16);
+            acc += bl < nb ? d * (P[0] + P[1]) : 0.f;
+            accm += bl < nb ? dmin * mt : 0.f;
+        }
+        accm += __shfl_xor(accm, 16, 64);
+        accm += __shfl_xor(accm, 32, 64);
+        yv += p.topk_w[j] * (acc - accm);
+    }
+    yv += ysh;
+    if (fc == 0) wsum[wave][fr] = yv;
+    __syncthreads();
+    if (tid < DF_ROWS) {
+        const int g2 = tid >> 4, r = tid & 15;
+        float y = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) y += wsum[2 * w2 + g2][r];
+        p.y[DF_ROWS * blockIdx.x + tid] = y;
+    }
+}
+
 // ============================================================== launchers
 namespace {
 
@@ -691,6 +917,37 @@ hipError_t launch_dec_down(const DecPass &p, hipStream_t s)
 hipError_t launch_dec_combine(const DecPass &p, hipStream_t s)
 {
     dec1_combine_kernel<<<(p.H / 4 + 63) / 64, 64, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+bool dec_fused_ok(int k, int I, int Ish)
+{
+    return k <= DF_MAXK && I <= 256 * DN_MAXB && Ish <= 4 * 32 * DF_SHS && Ish % 128 == 0;
+}
+
+size_t lds_dn_fused(int k, int I, int nbI, int Ish)
+{
+    return 16 * 256 * 4 * 2 + (size_t)k * I * 2 * 2 + (size_t)k * nbI * 16 * 4 + (size_t)Ish * 2 * 2;
+}
+
+hipError_t launch_dec_hform(const DecPass &p, hipStream_t s)
+{
+    const int nq = p.k * (p.I / 4) + p.Ish / 4;
+    dec1_hform_kernel<<<(nq + 255) / 256, 256, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+hipError_t launch_dec_down_fused(const DecPass &p, hipStream_t s)
+{
+    const size_t lds = lds_dn_fused(p.k, p.I, p.nbI, p.Ish);
+    static std::atomic<size_t> attr{0};                            // the dynamic LDS limit last set
+    if (attr.load(std::memory_order_relaxed) < lds) {
+        const hipError_t e = hipFuncSetAttribute((const void *)dec1_down_fused_kernel,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr.store(lds, std::memory_order_relaxed);
+    }
+    dec1_down_fused_kernel<<<p.H / DF_ROWS, D1_THREADS, lds, s>>>(p);
     return hipGetLastError();
 }
 
