@@ -1,6 +1,6 @@
 // Single-token decode (T = 1): the memory-bound case the pages describe for
 // decode, where every routed weight is read once per token step while compute
-// idles ("Part 5: 服务层", section 6).  Three launches after the router:
+// idles ("Part 5: 服务层", section 6).  After the router:
 //
 //   dec1_gateup: gate/up GEMVs.  One persistent work-group per resident slot;
 //     each takes one role.  Shared-expert units are 16 bf16 rows x one K
@@ -12,17 +12,22 @@
 //     read per 8 weights, with the fp32 sub-block scale s_j and block scale d
 //     applied to the sums.  It writes one fp32 partial per row and chunk; the
 //     shared expert writes fp32 partial sums of its K eighths.
-//   dec1_down: persistent again.  A routed work-group first forms h = silu(g)
-//     * u for the slots of its units from the gate/up chunk partials (added
-//     in chunk order) as two bf16 terms (hi + lo, relative error below 2^-17)
-//     with the per-16 sums Q2_K's min term needs.  A unit is 128 output rows
-//     (16 per wave, each wave over the whole K) of one selected expert's Q2_K
-//     down, or of one 512-wide K part of the bf16 shared down.  Q2_K codes
-//     become exact bf16 values sc*q through a 32 KB LDS table indexed by (sc,
-//     code byte); the block scale d and the min term dmin * sum_j m_j X_j
-//     apply to the fp32 sums of each 256-wide block.
-//   dec1_combine: y = the shared expert's K parts in order + the routed
-//     outputs weighted in top-k order.
+//   dec1_hform + dec1_down_fused (k <= 8, I <= 2048, sh_inter <= 2048):
+//     dec1_hform forms h = silu(g) * u once -- the routed chunk partials and
+//     the shared K parts added in order -- as two bf16 terms (hi + lo,
+//     relative error below 2^-17), with the per-16 sums Q2_K's min term needs.
+//     dec1_down_fused: a work-group owns 32 output rows; each wave takes 16 of
+//     them for two top-k slots (Q2_K) and one K quarter of the bf16 shared
+//     down, so each CU mixes table lookups with streaming; the wave sums meet
+//     in LDS and y is written directly.  Q2_K codes become exact bf16 values
+//     sc*q through a 32 KB LDS table indexed by (sc, code byte); the block
+//     scale d and the min term dmin * sum_j m_j X_j apply to the fp32 sums of
+//     each 256-wide block.
+//   Other shapes: dec1_down (persistent; a routed work-group forms h for its
+//     slots itself; a unit is 128 output rows of one slot's Q2_K down or of
+//     one 512-wide K part of the shared down) and dec1_combine (y = the
+//     shared expert's K parts in order + the routed outputs weighted in top-k
+//     order).
 //
 // The role split gives each role work-groups in proportion to its measured
 // cost per byte.  Routed buffers are indexed by top-k slot j (partials, O),

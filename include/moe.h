@@ -150,11 +150,12 @@ int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bi
  *   an exact evaluation is far below 1e-4.  Formats: CB2 or Q4K gate/up, Q2K
  *   or Q4K down, BF16 shared; Q4K needs hidden, inter and sh_inter multiples of
  *   512 (MOE_ERR_UNSUPPORTED otherwise; Q4K codes enter as sc*q split exactly
- *   into two bf16 terms).  Launches: for T <= 4 (with H % 512 == 0, H <= 8192, I % 256 ==
- *   0, I <= 2048, sh_inter % 512 == 0, k <= 64) per token, in order: gate/up,
- *   down (SwiGLU as it forms h), combine -- so such a token's y does not
- *   depend on the other tokens of the call; otherwise schedule,
- *   gate/up+SwiGLU, down, combine.
+ *   into two bf16 terms).  Launches: for T <= 4 (with H % 512 == 0,
+ *   H <= 8192, I % 256 == 0, I <= 2048, sh_inter % 512 == 0, k <= 64) per
+ *   token, in order: gate/up, then (k <= 8, sh_inter <= 2048) h+SwiGLU and
+ *   one down launch that writes y, else down (SwiGLU as it forms h) and
+ *   combine -- so such a token's y does not depend on the other tokens of the
+ *   call; otherwise schedule, gate/up+SwiGLU, down, combine.
  * moe_expert_ffn_prefill -- bf16 MFMA path for any T: x must be bf16;
  *   dequantized weights rounded to bf16 (RNE) in LDS; fp32 accumulation;
  *   h rounded to bf16; down output and combine in fp32.  Relative L2 error
