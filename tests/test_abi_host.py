@@ -80,7 +80,7 @@ def test_ffn_validation_misc():
     dec, pre = M.lib().moe_expert_ffn_decode, M.lib().moe_expert_ffn_prefill
     L = _layer()
     assert _ffn(pre, L, act=0) == -1                           # prefill needs bf16 activations
-    assert _ffn(dec, _layer(fmt_gate_up=3, fmt_down=3)) == -2  # decode: CB2/Q2K only
+    assert _ffn(dec, _layer(fmt_gate_up=3, fmt_down=3)) == -2  # decode: Q4K needs K multiples of 512
     assert _ffn(dec, L, ws_bytes=100) == -3
     assert _ffn(pre, L, ws_bytes=100) == -3
     assert _ffn(dec, L, T=-2) == -1
