@@ -13,6 +13,7 @@ import json
 import os
 import sys
 import time
+import warnings
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -92,7 +93,11 @@ class Workload:
         self.layers = []
         self.routed = []
         for _ in range(replicas):
-            dev = [torch.from_numpy(np.ascontiguousarray(a)).to(device) for a in self.packed]
+            with warnings.catch_warnings():
+                # the cached packed bytes are memory-mapped read-only; the host
+                # tensor is only read, to copy it to the device
+                warnings.filterwarnings("ignore", message="The given NumPy array is not writable")
+                dev = [torch.from_numpy(np.ascontiguousarray(a)).to(device) for a in self.packed]
             wr = self.w_router.clone() if replicas > 1 else self.w_router
             shd = [s.clone() for s in self.shared] if (self.shared and replicas > 1) else self.shared
             self.routed.append((dev, wr, shd))
