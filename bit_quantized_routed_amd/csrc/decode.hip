@@ -2,8 +2,8 @@
 // decode, where every routed weight is read once per token step while compute
 // idles ("Part 5: 服务层", section 6).  After the router:
 //
-//   dec1_gateup: gate/up GEMVs.  One persistent work-group per resident slot;
-//     each takes one role.  Shared-expert units are 16 bf16 rows x one K
+//   dec1_gateup: gate/up GEMVs.  One persistent work-group of 16 waves per
+//     CU (the waves share one routed table); each takes one role.  Shared-expert units are 16 bf16 rows x one K
 //     eighth, loaded straight into MFMA B registers, x as the A operand.  The
 //     routed role is a table lookup: a work-group owns one 1024-wide K chunk,
 //     builds T[g][c] = codeword c . x[8g .. 8g+7] for the chunk's 128 groups
@@ -45,8 +45,10 @@
 namespace moe {
 
 constexpr int D1_THREADS = 512;
+constexpr int GU_THREADS = 1024;   // gate/up: 16 waves share one routed table per CU
+constexpr int GU_WAVES = GU_THREADS / 64;
 constexpr int SH_KQ = DEC_SH_KQ;   // K parts of the shared gate/up
-constexpr int SH_MAXS = 4;         // shared gate/up K steps (of 32) per wave and unit
+constexpr int SH_MAXS = 2;         // shared gate/up K steps (of 32) per wave and unit
 constexpr int DN_ROWS = 128;       // output rows of a down unit (16 per wave)
 constexpr int DN_KPART = 512;      // K part of a shared down unit
 constexpr int DN_MAXB = 8;         // Q2_K blocks per row of a routed down unit (I <= 2048)
@@ -95,7 +97,7 @@ __device__ __forceinline__ int clamp_expert(int g, int E) { return min(max(g, 0)
 // Work-groups [0, gu_sh_wg) take shared-expert units u = wg, wg + gu_sh_wg, ...;
 // the others take routed units the same way.
 template <bool XF32>
-__global__ __launch_bounds__(D1_THREADS) void dec1_gateup_kernel(DecPass p)
+__global__ __launch_bounds__(GU_THREADS) void dec1_gateup_kernel(DecPass p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
     __shared__ int kid[64];
@@ -113,9 +115,9 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_gateup_kernel(DecPass p)
         if (u >= n_units) return;                                 // uniform over the work-group
         uint16_t *xh = (uint16_t *)dsm;                           // [H]
         uint16_t *xl = xh + H;                                    // [H] (fp32 x only)
-        float *red = (float *)(dsm + (XF32 ? 4 : 2) * (size_t)H); // [8 waves][2][16]
+        float *red = (float *)(dsm + (XF32 ? 4 : 2) * (size_t)H); // [16 waves][2][16]
         // x (hi, and lo for fp32 x) into LDS once
-        for (int i = tid; i < H / 8; i += D1_THREADS) {
+        for (int i = tid; i < H / 8; i += GU_THREADS) {
             if (XF32) {
                 const float *src = (const float *)p.x + 8 * i;
                 uint32_t h[8], l[8];
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_gateup_kernel(DecPass p)
             // are never used): a load under a branch makes the compiler wait for it
 #pragma unroll
             for (int j = 0; j < SH_MAXS; ++j) {
-                const int st = min(wave + 8 * j, nsteps - 1);
+                const int st = min(wave + GU_WAVES * j, nsteps - 1);
                 G4[j] = *(const u32x4 *)(rg + 32 * st);
                 U4[j] = *(const u32x4 *)(ru + 32 * st);
             }
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_gateup_kernel(DecPass p)
             // pending there, and the next load into it would wait for it
 #pragma unroll
             for (int j = 0; j < SH_MAXS; ++j) {
-                const int st = wave + 8 * j;
+                const int st = wave + GU_WAVES * j;
                 bf16x8 a = act_rows<XF32>(xh, xl, k0 + 32 * min(st, nsteps - 1) + 8 * fc, fr);
                 if (st >= nsteps) a = bf16x8{};
                 ag = mfma16x16x32(a, __builtin_bit_cast(bf16x8, G4[j]), ag);
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_gateup_kernel(DecPass p)
                 const int m = tid >> 4, n = tid & 15;
                 float sum = 0.f;
 #pragma unroll
-                for (int w = 0; w < 8; ++w) sum += red[(w * 2 + m) * 16 + n];
+                for (int w = 0; w < GU_WAVES; ++w) sum += red[(w * 2 + m) * 16 + n];
                 p.part_sh[(int64_t)(q * 2 + m) * p.Ish + r0 + n] = sum;
             }
             __syncthreads();
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_gateup_kernel(DecPass p)
     // at or below the block covers it, and stays in the row (a block at a
     // dword boundary is never the last one, since every row has an even
     // number of blocks).
-    const int bw = wave & 3, hr = wave >> 2;
+    const int bw = wave & 3, hr = (wave >> 2) & 1, i0 = wave >> 3;
     const int B = DEC_LUT_KB * kc + min(bw, kb - 1);
     const int boff = (38 * B) & ~3;
     const bool odd = __builtin_amdgcn_readfirstlane(B & 1);
@@ -227,27 +229,24 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_gateup_kernel(DecPass p)
         const int s = t / nft, f = 128 * (t - s * nft) + 64 * i + lane;
         return (const uint32_t *)(wmat + (int64_t)kid[s] * p.gu_expert_bytes + (int64_t)f * rb + boff);
     };
-    uint32_t wa[2][10], wb2[2][10];
-    auto load = [&](int t, uint32_t (&W)[2][10]) {
+    uint32_t wa[10], wb2[10];
+    auto load = [&](int t, uint32_t (&W)[10]) {
+        const uint32_t *src = rowp(t, i0);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint32_t *src = rowp(t, i);
-#pragma unroll
-            for (int e = 0; e < 10; ++e) W[i][e] = src[e];
-        }
+        for (int e = 0; e < 10; ++e) W[e] = src[e];
     };
     // the first tile loads while the table is built
     int t = j0;
     load(t, wa);
     {
-        // wave w: codewords 32 w .. 32 w + 31 against each 32-group tile
-        const int c = 32 * wave + (lane & 31), hl = lane >> 5;
+        // wave w: codewords 32 (w % 8) .. + 31 against the 32-group tiles w / 8, w / 8 + 2, ...
+        const int c = 32 * (wave & 7) + (lane & 31), hl = lane >> 5;
         const uint64_t cw = *(const uint64_t *)(p.codebook + 8 * c);
         uint32_t cb[8];
 #pragma unroll
         for (int v = 0; v < 8; ++v) cb[v] = f32_to_bf16_exact((float)(int8_t)(cw >> (8 * v)));
         const bf16x8 Bc = __builtin_bit_cast(bf16x8, pack8(cb));
-        for (int gt = 0; gt < kb; ++gt) {
+        for (int gt = wave >> 3; gt < kb; gt += 2) {
             const int k = 256 * (DEC_LUT_KB * kc + gt) + 8 * (lane & 31);
             bf16x8 A = {};
             if (XF32) {
@@ -297,13 +296,8 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_gateup_kernel(DecPass p)
         return f16_bits_to_f32(d16) * acc;
     };
     const int64_t cstride = (int64_t)2 * p.k * p.I;               // one K chunk of part_rt
-    auto tile = [&](int tt, int buf, const uint32_t (&W)[2][10]) {
-        float a0, a1;
-        if (odd) { a0 = task(W[0], std::true_type{}); a1 = task(W[1], std::true_type{}); }
-        else { a0 = task(W[0], std::false_type{}); a1 = task(W[1], std::false_type{}); }
-        float *rr = red + (buf * 4 + bw) * 256 + 128 * hr + lane;
-        rr[0] = a0;
-        rr[64] = a1;
+    auto tile = [&](int tt, int buf, const uint32_t (&W)[10]) {
+        red[(buf * 4 + bw) * 256 + 128 * hr + 64 * i0 + lane] = odd ? task(W, std::true_type{}) : task(W, std::false_type{});
         __syncthreads();
         if (tid < 256) {
             const int s = tt / nft, f0 = 128 * (tt - s * nft);
@@ -826,7 +820,7 @@ int cu_count()
 // chunk's table and the two buffers of block sums.  One launch, so the larger.
 size_t lds_gateup(int H, bool xf32)
 {
-    const size_t sh = (size_t)(xf32 ? 4 : 2) * H + 256 * sizeof(float);
+    const size_t sh = (size_t)(xf32 ? 4 : 2) * H + 2 * 16 * GU_WAVES * sizeof(float);
     const size_t rt = (32 * DEC_LUT_KB * 256 + 2 * 4 * 256) * sizeof(float);
     return std::max(sh, rt);
 }
@@ -836,13 +830,13 @@ size_t lds_down(int nbI, int k) { return 16 * 256 * 4 * 2 + (size_t)k * (2 * (si
 // Resident work-groups per CU for a kernel at a dynamic LDS size; also lifts
 // the kernel's dynamic LDS limit to that size.  Cached per kernel.
 template <typename K>
-int resident(K kernel, size_t lds, std::atomic<uint64_t> &cache)
+int resident(K kernel, size_t lds, std::atomic<uint64_t> &cache, int threads = D1_THREADS)
 {
     const uint64_t c = cache.load(std::memory_order_relaxed);
     if (c && (c >> 32) == lds) return (int)(c & 0xffffffffu);
     (void)hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, D1_THREADS, lds) != hipSuccess || n < 1) n = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess || n < 1) n = 1;
     cache.store(((uint64_t)lds << 32) | (uint32_t)n, std::memory_order_relaxed);
     return n;
 }
@@ -872,7 +866,7 @@ void split_roles(int n_a, double c_a, int n_b, double c_b, int G, int &g_a, int 
 // table reads (one 4-byte read per 8 weights) and its rows' strided bytes, a
 // Q2_K unit by its LDS table reads and VALU work.  The role split gives each
 // role work in proportion to these costs.
-constexpr double CB2_COST = 2.0;
+constexpr double CB2_COST = 1.5;
 constexpr double Q2K_COST = 2.5;
 
 }  // namespace
@@ -880,7 +874,7 @@ constexpr double Q2K_COST = 2.5;
 bool dec_single_ok(int T, int H, int I, int Ish, int k, int gu_row_bytes, bool x_f32)
 {
     return T == 1 && k <= 64 && H % 512 == 0 && H <= 256 * DEC_LUT_KB * DN_MAXKC && (Ish == 0 || Ish % DN_KPART == 0) &&
-           I % 256 == 0 && I / 256 <= DN_MAXB && gu_row_bytes == 38 * (H / 256) && H / SH_KQ / 32 <= 8 * SH_MAXS &&
+           I % 256 == 0 && I / 256 <= DN_MAXB && gu_row_bytes == 38 * (H / 256) && H / SH_KQ / 32 <= GU_WAVES * SH_MAXS &&
            lds_gateup(H, x_f32) <= LDS_MAX && lds_down(I / 256, k) <= LDS_MAX;
 }
 
@@ -888,8 +882,8 @@ void dec_plan(DecPass &p)
 {
     const int ncu = cu_count();
     const size_t lgu = lds_gateup(p.H, p.x_f32);
-    const int occ_gu = p.x_f32 ? resident(dec1_gateup_kernel<true>, lgu, occ_gu_f32)
-                               : resident(dec1_gateup_kernel<false>, lgu, occ_gu_bf16);
+    const int occ_gu = p.x_f32 ? resident(dec1_gateup_kernel<true>, lgu, occ_gu_f32, GU_THREADS)
+                               : resident(dec1_gateup_kernel<false>, lgu, occ_gu_bf16, GU_THREADS);
     const int occ_d = resident(dec1_down_kernel, lds_down(p.nbI, p.k), occ_dn);
     // routed gate/up: work-groups in whole multiples of the K chunk count
     const int n_sh = (p.Ish / 16) * SH_KQ, ntile = p.k * p.I / 128, G = occ_gu * ncu;
@@ -907,8 +901,8 @@ hipError_t launch_dec_gateup(const DecPass &p, hipStream_t s)
 {
     const int grid = p.gu_sh_wg + p.gu_rt_wg;
     const size_t lds = lds_gateup(p.H, p.x_f32);
-    if (p.x_f32) dec1_gateup_kernel<true><<<grid, D1_THREADS, lds, s>>>(p);
-    else dec1_gateup_kernel<false><<<grid, D1_THREADS, lds, s>>>(p);
+    if (p.x_f32) dec1_gateup_kernel<true><<<grid, GU_THREADS, lds, s>>>(p);
+    else dec1_gateup_kernel<false><<<grid, GU_THREADS, lds, s>>>(p);
     return hipGetLastError();
 }
 
