@@ -16,9 +16,9 @@
 //     dec1_hform forms h = silu(g) * u once -- the routed chunk partials and
 //     the shared K parts added in order -- as two bf16 terms (hi + lo,
 //     relative error below 2^-17), with the per-16 sums Q2_K's min term needs.
-//     dec1_down_fused: a work-group owns 32 output rows; each wave takes 16 of
-//     them for two top-k slots (Q2_K) and one K quarter of the bf16 shared
-//     down, so each CU mixes table lookups with streaming; the wave sums meet
+//     dec1_down_fused: a work-group of 16 waves owns 32 output rows; each wave
+//     takes 16 of them for one top-k slot (Q2_K) and one K eighth of the bf16
+//     shared down, so each CU mixes table lookups with streaming; the wave sums meet
 //     in LDS and y is written directly.  Q2_K codes become exact bf16 values
 //     sc*q through a 32 KB LDS table indexed by (sc, code byte); the block
 //     scale d and the min term dmin * sum_j m_j X_j apply to the fp32 sums of
@@ -581,18 +581,18 @@ __global__ __launch_bounds__(64) void dec1_combine_kernel(DecPass p)
 // ============================================================== fused down
 // For k <= DF_MAXK slots, I <= 2048 and sh_inter <= 2048, h is formed once
 // (dec1_hform) and one launch computes y (dec1_down_fused).  Work-group wg
-// owns output rows DF_ROWS wg .. + DF_ROWS - 1; wave w takes the 16-row half
-// w % 2 of them for the routed slots w / 2 + 4 i (i < DF_SPW, j < k; output
-// weighted by w_j) and the shared expert's K quarter w / 2, so every CU streams
-// bf16 shared rows while it looks up Q2_K codes.  All of a wave's weight bytes
-// are requested before it computes.  The eight wave sums of a row meet in LDS
+// owns output rows DF_ROWS wg .. + DF_ROWS - 1 with 16 waves: wave w takes
+// the 16-row half w % 2 of them for top-k slot w / 2 (if < k; output weighted
+// by w_j) and the shared expert's K eighth w / 2, so every CU streams bf16
+// shared rows while it looks up Q2_K codes.  All of a wave's weight bytes are
+// requested before it computes.  The sixteen wave sums of a row meet in LDS
 // and are added in wave order.
 constexpr int DF_ROWS = 32;
 constexpr int DF_MAXK = 8;
-constexpr int DF_SPW = DF_MAXK / 4;              // routed slots per wave
-constexpr int DF_SHS = 2048 / 4 / 32;            // shared K steps per wave (sh_inter <= 2048)
-constexpr int DF_ST = DF_MAXK * 2048 / 8 / D1_THREADS;   // staged 8-element chunks of h per thread
-constexpr int DF_SX = (DF_MAXK * 8 * 16 + D1_THREADS - 1) / D1_THREADS;  // staged per-16 sums per thread
+constexpr int DF_THREADS = 1024;                 // 16 waves: one slot and one shared K eighth each
+constexpr int DF_SHS = 2048 / 8 / 32;            // shared K steps per wave (sh_inter <= 2048)
+constexpr int DF_ST = DF_MAXK * 2048 / 8 / DF_THREADS;   // staged 8-element chunks of h per thread
+constexpr int DF_SX = (DF_MAXK * 8 * 16 + DF_THREADS - 1) / DF_THREADS;  // staged per-16 sums per thread
 
 // Routed h of every slot (chunk partials added in chunk order) and shared h
 // (K parts added in order): silu(g) * u as hi + lo bf16 terms, and the
@@ -657,11 +657,11 @@ __global__ __launch_bounds__(256) void dec1_hform_kernel(DecPass p)
     }
 }
 
-__global__ __launch_bounds__(D1_THREADS) void dec1_down_fused_kernel(DecPass p)
+__global__ __launch_bounds__(DF_THREADS) void dec1_down_fused_kernel(DecPass p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
     __shared__ int kid[64];
-    __shared__ float wsum[8][16];
+    __shared__ float wsum[DF_THREADS / 64][16];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int fr = lane & 15, fc = lane >> 4;
     const int nb = p.nbI, I = p.I, k = p.k, Ish = p.Ish;
@@ -681,45 +681,44 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_down_fused_kernel(DecPass p)
     float rxm[DF_SX];
 #pragma unroll
     for (int j = 0; j < DF_ST; ++j) {
-        const int i = min(tid + D1_THREADS * j, nch - 1), slot = i / (I / 8), c = i % (I / 8);
+        const int i = min(tid + DF_THREADS * j, nch - 1), slot = i / (I / 8), c = i % (I / 8);
         rhh[j] = *(const u32x4 *)(p.h_hi + (int64_t)slot * p.hstride + 8 * c);
         rhl[j] = *(const u32x4 *)(p.h_lo + (int64_t)slot * p.hstride + 8 * c);
     }
 #pragma unroll
-    for (int j = 0; j < DF_SX; ++j) rxm[j] = p.X[min(tid + D1_THREADS * j, nxm - 1)];
+    for (int j = 0; j < DF_SX; ++j) rxm[j] = p.X[min(tid + DF_THREADS * j, nxm - 1)];
     if (Ish > 0) {
         rsh = *(const u32x4 *)(p.sh_hi + 8 * min(tid, nsc - 1));
         rsl = *(const u32x4 *)(p.sh_lo + 8 * min(tid, nsc - 1));
     }
-    const int hg = wave & 1, wp = wave >> 1;
+    const int hg = wave & 1, wp = wave >> 1;                       // wp: this wave's slot and shared K eighth
     const int row = DF_ROWS * blockIdx.x + 16 * hg + fr;           // < H (H % 512 == 0)
     // this wave's weight bytes, all requested up front (unconditional loads:
-    // slots past k re-read slot k - 1, blocks past nb the last block, steps
-    // past the quarter its last step; none of those are used)
-    u32x4 C[DF_SPW][DN_MAXB];
-    uint32_t Sc[DF_SPW][DN_MAXB], Dd[DF_SPW][DN_MAXB];
-#pragma unroll
-    for (int i = 0; i < DF_SPW; ++i) {
-        const int j = min(wp + 4 * i, k - 1);
+    // a slot past k re-reads slot k - 1, blocks past nb the last block, steps
+    // past the eighth its last step; none of those are used)
+    u32x4 C[DN_MAXB];
+    uint32_t Sc[DN_MAXB], Dd[DN_MAXB];
+    {
+        const int j = min(wp, k - 1);
         const uint8_t *wrow = p.wd + (int64_t)kid[j] * p.d_expert_bytes + (int64_t)row * p.d_row_bytes;
 #pragma unroll
         for (int b = 0; b < DN_MAXB; ++b) {
             const uint8_t *blk = wrow + 84 * min(b, nb - 1);
-            C[i][b] = *(const u32x4 *)(blk + 20 + 16 * fc);
-            Sc[i][b] = *(const uint32_t *)(blk + 4 + 4 * fc);
-            Dd[i][b] = *(const uint32_t *)blk;
+            C[b] = *(const u32x4 *)(blk + 20 + 16 * fc);
+            Sc[b] = *(const uint32_t *)(blk + 4 + 4 * fc);
+            Dd[b] = *(const uint32_t *)blk;
         }
     }
-    const int KQs = Ish / 4, nsh = KQs / 32, kq0 = wp * KQs;
+    const int KQs = Ish / 8, nsh = KQs / 32, kq0 = wp * KQs;
     u32x4 Wsh[DF_SHS];
     if (Ish > 0) {
 #pragma unroll
-        for (int s = 0; s < DF_SHS; ++s)
-            Wsh[s] = *(const u32x4 *)(p.sd + (int64_t)row * Ish + kq0 + 32 * min(s, nsh - 1) + 8 * fc);
+        for (int st = 0; st < DF_SHS; ++st)
+            Wsh[st] = *(const u32x4 *)(p.sd + (int64_t)row * Ish + kq0 + 32 * min(st, nsh - 1) + 8 * fc);
     }
     // the code table, then the staged values (indices past the end rewrite
     // the last element with its own value)
-    for (int i = tid; i < 16 * 256; i += D1_THREADS) {
+    for (int i = tid; i < 16 * 256; i += DF_THREADS) {
         const int sc = i >> 8, byte = i & 255;
         uint32_t v[4];
 #pragma unroll
@@ -728,12 +727,12 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_down_fused_kernel(DecPass p)
     }
 #pragma unroll
     for (int j = 0; j < DF_ST; ++j) {
-        const int i = min(tid + D1_THREADS * j, nch - 1);
+        const int i = min(tid + DF_THREADS * j, nch - 1);
         *(u32x4 *)&hh[8 * i] = rhh[j];
         *(u32x4 *)&hl[8 * i] = rhl[j];
     }
 #pragma unroll
-    for (int j = 0; j < DF_SX; ++j) xm[min(tid + D1_THREADS * j, nxm - 1)] = rxm[j];
+    for (int j = 0; j < DF_SX; ++j) xm[min(tid + DF_THREADS * j, nxm - 1)] = rxm[j];
     if (Ish > 0) {
         *(u32x4 *)&sh[8 * min(tid, nsc - 1)] = rsh;
         *(u32x4 *)&sl[8 * min(tid, nsc - 1)] = rsl;
@@ -741,7 +740,6 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_down_fused_kernel(DecPass p)
     __syncthreads();                                               // h, X, shared h, table staged
 
     float yv = 0.f;                                                // this lane's row (lanes fc == 0)
-    float ysh = 0.f;
     if (Ish > 0) {
         f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -750,56 +748,55 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_down_fused_kernel(DecPass p)
             if (st >= nsh) a = bf16x8{};
             P = mfma16x16x32(a, __builtin_bit_cast(bf16x8, Wsh[st]), P);
         }
-        ysh = P[0] + P[1];
+        yv = P[0] + P[1];
     }
-    const uint16_t *hrow = (fr & 1) ? hl : hh;                     // A rows 0, 1: h hi, lo
-#pragma unroll
-    for (int i = 0; i < DF_SPW; ++i) {
-        const int j = wp + 4 * i;
-        if (j >= k) break;                                         // uniform over the wave
-        const uint16_t *sa_row = hrow + j * I;
-        const float *sx = xm + j * nb * 16;
+    if (wp < k) {                                                  // uniform over the wave
+        const uint16_t *sa_row = ((fr & 1) ? hl : hh) + wp * I;    // A rows 0, 1: h hi, lo
+        const float *sx = xm + wp * nb * 16;
         float acc = 0.f, accm = 0.f;
 #pragma unroll
         for (int bl = 0; bl < DN_MAXB; ++bl) {
             const int b = min(bl, nb - 1);
-            const uint32_t cw[4] = {C[i][bl].x, C[i][bl].y, C[i][bl].z, C[i][bl].w};
-            const uint32_t scw = Sc[i][bl];
-            bf16x8 a[8];
-            act_block<true>(sa_row, 256 * b + 64 * fc, 8, fr, a);
-            u32x4 Bq[8];
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int sc = (scw >> (8 * (m >> 1))) & 15;
-                const uint32_t word = cw[m >> 1];
-                const int by0 = (word >> (16 * (m & 1))) & 255, by1 = (word >> (16 * (m & 1) + 8)) & 255;
-                const uint2 t0 = *(const uint2 *)&tab[4 * (sc * 256 + by0)];
-                const uint2 t1 = *(const uint2 *)&tab[4 * (sc * 256 + by1)];
-                Bq[m] = u32x4{t0.x, t0.y, t1.x, t1.y};
-            }
+            const uint32_t cw[4] = {C[bl].x, C[bl].y, C[bl].z, C[bl].w};
+            const uint32_t scw = Sc[bl];
             f32x4 P = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < 8; ++m) P = mfma16x16x32(a[m], __builtin_bit_cast(bf16x8, Bq[m]), P);
+            for (int mh = 0; mh < 2; ++mh) {
+                bf16x8 a[4];
+                u32x4 Bq[4];
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) {
+                    const int m = 4 * mh + mm;
+                    a[mm] = fr < 2 ? *(const bf16x8 *)&sa_row[256 * b + 64 * fc + 8 * m] : bf16x8{};
+                    const int sc = (scw >> (8 * (m >> 1))) & 15;
+                    const uint32_t word = cw[m >> 1];
+                    const int by0 = (word >> (16 * (m & 1))) & 255, by1 = (word >> (16 * (m & 1) + 8)) & 255;
+                    const uint2 t0 = *(const uint2 *)&tab[4 * (sc * 256 + by0)];
+                    const uint2 t1 = *(const uint2 *)&tab[4 * (sc * 256 + by1)];
+                    Bq[mm] = u32x4{t0.x, t0.y, t1.x, t1.y};
+                }
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) P = mfma16x16x32(a[mm], __builtin_bit_cast(bf16x8, Bq[mm]), P);
+            }
             const f32x4 xv = *(const f32x4 *)&sx[b * 16 + 4 * fc];
             float mt = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) mt += (float)((scw >> (8 * e + 4)) & 15) * xv[e];
-            const float d = f16_bits_to_f32(Dd[i][bl] & 0xffffu), dmin = f16_bits_to_f32(Dd[i][bl] >> 16);
+            const float d = f16_bits_to_f32(Dd[bl] & 0xffffu), dmin = f16_bits_to_f32(Dd[bl] >> 16);
             acc += bl < nb ? d * (P[0] + P[1]) : 0.f;
             accm += bl < nb ? dmin * mt : 0.f;
         }
         accm += __shfl_xor(accm, 16, 64);
         accm += __shfl_xor(accm, 32, 64);
-        yv += p.topk_w[j] * (acc - accm);
+        yv += p.topk_w[wp] * (acc - accm);
     }
-    yv += ysh;
     if (fc == 0) wsum[wave][fr] = yv;
     __syncthreads();
     if (tid < DF_ROWS) {
         const int g2 = tid >> 4, r = tid & 15;
         float y = 0.f;
 #pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) y += wsum[2 * w2 + g2][r];
+        for (int w2 = 0; w2 < DF_THREADS / 128; ++w2) y += wsum[2 * w2 + g2][r];
         p.y[DF_ROWS * blockIdx.x + tid] = y;
     }
 }
@@ -921,7 +918,7 @@ hipError_t launch_dec_combine(const DecPass &p, hipStream_t s)
 
 bool dec_fused_ok(int k, int I, int Ish)
 {
-    return k <= DF_MAXK && I <= 256 * DN_MAXB && Ish <= 4 * 32 * DF_SHS && Ish % 128 == 0;
+    return k <= DF_MAXK && I <= 256 * DN_MAXB && Ish <= 8 * 32 * DF_SHS && Ish % 256 == 0;
 }
 
 size_t lds_dn_fused(int k, int I, int nbI, int Ish)
@@ -946,7 +943,7 @@ hipError_t launch_dec_down_fused(const DecPass &p, hipStream_t s)
         if (e != hipSuccess) return e;
         attr.store(lds, std::memory_order_relaxed);
     }
-    dec1_down_fused_kernel<<<p.H / DF_ROWS, D1_THREADS, lds, s>>>(p);
+    dec1_down_fused_kernel<<<p.H / DF_ROWS, DF_THREADS, lds, s>>>(p);
     return hipGetLastError();
 }
 
