@@ -584,15 +584,20 @@ __global__ __launch_bounds__(64) void dec1_combine_kernel(DecPass p)
 // owns output rows DF_ROWS wg .. + DF_ROWS - 1 with 16 waves: wave w takes
 // the 16-row half w % 2 of them for top-k slot w / 2 (if < k; output weighted
 // by w_j) and the shared expert's K eighth w / 2, so every CU streams bf16
-// shared rows while it looks up Q2_K codes.  All of a wave's weight bytes are
-// requested before it computes.  The sixteen wave sums of a row meet in LDS
-// and are added in wave order.
+// shared rows while it looks up Q2_K codes.  A wave's shared bytes are
+// requested before it computes, its routed blocks one ahead of use.  The
+// sixteen wave sums of a row meet in LDS and are added in wave order.
 constexpr int DF_ROWS = 32;
 constexpr int DF_MAXK = 8;
 constexpr int DF_THREADS = 1024;                 // 16 waves: one slot and one shared K eighth each
 constexpr int DF_SHS = 2048 / 8 / 32;            // shared K steps per wave (sh_inter <= 2048)
 constexpr int DF_ST = DF_MAXK * 2048 / 8 / DF_THREADS;   // staged 8-element chunks of h per thread
 constexpr int DF_SX = (DF_MAXK * 8 * 16 + DF_THREADS - 1) / DF_THREADS;  // staged per-16 sums per thread
+// Routed Q2_K blocks requested ahead of the one being computed.  Each wave
+// keeps few loads in flight: with all of a wave's blocks requested up front
+// the waves stall at issue until the loads drain, and the table lookups then
+// run after the stream instead of under it.
+constexpr int DF_PF = 1;
 
 // Routed h of every slot (chunk partials added in chunk order) and shared h
 // (K parts added in order): silu(g) * u as hi + lo bf16 terms, and the
@@ -693,22 +698,10 @@ __global__ __launch_bounds__(DF_THREADS) void dec1_down_fused_kernel(DecPass p)
     }
     const int hg = wave & 1, wp = wave >> 1;                       // wp: this wave's slot and shared K eighth
     const int row = DF_ROWS * blockIdx.x + 16 * hg + fr;           // < H (H % 512 == 0)
-    // this wave's weight bytes, all requested up front (unconditional loads:
-    // a slot past k re-reads slot k - 1, blocks past nb the last block, steps
-    // past the eighth its last step; none of those are used)
-    u32x4 C[DN_MAXB];
-    uint32_t Sc[DN_MAXB], Dd[DN_MAXB];
-    {
-        const int j = min(wp, k - 1);
-        const uint8_t *wrow = p.wd + (int64_t)kid[j] * p.d_expert_bytes + (int64_t)row * p.d_row_bytes;
-#pragma unroll
-        for (int b = 0; b < DN_MAXB; ++b) {
-            const uint8_t *blk = wrow + 84 * min(b, nb - 1);
-            C[b] = *(const u32x4 *)(blk + 20 + 16 * fc);
-            Sc[b] = *(const uint32_t *)(blk + 4 + 4 * fc);
-            Dd[b] = *(const uint32_t *)blk;
-        }
-    }
+    // this wave's shared-down bytes up front, its routed blocks DF_PF ahead of
+    // use (unconditional loads: a slot past k re-reads slot k - 1, blocks past
+    // nb the last block, steps past the eighth its last step; none of those
+    // are used)
     const int KQs = Ish / 8, nsh = KQs / 32, kq0 = wp * KQs;
     u32x4 Wsh[DF_SHS];
     if (Ish > 0) {
@@ -716,6 +709,17 @@ __global__ __launch_bounds__(DF_THREADS) void dec1_down_fused_kernel(DecPass p)
         for (int st = 0; st < DF_SHS; ++st)
             Wsh[st] = *(const u32x4 *)(p.sd + (int64_t)row * Ish + kq0 + 32 * min(st, nsh - 1) + 8 * fc);
     }
+    u32x4 C[DN_MAXB];
+    uint32_t Sc[DN_MAXB], Dd[DN_MAXB];
+    const uint8_t *wrow = p.wd + (int64_t)kid[min(wp, k - 1)] * p.d_expert_bytes + (int64_t)row * p.d_row_bytes;
+    auto load_block = [&](int b) {
+        const uint8_t *blk = wrow + 84 * min(b, nb - 1);
+        C[b] = *(const u32x4 *)(blk + 20 + 16 * fc);
+        Sc[b] = *(const uint32_t *)(blk + 4 + 4 * fc);
+        Dd[b] = *(const uint32_t *)blk;
+    };
+#pragma unroll
+    for (int b = 0; b < DF_PF; ++b) load_block(b);
     // the code table, then the staged values (indices past the end rewrite
     // the last element with its own value)
     for (int i = tid; i < 16 * 256; i += DF_THREADS) {
@@ -756,6 +760,7 @@ __global__ __launch_bounds__(DF_THREADS) void dec1_down_fused_kernel(DecPass p)
         float acc = 0.f, accm = 0.f;
 #pragma unroll
         for (int bl = 0; bl < DN_MAXB; ++bl) {
+            if (bl + DF_PF < DN_MAXB) load_block(bl + DF_PF);
             const int b = min(bl, nb - 1);
             const uint32_t cw[4] = {C[bl].x, C[bl].y, C[bl].z, C[bl].w};
             const uint32_t scw = Sc[bl];
