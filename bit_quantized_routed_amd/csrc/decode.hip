@@ -581,9 +581,10 @@ __global__ __launch_bounds__(64) void dec1_combine_kernel(DecPass p)
 // ============================================================== fused down
 // For k <= DF_MAXK slots, I <= 2048 and sh_inter <= 2048, h is formed once
 // (dec1_hform) and one launch computes y (dec1_down_fused).  Work-group wg
-// owns output rows DF_ROWS wg .. + DF_ROWS - 1 with 16 waves: wave w takes
-// the 16-row half w % 2 of them for top-k slot w / 2 (if < k; output weighted
-// by w_j) and the shared expert's K eighth w / 2, so every CU streams bf16
+// owns output rows rows * wg .. + rows - 1 (16 <= rows <= DF_ROWS, chosen so
+// that the work-groups cover the CUs once) with 16 waves: wave w takes the
+// 16-row half w % 2 of them for top-k slot w / 2 (if < k; output weighted by
+// w_j) and the shared expert's K eighth w / 2, so every CU streams bf16
 // shared rows while it looks up Q2_K codes.  A wave's shared bytes are
 // requested before it computes, its routed blocks one ahead of use.  The
 // sixteen wave sums of a row meet in LDS and are added in wave order.
@@ -662,7 +663,7 @@ __global__ __launch_bounds__(256) void dec1_hform_kernel(DecPass p)
     }
 }
 
-__global__ __launch_bounds__(DF_THREADS) void dec1_down_fused_kernel(DecPass p)
+__global__ __launch_bounds__(DF_THREADS) void dec1_down_fused_kernel(DecPass p, int rows)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
     __shared__ int kid[64];
@@ -697,7 +698,9 @@ __global__ __launch_bounds__(DF_THREADS) void dec1_down_fused_kernel(DecPass p)
         rsl = *(const u32x4 *)(p.sh_lo + 8 * min(tid, nsc - 1));
     }
     const int hg = wave & 1, wp = wave >> 1;                       // wp: this wave's slot and shared K eighth
-    const int row = DF_ROWS * blockIdx.x + 16 * hg + fr;           // < H (H % 512 == 0)
+    // lanes past the work-group's rows (or past H) repeat its last row; their
+    // sums are not stored
+    const int row = min(rows * (int)blockIdx.x + min(16 * hg + fr, rows - 1), p.H - 1);
     // this wave's shared-down bytes up front, its routed blocks DF_PF ahead of
     // use (unconditional loads: a slot past k re-reads slot k - 1, blocks past
     // nb the last block, steps past the eighth its last step; none of those
@@ -797,12 +800,12 @@ __global__ __launch_bounds__(DF_THREADS) void dec1_down_fused_kernel(DecPass p)
     }
     if (fc == 0) wsum[wave][fr] = yv;
     __syncthreads();
-    if (tid < DF_ROWS) {
+    if (tid < rows && rows * (int)blockIdx.x + tid < p.H) {
         const int g2 = tid >> 4, r = tid & 15;
         float y = 0.f;
 #pragma unroll
         for (int w2 = 0; w2 < DF_THREADS / 128; ++w2) y += wsum[2 * w2 + g2][r];
-        p.y[DF_ROWS * blockIdx.x + tid] = y;
+        p.y[rows * blockIdx.x + tid] = y;
     }
 }
 
@@ -948,7 +951,11 @@ hipError_t launch_dec_down_fused(const DecPass &p, hipStream_t s)
         if (e != hipSuccess) return e;
         attr.store(lds, std::memory_order_relaxed);
     }
-    dec1_down_fused_kernel<<<p.H / DF_ROWS, DF_THREADS, lds, s>>>(p);
+    // one work-group per CU where H allows: fewer rows per CU than a fixed
+    // 32 when H / 32 work-groups would leave CUs idle
+    const int ncu = cu_count();
+    const int rows = std::min(DF_ROWS, std::max(16, (p.H + ncu - 1) / ncu));
+    dec1_down_fused_kernel<<<(p.H + rows - 1) / rows, DF_THREADS, lds, s>>>(p, rows);
     return hipGetLastError();
 }
 
