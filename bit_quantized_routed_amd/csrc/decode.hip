@@ -602,26 +602,27 @@ constexpr int DF_PF = 1;
 
 // Routed h of every slot (chunk partials added in chunk order) and shared h
 // (K parts added in order): silu(g) * u as hi + lo bf16 terms, and the
-// per-16 sums of routed h for the Q2_K min term.  Four features per thread;
+// per-16 sums of routed h for the Q2_K min term.  One feature per thread, so
+// that the few bytes spread over many waves (the launch is latency-bound);
 // I % 256 == 0 and sh_inter % 512 == 0 keep whole waves on one side.
 __global__ __launch_bounds__(256) void dec1_hform_kernel(DecPass p)
 {
     const int q = blockIdx.x * 256 + threadIdx.x, lane = threadIdx.x & 63;
-    const int I = p.I, nq_rt = p.k * (I / 4);
-    if (q >= nq_rt + p.Ish / 4) return;                            // uniform over each wave
-    f32x4 g, uu;
+    const int I = p.I, nq_rt = p.k * I;
+    if (q >= nq_rt + p.Ish) return;                                // uniform over each wave
+    float g, uu;
     int slot = 0, f;
     if (q < nq_rt) {
-        slot = q / (I / 4);
-        f = 4 * (q % (I / 4));
+        slot = q / I;
+        f = q % I;
         const int64_t cstride = (int64_t)2 * p.k * I;
         const float *pg = p.part_rt + (int64_t)2 * slot * I + f;
-        f32x4 gv[DN_MAXKC], uv[DN_MAXKC];
+        float gv[DN_MAXKC], uv[DN_MAXKC];
 #pragma unroll
         for (int c = 0; c < DN_MAXKC; ++c) {
             const int64_t o = cstride * min(c, p.nkc - 1);
-            gv[c] = *(const f32x4 *)(pg + o);
-            uv[c] = *(const f32x4 *)(pg + o + I);
+            gv[c] = pg[o];
+            uv[c] = pg[o + I];
         }
         g = gv[0];
         uu = uv[0];
@@ -629,37 +630,33 @@ __global__ __launch_bounds__(256) void dec1_hform_kernel(DecPass p)
         for (int c = 1; c < DN_MAXKC; ++c)
             if (c < p.nkc) { g += gv[c]; uu += uv[c]; }
     } else {
-        f = 4 * (q - nq_rt);
-        f32x4 gv[SH_KQ], uv[SH_KQ];
+        f = q - nq_rt;
+        float gv[SH_KQ], uv[SH_KQ];
 #pragma unroll
         for (int c = 0; c < SH_KQ; ++c) {
-            gv[c] = *(const f32x4 *)&p.part_sh[(int64_t)(2 * c) * p.Ish + f];
-            uv[c] = *(const f32x4 *)&p.part_sh[(int64_t)(2 * c + 1) * p.Ish + f];
+            gv[c] = p.part_sh[(int64_t)(2 * c) * p.Ish + f];
+            uv[c] = p.part_sh[(int64_t)(2 * c + 1) * p.Ish + f];
         }
         g = gv[0];
         uu = uv[0];
 #pragma unroll
         for (int c = 1; c < SH_KQ; ++c) { g += gv[c]; uu += uv[c]; }
     }
-    uint32_t hi[4], lo[4];
-    float hs = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float h = g[e] / (1.0f + expf(-g[e])) * uu[e];
-        split_bf16(h, hi[e], lo[e]);
-        hs += h;
-    }
-    const uint2 vh = uint2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
-    const uint2 vl = uint2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+    const float h = g / (1.0f + expf(-g)) * uu;
+    uint32_t hi, lo;
+    split_bf16(h, hi, lo);
     if (q < nq_rt) {
-        *(uint2 *)&p.h_hi[(int64_t)slot * p.hstride + f] = vh;
-        *(uint2 *)&p.h_lo[(int64_t)slot * p.hstride + f] = vl;
+        p.h_hi[(int64_t)slot * p.hstride + f] = (uint16_t)hi;
+        p.h_lo[(int64_t)slot * p.hstride + f] = (uint16_t)lo;
+        float hs = h;
         hs += __shfl_xor(hs, 1, 64);
         hs += __shfl_xor(hs, 2, 64);
-        if ((lane & 3) == 0) p.X[((int64_t)slot * p.nbI + (f >> 8)) * 16 + ((f & 255) >> 4)] = hs;
+        hs += __shfl_xor(hs, 4, 64);
+        hs += __shfl_xor(hs, 8, 64);
+        if ((lane & 15) == 0) p.X[((int64_t)slot * p.nbI + (f >> 8)) * 16 + ((f & 255) >> 4)] = hs;
     } else {
-        *(uint2 *)&p.sh_hi[f] = vh;
-        *(uint2 *)&p.sh_lo[f] = vl;
+        p.sh_hi[f] = (uint16_t)hi;
+        p.sh_lo[f] = (uint16_t)lo;
     }
 }
 
@@ -936,7 +933,7 @@ size_t lds_dn_fused(int k, int I, int nbI, int Ish)
 
 hipError_t launch_dec_hform(const DecPass &p, hipStream_t s)
 {
-    const int nq = p.k * (p.I / 4) + p.Ish / 4;
+    const int nq = p.k * p.I + p.Ish;
     dec1_hform_kernel<<<(nq + 255) / 256, 256, 0, s>>>(p);
     return hipGetLastError();
 }
