@@ -537,25 +537,34 @@ hipError_t launch_ffn_prefill(const FfnPass &p, bool gateup, hipStream_t s)
 __global__ __launch_bounds__(256) void combine_kernel(const float *O, const int32_t *inv, const float *topk_w,
                                                       int T, int k, int H, int sh_parts, const float *sh, float *y)
 {
-    const int t = blockIdx.x;
+    const int t = blockIdx.x, n = 1024 * blockIdx.y + 4 * threadIdx.x;
     const int Tk = T * k;
-    for (int n = 4 * threadIdx.x; n < H; n += 4 * 256) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int q = 0; q < sh_parts; ++q) acc += *(const f32x4 *)&sh[((int64_t)q * T + t) * H + n];
-        for (int j = 0; j < k; ++j) {
-            const float w = topk_w[t * k + j];
+    if (n >= H) return;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < sh_parts; ++q) acc += *(const f32x4 *)&sh[((int64_t)q * T + t) * H + n];
+    // eight slots' rows requested together (each read once: non-temporal),
+    // then added in slot order
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        f32x4 o[8];
+        float w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = min(j0 + i, k - 1);
             const int pos = min(max(inv[t * k + j], 0), Tk - 1);
-            const f32x4 o = *(const f32x4 *)&O[(int64_t)pos * H + n];
-            acc += w * o;
+            o[i] = __builtin_nontemporal_load((const f32x4 *)&O[(int64_t)pos * H + n]);
+            w[i] = topk_w[t * k + j];
         }
-        *(f32x4 *)&y[(int64_t)t * H + n] = acc;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (j0 + i < k) acc += w[i] * o[i];
     }
+    *(f32x4 *)&y[(int64_t)t * H + n] = acc;
 }
 
 void launch_combine(const float *O, const int32_t *inv, const float *topk_w, int T, int k, int H, int sh_parts,
                     const float *sh, float *y, hipStream_t s)
 {
-    combine_kernel<<<T, 256, 0, s>>>(O, inv, topk_w, T, k, H, sh_parts, sh, y);
+    combine_kernel<<<dim3(T, (H + 1023) / 1024), 256, 0, s>>>(O, inv, topk_w, T, k, H, sh_parts, sh, y);
 }
 
 // ============================================================== unpack
