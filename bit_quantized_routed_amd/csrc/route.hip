@@ -302,10 +302,17 @@ __global__ __launch_bounds__(1024) void route_scan(int ntiles, int E, int Tk, in
     const int e = threadIdx.x;
     int run = 0;
     if (e < E)
-        for (int tile = 0; tile < ntiles; ++tile) {
-            const int c = tile_counts[(size_t)tile * E + e];
-            tile_counts[(size_t)tile * E + e] = run;    // becomes the tile base
-            run += c;
+        for (int t0 = 0; t0 < ntiles; t0 += 16) {
+            // sixteen tiles' counts requested together, then the running sum
+            int c[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c[i] = t0 + i < ntiles ? tile_counts[(size_t)(t0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (t0 + i < ntiles) {
+                    tile_counts[(size_t)(t0 + i) * E + e] = run;   // becomes the tile base
+                    run += c[i];
+                }
         }
     part[e] = e < E ? run : 0;
     __syncthreads();
