@@ -197,11 +197,11 @@ __global__ __launch_bounds__(256) void route_logits_mfma(const void *x, const fl
 // arg-max over (logit desc, expert asc).  Each lane holds experts lane+64*i.
 // l: the token's logits, or its first partial-logit row when nparts > 1 (the
 // parts, pstride apart, are added in part order, then the bias)
+template <int MAXPL = 16>                        // experts per lane: E <= 64 * MAXPL
 __device__ __forceinline__ void wave_topk(const double *l, int E, int k, int lane, int32_t *idx_out,
                                           float *w_out, int32_t *idx_lds, int nparts = 1, size_t pstride = 0,
                                           const float *bias = nullptr)
 {
-    constexpr int MAXPL = 16;                    // E <= 1024
     // the same sum wherever a logit is needed (selection and normalisation)
     auto logit = [&](int e) {
         double s = l[e];
@@ -252,13 +252,14 @@ __device__ __forceinline__ void wave_topk(const double *l, int E, int k, int lan
     }
 }
 
+template <int MAXPL>
 __global__ __launch_bounds__(256) void route_topk(const double *logits, const float *bias, int nparts, int T,
                                                   int E, int k, int32_t *topk_idx, float *topk_w)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
-    wave_topk(logits + (size_t)t * E, E, k, lane, topk_idx + (size_t)t * k, topk_w + (size_t)t * k, nullptr,
+    wave_topk<MAXPL>(logits + (size_t)t * E, E, k, lane, topk_idx + (size_t)t * k, topk_w + (size_t)t * k, nullptr,
               nparts, (size_t)T * E, bias);
 }
 
@@ -407,7 +408,14 @@ void launch_route_topk(const double *logits, const float *bias, int T, int H, in
     // the fp64 MFMA logits leave partial sums without the bias; the other
     // logits kernels leave finished logits
     const int np = route_logits_parts(T, H);
-    route_topk<<<(T + 3) / 4, 256, 0, s>>>(logits, np > 1 ? bias : nullptr, np, T, E, k, topk_idx, topk_w);
+    // unrolled for the experts each lane holds (E <= 64 * MAXPL)
+#define MOE_TOPK(pl) route_topk<pl><<<(T + 3) / 4, 256, 0, s>>>(logits, np > 1 ? bias : nullptr, np, T, E, k, topk_idx, topk_w)
+    if (E <= 64) MOE_TOPK(1);
+    else if (E <= 128) MOE_TOPK(2);
+    else if (E <= 256) MOE_TOPK(4);
+    else if (E <= 512) MOE_TOPK(8);
+    else MOE_TOPK(16);
+#undef MOE_TOPK
 }
 
 int route_logits_parts(int T, int H) { return T > 64 && H % 64 == 0 ? ROUTE_KPARTS : 1; }
