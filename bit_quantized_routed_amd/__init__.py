@@ -53,9 +53,11 @@ class Profile(ctypes.Structure):
 
 
 _lib = None
+# the C ABI declared in include/moe.h
 EXPORTS = ["moe_route", "moe_expert_ffn_decode", "moe_expert_ffn_prefill", "q2_pack", "q2_unpack",
-           "q2_packed_bytes", "moe_workspace_bytes", "moe_status_str", "moe_last_error",
-           "moe_probe_stream_read", "moe_probe_mfma_loop"]
+           "q2_packed_bytes", "moe_workspace_bytes", "moe_status_str", "moe_last_error"]
+# measurement kernels the benchmark uses (csrc/moe_probe.h; not part of the layer's ABI)
+PROBE_EXPORTS = ["moe_probe_stream_read", "moe_probe_mfma_loop"]
 
 
 def lib():

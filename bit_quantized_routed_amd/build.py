@@ -5,6 +5,7 @@
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -45,15 +46,18 @@ def _run(cmd, verbose):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
-    objs = []
+    jobs = []
     for src in HOST_SOURCES:
         obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".host.o")
-        _run([CXX] + HOST_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+        jobs.append(([CXX] + HOST_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj], obj))
     for src in HIP_SOURCES:
         obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
-        _run([HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+        jobs.append(([HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj], obj))
+    # one compiler process per source, a few at a time
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", "0") or 0) or (os.cpu_count() or 1), 8))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda j: _run(j[0], verbose), jobs))
+    objs = [o for _, o in jobs]
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp, "-lpthread"], verbose)
     os.replace(tmp, LIB)

@@ -11,16 +11,17 @@
 #include "kernels.h"
 #include "route.h"
 #include "probe.h"
+#include "status.h"
 #include "moe.h"
 #include "moe_probe.h"
 
-using namespace moe;
+namespace moe {
 
 namespace {
-
 thread_local std::string g_err;
+}
 
-int fail(int code, const char *fmt, ...)
+int set_error(int code, const char *fmt, ...)
 {
     char buf[512];
     va_list ap;
@@ -31,9 +32,15 @@ int fail(int code, const char *fmt, ...)
     return code;
 }
 
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
 int hip_fail(hipError_t e, const char *what)
 {
-    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return set_error(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
 constexpr size_t ALIGN = 256;
@@ -67,11 +74,11 @@ int nblocks(int K) { return (K + 255) / 256; }
 
 int check_router(const moe_layer *L)
 {
-    if (!L) return fail(MOE_ERR_INVALID_ARG, "layer is NULL");
-    if (L->hidden < 8 || L->hidden % 8) return fail(MOE_ERR_INVALID_ARG, "hidden=%d must be a positive multiple of 8", L->hidden);
-    if (L->n_experts < 1 || L->n_experts > 1024) return fail(MOE_ERR_INVALID_ARG, "n_experts=%d outside [1,1024]", L->n_experts);
-    if (L->top_k < 1 || L->top_k > L->n_experts) return fail(MOE_ERR_INVALID_ARG, "top_k=%d outside [1,n_experts]", L->top_k);
-    if (!L->w_router) return fail(MOE_ERR_INVALID_ARG, "w_router is NULL");
+    if (!L) return set_error(MOE_ERR_INVALID_ARG, "layer is NULL");
+    if (L->hidden < 8 || L->hidden % 8) return set_error(MOE_ERR_INVALID_ARG, "hidden=%d must be a positive multiple of 8", L->hidden);
+    if (L->n_experts < 1 || L->n_experts > 1024) return set_error(MOE_ERR_INVALID_ARG, "n_experts=%d outside [1,1024]", L->n_experts);
+    if (L->top_k < 1 || L->top_k > L->n_experts) return set_error(MOE_ERR_INVALID_ARG, "top_k=%d outside [1,n_experts]", L->top_k);
+    if (!L->w_router) return set_error(MOE_ERR_INVALID_ARG, "w_router is NULL");
     return MOE_OK;
 }
 
@@ -79,21 +86,21 @@ int check_layer(const moe_layer *L)
 {
     int rc = check_router(L);
     if (rc) return rc;
-    if (L->inter < 8 || L->inter % 8) return fail(MOE_ERR_INVALID_ARG, "inter=%d must be a positive multiple of 8", L->inter);
+    if (L->inter < 8 || L->inter % 8) return set_error(MOE_ERR_INVALID_ARG, "inter=%d must be a positive multiple of 8", L->inter);
     if (L->fmt_gate_up != MOE_FMT_CB2 && L->fmt_gate_up != MOE_FMT_Q4K)
-        return fail(MOE_ERR_INVALID_ARG, "fmt_gate_up=%d must be CB2 or Q4K", L->fmt_gate_up);
+        return set_error(MOE_ERR_INVALID_ARG, "fmt_gate_up=%d must be CB2 or Q4K", L->fmt_gate_up);
     if (L->fmt_down != MOE_FMT_Q2K && L->fmt_down != MOE_FMT_Q4K)
-        return fail(MOE_ERR_INVALID_ARG, "fmt_down=%d must be Q2K or Q4K", L->fmt_down);
-    if (!L->w_gate || !L->w_up || !L->w_down) return fail(MOE_ERR_INVALID_ARG, "routed expert weights are NULL");
-    if (L->fmt_gate_up == MOE_FMT_CB2 && !L->codebook) return fail(MOE_ERR_INVALID_ARG, "CB2 needs a codebook");
+        return set_error(MOE_ERR_INVALID_ARG, "fmt_down=%d must be Q2K or Q4K", L->fmt_down);
+    if (!L->w_gate || !L->w_up || !L->w_down) return set_error(MOE_ERR_INVALID_ARG, "routed expert weights are NULL");
+    if (L->fmt_gate_up == MOE_FMT_CB2 && !L->codebook) return set_error(MOE_ERR_INVALID_ARG, "CB2 needs a codebook");
     for (const void *ptr : {L->w_gate, L->w_up, L->w_down, (const void *)L->codebook, L->sh_gate, L->sh_up,
                             L->sh_down, (const void *)L->w_router})
-        if ((uintptr_t)ptr % 16) return fail(MOE_ERR_INVALID_ARG, "layer pointer %p is not 16-byte aligned", ptr);
-    if (L->sh_inter < 0) return fail(MOE_ERR_INVALID_ARG, "sh_inter=%d < 0", L->sh_inter);
+        if ((uintptr_t)ptr % 16) return set_error(MOE_ERR_INVALID_ARG, "layer pointer %p is not 16-byte aligned", ptr);
+    if (L->sh_inter < 0) return set_error(MOE_ERR_INVALID_ARG, "sh_inter=%d < 0", L->sh_inter);
     if (L->sh_inter > 0) {
-        if (!L->sh_gate || !L->sh_up || !L->sh_down) return fail(MOE_ERR_INVALID_ARG, "shared expert weights are NULL");
+        if (!L->sh_gate || !L->sh_up || !L->sh_down) return set_error(MOE_ERR_INVALID_ARG, "shared expert weights are NULL");
         if (L->sh_inter % 256 || L->hidden % 256)
-            return fail(MOE_ERR_INVALID_ARG, "shared expert needs sh_inter and hidden multiples of 256");
+            return set_error(MOE_ERR_INVALID_ARG, "shared expert needs sh_inter and hidden multiples of 256");
     }
     return MOE_OK;
 }
@@ -229,26 +236,30 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
 {
     int rc = check_layer(L);
     if (rc) return rc;
-    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d < 0", T);
-    if (act != MOE_ACT_F32 && act != MOE_ACT_BF16) return fail(MOE_ERR_INVALID_ARG, "act=%d unknown", act);
+    if (T < 0) return set_error(MOE_ERR_INVALID_ARG, "T=%d < 0", T);
+    if (act != MOE_ACT_F32 && act != MOE_ACT_BF16) return set_error(MOE_ERR_INVALID_ARG, "act=%d unknown", act);
     if (prof) prof->n_launches = 0;
     if (T == 0) return MOE_OK;
-    if ((int64_t)T * L->top_k > (1 << 30)) return fail(MOE_ERR_INVALID_ARG, "T*k too large");
-    if (!x || !topk_idx || !topk_w || !offsets || !perm || !inv || !y) return fail(MOE_ERR_INVALID_ARG, "NULL tensor argument");
-    if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+    if ((int64_t)T * L->top_k > (1 << 30)) return set_error(MOE_ERR_INVALID_ARG, "T*k too large");
+    if (!x || !topk_idx || !topk_w || !offsets || !perm || !inv || !y) return set_error(MOE_ERR_INVALID_ARG, "NULL tensor argument");
+    if (!ws) return set_error(MOE_ERR_INVALID_ARG, "workspace is NULL");
     if ((uintptr_t)x % 16 || (uintptr_t)y % 16 || (uintptr_t)ws % 16)
-        return fail(MOE_ERR_INVALID_ARG, "x, y and the workspace must be 16-byte aligned");
+        return set_error(MOE_ERR_INVALID_ARG, "x, y and the workspace must be 16-byte aligned");
     if (prefill) {
-        if (act != MOE_ACT_BF16) return fail(MOE_ERR_INVALID_ARG, "prefill needs bf16 activations");
+        if (act != MOE_ACT_BF16) return set_error(MOE_ERR_INVALID_ARG, "prefill needs bf16 activations");
     } else {
         // Q4_K runs on the grouped-GEMM decode kernels only: every K a multiple of 512
         const bool cb2q2k = L->fmt_gate_up == MOE_FMT_CB2 && L->fmt_down == MOE_FMT_Q2K;
         const bool gemm = L->hidden % 512 == 0 && L->inter % 512 == 0 && (L->sh_inter == 0 || L->sh_inter % 512 == 0);
         if (!cb2q2k && !gemm)
-            return fail(MOE_ERR_UNSUPPORTED, "decode with Q4K needs hidden, inter and sh_inter multiples of 512");
+            return set_error(MOE_ERR_UNSUPPORTED, "decode with Q4K needs hidden, inter and sh_inter multiples of 512");
     }
+    // the grouped-GEMM kernels index activation rows with 32-bit element offsets
+    const int64_t act_rows = (int64_t)T * L->top_k + (L->sh_inter > 0 ? T : 0);
+    if ((int64_t)T * L->hidden >= ((int64_t)1 << 31) || act_rows * std::max(L->inter, L->sh_inter) >= ((int64_t)1 << 31))
+        return set_error(MOE_ERR_UNSUPPORTED, "T=%d: activations beyond 2^31 elements per call", T);
     const size_t need = ffn_ws_bytes(L, T, prefill);
-    if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    if (ws_bytes < need) return set_error(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
     const bool single = dec_single(L, T, prefill, act == MOE_ACT_F32);
     FfnWs w = ffn_ws(L, single ? 1 : T, prefill, single, (char *)ws);
 
@@ -425,15 +436,18 @@ int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bi
 {
     int rc = check_router(L);
     if (rc) return rc;
-    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%d < 0", T);
-    if (act != MOE_ACT_F32 && act != MOE_ACT_BF16) return fail(MOE_ERR_INVALID_ARG, "act=%d unknown", act);
+    if (T < 0) return set_error(MOE_ERR_INVALID_ARG, "T=%d < 0", T);
+    if (act != MOE_ACT_F32 && act != MOE_ACT_BF16) return set_error(MOE_ERR_INVALID_ARG, "act=%d unknown", act);
     if (prof) prof->n_launches = 0;
     if (T == 0) return MOE_OK;
-    if ((int64_t)T * L->top_k > (1 << 30)) return fail(MOE_ERR_INVALID_ARG, "T*k too large");
-    if (!x || !topk_idx || !topk_w || !offsets || !perm || !inv) return fail(MOE_ERR_INVALID_ARG, "NULL tensor argument");
-    if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+    if ((int64_t)T * L->top_k > (1 << 30)) return set_error(MOE_ERR_INVALID_ARG, "T*k too large");
+    if (!x || !topk_idx || !topk_w || !offsets || !perm || !inv) return set_error(MOE_ERR_INVALID_ARG, "NULL tensor argument");
+    if (!ws) return set_error(MOE_ERR_INVALID_ARG, "workspace is NULL");
+    // the logit kernels read x and W_r in 8- and 16-byte pieces
+    if ((uintptr_t)x % 16 || (uintptr_t)L->w_router % 16 || (uintptr_t)ws % 16)
+        return set_error(MOE_ERR_INVALID_ARG, "x, w_router and the workspace must be 16-byte aligned");
     RouteWs w = route_ws(L, T, (char *)ws);
-    if (ws_bytes < w.bytes) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.bytes);
+    if (ws_bytes < w.bytes) return set_error(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, w.bytes);
 
     hipStream_t s = (hipStream_t)stream;
     Prof pr{prof, s};
@@ -484,12 +498,12 @@ int moe_expert_ffn_prefill(const moe_layer *L, const void *x, int act, int T, co
 int q2_unpack(int fmt, const void *packed_dev, int64_t rows, int K, const int8_t *codebook_dev, float *out_dev,
               void *stream)
 {
-    if (!fmt_ok(fmt)) return fail(MOE_ERR_INVALID_ARG, "fmt=%d unknown", fmt);
-    if (rows < 0 || K < 1) return fail(MOE_ERR_INVALID_ARG, "rows=%lld K=%d", (long long)rows, K);
+    if (!fmt_ok(fmt)) return set_error(MOE_ERR_INVALID_ARG, "fmt=%d unknown", fmt);
+    if (rows < 0 || K < 1) return set_error(MOE_ERR_INVALID_ARG, "rows=%lld K=%d", (long long)rows, K);
     if (rows == 0) return MOE_OK;
-    if (!packed_dev || !out_dev) return fail(MOE_ERR_INVALID_ARG, "NULL tensor argument");
-    if (fmt == MOE_FMT_CB2 && !codebook_dev) return fail(MOE_ERR_INVALID_ARG, "CB2 needs a codebook");
-    if (rows * nblocks(K) * 8 > ((int64_t)1 << 40)) return fail(MOE_ERR_INVALID_ARG, "too large");
+    if (!packed_dev || !out_dev) return set_error(MOE_ERR_INVALID_ARG, "NULL tensor argument");
+    if (fmt == MOE_FMT_CB2 && !codebook_dev) return set_error(MOE_ERR_INVALID_ARG, "CB2 needs a codebook");
+    if (rows * nblocks(K) * 8 > ((int64_t)1 << 40)) return set_error(MOE_ERR_INVALID_ARG, "too large");
     hipError_t e = launch_unpack(fmt, (const uint8_t *)packed_dev, rows, K, codebook_dev, out_dev, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "q2_unpack launch");
     return MOE_OK;
@@ -497,10 +511,10 @@ int q2_unpack(int fmt, const void *packed_dev, int64_t rows, int K, const int8_t
 
 int moe_probe_stream_read(const void *buf, size_t bytes, int grid, int nontemporal, void *sink, void *stream)
 {
-    if (!buf || !sink) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
+    if (!buf || !sink) return set_error(MOE_ERR_INVALID_ARG, "NULL pointer");
     if (bytes == 0 || bytes % 16 || (uintptr_t)buf % 16 || (uintptr_t)sink % 16)
-        return fail(MOE_ERR_INVALID_ARG, "bytes=%zu and both pointers must be 16-byte multiples", bytes);
-    if (grid < 1 || grid > 65536) return fail(MOE_ERR_INVALID_ARG, "grid=%d outside [1, 65536]", grid);
+        return set_error(MOE_ERR_INVALID_ARG, "bytes=%zu and both pointers must be 16-byte multiples", bytes);
+    if (grid < 1 || grid > 65536) return set_error(MOE_ERR_INVALID_ARG, "grid=%d outside [1, 65536]", grid);
     hipError_t e = launch_probe_stream(buf, bytes, grid, nontemporal, sink, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "moe_probe_stream_read launch");
     return MOE_OK;
@@ -508,10 +522,10 @@ int moe_probe_stream_read(const void *buf, size_t bytes, int grid, int nontempor
 
 int moe_probe_mfma_loop(int shape, int grid, int iters, float *sink, void *stream)
 {
-    if (!sink) return fail(MOE_ERR_INVALID_ARG, "NULL pointer");
-    if (shape != 0 && shape != 1) return fail(MOE_ERR_INVALID_ARG, "shape=%d must be 0 or 1", shape);
+    if (!sink) return set_error(MOE_ERR_INVALID_ARG, "NULL pointer");
+    if (shape != 0 && shape != 1) return set_error(MOE_ERR_INVALID_ARG, "shape=%d must be 0 or 1", shape);
     if (grid < 1 || grid > 65536 || iters < 1 || iters > (1 << 24))
-        return fail(MOE_ERR_INVALID_ARG, "grid=%d or iters=%d out of range", grid, iters);
+        return set_error(MOE_ERR_INVALID_ARG, "grid=%d or iters=%d out of range", grid, iters);
     hipError_t e = launch_probe_mfma(shape, grid, iters, sink, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "moe_probe_mfma_loop launch");
     return MOE_OK;

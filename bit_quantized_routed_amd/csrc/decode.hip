@@ -40,6 +40,7 @@
 
 #include "common.h"
 #include "decode.h"
+#include "devcache.h"
 #include "kernels.h"
 
 namespace moe {
@@ -809,15 +810,6 @@ __global__ __launch_bounds__(DF_THREADS) void dec1_down_fused_kernel(DecPass p, 
 // ============================================================== launchers
 namespace {
 
-int cu_count()
-{
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-        n = 256;
-    return n;
-}
-
 // shared role: x (one or two bf16 terms) and the wave sums; routed role: the
 // chunk's table and the two buffers of block sums.  One launch, so the larger.
 size_t lds_gateup(int H, bool xf32)
@@ -830,20 +822,22 @@ size_t lds_gateup(int H, bool xf32)
 size_t lds_down(int nbI, int k) { return 16 * 256 * 4 * 2 + (size_t)k * (2 * (size_t)nbI * 256 * 2 + (size_t)nbI * 32 * 2); }
 
 // Resident work-groups per CU for a kernel at a dynamic LDS size; also lifts
-// the kernel's dynamic LDS limit to that size.  Cached per kernel.
+// the kernel's dynamic LDS limit to that size.  Kept per device, with the LDS
+// size it was computed for.
 template <typename K>
-int resident(K kernel, size_t lds, std::atomic<uint64_t> &cache, int threads = D1_THREADS)
+int resident(K kernel, size_t lds, DevSlots &cache, int threads = D1_THREADS)
 {
-    const uint64_t c = cache.load(std::memory_order_relaxed);
+    const int slot = device_slot();
+    const uint64_t c = cache.get(slot);
     if (c && (c >> 32) == lds) return (int)(c & 0xffffffffu);
     (void)hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess || n < 1) n = 1;
-    cache.store(((uint64_t)lds << 32) | (uint32_t)n, std::memory_order_relaxed);
+    cache.set(slot, ((uint64_t)lds << 32) | (uint32_t)n);
     return n;
 }
 
-std::atomic<uint64_t> occ_gu_bf16{0}, occ_gu_f32{0}, occ_dn{0};
+DevSlots occ_gu_bf16{}, occ_gu_f32{}, occ_dn{};
 
 // Split G work-groups between two roles with n_a units of cost c_a and n_b
 // units of cost c_b, minimising the larger per-work-group load.
@@ -941,13 +935,9 @@ hipError_t launch_dec_hform(const DecPass &p, hipStream_t s)
 hipError_t launch_dec_down_fused(const DecPass &p, hipStream_t s)
 {
     const size_t lds = lds_dn_fused(p.k, p.I, p.nbI, p.Ish);
-    static std::atomic<size_t> attr{0};                            // the dynamic LDS limit last set
-    if (attr.load(std::memory_order_relaxed) < lds) {
-        const hipError_t e = hipFuncSetAttribute((const void *)dec1_down_fused_kernel,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr.store(lds, std::memory_order_relaxed);
-    }
+    static DevSlots attr{};                                        // dynamic LDS limit set, per device
+    const hipError_t e = lds_limit((const void *)dec1_down_fused_kernel, attr, lds);
+    if (e != hipSuccess) return e;
     // one work-group per CU where H allows: fewer rows per CU than a fixed
     // 32 when H / 32 work-groups would leave CUs idle
     const int ncu = cu_count();

@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "moe.h"
+#include "status.h"
 
 namespace {
 
@@ -172,10 +173,13 @@ void block_cb2(const float *x, const Codebook &C, uint8_t *o)
 
 extern "C" int q2_pack(int fmt, const float *w_host, int64_t rows, int K, const int8_t *codebook_host, void *out_host)
 {
-    if (fmt != MOE_FMT_CB2 && fmt != MOE_FMT_Q2K && fmt != MOE_FMT_Q4K) return MOE_ERR_INVALID_ARG;
-    if (rows < 0 || K < 1) return MOE_ERR_INVALID_ARG;
+    using moe::set_error;
+    if (fmt != MOE_FMT_CB2 && fmt != MOE_FMT_Q2K && fmt != MOE_FMT_Q4K)
+        return set_error(MOE_ERR_INVALID_ARG, "q2_pack: fmt=%d is not CB2, Q2K or Q4K", fmt);
+    if (rows < 0 || K < 1) return set_error(MOE_ERR_INVALID_ARG, "q2_pack: rows=%lld K=%d", (long long)rows, K);
     if (rows == 0) return MOE_OK;
-    if (!w_host || !out_host || (fmt == MOE_FMT_CB2 && !codebook_host)) return MOE_ERR_INVALID_ARG;
+    if (!w_host || !out_host) return set_error(MOE_ERR_INVALID_ARG, "q2_pack: NULL input or output");
+    if (fmt == MOE_FMT_CB2 && !codebook_host) return set_error(MOE_ERR_INVALID_ARG, "q2_pack: CB2 needs a codebook");
     const int nb = (K + 255) / 256;
     const int bb = fmt == MOE_FMT_CB2 ? 38 : fmt == MOE_FMT_Q2K ? 84 : 144;
     Codebook *cbp = fmt == MOE_FMT_CB2 ? new Codebook(codebook_host) : nullptr;

@@ -37,6 +37,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "devcache.h"
 #include "kernels.h"
 
 namespace moe {
@@ -964,13 +965,9 @@ template <int FMT, bool GATEUP, bool DEC, bool TWO>
 hipError_t np_launch(const FfnPass &p, hipStream_t s)
 {
     constexpr int lds = np_lds_bytes<FMT, TWO>();
-    static bool attr = false;
-    if (!attr) {
-        const hipError_t e = hipFuncSetAttribute((const void *)np_kernel<FMT, GATEUP, DEC, TWO>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    static DevSlots attr{};                        // dynamic LDS limit set, per device
+    const hipError_t e = lds_limit((const void *)np_kernel<FMT, GATEUP, DEC, TWO>, attr, lds);
+    if (e != hipSuccess) return e;
     const int wg_cols = GATEUP ? 256 : 512;
     const int S = (std::max(p.N, p.Nsh) + wg_cols - 1) / wg_cols;
     // every tile the schedule can hold, the shared expert's K parts included

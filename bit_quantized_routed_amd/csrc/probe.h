@@ -1,4 +1,4 @@
-// Launchers of the machine-ceiling probes (include/moe_probe.h).
+// Launchers of the machine-ceiling probes (moe_probe.h).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stddef.h>

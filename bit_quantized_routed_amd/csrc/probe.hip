@@ -1,4 +1,4 @@
-// Machine ceilings for the benchmark (see include/moe_probe.h): a streaming
+// Machine ceilings for the benchmark (see moe_probe.h): a streaming
 // HBM read and a bf16 MFMA loop, measured on the box the kernels run on.
 #include "common.h"
 #include "probe.h"

@@ -214,7 +214,8 @@ __device__ __forceinline__ void wave_topk(const double *l, int E, int k, int lan
 #pragma unroll
     for (int i = 0; i < MAXPL; ++i) {
         const int e = lane + 64 * i;
-        v[i] = e < E ? logit(e) : -INFINITY;
+        const double s = e < E ? logit(e) : -INFINITY;
+        v[i] = s != s ? -INFINITY : s;            // NaN ranks below every number, so every lane agrees
     }
     double ssum = 0.0;
     for (int j = 0; j < k; ++j) {

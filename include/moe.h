@@ -31,6 +31,14 @@
  *    every access stays in bounds.
  *  - Calls on one stream run in order; calls on different streams that share
  *    a workspace or an output race.
+ *  - Thread safety: every entry point may be called from several host threads
+ *    at once (on one device or several).  The only state the library keeps
+ *    between calls is (a) the last error text, per thread, and (b) per-device
+ *    caches of launch facts -- a kernel's raised dynamic-LDS limit, its
+ *    resident work-groups per CU and the device's CU count -- each computed on
+ *    first use on a device, stored atomically and never changed afterwards
+ *    except upwards (the LDS limit), so a racing caller at most repeats the
+ *    query.  No entry point allocates, and none holds a lock.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -128,7 +136,8 @@ typedef struct moe_profile {
  * section 3.4.3; section 9.2 on routing quality); the function (sigmoid,
  * top-k, renormalised weights) is the workload's definition.
  * x: [T][H] of type `act` (device).  bias: fp32 [E] or NULL.  All outputs are
- * device arrays of the sizes shown.  Launches: for T <= 64 and k <= 64 fp64
+ * device arrays of the sizes shown.  x, L->w_router and ws must be 16-byte
+ * aligned (MOE_ERR_INVALID_ARG otherwise).  Launches: for T <= 64 and k <= 64 fp64
  * partial logits, then one work-group that selects and groups; otherwise
  * logits, then top-k, rank, scan and scatter. */
 int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bias,
@@ -139,7 +148,9 @@ int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bi
  * Both compute y [T][H] fp32 (overwritten) = shared expert + routing-weighted
  * sum of the k routed expert FFNs (SwiGLU), from the routing that moe_route
  * produced.  Inputs as in moe_route; x, y and ws must be 16-byte aligned
- * (MOE_ERR_INVALID_ARG otherwise).
+ * (MOE_ERR_INVALID_ARG otherwise).  One call handles at most 2^31 - 1
+ * activation elements per operand (T*H, and (T*k + T)*max(I, sh_inter)):
+ * larger T returns MOE_ERR_UNSUPPORTED (split the batch).
  *
  * moe_expert_ffn_decode -- fp32-accurate path meant for small T (any T works):
  *   weights applied exactly (integer codes as exact bf16 MFMA operands, or,
@@ -187,7 +198,7 @@ int moe_expert_ffn_prefill(const moe_layer *L, const void *x, int act, int T,
  *     codebook of the integer distance sum_i (t_i - 4096*C[idx][i])^2, lowest
  *     index on ties (0 when step == 0).
  * Rows are spread over at most 16 host threads; the bytes do not depend on the thread
- * count.  Returns MOE_OK or MOE_ERR_INVALID_ARG. */
+ * count.  Returns MOE_OK or MOE_ERR_INVALID_ARG (with moe_last_error() set). */
 int q2_pack(int fmt, const float *w_host, int64_t rows, int K, const int8_t *codebook_host,
             void *out_host);
 

@@ -28,6 +28,12 @@ def test_exports_every_declared_function():
     for name in declared:
         assert hasattr(L, name), name
     assert declared == set(M.EXPORTS)
+    # the benchmark's measurement kernels live in a header of their own, outside the public ABI
+    probe = open(os.path.join(ROOT, "bit_quantized_routed_amd", "csrc", "moe_probe.h")).read()
+    declared_probe = set(re.findall(r"^(?:int|size_t|const char \*)\s*(\w+)\s*\(", probe, flags=re.M))
+    assert declared_probe == set(M.PROBE_EXPORTS)
+    for name in declared_probe:
+        assert hasattr(L, name), name
 
 
 def _layer(**kw):
@@ -86,6 +92,40 @@ def test_ffn_validation_misc():
     assert _ffn(dec, L, T=-2) == -1
     assert _ffn(dec, L, T=0, ws=None, out=None) == 0
     assert _ffn(pre, L, out=None) == -1
+
+
+def test_route_alignment():
+    """moe_route reads x and W_r in 8- and 16-byte pieces: misaligned pointers are refused."""
+    L = M.lib()
+    out = FAKE
+    args = lambda lay, x, ws: (ctypes.byref(lay), x, 1, 4, None, out, out, out, out, out, ws, 1 << 30, None, None)
+    assert L.moe_route(*args(_layer(), FAKE + 8, FAKE)) == -1
+    assert b"aligned" in L.moe_last_error()
+    assert L.moe_route(*args(_layer(w_router=FAKE + 4), FAKE, FAKE)) == -1
+    assert L.moe_route(*args(_layer(), FAKE, FAKE + 2)) == -1
+
+
+def test_ffn_activation_offset_guard():
+    """Calls whose activation rows would pass 2^31 elements are refused (the
+    grouped-GEMM kernels use 32-bit element offsets) before any launch."""
+    dec, pre = M.lib().moe_expert_ffn_decode, M.lib().moe_expert_ffn_prefill
+    L = _layer()                                   # H 256, I 128, k 2, no shared: 2 T * 128 >= 2^31 from T = 8.4 M
+    for fn in (dec, pre):
+        assert _ffn(fn, L, T=9_000_000) == -2
+        assert b"2^31" in M.lib().moe_last_error()
+    assert _ffn(dec, _layer(hidden=7168 * 2, inter=256), T=160_000) == -2    # T * H >= 2^31
+
+
+def test_pack_sets_last_error():
+    P = M.lib().q2_pack
+    w = np.zeros((2, 256), np.float32)
+    o = np.zeros(1024, np.uint8)
+    assert P(9, w.ctypes.data, 2, 256, None, o.ctypes.data) == -1
+    assert b"q2_pack" in M.lib().moe_last_error()
+    assert P(1, w.ctypes.data, 2, 256, None, o.ctypes.data) == -1          # CB2 needs a codebook
+    assert b"codebook" in M.lib().moe_last_error()
+    assert P(2, w.ctypes.data, -1, 256, None, o.ctypes.data) == -1
+    assert P(2, None, 2, 256, None, o.ctypes.data) == -1
 
 
 def test_unpack_validation():

@@ -1,4 +1,4 @@
-"""The machine-ceiling probes (include/moe_probe.h) run and read what they
+"""The machine-ceiling probes (bit_quantized_routed_amd/csrc/moe_probe.h) run and read what they
 claim to read.  They compute nothing of the layer; the benchmark uses them to
 report rates against what this machine sustains."""
 import numpy as np
