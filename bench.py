@@ -10,8 +10,11 @@ bytes / step time in GB/s.  The weights of the timed steps rotate over
 several copies at distinct addresses, as a model cycles through its layers,
 so they do not stay in the on-chip caches.
 
-Prints one JSON line (rank 0, one GPU).  Extra workloads (batched decode,
-prefill) are reported inside it under "workloads" as context.
+Prints one JSON line (rank 0, one GPU).  Every other workload of the layer
+(batched decode, prefill, the Q4_K variants) is measured the same way and
+reported inside it under "workloads": ms per step (mean, and median / p10 /
+p90 of single steps), throughput, the dominant kernel's roofline and the
+oracle's time on the host over a bounded sample.
 """
 from __future__ import annotations
 
@@ -232,6 +235,29 @@ class Stepper:
         ms = start.elapsed_time(stop) / steps
         if not dominant:
             return ms, None, wall
+        kms = self.dominant_ms(steps, dominant)
+        return ms, kms, wall
+
+    def step_percentiles(self, steps):
+        """Median, p10 and p90 of single-step times (ms), each step bracketed by
+        its own pair of events on the layer's stream."""
+        import numpy as np
+        torch = self.torch
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for a, b in pairs:
+            a.record()
+            self.step()
+            b.record()
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in pairs])
+        return {"median": round(float(np.median(t)), 5), "p10": round(float(np.percentile(t, 10)), 5),
+                "p90": round(float(np.percentile(t, 90)), 5)}
+
+    def dominant_ms(self, steps, dominant):
+        """Average duration (ms) of launch `dominant` = (which, index) over `steps`
+        steps, bracketed by HIP events the library records on its stream."""
+        torch, M = self.torch, self.M
         pairs, profs = [], []
         for _ in range(steps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -242,33 +268,49 @@ class Stepper:
         for i in range(steps):
             self.step(profs[i] if dominant[0] == "route" else None, profs[i] if dominant[0] == "ffn" else None)
         torch.cuda.synchronize()
-        kms = sum(a.elapsed_time(b) for a, b in pairs) / steps
-        return ms, kms, wall
+        return sum(a.elapsed_time(b) for a, b in pairs) / steps
 
 
 # ------------------------------------------------------------------ CPU baseline
-def cpu_baseline(cfg, nbytes):
-    """The oracle, untuned, on the host cores: one full step of the workload
-    (route + dequantize the needed experts + FFN + combine), timed after its own
-    quantization (which is excluded)."""
-    import numpy as np
+def _blas():
     from threadpoolctl import threadpool_info
+    info = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] + [1])
+    vendor = ",".join(sorted({str(i.get("internal_api", i.get("user_api", "?"))) for i in info})) or "none"
+    return int(threads), vendor
+
+
+def cpu_baseline(cfg, n_tok):
+    """The oracle, untuned, on the host cores, over the first n_tok tokens of
+    the workload (the whole step when n_tok >= T): route + dequantize the
+    experts those tokens select + fp64 FFN + combine.  Quantizing the experts
+    beforehand (the oracle's own quantizer) is excluded.  Decode workloads
+    report the sample's algorithmic bytes (its experts, the shared expert and
+    the router, x and y) per second, prefill workloads tokens per second."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
 
     import synthetic as S
     from oracle import formats as F
     from oracle import moe_ref as R
+    import bit_quantized_routed_amd as M
 
+    n_tok = min(n_tok, cfg["T"])
     x, kind = S.tokens(cfg)
+    x = x[:n_tok]
     xf = S.bf16_to_f32(x) if kind == "bf16" else x
     wr, b = S.router_weight(cfg), S.logit_bias(cfg)
     idx0, _, _ = R.route(xf, wr, cfg["top_k"], b)
     cb = S.codebook()
     H, I = cfg["hidden"], cfg["inter"]
-    packed = {}
-    for e in np.unique(idx0):
-        packed[int(e)] = [F.pack(fmt, S.expert_weight(cfg, which, int(e)), cb)
-                          for which, fmt in (("gate", cfg["fmt_gate_up"]), ("up", cfg["fmt_gate_up"]),
-                                             ("down", cfg["fmt_down"]))]
+
+    def pack(e):
+        return e, [F.pack(fmt, S.expert_weight(cfg, which, e), cb)
+                   for which, fmt in (("gate", cfg["fmt_gate_up"]), ("up", cfg["fmt_gate_up"]),
+                                      ("down", cfg["fmt_down"]))]
+
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        packed = dict(ex.map(pack, [int(e) for e in np.unique(idx0)]))
     sh = tuple(S.bf16_to_f32(S.shared_weight_bf16(cfg, n)) for n in ("gate", "up", "down")) if cfg["sh_inter"] else None
     t0 = time.perf_counter()
     idx, w, _ = R.route(xf, wr, cfg["top_k"], b)
@@ -280,10 +322,20 @@ def cpu_baseline(cfg, nbytes):
                       F.unpack(cfg["fmt_down"], p[2], H, I, cb))
     R.moe_layer(xf, idx, w, ex, sh)
     dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": "one full %s step (T=%d): fp64 route, numpy dequant of the %d selected experts, fp64 FFN "
-                      "and combine; %.2f s" % (cfg["name"], cfg["T"], len(ex), dt)}
+    threads, vendor = _blas()
+    decode = cfg["name"].startswith("decode")
+    what = ("%d of %d tokens" % (n_tok, cfg["T"])) if n_tok < cfg["T"] else "the whole step (T=%d)" % cfg["T"]
+    sample = ("%s of %s: fp64 route, numpy dequant of the %d experts they select, fp64 FFN and combine; "
+              "%.2f s; BLAS %s" % (what, cfg["name"], len(ex), dt, vendor))
+    if decode:
+        per_expert = 2 * M.q2_packed_bytes(cfg["fmt_gate_up"], I, H) + M.q2_packed_bytes(cfg["fmt_down"], H, I)
+        xb = 2 if cfg["x_dtype"] == "bf16" else 4
+        nbytes = (len(ex) * per_expert + 3 * cfg["sh_inter"] * H * 2 + cfg["n_experts"] * H * 4
+                  + n_tok * H * (xb + 4))
+        return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "blas": vendor, "sample": sample}
+    return {"value": round(n_tok / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "blas": vendor, "sample": sample}
 
 
 # ------------------------------------------------------------------ traffic (rocprofv3 --pmc)
@@ -299,6 +351,20 @@ def read_traffic(kernel, workload):
     if not m or not h or h.group(1) != kernel_source_hash(kernel):
         return None
     return float(m.group(1))
+
+
+def read_trace_avg(kernel, workload):
+    """Average kernel execution time (ms) from the committed rocprofv3 kernel
+    trace of the workload, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "%s_kernel_trace.md" % workload)
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"trace_avg_us %s:\s*([0-9.eE+]+)" % re.escape(kernel), txt)
+    h = re.search(r"kernel_source_hash:?\s*(\w+)", txt)
+    if not m or not h or h.group(1) != kernel_source_hash():
+        return None
+    return float(m.group(1)) * 1e-3
 
 
 SWEEP_T = (1, 2, 4, 8, 16, 24, 32, 48, 64)
@@ -348,6 +414,68 @@ def sweep(args):
                       "rows": rows, "crossover_T": cross}), flush=True)
 
 
+DEFAULT_EXTRA = "decode32,prefill2048,prefill8192,prefill8192_q4k,decode32_q4k"
+# tokens of each workload the oracle baseline evaluates (the whole step at T = 1)
+CPU_SAMPLE = {"decode1": 1, "decode32": 2, "decode32_q4k": 2, "prefill2048": 2, "prefill8192": 2,
+              "prefill8192_q4k": 2}
+
+
+def measure(wl, cfg, name, steps, warmup, with_cpu):
+    """One workload on its layer: per-kernel times, the dominant kernel's
+    roofline, ms per step (mean over `steps`, and median / p10 / p90 of single
+    steps), throughput in the metric's unit and the oracle baseline."""
+    import torch
+    decode = name.startswith("decode")
+    st = Stepper(wl, cfg, decode)
+    st.step()
+    torch.cuda.synchronize()
+    n_active = st.n_active()
+    kt = st.kernel_times()
+    dom_name = max(kt, key=lambda n: kt[n][2])
+    which, kidx, _ = kt[dom_name]
+    log("%s per-kernel ms: %s" % (name, ", ".join("%s=%.4f" % (n, v[2]) for n, v in kt.items())))
+    ms, kms, wall = st.timed(steps, warmup, (which, kidx))
+    pct = st.step_percentiles(steps)
+    T = st.T
+    trace_ms = read_trace_avg(dom_name, name)
+    if decode:
+        nbytes = layer_bytes(cfg, n_active, T)
+        value = nbytes / (ms * 1e-3) / 1e9
+        kb = kernel_bytes(cfg, n_active, T, dom_name)
+        ach = kb / (kms * 1e-3) / 1e9 if kb else None
+        roof = {"bound": "hbm", "kernel": dom_name, "achieved": round(ach, 1) if ach else None,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4) if ach else None,
+                "traffic": read_traffic(dom_name, name), "algorithmic_bytes": kb, "avg_launch_ms": round(kms, 5)}
+        if trace_ms and kb:
+            roof["trace_avg_ms"] = trace_ms
+            roof["achieved_trace"] = round(kb / (trace_ms * 1e-3) / 1e9, 1)
+            roof["frac_trace"] = round(roof["achieved_trace"] / HBM_PEAK_GBS, 4)
+        out = {"ms_per_step": round(ms, 5), "GB/s": round(value, 1), "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+               "algorithmic_bytes": nbytes}
+    else:
+        fl = layer_flops(cfg, T)
+        tf = fl / (ms * 1e-3) / 1e12
+        kf = kernel_flops(cfg, T, dom_name)
+        ach = kf / (kms * 1e-3) / 1e12 if kf else None
+        roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(ach, 1) if ach else None,
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4) if ach else None,
+                "traffic": read_traffic(dom_name, name), "algorithmic_flops": kf, "avg_launch_ms": round(kms, 5)}
+        if trace_ms and kf:
+            roof["trace_avg_ms"] = trace_ms
+            roof["achieved_trace"] = round(kf / (trace_ms * 1e-3) / 1e12, 1)
+            roof["frac_trace"] = round(roof["achieved_trace"] / BF16_PEAK_TFLOPS, 4)
+        value = T / (ms * 1e-3)
+        out = {"ms_per_step": round(ms, 5), "tokens/s": round(value, 1), "TFLOP/s": round(tf, 1),
+               "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4), "algorithmic_flops": fl}
+    out.update({"T": T, "active_experts": n_active, "steps": steps, "step_ms": pct, "wall_ms_per_step": round(wall, 5),
+                "roofline": roof, "kernels_ms": {n: round(v[2], 5) for n, v in kt.items()}})
+    if with_cpu:
+        log("%s: timing the oracle on the host (cpu_baseline)" % name)
+        out["cpu_baseline"] = cpu_baseline(cfg, CPU_SAMPLE.get(name, 4))
+    log("%s: %s" % (name, {k: v for k, v in out.items() if k not in ("kernels_ms",)}))
+    return value, out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,9 +483,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode1")
     ap.add_argument("--replicas", type=int, default=8)
-    ap.add_argument("--extra", default="decode32,prefill2048",
-                    help="comma-separated extra workloads reported as context ('' for none)")
+    ap.add_argument("--extra", default=DEFAULT_EXTRA,
+                    help="comma-separated extra workloads, each measured like the headline one ('' for none)")
+    ap.add_argument("--extra-steps", type=int, default=20, help="minimum timed steps of each extra workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the machine-ceiling probes")
     ap.add_argument("--sweep", action="store_true",
                     help="only the micro-batch sweep: decode and prefill paths at T = 1..64 on the full layer "
                          "(Zipf-skewed routing), with the crossover T; one JSON line")
@@ -381,97 +511,62 @@ def main():
         sweep(args)
         return
     cfg = S.config(args.workload)
+    layers = {}
+
+    def layer_for(c, replicas):
+        key = (c["fmt_gate_up"], c["fmt_down"])
+        if key not in layers:
+            log("building layer (%s formats), %d replicas" % (c["name"], replicas))
+            t0 = time.time()
+            layers[key] = W.Workload(c, cache_dir=CACHE, progress=True, replicas=replicas)
+            log("layer ready in %.0f s" % (time.time() - t0))
+        return layers[key]
+
+    wl = layer_for(cfg, args.replicas)
+    value, head = measure(wl, cfg, args.workload, args.steps, args.warmup, not args.no_cpu_baseline)
     decode = args.workload.startswith("decode")
-    log("building layer (%s), %d replicas" % (args.workload, args.replicas))
-    t0 = time.time()
-    wl = W.Workload(cfg, cache_dir=CACHE, progress=True, replicas=args.replicas)
-    log("layer ready in %.0f s" % (time.time() - t0))
-
-    st = Stepper(wl, cfg, decode)
-    st.step()
-    torch.cuda.synchronize()
-    n_active = st.n_active()
-    kt = st.kernel_times()
-    dom_name = max(kt, key=lambda n: kt[n][2])
-    which, kidx, _ = kt[dom_name]
-    log("per-kernel ms: " + ", ".join("%s=%.4f" % (n, v[2]) for n, v in kt.items()))
-    ms, kms, wall = st.timed(args.steps, args.warmup, (which, kidx))
-    T = st.T
-    nbytes = layer_bytes(cfg, n_active, T)
-    value = nbytes / (ms * 1e-3) / 1e9
-
-    if decode:
-        kb = kernel_bytes(cfg, n_active, T, dom_name)
-        ach = kb / (kms * 1e-3) / 1e9 if kb else None
-        roof = {"bound": "hbm", "kernel": dom_name, "achieved": round(ach, 1) if ach else None,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4) if ach else None,
-                "traffic": read_traffic(dom_name, args.workload), "algorithmic_bytes": kb,
-                "avg_launch_ms": round(kms, 5)}
-    else:
-        kf = kernel_flops(cfg, T, dom_name)
-        ach = kf / (kms * 1e-3) / 1e12 if kf else None
-        roof = {"bound": "mfma", "kernel": dom_name, "achieved": round(ach, 1) if ach else None,
-                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4) if ach else None,
-                "traffic": read_traffic(dom_name, args.workload), "algorithmic_flops": kf,
-                "avg_launch_ms": round(kms, 5)}
 
     workloads = {}
     for name in [w for w in args.extra.split(",") if w and w != args.workload]:
         c2 = S.config(name)
-        dec2 = name.startswith("decode")
-        if (c2["fmt_gate_up"], c2["fmt_down"]) != (cfg["fmt_gate_up"], cfg["fmt_down"]):
-            log("skip %s (different formats)" % name)
-            continue
-        s2 = Stepper(wl, c2, dec2)
-        s2.step()
-        torch.cuda.synchronize()
-        na2 = s2.n_active()
-        steps2 = args.steps if dec2 else max(5, args.steps // 10)
-        ms2, _, _ = s2.timed(steps2, max(2, args.warmup // 4))
-        if dec2:
-            b2 = layer_bytes(c2, na2, s2.T)
-            gbs = b2 / (ms2 * 1e-3) / 1e9
-            workloads[name] = {"ms_per_step": round(ms2, 4), "GB/s": round(gbs, 1),
-                               "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "active_experts": na2, "T": s2.T}
-        else:
-            fl = layer_flops(c2, s2.T)
-            tf = fl / (ms2 * 1e-3) / 1e12
-            workloads[name] = {"ms_per_step": round(ms2, 4), "tokens/s": round(s2.T / (ms2 * 1e-3), 1),
-                               "TFLOP/s": round(tf, 1), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4), "T": s2.T}
-        log("%s: %s" % (name, workloads[name]))
+        # a layer of other formats is built once, with fewer copies (its
+        # workloads stream more bytes per step than the on-chip caches hold)
+        wl2 = layer_for(c2, min(args.replicas, 2))
+        _, workloads[name] = measure(wl2, c2, name, max(args.extra_steps, args.steps // 10),
+                                     max(2, args.warmup // 4), not args.no_cpu_baseline)
 
-    ceil = machine_ceilings()
-    log("machine ceilings: %s" % ceil)
-    meas = ceil["stream_read_GBps"] if decode else ceil["mfma_bf16_TFLOPs"]
-    roof["measured_peak"] = meas
-    roof["frac_of_measured"] = round(roof["achieved"] / meas, 4) if roof["achieved"] and meas else None
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("timing the oracle on the host (cpu_baseline)")
-        cpu = cpu_baseline(cfg, nbytes)
+    ceil = None
+    roof = head["roofline"]
+    if not args.no_ceilings:
+        ceil = machine_ceilings()
+        log("machine ceilings: %s" % ceil)
+        meas = ceil["stream_read_GBps"] if decode else ceil["mfma_bf16_TFLOPs"]
+        roof["measured_peak"] = meas
+        roof["frac_of_measured"] = round(roof["achieved"] / meas, 4) if roof["achieved"] and meas else None
 
     out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s" if decode else "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "metric": METRIC, "value": round(value, 2) if decode else round(value, 1),
+        "unit": "GB/s" if decode else "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": args.workload, "T": T, "hidden": cfg["hidden"], "inter": cfg["inter"],
+        "config": {"workload": args.workload, "T": head["T"], "hidden": cfg["hidden"], "inter": cfg["inter"],
                    "experts": cfg["n_experts"], "top_k": cfg["top_k"], "shared_inter": cfg["sh_inter"],
                    "formats": "gate/up %s, down %s, shared bf16" % (
                        {1: "CB2", 3: "Q4_K"}[cfg["fmt_gate_up"]], {2: "Q2_K", 3: "Q4_K"}[cfg["fmt_down"]]),
-                   "active_experts": n_active, "algorithmic_bytes": nbytes, "weight_replicas": args.replicas},
-        "hbm_frac": round(value / HBM_PEAK_GBS, 4) if decode else None,
-        "wall_ms_per_step": round(wall, 5),
+                   "active_experts": head["active_experts"], "weight_replicas": args.replicas},
+        "hbm_frac": head.get("hbm_frac"), "mfma_frac": head.get("mfma_frac"),
+        "step_ms": head["step_ms"],
+        "wall_ms_per_step": head["wall_ms_per_step"],
         "roofline": roof,
-        "cpu_baseline": cpu,
-        "kernels_ms": {n: round(v[2], 5) for n, v in kt.items()},
+        "cpu_baseline": head.get("cpu_baseline"),
+        "kernels_ms": head["kernels_ms"],
         "machine_ceilings": ceil,
         "kernel_source_hash": kernel_source_hash(),
         "workloads": workloads,
     }
-    if not decode:
-        out["value"] = round(T / (ms * 1e-3), 1)
+    if decode:
+        out["config"]["algorithmic_bytes"] = head["algorithmic_bytes"]
     print(json.dumps(out), flush=True)
 
 

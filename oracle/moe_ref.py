@@ -95,22 +95,37 @@ def swiglu_ffn(x: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.n
     return h @ np.asarray(w_down, np.float64).T
 
 
-def moe_layer(x, topk_idx, topk_w, expert_weights, shared=None) -> np.ndarray:
+def moe_layer(x, topk_idx, topk_w, expert_weights, shared=None, threads: int = 1) -> np.ndarray:
     """y [T, H] fp64 for the given routing.
 
     expert_weights: mapping e -> (W_gate, W_up, W_down) of dequantized fp32
-    weights; only the experts the routing selects are looked up.
+    weights, or a callable e -> the same (called once per selected expert, so
+    a full-size layer never has to be held at once); only the experts the
+    routing selects are looked up.
     shared: (W_gate, W_up, W_down) of the shared expert (bf16 values as fp32)
     or None.
+    threads > 1 evaluates the selected experts concurrently; each expert's
+    outputs depend on that expert alone, so the result is the same.
     """
     x = np.asarray(x, np.float64)
     T, k = topk_idx.shape
     H = x.shape[1]
     routed = np.zeros((T, k, H), np.float64)
-    for e in np.unique(topk_idx):
+    get = expert_weights if callable(expert_weights) else expert_weights.__getitem__
+
+    def one(e):
         rows, cols = np.nonzero(topk_idx == e)
-        wg, wu, wd = expert_weights[int(e)]
+        wg, wu, wd = get(int(e))
         routed[rows, cols] = swiglu_ffn(x[rows], wg, wu, wd)
+
+    experts = np.unique(topk_idx)
+    if threads > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(one, experts))
+    else:
+        for e in experts:
+            one(e)
     y = swiglu_ffn(x, *shared) if shared is not None else np.zeros((T, H), np.float64)
     w = np.asarray(topk_w, np.float64)
     for j in range(k):

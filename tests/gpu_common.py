@@ -58,6 +58,18 @@ def oracle_experts(cfg, experts, lib_packed=None):
     return out
 
 
+def expert_loader(cfg, lib_packed=None):
+    """e -> dequantized (oracle-packed) weights of routed expert e, one expert at
+    a time (for R.moe_layer's loader form).  When the library's packed bytes are
+    given, they must equal the oracle's."""
+    def load(e):
+        return oracle_experts(cfg, [e], lib_packed)[int(e)]
+    return load
+
+
+ORACLE_THREADS = min(16, os.cpu_count() or 1)
+
+
 def oracle_shared(cfg):
     if not cfg["sh_inter"]:
         return None

@@ -16,7 +16,8 @@ import synthetic as S
 import workload as W
 from oracle import formats as F
 from oracle import moe_ref as R
-from gpu_common import CACHE, need_gpu, oracle_experts, oracle_routing, oracle_shared, rel_l2
+from gpu_common import (CACHE, ORACLE_THREADS, expert_loader, need_gpu, oracle_experts, oracle_routing,
+                        oracle_shared, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -159,6 +160,63 @@ def test_prefill_small(small_cases, name, cfg):
 
 Q4D = dict(hidden=1024, inter=512, sh_inter=512, fmt_gate_up=S.FMT_Q4K, fmt_down=S.FMT_Q4K)
 
+# Shapes where every K is a multiple of 512, so the in-register-dequant grouped
+# GEMMs run (prefill: 96-row routed tiles, 80-row shared tiles; batched decode:
+# 32-row tiles), with enough rows per expert that hot experts span several
+# tiles and end in a partial one, and the shared expert spans several tiles.
+GEMM = dict(hidden=1024, inter=512, sh_inter=512, n_experts=8, top_k=2)
+MULTI_PRE = [
+    ("np_T600_skew", mid(600, 40, skew=True, **GEMM)),
+    ("np_T480_k4", mid(480, 41, **dict(GEMM, top_k=4))),
+    ("np_T600_skew_q4k", mid(600, 42, skew=True, fmt_gate_up=S.FMT_Q4K, fmt_down=S.FMT_Q4K, **GEMM)),
+    ("np_T400_k4_q4k", mid(400, 43, fmt_gate_up=S.FMT_Q4K, fmt_down=S.FMT_Q4K, **dict(GEMM, top_k=4))),
+]
+MULTI_DEC = [
+    ("npd_T100_skew", mid(100, 44, skew=True, **GEMM)),
+    ("npd_T90_skew_f32x", mid(90, 45, x_dtype="f32", skew=True, **GEMM)),
+    ("npd_T128_skew_q4k", mid(128, 46, skew=True, fmt_gate_up=S.FMT_Q4K, fmt_down=S.FMT_Q4K, **GEMM)),
+]
+
+
+def _tile_structure(off, bm, T, bm_sh):
+    """The routing puts several tiles on one expert, a partial last tile on
+    some expert, and several tiles on the shared expert."""
+    counts = np.diff(off)
+    assert counts.max() > 2 * bm, counts
+    assert np.any((counts % bm != 0) & (counts > bm)), counts
+    assert T > 2 * bm_sh
+
+
+@pytest.mark.parametrize("name,cfg", MULTI_PRE, ids=[n for n, _ in MULTI_PRE])
+def test_prefill_multitile(small_cases, name, cfg):
+    """Every output element of the prefill grouped GEMMs on multi-tile experts
+    (routed tiles of 96 rows, shared tiles of 80, the 32x32x16 down body on
+    1..3 row fragments)."""
+    wl, yref, routing = _case(small_cases, name, cfg)
+    _tile_structure(routing[2], 96, cfg["T"], 80)
+    x, act, r = run_route(wl, cfg)
+    check_route(r, *routing)
+    y = run_ffn(wl, x, act, r, decode=False)
+    err = rel_l2(y, yref)
+    print("[prefill] %s rel_l2=%.3e" % (name, err))
+    assert np.all(np.isfinite(y))
+    assert err <= PRE_TOL
+
+
+@pytest.mark.parametrize("name,cfg", MULTI_DEC, ids=[n for n, _ in MULTI_DEC])
+def test_decode_multitile(small_cases, name, cfg):
+    """Every output element of the batched decode GEMMs (32-row tiles, the
+    shared expert split over K parts) on multi-tile experts."""
+    wl, yref, routing = _case(small_cases, name, cfg)
+    _tile_structure(routing[2], 32, cfg["T"], 32)
+    x, act, r = run_route(wl, cfg)
+    check_route(r, *routing)
+    y = run_ffn(wl, x, act, r, decode=True)
+    err = rel_l2(y, yref)
+    print("[decode] %s rel_l2=%.3e" % (name, err))
+    assert np.all(np.isfinite(y))
+    assert err <= DEC_TOL
+
 
 @pytest.mark.parametrize("name,cfg", [("q4k_dec_T1", mid(1, 31, **Q4D)),
                                       ("q4k_dec_T5", mid(5, 32, **Q4D)),
@@ -286,16 +344,25 @@ def big_q4k():
     return W.Workload(S.config("prefill8192_q4k"), cache_dir=CACHE, progress=True)
 
 
-def sampled_check(wl, cfg, decode, n_sample):
+def sampled_check(wl, cfg, decode, n_sample, hot=0):
+    """Routing in full; y on sampled tokens: the first, the last, n_sample drawn
+    ones and, with hot > 0, the tokens in the first and last rows of the `hot`
+    most-assigned experts (their last row tile is the partial one).  n_sample
+    >= T compares every token."""
     x, act, r = run_route(wl, cfg)
     xf, idx, w, l, off, perm, inv = oracle_routing(cfg)
     check_route(r, idx, w, off, perm, inv)
     y = run_ffn(wl, x, act, r, decode=decode)
-    T = x.shape[0]
+    T, k = x.shape[0], cfg["top_k"]
     rng = np.random.default_rng(T)
-    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=min(n_sample, T), replace=False)]))[:n_sample + 1]
-    ex = oracle_experts(cfg, np.unique(idx[toks]), lib_packed=wl.packed)
-    yref = R.moe_layer(xf[toks], idx[toks], w[toks], ex, oracle_shared(cfg))
+    picks = [[0, T - 1], rng.choice(T, size=min(n_sample, T), replace=False)]
+    if hot:
+        counts = np.diff(off)
+        for e in np.argsort(-counts, kind="stable")[:hot]:
+            picks.append([perm[off[e]] // k, perm[off[e + 1] - 1] // k])
+    toks = np.unique(np.concatenate(picks))
+    yref = R.moe_layer(xf[toks], idx[toks], w[toks], expert_loader(cfg, wl.packed), oracle_shared(cfg),
+                       threads=ORACLE_THREADS)
     err = rel_l2(y[toks], yref)
     print("[%s] %s tokens=%s rel_l2=%.3e" % ("decode" if decode else "prefill", cfg["name"], toks.tolist(), err))
     assert np.all(np.isfinite(y))
@@ -307,7 +374,8 @@ def test_full_decode1(big):
 
 
 def test_full_decode32(big):
-    assert sampled_check(big, S.config("decode32"), True, 3) <= DEC_TOL
+    """Every one of the 32 tokens at the full layer shape."""
+    assert sampled_check(big, S.config("decode32"), True, 32) <= DEC_TOL
 
 
 @pytest.mark.parametrize("T", [2, 3, 4, 6])
@@ -332,19 +400,19 @@ def test_full_decode_tokenwise_bit_identical(big):
 
 
 def test_full_decode32_q4k(big_q4k):
-    assert sampled_check(big_q4k, S.config("prefill8192_q4k", T=32), True, 2) <= DEC_TOL
+    assert sampled_check(big_q4k, S.config("decode32_q4k"), True, 8) <= DEC_TOL
 
 
 def test_full_prefill2048(big):
-    assert sampled_check(big, S.config("prefill2048"), False, 2) <= PRE_TOL
+    assert sampled_check(big, S.config("prefill2048"), False, 2, hot=8) <= PRE_TOL
 
 
 def test_full_prefill8192(big):
-    assert sampled_check(big, S.config("prefill8192"), False, 2) <= PRE_TOL
+    assert sampled_check(big, S.config("prefill8192"), False, 2, hot=8) <= PRE_TOL
 
 
 def test_full_prefill8192_q4k(big_q4k):
-    assert sampled_check(big_q4k, S.config("prefill8192_q4k"), False, 2) <= PRE_TOL
+    assert sampled_check(big_q4k, S.config("prefill8192_q4k"), False, 2, hot=8) <= PRE_TOL
 
 
 # ------------------------------------------------------------------ router shapes
@@ -373,3 +441,31 @@ def test_route_shapes(T, E, k, H, bias):
     idx, w, _ = R.route(S.bf16_to_f32(xb), wr, k, b)
     off, perm, inv = R.group(idx, E)
     check_route(r, idx, w, off, perm, inv)
+
+
+# ------------------------------------------------------------------ non-finite router input
+@pytest.mark.parametrize("T", [1, 20, 100])
+def test_route_nan_token_stays_a_permutation(T):
+    """A token whose activations are NaN has NaN logits, which rank below every
+    number: its k experts are still distinct, perm stays a permutation, and the
+    other tokens route exactly as the oracle routes them (one T per router
+    path: single token, small batch, large batch)."""
+    cfg = mid(T, 47, n_experts=16, top_k=4)
+    wl = W.Workload(cfg)
+    x, act = wl.tokens(cfg)
+    bad = T // 2
+    x[bad] = 0x7fc0                                      # bf16 quiet NaN
+    r = M.Routing(T, cfg["top_k"], cfg["n_experts"])
+    M.route(wl.layer, x, act, T, None, r, wl.layer.workspace(T, M.PATH_ROUTE))
+    torch.cuda.synchronize()
+    idx, off, perm, inv = (a.cpu().numpy() for a in (r.topk_idx, r.offsets, r.perm, r.inv))
+    k, E = cfg["top_k"], cfg["n_experts"]
+    assert all(len(set(row.tolist())) == k for row in idx)
+    assert idx.min() >= 0 and idx.max() < E
+    assert np.array_equal(np.sort(perm), np.arange(T * k))
+    assert np.array_equal(inv[perm], np.arange(T * k))
+    assert np.array_equal(np.diff(off), np.bincount(idx.reshape(-1), minlength=E))
+    xf = S.bf16_to_f32(S.tokens(cfg)[0])
+    ref, _, _ = R.route(xf, S.router_weight(cfg), k)
+    keep = np.arange(T) != bad
+    assert np.array_equal(idx[keep], ref[keep])

@@ -112,3 +112,20 @@ def test_tokens_are_independent():
     for t in range(6):
         yt = R.moe_layer(x[t:t + 1], idx[t:t + 1], w[t:t + 1], ex, shared)
         assert np.allclose(yt[0], y[t], rtol=0, atol=1e-14)
+
+
+def test_expert_loader_and_threads_give_the_same_layer():
+    """Passing the experts as a loader (one at a time) and evaluating them in
+    threads changes nothing: same bits as the mapping form."""
+    rng = np.random.default_rng(5)
+    T, H, I, E, k = 9, 32, 16, 6, 3
+    x = rng.standard_normal((T, H))
+    ex = {e: tuple(rng.standard_normal(s) * 0.1 for s in ((I, H), (I, H), (H, I))) for e in range(E)}
+    idx = np.argsort(rng.standard_normal((T, E)), axis=1)[:, :k].astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    calls = []
+    load = lambda e: (calls.append(e), ex[e])[1]
+    a = R.moe_layer(x, idx, w, ex)
+    b = R.moe_layer(x, idx, w, load, threads=4)
+    assert np.array_equal(a, b)
+    assert sorted(calls) == sorted(set(idx.reshape(-1).tolist()))

@@ -33,7 +33,7 @@ def layer_key(cfg: dict) -> str:
     return hashlib.sha1(json.dumps(d, sort_keys=True).encode()).hexdigest()[:16]
 
 
-def pack_layer(cfg: dict, threads: int = 4, cache_dir: str | None = None, progress: bool = False):
+def pack_layer(cfg: dict, threads: int = 8, cache_dir: str | None = None, progress: bool = False):
     """Packed routed experts as three uint8 arrays [E, bytes_per_matrix] (gate, up, down)."""
     H, I, E = cfg["hidden"], cfg["inter"], cfg["n_experts"]
     fg, fd = cfg["fmt_gate_up"], cfg["fmt_down"]
