@@ -55,7 +55,9 @@ class Profile(ctypes.Structure):
 _lib = None
 # the C ABI declared in include/moe.h
 EXPORTS = ["moe_route", "moe_expert_ffn_decode", "moe_expert_ffn_prefill", "q2_pack", "q2_unpack",
-           "q2_packed_bytes", "moe_workspace_bytes", "moe_status_str", "moe_last_error"]
+           "q2_packed_bytes", "moe_workspace_bytes", "moe_status_str", "moe_last_error",
+           "moe_expert_ffn_decode_noalloc"]
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 # measurement kernels the benchmark uses (csrc/moe_probe.h; not part of the layer's ABI)
 PROBE_EXPORTS = ["moe_probe_stream_read", "moe_probe_mfma_loop"]
 
@@ -75,6 +77,8 @@ def lib():
     for f in (L.moe_expert_ffn_decode, L.moe_expert_ffn_prefill):
         f.argtypes = [lp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, pp]
         f.restype = i32
+    L.moe_expert_ffn_decode_noalloc.argtypes = [lp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, pp]
+    L.moe_expert_ffn_decode_noalloc.restype = i32
     L.q2_pack.argtypes = [i32, vp, i64, i32, vp, vp]
     L.q2_pack.restype = i32
     L.q2_unpack.argtypes = [i32, vp, i64, i32, vp, vp, vp]
@@ -173,6 +177,15 @@ def _ffn(fn, name, layer, x, act, T, topk_idx, topk_w, offsets, perm, inv, y, ws
 def moe_expert_ffn_decode(layer, x, act, T, topk_idx, topk_w, offsets, perm, inv, y, ws, stream=None, prof=None):
     _ffn(lib().moe_expert_ffn_decode, "moe_expert_ffn_decode", layer, x, act, T, topk_idx, topk_w, offsets,
          perm, inv, y, ws, stream, prof)
+
+
+def moe_expert_ffn_decode_noalloc(layer, x, act, T, topk_idx, topk_w, offsets, perm, inv, y, stream=None,
+                                  prof=None):
+    """moe_expert_ffn_decode on the library's fixed per-device scratch (no workspace argument)."""
+    _check(lib().moe_expert_ffn_decode_noalloc(ctypes.byref(layer), _ptr(x), act, T, _ptr(topk_idx), _ptr(topk_w),
+                                               _ptr(offsets), _ptr(perm), _ptr(inv), _ptr(y), _stream(stream),
+                                               None if prof is None else ctypes.byref(prof)),
+           "moe_expert_ffn_decode_noalloc")
 
 
 def moe_expert_ffn_prefill(layer, x, act, T, topk_idx, topk_w, offsets, perm, inv, y, ws, stream=None, prof=None):

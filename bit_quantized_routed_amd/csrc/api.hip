@@ -8,6 +8,7 @@
 #include <string>
 
 #include "decode.h"
+#include "devcache.h"
 #include "kernels.h"
 #include "route.h"
 #include "probe.h"
@@ -394,6 +395,32 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
     return MOE_OK;
 }
 
+// ---------------------------------------------------------------- no-allocation decode
+// The decode workspace of moe_expert_ffn_decode_noalloc: one fixed array per
+// device, which the library holds until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: its device
+// address is looked up once per device (hipGetSymbolAddress with that device
+// current) and only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+DevSlots g_scratch_addr{};
+
+// device address of this device's scratch array (looked up on the first call on
+// the device), or nullptr with the error text set
+void *scratch_address()
+{
+    const int slot = device_slot();
+    if (const uint64_t a = g_scratch_addr.get(slot)) return (void *)(uintptr_t)a;
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+        hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+        return nullptr;
+    }
+    g_scratch_addr.set(slot, (uint64_t)(uintptr_t)ptr);
+    return ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -486,6 +513,25 @@ int moe_expert_ffn_decode(const moe_layer *L, const void *x, int act, int T, con
                           float *y, void *ws, size_t ws_bytes, void *stream, moe_profile *prof)
 {
     return ffn_common(L, x, act, T, topk_idx, topk_w, offsets, perm, inv, y, ws, ws_bytes, stream, prof, false);
+}
+
+int moe_expert_ffn_decode_noalloc(const moe_layer *L, const void *x, int act, int T, const int32_t *topk_idx,
+                                  const float *topk_w, const int32_t *offsets, const int32_t *perm,
+                                  const int32_t *inv, float *y, void *stream, moe_profile *prof)
+{
+    int rc = check_layer(L);
+    if (rc) return rc;
+    if (T < 0) return set_error(MOE_ERR_INVALID_ARG, "T=%d < 0", T);
+    if (prof) prof->n_launches = 0;
+    if (T == 0) return MOE_OK;
+    const size_t need = ffn_ws_bytes(L, T, false);
+    if (need > MOE_NOALLOC_SCRATCH_BYTES)
+        return set_error(MOE_ERR_WORKSPACE, "decode of T=%d needs %zu workspace bytes, more than the %d of the "
+                         "no-allocation scratch", T, need, MOE_NOALLOC_SCRATCH_BYTES);
+    void *ws = scratch_address();
+    if (!ws) return MOE_ERR_HIP;
+    return ffn_common(L, x, act, T, topk_idx, topk_w, offsets, perm, inv, y, ws, MOE_NOALLOC_SCRATCH_BYTES, stream,
+                      prof, false);
 }
 
 int moe_expert_ffn_prefill(const moe_layer *L, const void *x, int act, int T, const int32_t *topk_idx,

@@ -33,12 +33,15 @@
  *    a workspace or an output race.
  *  - Thread safety: every entry point may be called from several host threads
  *    at once (on one device or several).  The only state the library keeps
- *    between calls is (a) the last error text, per thread, and (b) per-device
+ *    between calls is (a) the last error text, per thread, (b) per-device
  *    caches of launch facts -- a kernel's raised dynamic-LDS limit, its
- *    resident work-groups per CU and the device's CU count -- each computed on
- *    first use on a device, stored atomically and never changed afterwards
- *    except upwards (the LDS limit), so a racing caller at most repeats the
- *    query.  No entry point allocates, and none holds a lock.
+ *    resident work-groups per CU, the device's CU count and the device
+ *    address of the no-allocation scratch array -- each computed on first use
+ *    on a device, stored atomically and never changed afterwards except
+ *    upwards (the LDS limit), so a racing caller at most repeats the query,
+ *    and (c) the contents of that scratch array (see
+ *    moe_expert_ffn_decode_noalloc).  No entry point allocates, and none holds
+ *    a lock.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -180,6 +183,28 @@ int moe_expert_ffn_prefill(const moe_layer *L, const void *x, int act, int T,
                            const int32_t *topk_idx, const float *topk_w, const int32_t *offsets,
                            const int32_t *perm, const int32_t *inv, float *y,
                            void *ws, size_t ws_bytes, void *stream, moe_profile *prof);
+
+/* ------------------------------------------------------------ no-allocation decode
+ * moe_expert_ffn_decode_noalloc: for callers that cannot allocate device
+ * memory -- code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, kernels and results (bit for bit) as
+ * moe_expert_ffn_decode, without `ws`: the workspace is a fixed array inside
+ * the library, MOE_NOALLOC_SCRATCH_BYTES (32 MiB) of device memory on each
+ * device the library runs on, held until the process ends (enough for decode
+ * batches of about 60 tokens at H=7168, I=2048, k=8; 17 MiB at T=32).
+ * A call whose moe_workspace_bytes(L, T, MOE_PATH_DECODE) exceeds it returns
+ * MOE_ERR_WORKSPACE and launches nothing.  The call allocates nothing (no
+ * hipMalloc, no allocating library routine); on the first call on a device it
+ * looks up the array's device address once.  Every call on one device shares
+ * that device's array and leaves its contents behind: the decode kernels write
+ * every workspace byte before they read it, so nothing needs clearing, but
+ * calls that overlap in time on one device (different streams, or threads
+ * whose calls are not ordered on one stream) race on it. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+int moe_expert_ffn_decode_noalloc(const moe_layer *L, const void *x, int act, int T,
+                                  const int32_t *topk_idx, const float *topk_w, const int32_t *offsets,
+                                  const int32_t *perm, const int32_t *inv, float *y, void *stream,
+                                  moe_profile *prof);
 
 /* ------------------------------------------------------------ pack / unpack
  * q2_pack (host): quantize a row-major fp32 matrix w_host [rows][K] into
