@@ -12,8 +12,10 @@ consecutive weights of one row; a row of K weights occupies ceil(K/256)
 blocks (zero padded).
 
 Dequantization is exact in fp32: every product d*s*C, d*sc*q, dmin*m needs at
-most 21 significant bits, so the only rounding is the single subtraction of
-the min term (round-to-nearest-even, as numpy float32 arithmetic does).
+most 24 significant bits (Q6_K: 11 + 7 + 6), so the only rounding is the
+single subtraction of the min term (round-to-nearest-even, as numpy float32
+arithmetic does).  Q5_K and Q6_K are the wider layouts the pages list for
+other models' routed experts ("ds4" README mirror, section on model weights).
 """
 from __future__ import annotations
 
@@ -25,9 +27,9 @@ import numpy as np
 
 from . import lib
 
-CB2, Q2K, Q4K, BF16 = 1, 2, 3, 4
+CB2, Q2K, Q4K, BF16, Q5K, Q6K = 1, 2, 3, 4, 5, 6
 QK = 256
-BLOCK_BYTES = {CB2: 38, Q2K: 84, Q4K: 144}
+BLOCK_BYTES = {CB2: 38, Q2K: 84, Q4K: 144, Q5K: 176, Q6K: 210}
 
 
 def n_blocks(K: int) -> int:
@@ -89,10 +91,17 @@ def fields(fmt: int, packed: np.ndarray, rows: int, K: int) -> dict:
 
     CB2 : d [r,nb], s [r,nb,8], idx [r,nb,32]
     Q2_K: d, dmin [r,nb], sc, m [r,nb,16], q [r,nb,256]
-    Q4_K: d, dmin [r,nb], sc, m [r,nb,8],  q [r,nb,256]
+    Q4_K, Q5_K: d, dmin [r,nb], sc, m [r,nb,8],  q [r,nb,256]
+    Q6_K: d [r,nb], sc [r,nb,16] (signed), q [r,nb,256] (-32..31)
     """
     nb = n_blocks(K)
     blk = np.asarray(packed, dtype=np.uint8).reshape(rows, nb, BLOCK_BYTES[fmt])
+    if fmt == Q6K:
+        lo = blk[..., 18:146].astype(np.int32)
+        hi = blk[..., 146:210].astype(np.int32)
+        u = np.stack([(lo >> (4 * t)) & 0xF for t in range(2)], axis=-1).reshape(rows, nb, QK)
+        u = u | (np.stack([(hi >> (2 * t)) & 3 for t in range(4)], axis=-1).reshape(rows, nb, QK) << 4)
+        return dict(d=_f16(blk[..., 0:2]), sc=blk[..., 2:18].view(np.int8).astype(np.int32), q=u - 32)
     if fmt == CB2:
         sb = blk[..., 2:6].astype(np.int32)
         s = np.empty((rows, nb, 8), np.int32)
@@ -106,7 +115,7 @@ def fields(fmt: int, packed: np.ndarray, rows: int, K: int) -> dict:
         qb = blk[..., 20:84].astype(np.int32)
         q = np.stack([(qb >> (2 * t)) & 3 for t in range(4)], axis=-1).reshape(rows, nb, QK)
         return dict(d=d, dmin=dmin, sc=sm & 0xF, m=sm >> 4, q=q)
-    if fmt == Q4K:
+    if fmt in (Q4K, Q5K):
         sb = blk[..., 4:16].astype(np.int64)
         f = np.zeros((rows, nb, 16), np.int32)
         for n in range(16):
@@ -115,6 +124,9 @@ def fields(fmt: int, packed: np.ndarray, rows: int, K: int) -> dict:
                 f[..., n] |= (((sb[..., bit // 8] >> (bit % 8)) & 1) << t).astype(np.int32)
         qb = blk[..., 16:144].astype(np.int32)
         q = np.stack([(qb >> (4 * t)) & 0xF for t in range(2)], axis=-1).reshape(rows, nb, QK)
+        if fmt == Q5K:
+            hb = blk[..., 144:176].astype(np.int32)
+            q = q | (np.stack([(hb >> t) & 1 for t in range(8)], axis=-1).reshape(rows, nb, QK) << 4)
         return dict(d=d, dmin=dmin, sc=f[..., :8], m=f[..., 8:], q=q)
     raise ValueError("bad format %d" % fmt)
 
@@ -130,6 +142,9 @@ def unpack(fmt: int, packed: np.ndarray, rows: int, K: int,
         step = F["d"][..., None] * F["s"].astype(np.float32)             # [r,nb,8]
         step_g = np.repeat(step, 4, axis=-1)                             # group g -> sub-block g//4
         w = step_g[..., None] * C[F["idx"]]                              # [r,nb,32,8]
+    elif fmt == Q6K:
+        mul = F["d"][..., None] * F["sc"].astype(np.float32)             # [r,nb,16], exact
+        w = np.repeat(mul, 16, axis=-1) * F["q"].astype(np.float32)      # exact (<= 24 bits)
     else:
         sub = 16 if fmt == Q2K else 32
         mul = (F["d"][..., None] * F["sc"].astype(np.float32))           # [r,nb,nsub]

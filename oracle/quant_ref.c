@@ -22,6 +22,19 @@
  *        little-endian 96-bit stream (field n at bits 6n..6n+5; n<8: sc_n,
  *        n>=8: m_{n-8}) | [16:144) 4-bit q_i in bits 4*(i%2) of byte i/2.
  *        w_i = d*sc_j*q_i - dmin*m_j, j = i/32.
+ *   Q5_K 176 B: as Q4_K with 5-bit codes: [0:16) as Q4_K | [16:144) the low
+ *        4 bits of q_i in bits 4*(i%2) of byte 16+i/2 | [144:176) bit 4 of q_i
+ *        in bit i%8 of byte 144+i/8.  w_i = d*sc_j*q_i - dmin*m_j, j = i/32.
+ *   Q6_K 210 B: [0:2) fp16 d | [2:18) sixteen int8 sub-block scales sc_j
+ *        (two's complement; 16 sub-blocks of 16) | [18:146) the low 4 bits of
+ *        u_i = q_i + 32 in bits 4*(i%2) of byte 18+i/2 | [146:210) the high 2
+ *        bits of u_i in bits 2*(i%4) of byte 146+i/4.  w_i = d*sc_j*q_i,
+ *        q_i in -32..31, j = i/16 (symmetric: no min term).
+ *
+ * The pages name Q5_K and Q6_K among the routed layouts of other models'
+ * files ("ds4" README mirror, section on model weights, GLM layouts: gate/up
+ * Q2_K/Q4_K/Q5_K, down Q2_K/Q4_K/Q5_K/Q6_K); as with the others, the byte
+ * layouts are this project's own.
  *
  * Arithmetic: IEEE fp32, round-half-to-even for every rounding (rintf in the
  * default rounding mode; fp16 conversion written out below), no contraction
@@ -164,6 +177,77 @@ void ref_quant_q4k_row(const float *w, int K, uint8_t *out)
     free(buf);
 }
 
+void ref_quant_q5k_row(const float *w, int K, uint8_t *out)
+{
+    int nb = (K + QK - 1) / QK;
+    float *buf = (float *)malloc(sizeof(float) * (size_t)nb * QK);
+    padded_row(w, K, nb, buf);
+    for (int b = 0; b < nb; ++b) {
+        uint16_t db, dmb;
+        int sc[16], m[16], q[QK];
+        affine_block(buf + (size_t)b * QK, 8, 32, 31, 63, &db, &dmb, sc, m, q);
+        uint8_t *p = out + (size_t)b * 176;
+        memset(p, 0, 176);
+        put_f16(p, db);
+        put_f16(p + 2, dmb);
+        for (int n = 0; n < 16; ++n) {
+            int f = n < 8 ? sc[n] : m[n - 8];
+            for (int t = 0; t < 6; ++t) {
+                int bit = 6 * n + t;
+                if ((f >> t) & 1) p[4 + bit / 8] |= (uint8_t)(1u << (bit % 8));
+            }
+        }
+        for (int i = 0; i < QK; ++i) {
+            p[16 + i / 2] |= (uint8_t)((q[i] & 15) << (4 * (i % 2)));
+            p[144 + i / 8] |= (uint8_t)((q[i] >> 4) << (i % 8));
+        }
+    }
+    free(buf);
+}
+
+/* Q6_K, symmetric.  Per sub-block j of 16 weights: scale_j = max|w| / 31.
+ * Per block: d = fp16(max_j scale_j / 127); sc_j = rint(scale_j / d) clamped
+ * to 0..127 (0 if d == 0); q_i = rint(w_i / (d*sc_j)) clamped to -32..31 (0 if
+ * d*sc_j == 0).  d*sc_j needs at most 18 significant bits and its product with
+ * q at most 24, so the dequantized value is exact in fp32. */
+void ref_quant_q6k_row(const float *w, int K, uint8_t *out)
+{
+    int nb = (K + QK - 1) / QK;
+    float *buf = (float *)malloc(sizeof(float) * (size_t)nb * QK);
+    padded_row(w, K, nb, buf);
+    for (int b = 0; b < nb; ++b) {
+        const float *x = buf + (size_t)b * QK;
+        float scale[16], max_scale = 0.0f;
+        for (int j = 0; j < 16; ++j) {
+            float amax = 0.0f;
+            for (int i = 0; i < 16; ++i) {
+                float a = fabsf(x[16 * j + i]);
+                if (a > amax) amax = a;
+            }
+            scale[j] = amax / 31.0f;
+            if (scale[j] > max_scale) max_scale = scale[j];
+        }
+        uint16_t db = ref_f32_to_f16_bits(max_scale / 127.0f);
+        float d = ref_f16_bits_to_f32(db);
+        uint8_t *p = out + (size_t)b * 210;
+        memset(p, 0, 210);
+        put_f16(p, db);
+        for (int j = 0; j < 16; ++j) {
+            int sc = d > 0.0f ? clampi((int)rintf(scale[j] / d), 0, 127) : 0;
+            p[2 + j] = (uint8_t)(int8_t)sc;
+            float step = d * (float)sc;
+            for (int i = 0; i < 16; ++i) {
+                int k = 16 * j + i;
+                int q = step > 0.0f ? clampi((int)rintf(x[k] / step), -32, 31) : 0;
+                int u = q + 32;
+                p[18 + k / 2] |= (uint8_t)((u & 15) << (4 * (k % 2)));
+                p[146 + k / 4] |= (uint8_t)((u >> 4) << (2 * (k % 4)));
+            }
+        }
+    }
+    free(buf);
+}
+
 /* -------------------------------------------------------------------- CB2
  * Per sub-block j of 32 weights: sigma_j = max|w| / 3.  Per block:
  * d = fp16(max_j sigma_j / 15), s_j = rint(sigma_j / d) clamped to 0..15.
@@ -222,18 +306,21 @@ void ref_quant_cb2_row(const float *w, int K, const int8_t *cb, uint8_t *out)
 
 /* Quantize rows [r0, r1) of a row-major [rows][K] matrix into the packed
  * output (row r occupies nb*block_bytes bytes at r*nb*block_bytes).
- * fmt: 1 = CB2, 2 = Q2_K, 3 = Q4_K.  Returns 0 on success, -1 on a bad fmt. */
+ * fmt: 1 = CB2, 2 = Q2_K, 3 = Q4_K, 5 = Q5_K, 6 = Q6_K.  Returns 0 on
+ * success, -1 on a bad fmt. */
 int ref_quant_rows(int fmt, const float *w, int64_t r0, int64_t r1, int K, const int8_t *cb, uint8_t *out)
 {
     int nb = (K + QK - 1) / QK;
-    int bb = fmt == 1 ? 38 : fmt == 2 ? 84 : fmt == 3 ? 144 : 0;
+    int bb = fmt == 1 ? 38 : fmt == 2 ? 84 : fmt == 3 ? 144 : fmt == 5 ? 176 : fmt == 6 ? 210 : 0;
     if (!bb) return -1;
     for (int64_t r = r0; r < r1; ++r) {
         const float *row = w + r * (int64_t)K;
         uint8_t *o = out + r * (int64_t)nb * bb;
         if (fmt == 1) ref_quant_cb2_row(row, K, cb, o);
         else if (fmt == 2) ref_quant_q2k_row(row, K, o);
-        else ref_quant_q4k_row(row, K, o);
+        else if (fmt == 3) ref_quant_q4k_row(row, K, o);
+        else if (fmt == 5) ref_quant_q5k_row(row, K, o);
+        else ref_quant_q6k_row(row, K, o);
     }
     return 0;
 }

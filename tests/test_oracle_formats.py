@@ -73,6 +73,26 @@ def test_q4k_hand_scales_and_block():
         assert np.all(w[32 * j:32 * (j + 1)] == g["expect_subblock_value"][j])
 
 
+def test_q5k_hand_block():
+    g = GOLD["q5k"]
+    blk = _block(F.Q5K, g["set_bytes"])
+    blk[4:16] = np.frombuffer(bytes.fromhex(g["scale_bytes_hex"]), np.uint8)
+    w = F.unpack(F.Q5K, blk, 1, 256)[0]
+    assert w[:10].tolist() == g["expect_first10"]
+    assert np.all(w[10:32] == 0)
+    for j in range(1, 8):
+        assert np.all(w[32 * j:32 * (j + 1)] == g["expect_subblock_value"][j])
+
+
+def test_q6k_hand_block():
+    g = GOLD["q6k"]
+    w = F.unpack(F.Q6K, _block(F.Q6K, g["set_bytes"]), 1, 256)[0]
+    assert w[:3].tolist() == g["expect_first3"]
+    assert np.all(w[2:16] == -32)
+    assert np.all(w[16:32] == g["expect_subblock_value"][1])
+    assert np.all(w[32:] == g["expect_subblock_value"][2])
+
+
 def test_q4k_pack_scale_stream_agrees_with_parser():
     # the writer (C) and the parser (numpy) are separate code; read the 12
     # scale bytes of freshly packed blocks as one little-endian 96-bit stream
@@ -104,7 +124,8 @@ def _random_affine_codes(rng, nsub, n, L, S_, rows, nb):
     return w.reshape(rows, nb * nsub * n), d, dmin, sc, m, q
 
 
-@pytest.mark.parametrize("fmt,nsub,n,L,S_", [(F.Q2K, 16, 16, 3, 15), (F.Q4K, 8, 32, 15, 63)])
+@pytest.mark.parametrize("fmt,nsub,n,L,S_", [(F.Q2K, 16, 16, 3, 15), (F.Q4K, 8, 32, 15, 63),
+                                            (F.Q5K, 8, 32, 31, 63)])
 def test_affine_quantizer_inverts_dequant(fmt, nsub, n, L, S_):
     rng = np.random.default_rng(7)
     rows, nb = 24, 3
@@ -115,6 +136,25 @@ def test_affine_quantizer_inverts_dequant(fmt, nsub, n, L, S_):
     assert np.array_equal(fl["sc"], sc) and np.array_equal(fl["m"], m)
     assert np.array_equal(fl["q"], q.reshape(rows, nb, 256))
     assert np.array_equal(F.unpack(fmt, p, rows, nb * 256), w)
+
+
+def test_q6k_quantizer_inverts_dequant():
+    """Codes on the symmetric quantizer's image: every sub-block holds a code of
+    magnitude 31 (so its max |w| is 31 d sc_j) and every block a scale of 127."""
+    rng = np.random.default_rng(9)
+    rows, nb = 20, 3
+    sc = rng.integers(1, 128, size=(rows, nb, 16))
+    sc[..., 3] = 127
+    q = rng.integers(-31, 32, size=(rows, nb, 16, 16))
+    q[..., 5] = rng.choice([-31, 31], size=(rows, nb, 16))
+    d = np.float16(2.0 ** rng.uniform(-14, -8, size=(rows, nb))).astype(np.float32)
+    w = ((d[..., None] * sc)[..., None] * q).astype(np.float32).reshape(rows, nb * 256)
+    p = F.pack(F.Q6K, w)
+    fl = F.fields(F.Q6K, p, rows, nb * 256)
+    assert np.array_equal(fl["d"], d)
+    assert np.array_equal(fl["sc"], sc)
+    assert np.array_equal(fl["q"], q.reshape(rows, nb, 256))
+    assert np.array_equal(F.unpack(F.Q6K, p, rows, nb * 256), w)
 
 
 def test_cb2_quantizer_inverts_dequant():
@@ -136,7 +176,7 @@ def test_cb2_quantizer_inverts_dequant():
 
 
 # ---------------------------------------------------- optimality (brute force)
-@pytest.mark.parametrize("fmt,n,L", [(F.Q2K, 16, 3), (F.Q4K, 32, 15)])
+@pytest.mark.parametrize("fmt,n,L", [(F.Q2K, 16, 3), (F.Q4K, 32, 15), (F.Q5K, 32, 31)])
 def test_affine_codes_are_nearest_levels(fmt, n, L):
     rng = np.random.default_rng(11)
     w = (rng.standard_normal((8, 512)) * 0.02).astype(np.float32)
@@ -157,6 +197,24 @@ def test_affine_codes_are_nearest_levels(fmt, n, L):
     recon = F.unpack(fmt, p, 8, 512).astype(np.float64).reshape(wv.shape)
     bound = 0.5 * step[..., None] + 0.5 * fl["dmin"].astype(np.float64)[..., None, None] \
         + 0.5 * L * fl["d"].astype(np.float64)[..., None, None]
+    assert np.all(np.abs(recon - wv) <= bound + 1e-12)
+
+
+def test_q6k_codes_are_nearest_levels():
+    rng = np.random.default_rng(16)
+    w = (rng.standard_normal((8, 512)) * 0.02).astype(np.float32)
+    p = F.pack(F.Q6K, w)
+    fl = F.fields(F.Q6K, p, 8, 512)
+    step = (fl["d"][..., None] * fl["sc"]).astype(np.float64)          # [r, nb, 16]
+    levels = step[..., None] * np.arange(-32, 32)                       # [r, nb, 16, 64]
+    wv = w.astype(np.float64).reshape(8, 2, 16, 16)
+    err = np.abs(wv[..., None] - levels[..., None, :])                   # [r, nb, 16, 16, 64]
+    chosen = np.take_along_axis(err, (fl["q"].reshape(8, 2, 16, 16) + 32)[..., None], axis=-1)[..., 0]
+    assert np.all(chosen <= err.min(axis=-1) + 1e-6 * step[..., None])
+    # |w| <= 31.5 steps of the rounded scale: the error is at most half a step
+    # plus the part of the range lost to rounding sc_j
+    recon = F.unpack(F.Q6K, p, 8, 512).astype(np.float64).reshape(wv.shape)
+    bound = 0.5 * step[..., None] + 31.5 * 0.5 * fl["d"].astype(np.float64)[..., None, None]
     assert np.all(np.abs(recon - wv) <= bound + 1e-12)
 
 
@@ -195,7 +253,7 @@ def test_cb2_error_is_bounded():
 
 
 # -------------------------------------------------------------- zero padding
-@pytest.mark.parametrize("fmt", [F.CB2, F.Q2K, F.Q4K])
+@pytest.mark.parametrize("fmt", [F.CB2, F.Q2K, F.Q4K, F.Q5K, F.Q6K])
 def test_padding_is_zero_extension(fmt):
     rng = np.random.default_rng(14)
     K = 128 + 64
@@ -212,7 +270,7 @@ def test_padding_is_zero_extension(fmt):
 def test_fully_padded_subblocks_dequantize_to_zero():
     rng = np.random.default_rng(15)
     w = (rng.standard_normal((3, 128)) * 0.02).astype(np.float32)
-    for fmt, sub in ((F.Q2K, 16), (F.Q4K, 32), (F.CB2, 32)):
+    for fmt, sub in ((F.Q2K, 16), (F.Q4K, 32), (F.CB2, 32), (F.Q5K, 32), (F.Q6K, 16)):
         p = F.pack(fmt, w, CB)
         full = F.unpack(fmt, p, 3, 256, CB)
         assert np.all(full[:, 128:] == 0)
@@ -222,6 +280,8 @@ def test_packed_sizes():
     assert F.packed_bytes(F.CB2, 2048, 7168) == 2048 * 28 * 38
     assert F.packed_bytes(F.Q2K, 7168, 2048) == 7168 * 8 * 84
     assert F.packed_bytes(F.Q4K, 7168, 2048) == 7168 * 8 * 144
+    assert F.packed_bytes(F.Q5K, 7168, 2048) == 7168 * 8 * 176
+    assert F.packed_bytes(F.Q6K, 7168, 2048) == 7168 * 8 * 210
 
 
 def test_codebook_is_distinct_and_on_levels():
