@@ -69,8 +69,12 @@ struct Prof {
     }
 };
 
-bool fmt_ok(int f) { return f == MOE_FMT_CB2 || f == MOE_FMT_Q2K || f == MOE_FMT_Q4K; }
-int bbytes(int f) { return f == MOE_FMT_CB2 ? 38 : f == MOE_FMT_Q2K ? 84 : f == MOE_FMT_Q4K ? 144 : 0; }
+bool fmt_ok(int f) { return f == MOE_FMT_CB2 || f == MOE_FMT_Q2K || f == MOE_FMT_Q4K || f == MOE_FMT_Q5K || f == MOE_FMT_Q6K; }
+int bbytes(int f)
+{
+    return f == MOE_FMT_CB2 ? 38 : f == MOE_FMT_Q2K ? 84 : f == MOE_FMT_Q4K ? 144 : f == MOE_FMT_Q5K ? 176
+         : f == MOE_FMT_Q6K ? 210 : 0;
+}
 int nblocks(int K) { return (K + 255) / 256; }
 
 int check_router(const moe_layer *L)
@@ -88,10 +92,11 @@ int check_layer(const moe_layer *L)
     int rc = check_router(L);
     if (rc) return rc;
     if (L->inter < 8 || L->inter % 8) return set_error(MOE_ERR_INVALID_ARG, "inter=%d must be a positive multiple of 8", L->inter);
-    if (L->fmt_gate_up != MOE_FMT_CB2 && L->fmt_gate_up != MOE_FMT_Q4K)
-        return set_error(MOE_ERR_INVALID_ARG, "fmt_gate_up=%d must be CB2 or Q4K", L->fmt_gate_up);
-    if (L->fmt_down != MOE_FMT_Q2K && L->fmt_down != MOE_FMT_Q4K)
-        return set_error(MOE_ERR_INVALID_ARG, "fmt_down=%d must be Q2K or Q4K", L->fmt_down);
+    const int fg = L->fmt_gate_up, fd = L->fmt_down;
+    if (fg != MOE_FMT_CB2 && fg != MOE_FMT_Q2K && fg != MOE_FMT_Q4K && fg != MOE_FMT_Q5K)
+        return set_error(MOE_ERR_INVALID_ARG, "fmt_gate_up=%d must be CB2, Q2K, Q4K or Q5K", fg);
+    if (fd != MOE_FMT_Q2K && fd != MOE_FMT_Q4K && fd != MOE_FMT_Q5K && fd != MOE_FMT_Q6K)
+        return set_error(MOE_ERR_INVALID_ARG, "fmt_down=%d must be Q2K, Q4K, Q5K or Q6K", fd);
     if (!L->w_gate || !L->w_up || !L->w_down) return set_error(MOE_ERR_INVALID_ARG, "routed expert weights are NULL");
     if (L->fmt_gate_up == MOE_FMT_CB2 && !L->codebook) return set_error(MOE_ERR_INVALID_ARG, "CB2 needs a codebook");
     for (const void *ptr : {L->w_gate, L->w_up, L->w_down, (const void *)L->codebook, L->sh_gate, L->sh_up,
@@ -246,14 +251,22 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
     if (!ws) return set_error(MOE_ERR_INVALID_ARG, "workspace is NULL");
     if ((uintptr_t)x % 16 || (uintptr_t)y % 16 || (uintptr_t)ws % 16)
         return set_error(MOE_ERR_INVALID_ARG, "x, y and the workspace must be 16-byte aligned");
+    // CB2/Q4K gate/up with Q2K/Q4K down run on every shape; the other format
+    // pairs, and decode with anything but CB2 + Q2K, only on the grouped GEMMs
+    // with in-register dequantization, which need every K a multiple of 512
+    const bool gemm = L->hidden % 512 == 0 && L->inter % 512 == 0 && (L->sh_inter == 0 || L->sh_inter % 512 == 0);
+    const bool base_fmts = (L->fmt_gate_up == MOE_FMT_CB2 || L->fmt_gate_up == MOE_FMT_Q4K) &&
+                           (L->fmt_down == MOE_FMT_Q2K || L->fmt_down == MOE_FMT_Q4K);
     if (prefill) {
         if (act != MOE_ACT_BF16) return set_error(MOE_ERR_INVALID_ARG, "prefill needs bf16 activations");
+        if (!base_fmts && !gemm)
+            return set_error(MOE_ERR_UNSUPPORTED, "prefill with gate/up fmt %d, down fmt %d needs hidden, inter and "
+                             "sh_inter multiples of 512", L->fmt_gate_up, L->fmt_down);
     } else {
-        // Q4_K runs on the grouped-GEMM decode kernels only: every K a multiple of 512
         const bool cb2q2k = L->fmt_gate_up == MOE_FMT_CB2 && L->fmt_down == MOE_FMT_Q2K;
-        const bool gemm = L->hidden % 512 == 0 && L->inter % 512 == 0 && (L->sh_inter == 0 || L->sh_inter % 512 == 0);
         if (!cb2q2k && !gemm)
-            return set_error(MOE_ERR_UNSUPPORTED, "decode with Q4K needs hidden, inter and sh_inter multiples of 512");
+            return set_error(MOE_ERR_UNSUPPORTED, "decode with gate/up fmt %d, down fmt %d needs hidden, inter and "
+                             "sh_inter multiples of 512", L->fmt_gate_up, L->fmt_down);
     }
     // the grouped-GEMM kernels index activation rows with 32-bit element offsets
     const int64_t act_rows = (int64_t)T * L->top_k + (L->sh_inter > 0 ? T : 0);

@@ -4,6 +4,8 @@
 //   CB2  38 B  fp16 d | 8 x 4-bit s_j | 32 codebook indices (group of 8 each)
 //   Q2_K 84 B  fp16 d | fp16 dmin | 16 x (sc | m<<4) | 64 B of 2-bit codes
 //   Q4_K 144 B fp16 d | fp16 dmin | 12 B of 6-bit sc/m | 128 B of 4-bit codes
+//   Q5_K 176 B as Q4_K | 32 B plane of the codes' fifth bit
+//   Q6_K 210 B fp16 d | 16 int8 scales | 128 B low nibbles, 64 B high 2 bits of q+32
 // Only the routed experts are quantized, gate/up in the 2-bit codebook format
 // and down in Q2_K ("DwarfStar" README, section on model weights).
 #pragma once
@@ -16,9 +18,12 @@ constexpr int QK = 256;          // weights per block
 constexpr int KS = 128;          // K-step of the FFN kernels (half a block)
 constexpr int LROW = KS + 8;     // LDS row stride in bf16 elements (16 B pad)
 
-enum { FMT_CB2 = 1, FMT_Q2K = 2, FMT_Q4K = 3, FMT_BF16 = 4 };
+enum { FMT_CB2 = 1, FMT_Q2K = 2, FMT_Q4K = 3, FMT_BF16 = 4, FMT_Q5K = 5, FMT_Q6K = 6 };
 
-constexpr int block_bytes(int fmt) { return fmt == FMT_CB2 ? 38 : fmt == FMT_Q2K ? 84 : fmt == FMT_Q4K ? 144 : 0; }
+constexpr int block_bytes(int fmt)
+{
+    return fmt == FMT_CB2 ? 38 : fmt == FMT_Q2K ? 84 : fmt == FMT_Q4K ? 144 : fmt == FMT_Q5K ? 176 : fmt == FMT_Q6K ? 210 : 0;
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -580,7 +580,7 @@ __global__ __launch_bounds__(256) void unpack_kernel(int fmt, const uint8_t *pac
     const int b = ur >> 3, k0 = (ur & 7) * 32;
     const int kbase = b * QK + k0;
     if (kbase >= K) return;
-    const int BB = fmt == FMT_CB2 ? 38 : fmt == FMT_Q2K ? 84 : 144;
+    const int BB = block_bytes(fmt);
     const uint8_t *blk = packed + (r * nb + b) * BB;
     float v[32];
     const float d = f16_bits_to_f32(ld_u16(blk));
@@ -600,13 +600,21 @@ __global__ __launch_bounds__(256) void unpack_kernel(int fmt, const uint8_t *pac
             const int q = (blk[20 + (i >> 2)] >> (2 * (i & 3))) & 3;
             v[e] = (d * (float)(sm & 15)) * (float)q - dmin * (float)(sm >> 4);
         }
+    } else if (fmt == FMT_Q6K) {
+        for (int e = 0; e < 32; ++e) {
+            const int i = k0 + e;
+            const float mul = d * (float)(int8_t)blk[2 + (i >> 4)];
+            const int u = ((blk[18 + (i >> 1)] >> (4 * (i & 1))) & 15) | (((blk[146 + (i >> 2)] >> (2 * (i & 3))) & 3) << 4);
+            v[e] = mul * (float)(u - 32);
+        }
     } else {
         const float dmin = f16_bits_to_f32(ld_u16(blk + 2));
         const int j = k0 >> 5;
         const float mul = d * (float)q4k_field(blk, j), off = dmin * (float)q4k_field(blk, 8 + j);
         for (int e = 0; e < 32; ++e) {
             const int i = k0 + e;
-            const int q = (blk[16 + (i >> 1)] >> (4 * (i & 1))) & 15;
+            int q = (blk[16 + (i >> 1)] >> (4 * (i & 1))) & 15;
+            if (fmt == FMT_Q5K) q |= ((blk[144 + (i >> 3)] >> (i & 7)) & 1) << 4;
             v[e] = mul * (float)q - off;
         }
     }

@@ -105,6 +105,64 @@ void block_q4k(const float *x, uint8_t *o)
     for (int b = 0; b < 128; ++b) o[16 + b] = (uint8_t)(a.q[2 * b] | (a.q[2 * b + 1] << 4));
 }
 
+// Q5_K: the Q4_K block with 5-bit codes (8 x 32, codes 0..31, scales 0..63);
+// the low nibbles as in Q4_K, bit 4 of every code in a 32-byte bit plane.
+void block_q5k(const float *x, uint8_t *o)
+{
+    Affine a;
+    affine(x, 8, 32, 31, 63, a);
+    std::memset(o, 0, 176);
+    store_half(o, a.d);
+    store_half(o + 2, a.dmin);
+    uint64_t lo = 0, hi = 0;
+    for (int n = 0; n < 16; ++n) {
+        const uint64_t f = (uint64_t)(n < 8 ? a.sc[n] : a.m[n - 8]);
+        const int bit = 6 * n;
+        if (bit + 6 <= 64) lo |= f << bit;
+        else if (bit >= 64) hi |= f << (bit - 64);
+        else { lo |= f << bit; hi |= f >> (64 - bit); }
+    }
+    for (int b = 0; b < 8; ++b) o[4 + b] = (uint8_t)(lo >> (8 * b));
+    for (int b = 0; b < 4; ++b) o[12 + b] = (uint8_t)(hi >> (8 * b));
+    for (int b = 0; b < 128; ++b) o[16 + b] = (uint8_t)((a.q[2 * b] & 15) | ((a.q[2 * b + 1] & 15) << 4));
+    for (int b = 0; b < 32; ++b) {
+        uint8_t plane = 0;
+        for (int t = 0; t < 8; ++t) plane |= (uint8_t)(((a.q[8 * b + t] >> 4) & 1) << t);
+        o[144 + b] = plane;
+    }
+}
+
+// Q6_K: symmetric, 16 x 16, signed codes -32..31 stored as u = q + 32 (low
+// nibbles, then the high two bits four to a byte), int8 sub-block scales.
+void block_q6k(const float *x, uint8_t *o)
+{
+    float scale[16], top = 0.f;
+    for (int j = 0; j < 16; ++j) {
+        float amax = 0.f;
+        for (int i = 0; i < 16; ++i) amax = std::max(amax, std::fabs(x[16 * j + i]));
+        scale[j] = amax / 31.f;
+        top = std::max(top, scale[j]);
+    }
+    const uint16_t db = half_bits(top / 127.f);
+    const float d = half_value(db);
+    std::memset(o, 0, 210);
+    store_half(o, db);
+    uint8_t u[256];
+    for (int j = 0; j < 16; ++j) {
+        const int sc = d > 0.f ? rne_clamp(scale[j] / d, 127) : 0;
+        o[2 + j] = (uint8_t)sc;
+        const float step = d * (float)sc;
+        for (int i = 0; i < 16; ++i) {
+            const int q = step > 0.f ? std::min(std::max((int)std::nearbyint(x[16 * j + i] / step), -32), 31) : 0;
+            u[16 * j + i] = (uint8_t)(q + 32);
+        }
+    }
+    for (int b = 0; b < 128; ++b) o[18 + b] = (uint8_t)((u[2 * b] & 15) | ((u[2 * b + 1] & 15) << 4));
+    for (int b = 0; b < 64; ++b)
+        o[146 + b] = (uint8_t)((u[4 * b] >> 4) | ((u[4 * b + 1] >> 4) << 2) | ((u[4 * b + 2] >> 4) << 4) |
+                               ((u[4 * b + 3] >> 4) << 6));
+}
+
 // CB2: nearest codeword in the integer metric.  With t the fixed-point target
 // and c a codeword, |t - 4096c|^2 = |t|^2 - 8192 (t.c - 2048 |c|^2), so the
 // argmin over c only needs v(c) = 2048 |c|^2 - t.c.  |t_i| <= 4.5*4096 and
@@ -174,14 +232,15 @@ void block_cb2(const float *x, const Codebook &C, uint8_t *o)
 extern "C" int q2_pack(int fmt, const float *w_host, int64_t rows, int K, const int8_t *codebook_host, void *out_host)
 {
     using moe::set_error;
-    if (fmt != MOE_FMT_CB2 && fmt != MOE_FMT_Q2K && fmt != MOE_FMT_Q4K)
-        return set_error(MOE_ERR_INVALID_ARG, "q2_pack: fmt=%d is not CB2, Q2K or Q4K", fmt);
+    if (fmt != MOE_FMT_CB2 && fmt != MOE_FMT_Q2K && fmt != MOE_FMT_Q4K && fmt != MOE_FMT_Q5K && fmt != MOE_FMT_Q6K)
+        return set_error(MOE_ERR_INVALID_ARG, "q2_pack: fmt=%d is not CB2, Q2K, Q4K, Q5K or Q6K", fmt);
     if (rows < 0 || K < 1) return set_error(MOE_ERR_INVALID_ARG, "q2_pack: rows=%lld K=%d", (long long)rows, K);
     if (rows == 0) return MOE_OK;
     if (!w_host || !out_host) return set_error(MOE_ERR_INVALID_ARG, "q2_pack: NULL input or output");
     if (fmt == MOE_FMT_CB2 && !codebook_host) return set_error(MOE_ERR_INVALID_ARG, "q2_pack: CB2 needs a codebook");
     const int nb = (K + 255) / 256;
-    const int bb = fmt == MOE_FMT_CB2 ? 38 : fmt == MOE_FMT_Q2K ? 84 : 144;
+    const int bb = fmt == MOE_FMT_CB2 ? 38 : fmt == MOE_FMT_Q2K ? 84 : fmt == MOE_FMT_Q4K ? 144
+                 : fmt == MOE_FMT_Q5K ? 176 : 210;
     Codebook *cbp = fmt == MOE_FMT_CB2 ? new Codebook(codebook_host) : nullptr;
     auto work = [&](int64_t r0, int64_t r1) {
         std::vector<float> row((size_t)nb * 256);
@@ -193,7 +252,9 @@ extern "C" int q2_pack(int fmt, const float *w_host, int64_t rows, int K, const 
                 const float *x = row.data() + 256 * b;
                 if (fmt == MOE_FMT_CB2) block_cb2(x, *cbp, o + (int64_t)b * bb);
                 else if (fmt == MOE_FMT_Q2K) block_q2k(x, o + (int64_t)b * bb);
-                else block_q4k(x, o + (int64_t)b * bb);
+                else if (fmt == MOE_FMT_Q4K) block_q4k(x, o + (int64_t)b * bb);
+                else if (fmt == MOE_FMT_Q5K) block_q5k(x, o + (int64_t)b * bb);
+                else block_q6k(x, o + (int64_t)b * bb);
             }
         }
     };

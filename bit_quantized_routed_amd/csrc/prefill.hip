@@ -147,12 +147,19 @@ __device__ __forceinline__ void np_build_table(const FfnPass &p, uint32_t *tab)
 struct RawCB2 { uint32_t d, sc, ix; };               // d, scale byte pair, 4 indices
 struct RawQ2K { uint32_t dd, scw, c0, c1; };         // d|dmin, 4 scale bytes, 16 codes
 struct RawQ4K { uint32_t dd, s0, s1, s2; u32x4 c; }; // d|dmin, 12 scale bytes, 32 codes
+struct RawQ5K { uint32_t dd, s0, s1, s2; u32x4 c; uint32_t hb; };  // + bit 4 of the 32 codes
+struct RawQ6K { uint32_t dd, sc2; u32x4 c; uint2 hb; };            // d, 2 int8 scales, 32 low nibbles, high bits
 struct RawBF16 { uint32_t unused; };                 // bf16 streams per MFMA step
 
 template <int FMT> struct RawOf;
 template <> struct RawOf<FMT_CB2> { using T = RawCB2; };
 template <> struct RawOf<FMT_Q2K> { using T = RawQ2K; };
 template <> struct RawOf<FMT_Q4K> { using T = RawQ4K; };
+template <> struct RawOf<FMT_Q5K> { using T = RawQ5K; };
+template <> struct RawOf<FMT_Q6K> { using T = RawQ6K; };
+
+// the formats staged half a block at a time (one lane: 32 weights of its row)
+template <int FMT> constexpr bool half_staged() { return FMT == FMT_Q4K || FMT == FMT_Q5K || FMT == FMT_Q6K; }
 template <> struct RawOf<FMT_BF16> { using T = RawBF16; };
 
 __device__ __forceinline__ uint32_t ld_u32_unaligned(const uint8_t *p)
@@ -179,18 +186,26 @@ __device__ __forceinline__ void raw_load(const uint8_t *row, int hs, int fc, typ
         const uint2 c = *(const uint2 *)(blk + 20 + 16 * fc + 8 * h);
         r.c0 = c.x;
         r.c1 = c.y;
-    } else if constexpr (FMT == FMT_Q4K) {
-        const uint8_t *blk = row + (int64_t)b * 144;
+    } else if constexpr (FMT == FMT_Q4K || FMT == FMT_Q5K) {
+        const uint8_t *blk = row + (int64_t)b * (FMT == FMT_Q4K ? 144 : 176);
         r.dd = *(const uint32_t *)blk;
         r.s0 = *(const uint32_t *)(blk + 4);
         r.s1 = *(const uint32_t *)(blk + 8);
         r.s2 = *(const uint32_t *)(blk + 12);
         r.c = *(const u32x4 *)(blk + 16 + 32 * fc + 16 * h);
+        if constexpr (FMT == FMT_Q5K) r.hb = *(const uint32_t *)(blk + 144 + 8 * fc + 4 * h);
+    } else if constexpr (FMT == FMT_Q6K) {
+        // 210-byte blocks start 2-byte aligned: every field is read unaligned
+        const uint8_t *blk = row + (int64_t)b * 210;
+        r.dd = ld_u16(blk);
+        r.sc2 = ld_u16(blk + 2 + 4 * fc + 2 * h);
+        __builtin_memcpy(&r.c, blk + 18 + 32 * fc + 16 * h, 16);
+        __builtin_memcpy(&r.hb, blk + 146 + 16 * fc + 8 * h, 8);
     }
 }
 
 // Per-half-block dequantization state of one lane and fragment.
-struct Pool { uint32_t lo[2], hi[2], mv[2]; float mul, off; };
+struct Pool { uint32_t lo[2], hi[2], mv[2]; float mul, off, mul1; };
 
 // DEC (decode): exact integer codes -- CB2 {+-s, +-3s}, Q2_K {0, sc, 2sc, 3sc}
 // and the sub-block min m as a separate operand -- whose block scales d
@@ -214,7 +229,14 @@ __device__ __forceinline__ void pool_prep(const typename RawOf<FMT>::T &r, int h
             P.lo[u] = pk_bf16(-off, mul - off);
             P.hi[u] = pk_bf16(2.0f * mul - off, 3.0f * mul - off);
         }
-    } else if constexpr (FMT == FMT_Q4K) {
+    } else if constexpr (FMT == FMT_Q6K) {
+        // sub-blocks 4 fc + 2 h + u (u = 0: MFMA steps 0, 1; u = 1: steps 2, 3),
+        // signed scales; no min term
+        const float s0 = (float)(int8_t)(r.sc2 & 0xffu), s1 = (float)(int8_t)(r.sc2 >> 8);
+        const float d = DEC ? 1.0f : f16_bits_to_f32(r.dd & 0xffffu);
+        P.mul = d * s0;                             // exact (11 x 7 bits)
+        P.mul1 = d * s1;
+    } else if constexpr (FMT == FMT_Q4K || FMT == FMT_Q5K) {
         // sub-block 2 fc + h; 6-bit fields sc_0..7, m_0..7 in a 96-bit stream
         const int j = 2 * fc + h;
         const uint64_t lo64 = (uint64_t)r.s0 | ((uint64_t)r.s1 << 32);
@@ -235,16 +257,56 @@ __device__ __forceinline__ void pool_prep(const typename RawOf<FMT>::T &r, int h
     }
 }
 
-// Q4_K decode operands of MFMA step s4: sc * q (integers up to 63 * 15 = 945)
-// as hi = bf16(sc * q) plus lo = sc * q - hi (an integer of magnitude <= 2),
-// both exact, so the two MFMAs sum the exact products.
-__device__ __forceinline__ void bfrag_q4k_dec(const RawQ4K &r, const Pool &P, int s4, uint32_t hi[4], uint32_t lo[4])
+// The 8 codes of MFMA step s4 (weights 8 s4 .. 8 s4 + 7 of the lane's half
+// block) as exact floats, element 2i and 2i + 1 in v[i][0], v[i][1]; the
+// multiplier that applies to them (Q6_K: its sub-block's).
+template <int FMT>
+__device__ __forceinline__ float step_codes(const typename RawOf<FMT>::T &r, const Pool &P, int s4, float v[4][2])
 {
     const uint32_t cw = r.c[s4];
     const uint32_t cl = cw & 0x0f0f0f0fu, ch = (cw >> 4) & 0x0f0f0f0fu;
+    if constexpr (FMT == FMT_Q4K) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { v[i][0] = ubyte(cl, i); v[i][1] = ubyte(ch, i); }
+        return P.mul;
+    } else if constexpr (FMT == FMT_Q5K) {
+        // bit 4 of weight 8 s4 + e is bit 8 s4 + e of the half-block's plane
+        const uint32_t hb = r.hb >> (8 * s4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i][0] = ubyte(cl, i) + (float)(((hb >> (2 * i)) & 1u) << 4);
+            v[i][1] = ubyte(ch, i) + (float)(((hb >> (2 * i + 1)) & 1u) << 4);
+        }
+        return P.mul;
+    } else {
+        // Q6_K: u = nibble | (two high bits << 4), q = u - 32; the high bits of
+        // weight 8 s4 + e sit at bits 2 e of the half-block's 16-bit group s4
+        const uint32_t hw = s4 < 2 ? r.hb.x : r.hb.y;
+        const uint32_t hg = hw >> (16 * (s4 & 1));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[i][0] = (float)((int)(((cl >> (8 * i)) & 15u) | (((hg >> (4 * i)) & 3u) << 4)) - 32);
+            v[i][1] = (float)((int)(((ch >> (8 * i)) & 15u) | (((hg >> (4 * i + 2)) & 3u) << 4)) - 32);
+        }
+        return s4 < 2 ? P.mul : P.mul1;
+    }
+}
+
+// Q4_K decode operands of MFMA step s4: sc * q (integers up to 63 * 15 = 945)
+// as hi = bf16(sc * q) plus lo = sc * q - hi (an integer of magnitude <= 2),
+// both exact, so the two MFMAs sum the exact products.
+// Q5_K: sc * q up to 63 * 31 = 1953, Q6_K: |sc * q| up to 128 * 32 = 4096;
+// the same split holds (the remainder of rounding an integer of at most 13
+// significant bits to bf16 has at most 5, so it is exact in bf16).
+template <int FMT>
+__device__ __forceinline__ void bfrag_split_dec(const typename RawOf<FMT>::T &r, const Pool &P, int s4, uint32_t hi[4],
+                                                uint32_t lo[4])
+{
+    float q[4][2];
+    const float mul = step_codes<FMT>(r, P, s4, q);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float v0 = P.mul * ubyte(cl, i), v1 = P.mul * ubyte(ch, i);
+        const float v0 = mul * q[i][0], v1 = mul * q[i][1];
         hi[i] = pk_bf16(v0, v1);
         lo[i] = pk_bf16(v0 - __uint_as_float(hi[i] << 16), v1 - __uint_as_float(hi[i] & 0xffff0000u));
     }
@@ -278,6 +340,15 @@ __device__ __forceinline__ void bfrag(const typename RawOf<FMT>::T &r, const Poo
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             out[i] = pk_bf16(__builtin_fmaf(P.mul, ubyte(lo, i), -P.off), __builtin_fmaf(P.mul, ubyte(hi, i), -P.off));
+    } else if constexpr (FMT == FMT_Q5K || FMT == FMT_Q6K) {
+        // the exact fp32 value (Q6_K: the product of exact factors, no min
+        // term), rounded to bf16
+        float q[4][2];
+        const float mul = step_codes<FMT>(r, P, s4, q);
+        const float off = FMT == FMT_Q5K ? P.off : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            out[i] = pk_bf16(__builtin_fmaf(mul, q[i][0], -off), __builtin_fmaf(mul, q[i][1], -off));
     }
 }
 
@@ -525,8 +596,10 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
     // DEC with packed weights: each block's sums (P1: codes, P2: Q2_K min
     // operand) are scaled by the block's d (and dmin) into acc
     constexpr bool PBLK = DEC && FMT != FMT_BF16;
-    constexpr bool PMIN = DEC && (FMT == FMT_Q2K || FMT == FMT_Q4K);
-    constexpr bool Q4D = DEC && FMT == FMT_Q4K;     // two exact B terms per step
+    constexpr bool HALF = half_staged<FMT>();
+    using RawH = typename RawOf<HALF ? FMT : FMT_Q4K>::T;
+    constexpr bool PMIN = DEC && (FMT == FMT_Q2K || FMT == FMT_Q4K || FMT == FMT_Q5K);
+    constexpr bool Q4D = DEC && HALF;               // two exact B terms per step
     f32x4 acc[NMF][4], P1[PBLK ? NMF : 1][4], P2[PMIN ? NMF : 1][4];
 #pragma unroll
     for (int mf = 0; mf < NMF; ++mf)
@@ -538,7 +611,7 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
         for (int nf = 0; nf < 4; ++nf) P1[mf][nf] = P2[mf][nf] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     Blk blk[2][4];                                   // CB2/Q2_K: [block parity][fragment]
-    RawQ4K r4[2][4];                                 // Q4_K: [half parity][fragment]
+    RawH r4[2][4];                                   // Q4_K/Q5_K/Q6_K: [half parity][fragment]
     u32x4 bw[4][4];                                  // bf16: [step mod 4][fragment]
     const int nks = 8 * nb;
     auto bw_load = [&](int ks) {
@@ -553,9 +626,9 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
             blk_load<FMT>(wrow(nf), 0, 0, fc, blk[0][nf]);
             blk_load<FMT>(wrow(nf), 0, 1, fc, blk[0][nf]);
         }
-    } else if constexpr (FMT == FMT_Q4K) {
+    } else if constexpr (HALF) {
 #pragma unroll
-        for (int nf = 0; nf < 4; ++nf) raw_load<FMT_Q4K>(wrow(nf), 0, fc, r4[0][nf]);
+        for (int nf = 0; nf < 4; ++nf) raw_load<FMT>(wrow(nf), 0, fc, r4[0][nf]);
     } else {
         bw_load(0);
         bw_load(1);
@@ -577,17 +650,17 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
                 if constexpr (BLK) {
 #pragma unroll
                     for (int nf = 0; nf < 4; ++nf) blk_load<FMT>(wrow(nf), min(bb + 1, nb - 1), h, fc, blk[q ^ 1][nf]);
-                } else if constexpr (FMT == FMT_Q4K) {
+                } else if constexpr (HALF) {
 #pragma unroll
-                    for (int nf = 0; nf < 4; ++nf) raw_load<FMT_Q4K>(wrow(nf), min(hs + 1, nhs - 1), fc, r4[h ^ 1][nf]);
+                    for (int nf = 0; nf < 4; ++nf) raw_load<FMT>(wrow(nf), min(hs + 1, nhs - 1), fc, r4[h ^ 1][nf]);
                 }
                 Pool P[4];
                 if constexpr (FMT == FMT_CB2) {
 #pragma unroll
                     for (int nf = 0; nf < 4; ++nf) blk_pool<FMT, DEC>(blk[q][nf], h, fc, P[nf]);
-                } else if constexpr (FMT == FMT_Q4K) {
+                } else if constexpr (HALF) {
 #pragma unroll
-                    for (int nf = 0; nf < 4; ++nf) pool_prep<FMT_Q4K, DEC>(r4[h][nf], h, fc, P[nf]);
+                    for (int nf = 0; nf < 4; ++nf) pool_prep<FMT, DEC>(r4[h][nf], h, fc, P[nf]);
                 }
                 const uint8_t *ab = As + h * NP_ABUF, *abl = As + (NP_NBUF + h) * NP_ABUF;
 #pragma unroll
@@ -610,7 +683,7 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
 #pragma unroll
                         for (int nf = 0; nf < 4; ++nf) {
                             uint32_t oh[4], ol[4];
-                            bfrag_q4k_dec(r4[h][nf], P[nf], s4, oh, ol);
+                            bfrag_split_dec<FMT>(r4[h][nf], P[nf], s4, oh, ol);
                             bq[nf] = __builtin_bit_cast(bf16x8, u32x4{oh[0], oh[1], oh[2], oh[3]});
                             bql[nf] = __builtin_bit_cast(bf16x8, u32x4{ol[0], ol[1], ol[2], ol[3]});
                         }
@@ -624,7 +697,7 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
                         for (int nf = 0; nf < 4; ++nf) {
                             uint32_t o[4];
                             if constexpr (BLK) blk_frag<FMT>(blk[q][nf], P[nf], h, s4, tab, copy, o);
-                            else bfrag<FMT_Q4K>(r4[h][nf], P[nf], s4, tab, copy, o);
+                            else bfrag<HALF ? FMT : FMT_Q4K>(r4[h][nf], P[nf], s4, tab, copy, o);
                             bq[nf] = __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
                         }
                     }
@@ -658,7 +731,8 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
                         for (int nf = 0; nf < 4; ++nf) {
                             float d, dmin = 0.f;
                             if constexpr (FMT == FMT_CB2) d = f16_bits_to_f32(blk[q][nf].d);
-                            else if constexpr (FMT == FMT_Q4K) {
+                            else if constexpr (FMT == FMT_Q6K) d = f16_bits_to_f32(r4[h][nf].dd & 0xffffu);
+                            else if constexpr (HALF) {
                                 d = f16_bits_to_f32(r4[h][nf].dd & 0xffffu);
                                 dmin = f16_bits_to_f32(r4[h][nf].dd >> 16);
                             } else {
@@ -994,11 +1068,19 @@ hipError_t launch_np_prefill(const FfnPass &p, bool gateup, hipStream_t s)
 {
     if (!np_prefill_ok(p) || p.out_f32 == gateup) return hipErrorInvalidValue;
     if (gateup) {
-        if (p.fmt == FMT_CB2) return np_launch<FMT_CB2, true, false, false>(p, s);
-        if (p.fmt == FMT_Q4K) return np_launch<FMT_Q4K, true, false, false>(p, s);
+        switch (p.fmt) {
+        case FMT_CB2: return np_launch<FMT_CB2, true, false, false>(p, s);
+        case FMT_Q2K: return np_launch<FMT_Q2K, true, false, false>(p, s);
+        case FMT_Q4K: return np_launch<FMT_Q4K, true, false, false>(p, s);
+        case FMT_Q5K: return np_launch<FMT_Q5K, true, false, false>(p, s);
+        }
     } else {
-        if (p.fmt == FMT_Q2K) return np_launch<FMT_Q2K, false, false, false>(p, s);
-        if (p.fmt == FMT_Q4K) return np_launch<FMT_Q4K, false, false, false>(p, s);
+        switch (p.fmt) {
+        case FMT_Q2K: return np_launch<FMT_Q2K, false, false, false>(p, s);
+        case FMT_Q4K: return np_launch<FMT_Q4K, false, false, false>(p, s);
+        case FMT_Q5K: return np_launch<FMT_Q5K, false, false, false>(p, s);
+        case FMT_Q6K: return np_launch<FMT_Q6K, false, false, false>(p, s);
+        }
     }
     return hipErrorInvalidValue;
 }
@@ -1007,22 +1089,38 @@ bool np_decode_ok(const FfnPass &p)
 {
     if (p.K % (2 * QK) || p.K < 2 * QK) return false;
     if (p.Nsh > 0 && (p.Ksh % (2 * QK) || p.Ksh < 2 * QK)) return false;
-    return p.out_f32 && (p.fmt == FMT_CB2 || p.fmt == FMT_Q2K || p.fmt == FMT_Q4K);
+    return p.out_f32 && (p.fmt == FMT_CB2 || p.fmt == FMT_Q2K || p.fmt == FMT_Q4K || p.fmt == FMT_Q5K ||
+                         p.fmt == FMT_Q6K);
+}
+
+// gate/up takes x (bf16, or fp32 as two bf16 terms); down takes the fp32 h
+template <int FMT>
+hipError_t np_decode_fmt(const FfnPass &p, bool gateup, hipStream_t s)
+{
+    if (gateup) {
+        if constexpr (FMT == FMT_Q6K) return hipErrorInvalidValue;
+        else {
+            if (p.act_f32) return np_launch<FMT, true, true, true>(p, s);
+            return np_launch<FMT, true, true, false>(p, s);
+        }
+    }
+    if constexpr (FMT == FMT_CB2) return hipErrorInvalidValue;
+    else {
+        if (!p.act_f32) return hipErrorInvalidValue;
+        return np_launch<FMT, false, true, true>(p, s);
+    }
 }
 
 hipError_t launch_np_decode(const FfnPass &p, bool gateup, hipStream_t s)
 {
     if (!np_decode_ok(p)) return hipErrorInvalidValue;
-    if (gateup && p.fmt == FMT_CB2) {
-        if (p.act_f32) return np_launch<FMT_CB2, true, true, true>(p, s);
-        return np_launch<FMT_CB2, true, true, false>(p, s);
+    switch (p.fmt) {
+    case FMT_CB2: return np_decode_fmt<FMT_CB2>(p, gateup, s);
+    case FMT_Q2K: return np_decode_fmt<FMT_Q2K>(p, gateup, s);
+    case FMT_Q4K: return np_decode_fmt<FMT_Q4K>(p, gateup, s);
+    case FMT_Q5K: return np_decode_fmt<FMT_Q5K>(p, gateup, s);
+    case FMT_Q6K: return np_decode_fmt<FMT_Q6K>(p, gateup, s);
     }
-    if (gateup && p.fmt == FMT_Q4K) {
-        if (p.act_f32) return np_launch<FMT_Q4K, true, true, true>(p, s);
-        return np_launch<FMT_Q4K, true, true, false>(p, s);
-    }
-    if (!gateup && p.fmt == FMT_Q2K && p.act_f32) return np_launch<FMT_Q2K, false, true, true>(p, s);
-    if (!gateup && p.fmt == FMT_Q4K && p.act_f32) return np_launch<FMT_Q4K, false, true, true>(p, s);
     return hipErrorInvalidValue;
 }
 

@@ -78,11 +78,22 @@ enum moe_status {
  *   fields at bits 6n..6n+5 of one little-endian 96-bit stream (n<8: sc_n,
  *   n>=8: m_{n-8}) | [16:144) 4-bit q_i in bits 4*(i%2) of byte i/2.
  *   w_i = d*sc_j*q_i - dmin*m_j, j = i/32.
+ * MOE_FMT_Q5K 176 B/block: Q4_K with 5-bit codes: [0:16) as Q4_K |
+ *   [16:144) the low 4 bits of q_i in bits 4*(i%2) of byte 16+i/2 |
+ *   [144:176) bit 4 of q_i in bit i%8 of byte 144+i/8.
+ *   w_i = d*sc_j*q_i - dmin*m_j, j = i/32.
+ * MOE_FMT_Q6K 210 B/block: [0:2) fp16 d | [2:18) sixteen int8 scales sc_j
+ *   (16 sub-blocks of 16) | [18:146) the low 4 bits of u_i = q_i + 32 in
+ *   bits 4*(i%2) of byte 18+i/2 | [146:210) the high 2 bits of u_i in bits
+ *   2*(i%4) of byte 146+i/4.  w_i = d*sc_j*q_i, q_i in -32..31, j = i/16.
+ *   (Q5_K and Q6_K are among the routed layouts the "ds4" README mirror lists
+ *   for other models' files, section on model weights.)
  * MOE_FMT_BF16 plain row-major bf16 (the shared expert), no blocks.
  *
- * Every dequantized value is exact in fp32 (products need at most 21
+ * Every dequantized value is exact in fp32 (products need at most 24
  * significant bits; the min term is subtracted with one rounding). */
-enum moe_format { MOE_FMT_CB2 = 1, MOE_FMT_Q2K = 2, MOE_FMT_Q4K = 3, MOE_FMT_BF16 = 4 };
+enum moe_format { MOE_FMT_CB2 = 1, MOE_FMT_Q2K = 2, MOE_FMT_Q4K = 3, MOE_FMT_BF16 = 4, MOE_FMT_Q5K = 5,
+                  MOE_FMT_Q6K = 6 };
 
 /* activation element type of x */
 enum moe_act { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 };
@@ -94,7 +105,10 @@ enum moe_path { MOE_PATH_ROUTE = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 };
  * it is device memory.
  *   hidden (H), inter (I), n_experts (E), top_k (k): 1 <= k <= E <= 1024,
  *     H % 8 == 0, I % 8 == 0.
- *   fmt_gate_up: MOE_FMT_CB2 or MOE_FMT_Q4K; fmt_down: MOE_FMT_Q2K or MOE_FMT_Q4K.
+ *   fmt_gate_up: MOE_FMT_CB2, Q2K, Q4K or Q5K; fmt_down: MOE_FMT_Q2K, Q4K, Q5K
+ *     or Q6K.  (CB2 or Q4K gate/up with Q2K or Q4K down run on any shape; the
+ *     other pairs need hidden, inter and sh_inter multiples of 512, else the
+ *     FFN calls return MOE_ERR_UNSUPPORTED.)
  *   w_gate, w_up: [E][I rows][ceil(H/256) blocks]; w_down: [E][H rows][ceil(I/256)
  *     blocks]; experts stored back to back with no gaps.
  *   codebook: int8 [256][8] (CB2 only, else may be NULL).
@@ -161,10 +175,11 @@ int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bi
  *   products; fp32 block rescale), activations exact (bf16) or split into two
  *   bf16 terms (fp32), fp32 accumulation, intermediate h in fp32
  *   (single-token path: h held as two bf16 terms).  Relative L2 error against
- *   an exact evaluation is far below 1e-4.  Formats: CB2 or Q4K gate/up, Q2K
- *   or Q4K down, BF16 shared; Q4K needs hidden, inter and sh_inter multiples of
- *   512 (MOE_ERR_UNSUPPORTED otherwise; Q4K codes enter as sc*q split exactly
- *   into two bf16 terms).  Launches: for T <= 4 (with H % 512 == 0,
+ *   an exact evaluation is far below 1e-4.  Formats: every pair the layer
+ *   struct allows; anything but CB2 gate/up with Q2K down needs hidden, inter
+ *   and sh_inter multiples of 512 (MOE_ERR_UNSUPPORTED otherwise; Q4K/Q5K/Q6K
+ *   codes enter as sc*q split exactly into two bf16 terms).  Launches: for
+ *   T <= 4 with CB2 gate/up and Q2K down (and H % 512 == 0,
  *   H <= 8192, I % 256 == 0, I <= 2048, sh_inter % 512 == 0, k <= 64) per
  *   token, in order: gate/up, then (k <= 8, sh_inter <= 2048) h+SwiGLU and
  *   one down launch that writes y, else down (SwiGLU as it forms h) and
@@ -173,7 +188,8 @@ int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bi
  * moe_expert_ffn_prefill -- bf16 MFMA path for any T: x must be bf16;
  *   dequantized weights rounded to bf16 (RNE) in LDS; fp32 accumulation;
  *   h rounded to bf16; down output and combine in fp32.  Relative L2 error
- *   below 5e-3.  Formats: CB2/Q4K gate/up, Q2K/Q4K down, BF16 shared.
+ *   below 5e-3.  Formats: every pair the layer struct allows (see there for
+ *   the shapes each needs), BF16 shared.
  *   Launches: schedule, gate/up+SwiGLU, down, combine. */
 int moe_expert_ffn_decode(const moe_layer *L, const void *x, int act, int T,
                           const int32_t *topk_idx, const float *topk_w, const int32_t *offsets,

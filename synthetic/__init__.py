@@ -39,7 +39,7 @@ _TAG_ROUTER = 5
 _TAG_CODEBOOK = 6
 _TAG_TOKENS = 7
 
-FMT_CB2, FMT_Q2K, FMT_Q4K, FMT_BF16 = 1, 2, 3, 4
+FMT_CB2, FMT_Q2K, FMT_Q4K, FMT_BF16, FMT_Q5K, FMT_Q6K = 1, 2, 3, 4, 5, 6
 
 _BIG = dict(hidden=7168, inter=2048, n_experts=256, top_k=8, sh_inter=2048)
 
@@ -63,6 +63,28 @@ CONFIGS = {
 
 _GOLDEN = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                        "tests", "golden")
+
+
+# Per-layer quantization recipes: (gate/up format, down format) of layer l of
+# an n-layer stack.  "q2" is the pages' 2-bit recipe for every layer; "q2-q4"
+# keeps the last 6 layers in Q4_K ("DwarfStar" README and "ds4" README
+# mirror, section on model weights: q2 with the last six layers in q4; a stack
+# shorter than 12 layers keeps its last half in Q4_K); "q4" is Q4_K throughout;
+# "q5-q6" is the wider routed mix the "ds4" mirror lists for other models
+# (gate/up Q5_K, down Q6_K).
+RECIPES = ("q2", "q2-q4", "q4", "q5-q6")
+
+
+def layer_formats(recipe: str, layer: int, n_layers: int) -> tuple:
+    if recipe == "q2":
+        return FMT_CB2, FMT_Q2K
+    if recipe == "q2-q4":
+        return (FMT_Q4K, FMT_Q4K) if layer >= n_layers - min(6, n_layers // 2) else (FMT_CB2, FMT_Q2K)
+    if recipe == "q4":
+        return FMT_Q4K, FMT_Q4K
+    if recipe == "q5-q6":
+        return FMT_Q5K, FMT_Q6K
+    raise ValueError("unknown recipe %r" % recipe)
 
 
 def config(name: str, **override) -> dict:

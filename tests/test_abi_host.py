@@ -74,7 +74,8 @@ def test_route_validation_misc():
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(fmt_gate_up=2), -1), (dict(fmt_down=1), -1), (dict(inter=100), -1), (dict(w_down=None), -1),
+    (dict(fmt_gate_up=6), -1), (dict(fmt_gate_up=4), -1), (dict(fmt_down=1), -1), (dict(fmt_down=7), -1),
+    (dict(inter=100), -1), (dict(w_down=None), -1),
     (dict(codebook=None), -1), (dict(sh_inter=128, sh_gate=FAKE, sh_up=FAKE, sh_down=FAKE), -1),
     (dict(sh_inter=256), -1), (dict(sh_inter=-1), -1)])
 def test_ffn_validation(kw, code):
@@ -87,6 +88,9 @@ def test_ffn_validation_misc():
     L = _layer()
     assert _ffn(pre, L, act=0) == -1                           # prefill needs bf16 activations
     assert _ffn(dec, _layer(fmt_gate_up=3, fmt_down=3)) == -2  # decode: Q4K needs K multiples of 512
+    for fg, fd in ((2, 2), (5, 6), (1, 6), (3, 5)):           # pairs that run on the 512-multiple GEMMs only
+        assert _ffn(pre, _layer(fmt_gate_up=fg, fmt_down=fd)) == -2
+        assert _ffn(dec, _layer(fmt_gate_up=fg, fmt_down=fd)) == -2
     assert _ffn(dec, L, ws_bytes=100) == -3
     assert _ffn(pre, L, ws_bytes=100) == -3
     assert _ffn(dec, L, T=-2) == -1
@@ -141,6 +145,8 @@ def test_sizes():
     assert M.q2_packed_bytes(1, 2048, 7168) == F.packed_bytes(F.CB2, 2048, 7168)
     assert M.q2_packed_bytes(2, 7168, 2048) == F.packed_bytes(F.Q2K, 7168, 2048)
     assert M.q2_packed_bytes(3, 7, 300) == F.packed_bytes(F.Q4K, 7, 300)
+    assert M.q2_packed_bytes(5, 7168, 2048) == F.packed_bytes(F.Q5K, 7168, 2048)
+    assert M.q2_packed_bytes(6, 33, 700) == F.packed_bytes(F.Q6K, 33, 700)
     assert M.q2_packed_bytes(4, 7, 300) == 0
     L = _layer()
     for path in (0, 1, 2):
@@ -151,7 +157,7 @@ def test_sizes():
         "ok", "invalid argument", "unsupported", "workspace too small", "HIP error"]
 
 
-@pytest.mark.parametrize("fmt", [F.CB2, F.Q2K, F.Q4K])
+@pytest.mark.parametrize("fmt", [F.CB2, F.Q2K, F.Q4K, F.Q5K, F.Q6K])
 @pytest.mark.parametrize("shape", [(1, 256), (7, 100), (33, 384), (5, 1000)])
 def test_pack_matches_oracle_bytes(fmt, shape):
     rng = np.random.default_rng(hash((fmt, shape)) % 2**32)
@@ -161,7 +167,8 @@ def test_pack_matches_oracle_bytes(fmt, shape):
 
 def test_pack_matches_oracle_on_workload_rows():
     cfg = S.config("decode1")
-    for which, fmt in (("gate", F.CB2), ("down", F.Q2K), ("down", F.Q4K), ("up", F.Q4K)):
+    for which, fmt in (("gate", F.CB2), ("down", F.Q2K), ("down", F.Q4K), ("up", F.Q4K), ("up", F.Q5K),
+                       ("down", F.Q6K), ("gate", F.Q2K)):
         w = S.expert_weight(cfg, which, 17)[:96]
         assert np.array_equal(M.q2_pack(fmt, w, CB), F.pack(fmt, w, CB)), which
 
@@ -174,7 +181,7 @@ def test_pack_edge_values():
     rows[3] = np.abs(np.linspace(0.01, 0.3, 256, dtype=np.float32))
     rows[4, 7] = 30.0
     rows[5] = np.tile(np.array([1e-6, -2e-6], np.float32), 128)
-    for fmt in (F.CB2, F.Q2K, F.Q4K):
+    for fmt in (F.CB2, F.Q2K, F.Q4K, F.Q5K, F.Q6K):
         assert np.array_equal(M.q2_pack(fmt, rows, CB), F.pack(fmt, rows, CB)), fmt
 
 

@@ -40,7 +40,7 @@ def _gpu():
 
 
 # ------------------------------------------------------------------ unpack
-@pytest.mark.parametrize("fmt", [F.CB2, F.Q2K, F.Q4K])
+@pytest.mark.parametrize("fmt", [F.CB2, F.Q2K, F.Q4K, F.Q5K, F.Q6K])
 @pytest.mark.parametrize("rows,K", [(1, 256), (5, 100), (19, 640), (64, 7168), (64, 2048)])
 def test_unpack_bit_exact(fmt, rows, K):
     rng = np.random.default_rng(rows * 1000 + K + fmt)
@@ -240,7 +240,7 @@ def test_decode_q4k_needs_512_multiples(small_cases):
     cfg = mid(8, 35, fmt_gate_up=S.FMT_Q4K, fmt_down=S.FMT_Q4K)     # inter 384
     wl = W.Workload(cfg)
     x, act, r = run_route(wl, cfg)
-    with pytest.raises(RuntimeError, match="unsupported|Q4K"):
+    with pytest.raises(RuntimeError, match="UNSUPPORTED"):
         run_ffn(wl, x, act, r, decode=True)
 
 
@@ -469,3 +469,80 @@ def test_route_nan_token_stays_a_permutation(T):
     ref, _, _ = R.route(xf, S.router_weight(cfg), k)
     keep = np.arange(T) != bad
     assert np.array_equal(idx[keep], ref[keep])
+
+
+# ------------------------------------------------------------------ format breadth
+# The wider routed layouts (Q5_K gate/up, Q5_K / Q6_K down, Q2_K gate/up) on
+# the in-register-dequant grouped GEMMs: every output element, prefill with
+# multi-tile experts, decode batched and single-token, fp32 and bf16 x.
+FMT_PAIRS = [(S.FMT_Q5K, S.FMT_Q6K), (S.FMT_Q2K, S.FMT_Q5K), (S.FMT_Q4K, S.FMT_Q6K), (S.FMT_CB2, S.FMT_Q6K),
+             (S.FMT_Q5K, S.FMT_Q5K)]
+PAIR_IDS = ["%s_%s" % ({1: "cb2", 2: "q2k", 3: "q4k", 5: "q5k"}[a], {2: "q2k", 3: "q4k", 5: "q5k", 6: "q6k"}[b])
+            for a, b in FMT_PAIRS]
+
+
+@pytest.mark.parametrize("fg,fd", FMT_PAIRS, ids=PAIR_IDS)
+def test_prefill_formats(small_cases, fg, fd):
+    name = "fmt_pre_%d_%d" % (fg, fd)
+    cfg = mid(400, 60 + 2 * fg + fd, skew=True, fmt_gate_up=fg, fmt_down=fd, **dict(GEMM, top_k=4))
+    wl, yref, routing = _case(small_cases, name, cfg)
+    x, act, r = run_route(wl, cfg)
+    check_route(r, *routing)
+    y = run_ffn(wl, x, act, r, decode=False)
+    err = rel_l2(y, yref)
+    print("[prefill] %s rel_l2=%.3e" % (name, err))
+    assert err <= PRE_TOL
+
+
+@pytest.mark.parametrize("T,xdt", [(1, "bf16"), (3, "f32"), (45, "bf16"), (70, "f32")])
+@pytest.mark.parametrize("fg,fd", FMT_PAIRS, ids=PAIR_IDS)
+def test_decode_formats(small_cases, fg, fd, T, xdt):
+    name = "fmt_dec_%d_%d_%d_%s" % (fg, fd, T, xdt)
+    cfg = mid(T, 70 + 2 * fg + fd, skew=True, x_dtype=xdt, fmt_gate_up=fg, fmt_down=fd, **GEMM)
+    wl, yref, routing = _case(small_cases, name, cfg)
+    x, act, r = run_route(wl, cfg)
+    check_route(r, *routing)
+    y = run_ffn(wl, x, act, r, decode=True)
+    err = rel_l2(y, yref)
+    print("[decode] %s rel_l2=%.3e" % (name, err))
+    assert err <= DEC_TOL
+
+
+@pytest.mark.parametrize("recipe", ["q2-q4", "q5-q6"])
+def test_layer_recipe_stack(recipe):
+    """A stack of four layers quantized by a per-layer recipe, each layer's fp32
+    output the next layer's input (decode path), every layer's output compared
+    with the oracle's own chain.  Each layer is its own seeded layer."""
+    n, T = 4, 12
+    base = mid(T, 80, x_dtype="bf16", **GEMM)
+    x_dev, act = None, None
+    x_ref = S.bf16_to_f32(S.tokens(base)[0])
+    for l in range(n):
+        fg, fd = S.layer_formats(recipe, l, n)
+        cfg = dict(base, seed=1000 + l, fmt_gate_up=fg, fmt_down=fd, x_dtype="bf16" if l == 0 else "f32")
+        wl = W.Workload(cfg)
+        if l == 0:
+            x_dev, act = wl.tokens(cfg)
+        r = M.Routing(T, cfg["top_k"], cfg["n_experts"])
+        M.route(wl.layer, x_dev, act, T, None, r, wl.layer.workspace(T, M.PATH_ROUTE))
+        y = torch.empty((T, cfg["hidden"]), device="cuda")
+        M.ffn_decode(wl.layer, x_dev, act, T, r, y, wl.layer.workspace(T, M.PATH_DECODE))
+        torch.cuda.synchronize()
+        seed = cfg["seed"]
+        idx, w, _ = R.route(x_ref, S.router_weight(cfg, seed), cfg["top_k"])
+        ex = {}
+        cb = S.codebook(seed)
+        for e in np.unique(idx):
+            mats = []
+            for which, fmt, rows, K in (("gate", fg, cfg["inter"], cfg["hidden"]), ("up", fg, cfg["inter"], cfg["hidden"]),
+                                        ("down", fd, cfg["hidden"], cfg["inter"])):
+                mats.append(F.unpack(fmt, F.pack(fmt, S.expert_weight(cfg, which, int(e), seed), cb), rows, K, cb))
+            ex[int(e)] = tuple(mats)
+        sh = tuple(S.bf16_to_f32(S.shared_weight_bf16(cfg, nm, seed)) for nm in ("gate", "up", "down"))
+        yref = R.moe_layer(x_ref, idx, w, ex, sh)
+        got = y.cpu().numpy()
+        err = rel_l2(got, yref)
+        print("[recipe %s] layer %d formats %d/%d rel_l2=%.3e" % (recipe, l, fg, fd, err))
+        assert err <= DEC_TOL
+        x_dev, act = y, M.ACT_F32
+        x_ref = yref.astype(np.float32)
