@@ -40,7 +40,7 @@ def log(msg):
 
 
 # sources that define each timed kernel (plus the shared headers)
-_KERNEL_SOURCES = {"dec_": ["decode.hip", "decode.h"], "route_": ["route.hip"], "ffn_prefill_": ["prefill.hip", "ffn.hip"],
+_KERNEL_SOURCES = {"dec_": ["decode.hip", "decode.h", "route_dev.h"], "route_": ["route.hip", "route_dev.h"], "ffn_prefill_": ["prefill.hip", "ffn.hip"],
                    "ffn_schedule": ["ffn.hip"], "combine": ["ffn.hip"]}
 
 
@@ -131,8 +131,15 @@ def kernel_bytes(cfg, n_active, T, name):
     xb = 2 if cfg["x_dtype"] == "bf16" else 4
     rows = T * k + (T if sh else 0)
     if name == "dec_down_fused":
-        # every selected expert's down and the shared down, h in (fp32), y out
-        return n_active * M.q2_packed_bytes(cfg["fmt_down"], H, I) + sh * H * 2 + rows * I * 4 + T * H * 4
+        # every selected expert's down, h in (fp32), the shared down's partial rows and y out
+        return n_active * M.q2_packed_bytes(cfg["fmt_down"], H, I) + T * k * I * 4 + (sh // 512) * H * 4 + T * H * 4
+    if name == "dec_stage1":
+        # the shared gate/up and the router weights, x in, the shared K-part sums out
+        return 2 * sh * H * 2 + cfg["n_experts"] * H * 4 + T * H * xb + 8 * 2 * sh * 4
+    if name == "dec_stage2":
+        # every selected expert's gate/up and the shared down, the per-chunk sums out
+        return (n_active * 2 * M.q2_packed_bytes(cfg["fmt_gate_up"], I, H) + sh * H * 2 + T * H * xb
+                + (H // 1024) * k * 2 * I * 4 + (sh // 512) * H * 4)
     if name.endswith("gateup"):
         hb = 4 if "decode" in name else 2
         return n_active * 2 * M.q2_packed_bytes(cfg["fmt_gate_up"], I, H) + 2 * sh * H * 2 + T * H * xb + rows * I * hb
@@ -170,7 +177,9 @@ class Stepper:
         self.r = M.Routing(self.T, c["top_k"], c["n_experts"])
         self.y = torch.empty((self.T, c["hidden"]), device="cuda")
         self.ws_route = wl.layer.workspace(self.T, M.PATH_ROUTE)
-        self.ws_ffn = wl.layer.workspace(self.T, M.PATH_DECODE if decode else M.PATH_PREFILL)
+        # decode steps are one moe_layer_decode call (router and FFN; the
+        # single-token layer runs the router inside the FFN's launches)
+        self.ws_ffn = wl.layer.workspace(self.T, M.PATH_LAYER_DECODE if decode else M.PATH_PREFILL)
         self.stream = torch.cuda.current_stream()
         self.i = 0
 
@@ -178,9 +187,12 @@ class Stepper:
         M = self.M
         layer = self.wl.layers[self.i % len(self.wl.layers)]
         self.i += 1
+        if self.decode:
+            M.layer_decode(layer, self.x, self.act, self.T, self.bias, self.r, self.y, self.ws_ffn, self.stream,
+                           prof_ffn)
+            return
         M.route(layer, self.x, self.act, self.T, self.bias, self.r, self.ws_route, self.stream, prof_route)
-        f = M.ffn_decode if self.decode else M.ffn_prefill
-        f(layer, self.x, self.act, self.T, self.r, self.y, self.ws_ffn, self.stream, prof_ffn)
+        M.ffn_prefill(layer, self.x, self.act, self.T, self.r, self.y, self.ws_ffn, self.stream, prof_ffn)
 
     def n_active(self):
         import numpy as np

@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_HERE, "_build", "libmoe.so")
 
 FMT_CB2, FMT_Q2K, FMT_Q4K, FMT_BF16, FMT_Q5K, FMT_Q6K = 1, 2, 3, 4, 5, 6
 ACT_F32, ACT_BF16 = 0, 1
-PATH_ROUTE, PATH_DECODE, PATH_PREFILL = 0, 1, 2
+PATH_ROUTE, PATH_DECODE, PATH_PREFILL, PATH_LAYER_DECODE = 0, 1, 2, 3
+LAYER_TOKENWISE_DECODE = 1
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
           -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
 BLOCK_BYTES = {FMT_CB2: 38, FMT_Q2K: 84, FMT_Q4K: 144, FMT_Q5K: 176, FMT_Q6K: 210}
@@ -38,7 +39,7 @@ class Layer(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("fmt_gate_up", ctypes.c_int32), ("fmt_down", ctypes.c_int32),
-                ("sh_inter", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("sh_inter", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
                 ("codebook", ctypes.c_void_p),
                 ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p),
@@ -56,7 +57,7 @@ _lib = None
 # the C ABI declared in include/moe.h
 EXPORTS = ["moe_route", "moe_expert_ffn_decode", "moe_expert_ffn_prefill", "q2_pack", "q2_unpack",
            "q2_packed_bytes", "moe_workspace_bytes", "moe_status_str", "moe_last_error",
-           "moe_expert_ffn_decode_noalloc"]
+           "moe_expert_ffn_decode_noalloc", "moe_layer_decode"]
 NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 # measurement kernels the benchmark uses (csrc/moe_probe.h; not part of the layer's ABI)
 PROBE_EXPORTS = ["moe_probe_stream_read", "moe_probe_mfma_loop"]
@@ -77,6 +78,8 @@ def lib():
     for f in (L.moe_expert_ffn_decode, L.moe_expert_ffn_prefill):
         f.argtypes = [lp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp, pp]
         f.restype = i32
+    L.moe_layer_decode.argtypes = [lp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, pp]
+    L.moe_layer_decode.restype = i32
     L.moe_expert_ffn_decode_noalloc.argtypes = [lp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, pp]
     L.moe_expert_ffn_decode_noalloc.restype = i32
     L.q2_pack.argtypes = [i32, vp, i64, i32, vp, vp]
@@ -188,6 +191,16 @@ def moe_expert_ffn_decode_noalloc(layer, x, act, T, topk_idx, topk_w, offsets, p
            "moe_expert_ffn_decode_noalloc")
 
 
+def moe_layer_decode(layer: Layer, x, act: int, T: int, bias, topk_idx, topk_w, offsets, perm, inv, y, ws,
+                     stream=None, prof: Profile | None = None):
+    """Router + decode FFN in one call (the single-token layer runs the router
+    inside the FFN's launches)."""
+    _check(lib().moe_layer_decode(ctypes.byref(layer), _ptr(x), act, T, _ptr(bias), _ptr(topk_idx), _ptr(topk_w),
+                                  _ptr(offsets), _ptr(perm), _ptr(inv), _ptr(y), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream),
+                                  None if prof is None else ctypes.byref(prof)), "moe_layer_decode")
+
+
 def moe_expert_ffn_prefill(layer, x, act, T, topk_idx, topk_w, offsets, perm, inv, y, ws, stream=None, prof=None):
     _ffn(lib().moe_expert_ffn_prefill, "moe_expert_ffn_prefill", layer, x, act, T, topk_idx, topk_w, offsets,
          perm, inv, y, ws, stream, prof)
@@ -202,11 +215,11 @@ class DeviceLayer:
     """
 
     def __init__(self, hidden, inter, n_experts, top_k, fmt_gate_up, fmt_down, w_gate, w_up, w_down,
-                 codebook, w_router, sh_gate=None, sh_up=None, sh_down=None, sh_inter=0):
+                 codebook, w_router, sh_gate=None, sh_up=None, sh_down=None, sh_inter=0, flags=0):
         self.tensors = [w_gate, w_up, w_down, codebook, w_router, sh_gate, sh_up, sh_down]
         self.hidden, self.inter, self.n_experts, self.top_k = hidden, inter, n_experts, top_k
         self.sh_inter = sh_inter
-        self.c = Layer(hidden, inter, n_experts, top_k, fmt_gate_up, fmt_down, sh_inter, 0,
+        self.c = Layer(hidden, inter, n_experts, top_k, fmt_gate_up, fmt_down, sh_inter, flags,
                        _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(codebook),
                        _ptr(sh_gate), _ptr(sh_up), _ptr(sh_down), _ptr(w_router))
 
@@ -238,6 +251,10 @@ def route(dl: DeviceLayer, x, act, T, bias, r: Routing, ws, stream=None, prof=No
 
 def ffn_decode(dl: DeviceLayer, x, act, T, r: Routing, y, ws, stream=None, prof=None):
     moe_expert_ffn_decode(dl.c, x, act, T, r.topk_idx, r.topk_w, r.offsets, r.perm, r.inv, y, ws, stream, prof)
+
+
+def layer_decode(dl: DeviceLayer, x, act, T, bias, r: Routing, y, ws, stream=None, prof=None):
+    moe_layer_decode(dl.c, x, act, T, bias, r.topk_idx, r.topk_w, r.offsets, r.perm, r.inv, y, ws, stream, prof)
 
 
 def ffn_prefill(dl: DeviceLayer, x, act, T, r: Routing, y, ws, stream=None, prof=None):

@@ -103,6 +103,7 @@ int check_layer(const moe_layer *L)
                             L->sh_down, (const void *)L->w_router})
         if ((uintptr_t)ptr % 16) return set_error(MOE_ERR_INVALID_ARG, "layer pointer %p is not 16-byte aligned", ptr);
     if (L->sh_inter < 0) return set_error(MOE_ERR_INVALID_ARG, "sh_inter=%d < 0", L->sh_inter);
+    if (L->flags & ~MOE_LAYER_TOKENWISE_DECODE) return set_error(MOE_ERR_INVALID_ARG, "flags=%#x: unknown bits", L->flags);
     if (L->sh_inter > 0) {
         if (!L->sh_gate || !L->sh_up || !L->sh_down) return set_error(MOE_ERR_INVALID_ARG, "shared expert weights are NULL");
         if (L->sh_inter % 256 || L->hidden % 256)
@@ -162,9 +163,10 @@ struct FfnWs {
 // not depend on the batch it came in.  They apply for CB2/Q2K and the shapes
 // the single-token kernels support.
 constexpr int DEC_TOKENWISE_MAX = 4;
+bool tokenwise_flag(const moe_layer *L) { return (L->flags & MOE_LAYER_TOKENWISE_DECODE) != 0; }
 bool dec_single(const moe_layer *L, int T, bool prefill, bool x_f32)
 {
-    if (prefill || T < 1 || T > DEC_TOKENWISE_MAX) return false;
+    if (prefill || T < 1 || (T > DEC_TOKENWISE_MAX && !tokenwise_flag(L))) return false;
     if (L->fmt_gate_up != MOE_FMT_CB2 || L->fmt_down != MOE_FMT_Q2K) return false;
     return dec_single_ok(1, L->hidden, L->inter, L->sh_inter, L->top_k, nblocks(L->hidden) * 38, x_f32);
 }
@@ -236,6 +238,50 @@ size_t ffn_ws_bytes(const moe_layer *L, int T, bool prefill)
     return b;
 }
 
+// The staged single-token layer: stage 1 (shared gate/up, and with d.route
+// the router's partial logits), stage 2 (routed gate/up -- with d.route after
+// selecting the experts -- beside the shared down), routed h, routed down + y.
+int launch_staged(const DecPass &d, Prof &pr)
+{
+    hipError_t e;
+#define MOE_STAGE(name, call)                                                      \
+    do {                                                                           \
+        if (!pr.before(name)) return hip_fail(hipGetLastError(), "event record");  \
+        e = call;                                                                  \
+        if (e != hipSuccess) return hip_fail(e, name);                             \
+        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");       \
+    } while (0)
+    MOE_STAGE("dec_stage1", launch_dec_stage1(d, pr.s));
+    MOE_STAGE("dec_stage2", launch_dec_stage2(d, pr.s));
+    MOE_STAGE("dec_hform", launch_dec_hform(d, pr.s));
+    MOE_STAGE("dec_down_fused", launch_dec_down_fused(d, pr.s));
+#undef MOE_STAGE
+    return MOE_OK;
+}
+
+// the single-token pass over one layer (everything but the activations, the
+// routing and the output), for the decode path's token-wise kernels
+DecPass single_pass(const moe_layer *L, const FfnWs &w, int act)
+{
+    DecPass d{};
+    const int H = L->hidden, I = L->inter;
+    d.T = 1; d.k = L->top_k; d.E = L->n_experts; d.H = H; d.I = I; d.Ish = L->sh_inter; d.nbI = nblocks(I);
+    d.wg = (const uint8_t *)L->w_gate; d.wu = (const uint8_t *)L->w_up; d.wd = (const uint8_t *)L->w_down;
+    d.gu_row_bytes = nblocks(H) * 38;
+    d.gu_expert_bytes = (int64_t)d.gu_row_bytes * I;
+    d.d_row_bytes = nblocks(I) * 84;
+    d.d_expert_bytes = (int64_t)d.d_row_bytes * H;
+    d.sg = (const uint16_t *)L->sh_gate; d.su = (const uint16_t *)L->sh_up; d.sd = (const uint16_t *)L->sh_down;
+    d.codebook = L->codebook;
+    d.x_f32 = act == MOE_ACT_F32;
+    d.nkc = w.nkc; d.part_rt = w.part_rt;
+    d.h_hi = w.h_hi; d.h_lo = w.h_lo; d.hstride = w.hstride; d.X = w.X; d.sh_hi = w.sh_hi; d.sh_lo = w.sh_lo;
+    d.fused = dec_fused_ok(d.k, I, d.Ish);
+    d.part_sh = w.part_sh;
+    d.O = w.O; d.O_sh = w.O_sh;
+    return d;
+}
+
 int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t *topk_idx, const float *topk_w,
                const int32_t *offsets, const int32_t *perm, const int32_t *inv, float *y, void *ws,
                size_t ws_bytes, void *stream, moe_profile *prof, bool prefill)
@@ -264,6 +310,10 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
                              "sh_inter multiples of 512", L->fmt_gate_up, L->fmt_down);
     } else {
         const bool cb2q2k = L->fmt_gate_up == MOE_FMT_CB2 && L->fmt_down == MOE_FMT_Q2K;
+        if (tokenwise_flag(L) && !dec_single(L, T, false, act == MOE_ACT_F32))
+            return set_error(MOE_ERR_UNSUPPORTED, "token-by-token decode needs a layer the single-token kernels take "
+                             "(CB2 gate/up, Q2K down, H %% 512 == 0, H <= 8192, I %% 256 == 0, I <= 2048, "
+                             "sh_inter %% 512 == 0)");
         if (!cb2q2k && !gemm)
             return set_error(MOE_ERR_UNSUPPORTED, "decode with gate/up fmt %d, down fmt %d needs hidden, inter and "
                              "sh_inter multiples of 512", L->fmt_gate_up, L->fmt_down);
@@ -284,45 +334,26 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
     const int BM = prefill ? PRE_BM : DEC_BM;
 
     if (w.single) {
-        DecPass d{};
-        d.T = 1; d.k = k; d.E = E; d.H = H; d.I = I; d.Ish = Ish; d.nbI = nblocks(I);
+        DecPass d = single_pass(L, w, act);
         d.topk_idx = topk_idx; d.offsets = offsets; d.inv = inv; d.topk_w = topk_w;
-        d.wg = (const uint8_t *)L->w_gate; d.wu = (const uint8_t *)L->w_up; d.wd = (const uint8_t *)L->w_down;
-        d.gu_row_bytes = nblocks(H) * 38;
-        d.gu_expert_bytes = (int64_t)d.gu_row_bytes * I;
-        d.d_row_bytes = nblocks(I) * 84;
-        d.d_expert_bytes = (int64_t)d.d_row_bytes * H;
-        d.sg = (const uint16_t *)L->sh_gate; d.su = (const uint16_t *)L->sh_up; d.sd = (const uint16_t *)L->sh_down;
-        d.codebook = L->codebook;
-        d.x = x; d.x_f32 = act == MOE_ACT_F32;
-        d.nkc = w.nkc; d.part_rt = w.part_rt;
-        d.h_hi = w.h_hi; d.h_lo = w.h_lo; d.hstride = w.hstride; d.X = w.X; d.sh_hi = w.sh_hi; d.sh_lo = w.sh_lo;
-        d.fused = dec_fused_ok(k, I, Ish);
-        d.part_sh = w.part_sh;
-        d.O = w.O; d.O_sh = w.O_sh; d.y = y;
+        d.x = x; d.y = y;
         dec_plan(d);
+        if (d.fused) dec_plan_staged(d);
         const size_t xrow = (size_t)H * (act == MOE_ACT_F32 ? 4 : 2);
         for (int t = 0; t < T; ++t) {                              // one token at a time, in order
             d.x = (const char *)x + t * xrow;
             d.topk_idx = topk_idx + (size_t)t * k;
             d.topk_w = topk_w + (size_t)t * k;
             d.y = y + (size_t)t * H;
+            if (d.fused) {
+                const int rc2 = launch_staged(d, pr);
+                if (rc2) return rc2;
+                continue;
+            }
             if (!pr.before("dec_gateup")) return hip_fail(hipGetLastError(), "event record");
             hipError_t e = launch_dec_gateup(d, s);
             if (e != hipSuccess) return hip_fail(e, "dec_gateup launch");
             if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
-            if (d.fused) {
-                // h once, then every slot and the shared expert straight into y
-                if (!pr.before("dec_hform")) return hip_fail(hipGetLastError(), "event record");
-                e = launch_dec_hform(d, s);
-                if (e != hipSuccess) return hip_fail(e, "dec_hform launch");
-                if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
-                if (!pr.before("dec_down_fused")) return hip_fail(hipGetLastError(), "event record");
-                e = launch_dec_down_fused(d, s);
-                if (e != hipSuccess) return hip_fail(e, "dec_down_fused launch");
-                if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
-                continue;
-            }
             if (!pr.before("dec_down")) return hip_fail(hipGetLastError(), "event record");
             e = launch_dec_down(d, s);
             if (e != hipSuccess) return hip_fail(e, "dec_down launch");
@@ -408,6 +439,17 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
     return MOE_OK;
 }
 
+// moe_layer_decode's workspace: the router's, then the decode FFN's
+size_t layer_ws_bytes(const moe_layer *L, int T) { return align_up(route_ws(L, T, nullptr).bytes) + ffn_ws_bytes(L, T, false); }
+
+// the fused single-token layer applies (router in the stages) for one token of
+// a CB2/Q2K layer of the single-token shapes with the fused down
+bool layer_fused(const moe_layer *L, int T, int act)
+{
+    return T == 1 && route_fused(L, 1) && dec_single(L, 1, false, act == MOE_ACT_F32) &&
+           dec_fused_ok(L->top_k, L->inter, L->sh_inter);
+}
+
 // ---------------------------------------------------------------- no-allocation decode
 // The decode workspace of moe_expert_ffn_decode_noalloc: one fixed array per
 // device, which the library holds until the process ends.  In host code
@@ -465,8 +507,9 @@ size_t moe_workspace_bytes(const moe_layer *L, int T, int path)
         if (check_router(L)) return 0;
         return route_ws(L, T, nullptr).bytes;
     }
-    if (path != MOE_PATH_DECODE && path != MOE_PATH_PREFILL) return 0;
+    if (path != MOE_PATH_DECODE && path != MOE_PATH_PREFILL && path != MOE_PATH_LAYER_DECODE) return 0;
     if (check_layer(L)) return 0;
+    if (path == MOE_PATH_LAYER_DECODE) return layer_ws_bytes(L, T);
     return ffn_ws_bytes(L, T, path == MOE_PATH_PREFILL);
 }
 
@@ -545,6 +588,62 @@ int moe_expert_ffn_decode_noalloc(const moe_layer *L, const void *x, int act, in
     if (!ws) return MOE_ERR_HIP;
     return ffn_common(L, x, act, T, topk_idx, topk_w, offsets, perm, inv, y, ws, MOE_NOALLOC_SCRATCH_BYTES, stream,
                       prof, false);
+}
+
+int moe_layer_decode(const moe_layer *L, const void *x, int act, int T, const float *bias, int32_t *topk_idx,
+                     float *topk_w, int32_t *offsets, int32_t *perm, int32_t *inv, float *y, void *ws,
+                     size_t ws_bytes, void *stream, moe_profile *prof)
+{
+    int rc = check_layer(L);
+    if (rc) return rc;
+    if (T < 0) return set_error(MOE_ERR_INVALID_ARG, "T=%d < 0", T);
+    if (act != MOE_ACT_F32 && act != MOE_ACT_BF16) return set_error(MOE_ERR_INVALID_ARG, "act=%d unknown", act);
+    if (prof) prof->n_launches = 0;
+    if (T == 0) return MOE_OK;
+    if (!x || !topk_idx || !topk_w || !offsets || !perm || !inv || !y) return set_error(MOE_ERR_INVALID_ARG, "NULL tensor argument");
+    if (!ws) return set_error(MOE_ERR_INVALID_ARG, "workspace is NULL");
+    if ((uintptr_t)x % 16 || (uintptr_t)y % 16 || (uintptr_t)ws % 16)
+        return set_error(MOE_ERR_INVALID_ARG, "x, y and the workspace must be 16-byte aligned");
+    if ((int64_t)T * L->top_k > (1 << 30)) return set_error(MOE_ERR_INVALID_ARG, "T*k too large");
+    const size_t need = layer_ws_bytes(L, T);
+    if (ws_bytes < need) return set_error(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    const size_t rbytes = align_up(route_ws(L, T, nullptr).bytes);
+    char *fws = (char *)ws + rbytes;
+    if (!layer_fused(L, T, act)) {
+        // the router's launches, then the decode FFN's, on the two parts of the
+        // workspace; the FFN's launches are numbered after the router's
+        rc = moe_route(L, x, act, T, bias, topk_idx, topk_w, offsets, perm, inv, ws, rbytes, stream, prof);
+        if (rc) return rc;
+        moe_profile fp{}, *fpp = nullptr;
+        const int nr = prof ? prof->n_launches : 0;
+        if (prof) {
+            fp = *prof;
+            fp.kernel = prof->kernel - nr;
+            fpp = &fp;
+        }
+        rc = ffn_common(L, x, act, T, topk_idx, topk_w, offsets, perm, inv, y, fws, ws_bytes - rbytes, stream, fpp,
+                        false);
+        if (prof) {
+            prof->n_launches = nr + fp.n_launches;
+            if (fp.kernel >= 0 && fp.kernel < fp.n_launches) prof->name = fp.name;
+        }
+        return rc;
+    }
+    FfnWs w = ffn_ws(L, 1, false, true, fws);
+    DecPass d = single_pass(L, w, act);
+    d.x = x; d.y = y;
+    d.topk_idx = topk_idx; d.topk_w = topk_w; d.offsets = offsets; d.inv = inv;
+    d.route = 1;
+    d.wr = L->w_router; d.bias = bias;
+    d.rpart = route_ws(L, 1, (char *)ws).logits;
+    d.rnc = route_decode_chunks(1, L->hidden);
+    const int steps = (L->hidden + 255) / 256;
+    d.rhc = ((steps + d.rnc - 1) / d.rnc) * 256;
+    d.o_idx = topk_idx; d.o_w = topk_w; d.o_off = offsets; d.o_perm = perm; d.o_inv = inv;
+    dec_plan(d);
+    dec_plan_staged(d);
+    Prof pr{prof, (hipStream_t)stream};
+    return launch_staged(d, pr);
 }
 
 int moe_expert_ffn_prefill(const moe_layer *L, const void *x, int act, int T, const int32_t *topk_idx,

@@ -29,6 +29,22 @@ struct DecPass {
     float *y;                                    // [H]
     int gu_sh_wg, gu_rt_wg;                      // gate/up work-groups: shared, routed role
     int dn_sh_wg, dn_rt_wg;                      // down work-groups: shared, routed role
+    // staged single-token layer (dec_stage1 / dec_stage2, then dec_hform and
+    // dec_down_fused with the shared down already done)
+    int s1_wg;                                   // stage 1 work-groups (every one takes shared gate/up units)
+    int s2_sd_wg, s2_rt_wg;                      // stage 2 work-groups: shared down role, routed gate/up role
+    int staged;                                  // 1: the shared down is done in stage 2 (O_sh parts),
+                                                 //    so dec_hform forms routed h only and dec_down_fused
+                                                 //    adds the O_sh parts to y
+    // router inside the stages (the fused layer entry point): stage 1 writes the
+    // partial logits, stage 2 selects from them
+    int route;                                   // 1: stage 1 computes the logits, stage 2 selects
+    const float *wr;                             // [E][H] fp32 router weights
+    const float *bias;                           // [E] or null
+    double *rpart;                               // [rnc][E] partial logits
+    int rnc, rhc;                                // H chunks and chunk length of the partial logits
+    int32_t *o_idx, *o_off, *o_perm, *o_inv;     // routing outputs written by stage 2
+    float *o_w;
 };
 constexpr int DEC_SH_KQ = 8;                     // K parts of the single-token shared gate/up (part_sh)
 constexpr int DEC_LUT_KB = 4;                    // 256-wide blocks per K chunk of a routed gate/up table
@@ -42,5 +58,12 @@ hipError_t launch_dec_combine(const DecPass &p, hipStream_t s);
 bool dec_fused_ok(int k, int I, int Ish);
 hipError_t launch_dec_hform(const DecPass &p, hipStream_t s);
 hipError_t launch_dec_down_fused(const DecPass &p, hipStream_t s);
+// the staged single-token layer (p.staged = 1; dec_fused_ok shapes): stage 1
+// (shared gate/up, and with p.route the router's partial logits), stage 2
+// (routed gate/up -- with p.route selecting the experts first -- and the
+// shared down), then dec_hform and dec_down_fused
+void dec_plan_staged(DecPass &p);
+hipError_t launch_dec_stage1(const DecPass &p, hipStream_t s);
+hipError_t launch_dec_stage2(const DecPass &p, hipStream_t s);
 
 }  // namespace moe

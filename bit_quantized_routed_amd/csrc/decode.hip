@@ -42,6 +42,7 @@
 #include "decode.h"
 #include "devcache.h"
 #include "kernels.h"
+#include "route_dev.h"
 
 namespace moe {
 
@@ -54,7 +55,14 @@ constexpr int DN_ROWS = 128;       // output rows of a down unit (16 per wave)
 constexpr int DN_KPART = 512;      // K part of a shared down unit
 constexpr int DN_MAXB = 8;         // Q2_K blocks per row of a routed down unit (I <= 2048)
 constexpr int DN_MAXKC = 8;        // K chunks of the routed gate/up tables (H <= 8192)
+constexpr int DF_SHSEG = 4;        // 512-wide K segments of the staged shared down (sh_inter <= 2048)
 constexpr size_t LDS_MAX = 160 * 1024;
+// Routed gate/up tiles per work-group in the register ring (2..6).  Measured
+// on decode1: 2 (the next tile in flight while one is computed) is fastest;
+// deeper rings put more scattered row windows in flight at once and were
+// slower (63.1 / 65.5 / 67.5 / 69.1 us per step for 2 / 3 / 4 / 5).
+constexpr int GU_PF = 2;
+static_assert(GU_PF >= 2 && GU_PF <= 6, "ring of 2 to 6 register sets");
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -95,9 +103,158 @@ __device__ __forceinline__ void act_block(const uint16_t *row, int k0, int step,
 __device__ __forceinline__ int clamp_expert(int g, int E) { return min(max(g, 0), E - 1); }
 
 // ============================================================== gate / up
-// Work-groups [0, gu_sh_wg) take shared-expert units u = wg, wg + gu_sh_wg, ...;
-// the others take routed units the same way.
+// One kernel, three launch modes:
+//   GU_SPLIT   work-groups [0, gu_sh_wg) take shared-expert gate/up units
+//              u = wg, wg + gu_sh_wg, ...; the others take routed units.
+//   GU_STAGE1  every work-group first takes router items (fp64 partial logits
+//              of one expert over one H chunk, when p.route), then shared
+//              gate/up units.
+//   GU_STAGE2  work-groups [0, s2_sd_wg) take shared down units (the shared
+//              h is complete after stage 1); the others take routed gate/up
+//              units, first selecting the experts from the partial logits
+//              when p.route (every routed work-group selects, the first also
+//              writes the routing outputs).
+enum { GU_SPLIT = 0, GU_STAGE1 = 1, GU_STAGE2 = 2 };
+
+// Whole-row GEMV pieces of the staged layer's shared expert.  A wave streams
+// rows from HBM in 512-wide K segments (64 lanes x 8 bf16, 1 KB contiguous per
+// load instruction), so every row is read front to back; the activation's
+// matching 8 values sit in the lane's registers (or come from LDS), and pairs
+// of bf16 products accumulate in fp32 (v_dot2c_f32_bf16: the products of
+// bf16 values are exact).  One wave reduction per row.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t a, float acc)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, a), acc, false);
+}
+
+// the elements are copied out first: a bit cast of a vector element (w.y)
+// would reinterpret the storage from the vector's start
+__device__ __forceinline__ float dot8(const u32x4 &w, const u32x4 &a, float acc)
+{
+    const uint32_t w0 = w.x, w1 = w.y, w2 = w.z, w3 = w.w, a0 = a.x, a1 = a.y, a2 = a.z, a3 = a.w;
+    acc = dot2(w0, a0, acc);
+    acc = dot2(w1, a1, acc);
+    acc = dot2(w2, a2, acc);
+    acc = dot2(w3, a3, acc);
+    return acc;
+}
+
+// sum over the 64 lanes (in a fixed butterfly order; every lane gets it)
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Stage 1, shared gate/up: unit = one feature and one half of K; waves 2i and
+// 2i + 1 of a work-group take the two halves of feature 8 (round * G + wg) + i.
+// The halves meet in LDS and the first wave writes the feature's
+// h = silu(g) * u as two bf16 terms (sh_hi, sh_lo).  x (one or two bf16 terms)
+// was staged in LDS by the caller.
 template <bool XF32>
+__device__ __forceinline__ void dec1_shared_gateup_rows(const DecPass &p, const uint16_t *xh, const uint16_t *xl,
+                                                        float *red, int G)
+{
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int H = p.H, ns = H / 512, half = wave & 1, nlo = ns / 2;
+    const int s0 = half ? nlo : 0, s1 = half ? ns : nlo;
+    const int rounds = (p.Ish + 8 * G - 1) / (8 * G);
+    constexpr int B = 4;                                          // segments requested together
+    for (int rd = 0; rd < rounds; ++rd) {
+        const int f = 8 * (rd * G + (int)blockIdx.x) + (wave >> 1);
+        float ag = 0.f, au = 0.f;
+        if (f < p.Ish) {                                          // uniform over the wave
+            const uint16_t *rg = p.sg + (int64_t)f * H + 8 * lane, *ru = p.su + (int64_t)f * H + 8 * lane;
+            for (int sb = s0; sb < s1; sb += B) {
+                u32x4 g4[B], u4[B];
+#pragma unroll
+                for (int i = 0; i < B; ++i) {
+                    const int sg = min(sb + i, s1 - 1);           // past the half: re-read, not used
+                    g4[i] = *(const u32x4 *)(rg + 512 * sg);
+                    u4[i] = *(const u32x4 *)(ru + 512 * sg);
+                }
+#pragma unroll
+                for (int i = 0; i < B; ++i) {
+                    if (sb + i >= s1) break;
+                    const int k = 512 * (sb + i) + 8 * lane;
+                    const u32x4 a = *(const u32x4 *)&xh[k];
+                    ag = dot8(g4[i], a, ag);
+                    au = dot8(u4[i], a, au);
+                    if (XF32) {
+                        const u32x4 al = *(const u32x4 *)&xl[k];
+                        ag = dot8(g4[i], al, ag);
+                        au = dot8(u4[i], al, au);
+                    }
+                }
+            }
+            ag = wave_sum(ag);
+            au = wave_sum(au);
+        }
+        if (half && lane == 0) { red[2 * (wave >> 1)] = ag; red[2 * (wave >> 1) + 1] = au; }
+        __syncthreads();
+        if (!half && lane == 0 && f < p.Ish) {
+            const float g = ag + red[2 * (wave >> 1)], uu = au + red[2 * (wave >> 1) + 1];
+            const float h = g / (1.0f + expf(-g)) * uu;
+            uint32_t hi, lo;
+            split_bf16(h, hi, lo);
+            p.sh_hi[f] = (uint16_t)hi;
+            p.sh_lo[f] = (uint16_t)lo;
+        }
+        __syncthreads();
+    }
+}
+
+// Stage 2, shared down: wave n of the role streams output rows n, n + NW, ...
+// (NW = the role's waves) over all of sh_inter, with the shared h for its lanes'
+// K positions (two bf16 terms per value) in registers; the row's sum goes to
+// O_sh[row] (one part).  Two rows are in flight per wave.
+__device__ __forceinline__ void dec1_shared_down_rows(const DecPass &p, int wg, int G)
+{
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int H = p.H, ns = p.Ish / 512;                          // <= DF_SHSEG segments
+    u32x4 hh[DF_SHSEG], hl[DF_SHSEG];
+#pragma unroll
+    for (int s = 0; s < DF_SHSEG; ++s) {
+        const int k = 512 * min(s, ns - 1) + 8 * lane;
+        hh[s] = *(const u32x4 *)(p.sh_hi + k);
+        hl[s] = *(const u32x4 *)(p.sh_lo + k);
+    }
+    const int NW = G * GU_WAVES, n = wg * GU_WAVES + wave;
+    u32x4 Wa[DF_SHSEG], Wb[DF_SHSEG];
+    auto load = [&](int r, u32x4 (&W4)[DF_SHSEG]) {
+        const uint16_t *rw = p.sd + (int64_t)min(r, H - 1) * p.Ish + 8 * lane;
+#pragma unroll
+        for (int s = 0; s < DF_SHSEG; ++s) W4[s] = *(const u32x4 *)(rw + 512 * min(s, ns - 1));
+    };
+    auto row = [&](int r, const u32x4 (&W4)[DF_SHSEG]) {
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < DF_SHSEG; ++s) {
+            if (s < ns) {
+                acc = dot8(W4[s], hh[s], acc);
+                acc = dot8(W4[s], hl[s], acc);
+            }
+        }
+        acc = wave_sum(acc);
+        if (lane == 0 && r < H) p.O_sh[r] = acc;
+    };
+    if (n >= H) return;                                           // uniform over the wave
+    // two register sets in turn; the prefetch past the last row re-reads it
+    load(n, Wa);
+    for (int r = n;;) {
+        load(r + NW < H ? r + NW : r, Wb);
+        row(r, Wa);
+        if ((r += NW) >= H) break;
+        load(r + NW < H ? r + NW : r, Wa);
+        row(r, Wb);
+        if ((r += NW) >= H) break;
+    }
+}
+
+template <bool XF32, int MODE = GU_SPLIT, int MAXPL = 4>
 __global__ __launch_bounds__(GU_THREADS) void dec1_gateup_kernel(DecPass p)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
@@ -106,10 +263,54 @@ __global__ __launch_bounds__(GU_THREADS) void dec1_gateup_kernel(DecPass p)
     const int fr = lane & 15, fc = lane >> 4;
     const int H = p.H;
 
-    const bool shared_role = (int)blockIdx.x < p.gu_sh_wg;
-    const int G = shared_role ? p.gu_sh_wg : p.gu_rt_wg;
-    int u = shared_role ? (int)blockIdx.x : (int)blockIdx.x - p.gu_sh_wg;
+    bool shared_role;
+    int G, u;
+    if constexpr (MODE == GU_STAGE1) {
+        if (p.route) {
+            // the router's partial logits, one item per wave, spread over the
+            // whole grid before the shared units (the same items and
+            // arithmetic as the router's own partial-logit launch)
+            const int nitems = p.E * p.rnc, nw = (int)gridDim.x * GU_WAVES;
+            for (int item = (int)blockIdx.x + (int)gridDim.x * wave; item < nitems; item += nw)
+                route_partial_item<1, 1, !XF32>(p.x, p.wr, 1, H, p.E, p.rnc, p.rhc, item, lane, p.rpart);
+        }
+        shared_role = true;
+        G = gridDim.x;
+        u = blockIdx.x;
+    } else {
+        const int na = MODE == GU_STAGE2 ? p.s2_sd_wg : p.gu_sh_wg;
+        shared_role = (int)blockIdx.x < na;
+        G = shared_role ? na : (MODE == GU_STAGE2 ? p.s2_rt_wg : p.gu_rt_wg);
+        u = shared_role ? (int)blockIdx.x : (int)blockIdx.x - na;
+    }
 
+    if constexpr (MODE == GU_STAGE2) {
+        if (shared_role) {
+            dec1_shared_down_rows(p, u, G);
+            return;
+        }
+    }
+    if constexpr (MODE == GU_STAGE1) {
+        // x (hi, and lo for fp32 x) into LDS, then whole shared gate/up rows
+        uint16_t *xh = (uint16_t *)dsm;                           // [H]
+        uint16_t *xl = xh + H;                                    // [H] (fp32 x only)
+        float *red = (float *)(dsm + (XF32 ? 4 : 2) * (size_t)H); // [8 features][2]
+        for (int i = tid; i < H / 8; i += GU_THREADS) {
+            if (XF32) {
+                const float *src = (const float *)p.x + 8 * i;
+                uint32_t h[8], l[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) split_bf16(src[e], h[e], l[e]);
+                *(u32x4 *)&xh[8 * i] = pack8(h);
+                *(u32x4 *)&xl[8 * i] = pack8(l);
+            } else {
+                *(u32x4 *)&xh[8 * i] = *(const u32x4 *)((const uint16_t *)p.x + 8 * i);
+            }
+        }
+        __syncthreads();
+        if (p.Ish > 0) dec1_shared_gateup_rows<XF32>(p, xh, xl, red, G);
+        return;
+    }
     if (shared_role) {
         // ---------------------------------------------- shared expert
         const int n_units = (p.Ish / 16) * SH_KQ;
@@ -211,7 +412,15 @@ __global__ __launch_bounds__(GU_THREADS) void dec1_gateup_kernel(DecPass p)
     const int kb = min(DEC_LUT_KB, nbH - DEC_LUT_KB * kc);        // blocks in this chunk (2 or 4: H % 512 == 0)
     float *tab = (float *)dsm;                                    // [32 * DEC_LUT_KB groups][256 codewords]
     float *red = tab + 32 * DEC_LUT_KB * 256;                     // [2][4 blocks][256 rows]
-    if (tid < p.k) kid[tid] = clamp_expert(p.topk_idx[tid], p.E);
+    if (MODE == GU_STAGE2 && p.route) {
+        // every routed work-group selects the same experts from the partial
+        // logits; the first one also writes the routing outputs
+        if (wave == 0)
+            select_one<MAXPL>(p.rpart, p.bias, p.E, p.k, p.rnc, lane, p.o_idx, p.o_w, p.o_off, p.o_perm, p.o_inv,
+                              u == 0, kid, nullptr);
+    } else if (tid < p.k) {
+        kid[tid] = clamp_expert(p.topk_idx[tid], p.E);
+    }
     __syncthreads();                                              // expert ids staged
     // this wave's block of the chunk; waves past a short chunk re-read its
     // last block and their sums are not added.  Blocks start 2-byte aligned
@@ -230,15 +439,21 @@ __global__ __launch_bounds__(GU_THREADS) void dec1_gateup_kernel(DecPass p)
         const int s = t / nft, f = 128 * (t - s * nft) + 64 * i + lane;
         return (const uint32_t *)(wmat + (int64_t)kid[s] * p.gu_expert_bytes + (int64_t)f * rb + boff);
     };
-    uint32_t wa[10], wb2[10];
-    auto load = [&](int t, uint32_t (&W)[10]) {
+    // GU_PF register sets in a ring: while one tile is computed, the next
+    // GU_PF - 1 tiles of this work-group are in flight (a work-group's tiles are
+    // scattered 40-byte row windows, so several must be requested at once to
+    // keep enough bytes moving per CU).  Loads past the last tile re-read the
+    // first one and are never used.
+    uint32_t W[GU_PF][10];
+    auto load = [&](int t, uint32_t (&Wr)[10]) {
         const uint32_t *src = rowp(t, i0);
 #pragma unroll
-        for (int e = 0; e < 10; ++e) W[e] = src[e];
+        for (int e = 0; e < 10; ++e) Wr[e] = src[e];
     };
-    // the first tile loads while the table is built
+    // the first tiles load while the table is built
     int t = j0;
-    load(t, wa);
+#pragma unroll
+    for (int i = 0; i < GU_PF; ++i) load(t + i * R < ntile ? t + i * R : t, W[i]);
     {
         // wave w: codewords 32 (w % 8) .. + 31 against the 32-group tiles w / 8, w / 8 + 2, ...
         const int c = 32 * (wave & 7) + (lane & 31), hl = lane >> 5;
@@ -309,20 +524,26 @@ __global__ __launch_bounds__(GU_THREADS) void dec1_gateup_kernel(DecPass p)
         }
     };
     __syncthreads();                                              // table staged
-    // two register buffers in turn: the next tile is in flight while this one
-    // is computed.  The prefetch is unconditional (the last tile re-reads its
-    // own rows); the two LDS buffers of block sums alternate, so one barrier
-    // per tile suffices.
-    for (int buf = 0;;) {
-        load(t + R < ntile ? t + R : t, wb2);
-        tile(t, buf, wa);
-        buf ^= 1;
-        if ((t += R) >= ntile) break;
-        load(t + R < ntile ? t + R : t, wa);
-        tile(t, buf, wb2);
-        buf ^= 1;
-        if ((t += R) >= ntile) break;
+    // the ring, unrolled so every register set has a fixed name: a tile is
+    // computed from its set, which then takes the tile GU_PF steps later (an
+    // unconditional load); the two LDS buffers of block sums alternate, so one
+    // barrier per tile suffices
+#define MOE_GU_STEP(i)                                                             \
+    if constexpr ((i) < GU_PF) {                                                   \
+        tile(t, buf, W[i]);                                                        \
+        buf ^= 1;                                                                  \
+        load(t + GU_PF * R < ntile ? t + GU_PF * R : t, W[i]);                     \
+        if ((t += R) >= ntile) break;                                              \
     }
+    for (int buf = 0;;) {
+        MOE_GU_STEP(0)
+        MOE_GU_STEP(1)
+        MOE_GU_STEP(2)
+        MOE_GU_STEP(3)
+        MOE_GU_STEP(4)
+        MOE_GU_STEP(5)
+    }
+#undef MOE_GU_STEP
 }
 
 // ============================================================== down
@@ -610,7 +831,8 @@ __global__ __launch_bounds__(256) void dec1_hform_kernel(DecPass p)
 {
     const int q = blockIdx.x * 256 + threadIdx.x, lane = threadIdx.x & 63;
     const int I = p.I, nq_rt = p.k * I;
-    if (q >= nq_rt + p.Ish) return;                                // uniform over each wave
+    // staged layer: the shared h was formed by stage 2's shared down units
+    if (q >= nq_rt + (p.staged ? 0 : p.Ish)) return;              // uniform over each wave
     float g, uu;
     int slot = 0, f;
     if (q < nq_rt) {
@@ -661,6 +883,10 @@ __global__ __launch_bounds__(256) void dec1_hform_kernel(DecPass p)
     }
 }
 
+// SHP: the staged layer, whose shared down is already done (O_sh parts, added
+// to y in part order after the wave sums); otherwise each wave also takes a K
+// eighth of the bf16 shared down.
+template <bool SHP>
 __global__ __launch_bounds__(DF_THREADS) void dec1_down_fused_kernel(DecPass p, int rows)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
@@ -668,7 +894,7 @@ __global__ __launch_bounds__(DF_THREADS) void dec1_down_fused_kernel(DecPass p, 
     __shared__ float wsum[DF_THREADS / 64][16];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int fr = lane & 15, fc = lane >> 4;
-    const int nb = p.nbI, I = p.I, k = p.k, Ish = p.Ish;
+    const int nb = p.nbI, I = p.I, k = p.k, Ish = SHP ? 0 : p.Ish;
     uint16_t *tab = (uint16_t *)dsm;                               // [16 sc][256 bytes][4]
     uint16_t *hh = tab + 16 * 256 * 4;                             // [k][I] routed h hi
     uint16_t *hl = hh + k * I;                                     // [k][I] lo
@@ -803,6 +1029,9 @@ __global__ __launch_bounds__(DF_THREADS) void dec1_down_fused_kernel(DecPass p, 
         float y = 0.f;
 #pragma unroll
         for (int w2 = 0; w2 < DF_THREADS / 128; ++w2) y += wsum[2 * w2 + g2][r];
+        if constexpr (SHP) {
+            if (p.Ish > 0) y += p.O_sh[rows * blockIdx.x + tid];      // the shared down's row
+        }
         p.y[rows * blockIdx.x + tid] = y;
     }
 }
@@ -864,6 +1093,9 @@ void split_roles(int n_a, double c_a, int n_b, double c_b, int G, int &g_a, int 
 // role work in proportion to these costs.
 constexpr double CB2_COST = 1.5;
 constexpr double Q2K_COST = 2.5;
+// the same for the staged layer's stage 2, against whole-row bf16 streaming
+// (decode1 measured within 1% for weights 2 to 6)
+constexpr double S2_CB2_COST = 3.0;
 
 }  // namespace
 
@@ -927,22 +1159,90 @@ size_t lds_dn_fused(int k, int I, int nbI, int Ish)
 
 hipError_t launch_dec_hform(const DecPass &p, hipStream_t s)
 {
-    const int nq = p.k * p.I + p.Ish;
+    const int nq = p.k * p.I + (p.staged ? 0 : p.Ish);
     dec1_hform_kernel<<<(nq + 255) / 256, 256, 0, s>>>(p);
     return hipGetLastError();
 }
 
 hipError_t launch_dec_down_fused(const DecPass &p, hipStream_t s)
 {
-    const size_t lds = lds_dn_fused(p.k, p.I, p.nbI, p.Ish);
-    static DevSlots attr{};                                        // dynamic LDS limit set, per device
-    const hipError_t e = lds_limit((const void *)dec1_down_fused_kernel, attr, lds);
+    const size_t lds = lds_dn_fused(p.k, p.I, p.nbI, p.staged ? 0 : p.Ish);
+    static DevSlots attr[2];                                       // dynamic LDS limit set, per device
+    const void *fn = p.staged ? (const void *)dec1_down_fused_kernel<true> : (const void *)dec1_down_fused_kernel<false>;
+    const hipError_t e = lds_limit(fn, attr[p.staged ? 1 : 0], lds);
     if (e != hipSuccess) return e;
     // one work-group per CU where H allows: fewer rows per CU than a fixed
     // 32 when H / 32 work-groups would leave CUs idle
     const int ncu = cu_count();
     const int rows = std::min(DF_ROWS, std::max(16, (p.H + ncu - 1) / ncu));
-    dec1_down_fused_kernel<<<(p.H + rows - 1) / rows, DF_THREADS, lds, s>>>(p, rows);
+    if (p.staged) dec1_down_fused_kernel<true><<<(p.H + rows - 1) / rows, DF_THREADS, lds, s>>>(p, rows);
+    else dec1_down_fused_kernel<false><<<(p.H + rows - 1) / rows, DF_THREADS, lds, s>>>(p, rows);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ staged layer
+namespace {
+
+size_t lds_stage1(int H, bool xf32) { return (size_t)(xf32 ? 4 : 2) * H + 2 * 16 * GU_WAVES * sizeof(float); }
+size_t lds_stage2() { return (32 * DEC_LUT_KB * 256 + 2 * 4 * 256) * sizeof(float); }
+
+// experts per lane of the selection: 4 (E <= 256) or 16 (E <= 1024)
+bool wide_select(const DecPass &p) { return p.route && p.E > 256; }
+
+DevSlots occ_s1[2], occ_s2[4];
+
+}  // namespace
+
+void dec_plan_staged(DecPass &p)
+{
+    const int ncu = cu_count();
+    // stage 1: work-groups of 8 shared features (both halves of K each), and
+    // router items spread over all of its waves
+    const size_t l1 = lds_stage1(p.H, p.x_f32);
+    const int occ1 = p.x_f32 ? resident(dec1_gateup_kernel<true, GU_STAGE1, 4>, l1, occ_s1[1], GU_THREADS)
+                             : resident(dec1_gateup_kernel<false, GU_STAGE1, 4>, l1, occ_s1[0], GU_THREADS);
+    int g1 = std::max(1, (p.Ish + 7) / 8);
+    if (p.route) g1 = std::max(g1, std::min(ncu, (p.E * p.rnc + GU_WAVES - 1) / GU_WAVES));
+    p.s1_wg = std::min(g1, occ1 * ncu);
+    // stage 2: the routed gate/up (one LDS table per work-group) beside the
+    // shared down's rows (16 per work-group and round), split by cost per byte
+    const size_t l2 = lds_stage2();
+    const int wide = wide_select(p) ? 1 : 0;
+    int occ2;
+    if (p.x_f32) occ2 = wide ? resident(dec1_gateup_kernel<true, GU_STAGE2, 16>, l2, occ_s2[3], GU_THREADS)
+                             : resident(dec1_gateup_kernel<true, GU_STAGE2, 4>, l2, occ_s2[2], GU_THREADS);
+    else occ2 = wide ? resident(dec1_gateup_kernel<false, GU_STAGE2, 16>, l2, occ_s2[1], GU_THREADS)
+                     : resident(dec1_gateup_kernel<false, GU_STAGE2, 4>, l2, occ_s2[0], GU_THREADS);
+    const int G = occ2 * ncu, ntile = p.k * p.I / 128;
+    const int n_sd = p.Ish > 0 ? (p.H + GU_WAVES - 1) / GU_WAVES : 0;
+    int g_sd = 0, g_rt = 0;
+    split_roles(n_sd, (double)GU_WAVES * p.Ish * 2, p.nkc * ntile, S2_CB2_COST * 256.0 * DEC_LUT_KB * 38, G, g_sd, g_rt);
+    const int R = std::max(1, std::min(ntile, (g_rt + p.nkc / 2) / p.nkc));
+    p.s2_rt_wg = R * p.nkc;
+    p.s2_sd_wg = n_sd ? std::max(1, std::min(n_sd, G - p.s2_rt_wg)) : 0;
+    p.staged = 1;
+}
+
+hipError_t launch_dec_stage1(const DecPass &p, hipStream_t s)
+{
+    const size_t lds = lds_stage1(p.H, p.x_f32);
+    if (p.x_f32) dec1_gateup_kernel<true, GU_STAGE1, 4><<<p.s1_wg, GU_THREADS, lds, s>>>(p);
+    else dec1_gateup_kernel<false, GU_STAGE1, 4><<<p.s1_wg, GU_THREADS, lds, s>>>(p);
+    return hipGetLastError();
+}
+
+hipError_t launch_dec_stage2(const DecPass &p, hipStream_t s)
+{
+    const size_t lds = lds_stage2();
+    const int grid = p.s2_sd_wg + p.s2_rt_wg;
+    const bool wide = wide_select(p);
+    if (p.x_f32) {
+        if (wide) dec1_gateup_kernel<true, GU_STAGE2, 16><<<grid, GU_THREADS, lds, s>>>(p);
+        else dec1_gateup_kernel<true, GU_STAGE2, 4><<<grid, GU_THREADS, lds, s>>>(p);
+    } else {
+        if (wide) dec1_gateup_kernel<false, GU_STAGE2, 16><<<grid, GU_THREADS, lds, s>>>(p);
+        else dec1_gateup_kernel<false, GU_STAGE2, 4><<<grid, GU_THREADS, lds, s>>>(p);
+    }
     return hipGetLastError();
 }
 

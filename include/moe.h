@@ -99,7 +99,7 @@ enum moe_format { MOE_FMT_CB2 = 1, MOE_FMT_Q2K = 2, MOE_FMT_Q4K = 3, MOE_FMT_BF1
 enum moe_act { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 };
 
 /* workspace query paths */
-enum moe_path { MOE_PATH_ROUTE = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 };
+enum moe_path { MOE_PATH_ROUTE = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2, MOE_PATH_LAYER_DECODE = 3 };
 
 /* One MoE layer.  The struct itself lives in host memory; every pointer in
  * it is device memory.
@@ -116,12 +116,26 @@ enum moe_path { MOE_PATH_ROUTE = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2 };
  *     (then sh_* are ignored); sh_gate, sh_up: [sh_inter][H] bf16; sh_down:
  *     [H][sh_inter] bf16; sh_inter % 256 == 0 and H % 256 == 0 when present.
  *   w_router: fp32 [E][H].
+ *   flags: 0, or MOE_LAYER_TOKENWISE_DECODE: decode computes every token of a
+ *     batch with the single-token kernels, one token after another, so each
+ *     token's y is bit-identical to decoding it alone whatever batch it
+ *     arrives in -- the property the pages' serving layer holds batched
+ *     decode to ("Part 5: 服务层", section 6: a batched step returns exactly
+ *     what running each session alone returns) -- at the single-token cost
+ *     per token (about 60 us at H=7168, I=2048, k=8, against about 26 us per
+ *     token for a 32-token batch on the grouped GEMMs).  Without it, batches
+ *     of up to 4 tokens still run token by token and larger ones on the
+ *     grouped GEMMs, which agree with the single-token result to about 1e-6
+ *     relative, not bit for bit.  It needs a layer the single-token kernels
+ *     take (CB2 gate/up, Q2K down; see moe_expert_ffn_decode), otherwise
+ *     decode returns MOE_ERR_UNSUPPORTED.  Other bits: MOE_ERR_INVALID_ARG.
  *   Every pointer must be 16-byte aligned (device allocations are); the
  *   kernels read weights and the codebook in 8- and 16-byte pieces. */
+#define MOE_LAYER_TOKENWISE_DECODE 1
 typedef struct moe_layer {
     int32_t hidden, inter, n_experts, top_k;
     int32_t fmt_gate_up, fmt_down;
-    int32_t sh_inter, reserved0;
+    int32_t sh_inter, flags;
     const void *w_gate, *w_up, *w_down;
     const int8_t *codebook;
     const void *sh_gate, *sh_up, *sh_down;
@@ -199,6 +213,26 @@ int moe_expert_ffn_prefill(const moe_layer *L, const void *x, int act, int T,
                            const int32_t *topk_idx, const float *topk_w, const int32_t *offsets,
                            const int32_t *perm, const int32_t *inv, float *y,
                            void *ws, size_t ws_bytes, void *stream, moe_profile *prof);
+
+/* ------------------------------------------------------------ fused layer decode
+ * moe_layer_decode (+): moe_route followed by moe_expert_ffn_decode in one
+ * call, with the same arguments and outputs as the two (the routing outputs
+ * are written too) and one workspace of moe_workspace_bytes(L, T,
+ * MOE_PATH_LAYER_DECODE) bytes.  For one token of a layer the single-token
+ * decode kernels take (CB2 gate/up, Q2K down, H % 512 == 0, H <= 8192,
+ * I % 256 == 0, I <= 2048, sh_inter % 512 == 0, sh_inter <= 2048, k <= 8,
+ * E <= 1024), the router runs inside the FFN's launches: the first launch
+ * computes the fp64 partial logits beside the shared expert's gate/up, which
+ * does not depend on the routing, and every work-group of the routed gate/up
+ * launch selects the experts itself (the same arithmetic as moe_route, so
+ * the routing and y are bit-identical to the two separate calls).  Four
+ * launches instead of six: decode reads every weight once per token while
+ * compute idles, so the shorter chain of dependent launches is what it buys
+ * ("Part 5: 服务层", section 6).  Otherwise it runs moe_route and
+ * moe_expert_ffn_decode.  Errors as in those two. */
+int moe_layer_decode(const moe_layer *L, const void *x, int act, int T, const float *bias, int32_t *topk_idx,
+                     float *topk_w, int32_t *offsets, int32_t *perm, int32_t *inv, float *y, void *ws,
+                     size_t ws_bytes, void *stream, moe_profile *prof);
 
 /* ------------------------------------------------------------ no-allocation decode
  * moe_expert_ffn_decode_noalloc: for callers that cannot allocate device

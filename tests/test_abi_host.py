@@ -37,7 +37,7 @@ def test_exports_every_declared_function():
 
 
 def _layer(**kw):
-    base = dict(hidden=256, inter=128, n_experts=8, top_k=2, fmt_gate_up=1, fmt_down=2, sh_inter=0, reserved0=0,
+    base = dict(hidden=256, inter=128, n_experts=8, top_k=2, fmt_gate_up=1, fmt_down=2, sh_inter=0, flags=0,
                 w_gate=FAKE, w_up=FAKE, w_down=FAKE, codebook=FAKE, sh_gate=None, sh_up=None, sh_down=None,
                 w_router=FAKE)
     base.update(kw)
@@ -81,6 +81,18 @@ def test_route_validation_misc():
 def test_ffn_validation(kw, code):
     for fn in (M.lib().moe_expert_ffn_decode, M.lib().moe_expert_ffn_prefill):
         assert _ffn(fn, _layer(**kw)) == code
+
+
+def test_tokenwise_flag_validation():
+    dec, pre = M.lib().moe_expert_ffn_decode, M.lib().moe_expert_ffn_prefill
+    for fn in (dec, pre):
+        assert _ffn(fn, _layer(flags=2)) == -1                 # unknown bits
+        assert b"flags" in M.lib().moe_last_error()
+    assert _route(_layer(flags=2, w_router=FAKE), ws_bytes=10) == -3   # the router does not read the flags
+    # token by token needs the single-token kernels; H = 256 is not a multiple of 512
+    assert _ffn(dec, _layer(flags=M.LAYER_TOKENWISE_DECODE)) == -2
+    assert b"token-by-token" in M.lib().moe_last_error()
+    assert _ffn(dec, _layer(flags=M.LAYER_TOKENWISE_DECODE, fmt_gate_up=3, fmt_down=3)) == -2
 
 
 def test_ffn_validation_misc():
@@ -130,6 +142,25 @@ def test_pack_sets_last_error():
     assert b"codebook" in M.lib().moe_last_error()
     assert P(2, w.ctypes.data, -1, 256, None, o.ctypes.data) == -1
     assert P(2, None, 2, 256, None, o.ctypes.data) == -1
+
+
+def test_layer_decode_validation():
+    F_ = M.lib().moe_layer_decode
+    call = lambda L, T=4, act=1, ws_bytes=1 << 30, ws=FAKE, out=FAKE, x=FAKE: F_(
+        ctypes.byref(L) if L is not None else None, x, act, T, None, out, out, out, out, out, out, ws, ws_bytes, None,
+        None)
+    L = _layer()
+    assert call(None) == -1
+    assert call(_layer(top_k=0)) == -1
+    assert call(L, T=-1) == -1
+    assert call(L, act=5) == -1
+    assert call(L, out=None) == -1
+    assert call(L, ws=None) == -1
+    assert call(L, x=FAKE + 4) == -1
+    assert call(L, ws_bytes=64) == -3
+    assert call(L, T=0, ws=None, out=None) == 0
+    need = M.workspace_bytes(L, 4, M.PATH_LAYER_DECODE)
+    assert need >= M.workspace_bytes(L, 4, M.PATH_ROUTE) + M.workspace_bytes(L, 4, M.PATH_DECODE)
 
 
 def test_unpack_validation():

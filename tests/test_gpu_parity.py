@@ -399,6 +399,34 @@ def test_full_decode_tokenwise_bit_identical(big):
         assert np.array_equal(y1[0].view(np.uint32), yb[t].view(np.uint32)), t
 
 
+def test_full_decode_tokenwise_flag(big):
+    """With the layer's token-by-token flag every decode batch runs the
+    single-token kernels, so all 32 tokens of the full-size decode batch come
+    out bit-identical to the same tokens in batches of 1, 3 and 8 (the pages
+    require batched decode to return exactly what each session alone would --
+    "Part 5: serving layer", section 6), and still match the oracle."""
+    cfg = S.config("decode32")
+    x, act, r = run_route(big, cfg)
+    T, k, E = x.shape[0], cfg["top_k"], cfg["n_experts"]
+    big.layer.c.flags = M.LAYER_TOKENWISE_DECODE
+    try:
+        y = run_ffn(big, x, act, r, decode=True)
+        for B in (1, 3, 8):
+            for t0 in range(0, T - B + 1, max(B, 5)):
+                xt = x[t0:t0 + B].contiguous()
+                rb = M.Routing(B, k, E)
+                M.route(big.layer, xt, act, B, big.bias(cfg), rb, big.layer.workspace(B, M.PATH_ROUTE))
+                yb = run_ffn(big, xt, act, rb, decode=True)
+                assert np.array_equal(yb.view(np.uint32), y[t0:t0 + B].view(np.uint32)), (B, t0)
+    finally:
+        big.layer.c.flags = 0
+    xf, idx, w, l, off, perm, inv = oracle_routing(cfg)
+    toks = np.array([0, 7, 19, 31])
+    yref = R.moe_layer(xf[toks], idx[toks], w[toks], expert_loader(cfg, big.packed), oracle_shared(cfg),
+                       threads=ORACLE_THREADS)
+    assert rel_l2(y[toks], yref) <= DEC_TOL
+
+
 def test_full_decode32_q4k(big_q4k):
     assert sampled_check(big_q4k, S.config("decode32_q4k"), True, 8) <= DEC_TOL
 
@@ -546,3 +574,60 @@ def test_layer_recipe_stack(recipe):
         assert err <= DEC_TOL
         x_dev, act = y, M.ACT_F32
         x_ref = yref.astype(np.float32)
+
+
+# ------------------------------------------------------------------ fused layer decode
+def run_layer_decode(wl, cfg, T=None):
+    x, act = wl.tokens(cfg, T)
+    T = x.shape[0]
+    r = M.Routing(T, wl.cfg["top_k"], wl.cfg["n_experts"])
+    y = torch.full((T, wl.cfg["hidden"]), float("nan"), device="cuda")
+    M.layer_decode(wl.layer, x, act, T, wl.bias(cfg), r, y, wl.layer.workspace(T, M.PATH_LAYER_DECODE))
+    torch.cuda.synchronize()
+    return r, y.cpu().numpy()
+
+
+LAYER = [c for c in SMALL if c[0].startswith("one_T1") or c[0] in ("mid_T1", "gemm_T37", "tiny")] + [
+    ("one_T1_skew", mid(1, 48, hidden=1024, inter=512, sh_inter=512, skew=True)),
+    ("one_T1_E300", mid(1, 49, hidden=1024, inter=512, sh_inter=512, n_experts=300, top_k=8)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", LAYER, ids=[n for n, _ in LAYER])
+def test_layer_decode(small_cases, name, cfg):
+    """moe_layer_decode: the routing outputs equal the oracle's, y is within the
+    decode bar, and both are bit-identical to moe_route + moe_expert_ffn_decode
+    (single tokens run the router inside the FFN's launches; other cases the
+    two calls)."""
+    wl, yref, routing = _case(small_cases, name, cfg)
+    r, y = run_layer_decode(wl, cfg)
+    check_route(r, *routing)
+    err = rel_l2(y, yref)
+    print("[layer] %s rel_l2=%.3e" % (name, err))
+    assert err <= DEC_TOL
+    x2, act2, r2 = run_route(wl, cfg)
+    y2 = run_ffn(wl, x2, act2, r2, decode=True)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    for a, b in ((r.topk_idx, r2.topk_idx), (r.topk_w, r2.topk_w), (r.offsets, r2.offsets), (r.perm, r2.perm),
+                 (r.inv, r2.inv)):
+        assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("wname", ["decode1", "decode32_T1"])
+def test_full_layer_decode(big, wname):
+    """The fused single-token layer at the full layer shape (with the Zipf bias
+    for decode32's first token): routing in full and y against the oracle, and
+    bit-identical to the two separate calls, also on a reused workspace."""
+    cfg = S.config("decode1") if wname == "decode1" else S.config("decode32", T=1)
+    r, y = run_layer_decode(big, cfg)
+    xf, idx, w, l, off, perm, inv = oracle_routing(cfg)
+    check_route(r, idx, w, off, perm, inv)
+    yref = R.moe_layer(xf, idx, w, expert_loader(cfg, big.packed), oracle_shared(cfg), threads=ORACLE_THREADS)
+    err = rel_l2(y, yref)
+    print("[layer] %s rel_l2=%.3e" % (wname, err))
+    assert err <= DEC_TOL
+    x2, act2, r2 = run_route(big, cfg)
+    y2 = run_ffn(big, x2, act2, r2, decode=True)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    r3, y3 = run_layer_decode(big, cfg)
+    assert np.array_equal(y.view(np.uint32), y3.view(np.uint32))
