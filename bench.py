@@ -40,8 +40,32 @@ def log(msg):
 
 
 # sources that define each timed kernel (plus the shared headers)
-_KERNEL_SOURCES = {"dec_": ["decode.hip", "decode.h", "route_dev.h"], "route_": ["route.hip", "route_dev.h"], "ffn_prefill_": ["prefill.hip", "ffn.hip"],
-                   "ffn_schedule": ["ffn.hip"], "combine": ["ffn.hip"]}
+_KERNEL_SOURCES = {"dec_": ["decode.hip", "decode.h", "route_dev.h"], "route_": ["route.hip", "route_dev.h"],
+                   "ffn_prefill_": ["prefill.hip", "ffn.hip"], "ffn_decode_": ["prefill.hip", "ffn.hip"],
+                   "ffn_schedule": ["ffn.hip"], "sh_finalize": ["ffn.hip"], "combine": ["ffn.hip"]}
+
+# the library's launch names (moe_profile.name) and the GPU kernel symbols each one runs
+LAUNCH_SYMBOLS = [
+    ("dec_stage1", r"dec1_gateup_kernel<(?:true|false), 1,"),
+    ("dec_stage2", r"dec1_gateup_kernel<(?:true|false), 2,"),
+    ("dec_hform", r"dec1_hform_kernel"),
+    ("dec_down_fused", r"dec1_down_fused_kernel"),
+    ("ffn_decode_gateup", r"np_kernel<\d+, true, true,"),
+    ("ffn_decode_down", r"np_kernel<\d+, false, true,"),
+    ("ffn_prefill_gateup", r"np_kernel<\d+, true, false,"),
+    ("ffn_prefill_down", r"np_kernel<\d+, false, false,"),
+    ("ffn_schedule", r"moe::ffn_schedule\("),
+    ("sh_finalize", r"sh_finalize_kernel"),
+    ("combine", r"moe::combine_kernel"),
+    ("route_logits", r"route_logits_(?:small|tiled|mfma)"),
+    ("route_partial", r"route_partial<"),
+    ("route_select", r"route_select_(?:one|tok)[<(]"),
+    ("route_select_small", r"route_select_small"),
+    ("route_topk", r"route_topk<"),
+    ("route_rank", r"route_rank\("),
+    ("route_scan", r"route_scan\("),
+    ("route_scatter", r"route_scatter\("),
+]
 
 
 def kernel_source_hash(kernel: str | None = None) -> str:
@@ -351,32 +375,140 @@ def cpu_baseline(cfg, n_tok):
 
 
 # ------------------------------------------------------------------ traffic (rocprofv3 --pmc)
-def read_traffic(kernel, workload):
-    """Per-launch HBM bytes from the committed counter summary, if it was taken
-    on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.md" % (kernel, workload))
+def _profile_value(path, key, kernel):
+    """`key <kernel>: <value> sources <hash>` from a committed profile summary,
+    if that hash is the one of the kernel's current sources."""
     if not os.path.exists(path):
         return None
-    txt = open(path).read()
-    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    h = re.search(r"kernel_source_hash:\s*(\w+)", txt)
-    if not m or not h or h.group(1) != kernel_source_hash(kernel):
+    m = re.search(r"^%s %s:\s*([0-9.eE+]+)\s+sources\s+(\w+)" % (key, re.escape(kernel)), open(path).read(), re.M)
+    if not m or m.group(2) != kernel_source_hash(kernel):
         return None
     return float(m.group(1))
 
 
+def read_traffic(kernel, workload):
+    """Per-launch HBM bytes (read + write) from the committed counter summary."""
+    return _profile_value(os.path.join(ROOT, "profiles", "%s_traffic.md" % workload), "traffic_bytes_per_launch", kernel)
+
+
 def read_trace_avg(kernel, workload):
-    """Average kernel execution time (ms) from the committed rocprofv3 kernel
-    trace of the workload, if it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", "%s_kernel_trace.md" % workload)
-    if not os.path.exists(path):
-        return None
-    txt = open(path).read()
-    m = re.search(r"trace_avg_us %s:\s*([0-9.eE+]+)" % re.escape(kernel), txt)
-    h = re.search(r"kernel_source_hash:?\s*(\w+)", txt)
-    if not m or not h or h.group(1) != kernel_source_hash():
-        return None
-    return float(m.group(1)) * 1e-3
+    """Average kernel execution time (ms) from the committed rocprofv3 kernel trace."""
+    us = _profile_value(os.path.join(ROOT, "profiles", "%s_kernel_trace.md" % workload), "trace_avg_us", kernel)
+    return us * 1e-3 if us is not None else None
+
+
+# ------------------------------------------------------------------ rocprofv3 summaries
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit("no *%s under %s" % (suffix, d))
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _launch_of(symbol):
+    for launch, pat in LAUNCH_SYMBOLS:
+        if re.search(pat, symbol):
+            return launch
+    return None
+
+
+def _command_text(cmd):
+    """The command with the repository root (wherever it was run) written as $R."""
+    return re.sub(r"(?:/[^\s/]+)*/repo(?=/(?:gpurun_out|bench\.py))", "$R", cmd.replace(ROOT, "$R"))
+
+
+def summarize_trace(workload, d, cmd):
+    """Markdown summary of a `rocprofv3 --kernel-trace --output-format csv` run:
+    per-kernel count / mean / median / min / max of the dispatch durations and,
+    per library launch, the mean in the form `bench.py` reads back."""
+    import statistics as st
+    by = {}
+    for r in _csv_rows(d, "kernel_trace.csv"):
+        by.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in by.values())
+    out = ["# Kernel trace: %s" % workload, "",
+           "Command (from the repository root R on the MI355X; the summary below is the second line's output):", "",
+           "```", _command_text(cmd), "python3 $R/bench.py --summarize-trace %s <the -d folder> '<the first line>'" % workload,
+           "```", "",
+           "| kernel | launch | calls | total (us) | mean (us) | median (us) | min (us) | max (us) | share |",
+           "|---|---|---:|---:|---:|---:|---:|---:|---:|"]
+    per_launch = {}
+    for name, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        launch = _launch_of(name)
+        if launch:
+            per_launch.setdefault(launch, []).extend(v)
+        out.append("| `%s` | %s | %d | %.1f | %.2f | %.2f | %.2f | %.2f | %.1f%% |" % (
+            name[:150], launch or "", len(v), sum(v), st.mean(v), st.median(v), min(v), max(v), 100 * sum(v) / total))
+    out += ["", "Per library launch (mean over its dispatches; the hash is that of the kernel's sources):", ""]
+    for launch, v in per_launch.items():
+        out.append("trace_avg_us %s: %.3f sources %s" % (launch, st.mean(v), kernel_source_hash(launch)))
+    print("\n".join(out))
+
+
+def summarize_counters(workload, copy_fetch, copy_write, fetch, write, cmds):
+    """Markdown summary of two `rocprofv3 --pmc` runs of a workload (FETCH_SIZE,
+    then WRITE_SIZE, in KiB per dispatch) scaled by what the same counters read
+    for a device copy of known size, per library launch."""
+    import statistics as st
+
+    def per_kernel(d, counter):
+        acc = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+        by = {}
+        for (_, name), v in acc.items():
+            by.setdefault(name, []).append(v)
+        return by
+
+    def copy_kib(d, counter):
+        by = per_kernel(d, counter)
+        big = max(by, key=lambda n: st.mean(by[n]))          # the 1 GiB copy is the largest dispatch
+        return st.mean(by[big]), big
+
+    cf, cname = copy_kib(copy_fetch, "FETCH_SIZE")
+    cw, _ = copy_kib(copy_write, "WRITE_SIZE")
+    gib = float(1 << 30)
+    fscale, wscale = gib / (cf * 1024), gib / (cw * 1024)
+    fb, wb = per_kernel(fetch, "FETCH_SIZE"), per_kernel(write, "WRITE_SIZE")
+    out = ["# HBM traffic per launch: %s" % workload, "",
+           "Counters from two `rocprofv3 --pmc` runs of the workload (one counter per run) and two of a",
+           "1 GiB device copy, each counter's KiB per dispatch scaled by copy bytes / counted bytes.",
+           "Commands (from the repository root R on the MI355X; the summary is the last line's output):", "",
+           "```"] + [_command_text(c) for c in cmds] + [
+           "python3 $R/bench.py --summarize-counters %s <the four -d folders, in this order>" % workload, "```", "",
+           "| quantity | value |", "|---|---:|",
+           "| copy kernel | `%s` |" % cname[:80],
+           "| copy: FETCH_SIZE KiB per 1 GiB read | %.1f |" % cf,
+           "| copy: WRITE_SIZE KiB per 1 GiB written | %.1f |" % cw,
+           "| fetch scale (bytes per counted byte) | %.4f |" % fscale,
+           "| write scale | %.4f |" % wscale, "",
+           "| kernel | launch | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes (scaled) | write bytes (scaled) |",
+           "|---|---|---:|---:|---:|---:|---:|"]
+    per_launch = {}
+    for name in sorted(set(fb) | set(wb), key=lambda n: -st.mean(fb.get(n, [0.0]))):
+        f = st.mean(fb[name]) if name in fb else 0.0
+        w = st.mean(wb[name]) if name in wb else 0.0
+        launch = _launch_of(name)
+        rb, wbytes = f * 1024 * fscale, w * 1024 * wscale
+        if launch:
+            per_launch.setdefault(launch, []).append((rb, wbytes, len(fb.get(name, []))))
+        out.append("| `%s` | %s | %d | %.1f | %.1f | %.0f | %.0f |" % (
+            name[:120], launch or "", len(fb.get(name, [])), f, w, rb, wbytes))
+    out += ["", "Per library launch (read + write bytes; the hash is that of the kernel's sources):", ""]
+    for launch, v in per_launch.items():
+        n = sum(c for _, _, c in v) or 1
+        tot = sum((r + w) * c for r, w, c in v) / n
+        out.append("traffic_bytes_per_launch %s: %.0f sources %s" % (launch, tot, kernel_source_hash(launch)))
+    print("\n".join(out))
 
 
 SWEEP_T = (1, 2, 4, 8, 16, 24, 32, 48, 64)
@@ -458,6 +590,8 @@ def measure(wl, cfg, name, steps, warmup, with_cpu):
         roof = {"bound": "hbm", "kernel": dom_name, "achieved": round(ach, 1) if ach else None,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4) if ach else None,
                 "traffic": read_traffic(dom_name, name), "algorithmic_bytes": kb, "avg_launch_ms": round(kms, 5)}
+        if roof["traffic"] and kb:
+            roof["traffic_ratio"] = round(roof["traffic"] / kb, 3)
         if trace_ms and kb:
             roof["trace_avg_ms"] = trace_ms
             roof["achieved_trace"] = round(kb / (trace_ms * 1e-3) / 1e9, 1)
@@ -505,7 +639,19 @@ def main():
                          "(Zipf-skewed routing), with the crossover T; one JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy 5 times (counter calibration under rocprofv3)")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("WORKLOAD", "DIR", "COMMAND"),
+                    help="only print the markdown summary of a rocprofv3 --kernel-trace csv run (no GPU)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="ARG",
+                    help="only print the markdown traffic summary: WORKLOAD COPY_FETCH_DIR COPY_WRITE_DIR "
+                         "FETCH_DIR WRITE_DIR COMMAND... (no GPU)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_counters:
+        a = args.summarize_counters
+        summarize_counters(a[0], a[1], a[2], a[3], a[4], a[5:])
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the layer's multi-GPU sharding is a design, not "
               "built); run with --gpus 1", file=sys.stderr)
