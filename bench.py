@@ -337,7 +337,7 @@ def cpu_baseline(cfg, n_tok):
     xf = S.bf16_to_f32(x) if kind == "bf16" else x
     wr, b = S.router_weight(cfg), S.logit_bias(cfg)
     idx0, _, _ = R.route(xf, wr, cfg["top_k"], b)
-    cb = S.codebook()
+    cb = S.codebook_for(cfg["fmt_gate_up"])
     H, I = cfg["hidden"], cfg["inter"]
 
     def pack(e):

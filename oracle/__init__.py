@@ -44,7 +44,8 @@ def lib():
     """The loaded reference-quantizer library (built on first use if absent)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        src = os.path.join(_HERE, "quant_ref.c")
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
             build_oracle_lib()
         L = ctypes.CDLL(_LIB_PATH)
         L.ref_quant_rows.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,

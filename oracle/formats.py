@@ -11,6 +11,12 @@ this project's own (see quant_ref.c for the byte map).  Blocks hold 256
 consecutive weights of one row; a row of K weights occupies ceil(K/256)
 blocks (zero padded).
 
+CB2S is the signed variant of the 2-bit codebook format, sized like the
+pages' IQ2_XXS (66 bytes per 256 weights): per group of 8 weights an index
+into a grid of non-negative magnitudes plus seven sign flags, the eighth sign
+being fixed by even parity (the pages name IQ2_XXS but print neither its
+grid nor its layout; grid, layout and quantizer here are this project's own).
+
 Dequantization is exact in fp32: every product d*s*C, d*sc*q, dmin*m needs at
 most 24 significant bits (Q6_K: 11 + 7 + 6), so the only rounding is the
 single subtraction of the min term (round-to-nearest-even, as numpy float32
@@ -27,9 +33,9 @@ import numpy as np
 
 from . import lib
 
-CB2, Q2K, Q4K, BF16, Q5K, Q6K = 1, 2, 3, 4, 5, 6
+CB2, Q2K, Q4K, BF16, Q5K, Q6K, CB2S = 1, 2, 3, 4, 5, 6, 7
 QK = 256
-BLOCK_BYTES = {CB2: 38, Q2K: 84, Q4K: 144, Q5K: 176, Q6K: 210}
+BLOCK_BYTES = {CB2: 38, Q2K: 84, Q4K: 144, Q5K: 176, Q6K: 210, CB2S: 66}
 
 
 def n_blocks(K: int) -> int:
@@ -56,10 +62,10 @@ def pack(fmt: int, w: np.ndarray, codebook: np.ndarray | None = None,
     w = np.ascontiguousarray(w, dtype=np.float32)
     rows, K = w.shape
     out = np.zeros(packed_bytes(fmt, rows, K), dtype=np.uint8)
-    if fmt == CB2:
+    if fmt in (CB2, CB2S):
         if codebook is None:
-            raise ValueError("CB2 needs a codebook")
-        cb = np.ascontiguousarray(codebook, dtype=np.int8)
+            raise ValueError("CB2 and CB2S need a codebook (CB2S: the magnitude grid)")
+        cb = np.ascontiguousarray(codebook, dtype=np.int8 if fmt == CB2 else np.uint8)
         cb_ptr = cb.ctypes.data
     else:
         cb = None
@@ -90,6 +96,7 @@ def fields(fmt: int, packed: np.ndarray, rows: int, K: int) -> dict:
     """Parse packed blocks into their integer/fp16 fields.
 
     CB2 : d [r,nb], s [r,nb,8], idx [r,nb,32]
+    CB2S: d [r,nb], s [r,nb,8], idx [r,nb,32], neg [r,nb,32,8] (0/1, parity filled in)
     Q2_K: d, dmin [r,nb], sc, m [r,nb,16], q [r,nb,256]
     Q4_K, Q5_K: d, dmin [r,nb], sc, m [r,nb,8],  q [r,nb,256]
     Q6_K: d [r,nb], sc [r,nb,16] (signed), q [r,nb,256] (-32..31)
@@ -102,6 +109,17 @@ def fields(fmt: int, packed: np.ndarray, rows: int, K: int) -> dict:
         u = np.stack([(lo >> (4 * t)) & 0xF for t in range(2)], axis=-1).reshape(rows, nb, QK)
         u = u | (np.stack([(hi >> (2 * t)) & 3 for t in range(4)], axis=-1).reshape(rows, nb, QK) << 4)
         return dict(d=_f16(blk[..., 0:2]), sc=blk[..., 2:18].view(np.int8).astype(np.int32), q=u - 32)
+    if fmt == CB2S:
+        rec = blk[..., 2:66].reshape(rows, nb, 8, 8)                     # eight 8-byte sub-block records
+        word = rec[..., 4:8].astype(np.int64)
+        word = word[..., 0] | (word[..., 1] << 8) | (word[..., 2] << 16) | (word[..., 3] << 24)
+        neg = np.zeros((rows, nb, 8, 4, 8), np.int32)
+        for u in range(4):
+            for i in range(7):
+                neg[..., u, i] = (word >> (7 * u + i)) & 1
+        neg[..., 7] = neg[..., :7].sum(axis=-1) & 1                      # even count of negatives
+        return dict(d=_f16(blk[..., 0:2]), s=(word >> 28).astype(np.int32),
+                    idx=rec[..., 0:4].reshape(rows, nb, 32).astype(np.int32), neg=neg.reshape(rows, nb, 32, 8))
     if fmt == CB2:
         sb = blk[..., 2:6].astype(np.int32)
         s = np.empty((rows, nb, 8), np.int32)
@@ -142,6 +160,12 @@ def unpack(fmt: int, packed: np.ndarray, rows: int, K: int,
         step = F["d"][..., None] * F["s"].astype(np.float32)             # [r,nb,8]
         step_g = np.repeat(step, 4, axis=-1)                             # group g -> sub-block g//4
         w = step_g[..., None] * C[F["idx"]]                              # [r,nb,32,8]
+    elif fmt == CB2S:
+        G = np.asarray(codebook, dtype=np.uint8).astype(np.float32)      # [256, 8] magnitudes
+        step = F["d"][..., None] * F["s"].astype(np.float32)             # [r,nb,8], exact
+        step_g = np.repeat(step, 4, axis=-1)
+        sgn = 1.0 - 2.0 * F["neg"].astype(np.float32)                    # [r,nb,32,8]
+        w = step_g[..., None] * (sgn * G[F["idx"]])                      # exact (<= 18 bits)
     elif fmt == Q6K:
         mul = F["d"][..., None] * F["sc"].astype(np.float32)             # [r,nb,16], exact
         w = np.repeat(mul, 16, axis=-1) * F["q"].astype(np.float32)      # exact (<= 24 bits)

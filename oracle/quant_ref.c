@@ -15,6 +15,15 @@
  *   CB2  38 B: [0:2) fp16 d | [2:6) eight 4-bit sub-block scales s_j (s_j in
  *        bits 4*(j%2).. of byte 2+j/2) | [6:38) 32 codebook indices, one per
  *        group of 8 weights.  w[8g+i] = d * s_{g/4} * C[idx_g][i].
+ *   CB2S 66 B (the signed codebook format, 2.0625 bits per weight, the byte
+ *        budget of the pages' IQ2_XXS): [0:2) fp16 d | eight 8-byte sub-block
+ *        records at [2+8j, 10+8j): bytes 0..3 the grid indices of groups
+ *        4j..4j+3, bytes 4..7 a little-endian word holding, for group 4j+u,
+ *        the negative-sign flags of its weights 0..6 at bits 7u..7u+6 and
+ *        s_j at bits 28..31.  Weight 7's flag is the parity of the other
+ *        seven (every group has an even number of negative weights).  The
+ *        grid G holds non-negative magnitudes.
+ *        w[8g+i] = d * s_{g/4} * (-1)^{neg_gi} * G[idx_g][i].
  *   Q2_K 84 B: [0:2) fp16 d | [2:4) fp16 dmin | [4:20) byte j = sc_j | m_j<<4
  *        (16 sub-blocks of 16) | [20:84) 2-bit q_i in bits 2*(i%4) of byte i/4.
  *        w_i = d*sc_j*q_i - dmin*m_j, j = i/16.
@@ -304,14 +313,91 @@ void ref_quant_cb2_row(const float *w, int K, const int8_t *cb, uint8_t *out)
     free(buf);
 }
 
+/* ------------------------------------------------------------------- CB2S
+ * Per sub-block j: sigma_j = max|w| / 5 (5 is the grid's largest magnitude);
+ * d and s_j as for CB2.  Per group of 8 with step = d*s_j > 0: the magnitude
+ * targets a_i = rint(|w_i| / step * 4096) (int32) and the natural signs
+ * neg_i = (w_i < 0).  For grid entry c the cost is the integer distance
+ * sum_i (a_i - 4096*G[c][i])^2; when the number of negative weights is odd,
+ * one sign must flip, and flipping weight p adds 4 * a_p * 4096*G[c][p], so
+ * the cheapest p (lowest on ties) is added to c's cost.  The chosen entry
+ * has the lowest cost (lowest index on ties) and its flip, if any, is
+ * applied.  A zero step gives index 0 and no negative flags. */
+void ref_quant_cb2s_row(const float *w, int K, const uint8_t *grid, uint8_t *out)
+{
+    int nb = (K + QK - 1) / QK;
+    float *buf = (float *)malloc(sizeof(float) * (size_t)nb * QK);
+    padded_row(w, K, nb, buf);
+    for (int b = 0; b < nb; ++b) {
+        const float *x = buf + (size_t)b * QK;
+        float sigma[8], max_sigma = 0.0f;
+        for (int j = 0; j < 8; ++j) {
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                float a = fabsf(x[32 * j + i]);
+                if (a > amax) amax = a;
+            }
+            sigma[j] = amax / 5.0f;
+            if (sigma[j] > max_sigma) max_sigma = sigma[j];
+        }
+        uint16_t db = ref_f32_to_f16_bits(max_sigma / 15.0f);
+        float d = ref_f16_bits_to_f32(db);
+        uint8_t *p = out + (size_t)b * 66;
+        memset(p, 0, 66);
+        put_f16(p, db);
+        for (int j = 0; j < 8; ++j) {
+            int s = d > 0.0f ? clampi((int)rintf(sigma[j] / d), 0, 15) : 0;
+            float step = d * (float)s;
+            uint32_t word = (uint32_t)s << 28;
+            for (int u = 0; u < 4; ++u) {
+                int g = 4 * j + u;
+                int best = 0, neg[8] = {0};
+                if (step > 0.0f) {
+                    int64_t a[8];
+                    int nneg = 0;
+                    for (int i = 0; i < 8; ++i) {
+                        a[i] = (int64_t)rintf(fabsf(x[8 * g + i]) / step * 4096.0f);
+                        neg[i] = x[8 * g + i] < 0.0f;
+                        nneg += neg[i];
+                    }
+                    int64_t best_cost = -1;
+                    int best_flip = -1;
+                    for (int c = 0; c < 256; ++c) {
+                        int64_t cost = 0;
+                        for (int i = 0; i < 8; ++i) {
+                            int64_t diff = a[i] - 4096 * (int64_t)grid[8 * c + i];
+                            cost += diff * diff;
+                        }
+                        int flip = -1;
+                        if (nneg & 1) {
+                            int64_t fc = -1;
+                            for (int i = 0; i < 8; ++i) {
+                                int64_t f = 4 * a[i] * 4096 * (int64_t)grid[8 * c + i];
+                                if (fc < 0 || f < fc) { fc = f; flip = i; }
+                            }
+                            cost += fc;
+                        }
+                        if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = c; best_flip = flip; }
+                    }
+                    if (best_flip >= 0) neg[best_flip] ^= 1;
+                }
+                p[2 + 8 * j + u] = (uint8_t)best;
+                for (int i = 0; i < 7; ++i) word |= (uint32_t)neg[i] << (7 * u + i);
+            }
+            for (int t = 0; t < 4; ++t) p[2 + 8 * j + 4 + t] = (uint8_t)(word >> (8 * t));
+        }
+    }
+    free(buf);
+}
+
 /* Quantize rows [r0, r1) of a row-major [rows][K] matrix into the packed
  * output (row r occupies nb*block_bytes bytes at r*nb*block_bytes).
- * fmt: 1 = CB2, 2 = Q2_K, 3 = Q4_K, 5 = Q5_K, 6 = Q6_K.  Returns 0 on
- * success, -1 on a bad fmt. */
+ * fmt: 1 = CB2, 2 = Q2_K, 3 = Q4_K, 5 = Q5_K, 6 = Q6_K, 7 = CB2S (cb is then
+ * the uint8 magnitude grid).  Returns 0 on success, -1 on a bad fmt. */
 int ref_quant_rows(int fmt, const float *w, int64_t r0, int64_t r1, int K, const int8_t *cb, uint8_t *out)
 {
     int nb = (K + QK - 1) / QK;
-    int bb = fmt == 1 ? 38 : fmt == 2 ? 84 : fmt == 3 ? 144 : fmt == 5 ? 176 : fmt == 6 ? 210 : 0;
+    int bb = fmt == 1 ? 38 : fmt == 2 ? 84 : fmt == 3 ? 144 : fmt == 5 ? 176 : fmt == 6 ? 210 : fmt == 7 ? 66 : 0;
     if (!bb) return -1;
     for (int64_t r = r0; r < r1; ++r) {
         const float *row = w + r * (int64_t)K;
@@ -320,6 +406,7 @@ int ref_quant_rows(int fmt, const float *w, int64_t r0, int64_t r1, int K, const
         else if (fmt == 2) ref_quant_q2k_row(row, K, o);
         else if (fmt == 3) ref_quant_q4k_row(row, K, o);
         else if (fmt == 5) ref_quant_q5k_row(row, K, o);
+        else if (fmt == 7) ref_quant_cb2s_row(row, K, (const uint8_t *)cb, o);
         else ref_quant_q6k_row(row, K, o);
     }
     return 0;

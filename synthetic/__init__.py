@@ -16,6 +16,8 @@ no shapes, so the shapes are the stated workload definitions):
   prefill8192  same layer                 T=8192  Zipf-skewed logits
   prefill8192_q4k  as prefill8192 with all three routed projections in Q4_K
   decode32_q4k     as decode32 with all three routed projections in Q4_K
+  prefill2048_cb2s, decode32_cb2s  as prefill2048 / decode32 with gate/up in
+                   the signed codebook format (66 B per 256 weights)
 
 Every tensor comes from its own child stream of one layer seed
 (``numpy.random.default_rng([seed, tag, index])``), so one expert can be
@@ -38,8 +40,9 @@ _TAG_SHARED = 4
 _TAG_ROUTER = 5
 _TAG_CODEBOOK = 6
 _TAG_TOKENS = 7
+_TAG_GRID = 8
 
-FMT_CB2, FMT_Q2K, FMT_Q4K, FMT_BF16, FMT_Q5K, FMT_Q6K = 1, 2, 3, 4, 5, 6
+FMT_CB2, FMT_Q2K, FMT_Q4K, FMT_BF16, FMT_Q5K, FMT_Q6K, FMT_CB2S = 1, 2, 3, 4, 5, 6, 7
 
 _BIG = dict(hidden=7168, inter=2048, n_experts=256, top_k=8, sh_inter=2048)
 
@@ -59,6 +62,10 @@ CONFIGS = {
                             fmt_gate_up=FMT_Q4K, fmt_down=FMT_Q4K, index=4),
     "decode32_q4k": dict(_BIG, T=32, x_dtype="bf16", skew=True,
                          fmt_gate_up=FMT_Q4K, fmt_down=FMT_Q4K, index=4),
+    "prefill2048_cb2s": dict(_BIG, T=2048, x_dtype="bf16", skew=False,
+                             fmt_gate_up=FMT_CB2S, fmt_down=FMT_Q2K, index=3),
+    "decode32_cb2s": dict(_BIG, T=32, x_dtype="bf16", skew=True,
+                          fmt_gate_up=FMT_CB2S, fmt_down=FMT_Q2K, index=2),
 }
 
 _GOLDEN = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
@@ -71,8 +78,9 @@ _GOLDEN = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__)
 # mirror, section on model weights: q2 with the last six layers in q4; a stack
 # shorter than 12 layers keeps its last half in Q4_K); "q4" is Q4_K throughout;
 # "q5-q6" is the wider routed mix the "ds4" mirror lists for other models
-# (gate/up Q5_K, down Q6_K).
-RECIPES = ("q2", "q2-q4", "q4", "q5-q6")
+# (gate/up Q5_K, down Q6_K); "q2s" is "q2" with gate/up in the signed codebook
+# format, the byte budget of the pages' 2-bit gate/up type.
+RECIPES = ("q2", "q2-q4", "q4", "q5-q6", "q2s")
 
 
 def layer_formats(recipe: str, layer: int, n_layers: int) -> tuple:
@@ -84,6 +92,8 @@ def layer_formats(recipe: str, layer: int, n_layers: int) -> tuple:
         return FMT_Q4K, FMT_Q4K
     if recipe == "q5-q6":
         return FMT_Q5K, FMT_Q6K
+    if recipe == "q2s":
+        return FMT_CB2S, FMT_Q2K
     raise ValueError("unknown recipe %r" % recipe)
 
 
@@ -115,6 +125,33 @@ def codebook(seed: int = LAYER_SEED) -> np.ndarray:
         out[i] = row
         i += 1
     return out
+
+
+def grid_cb2s(seed: int = LAYER_SEED) -> np.ndarray:
+    """The magnitude grid of the signed codebook format: 256 distinct 8-vectors
+    with entries drawn from {1, 3, 5} with probabilities 1/2, 1/3, 1/6 (small
+    magnitudes are the common ones for bell-shaped weights).  Duplicates are
+    redrawn in index order.  Returned as uint8 [256, 8]."""
+    rng = np.random.default_rng([seed, _TAG_GRID])
+    levels = np.array([1, 3, 5], dtype=np.uint8)
+    out = np.empty((256, 8), dtype=np.uint8)
+    seen = set()
+    i = 0
+    while i < 256:
+        row = levels[rng.choice(3, size=8, p=[0.5, 1.0 / 3.0, 1.0 / 6.0])]
+        key = row.tobytes()
+        if key in seen:
+            continue
+        seen.add(key)
+        out[i] = row
+        i += 1
+    return out
+
+
+def codebook_for(fmt: int, seed: int = LAYER_SEED) -> np.ndarray:
+    """The table a gate/up format reads: the signed grid for FMT_CB2S, else the
+    CB2 codebook (ignored by the formats that have none)."""
+    return grid_cb2s(seed) if fmt == FMT_CB2S else codebook(seed)
 
 
 # ------------------------------------------------------------------ weights

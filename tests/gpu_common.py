@@ -43,7 +43,7 @@ def oracle_routing(cfg, T=None):
 def oracle_experts(cfg, experts, lib_packed=None):
     """Dequantized (oracle-packed) weights of the given experts.  When the
     library's packed bytes are given, they must equal the oracle's."""
-    cb = S.codebook()
+    cb = S.codebook_for(cfg["fmt_gate_up"])
     H, I = cfg["hidden"], cfg["inter"]
     out = {}
     for e in experts:

@@ -16,6 +16,11 @@ import synthetic as S
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_blocks.json")))
 CB = S.codebook()
+GRID = S.grid_cb2s()
+
+
+def _cb(fmt):
+    return GRID if fmt == F.CB2S else CB
 
 
 # ------------------------------------------------------------------ fp16 RNE
@@ -56,6 +61,16 @@ def test_cb2_hand_block():
     w = F.unpack(F.CB2, _block(F.CB2, g["set_bytes"]), 1, 256, CB)[0]
     assert np.array_equal(w[:8], CB[g["codeword"]].astype(np.float32))
     assert np.array_equal(w[8:32], np.tile(CB[0], 3).astype(np.float32))
+    assert np.all(w[32:] == 0)
+
+
+def test_cb2s_hand_block():
+    g = GOLD["cb2s"]
+    w = F.unpack(F.CB2S, _block(F.CB2S, g["set_bytes"]), 1, 256, GRID)[0]
+    G = GRID.astype(np.float32)
+    assert np.array_equal(w[0:8], np.array(g["signs_group0"], np.float32) * G[g["idx_group0"]])
+    assert np.array_equal(w[8:16], np.array(g["signs_group1"], np.float32) * G[0])
+    assert np.array_equal(w[16:32], np.tile(G[0], 2))
     assert np.all(w[32:] == 0)
 
 
@@ -175,6 +190,36 @@ def test_cb2_quantizer_inverts_dequant():
     assert np.array_equal(fl["idx"], idx)
 
 
+def _even_sign_patterns():
+    """All 128 sign vectors of 8 entries with an even number of -1 (brute force)."""
+    pats = np.array([[1 - 2 * ((m >> i) & 1) for i in range(8)] for m in range(256)], np.float64)
+    return pats[(pats < 0).sum(axis=1) % 2 == 0]
+
+
+def test_cb2s_quantizer_inverts_dequant():
+    """Weights on the format's own image (magnitudes from the grid, an even
+    number of negatives per group, a 5 in every sub-block so that max|w| =
+    5*d*s) come back as exactly the codes that made them."""
+    rng = np.random.default_rng(18)
+    rows, nb = 16, 3
+    has5 = np.nonzero(GRID.max(axis=1) == 5)[0]
+    idx = rng.choice(has5, size=(rows, nb, 32))
+    pats = _even_sign_patterns()
+    sg = pats[rng.integers(0, len(pats), size=(rows, nb, 32))]          # [r, nb, 32, 8]
+    s = rng.integers(1, 16, size=(rows, nb, 8))
+    s[..., 0] = 15
+    d = np.float16(2.0 ** rng.uniform(-12, -6, size=(rows, nb))).astype(np.float32)
+    step = np.repeat(d[..., None] * s, 4, axis=-1)
+    w = (step[..., None] * (sg * GRID[idx])).reshape(rows, nb * 256).astype(np.float32)
+    p = F.pack(F.CB2S, w, GRID)
+    fl = F.fields(F.CB2S, p, rows, nb * 256)
+    assert np.array_equal(fl["d"], d)
+    assert np.array_equal(fl["s"], s)
+    assert np.array_equal(fl["idx"], idx)
+    assert np.array_equal(fl["neg"], (sg < 0).astype(np.int32))
+    assert np.array_equal(F.unpack(F.CB2S, p, rows, nb * 256, GRID), w)
+
+
 # ---------------------------------------------------- optimality (brute force)
 @pytest.mark.parametrize("fmt,n,L", [(F.Q2K, 16, 3), (F.Q4K, 32, 15), (F.Q5K, 32, 31)])
 def test_affine_codes_are_nearest_levels(fmt, n, L):
@@ -238,6 +283,46 @@ def test_cb2_codes_are_nearest_codewords():
             assert chosen <= dist.min() + 8 * (2.0 / 4096) * 4 + 1e-9
 
 
+def test_cb2s_codes_are_optimal_over_every_signed_codeword():
+    """For the block's step, the chosen (grid entry, signs) minimises the
+    squared error over all 256 x 128 codewords with an even number of negative
+    signs, by brute force."""
+    rng = np.random.default_rng(19)
+    w = (rng.standard_normal((3, 256)) * 0.02).astype(np.float32)
+    w[0, :8] = [0.01, -0.02, 0.0, 0.03, -0.001, 0.002, -0.04, 0.005]     # odd number of negatives
+    p = F.pack(F.CB2S, w, GRID)
+    fl = F.fields(F.CB2S, p, 3, 256)
+    step = fl["d"][..., None].astype(np.float64) * fl["s"]              # [3, 1, 8]
+    cand = (_even_sign_patterns()[None, :, :] * GRID.astype(np.float64)[:, None, :]).reshape(-1, 8)
+    for r in range(3):
+        for g in range(32):
+            st = step[r, 0, g // 4]
+            if st == 0:
+                assert fl["idx"][r, 0, g] == 0 and not fl["neg"][r, 0, g].any()
+                continue
+            t = w[r, 8 * g:8 * g + 8].astype(np.float64) / st
+            err = ((t[None, :] - cand) ** 2).sum(axis=1)
+            code = (1 - 2 * fl["neg"][r, 0, g]) * GRID[fl["idx"][r, 0, g]].astype(np.float64)
+            chosen = ((t - code) ** 2).sum()
+            # targets are fixed point (1/4096): each term may move by at most
+            # 2 (|t| + 5) (0.6 / 4096), so only near-ties can flip
+            slack = 2.0 * (np.abs(t) + 5.0).sum() * 0.6 / 4096
+            assert chosen <= err.min() + slack
+
+
+def test_cb2s_error_beats_cb2():
+    """The sign field is what the signed format adds: on bell-shaped weights it
+    fits much closer than the sign-less codebook of the same grid size."""
+    rng = np.random.default_rng(13)
+    w = (rng.standard_normal((64, 1024)) * 0.02).astype(np.float32)
+    rel = {}
+    for fmt in (F.CB2, F.CB2S):
+        r = F.unpack(fmt, F.pack(fmt, w, _cb(fmt)), 64, 1024, _cb(fmt))
+        rel[fmt] = np.linalg.norm(r - w) / np.linalg.norm(w)
+    assert rel[F.CB2S] < 0.75 * rel[F.CB2]
+    assert rel[F.CB2S] < 0.6
+
+
 def test_cb2_error_is_bounded():
     rng = np.random.default_rng(13)
     w = (rng.standard_normal((64, 1024)) * 0.02).astype(np.float32)
@@ -253,26 +338,26 @@ def test_cb2_error_is_bounded():
 
 
 # -------------------------------------------------------------- zero padding
-@pytest.mark.parametrize("fmt", [F.CB2, F.Q2K, F.Q4K, F.Q5K, F.Q6K])
+@pytest.mark.parametrize("fmt", [F.CB2, F.Q2K, F.Q4K, F.Q5K, F.Q6K, F.CB2S])
 def test_padding_is_zero_extension(fmt):
     rng = np.random.default_rng(14)
     K = 128 + 64
     w = (rng.standard_normal((5, K)) * 0.02).astype(np.float32)
     wp = np.zeros((5, 256), np.float32)
     wp[:, :K] = w
-    a = F.pack(fmt, w, CB)
-    b = F.pack(fmt, wp, CB)
+    a = F.pack(fmt, w, _cb(fmt))
+    b = F.pack(fmt, wp, _cb(fmt))
     assert np.array_equal(a, b)
-    full = F.unpack(fmt, b, 5, 256, CB)
-    assert np.array_equal(F.unpack(fmt, a, 5, K, CB), full[:, :K])
+    full = F.unpack(fmt, b, 5, 256, _cb(fmt))
+    assert np.array_equal(F.unpack(fmt, a, 5, K, _cb(fmt)), full[:, :K])
 
 
 def test_fully_padded_subblocks_dequantize_to_zero():
     rng = np.random.default_rng(15)
     w = (rng.standard_normal((3, 128)) * 0.02).astype(np.float32)
-    for fmt, sub in ((F.Q2K, 16), (F.Q4K, 32), (F.CB2, 32), (F.Q5K, 32), (F.Q6K, 16)):
-        p = F.pack(fmt, w, CB)
-        full = F.unpack(fmt, p, 3, 256, CB)
+    for fmt, sub in ((F.Q2K, 16), (F.Q4K, 32), (F.CB2, 32), (F.Q5K, 32), (F.Q6K, 16), (F.CB2S, 32)):
+        p = F.pack(fmt, w, _cb(fmt))
+        full = F.unpack(fmt, p, 3, 256, _cb(fmt))
         assert np.all(full[:, 128:] == 0)
 
 
@@ -282,9 +367,17 @@ def test_packed_sizes():
     assert F.packed_bytes(F.Q4K, 7168, 2048) == 7168 * 8 * 144
     assert F.packed_bytes(F.Q5K, 7168, 2048) == 7168 * 8 * 176
     assert F.packed_bytes(F.Q6K, 7168, 2048) == 7168 * 8 * 210
+    assert F.packed_bytes(F.CB2S, 2048, 7168) == 2048 * 28 * 66
+    assert 66 * 8 / 256 == 2.0625                                        # bits per weight
 
 
 def test_codebook_is_distinct_and_on_levels():
     assert CB.shape == (256, 8)
     assert set(np.unique(CB).tolist()) <= {-3, -1, 1, 3}
     assert len({r.tobytes() for r in CB}) == 256
+
+
+def test_cb2s_grid_is_distinct_and_on_levels():
+    assert GRID.shape == (256, 8) and GRID.dtype == np.uint8
+    assert set(np.unique(GRID).tolist()) <= {1, 3, 5}
+    assert len({r.tobytes() for r in GRID}) == 256

@@ -45,7 +45,7 @@ def pack_layer(cfg: dict, threads: int = 8, cache_dir: str | None = None, progre
         paths = [os.path.join(cache_dir, "%s_%s.npy" % (key, n)) for n in ("gate", "up", "down")]
         if all(os.path.exists(p) for p in paths):
             return [np.load(p, mmap_mode="r") for p in paths]
-    cb = S.codebook(seed)
+    cb = S.codebook_for(fg, seed)
     gate = np.empty((E, M.q2_packed_bytes(fg, I, H)), np.uint8)
     up = np.empty_like(gate)
     down = np.empty((E, M.q2_packed_bytes(fd, H, I)), np.uint8)
@@ -80,7 +80,7 @@ class Workload:
         H, I, E, k = cfg["hidden"], cfg["inter"], cfg["n_experts"], cfg["top_k"]
         seed = cfg.get("seed", S.LAYER_SEED)
         self.packed = pack_layer(cfg, cache_dir=cache_dir, progress=progress)
-        self.codebook = torch.from_numpy(S.codebook(seed)).to(device)
+        self.codebook = torch.from_numpy(S.codebook_for(cfg["fmt_gate_up"], seed)).to(device)
         self.w_router = torch.from_numpy(S.router_weight(cfg, seed)).to(device)
         sh = cfg["sh_inter"]
         self.shared = None
