@@ -558,10 +558,11 @@ def sweep(args):
                       "rows": rows, "crossover_T": cross}), flush=True)
 
 
-DEFAULT_EXTRA = "decode32,prefill2048,prefill8192,prefill8192_q4k,decode32_q4k"
+DEFAULT_EXTRA = "decode32,prefill2048,prefill8192,prefill8192_q4k,decode32_q4k,prefill2048_cb2s,decode32_cb2s"
 # tokens of each workload the oracle baseline evaluates (the whole step at T = 1)
 CPU_SAMPLE = {"decode1": 1, "decode32": 2, "decode32_q4k": 2, "prefill2048": 2, "prefill8192": 2,
-              "prefill8192_q4k": 2}
+              "prefill8192_q4k": 2, "prefill2048_cb2s": 1, "decode32_cb2s": 1}
+FMT_NAMES = {1: "CB2", 2: "Q2_K", 3: "Q4_K", 5: "Q5_K", 6: "Q6_K", 7: "CB2S"}
 
 
 def measure(wl, cfg, name, steps, warmup, with_cpu):
@@ -613,7 +614,8 @@ def measure(wl, cfg, name, steps, warmup, with_cpu):
         value = T / (ms * 1e-3)
         out = {"ms_per_step": round(ms, 5), "tokens/s": round(value, 1), "TFLOP/s": round(tf, 1),
                "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4), "algorithmic_flops": fl}
-    out.update({"T": T, "active_experts": n_active, "steps": steps, "step_ms": pct, "wall_ms_per_step": round(wall, 5),
+    out.update({"T": T, "formats": "gate/up %s, down %s" % (FMT_NAMES[cfg["fmt_gate_up"]], FMT_NAMES[cfg["fmt_down"]]),
+                "active_experts": n_active, "steps": steps, "step_ms": pct, "wall_ms_per_step": round(wall, 5),
                 "roofline": roof, "kernels_ms": {n: round(v[2], 5) for n, v in kt.items()}})
     if with_cpu:
         log("%s: timing the oracle on the host (cpu_baseline)" % name)
@@ -711,7 +713,7 @@ def main():
         "config": {"workload": args.workload, "T": head["T"], "hidden": cfg["hidden"], "inter": cfg["inter"],
                    "experts": cfg["n_experts"], "top_k": cfg["top_k"], "shared_inter": cfg["sh_inter"],
                    "formats": "gate/up %s, down %s, shared bf16" % (
-                       {1: "CB2", 3: "Q4_K"}[cfg["fmt_gate_up"]], {2: "Q2_K", 3: "Q4_K"}[cfg["fmt_down"]]),
+                       FMT_NAMES[cfg["fmt_gate_up"]], FMT_NAMES[cfg["fmt_down"]]),
                    "active_experts": head["active_experts"], "weight_replicas": args.replicas},
         "hbm_frac": head.get("hbm_frac"), "mfma_frac": head.get("mfma_frac"),
         "step_ms": head["step_ms"],

@@ -19,13 +19,13 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_build", "libmoe.so")
 
-FMT_CB2, FMT_Q2K, FMT_Q4K, FMT_BF16, FMT_Q5K, FMT_Q6K = 1, 2, 3, 4, 5, 6
+FMT_CB2, FMT_Q2K, FMT_Q4K, FMT_BF16, FMT_Q5K, FMT_Q6K, FMT_CB2S = 1, 2, 3, 4, 5, 6, 7
 ACT_F32, ACT_BF16 = 0, 1
 PATH_ROUTE, PATH_DECODE, PATH_PREFILL, PATH_LAYER_DECODE = 0, 1, 2, 3
 LAYER_TOKENWISE_DECODE = 1
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
           -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
-BLOCK_BYTES = {FMT_CB2: 38, FMT_Q2K: 84, FMT_Q4K: 144, FMT_Q5K: 176, FMT_Q6K: 210}
+BLOCK_BYTES = {FMT_CB2: 38, FMT_Q2K: 84, FMT_Q4K: 144, FMT_Q5K: 176, FMT_Q6K: 210, FMT_CB2S: 66}
 
 
 class MoeError(RuntimeError):
@@ -142,7 +142,10 @@ def q2_pack(fmt: int, w: np.ndarray, codebook: np.ndarray | None = None) -> np.n
     w = np.ascontiguousarray(w, dtype=np.float32)
     rows, K = w.shape
     out = np.empty(q2_packed_bytes(fmt, rows, K), np.uint8)
-    cb = None if codebook is None else np.ascontiguousarray(codebook, dtype=np.int8)
+    cb = None
+    if codebook is not None:                       # CB2: int8 codebook; CB2S: uint8 grid (same bytes)
+        cb = np.ascontiguousarray(codebook)
+        cb = cb.view(np.int8) if cb.dtype == np.uint8 else cb.astype(np.int8)
     _check(lib().q2_pack(fmt, w.ctypes.data, rows, K, _ptr(cb), out.ctypes.data), "q2_pack")
     return out
 

@@ -69,11 +69,15 @@ struct Prof {
     }
 };
 
-bool fmt_ok(int f) { return f == MOE_FMT_CB2 || f == MOE_FMT_Q2K || f == MOE_FMT_Q4K || f == MOE_FMT_Q5K || f == MOE_FMT_Q6K; }
+bool fmt_ok(int f)
+{
+    return f == MOE_FMT_CB2 || f == MOE_FMT_Q2K || f == MOE_FMT_Q4K || f == MOE_FMT_Q5K || f == MOE_FMT_Q6K ||
+           f == MOE_FMT_CB2S;
+}
 int bbytes(int f)
 {
     return f == MOE_FMT_CB2 ? 38 : f == MOE_FMT_Q2K ? 84 : f == MOE_FMT_Q4K ? 144 : f == MOE_FMT_Q5K ? 176
-         : f == MOE_FMT_Q6K ? 210 : 0;
+         : f == MOE_FMT_Q6K ? 210 : f == MOE_FMT_CB2S ? 66 : 0;
 }
 int nblocks(int K) { return (K + 255) / 256; }
 
@@ -93,12 +97,13 @@ int check_layer(const moe_layer *L)
     if (rc) return rc;
     if (L->inter < 8 || L->inter % 8) return set_error(MOE_ERR_INVALID_ARG, "inter=%d must be a positive multiple of 8", L->inter);
     const int fg = L->fmt_gate_up, fd = L->fmt_down;
-    if (fg != MOE_FMT_CB2 && fg != MOE_FMT_Q2K && fg != MOE_FMT_Q4K && fg != MOE_FMT_Q5K)
-        return set_error(MOE_ERR_INVALID_ARG, "fmt_gate_up=%d must be CB2, Q2K, Q4K or Q5K", fg);
+    if (fg != MOE_FMT_CB2 && fg != MOE_FMT_CB2S && fg != MOE_FMT_Q2K && fg != MOE_FMT_Q4K && fg != MOE_FMT_Q5K)
+        return set_error(MOE_ERR_INVALID_ARG, "fmt_gate_up=%d must be CB2, CB2S, Q2K, Q4K or Q5K", fg);
     if (fd != MOE_FMT_Q2K && fd != MOE_FMT_Q4K && fd != MOE_FMT_Q5K && fd != MOE_FMT_Q6K)
         return set_error(MOE_ERR_INVALID_ARG, "fmt_down=%d must be Q2K, Q4K, Q5K or Q6K", fd);
     if (!L->w_gate || !L->w_up || !L->w_down) return set_error(MOE_ERR_INVALID_ARG, "routed expert weights are NULL");
-    if (L->fmt_gate_up == MOE_FMT_CB2 && !L->codebook) return set_error(MOE_ERR_INVALID_ARG, "CB2 needs a codebook");
+    if ((fg == MOE_FMT_CB2 || fg == MOE_FMT_CB2S) && !L->codebook)
+        return set_error(MOE_ERR_INVALID_ARG, "CB2 needs a codebook, CB2S its magnitude grid");
     for (const void *ptr : {L->w_gate, L->w_up, L->w_down, (const void *)L->codebook, L->sh_gate, L->sh_up,
                             L->sh_down, (const void *)L->w_router})
         if ((uintptr_t)ptr % 16) return set_error(MOE_ERR_INVALID_ARG, "layer pointer %p is not 16-byte aligned", ptr);
@@ -660,7 +665,8 @@ int q2_unpack(int fmt, const void *packed_dev, int64_t rows, int K, const int8_t
     if (rows < 0 || K < 1) return set_error(MOE_ERR_INVALID_ARG, "rows=%lld K=%d", (long long)rows, K);
     if (rows == 0) return MOE_OK;
     if (!packed_dev || !out_dev) return set_error(MOE_ERR_INVALID_ARG, "NULL tensor argument");
-    if (fmt == MOE_FMT_CB2 && !codebook_dev) return set_error(MOE_ERR_INVALID_ARG, "CB2 needs a codebook");
+    if ((fmt == MOE_FMT_CB2 || fmt == MOE_FMT_CB2S) && !codebook_dev)
+        return set_error(MOE_ERR_INVALID_ARG, "CB2 needs a codebook, CB2S its grid");
     if (rows * nblocks(K) * 8 > ((int64_t)1 << 40)) return set_error(MOE_ERR_INVALID_ARG, "too large");
     hipError_t e = launch_unpack(fmt, (const uint8_t *)packed_dev, rows, K, codebook_dev, out_dev, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "q2_unpack launch");

@@ -18,11 +18,12 @@ constexpr int QK = 256;          // weights per block
 constexpr int KS = 128;          // K-step of the FFN kernels (half a block)
 constexpr int LROW = KS + 8;     // LDS row stride in bf16 elements (16 B pad)
 
-enum { FMT_CB2 = 1, FMT_Q2K = 2, FMT_Q4K = 3, FMT_BF16 = 4, FMT_Q5K = 5, FMT_Q6K = 6 };
+enum { FMT_CB2 = 1, FMT_Q2K = 2, FMT_Q4K = 3, FMT_BF16 = 4, FMT_Q5K = 5, FMT_Q6K = 6, FMT_CB2S = 7 };
 
 constexpr int block_bytes(int fmt)
 {
-    return fmt == FMT_CB2 ? 38 : fmt == FMT_Q2K ? 84 : fmt == FMT_Q4K ? 144 : fmt == FMT_Q5K ? 176 : fmt == FMT_Q6K ? 210 : 0;
+    return fmt == FMT_CB2 ? 38 : fmt == FMT_Q2K ? 84 : fmt == FMT_Q4K ? 144 : fmt == FMT_Q5K ? 176 : fmt == FMT_Q6K ? 210
+         : fmt == FMT_CB2S ? 66 : 0;
 }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

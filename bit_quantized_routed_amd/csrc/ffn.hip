@@ -592,6 +592,20 @@ __global__ __launch_bounds__(256) void unpack_kernel(int fmt, const uint8_t *pac
             const int8_t *c = cb + 8 * blk[6 + 4 * j + g];
             for (int i = 0; i < 8; ++i) v[8 * g + i] = step * (float)c[i];
         }
+    } else if (fmt == FMT_CB2S) {
+        // sub-block record: 4 grid indices, then signs (7 per group) and s_j
+        const int j = k0 >> 5;
+        const uint8_t *rec = blk + 2 + 8 * j;
+        const uint32_t word = (uint32_t)rec[4] | ((uint32_t)rec[5] << 8) | ((uint32_t)rec[6] << 16) |
+                              ((uint32_t)rec[7] << 24);
+        const float step = d * (float)(word >> 28);
+        const uint8_t *grid = (const uint8_t *)cb;
+        for (int g = 0; g < 4; ++g) {
+            uint32_t neg = (word >> (7 * g)) & 0x7fu;
+            neg |= (uint32_t)(__builtin_popcount(neg) & 1) << 7;
+            const uint8_t *c = grid + 8 * rec[g];
+            for (int i = 0; i < 8; ++i) v[8 * g + i] = step * ((neg >> i) & 1 ? -(float)c[i] : (float)c[i]);
+        }
     } else if (fmt == FMT_Q2K) {
         const float dmin = f16_bits_to_f32(ld_u16(blk + 2));
         for (int e = 0; e < 32; ++e) {

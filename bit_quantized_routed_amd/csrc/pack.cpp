@@ -9,6 +9,7 @@
 #pragma clang fp contract(off)
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -227,21 +228,109 @@ void block_cb2(const float *x, const Codebook &C, uint8_t *o)
     }
 }
 
+// CB2S: the same integer metric on magnitudes.  With a the fixed-point
+// magnitude targets, |a - 4096G|^2 = |a|^2 - 8192 (a.G - 2048 |G|^2), and a
+// sign flip at p adds 4 a_p 4096 G_p = 8192 (2 a_p G_p), so every candidate's
+// cost is |a|^2 + 8192 u(c) with u(c) = 2048 |G_c|^2 - a.G_c (+ 2 min_p a_p
+// G_cp when the count of negatives is odd).  a_i <= 7.5*4096 and G <= 15
+// keep u in int32.  Strict '<' over increasing c (and over p) keeps the
+// lowest index on ties.
+struct Grid {
+    int32_t gt[8][256];                             // gt[i][c] = G[c][i]
+    int32_t base[256];                              // 2048 |G_c|^2
+    explicit Grid(const uint8_t *g)
+    {
+        for (int e = 0; e < 256; ++e) {
+            int32_t n = 0;
+            for (int i = 0; i < 8; ++i) { gt[i][e] = g[8 * e + i]; n += (int32_t)g[8 * e + i] * g[8 * e + i]; }
+            base[e] = 2048 * n;
+        }
+    }
+};
+
+__attribute__((target_clones("avx2", "default")))
+int best_signed_entry(const int32_t a[8], bool odd, const Grid &G)
+{
+    int32_t u[256], m[256];
+    for (int e = 0; e < 256; ++e) { u[e] = G.base[e]; m[e] = INT32_MAX; }
+    for (int i = 0; i < 8; ++i) {
+        const int32_t ai = a[i];
+        for (int e = 0; e < 256; ++e) {
+            const int32_t p = ai * G.gt[i][e];
+            u[e] -= p;
+            m[e] = std::min(m[e], p);
+        }
+    }
+    if (odd)
+        for (int e = 0; e < 256; ++e) u[e] += 2 * m[e];
+    int best = 0;
+    for (int e = 1; e < 256; ++e)
+        if (u[e] < u[best]) best = e;
+    return best;
+}
+
+void block_cb2s(const float *x, const Grid &G, uint8_t *o)
+{
+    float sigma[8], top = 0.f;
+    for (int j = 0; j < 8; ++j) {
+        float amax = 0.f;
+        for (int i = 0; i < 32; ++i) amax = std::max(amax, std::fabs(x[32 * j + i]));
+        sigma[j] = amax / 5.f;
+        top = std::max(top, sigma[j]);
+    }
+    const uint16_t db = half_bits(top / 15.f);
+    const float d = half_value(db);
+    std::memset(o, 0, 66);
+    store_half(o, db);
+    for (int j = 0; j < 8; ++j) {
+        const int s = d > 0.f ? rne_clamp(sigma[j] / d, 15) : 0;
+        const float step = d * (float)s;
+        uint8_t *rec = o + 2 + 8 * j;
+        uint32_t word = (uint32_t)s << 28;
+        for (int u = 0; u < 4; ++u) {
+            const float *v = x + 32 * j + 8 * u;
+            int idx = 0;
+            uint32_t neg = 0;                                   // bit i: weight i negative
+            if (step > 0.f) {
+                int32_t a[8];
+                for (int i = 0; i < 8; ++i) {
+                    a[i] = (int32_t)std::nearbyint(std::fabs(v[i]) / step * 4096.f);
+                    neg |= (uint32_t)(v[i] < 0.f) << i;
+                }
+                const bool odd = __builtin_popcount(neg) & 1;
+                idx = best_signed_entry(a, odd, G);
+                if (odd) {
+                    int p = 0;
+                    for (int i = 1; i < 8; ++i)
+                        if (a[i] * G.gt[i][idx] < a[p] * G.gt[p][idx]) p = i;
+                    neg ^= 1u << p;
+                }
+            }
+            rec[u] = (uint8_t)idx;
+            word |= (neg & 0x7fu) << (7 * u);
+        }
+        for (int t = 0; t < 4; ++t) rec[4 + t] = (uint8_t)(word >> (8 * t));
+    }
+}
+
 }  // namespace
 
 extern "C" int q2_pack(int fmt, const float *w_host, int64_t rows, int K, const int8_t *codebook_host, void *out_host)
 {
     using moe::set_error;
-    if (fmt != MOE_FMT_CB2 && fmt != MOE_FMT_Q2K && fmt != MOE_FMT_Q4K && fmt != MOE_FMT_Q5K && fmt != MOE_FMT_Q6K)
-        return set_error(MOE_ERR_INVALID_ARG, "q2_pack: fmt=%d is not CB2, Q2K, Q4K, Q5K or Q6K", fmt);
+    if (fmt != MOE_FMT_CB2 && fmt != MOE_FMT_Q2K && fmt != MOE_FMT_Q4K && fmt != MOE_FMT_Q5K && fmt != MOE_FMT_Q6K &&
+        fmt != MOE_FMT_CB2S)
+        return set_error(MOE_ERR_INVALID_ARG, "q2_pack: fmt=%d is not CB2, CB2S, Q2K, Q4K, Q5K or Q6K", fmt);
     if (rows < 0 || K < 1) return set_error(MOE_ERR_INVALID_ARG, "q2_pack: rows=%lld K=%d", (long long)rows, K);
     if (rows == 0) return MOE_OK;
     if (!w_host || !out_host) return set_error(MOE_ERR_INVALID_ARG, "q2_pack: NULL input or output");
-    if (fmt == MOE_FMT_CB2 && !codebook_host) return set_error(MOE_ERR_INVALID_ARG, "q2_pack: CB2 needs a codebook");
+    if ((fmt == MOE_FMT_CB2 || fmt == MOE_FMT_CB2S) && !codebook_host)
+        return set_error(MOE_ERR_INVALID_ARG, "q2_pack: CB2 needs a codebook, CB2S its grid");
     const int nb = (K + 255) / 256;
     const int bb = fmt == MOE_FMT_CB2 ? 38 : fmt == MOE_FMT_Q2K ? 84 : fmt == MOE_FMT_Q4K ? 144
-                 : fmt == MOE_FMT_Q5K ? 176 : 210;
+                 : fmt == MOE_FMT_Q5K ? 176 : fmt == MOE_FMT_CB2S ? 66 : 210;
     Codebook *cbp = fmt == MOE_FMT_CB2 ? new Codebook(codebook_host) : nullptr;
+    Grid *gp = fmt == MOE_FMT_CB2S ? new Grid((const uint8_t *)codebook_host) : nullptr;
     auto work = [&](int64_t r0, int64_t r1) {
         std::vector<float> row((size_t)nb * 256);
         for (int64_t r = r0; r < r1; ++r) {
@@ -254,6 +343,7 @@ extern "C" int q2_pack(int fmt, const float *w_host, int64_t rows, int K, const 
                 else if (fmt == MOE_FMT_Q2K) block_q2k(x, o + (int64_t)b * bb);
                 else if (fmt == MOE_FMT_Q4K) block_q4k(x, o + (int64_t)b * bb);
                 else if (fmt == MOE_FMT_Q5K) block_q5k(x, o + (int64_t)b * bb);
+                else if (fmt == MOE_FMT_CB2S) block_cb2s(x, *gp, o + (int64_t)b * bb);
                 else block_q6k(x, o + (int64_t)b * bb);
             }
         }
@@ -268,5 +358,6 @@ extern "C" int q2_pack(int fmt, const float *w_host, int64_t rows, int K, const 
     }
     for (auto &th : pool) th.join();
     delete cbp;
+    delete gp;
     return MOE_OK;
 }

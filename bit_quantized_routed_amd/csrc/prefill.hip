@@ -131,6 +131,17 @@ __device__ __forceinline__ void np_build_table(const FfnPass &p, uint32_t *tab)
 #pragma unroll
             for (int c = 0; c < NP_COPIES; ++c) tab[(idx * NP_COPIES + c) * 4 + i] = sel;
         }
+    } else if constexpr (FMT == FMT_CB2S) {
+        // CB2S: the selectors of grid entry idx into the magnitude pool
+        // {lo: bf16(ds) | bf16(3ds), hi: bf16(5ds) | bf16(7ds)}
+        const uint8_t *grid = (const uint8_t *)p.codebook;
+        for (int e = threadIdx.x; e < 256 * 4; e += NP_THREADS) {
+            const int idx = e >> 2, i = e & 3;
+            const uint32_t b0 = (uint32_t)(grid[8 * idx + 2 * i] - 1), b1 = (uint32_t)(grid[8 * idx + 2 * i + 1] - 1);
+            const uint32_t sel = b0 | ((b0 + 1) << 8) | (b1 << 16) | ((b1 + 1) << 24);
+#pragma unroll
+            for (int c = 0; c < NP_COPIES; ++c) tab[(idx * NP_COPIES + c) * 4 + i] = sel;
+        }
     } else if constexpr (FMT == FMT_Q2K) {
         for (int e = threadIdx.x; e < 256 * 2; e += NP_THREADS) {
             const int byte = e >> 1, i = e & 1;
@@ -436,9 +447,11 @@ __device__ __forceinline__ void np_epilogue(const FfnPass &p, const NpTile &t, c
 // swizzled LDS layout) never force the weight loads issued after them.
 struct BlkCB2 { uint32_t d, sc, i0, i1; };            // d, scale byte pair, 8 indices
 struct BlkQ2K { uint32_t dd, scw; uint2 c0, c1; };    // d|dmin, 4 scale bytes, 2 x 16 codes
+struct BlkCB2S { uint32_t d; u32x4 rec; };            // d, records of sub-blocks 2 fc and 2 fc + 1
 template <int FMT> struct BlkOf;
 template <> struct BlkOf<FMT_CB2> { using T = BlkCB2; };
 template <> struct BlkOf<FMT_Q2K> { using T = BlkQ2K; };
+template <> struct BlkOf<FMT_CB2S> { using T = BlkCB2S; };
 
 // the part of block b that half h of the previous block requests (Q2_K
 // splits its codes so that only half of them are in flight at a time)
@@ -452,6 +465,26 @@ __device__ __forceinline__ void blk_load(const uint8_t *row, int b, int h, int f
             r.sc = ld_u16(blk + 2 + 2 * (fc >> 1));
             r.i0 = ld_u32_unaligned(blk + 6 + 8 * fc);           // 2-byte aligned
             r.i1 = ld_u32_unaligned(blk + 10 + 8 * fc);
+        }
+    } else if constexpr (FMT == FMT_CB2S) {
+        if (h == 0) {
+            // rows are a multiple of 4 bytes long (an even number of 66-byte
+            // blocks), so the 16 record bytes at 2 + 16 fc start 4-byte
+            // aligned in odd blocks and 2 bytes past a dword in even ones:
+            // there they come from five aligned dwords that end at the
+            // record's last byte
+            const uint8_t *blk = row + (int64_t)b * 66;
+            r.d = ld_u16(blk);
+            const uint8_t *rec = blk + 2 + 16 * fc;
+            if (b & 1) {
+                r.rec = *(const u32x4 *)rec;
+            } else {
+                const uint32_t *a4 = (const uint32_t *)(rec - 2);
+                const u32x4 v = *(const u32x4 *)a4;
+                const uint32_t w = a4[4];
+                r.rec = u32x4{__builtin_amdgcn_alignbit(v.y, v.x, 16), __builtin_amdgcn_alignbit(v.z, v.y, 16),
+                              __builtin_amdgcn_alignbit(v.w, v.z, 16), __builtin_amdgcn_alignbit(w, v.w, 16)};
+            }
         }
     } else {
         const uint8_t *blk = row + (int64_t)b * 84;
@@ -471,6 +504,13 @@ __device__ __forceinline__ void blk_pool(const typename BlkOf<FMT>::T &r, int h,
     if constexpr (FMT == FMT_CB2) {
         RawCB2 x{r.d, r.sc, 0u};
         pool_prep<FMT_CB2, DEC>(x, h, fc, P);
+    } else if constexpr (FMT == FMT_CB2S) {
+        // sub-block 2 fc + h: s in the top nibble of its record's sign word;
+        // DEC keeps the block scale d out (applied to the block's sums)
+        const uint32_t s = (h == 0 ? r.rec.y : r.rec.w) >> 28;
+        const float ds = DEC ? (float)s : f16_bits_to_f32(r.d) * (float)s;   // exact (11 x 4 bits)
+        P.lo[0] = pk_bf16(ds, 3.0f * ds);
+        P.hi[0] = pk_bf16(5.0f * ds, 7.0f * ds);
     } else {
         RawQ2K x{r.dd, r.scw, 0u, 0u};
         pool_prep<FMT_Q2K, DEC>(x, h, fc, P);
@@ -501,6 +541,21 @@ __device__ __forceinline__ void blk_frag(const typename BlkOf<FMT>::T &r, const 
     if constexpr (FMT == FMT_CB2) {
         RawCB2 x{r.d, r.sc, h == 0 ? r.i0 : r.i1};
         bfrag<FMT_CB2>(x, P, s4, tab, copy, out);
+    } else if constexpr (FMT == FMT_CB2S) {
+        // magnitudes through the selector table, then the group's signs: 7
+        // stored flags and their parity as the eighth, XORed into the bf16
+        // sign bits (element 2i in bit 15, 2i + 1 in bit 31 of dword i)
+        const uint32_t iw = h == 0 ? r.rec.x : r.rec.z, sw = h == 0 ? r.rec.y : r.rec.w;
+        const uint32_t idx = (iw >> (8 * s4)) & 0xffu;
+        const uint32_t n7 = (sw >> (7 * s4)) & 0x7fu;
+        const uint32_t neg = n7 | ((uint32_t)(__builtin_popcount(n7) & 1) << 7);
+        const u32x4 sel = *(const u32x4 *)&tab[(idx * NP_COPIES + copy) * 4];
+        const uint32_t sv[4] = {sel.x, sel.y, sel.z, sel.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t m = ((neg >> (2 * i)) & 1u) << 15 | ((neg >> (2 * i + 1)) & 1u) << 31;
+            out[i] = vperm(P.hi[0], P.lo[0], sv[i]) ^ m;
+        }
     } else {
         const uint2 c = h == 0 ? r.c0 : r.c1;
         RawQ2K x{r.dd, r.scw, c.x, c.y};
@@ -515,7 +570,7 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
 {
     // per-format weight staging: CB2/Q2_K whole blocks (two sets), Q4_K
     // half-blocks (two sets), bf16 one MFMA step at a time (a ring of four)
-    constexpr bool BLK = FMT == FMT_CB2 || FMT == FMT_Q2K;
+    constexpr bool BLK = FMT == FMT_CB2 || FMT == FMT_Q2K || FMT == FMT_CB2S;
     using Blk = typename BlkOf<BLK ? FMT : FMT_CB2>::T;
     // bf16 weights use the natural K order (MFMA step s of a block covers K
     // 32 s .. 32 s + 31, lane group fc its 8-wide slice), so the 4 lanes of a
@@ -655,7 +710,7 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
                     for (int nf = 0; nf < 4; ++nf) raw_load<FMT>(wrow(nf), min(hs + 1, nhs - 1), fc, r4[h ^ 1][nf]);
                 }
                 Pool P[4];
-                if constexpr (FMT == FMT_CB2) {
+                if constexpr (FMT == FMT_CB2 || FMT == FMT_CB2S) {
 #pragma unroll
                     for (int nf = 0; nf < 4; ++nf) blk_pool<FMT, DEC>(blk[q][nf], h, fc, P[nf]);
                 } else if constexpr (HALF) {
@@ -730,7 +785,7 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
 #pragma unroll
                         for (int nf = 0; nf < 4; ++nf) {
                             float d, dmin = 0.f;
-                            if constexpr (FMT == FMT_CB2) d = f16_bits_to_f32(blk[q][nf].d);
+                            if constexpr (FMT == FMT_CB2 || FMT == FMT_CB2S) d = f16_bits_to_f32(blk[q][nf].d);
                             else if constexpr (FMT == FMT_Q6K) d = f16_bits_to_f32(r4[h][nf].dd & 0xffffu);
                             else if constexpr (HALF) {
                                 d = f16_bits_to_f32(r4[h][nf].dd & 0xffffu);
@@ -1010,7 +1065,10 @@ __device__ __forceinline__ void np_dispatch(const FfnPass &p, const NpTile &t, u
     }
 }
 
-template <int FMT> constexpr int np_tab_bytes() { return FMT == FMT_CB2 ? NP_TAB_CB2 : FMT == FMT_Q2K ? NP_TAB_Q2K : 0; }
+template <int FMT> constexpr int np_tab_bytes()
+{
+    return FMT == FMT_CB2 || FMT == FMT_CB2S ? NP_TAB_CB2 : FMT == FMT_Q2K ? NP_TAB_Q2K : 0;
+}
 template <int FMT, bool TWO> constexpr int np_lds_bytes() { return (TWO ? 2 : 1) * NP_NBUF * NP_ABUF + np_tab_bytes<FMT>(); }
 
 template <int FMT, bool GATEUP, bool DEC, bool TWO>
@@ -1070,6 +1128,7 @@ hipError_t launch_np_prefill(const FfnPass &p, bool gateup, hipStream_t s)
     if (gateup) {
         switch (p.fmt) {
         case FMT_CB2: return np_launch<FMT_CB2, true, false, false>(p, s);
+        case FMT_CB2S: return np_launch<FMT_CB2S, true, false, false>(p, s);
         case FMT_Q2K: return np_launch<FMT_Q2K, true, false, false>(p, s);
         case FMT_Q4K: return np_launch<FMT_Q4K, true, false, false>(p, s);
         case FMT_Q5K: return np_launch<FMT_Q5K, true, false, false>(p, s);
@@ -1090,7 +1149,7 @@ bool np_decode_ok(const FfnPass &p)
     if (p.K % (2 * QK) || p.K < 2 * QK) return false;
     if (p.Nsh > 0 && (p.Ksh % (2 * QK) || p.Ksh < 2 * QK)) return false;
     return p.out_f32 && (p.fmt == FMT_CB2 || p.fmt == FMT_Q2K || p.fmt == FMT_Q4K || p.fmt == FMT_Q5K ||
-                         p.fmt == FMT_Q6K);
+                         p.fmt == FMT_Q6K || p.fmt == FMT_CB2S);
 }
 
 // gate/up takes x (bf16, or fp32 as two bf16 terms); down takes the fp32 h
@@ -1104,7 +1163,7 @@ hipError_t np_decode_fmt(const FfnPass &p, bool gateup, hipStream_t s)
             return np_launch<FMT, true, true, false>(p, s);
         }
     }
-    if constexpr (FMT == FMT_CB2) return hipErrorInvalidValue;
+    if constexpr (FMT == FMT_CB2 || FMT == FMT_CB2S) return hipErrorInvalidValue;
     else {
         if (!p.act_f32) return hipErrorInvalidValue;
         return np_launch<FMT, false, true, true>(p, s);
@@ -1116,6 +1175,7 @@ hipError_t launch_np_decode(const FfnPass &p, bool gateup, hipStream_t s)
     if (!np_decode_ok(p)) return hipErrorInvalidValue;
     switch (p.fmt) {
     case FMT_CB2: return np_decode_fmt<FMT_CB2>(p, gateup, s);
+    case FMT_CB2S: return np_decode_fmt<FMT_CB2S>(p, gateup, s);
     case FMT_Q2K: return np_decode_fmt<FMT_Q2K>(p, gateup, s);
     case FMT_Q4K: return np_decode_fmt<FMT_Q4K>(p, gateup, s);
     case FMT_Q5K: return np_decode_fmt<FMT_Q5K>(p, gateup, s);

@@ -71,6 +71,15 @@ enum moe_status {
  *   s_j in bits 4*(j%2).. of byte 2+j/2 | [6:38) 32 one-byte codebook indices,
  *   one per group of 8 weights.  w[8g+i] = d * s_{g/4} * C[idx_g][i], with C
  *   a caller-supplied int8 codebook [256][8] of values in {-3,-1,1,3}.
+ * MOE_FMT_CB2S 66 B/block (2.0625 bits per weight, the byte budget of the
+ *   pages' IQ2_XXS, with a sign field): [0:2) fp16 d | eight 8-byte
+ *   sub-block records at [2+8j, 10+8j): bytes 0..3 the grid indices of groups
+ *   4j..4j+3; bytes 4..7 a little-endian word with, for group 4j+u, the
+ *   negative flags of its weights 0..6 at bits 7u..7u+6, and s_j at bits
+ *   28..31.  Weight 7's flag is the parity of the other seven (an even
+ *   number of negatives per group).  w[8g+i] = d * s_{g/4} * (-1)^neg *
+ *   G[idx_g][i], with G a caller-supplied uint8 grid [256][8] of magnitudes
+ *   (the synthetic workloads use values in {1,3,5}; any up to 15 are exact).
  * MOE_FMT_Q2K  84 B/block: [0:2) fp16 d | [2:4) fp16 dmin | [4:20) byte j =
  *   sc_j | m_j<<4 for 16 sub-blocks of 16 | [20:84) 2-bit q_i in bits
  *   2*(i%4) of byte i/4.  w_i = d*sc_j*q_i - dmin*m_j, j = i/16.
@@ -93,7 +102,7 @@ enum moe_status {
  * Every dequantized value is exact in fp32 (products need at most 24
  * significant bits; the min term is subtracted with one rounding). */
 enum moe_format { MOE_FMT_CB2 = 1, MOE_FMT_Q2K = 2, MOE_FMT_Q4K = 3, MOE_FMT_BF16 = 4, MOE_FMT_Q5K = 5,
-                  MOE_FMT_Q6K = 6 };
+                  MOE_FMT_Q6K = 6, MOE_FMT_CB2S = 7 };
 
 /* activation element type of x */
 enum moe_act { MOE_ACT_F32 = 0, MOE_ACT_BF16 = 1 };
@@ -105,13 +114,14 @@ enum moe_path { MOE_PATH_ROUTE = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2, M
  * it is device memory.
  *   hidden (H), inter (I), n_experts (E), top_k (k): 1 <= k <= E <= 1024,
  *     H % 8 == 0, I % 8 == 0.
- *   fmt_gate_up: MOE_FMT_CB2, Q2K, Q4K or Q5K; fmt_down: MOE_FMT_Q2K, Q4K, Q5K
- *     or Q6K.  (CB2 or Q4K gate/up with Q2K or Q4K down run on any shape; the
+ *   fmt_gate_up: MOE_FMT_CB2, CB2S, Q2K, Q4K or Q5K; fmt_down: MOE_FMT_Q2K,
+ *     Q4K, Q5K or Q6K.  (CB2 or Q4K gate/up with Q2K or Q4K down run on any shape; the
  *     other pairs need hidden, inter and sh_inter multiples of 512, else the
  *     FFN calls return MOE_ERR_UNSUPPORTED.)
  *   w_gate, w_up: [E][I rows][ceil(H/256) blocks]; w_down: [E][H rows][ceil(I/256)
  *     blocks]; experts stored back to back with no gaps.
- *   codebook: int8 [256][8] (CB2 only, else may be NULL).
+ *   codebook: int8 [256][8] codebook for CB2, the uint8 [256][8] magnitude
+ *     grid (passed through this pointer) for CB2S, else may be NULL.
  *   sh_inter: intermediate size of the bf16 shared expert, 0 if there is none
  *     (then sh_* are ignored); sh_gate, sh_up: [sh_inter][H] bf16; sh_down:
  *     [H][sh_inter] bf16; sh_inter % 256 == 0 and H % 256 == 0 when present.
@@ -259,7 +269,8 @@ int moe_expert_ffn_decode_noalloc(const moe_layer *L, const void *x, int act, in
 /* ------------------------------------------------------------ pack / unpack
  * q2_pack (host): quantize a row-major fp32 matrix w_host [rows][K] into
  * out_host (q2_packed_bytes(fmt, rows, K) bytes).  fmt: CB2 (needs
- * codebook_host int8 [256][8]), Q2K or Q4K.  Quantizer (fp32 arithmetic,
+ * codebook_host int8 [256][8]), CB2S (needs the uint8 grid [256][8] there),
+ * Q2K, Q4K, Q5K or Q6K.  Quantizer (fp32 arithmetic,
  * round-half-to-even everywhere, fp16 conversion RNE):
  *   Q2_K / Q4_K, per sub-block j (16 / 32 weights): lo = min(0, min w),
  *     hi = max w, scale_j = (hi-lo)/L, mn_j = -lo (L = 3 / 15); per block
@@ -272,6 +283,17 @@ int moe_expert_ffn_decode_noalloc(const moe_layer *L, const void *x, int act, in
  *     step = d*s_j > 0: t_i = rint(w_i/step*4096), idx = argmin over the
  *     codebook of the integer distance sum_i (t_i - 4096*C[idx][i])^2, lowest
  *     index on ties (0 when step == 0).
+ *   CB2S: as CB2 with sigma_j = max|w|/5 and, per group with step > 0,
+ *     magnitude targets a_i = rint(|w_i|/step*4096) and natural signs
+ *     neg_i = (w_i < 0); entry c costs sum_i (a_i - 4096*G[c][i])^2 plus, if
+ *     the count of negatives is odd, the cheapest single sign flip
+ *     min_p 4*a_p*4096*G[c][p] (lowest p on ties); the lowest-cost entry
+ *     (lowest index on ties) is chosen and its flip applied (index 0 and no
+ *     flags when step == 0).
+ *   Q5_K: as Q4_K with L = 31.
+ *   Q6_K, per sub-block j of 16: scale_j = max|w|/31; d = fp16(max
+ *     scale_j/127); sc_j = rint(scale_j/d) clamped to [0,127] (0 if d == 0);
+ *     q_i = rint(w_i/(d*sc_j)) clamped to [-32,31] (0 if d*sc_j == 0).
  * Rows are spread over at most 16 host threads; the bytes do not depend on the thread
  * count.  Returns MOE_OK or MOE_ERR_INVALID_ARG (with moe_last_error() set). */
 int q2_pack(int fmt, const float *w_host, int64_t rows, int K, const int8_t *codebook_host,
@@ -279,7 +301,8 @@ int q2_pack(int fmt, const float *w_host, int64_t rows, int K, const int8_t *cod
 
 /* q2_unpack (device): dequantize packed_dev [rows][nb blocks] to out_dev fp32
  * [rows][K] (padding dropped), bit-exact with the definitions above.
- * codebook_dev: int8 [256][8] device array for CB2, else ignored. */
+ * codebook_dev: int8 [256][8] device array for CB2, the uint8 grid for CB2S,
+ * else ignored. */
 int q2_unpack(int fmt, const void *packed_dev, int64_t rows, int K, const int8_t *codebook_dev,
               float *out_dev, void *stream);
 

@@ -17,6 +17,11 @@ from oracle import formats as F
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CB = S.codebook()
+GRID = S.grid_cb2s()
+
+
+def _cb(fmt):
+    return GRID if fmt == F.CB2S else CB
 FAKE = 0x1000            # never dereferenced: every call below fails validation first
 
 
@@ -74,7 +79,8 @@ def test_route_validation_misc():
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(fmt_gate_up=6), -1), (dict(fmt_gate_up=4), -1), (dict(fmt_down=1), -1), (dict(fmt_down=7), -1),
+    (dict(fmt_gate_up=6), -1), (dict(fmt_gate_up=4), -1), (dict(fmt_gate_up=8), -1), (dict(fmt_down=1), -1),
+    (dict(fmt_down=7), -1), (dict(fmt_gate_up=7, codebook=None), -1),
     (dict(inter=100), -1), (dict(w_down=None), -1),
     (dict(codebook=None), -1), (dict(sh_inter=128, sh_gate=FAKE, sh_up=FAKE, sh_down=FAKE), -1),
     (dict(sh_inter=256), -1), (dict(sh_inter=-1), -1)])
@@ -100,7 +106,7 @@ def test_ffn_validation_misc():
     L = _layer()
     assert _ffn(pre, L, act=0) == -1                           # prefill needs bf16 activations
     assert _ffn(dec, _layer(fmt_gate_up=3, fmt_down=3)) == -2  # decode: Q4K needs K multiples of 512
-    for fg, fd in ((2, 2), (5, 6), (1, 6), (3, 5)):           # pairs that run on the 512-multiple GEMMs only
+    for fg, fd in ((2, 2), (5, 6), (1, 6), (3, 5), (7, 2), (7, 3)):   # pairs that run on the 512-multiple GEMMs only
         assert _ffn(pre, _layer(fmt_gate_up=fg, fmt_down=fd)) == -2
         assert _ffn(dec, _layer(fmt_gate_up=fg, fmt_down=fd)) == -2
     assert _ffn(dec, L, ws_bytes=100) == -3
@@ -140,6 +146,8 @@ def test_pack_sets_last_error():
     assert b"q2_pack" in M.lib().moe_last_error()
     assert P(1, w.ctypes.data, 2, 256, None, o.ctypes.data) == -1          # CB2 needs a codebook
     assert b"codebook" in M.lib().moe_last_error()
+    assert P(7, w.ctypes.data, 2, 256, None, o.ctypes.data) == -1          # CB2S needs its grid
+    assert b"grid" in M.lib().moe_last_error()
     assert P(2, w.ctypes.data, -1, 256, None, o.ctypes.data) == -1
     assert P(2, None, 2, 256, None, o.ctypes.data) == -1
 
@@ -167,6 +175,7 @@ def test_unpack_validation():
     U = M.lib().q2_unpack
     assert U(9, FAKE, 4, 256, FAKE, FAKE, None) == -1
     assert U(1, FAKE, 4, 256, None, FAKE, None) == -1          # CB2 needs a codebook
+    assert U(7, FAKE, 4, 256, None, FAKE, None) == -1          # CB2S needs its grid
     assert U(2, None, 4, 256, None, FAKE, None) == -1
     assert U(2, FAKE, -1, 256, None, FAKE, None) == -1
     assert U(2, FAKE, 0, 256, None, None, None) == 0
@@ -178,7 +187,9 @@ def test_sizes():
     assert M.q2_packed_bytes(3, 7, 300) == F.packed_bytes(F.Q4K, 7, 300)
     assert M.q2_packed_bytes(5, 7168, 2048) == F.packed_bytes(F.Q5K, 7168, 2048)
     assert M.q2_packed_bytes(6, 33, 700) == F.packed_bytes(F.Q6K, 33, 700)
+    assert M.q2_packed_bytes(7, 2048, 7168) == F.packed_bytes(F.CB2S, 2048, 7168) == 2048 * 28 * 66
     assert M.q2_packed_bytes(4, 7, 300) == 0
+    assert M.q2_packed_bytes(8, 7, 300) == 0
     L = _layer()
     for path in (0, 1, 2):
         a, b = M.workspace_bytes(L, 4, path), M.workspace_bytes(L, 400, path)
@@ -188,20 +199,20 @@ def test_sizes():
         "ok", "invalid argument", "unsupported", "workspace too small", "HIP error"]
 
 
-@pytest.mark.parametrize("fmt", [F.CB2, F.Q2K, F.Q4K, F.Q5K, F.Q6K])
+@pytest.mark.parametrize("fmt", [F.CB2, F.Q2K, F.Q4K, F.Q5K, F.Q6K, F.CB2S])
 @pytest.mark.parametrize("shape", [(1, 256), (7, 100), (33, 384), (5, 1000)])
 def test_pack_matches_oracle_bytes(fmt, shape):
     rng = np.random.default_rng(hash((fmt, shape)) % 2**32)
     w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
-    assert np.array_equal(M.q2_pack(fmt, w, CB), F.pack(fmt, w, CB))
+    assert np.array_equal(M.q2_pack(fmt, w, _cb(fmt)), F.pack(fmt, w, _cb(fmt)))
 
 
 def test_pack_matches_oracle_on_workload_rows():
     cfg = S.config("decode1")
     for which, fmt in (("gate", F.CB2), ("down", F.Q2K), ("down", F.Q4K), ("up", F.Q4K), ("up", F.Q5K),
-                       ("down", F.Q6K), ("gate", F.Q2K)):
+                       ("down", F.Q6K), ("gate", F.Q2K), ("gate", F.CB2S), ("up", F.CB2S)):
         w = S.expert_weight(cfg, which, 17)[:96]
-        assert np.array_equal(M.q2_pack(fmt, w, CB), F.pack(fmt, w, CB)), which
+        assert np.array_equal(M.q2_pack(fmt, w, _cb(fmt)), F.pack(fmt, w, _cb(fmt))), which
 
 
 def test_pack_edge_values():
@@ -212,8 +223,8 @@ def test_pack_edge_values():
     rows[3] = np.abs(np.linspace(0.01, 0.3, 256, dtype=np.float32))
     rows[4, 7] = 30.0
     rows[5] = np.tile(np.array([1e-6, -2e-6], np.float32), 128)
-    for fmt in (F.CB2, F.Q2K, F.Q4K, F.Q5K, F.Q6K):
-        assert np.array_equal(M.q2_pack(fmt, rows, CB), F.pack(fmt, rows, CB)), fmt
+    for fmt in (F.CB2, F.Q2K, F.Q4K, F.Q5K, F.Q6K, F.CB2S):
+        assert np.array_equal(M.q2_pack(fmt, rows, _cb(fmt)), F.pack(fmt, rows, _cb(fmt))), fmt
 
 
 def test_probe_argument_checks():

@@ -40,12 +40,12 @@ def _gpu():
 
 
 # ------------------------------------------------------------------ unpack
-@pytest.mark.parametrize("fmt", [F.CB2, F.Q2K, F.Q4K, F.Q5K, F.Q6K])
+@pytest.mark.parametrize("fmt", [F.CB2, F.Q2K, F.Q4K, F.Q5K, F.Q6K, F.CB2S])
 @pytest.mark.parametrize("rows,K", [(1, 256), (5, 100), (19, 640), (64, 7168), (64, 2048)])
 def test_unpack_bit_exact(fmt, rows, K):
     rng = np.random.default_rng(rows * 1000 + K + fmt)
     w = (rng.standard_normal((rows, K)) * 0.02).astype(np.float32)
-    cb = S.codebook()
+    cb = S.codebook_for(fmt)
     p = F.pack(fmt, w, cb)
     ref = F.unpack(fmt, p, rows, K, cb)
     out = torch.full((rows, K), float("nan"), device="cuda")
@@ -443,6 +443,23 @@ def test_full_prefill8192_q4k(big_q4k):
     assert sampled_check(big_q4k, S.config("prefill8192_q4k"), False, 2, hot=8) <= PRE_TOL
 
 
+@pytest.fixture(scope="module")
+def big_cb2s():
+    return W.Workload(S.config("prefill2048_cb2s"), cache_dir=CACHE, progress=True)
+
+
+def test_full_prefill2048_cb2s(big_cb2s):
+    """The signed codebook format at the full layer shape: the in-register
+    dequant grouped GEMM, sampled tokens including the first and last rows of
+    the two most-assigned experts (the oracle packs every expert it reads and
+    checks the library's bytes against its own)."""
+    assert sampled_check(big_cb2s, S.config("prefill2048_cb2s"), False, 1, hot=2) <= PRE_TOL
+
+
+def test_full_decode32_cb2s(big_cb2s):
+    assert sampled_check(big_cb2s, S.config("decode32_cb2s"), True, 2) <= DEC_TOL
+
+
 # ------------------------------------------------------------------ router shapes
 # Router alone (the expert weights are never read by moe_route): every
 # selection-kernel specialisation at T = 1 (experts per lane 1, 2, 4, 8, 16),
@@ -504,9 +521,9 @@ def test_route_nan_token_stays_a_permutation(T):
 # the in-register-dequant grouped GEMMs: every output element, prefill with
 # multi-tile experts, decode batched and single-token, fp32 and bf16 x.
 FMT_PAIRS = [(S.FMT_Q5K, S.FMT_Q6K), (S.FMT_Q2K, S.FMT_Q5K), (S.FMT_Q4K, S.FMT_Q6K), (S.FMT_CB2, S.FMT_Q6K),
-             (S.FMT_Q5K, S.FMT_Q5K)]
-PAIR_IDS = ["%s_%s" % ({1: "cb2", 2: "q2k", 3: "q4k", 5: "q5k"}[a], {2: "q2k", 3: "q4k", 5: "q5k", 6: "q6k"}[b])
-            for a, b in FMT_PAIRS]
+             (S.FMT_Q5K, S.FMT_Q5K), (S.FMT_CB2S, S.FMT_Q2K), (S.FMT_CB2S, S.FMT_Q4K)]
+PAIR_IDS = ["%s_%s" % ({1: "cb2", 2: "q2k", 3: "q4k", 5: "q5k", 7: "cb2s"}[a],
+                       {2: "q2k", 3: "q4k", 5: "q5k", 6: "q6k"}[b]) for a, b in FMT_PAIRS]
 
 
 @pytest.mark.parametrize("fg,fd", FMT_PAIRS, ids=PAIR_IDS)
@@ -536,7 +553,7 @@ def test_decode_formats(small_cases, fg, fd, T, xdt):
     assert err <= DEC_TOL
 
 
-@pytest.mark.parametrize("recipe", ["q2-q4", "q5-q6"])
+@pytest.mark.parametrize("recipe", ["q2-q4", "q5-q6", "q2s"])
 def test_layer_recipe_stack(recipe):
     """A stack of four layers quantized by a per-layer recipe, each layer's fp32
     output the next layer's input (decode path), every layer's output compared
@@ -559,7 +576,7 @@ def test_layer_recipe_stack(recipe):
         seed = cfg["seed"]
         idx, w, _ = R.route(x_ref, S.router_weight(cfg, seed), cfg["top_k"])
         ex = {}
-        cb = S.codebook(seed)
+        cb = S.codebook_for(fg, seed)
         for e in np.unique(idx):
             mats = []
             for which, fmt, rows, K in (("gate", fg, cfg["inter"], cfg["hidden"]), ("up", fg, cfg["inter"], cfg["hidden"]),
