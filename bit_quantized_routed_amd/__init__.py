@@ -43,7 +43,18 @@ class Layer(ctypes.Structure):
                 ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
                 ("codebook", ctypes.c_void_p),
                 ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p),
-                ("w_router", ctypes.c_void_p)]
+                ("w_router", ctypes.c_void_p), ("expert_slot", ctypes.c_void_p)]
+
+
+class ExpertCacheC(ctypes.Structure):
+    """struct moe_expert_cache (host struct of device pointers)."""
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("n_slots", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("fmt_gate_up", ctypes.c_int32),
+                ("fmt_down", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("gate_bytes", ctypes.c_int64), ("down_bytes", ctypes.c_int64),
+                ("slots_gate", ctypes.c_void_p), ("slots_up", ctypes.c_void_p), ("slots_down", ctypes.c_void_p),
+                ("slot_of", ctypes.c_void_p), ("key_of", ctypes.c_void_p), ("stamp", ctypes.c_void_p),
+                ("ctl", ctypes.c_void_p), ("stats", ctypes.c_void_p)]
 
 
 class Profile(ctypes.Structure):
@@ -57,7 +68,8 @@ _lib = None
 # the C ABI declared in include/moe.h
 EXPORTS = ["moe_route", "moe_expert_ffn_decode", "moe_expert_ffn_prefill", "q2_pack", "q2_unpack",
            "q2_packed_bytes", "moe_workspace_bytes", "moe_status_str", "moe_last_error",
-           "moe_expert_ffn_decode_noalloc", "moe_layer_decode"]
+           "moe_expert_ffn_decode_noalloc", "moe_layer_decode", "moe_expert_cache_bytes", "moe_expert_cache_init",
+           "moe_expert_cache_map", "moe_expert_cache_prefetch"]
 NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 # measurement kernels the benchmark uses (csrc/moe_probe.h; not part of the layer's ABI)
 PROBE_EXPORTS = ["moe_probe_stream_read", "moe_probe_mfma_loop"]
@@ -94,6 +106,15 @@ def lib():
     L.moe_status_str.restype = ctypes.c_char_p
     L.moe_last_error.argtypes = []
     L.moe_last_error.restype = ctypes.c_char_p
+    cp = ctypes.POINTER(ExpertCacheC)
+    L.moe_expert_cache_bytes.argtypes = [lp, i32, i32]
+    L.moe_expert_cache_bytes.restype = sz
+    L.moe_expert_cache_init.argtypes = [cp, lp, i32, i32, vp, sz, vp]
+    L.moe_expert_cache_init.restype = i32
+    L.moe_expert_cache_map.argtypes = [cp, i32, lp, vp, i32, lp, vp]
+    L.moe_expert_cache_map.restype = i32
+    L.moe_expert_cache_prefetch.argtypes = [cp, i32, lp, vp, i32, vp]
+    L.moe_expert_cache_prefetch.restype = i32
     L.moe_probe_stream_read.argtypes = [vp, sz, i32, i32, vp, vp]
     L.moe_probe_stream_read.restype = i32
     L.moe_probe_mfma_loop.argtypes = [i32, i32, i32, vp, vp]
@@ -224,7 +245,7 @@ class DeviceLayer:
         self.sh_inter = sh_inter
         self.c = Layer(hidden, inter, n_experts, top_k, fmt_gate_up, fmt_down, sh_inter, flags,
                        _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(codebook),
-                       _ptr(sh_gate), _ptr(sh_up), _ptr(sh_down), _ptr(w_router))
+                       _ptr(sh_gate), _ptr(sh_up), _ptr(sh_down), _ptr(w_router), None)
 
     def workspace(self, T: int, path: int, device="cuda"):
         """A workspace for `path` at T tokens (the library needs no particular
@@ -262,3 +283,78 @@ def layer_decode(dl: DeviceLayer, x, act, T, bias, r: Routing, y, ws, stream=Non
 
 def ffn_prefill(dl: DeviceLayer, x, act, T, r: Routing, y, ws, stream=None, prof=None):
     moe_expert_ffn_prefill(dl.c, x, act, T, r.topk_idx, r.topk_w, r.offsets, r.perm, r.inv, y, ws, stream, prof)
+
+
+# ------------------------------------------------------------------ expert streaming
+class HostLayer(DeviceLayer):
+    """A layer whose routed weights (gate, up, down) live in pinned host
+    memory while the codebook, router and shared expert stay on the device:
+    the backing store of an expert cache."""
+
+    def __init__(self, dl: DeviceLayer):
+        import torch
+        w_gate, w_up, w_down = (t.cpu().pin_memory() for t in dl.tensors[:3])
+        codebook, w_router, sh_gate, sh_up, sh_down = dl.tensors[3:]
+        c = dl.c
+        super().__init__(c.hidden, c.inter, c.n_experts, c.top_k, c.fmt_gate_up, c.fmt_down, w_gate, w_up, w_down,
+                         codebook, w_router, sh_gate, sh_up, sh_down, c.sh_inter, c.flags)
+        assert all(t.is_pinned() for t in (w_gate, w_up, w_down)), torch.cuda.is_available()
+
+
+class LayerView:
+    """The layer view an expert cache hands out (struct moe_layer with the slot
+    arrays and the slot map); FFN calls take it like a device layer."""
+
+    def __init__(self, c: Layer, keep):
+        self.c, self._keep = c, keep
+
+    def workspace(self, T: int, path: int, device="cuda"):
+        import torch
+        return torch.zeros(max(workspace_bytes(self.c, T, path), 256), dtype=torch.uint8, device=device)
+
+
+def expert_cache_bytes(layer: Layer, n_layers: int, n_slots: int) -> int:
+    return int(lib().moe_expert_cache_bytes(ctypes.byref(layer), n_layers, n_slots))
+
+
+class ExpertCache:
+    """An HBM cache of n_slots routed-expert slots for n_layers layers of one
+    geometry (device memory held by a torch tensor)."""
+
+    def __init__(self, layer: Layer, n_layers: int, n_slots: int, stream=None, device="cuda"):
+        import torch
+        n = expert_cache_bytes(layer, n_layers, n_slots)
+        if n == 0:
+            raise ValueError("invalid cache geometry (n_layers=%d, n_slots=%d)" % (n_layers, n_slots))
+        self.mem = torch.empty(n, dtype=torch.uint8, device=device)
+        self.c = ExpertCacheC()
+        _check(lib().moe_expert_cache_init(ctypes.byref(self.c), ctypes.byref(layer), n_layers, n_slots,
+                                           _ptr(self.mem), n, _stream(stream)), "moe_expert_cache_init")
+
+    def _field(self, ptr, count, dtype):
+        off = ptr - self.mem.data_ptr()
+        return self.mem[off:off + count * dtype.itemsize].view(dtype)
+
+    def map(self, layer_id: int, host: DeviceLayer, topk_idx, T: int, stream=None) -> LayerView:
+        v = Layer()
+        _check(lib().moe_expert_cache_map(ctypes.byref(self.c), layer_id, ctypes.byref(host.c), _ptr(topk_idx), T,
+                                          ctypes.byref(v), _stream(stream)), "moe_expert_cache_map")
+        return LayerView(v, (self, host))
+
+    def prefetch(self, layer_id: int, host: DeviceLayer, experts, n: int, stream=None):
+        _check(lib().moe_expert_cache_prefetch(ctypes.byref(self.c), layer_id, ctypes.byref(host.c), _ptr(experts),
+                                               n, _stream(stream)), "moe_expert_cache_prefetch")
+
+    def stats(self):
+        """(hits, misses, bytes copied, calls) since init (synchronises)."""
+        import torch
+        return [int(v) for v in self._field(self.c.stats, 4, torch.int64).cpu()]
+
+    def slot_of(self, layer_id: int):
+        import torch
+        E = self.c.n_experts
+        return self._field(self.c.slot_of + 4 * E * layer_id, E, torch.int32)
+
+    def key_of(self):
+        import torch
+        return self._field(self.c.key_of, self.c.n_slots, torch.int32)

@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libmoe.so")
 
-HIP_SOURCES = ["route.hip", "ffn.hip", "prefill.hip", "decode.hip", "probe.hip", "api.hip"]
+HIP_SOURCES = ["route.hip", "ffn.hip", "prefill.hip", "decode.hip", "cache.hip", "probe.hip", "api.hip"]
 # plain host C++ (the quantizer); built at -O2 as C++: clang's -O3 loop
 # optimisation of the codebook search does not terminate in reasonable time
 HOST_SOURCES = ["pack.cpp"]

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <string>
 
+#include "cache.h"
 #include "decode.h"
 #include "devcache.h"
 #include "kernels.h"
@@ -108,6 +109,7 @@ int check_layer(const moe_layer *L)
                             L->sh_down, (const void *)L->w_router})
         if ((uintptr_t)ptr % 16) return set_error(MOE_ERR_INVALID_ARG, "layer pointer %p is not 16-byte aligned", ptr);
     if (L->sh_inter < 0) return set_error(MOE_ERR_INVALID_ARG, "sh_inter=%d < 0", L->sh_inter);
+    if ((uintptr_t)L->expert_slot % 4) return set_error(MOE_ERR_INVALID_ARG, "expert_slot is not 4-byte aligned");
     if (L->flags & ~MOE_LAYER_TOKENWISE_DECODE) return set_error(MOE_ERR_INVALID_ARG, "flags=%#x: unknown bits", L->flags);
     if (L->sh_inter > 0) {
         if (!L->sh_gate || !L->sh_up || !L->sh_down) return set_error(MOE_ERR_INVALID_ARG, "shared expert weights are NULL");
@@ -272,6 +274,7 @@ DecPass single_pass(const moe_layer *L, const FfnWs &w, int act)
     const int H = L->hidden, I = L->inter;
     d.T = 1; d.k = L->top_k; d.E = L->n_experts; d.H = H; d.I = I; d.Ish = L->sh_inter; d.nbI = nblocks(I);
     d.wg = (const uint8_t *)L->w_gate; d.wu = (const uint8_t *)L->w_up; d.wd = (const uint8_t *)L->w_down;
+    d.slot = L->expert_slot;
     d.gu_row_bytes = nblocks(H) * 38;
     d.gu_expert_bytes = (int64_t)d.gu_row_bytes * I;
     d.d_row_bytes = nblocks(I) * 84;
@@ -384,6 +387,7 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
     up.act = x; up.act_f32 = act == MOE_ACT_F32; up.act_by_token = 1; up.act_stride = H;
     up.out = w.h; up.out_f32 = prefill ? 0 : 1; up.out_stride = w.hstride;
     up.sched = w.sched;
+    up.slot = L->expert_slot;
 
     FfnPass dn = up;
     dn.fmt = L->fmt_down;
@@ -601,6 +605,9 @@ int moe_layer_decode(const moe_layer *L, const void *x, int act, int T, const fl
 {
     int rc = check_layer(L);
     if (rc) return rc;
+    if (L->expert_slot)
+        return set_error(MOE_ERR_UNSUPPORTED, "moe_layer_decode takes a resident layer; with an expert cache view "
+                         "call moe_route, moe_expert_cache_map, then moe_expert_ffn_decode");
     if (T < 0) return set_error(MOE_ERR_INVALID_ARG, "T=%d < 0", T);
     if (act != MOE_ACT_F32 && act != MOE_ACT_BF16) return set_error(MOE_ERR_INVALID_ARG, "act=%d unknown", act);
     if (prof) prof->n_launches = 0;
@@ -671,6 +678,139 @@ int q2_unpack(int fmt, const void *packed_dev, int64_t rows, int K, const int8_t
     hipError_t e = launch_unpack(fmt, (const uint8_t *)packed_dev, rows, K, codebook_dev, out_dev, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "q2_unpack launch");
     return MOE_OK;
+}
+
+// ------------------------------------------------------------ expert streaming
+namespace {
+
+struct CacheLayout {
+    int64_t gate_bytes, down_bytes;
+    size_t o_sg, o_su, o_sd, o_slot_of, o_key_of, o_stamp, o_ctl, o_stats, bytes;
+};
+
+bool cache_layout(const moe_layer *L, int n_layers, int n_slots, CacheLayout &c)
+{
+    if (!L || check_layer(L) || n_slots < 1 || n_slots > CACHE_MAX_SLOTS || n_layers < 1 ||
+        (int64_t)n_layers * L->n_experts >= ((int64_t)1 << 24))
+        return false;
+    c.gate_bytes = (int64_t)L->inter * nblocks(L->hidden) * bbytes(L->fmt_gate_up);
+    c.down_bytes = (int64_t)L->hidden * nblocks(L->inter) * bbytes(L->fmt_down);
+    if (c.gate_bytes % 16 || c.down_bytes % 16) return false;      // copied in 16-byte pieces (H, I % 8 == 0 give it)
+    size_t off = 0;
+    c.o_sg = off; off = align_up(off + (size_t)n_slots * c.gate_bytes);
+    c.o_su = off; off = align_up(off + (size_t)n_slots * c.gate_bytes);
+    c.o_sd = off; off = align_up(off + (size_t)n_slots * c.down_bytes);
+    c.o_slot_of = off; off = align_up(off + (size_t)n_layers * L->n_experts * sizeof(int32_t));
+    c.o_key_of = off; off = align_up(off + (size_t)n_slots * sizeof(int32_t));
+    c.o_stamp = off; off = align_up(off + (size_t)n_slots * sizeof(uint32_t));
+    c.o_ctl = off; off = align_up(off + (size_t)cache_ctl_len(L->n_experts) * sizeof(int32_t));
+    c.o_stats = off; off = align_up(off + 4 * sizeof(uint64_t));
+    c.bytes = off;
+    return true;
+}
+
+// the device address of host memory the GPU may read (pinned, mapped)
+int mapped(const void *host, const void **dev, const char *what)
+{
+    void *d = nullptr;
+    const hipError_t e = hipHostGetDevicePointer(&d, const_cast<void *>(host), 0);
+    if (e != hipSuccess || !d) {
+        (void)hipGetLastError();
+        return set_error(MOE_ERR_INVALID_ARG, "%s is not pinned host memory the GPU can read (%s)", what,
+                         hipGetErrorString(e));
+    }
+    *dev = d;
+    return MOE_OK;
+}
+
+// resolve `n` expert ids of layer `layer_id` and fetch the misses
+int cache_load(moe_expert_cache *c, int layer_id, const moe_layer *H, const int32_t *ids, int n, void *stream)
+{
+    if (!c || !H || !ids) return set_error(MOE_ERR_INVALID_ARG, "NULL cache, layer or expert ids");
+    int rc = check_layer(H);
+    if (rc) return rc;
+    if (H->hidden != c->hidden || H->inter != c->inter || H->n_experts != c->n_experts ||
+        H->fmt_gate_up != c->fmt_gate_up || H->fmt_down != c->fmt_down)
+        return set_error(MOE_ERR_INVALID_ARG, "the layer's shape or formats differ from the cache's");
+    if (layer_id < 0 || layer_id >= c->n_layers)
+        return set_error(MOE_ERR_INVALID_ARG, "layer_id=%d outside [0, %d)", layer_id, c->n_layers);
+    if (n < 0) return set_error(MOE_ERR_INVALID_ARG, "%d expert ids", n);
+    if (std::min(n, c->n_experts) > c->n_slots)
+        return set_error(MOE_ERR_UNSUPPORTED, "a call may need %d experts, the cache has %d slots",
+                         std::min(n, c->n_experts), c->n_slots);
+    const void *hg, *hu, *hd;
+    if ((rc = mapped(H->w_gate, &hg, "w_gate")) || (rc = mapped(H->w_up, &hu, "w_up")) ||
+        (rc = mapped(H->w_down, &hd, "w_down")))
+        return rc;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_cache_resolve(ids, n, c->n_experts, c->n_slots, layer_id * c->n_experts, c->slot_of,
+                                        c->key_of, c->stamp, c->ctl, c->stats, 2 * c->gate_bytes + c->down_bytes, s);
+    if (e != hipSuccess) return hip_fail(e, "cache resolve launch");
+    e = launch_cache_fetch(c->ctl, (const uint8_t *)hg, (const uint8_t *)hu, (const uint8_t *)hd,
+                           (uint8_t *)c->slots_gate, (uint8_t *)c->slots_up, (uint8_t *)c->slots_down,
+                           c->gate_bytes, c->down_bytes, s);
+    if (e != hipSuccess) return hip_fail(e, "cache fetch launch");
+    return MOE_OK;
+}
+
+}  // namespace
+
+size_t moe_expert_cache_bytes(const moe_layer *L, int n_layers, int n_slots)
+{
+    CacheLayout c;
+    return cache_layout(L, n_layers, n_slots, c) ? c.bytes : 0;
+}
+
+int moe_expert_cache_init(moe_expert_cache *c, const moe_layer *L, int n_layers, int n_slots, void *dev,
+                          size_t dev_bytes, void *stream)
+{
+    if (!c || !L) return set_error(MOE_ERR_INVALID_ARG, "NULL cache or layer");
+    int rc = check_layer(L);
+    if (rc) return rc;
+    CacheLayout lay;
+    if (!cache_layout(L, n_layers, n_slots, lay))
+        return set_error(MOE_ERR_INVALID_ARG, "n_layers=%d n_slots=%d (1..%d slots, n_layers * n_experts < 2^24)",
+                         n_layers, n_slots, CACHE_MAX_SLOTS);
+    if (!dev || (uintptr_t)dev % ALIGN) return set_error(MOE_ERR_INVALID_ARG, "device memory NULL or not 256-byte aligned");
+    if (dev_bytes < lay.bytes) return set_error(MOE_ERR_WORKSPACE, "cache memory %zu < %zu bytes", dev_bytes, lay.bytes);
+    char *b = (char *)dev;
+    moe_expert_cache x{};
+    x.n_layers = n_layers; x.n_experts = L->n_experts; x.n_slots = n_slots;
+    x.hidden = L->hidden; x.inter = L->inter; x.fmt_gate_up = L->fmt_gate_up; x.fmt_down = L->fmt_down;
+    x.gate_bytes = lay.gate_bytes; x.down_bytes = lay.down_bytes;
+    x.slots_gate = b + lay.o_sg; x.slots_up = b + lay.o_su; x.slots_down = b + lay.o_sd;
+    x.slot_of = (int32_t *)(b + lay.o_slot_of);
+    x.key_of = (int32_t *)(b + lay.o_key_of);
+    x.stamp = (uint32_t *)(b + lay.o_stamp);
+    x.ctl = (int32_t *)(b + lay.o_ctl);
+    x.stats = (uint64_t *)(b + lay.o_stats);
+    const hipError_t e = launch_cache_clear(x.slot_of, (int64_t)n_layers * L->n_experts, x.key_of, x.stamp, n_slots,
+                                            x.ctl, cache_ctl_len(L->n_experts), x.stats, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "cache clear launch");
+    *c = x;
+    return MOE_OK;
+}
+
+int moe_expert_cache_map(moe_expert_cache *c, int layer_id, const moe_layer *host_layer, const int32_t *topk_idx,
+                         int T, moe_layer *view, void *stream)
+{
+    if (!view) return set_error(MOE_ERR_INVALID_ARG, "NULL view");
+    if (!host_layer) return set_error(MOE_ERR_INVALID_ARG, "NULL layer");
+    if (T < 0 || (int64_t)T * host_layer->top_k > (1 << 30)) return set_error(MOE_ERR_INVALID_ARG, "T=%d", T);
+    int rc = cache_load(c, layer_id, host_layer, topk_idx, T * host_layer->top_k, stream);
+    if (rc) return rc;
+    *view = *host_layer;
+    view->w_gate = c->slots_gate;
+    view->w_up = c->slots_up;
+    view->w_down = c->slots_down;
+    view->expert_slot = c->slot_of + (size_t)layer_id * c->n_experts;
+    return MOE_OK;
+}
+
+int moe_expert_cache_prefetch(moe_expert_cache *c, int layer_id, const moe_layer *host_layer,
+                              const int32_t *experts_dev, int n, void *stream)
+{
+    return cache_load(c, layer_id, host_layer, experts_dev, n, stream);
 }
 
 int moe_probe_stream_read(const void *buf, size_t bytes, int grid, int nontemporal, void *sink, void *stream)

@@ -10,6 +10,7 @@ struct DecPass {
     const int32_t *topk_idx, *offsets, *inv;
     const float *topk_w;
     const uint8_t *wg, *wu, *wd;                 // routed CB2 gate, up; Q2_K down
+    const int32_t *slot;                         // null, or expert -> index of its matrices (expert cache view)
     int64_t gu_expert_bytes, d_expert_bytes;
     int gu_row_bytes, d_row_bytes;
     const uint16_t *sg, *su, *sd;                // shared expert bf16 (Ish == 0: none)

@@ -101,6 +101,9 @@ __device__ __forceinline__ void act_block(const uint16_t *row, int k0, int step,
 }
 
 __device__ __forceinline__ int clamp_expert(int g, int E) { return min(max(g, 0), E - 1); }
+// index of expert e's matrices in the routed weight arrays (an expert cache
+// view maps experts to slots)
+__device__ __forceinline__ int expert_matrix(const DecPass &p, int e) { return p.slot ? max(p.slot[e], 0) : e; }
 
 // ============================================================== gate / up
 // One kernel, three launch modes:
@@ -419,7 +422,7 @@ __global__ __launch_bounds__(GU_THREADS) void dec1_gateup_kernel(DecPass p)
             select_one<MAXPL>(p.rpart, p.bias, p.E, p.k, p.rnc, lane, p.o_idx, p.o_w, p.o_off, p.o_perm, p.o_inv,
                               u == 0, kid, nullptr);
     } else if (tid < p.k) {
-        kid[tid] = clamp_expert(p.topk_idx[tid], p.E);
+        kid[tid] = expert_matrix(p, clamp_expert(p.topk_idx[tid], p.E));
     }
     __syncthreads();                                              // expert ids staged
     // this wave's block of the chunk; waves past a short chunk re-read its
@@ -629,7 +632,7 @@ __global__ __launch_bounds__(D1_THREADS) void dec1_down_kernel(DecPass p)
     uint16_t *hh = tab + 16 * 256 * 4;                             // [k][nb*256] hi
     uint16_t *hl = hh + p.k * nb * 256;                            // [k][nb*256] lo
     float *xm = (float *)(hl + p.k * nb * 256);                    // [k][nb][16] sub-block sums of h
-    if (tid < p.k) kid[tid] = clamp_expert(p.topk_idx[tid], p.E);
+    if (tid < p.k) kid[tid] = expert_matrix(p, clamp_expert(p.topk_idx[tid], p.E));
     __syncthreads();
     // two register buffers in turn, per block: this lane's 16 code bytes, the
     // sc|m bytes of its four sub-blocks, and d|dmin.  While one unit is
@@ -901,7 +904,7 @@ __global__ __launch_bounds__(DF_THREADS) void dec1_down_fused_kernel(DecPass p, 
     float *xm = (float *)(hl + k * I);                             // [k][nb][16]
     uint16_t *sh = (uint16_t *)(xm + k * nb * 16);                 // [Ish] shared h hi
     uint16_t *sl = sh + Ish;                                       // [Ish] lo
-    if (tid < k) kid[tid] = clamp_expert(p.topk_idx[tid], p.E);
+    if (tid < k) kid[tid] = expert_matrix(p, clamp_expert(p.topk_idx[tid], p.E));
     __syncthreads();                                               // expert ids
     // h (every slot), its per-16 sums and shared h: loaded into registers
     // before any weight byte is requested, so that storing them into LDS

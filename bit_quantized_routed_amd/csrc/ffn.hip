@@ -115,6 +115,7 @@ void launch_sh_finalize(const float *part, int KS, int T, int I, int Tk, uint16_
 // ============================================================== tile helpers
 struct Tile {
     int g, m0, n0, Ng, Kg, row0, nvalid;
+    int w;                                         // index of the routed group's matrices in w0 / w1
     bool sh;
 };
 
@@ -136,6 +137,7 @@ __device__ __forceinline__ bool tile_of(const FfnPass &p, int BM, int BN, Tile &
     else { pb = min(max(p.offsets[t.g], 0), Tk); pe = min(max(p.offsets[t.g + 1], pb), Tk); }
     t.row0 = pb + t.m0;
     t.nvalid = min(BM, pe - t.row0);
+    t.w = t.sh ? 0 : p.slot ? max(p.slot[t.g], 0) : t.g;
     return t.nvalid > 0;
 }
 
@@ -289,7 +291,7 @@ __device__ __forceinline__ void decode_tile(const FfnPass &p, const Tile &t, L *
                         load32_bf16(srow(p, m, t.Kg, r), s * KS + 32 * q, t.Kg, v);
                         dsc = 1.f;
                     } else {
-                        const uint8_t *blk = wrow(p, m, t.g, r) + (int64_t)(s >> 1) * BB;
+                        const uint8_t *blk = wrow(p, m, t.w, r) + (int64_t)(s >> 1) * BB;
                         const int k0 = (s & 1) * KS + 32 * q;
                         if (FMTW == FMT_CB2) unit_cb2<true>(blk, k0, p.codebook, v, &dsc);
                         else unit_q2k<true>(blk, k0, v, &dsc, &dmn, m2);
@@ -450,7 +452,7 @@ __device__ __forceinline__ void prefill_tile(const FfnPass &p, const Tile &t, ui
                 if (FMTW == FMT_BF16) {
                     load32_bf16(srow(p, m, t.Kg, r), s * KS + 32 * q, t.Kg, v);
                 } else {
-                    const uint8_t *blk = wrow(p, m, t.g, r) + (int64_t)(s >> 1) * BB;
+                    const uint8_t *blk = wrow(p, m, t.w, r) + (int64_t)(s >> 1) * BB;
                     const int k0 = (s & 1) * KS + 32 * q;
                     float dd, dm;
                     int m2[2];

@@ -36,6 +36,7 @@ struct FfnPass {
     float *sh_part_out;               // null: shared rows go to out like the others
     int sched_parts;                  // shared K parts the schedule was built with (>= sh_parts; 0 or 1: one);
                                       // the launch grid covers every tile of that schedule
+    const int32_t *slot;              // null, or expert -> index of its matrices in w0/w1 (expert cache view)
 };
 
 // tiles of BM rows per routed group and BMsh (<= 0: BM) for the shared group,

@@ -69,6 +69,7 @@ __device__ __forceinline__ float ubyte(uint32_t v, int i) { return (float)((v >>
 
 struct NpTile {
     int g, row0, nvalid, Ng, Kg, n0;
+    int w;                            // index of the routed group's matrices in w0 / w1
     int part, k0, Kfull;              // shared expert: K part, its first K, full K
     bool sh;
 };
@@ -99,6 +100,7 @@ __device__ __forceinline__ bool np_tile(const FfnPass &p, int S, int wg_cols, in
     else { pb = min(max(p.offsets[t.g], 0), Tk); pe = min(max(p.offsets[t.g + 1], pb), Tk); }
     t.row0 = pb + m0;
     t.nvalid = min(t.sh ? bm_sh : bm, pe - t.row0);
+    t.w = t.sh ? 0 : p.slot ? max(p.slot[t.g], 0) : t.g;
     return t.nvalid > 0;
 }
 
@@ -633,8 +635,8 @@ __device__ __forceinline__ void np_body_r(const FfnPass &p, const NpTile &t, uin
     const uint8_t *wb0, *wb1;
     if (FMT == FMT_BF16) { wb0 = (const uint8_t *)p.s0; wb1 = (const uint8_t *)p.s1; }
     else {
-        wb0 = p.w0 + (int64_t)t.g * p.w_expert_bytes;
-        wb1 = GATEUP ? p.w1 + (int64_t)t.g * p.w_expert_bytes : wb0;
+        wb0 = p.w0 + (int64_t)t.w * p.w_expert_bytes;
+        wb1 = GATEUP ? p.w1 + (int64_t)t.w * p.w_expert_bytes : wb0;
     }
     uint32_t wo[4];
 #pragma unroll
@@ -900,7 +902,7 @@ __device__ __forceinline__ void np_body32_down(const FfnPass &p, const NpTile &t
     for (int s8 = 0; s8 < 8; ++s8) aoff[s8] = c32 * 256 + (((8 * kg + s8) ^ (c32 & 15)) << 4);
 
     // ---- weight rows of this lane's two column fragments
-    const uint8_t *wb = p.w0 + (int64_t)t.g * p.w_expert_bytes;
+    const uint8_t *wb = p.w0 + (int64_t)t.w * p.w_expert_bytes;
     const uint8_t *wr[2];
 #pragma unroll
     for (int cf = 0; cf < 2; ++cf) {

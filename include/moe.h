@@ -139,6 +139,15 @@ enum moe_path { MOE_PATH_ROUTE = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2, M
  *     relative, not bit for bit.  It needs a layer the single-token kernels
  *     take (CB2 gate/up, Q2K down; see moe_expert_ffn_decode), otherwise
  *     decode returns MOE_ERR_UNSUPPORTED.  Other bits: MOE_ERR_INVALID_ARG.
+ *   expert_slot: NULL, or a device int32 [n_experts] map from expert to slot:
+ *     the FFN calls then read expert e's routed weights at w_* + expert_slot[e]
+ *     * (bytes of one expert's matrix) -- the layer view of an expert cache
+ *     (moe_expert_cache_map fills one in; every expert the routing selects
+ *     must map to a slot the weight arrays hold).  Nothing else changes:
+ *     routing, tiles and sums are those of the resident layer, so y is
+ *     bit-identical.  The router and moe_layer_decode's fused single-token
+ *     path need the resident layout (moe_layer_decode returns
+ *     MOE_ERR_UNSUPPORTED for a view).
  *   Every pointer must be 16-byte aligned (device allocations are); the
  *   kernels read weights and the codebook in 8- and 16-byte pieces. */
 #define MOE_LAYER_TOKENWISE_DECODE 1
@@ -150,6 +159,7 @@ typedef struct moe_layer {
     const int8_t *codebook;
     const void *sh_gate, *sh_up, *sh_down;
     const float *w_router;
+    const int32_t *expert_slot;
 } moe_layer;
 
 /* Optional per-kernel timing.  When `prof` is non-NULL and prof->kernel is
@@ -265,6 +275,62 @@ int moe_expert_ffn_decode_noalloc(const moe_layer *L, const void *x, int act, in
                                   const int32_t *topk_idx, const float *topk_w, const int32_t *offsets,
                                   const int32_t *perm, const int32_t *inv, float *y, void *stream,
                                   moe_profile *prof);
+
+/* ------------------------------------------------------------ expert streaming
+ * An HBM-resident cache of routed-expert slots for layers whose routed
+ * weights live in pinned host memory: the non-routed weights (router, shared
+ * expert, codebook) stay resident, each slot holds one whole expert (gate, up
+ * and down), and a miss is copied from host memory into a slot by the GPU
+ * itself, with no host round trip -- the MI355X form of the pages' streaming
+ * mode, which keeps routed experts in a cache of dynamic expert slots and
+ * loads them on a miss ("DwarfStar" README and the "ds4" README mirror,
+ * section on running models larger than RAM).
+ *
+ * moe_expert_cache_bytes: device bytes a cache of n_slots slots for n_layers
+ *   layers of L's geometry (hidden, inter, n_experts, formats) needs; 0 if
+ *   invalid (1 <= n_slots <= 8192, 1 <= n_layers, n_layers * n_experts <
+ *   2^24).
+ * moe_expert_cache_init: carve the cache out of dev (dev_bytes >= the size
+ *   above, 256-byte aligned; owned by the caller, which keeps it alive and
+ *   must not touch it while the cache is in use) and clear it on `stream`
+ *   (every slot empty).  Fills *c (host memory).
+ * moe_expert_cache_map: for layer layer_id, make every expert that
+ *   topk_idx [T][k] (device, from moe_route) selects resident, and fill *view
+ *   with the layer view the FFN calls take: host_layer with w_gate, w_up,
+ *   w_down set to the slot arrays and expert_slot to the layer's slot map.
+ *   host_layer is the layer with its routed weights in pinned host memory
+ *   (hipHostMalloc; device-accessible), its other pointers in device memory.
+ *   On `stream`: one work-group resolves hits and misses and picks victims
+ *   -- the least recently used slots not needed by this call, ties to the
+ *   lower slot -- then a copy kernel pulls each miss's three matrices from
+ *   host memory into its slot.  Needs n_slots >= min(n_experts, T * k) so
+ *   that the whole call fits (MOE_ERR_UNSUPPORTED otherwise).
+ * moe_expert_cache_prefetch: the same for the n expert ids in experts_dev
+ *   (device int32; duplicates allowed), without a view: run it on another
+ *   stream to load a layer's experts while the previous layer computes.
+ *   Calls on one cache must not overlap in time (one stream, or ordered by
+ *   events): they update its slot state.  Overlap loads with compute by
+ *   giving consecutive layers their own caches (the pages reserve two full
+ *   routed layers for overlapped streaming prefill, same section).
+ * c->stats (device uint64 [4]): hits, misses, bytes copied and calls, summed
+ *   since init. */
+typedef struct moe_expert_cache {
+    int32_t n_layers, n_experts, n_slots, hidden, inter, fmt_gate_up, fmt_down, reserved0;
+    int64_t gate_bytes, down_bytes;           /* one expert's gate (= up) and down matrix */
+    void *slots_gate, *slots_up, *slots_down; /* device [n_slots][bytes] */
+    int32_t *slot_of;                         /* device [n_layers][n_experts], -1 = absent */
+    int32_t *key_of;                          /* device [n_slots]: layer * n_experts + expert, or -1 */
+    uint32_t *stamp;                          /* device [n_slots]: call counter at last use */
+    int32_t *ctl;                             /* device: clock, fetch count, fetch list */
+    uint64_t *stats;                          /* device [4] */
+} moe_expert_cache;
+size_t moe_expert_cache_bytes(const moe_layer *L, int n_layers, int n_slots);
+int moe_expert_cache_init(moe_expert_cache *c, const moe_layer *L, int n_layers, int n_slots, void *dev,
+                          size_t dev_bytes, void *stream);
+int moe_expert_cache_map(moe_expert_cache *c, int layer_id, const moe_layer *host_layer, const int32_t *topk_idx,
+                         int T, moe_layer *view, void *stream);
+int moe_expert_cache_prefetch(moe_expert_cache *c, int layer_id, const moe_layer *host_layer,
+                              const int32_t *experts_dev, int n, void *stream);
 
 /* ------------------------------------------------------------ pack / unpack
  * q2_pack (host): quantize a row-major fp32 matrix w_host [rows][K] into

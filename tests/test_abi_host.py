@@ -236,3 +236,61 @@ def test_probe_argument_checks():
     assert L.moe_probe_mfma_loop(0, 1, 0, FAKE, None) == -1
     assert L.moe_probe_mfma_loop(0, 1, 1, None, None) == -1
     assert L.moe_probe_mfma_loop(2, 1, 1, FAKE, None) == -1
+
+
+# ------------------------------------------------------------------ expert cache (host checks only)
+def _cache_struct(layer, n_layers=2, n_slots=4):
+    c = M.ExpertCacheC()
+    c.n_layers, c.n_experts, c.n_slots = n_layers, layer.n_experts, n_slots
+    c.hidden, c.inter, c.fmt_gate_up, c.fmt_down = layer.hidden, layer.inter, layer.fmt_gate_up, layer.fmt_down
+    return c
+
+
+def test_expert_cache_sizes():
+    L = _layer()
+    per = 2 * M.q2_packed_bytes(1, 128, 256) + M.q2_packed_bytes(2, 256, 128)
+    b = M.expert_cache_bytes(L, 3, 5)
+    assert b >= 5 * per + 3 * 8 * 4
+    assert M.expert_cache_bytes(L, 3, 6) > b
+    for nl, ns in ((0, 4), (1, 0), (1, 8193), (1 << 22, 4)):
+        assert M.expert_cache_bytes(L, nl, ns) == 0
+    assert M.expert_cache_bytes(_layer(top_k=0), 1, 4) == 0
+
+
+def test_expert_cache_init_validation():
+    I = M.lib().moe_expert_cache_init
+    L = _layer()
+    c = M.ExpertCacheC()
+    need = M.expert_cache_bytes(L, 1, 4)
+    assert I(None, ctypes.byref(L), 1, 4, FAKE, need, None) == -1
+    assert I(ctypes.byref(c), ctypes.byref(L), 1, 0, FAKE, need, None) == -1
+    assert I(ctypes.byref(c), ctypes.byref(L), 1, 4, FAKE + 16, need, None) == -1      # 256-byte alignment
+    assert I(ctypes.byref(c), ctypes.byref(L), 1, 4, FAKE, need - 1, None) == -3
+
+
+def test_expert_cache_map_validation():
+    Mp, Pf = M.lib().moe_expert_cache_map, M.lib().moe_expert_cache_prefetch
+    L = _layer()
+    c = _cache_struct(L, n_layers=2, n_slots=4)
+    v = M.Layer()
+    call = lambda lid=0, lay=L, T=2, view=v, cache=c: Mp(ctypes.byref(cache) if cache is not None else None, lid,
+                                                         ctypes.byref(lay), FAKE, T, ctypes.byref(view) if view is not None else None, None)
+    assert call(view=None) == -1
+    assert call(cache=None) == -1
+    assert call(lid=2) == -1 and b"layer_id" in M.lib().moe_last_error()
+    assert call(lid=-1) == -1
+    assert call(lay=_layer(inter=256)) == -1 and b"differ" in M.lib().moe_last_error()
+    assert call(lay=_layer(fmt_down=3)) == -1
+    assert call(T=-1) == -1
+    # T * k = 6 experts may be needed, only 4 slots: refused before any launch
+    assert call(T=3) == -2 and b"slots" in M.lib().moe_last_error()
+    assert Pf(ctypes.byref(c), 0, ctypes.byref(L), FAKE, 5, None) == -2
+    assert Pf(ctypes.byref(c), 0, ctypes.byref(L), None, 3, None) == -1
+
+
+def test_layer_decode_refuses_a_cache_view():
+    F_ = M.lib().moe_layer_decode
+    L = _layer(expert_slot=FAKE)
+    assert F_(ctypes.byref(L), FAKE, 1, 1, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None, None) == -2
+    assert b"moe_expert_cache_map" in M.lib().moe_last_error()
+    assert _ffn(M.lib().moe_expert_ffn_decode, _layer(expert_slot=FAKE + 2)) == -1      # alignment
