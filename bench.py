@@ -624,6 +624,150 @@ def measure(wl, cfg, name, steps, warmup, with_cpu):
     return value, out
 
 
+HOST_LINK_PEAK_GBS = 64.0     # PCIe 5.0 x16, one direction
+
+
+def measure_stream(wl, steps, warmup, n_slots):
+    """Expert streaming on the full layer: its routed experts in pinned host
+    memory, an HBM cache of n_slots slots.  Decode: single-token steps over a
+    stream of distinct tokens (route, cache map -- resolve plus the copy of the
+    misses -- and the decode FFN on the cache view), with the hit rate and the
+    copy kernel's rate from host memory.  Prefill: a 2048-token layer call
+    while the next layer's experts are loaded into a second cache on another
+    stream, against the same two steps one after the other."""
+    import numpy as np
+    import torch
+    import synthetic as S
+    import bit_quantized_routed_amd as M
+    base = wl.layer
+    host = M.HostLayer(base)
+    cache = M.ExpertCache(base.c, 1, n_slots)
+    cfg1 = S.config("decode1")
+    xs, act = wl.tokens(S.config("prefill2048"))          # 2048 distinct tokens, one per step
+    T1 = 1
+    r = M.Routing(T1, cfg1["top_k"], cfg1["n_experts"])
+    ws_r = base.workspace(T1, M.PATH_ROUTE)
+    y = torch.empty((T1, cfg1["hidden"]), device="cuda")
+    ws_f = None
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        nonlocal ws_f
+        x = xs[i % xs.shape[0]:i % xs.shape[0] + 1]
+        M.route(base, x, act, T1, None, r, ws_r)
+        if ev:
+            ev[0].record()
+        view = cache.map(0, host, r.topk_idx, T1)
+        if ev:
+            ev[1].record()
+        if ws_f is None:
+            ws_f = view.workspace(T1, M.PATH_DECODE)
+        M.ffn_decode(view, x, act, T1, r, y, ws_f)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    h0, m0, b0, _ = cache.stats()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    maps = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        pairs[i][0].record()
+        step(warmup + i, maps[i])
+        pairs[i][1].record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in pairs])
+    tm = np.array([a.elapsed_time(b) for a, b in maps])
+    h1, m1, b1, _ = cache.stats()
+    hits, misses, nbytes = h1 - h0, m1 - m0, b1 - b0
+    fetch_gbs = nbytes / (tm.sum() * 1e-3) / 1e9 if tm.sum() > 0 else None
+    dec = {"n_slots": n_slots, "experts": cfg1["n_experts"], "steps": steps,
+           "ms_per_step": {"median": round(float(np.median(t)), 4), "p10": round(float(np.percentile(t, 10)), 4),
+                           "p90": round(float(np.percentile(t, 90)), 4)},
+           "hit_rate": round(hits / max(hits + misses, 1), 4), "misses_per_step": round(misses / steps, 3),
+           "copied_bytes_per_step": int(nbytes / steps),
+           "map_ms_per_step": round(float(tm.mean()), 4),
+           "roofline": {"bound": "host-link", "kernel": "cache map (resolve + copy of the misses)",
+                        "achieved": round(fetch_gbs, 2) if fetch_gbs else None, "peak": HOST_LINK_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(fetch_gbs / HOST_LINK_PEAK_GBS, 4) if fetch_gbs else None}}
+    # the same bytes by the copy engines (pinned host -> device), for context
+    src = host.tensors[0]
+    dst = torch.empty_like(src, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        dst.copy_(src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    dec["copy_engine_GBps"] = round(3 * src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9, 2)
+    del dst
+    log("decode1_stream: %s" % dec)
+
+    # prefill: the next layer's experts load on a second stream during this layer's call
+    cfgp = S.config("prefill2048")
+    xp, actp = wl.tokens(cfgp)
+    T = xp.shape[0]
+    rp = M.Routing(T, cfgp["top_k"], cfgp["n_experts"])
+    ws_rp = base.workspace(T, M.PATH_ROUTE)
+    yp = torch.empty((T, cfgp["hidden"]), device="cuda")
+    E = cfgp["n_experts"]
+    full = [M.ExpertCache(base.c, 1, E), M.ExpertCache(base.c, 1, E)]
+    experts = torch.arange(E, dtype=torch.int32, device="cuda")
+    copy_stream = torch.cuda.Stream()
+    M.route(base, xp, actp, T, None, rp, ws_rp)
+    full[0].prefetch(0, host, experts, E)
+    view = full[0].map(0, host, rp.topk_idx, T)
+    ws_p = view.workspace(T, M.PATH_PREFILL)
+    torch.cuda.synchronize()
+
+    def layer_call():
+        M.route(base, xp, actp, T, None, rp, ws_rp)
+        v = full[0].map(0, host, rp.topk_idx, T)           # all hits: loaded before
+        M.ffn_prefill(v, xp, actp, T, rp, yp, ws_p)
+
+    def timed(fn, reps=3):
+        out = []
+        for _ in range(reps):
+            full[1] = M.ExpertCache(base.c, 1, E)              # empty: the next layer's experts all miss
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            out.append((time.perf_counter() - t0) * 1e3)
+        return float(np.median(out))
+
+    def serial():
+        full[1].prefetch(0, host, experts, E)
+        layer_call()
+
+    def overlapped():
+        ready = torch.cuda.Event()
+        with torch.cuda.stream(copy_stream):
+            full[1].prefetch(0, host, experts, E, stream=copy_stream)
+            ready.record(copy_stream)
+        layer_call()
+        stream.wait_event(ready)
+
+    t_layer = timed(layer_call)
+    t_fetch = timed(lambda: full[1].prefetch(0, host, experts, E))
+    t_serial, t_over = timed(serial), timed(overlapped)
+    per_expert = 2 * base_bytes(wl.cfg)[0] + base_bytes(wl.cfg)[1]
+    pre = {"T": T, "layer_ms": round(t_layer, 3), "next_layer_fetch_ms": round(t_fetch, 3),
+           "next_layer_fetch_GBps": round(E * per_expert / (t_fetch * 1e-3) / 1e9, 2),
+           "serial_ms": round(t_serial, 3), "overlapped_ms": round(t_over, 3),
+           "hidden_fraction_of_layer": round((t_serial - t_over) / t_layer, 3) if t_layer > 0 else None}
+    log("prefill2048_stream: %s" % pre)
+    return {"decode1_stream": dec, "prefill2048_stream": pre}
+
+
+def base_bytes(cfg):
+    import bit_quantized_routed_amd as M
+    H, I = cfg["hidden"], cfg["inter"]
+    return M.q2_packed_bytes(cfg["fmt_gate_up"], I, H), M.q2_packed_bytes(cfg["fmt_down"], H, I)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -636,6 +780,8 @@ def main():
     ap.add_argument("--extra-steps", type=int, default=20, help="minimum timed steps of each extra workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the machine-ceiling probes")
+    ap.add_argument("--stream-slots", type=int, default=128,
+                    help="HBM slots of the expert-streaming measurement (0: skip it)")
     ap.add_argument("--sweep", action="store_true",
                     help="only the micro-batch sweep: decode and prefill paths at T = 1..64 on the full layer "
                          "(Zipf-skewed routing), with the crossover T; one JSON line")
@@ -694,6 +840,9 @@ def main():
         wl2 = layer_for(c2, min(args.replicas, 2))
         _, workloads[name] = measure(wl2, c2, name, max(args.extra_steps, args.steps // 10),
                                      max(2, args.warmup // 4), not args.no_cpu_baseline)
+    if args.stream_slots > 0 and args.extra:
+        workloads.update(measure_stream(layer_for(S.config("decode1"), args.replicas), max(args.extra_steps, 50),
+                                        10, args.stream_slots))
 
     ceil = None
     roof = head["roofline"]

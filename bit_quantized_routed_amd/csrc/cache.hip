@@ -199,9 +199,11 @@ hipError_t launch_cache_fetch(const int32_t *ctl, const uint8_t *hg, const uint8
                               uint8_t *sg, uint8_t *su, uint8_t *sd, int64_t gate_bytes, int64_t down_bytes,
                               hipStream_t s)
 {
-    // the miss count is only known on the device: a fixed grid of two
-    // work-groups per compute unit strides over whatever the list holds
-    const int grid = 2 * cu_count();
+    // the miss count is only known on the device: a fixed grid strides over
+    // whatever the list holds.  The host link, not the CUs, bounds the copy:
+    // 64 work-groups keep 256 KB of reads in flight (enough for the link's
+    // latency) and leave the other compute units to a layer running beside it
+    const int grid = std::max(16, cu_count() / 4);
     cache_fetch_kernel<<<grid, FETCH_THREADS, 0, s>>>(ctl, hg, hu, hd, sg, su, sd, gate_bytes, down_bytes);
     return hipGetLastError();
 }
