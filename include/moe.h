@@ -213,12 +213,14 @@ int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bi
  *   struct allows; anything but CB2 gate/up with Q2K down needs hidden, inter
  *   and sh_inter multiples of 512 (MOE_ERR_UNSUPPORTED otherwise; Q4K/Q5K/Q6K
  *   codes enter as sc*q split exactly into two bf16 terms).  Launches: for
- *   T <= 4 with CB2 gate/up and Q2K down (and H % 512 == 0,
- *   H <= 8192, I % 256 == 0, I <= 2048, sh_inter % 512 == 0, k <= 64) per
- *   token, in order: gate/up, then (k <= 8, sh_inter <= 2048) h+SwiGLU and
- *   one down launch that writes y, else down (SwiGLU as it forms h) and
- *   combine -- so such a token's y does not depend on the other tokens of the
- *   call; otherwise schedule, gate/up+SwiGLU, down, combine.
+ *   T <= 4 (any T with MOE_LAYER_TOKENWISE_DECODE) with CB2 gate/up and Q2K
+ *   down (and H % 512 == 0, H <= 8192, I % 256 == 0, I <= 2048,
+ *   sh_inter % 512 == 0, k <= 64) per token, in order: for k <= 8 and
+ *   sh_inter <= 2048 four launches -- the shared gate/up; the routed gate/up
+ *   beside the shared down; routed h; the routed down, which adds the shared
+ *   output and writes y -- else gate/up, down (SwiGLU as it forms h) and
+ *   combine; so such a token's y does not depend on the other tokens of the
+ *   call.  Otherwise schedule, gate/up+SwiGLU, down, combine.
  * moe_expert_ffn_prefill -- bf16 MFMA path for any T: x must be bf16;
  *   dequantized weights rounded to bf16 (RNE) in LDS; fp32 accumulation;
  *   h rounded to bf16; down output and combine in fp32.  Relative L2 error
