@@ -42,6 +42,7 @@ def log(msg):
 # sources that define each timed kernel (plus the shared headers)
 _KERNEL_SOURCES = {"dec_": ["decode.hip", "decode.h", "route_dev.h"], "route_": ["route.hip", "route_dev.h"],
                    "ffn_prefill_": ["prefill.hip", "ffn.hip"], "ffn_decode_": ["prefill.hip", "ffn.hip"],
+                   "bd_": ["prefill.hip", "ffn.hip"],
                    "ffn_schedule": ["ffn.hip"], "sh_finalize": ["ffn.hip"], "combine": ["ffn.hip"]}
 
 # the library's launch names (moe_profile.name) and the GPU kernel symbols each one runs
@@ -50,6 +51,8 @@ LAUNCH_SYMBOLS = [
     ("dec_stage2", r"dec1_gateup_kernel<(?:true|false), 2,"),
     ("dec_hform", r"dec1_hform_kernel"),
     ("dec_down_fused", r"dec1_down_fused_kernel"),
+    ("bd_gateup", r"bd_kernel<true,"),
+    ("bd_down", r"bd_kernel<false,"),
     ("ffn_decode_gateup", r"np_kernel<\d+, true, true,"),
     ("ffn_decode_down", r"np_kernel<\d+, false, true,"),
     ("ffn_prefill_gateup", r"np_kernel<\d+, true, false,"),
@@ -164,6 +167,11 @@ def kernel_bytes(cfg, n_active, T, name):
         # every selected expert's gate/up and the shared down, the per-chunk sums out
         return (n_active * 2 * M.q2_packed_bytes(cfg["fmt_gate_up"], I, H) + sh * H * 2 + T * H * xb
                 + (H // 1024) * k * 2 * I * 4 + (sh // 512) * H * 4)
+    if name == "bd_gateup":
+        # the routed experts' gate/up (the shared expert runs in the grouped GEMM beside it), x in, h out
+        return n_active * 2 * M.q2_packed_bytes(cfg["fmt_gate_up"], I, H) + T * H * xb + T * k * I * 4
+    if name == "bd_down":
+        return n_active * M.q2_packed_bytes(cfg["fmt_down"], H, I) + T * k * I * 4 + T * k * H * 4
     if name.endswith("gateup"):
         hb = 4 if "decode" in name else 2
         return n_active * 2 * M.q2_packed_bytes(cfg["fmt_gate_up"], I, H) + 2 * sh * H * 2 + T * H * xb + rows * I * hb

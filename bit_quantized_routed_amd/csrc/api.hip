@@ -222,9 +222,12 @@ FfnWs ffn_ws(const moe_layer *L, int T, bool prefill, bool single, char *base)
         w.ks_dn = std::max(1, L->sh_inter / 512);
     }
     int tiles = ffn_max_tiles(T, L->top_k, L->n_experts, has_sh, BM);
-    if (!prefill)
+    if (!prefill) {
         tiles = std::max(tiles, ffn_max_tiles(T, L->top_k, L->n_experts, has_sh, NP_BM_DEC, NP_BM_DEC,
                                               std::max(w.ks_gu, w.ks_dn)));
+        tiles = std::max(tiles, ffn_max_tiles(T, L->top_k, L->n_experts, has_sh, BD_BM, NP_BM_DEC,
+                                              std::max(w.ks_gu, w.ks_dn)));
+    }
     w.sched = (int32_t *)(base + off);
     off = align_up(off + (1 + 2 * (size_t)tiles) * sizeof(int32_t));
     w.sh_part = (float *)(base + off);
@@ -402,7 +405,10 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
     // prefill: in-register dequantization kernels when every K is a multiple of 256
     const bool np = prefill && np_prefill_ok(up) && np_prefill_ok(dn);
     const bool npd = !prefill && np_decode_ok(up) && np_decode_ok(dn);
-    const int sched_bm = np ? NP_BM : npd ? NP_BM_DEC : BM;
+    // batched decode of CB2/Q2_K layers: routed tiles on the LDS-staged
+    // kernels, the shared expert's tiles on the grouped GEMM
+    const bool bd = npd && bd_ok(up, dn, T);
+    const int sched_bm = np ? NP_BM : bd ? BD_BM : npd ? NP_BM_DEC : BM;
     // batched decode: the shared expert's few rows are spread over K parts so
     // that its work-groups stream no more than a routed tile's
     const bool split = npd && has_sh && H % 512 == 0 && Ish % 512 == 0;
@@ -412,7 +418,7 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
         up.sched_parts = dn.sched_parts = std::max(w.ks_gu, w.ks_dn);
     }
     if (!pr.before("ffn_schedule")) return hip_fail(hipGetLastError(), "event record");
-    launch_ffn_schedule(offsets, T, k, E, has_sh, sched_bm, w.sched, s, np ? NP_BM_SH : sched_bm,
+    launch_ffn_schedule(offsets, T, k, E, has_sh, sched_bm, w.sched, s, np ? NP_BM_SH : bd ? NP_BM_DEC : sched_bm,
                         split ? std::max(w.ks_gu, w.ks_dn) : 1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "ffn_schedule launch");
@@ -420,11 +426,20 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
 
     const char *nm_up = prefill ? "ffn_prefill_gateup" : "ffn_decode_gateup";
     const char *nm_dn = prefill ? "ffn_prefill_down" : "ffn_decode_down";
-    if (!pr.before(nm_up)) return hip_fail(hipGetLastError(), "event record");
-    e = np ? launch_np_prefill(up, true, s) : npd ? launch_np_decode(up, true, s)
-           : prefill ? launch_ffn_prefill(up, true, s) : launch_ffn_decode(up, true, s);
-    if (e != hipSuccess) return hip_fail(e, nm_up);
-    if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+    if (bd) {
+        if (!pr.before("bd_gateup")) return hip_fail(hipGetLastError(), "event record");
+        e = launch_bd(up, true, s);
+        if (e != hipSuccess) return hip_fail(e, "bd_gateup");
+        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+        up.skip_routed = dn.skip_routed = 1;
+    }
+    if (!bd || has_sh) {
+        if (!pr.before(nm_up)) return hip_fail(hipGetLastError(), "event record");
+        e = np ? launch_np_prefill(up, true, s) : npd ? launch_np_decode(up, true, s)
+               : prefill ? launch_ffn_prefill(up, true, s) : launch_ffn_decode(up, true, s);
+        if (e != hipSuccess) return hip_fail(e, nm_up);
+        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+    }
     if (split) {
         if (!pr.before("sh_finalize")) return hip_fail(hipGetLastError(), "event record");
         launch_sh_finalize(w.sh_part, w.ks_gu, T, Ish, T * k, nullptr, (float *)w.h, w.hstride, s);
@@ -433,11 +448,21 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
         if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
     }
 
-    if (!pr.before(nm_dn)) return hip_fail(hipGetLastError(), "event record");
-    e = np ? launch_np_prefill(dn, false, s) : npd ? launch_np_decode(dn, false, s)
-           : prefill ? launch_ffn_prefill(dn, false, s) : launch_ffn_decode(dn, false, s);
-    if (e != hipSuccess) return hip_fail(e, nm_dn);
-    if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+    if (bd) {
+        if (!pr.before("bd_down")) return hip_fail(hipGetLastError(), "event record");
+        FfnPass dr = dn;
+        dr.skip_routed = 0;
+        e = launch_bd(dr, false, s);
+        if (e != hipSuccess) return hip_fail(e, "bd_down");
+        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+    }
+    if (!bd || has_sh) {
+        if (!pr.before(nm_dn)) return hip_fail(hipGetLastError(), "event record");
+        e = np ? launch_np_prefill(dn, false, s) : npd ? launch_np_decode(dn, false, s)
+               : prefill ? launch_ffn_prefill(dn, false, s) : launch_ffn_decode(dn, false, s);
+        if (e != hipSuccess) return hip_fail(e, nm_dn);
+        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+    }
 
     if (!pr.before("combine")) return hip_fail(hipGetLastError(), "event record");
     launch_combine(w.O, inv, topk_w, T, k, H, has_sh ? (split ? w.ks_dn : 1) : 0,

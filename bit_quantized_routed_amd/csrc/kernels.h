@@ -37,6 +37,8 @@ struct FfnPass {
     int sched_parts;                  // shared K parts the schedule was built with (>= sh_parts; 0 or 1: one);
                                       // the launch grid covers every tile of that schedule
     const int32_t *slot;              // null, or expert -> index of its matrices in w0/w1 (expert cache view)
+    int skip_routed;                  // 1: the grouped GEMM runs the shared expert's tiles only (the
+                                      // routed tiles go to the batched-decode kernels)
 };
 
 // tiles of BM rows per routed group and BMsh (<= 0: BM) for the shared group,
@@ -71,5 +73,14 @@ hipError_t launch_np_prefill(const FfnPass &p, bool gateup, hipStream_t s);
 constexpr int NP_BM_DEC = 32;
 bool np_decode_ok(const FfnPass &p);
 hipError_t launch_np_decode(const FfnPass &p, bool gateup, hipStream_t s);
+
+// Batched decode of the routed tiles (CB2 gate/up, Q2_K down; every K a
+// multiple of 512): weights staged through LDS in block pairs with coalesced
+// loads, BD_BM positions per tile.  The schedule must be built with BD_BM
+// rows per routed tile and NP_BM_DEC per shared tile; the shared tiles are
+// left to launch_np_decode with skip_routed set.
+constexpr int BD_BM = 16;
+bool bd_ok(const FfnPass &up, const FfnPass &dn, int T);
+hipError_t launch_bd(const FfnPass &p, bool gateup, hipStream_t s);
 
 }  // namespace moe

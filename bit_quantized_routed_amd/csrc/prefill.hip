@@ -35,6 +35,7 @@
 // Work-groups are mapped to tiles XCD by XCD, so all column slices of a tile
 // (which share its activations) run on the same XCD and its L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "devcache.h"
@@ -1085,6 +1086,8 @@ __global__ __launch_bounds__(NP_THREADS) void np_kernel(FfnPass p, int S)
         // shared-expert tiles are at most 80 rows: the bf16 weight ring and
         // six row fragments would not fit the register budget together
         np_dispatch<FMT_BF16, GATEUP, DEC, TWO, DEC ? 2 : 5>(p, t, As, tab);
+    } else if (p.skip_routed) {
+        return;
     } else {
         np_build_table<FMT>(p, tab);
         __syncthreads();
@@ -1111,6 +1114,369 @@ hipError_t np_launch(const FfnPass &p, hipStream_t s)
                           : ffn_max_tiles(p.T, p.k, p.E, p.Nsh > 0, NP_BM, NP_BM_SH, ks);
     const int64_t grid = (int64_t)((tiles + 7) / 8) * 8 * S;
     np_kernel<FMT, GATEUP, DEC, TWO><<<dim3((unsigned)grid), NP_THREADS, lds, s>>>(p, S);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Batched decode of the routed tiles.  At decode sizes (a few tokens per
+// expert) the grouped GEMM above is bound by how it reads weights: every lane
+// owns one weight row and reads a few bytes of it per step, so each load
+// instruction touches as many cache lines as rows.  Here a work-group stages
+// its weight rows through LDS one block pair (512 K) at a time with
+// lane-consecutive dword loads (a wave's load covers a few rows' contiguous
+// bytes), two pairs in flight in registers while the pair before them is
+// computed from LDS.  The arithmetic is the decode precision of the grouped
+// GEMM: exact integer codes as bf16 MFMA operands, the fp32 sums of each
+// block scaled by its d (and the Q2_K min term by dmin), fp32 activations as
+// hi + lo bf16 terms.  The K order is the natural one (step s of a block
+// covers K 32s..32s+31, lane group fc its 8-wide slice), so the activations
+// are staged in plain row order, 16-byte pieces XOR-swizzled by the row.
+//
+// Tiles are BD_BM = 16 positions of one expert (one MFMA row fragment).
+// gate/up (CB2): 4 waves, each 16 h-features x {gate, up}: 128 weight rows;
+// a block's bytes start 2 bytes past a dword in odd blocks, so each block is
+// staged as the 10-dword window from the dword at or below it.
+// down (Q2_K): 8 waves, each 32 output features: 256 weight rows, 42 dwords
+// per row and pair (84-byte blocks are dword aligned).
+constexpr int BD_COPIES = 4;                       // selector-table copies
+
+template <bool GATEUP> struct Bd {
+    static constexpr int FMT = GATEUP ? FMT_CB2 : FMT_Q2K;
+    static constexpr int WAVES = GATEUP ? 4 : 8;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int ROWS = 32 * WAVES;                       // weight rows per work-group
+    static constexpr int COLS = GATEUP ? 16 * WAVES : 32 * WAVES; // GEMM output columns per work-group
+    static constexpr int WDW = GATEUP ? 20 : 42;                  // dwords per row and block pair
+    static constexpr int WLD = ROWS * WDW / THREADS;              // weight dwords one thread loads per pair
+    static constexpr int WSLOT = ROWS * WDW * 4;                  // bytes of one weight stage
+    static constexpr int APLANE = BD_BM * 1024;                   // 16 rows x 512 K bf16
+    static constexpr int APT = BD_BM * 64 / THREADS;              // 8-K pieces one thread loads per pair
+    static constexpr int TAB = 256 * BD_COPIES * (GATEUP ? 16 : 8);
+    // Q2_K min term: per slot, the 16-K sub-block sums of the staged rows as
+    // MFMA A operands, [block][hi, lo][16 rows][16 bf16]
+    static constexpr int XSLOT = GATEUP ? 0 : 2 * 2 * BD_BM * 32;
+    static_assert(ROWS * WDW % THREADS == 0 && BD_BM * 64 % THREADS == 0, "whole loads per thread");
+};
+
+template <bool GATEUP, bool TWO> constexpr int bd_lds_bytes()
+{
+    return 2 * Bd<GATEUP>::WSLOT + 2 * (TWO ? 2 : 1) * Bd<GATEUP>::APLANE + Bd<GATEUP>::TAB + 2 * Bd<GATEUP>::XSLOT;
+}
+
+// the selector tables of np_build_table, BD_COPIES copies, built by THREADS threads
+template <int FMT, int THREADS>
+__device__ __forceinline__ void bd_build_table(const FfnPass &p, uint32_t *tab)
+{
+    if constexpr (FMT == FMT_CB2) {
+        for (int e = threadIdx.x; e < 256 * 4; e += THREADS) {
+            const int idx = e >> 2, i = e & 3;
+            const uint32_t b0 = cb2_pos(p.codebook[8 * idx + 2 * i]), b1 = cb2_pos(p.codebook[8 * idx + 2 * i + 1]);
+            const uint32_t sel = b0 | ((b0 + 1) << 8) | (b1 << 16) | ((b1 + 1) << 24);
+#pragma unroll
+            for (int c = 0; c < BD_COPIES; ++c) tab[(idx * BD_COPIES + c) * 4 + i] = sel;
+        }
+    } else {
+        for (int e = threadIdx.x; e < 256 * 2; e += THREADS) {
+            const int byte = e >> 1, i = e & 1;
+            const uint32_t q0 = (byte >> (4 * i)) & 3, q1 = (byte >> (4 * i + 2)) & 3;
+            const uint32_t sel = (2 * q0) | ((2 * q0 + 1) << 8) | ((2 * q1) << 16) | ((2 * q1 + 1) << 24);
+#pragma unroll
+            for (int c = 0; c < BD_COPIES; ++c) tab[(byte * BD_COPIES + c) * 2 + i] = sel;
+        }
+    }
+}
+
+template <bool GATEUP, bool TWO>
+__global__ __launch_bounds__(Bd<GATEUP>::THREADS) void bd_kernel(FfnPass p, int S)
+{
+    using C = Bd<GATEUP>;
+    constexpr int FMT = C::FMT, THREADS = C::THREADS, NF = 2;
+    extern __shared__ __attribute__((aligned(16))) uint8_t bd_smem[];
+    NpTile t;
+    if (!np_tile(p, S, C::COLS, BD_BM, NP_BM_DEC, t)) return;
+    if (t.sh) return;                                        // the grouped GEMM takes the shared tiles
+    uint8_t *Ws = bd_smem;                                   // [2][ROWS][WDW] dwords
+    uint8_t *As = bd_smem + 2 * C::WSLOT;                    // [2][hi, lo][16][1024 B]
+    uint32_t *tab = (uint32_t *)(As + 2 * (TWO ? 2 : 1) * C::APLANE);
+    uint8_t *Xs = (uint8_t *)tab + C::TAB;                   // [2][XSLOT] (Q2_K)
+    bd_build_table<FMT, THREADS>(p, tab);
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int fr = lane & 15, fc = lane >> 4, copy = lane & (BD_COPIES - 1);
+    const int npair = t.Kg >> 9;                             // >= 1 (K % 512 == 0, checked on the host)
+
+    // ---- this thread's load slots: weight dwords (row, dword) and activation pieces (row, 8-K piece)
+    const uint8_t *wb0 = p.w0 + (int64_t)t.w * p.w_expert_bytes;
+    const uint8_t *wb1 = GATEUP ? p.w1 + (int64_t)t.w * p.w_expert_bytes : wb0;
+    uint32_t woff[C::WLD];                                   // byte offset inside the expert's matrix
+    const uint8_t *wsrc[C::WLD];
+#pragma unroll
+    for (int j = 0; j < C::WLD; ++j) {
+        const int q = tid + THREADS * j, r = q / C::WDW, i = q - r * C::WDW;
+        int col, off;
+        const uint8_t *base;
+        if (GATEUP) {
+            col = t.n0 + (r & 63);
+            base = r < 64 ? wb0 : wb1;
+            off = i < 10 ? 4 * i : 36 + 4 * (i - 10);        // the two 40-byte block windows of the pair
+        } else {
+            col = t.n0 + r;
+            base = wb0;
+            off = 4 * i;
+        }
+        col = min(col, t.Ng - 1);
+        wsrc[j] = base;
+        woff[j] = (uint32_t)col * (uint32_t)p.w_row_bytes + (uint32_t)off;
+    }
+    constexpr int PB = GATEUP ? 76 : 168;                    // bytes of a block pair in a row
+    int64_t arow[C::APT];
+    int akp[C::APT], ar[C::APT];
+#pragma unroll
+    for (int j = 0; j < C::APT; ++j) {
+        const int q = tid + THREADS * j;
+        ar[j] = q >> 6;
+        akp[j] = q & 63;
+        arow[j] = np_act_row(p, t, min(ar[j], t.nvalid - 1)) * p.act_stride + t.k0;
+    }
+    // ---- prefetch registers: two sets (two objects, never indexed at run time)
+    struct Regs {
+        uint32_t w[C::WLD];
+        u32x4 a0[C::APT], a1[TWO ? C::APT : 1];
+    };
+    Regs R0, R1;
+    auto load_pair = [&](int pr, Regs &R) {
+#pragma unroll
+        for (int j = 0; j < C::WLD; ++j) R.w[j] = *(const uint32_t *)(wsrc[j] + woff[j] + (uint32_t)(PB * pr));
+#pragma unroll
+        for (int j = 0; j < C::APT; ++j) {
+            const int64_t e = arow[j] + 512 * pr + 8 * akp[j];
+            if constexpr (TWO) {
+                const u32x4 *src = (const u32x4 *)((const float *)p.act + e);
+                R.a0[j] = src[0];
+                R.a1[j] = src[1];
+            } else {
+                R.a0[j] = *(const u32x4 *)((const uint16_t *)p.act + e);
+            }
+        }
+    };
+    auto store_pair = [&](const Regs &R, int slot) {
+        uint32_t *w = (uint32_t *)(Ws + slot * C::WSLOT);
+#pragma unroll
+        for (int j = 0; j < C::WLD; ++j) w[tid + THREADS * j] = R.w[j];
+        uint8_t *a = As + slot * (TWO ? 2 : 1) * C::APLANE;
+#pragma unroll
+        for (int j = 0; j < C::APT; ++j) {
+            const int o = ar[j] * 1024 + ((akp[j] ^ (ar[j] & 15)) << 4);
+            if constexpr (TWO) {
+                const u32x4 v0 = R.a0[j], v1 = R.a1[j];
+                const float v[8] = {__uint_as_float(v0.x), __uint_as_float(v0.y), __uint_as_float(v0.z),
+                                    __uint_as_float(v0.w), __uint_as_float(v1.x), __uint_as_float(v1.y),
+                                    __uint_as_float(v1.z), __uint_as_float(v1.w)};
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hi[e] = pk_bf16(v[2 * e], v[2 * e + 1]);
+                    lo[e] = pk_bf16(v[2 * e] - __uint_as_float(hi[e] << 16),
+                                    v[2 * e + 1] - __uint_as_float(hi[e] & 0xffff0000u));
+                }
+                *(u32x4 *)(a + o) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+                *(u32x4 *)(a + C::APLANE + o) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+                if constexpr (FMT == FMT_Q2K) {
+                    // sub-block sum over K 16 u .. 16 u + 15 of the pair (u = akp / 2):
+                    // this piece's 8 values, then the neighbouring lane's (akp ^ 1)
+                    float s8 = v[0];
+#pragma unroll
+                    for (int e = 1; e < 8; ++e) s8 += v[e];
+                    const float other = __shfl_xor(s8, 1);
+                    if ((akp[j] & 1) == 0) {
+                        const float xs = s8 + other;
+                        const uint32_t xh = pk_bf16(xs, 0.f) & 0xffffu;
+                        const uint32_t xl = pk_bf16(xs - __uint_as_float(xh << 16), 0.f) & 0xffffu;
+                        const int u = akp[j] >> 1, blkx = u >> 4, jj = u & 15;
+                        uint16_t *xp = (uint16_t *)(Xs + slot * C::XSLOT + blkx * 2 * BD_BM * 32);
+                        xp[ar[j] * 16 + jj] = (uint16_t)xh;
+                        xp[BD_BM * 16 + ar[j] * 16 + jj] = (uint16_t)xl;
+                    }
+                }
+            } else {
+                *(u32x4 *)(a + o) = R.a0[j];
+            }
+        }
+    };
+
+    f32x4 acc[NF], P1[NF];
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf) acc[nf] = P1[nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // LDS row of fragment nf of this lane: gate/up nf 0 = gate, 1 = up of feature
+    // n0 + 16 wave + fr; down: feature n0 + 32 wave + 16 nf + fr
+    int wrow[NF];
+#pragma unroll
+    for (int nf = 0; nf < NF; ++nf) wrow[nf] = GATEUP ? nf * 64 + 16 * wave + fr : 32 * wave + 16 * nf + fr;
+    // byte of this lane's codebook index inside its CB2 window dwords: group
+    // 4 s + fc is byte 6 + 4 s + fc of the block, dword 1 + s + hsel
+    const int hsel = (2 + fc) >> 2, bsh = 8 * ((2 + fc) & 3);
+
+    auto compute_pair = [&](int slot) {
+        const uint32_t *w = (const uint32_t *)(Ws + slot * C::WSLOT);
+        const uint8_t *a = As + slot * (TWO ? 2 : 1) * C::APLANE;
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+            uint32_t blk[NF][FMT == FMT_CB2 ? 10 : 21];
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf) {
+                if constexpr (FMT == FMT_CB2) {
+                    uint32_t v[10];
+                    const uint2 *src = (const uint2 *)(w + wrow[nf] * C::WDW + 10 * b2);
+#pragma unroll
+                    for (int i = 0; i < 5; ++i) {
+                        const uint2 x = src[i];
+                        v[2 * i] = x.x;
+                        v[2 * i + 1] = x.y;
+                    }
+                    // odd blocks start 2 bytes into their window
+#pragma unroll
+                    for (int i = 0; i < 10; ++i)
+                        blk[nf][i] = b2 ? (i < 9 ? __builtin_amdgcn_alignbit(v[i + 1], v[i], 16) : v[9] >> 16) : v[i];
+                } else {
+                    const uint32_t *src = w + wrow[nf] * C::WDW + 21 * b2;
+#pragma unroll
+                    for (int i = 0; i < 21; ++i) blk[nf][i] = src[i];
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int o = (32 * b2 + 4 * s + fc) ^ fr;
+                const bf16x8 ah = *(const bf16x8 *)(a + fr * 1024 + (o << 4));
+                bf16x8 al;
+                if constexpr (TWO) al = *(const bf16x8 *)(a + C::APLANE + fr * 1024 + (o << 4));
+#pragma unroll
+                for (int nf = 0; nf < NF; ++nf) {
+                    uint32_t ob[4];
+                    if constexpr (FMT == FMT_CB2) {
+                        // step s covers sub-block s in every lane: pool {s, 3s} and its
+                        // negation (exact integers); d scales the block's sums
+                        const uint32_t sc32 = (blk[nf][0] >> 16) | (blk[nf][1] << 16);
+                        const float sj = (float)((sc32 >> (4 * s)) & 15u);
+                        const uint32_t lo = pk_bf16(sj, 3.0f * sj), hi = lo ^ 0x80008000u;
+                        const uint32_t dw = hsel ? blk[nf][2 + s] : blk[nf][1 + s];
+                        const uint32_t idx = (dw >> bsh) & 0xffu;
+                        const u32x4 sel = *(const u32x4 *)&tab[(idx * BD_COPIES + copy) * 4];
+                        ob[0] = vperm(hi, lo, sel.x);
+                        ob[1] = vperm(hi, lo, sel.y);
+                        ob[2] = vperm(hi, lo, sel.z);
+                        ob[3] = vperm(hi, lo, sel.w);
+                    } else {
+                        // weights 32 s + 8 fc .. + 7: sub-block 2 s + fc / 2, code bytes
+                        // 20 + 8 s + 2 fc and the next one
+                        // (sub-block byte 4 + j, j = 2 s + f: dword 1 + s / 2, byte 2 (s & 1) + f;
+                        // code dword 5 + 2 s + f; f = fc / 2 picks between static indices)
+                        const int f = fc >> 1;
+                        const uint32_t sm = (blk[nf][1 + (s >> 1)] >> (16 * (s & 1) + 8 * f)) & 0xffu;
+                        const float sc = (float)(sm & 15u), m = (float)(sm >> 4);
+                        const uint32_t lo = pk_bf16(0.0f, sc), hi = pk_bf16(2.0f * sc, 3.0f * sc);
+                        const uint32_t cw = (f ? blk[nf][6 + 2 * s] : blk[nf][5 + 2 * s]) >> (16 * (fc & 1));
+                        const uint2 s0 = *(const uint2 *)&tab[((cw & 0xffu) * BD_COPIES + copy) * 2];
+                        const uint2 s1 = *(const uint2 *)&tab[(((cw >> 8) & 0xffu) * BD_COPIES + copy) * 2];
+                        ob[0] = vperm(hi, lo, s0.x);
+                        ob[1] = vperm(hi, lo, s0.y);
+                        ob[2] = vperm(hi, lo, s1.x);
+                        ob[3] = vperm(hi, lo, s1.y);
+                        (void)m;
+                    }
+                    const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{ob[0], ob[1], ob[2], ob[3]});
+                    P1[nf] = mfma16x16x32(ah, bq, P1[nf]);
+                    if constexpr (TWO) P1[nf] = mfma16x16x32(al, bq, P1[nf]);
+                }
+            }
+            if constexpr (FMT == FMT_CB2) {
+#pragma unroll
+                for (int nf = 0; nf < NF; ++nf) {
+                    acc[nf] += f16_bits_to_f32(blk[nf][0] & 0xffffu) * P1[nf];
+                    P1[nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            } else {
+                // the block's code sums times d; the min term: the 16 sub-block
+                // sums of the activation rows (K 0..15; lanes fc >= 2 supply the
+                // zero K 16..31) against the sub-blocks' m (exact integers),
+                // times dmin
+                const uint16_t *xp = (const uint16_t *)(Xs + slot * C::XSLOT + b2 * 2 * BD_BM * 32);
+                u32x4 xh{0u, 0u, 0u, 0u}, xl{0u, 0u, 0u, 0u};
+                if (fc < 2) {
+                    xh = *(const u32x4 *)(xp + fr * 16 + 8 * fc);
+                    xl = *(const u32x4 *)(xp + BD_BM * 16 + fr * 16 + 8 * fc);
+                }
+#pragma unroll
+                for (int nf = 0; nf < NF; ++nf) {
+                    acc[nf] += f16_bits_to_f32(blk[nf][0] & 0xffffu) * P1[nf];
+                    P1[nf] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    // m of sub-blocks 8 fc .. 8 fc + 7: high nibbles of bytes 4 + 8 fc ..
+                    const uint32_t m0 = (fc & 1) ? blk[nf][3] : blk[nf][1];
+                    const uint32_t m1 = (fc & 1) ? blk[nf][4] : blk[nf][2];
+                    uint32_t mb[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t wv = e < 2 ? m0 : m1;
+                        const int sh = 16 * (e & 1);
+                        mb[e] = fc < 2 ? pk_bf16((float)((wv >> (sh + 4)) & 15u), (float)((wv >> (sh + 12)) & 15u)) : 0u;
+                    }
+                    const bf16x8 bm = __builtin_bit_cast(bf16x8, u32x4{mb[0], mb[1], mb[2], mb[3]});
+                    f32x4 Pm = mfma16x16x32(__builtin_bit_cast(bf16x8, xh), bm, f32x4{0.f, 0.f, 0.f, 0.f});
+                    Pm = mfma16x16x32(__builtin_bit_cast(bf16x8, xl), bm, Pm);
+                    acc[nf] -= f16_bits_to_f32(blk[nf][0] >> 16) * Pm;
+                }
+            }
+        }
+    };
+
+    // ---- pipeline: pairs p + 1 and p + 2 in flight while pair p is computed
+    load_pair(0, R0);
+    if (npair > 1) load_pair(1, R1);
+    store_pair(R0, 0);
+    if (npair > 2) load_pair(2, R0);
+    __syncthreads();
+    // pair pr sits in LDS slot pr % 2; `nx` holds pair pr + 1 (requested two
+    // steps back) and takes pair pr + 3
+    auto iter = [&](int pr, Regs &nx) {
+        compute_pair(pr & 1);
+        if (pr + 1 < npair) store_pair(nx, (pr + 1) & 1);
+        if (pr + 3 < npair) load_pair(pr + 3, nx);
+        __syncthreads();
+    };
+    for (int pr = 0; pr < npair; pr += 2) {
+        iter(pr, R1);
+        if (pr + 1 < npair) iter(pr + 1, R0);
+    }
+
+    // ---- epilogue: D lane (fr, fc) holds rows 4 fc + v of column fr
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int i = 4 * fc + v;
+        if (i >= t.nvalid) continue;
+        const int64_t pos = t.row0 + i;
+        if (GATEUP) {
+            const int n = t.n0 + 16 * wave + fr;
+            if (n < t.Ng) ((float *)p.out)[pos * p.out_stride + n] = np_silu_mul(acc[0][v], acc[1][v]);
+        } else {
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf) {
+                const int n = t.n0 + 32 * wave + 16 * nf + fr;
+                if (n < t.Ng) ((float *)p.out)[pos * p.out_stride + n] = acc[nf][v];
+            }
+        }
+    }
+}
+
+template <bool GATEUP, bool TWO>
+hipError_t bd_launch(const FfnPass &p, hipStream_t s)
+{
+    constexpr int lds = bd_lds_bytes<GATEUP, TWO>();
+    static DevSlots attr{};
+    const hipError_t e = lds_limit((const void *)bd_kernel<GATEUP, TWO>, attr, lds);
+    if (e != hipSuccess) return e;
+    const int S = (p.N + Bd<GATEUP>::COLS - 1) / Bd<GATEUP>::COLS;
+    const int tiles = ffn_max_tiles(p.T, p.k, p.E, p.Nsh > 0, BD_BM, NP_BM_DEC, std::max(p.sched_parts, 1));
+    const int64_t grid = (int64_t)((tiles + 7) / 8) * 8 * S;
+    bd_kernel<GATEUP, TWO><<<dim3((unsigned)grid), Bd<GATEUP>::THREADS, lds, s>>>(p, S);
     return hipGetLastError();
 }
 
@@ -1170,6 +1536,20 @@ hipError_t np_decode_fmt(const FfnPass &p, bool gateup, hipStream_t s)
         if (!p.act_f32) return hipErrorInvalidValue;
         return np_launch<FMT, false, true, true>(p, s);
     }
+}
+
+bool bd_ok(const FfnPass &up, const FfnPass &dn, int T)
+{
+    // CB2 gate/up, Q2_K down, every K a multiple of 512, at most 64 tokens
+    return up.fmt == FMT_CB2 && dn.fmt == FMT_Q2K && up.K % 512 == 0 && dn.K % 512 == 0 && T <= 64 &&
+           up.out_f32 && dn.act_f32 && !up.slot == !dn.slot;
+}
+
+hipError_t launch_bd(const FfnPass &p, bool gateup, hipStream_t s)
+{
+    if (gateup) return p.act_f32 ? bd_launch<true, true>(p, s) : bd_launch<true, false>(p, s);
+    if (!p.act_f32) return hipErrorInvalidValue;
+    return bd_launch<false, true>(p, s);
 }
 
 hipError_t launch_np_decode(const FfnPass &p, bool gateup, hipStream_t s)
