@@ -527,7 +527,9 @@ def sweep(args):
     T = SWEEP_T tokens, Zipf-skewed routing as in decode32: time per step of each,
     the decode path's algorithmic GB/s, the first T at which prefill is faster,
     and how far each token's decode output in the batch is from the same token
-    decoded alone (max |difference| relative to max |y|; 0 means bit-identical)."""
+    decoded alone (max |difference| relative to max |y|; 0 means bit-identical);
+    the same for decode with the layer's token-by-token flag, whose outputs must
+    be bit-identical to decoding each token alone."""
     import torch
     import synthetic as S
     import workload as W
@@ -556,11 +558,35 @@ def sweep(args):
         torch.cuda.synchronize()
         d = (one.y[0] - ys["batch"][0]).abs().max().item()
         row["token0_alone_vs_batch"] = d / max(ys["batch"][0].abs().max().item(), 1e-30)
+        # token by token (the layer flag), on every replica
+        for lay in wl.layers:
+            lay.c.flags = M.LAYER_TOKENWISE_DECODE
+        try:
+            st = Stepper(wl, c, True)
+            st.step()
+            torch.cuda.synchronize()
+            dt = (one.y[0] - st.y[0]).abs().max().item()
+            row["tokenwise_token0_vs_alone"] = dt / max(one.y[0].abs().max().item(), 1e-30)
+            ms, _, _ = st.timed(args.steps, args.warmup)
+            row["tokenwise_ms"] = round(ms, 5)
+        finally:
+            for lay in wl.layers:
+                lay.c.flags = 0
         row["decode_GBps"] = round(layer_bytes(c, row["active_experts"], T) / (row["decode_ms"] * 1e-3) / 1e9, 1)
         row["faster"] = "prefill" if row["prefill_ms"] < row["decode_ms"] else "decode"
         log("sweep T=%d: %s" % (T, row))
         rows.append(row)
     cross = next((r["T"] for r in rows if r["faster"] == "prefill"), None)
+    if args.sweep_md:
+        print("| T | active experts | decode path (ms) | decode GB/s | token-by-token (ms) | prefill path (ms) | "
+              "faster | token0 alone vs batch | token-by-token vs alone |")
+        print("|---:|---:|---:|---:|---:|---:|---|---:|---:|")
+        for r in rows:
+            print("| %d | %d | %.4f | %.1f | %.4f | %.4f | %s | %.2e | %.2e |" % (
+                r["T"], r["active_experts"], r["decode_ms"], r["decode_GBps"], r["tokenwise_ms"], r["prefill_ms"],
+                r["faster"], r["token0_alone_vs_batch"], r["tokenwise_token0_vs_alone"]))
+        print("\ncrossover_T (first T where the prefill path is faster): %s" % cross)
+        return
     print(json.dumps({"sweep": "decode vs prefill path, full layer (H=7168, I=2048, E=256, k=8, bf16 shared), "
                                "Zipf-skewed routing", "steps": args.steps, "warmup": args.warmup,
                       "rows": rows, "crossover_T": cross}), flush=True)
@@ -793,6 +819,7 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="only the micro-batch sweep: decode and prefill paths at T = 1..64 on the full layer "
                          "(Zipf-skewed routing), with the crossover T; one JSON line")
+    ap.add_argument("--sweep-md", action="store_true", help="with --sweep: print the table as markdown")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy 5 times (counter calibration under rocprofv3)")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("WORKLOAD", "DIR", "COMMAND"),
