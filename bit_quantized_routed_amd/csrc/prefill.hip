@@ -1312,86 +1312,93 @@ __global__ __launch_bounds__(Bd<GATEUP>::THREADS) void bd_kernel(FfnPass p, int 
     int wrow[NF];
 #pragma unroll
     for (int nf = 0; nf < NF; ++nf) wrow[nf] = GATEUP ? nf * 64 + 16 * wave + fr : 32 * wave + 16 * nf + fr;
-    // byte of this lane's codebook index inside its CB2 window dwords: group
-    // 4 s + fc is byte 6 + 4 s + fc of the block, dword 1 + s + hsel
-    const int hsel = (2 + fc) >> 2, bsh = 8 * ((2 + fc) & 3);
-
+    // K order inside a block, as in the grouped GEMM: MFMA step s4 of half h
+    // gives lane group fc the 8 weights 64 fc + 32 h + 8 s4 .. + 7, so a lane's
+    // half-block is one sub-block (CB2) or two (Q2_K) and its pool is built once
+    // per half; the activation pieces are read in the same order.
     auto compute_pair = [&](int slot) {
         const uint32_t *w = (const uint32_t *)(Ws + slot * C::WSLOT);
         const uint8_t *a = As + slot * (TWO ? 2 : 1) * C::APLANE;
 #pragma unroll
         for (int b2 = 0; b2 < 2; ++b2) {
-            uint32_t blk[NF][FMT == FMT_CB2 ? 10 : 21];
+            // this lane's fields of block b2 for each fragment
+            uint32_t d16[NF], f0[NF], f1[NF], f2[NF], f3[NF] = {}, f4[NF] = {}, f5[NF] = {};
 #pragma unroll
             for (int nf = 0; nf < NF; ++nf) {
                 if constexpr (FMT == FMT_CB2) {
-                    uint32_t v[10];
-                    const uint2 *src = (const uint2 *)(w + wrow[nf] * C::WDW + 10 * b2);
-#pragma unroll
-                    for (int i = 0; i < 5; ++i) {
-                        const uint2 x = src[i];
-                        v[2 * i] = x.x;
-                        v[2 * i + 1] = x.y;
-                    }
-                    // odd blocks start 2 bytes into their window
-#pragma unroll
-                    for (int i = 0; i < 10; ++i)
-                        blk[nf][i] = b2 ? (i < 9 ? __builtin_amdgcn_alignbit(v[i + 1], v[i], 16) : v[9] >> 16) : v[i];
+                    // odd blocks start 2 bytes into their 10-dword window
+                    const uint16_t *bp = (const uint16_t *)(w + wrow[nf] * C::WDW + 10 * b2) + b2;
+                    d16[nf] = bp[0];
+                    f0[nf] = bp[1 + (fc >> 1)];                              // scale byte pair
+                    f1[nf] = (uint32_t)bp[3 + 4 * fc] | ((uint32_t)bp[4 + 4 * fc] << 16);   // indices, half 0
+                    f2[nf] = (uint32_t)bp[5 + 4 * fc] | ((uint32_t)bp[6 + 4 * fc] << 16);   // indices, half 1
                 } else {
-                    const uint32_t *src = w + wrow[nf] * C::WDW + 21 * b2;
-#pragma unroll
-                    for (int i = 0; i < 21; ++i) blk[nf][i] = src[i];
+                    const uint32_t *bp = w + wrow[nf] * C::WDW + 21 * b2;
+                    d16[nf] = bp[0];                                         // d | dmin << 16
+                    f0[nf] = bp[1 + fc];                                     // sc|m of sub-blocks 4 fc ..
+                    f1[nf] = bp[5 + 4 * fc];                                 // codes, half 0
+                    f2[nf] = bp[6 + 4 * fc];
+                    f3[nf] = bp[7 + 4 * fc];                                 // codes, half 1
+                    f4[nf] = bp[8 + 4 * fc];
+                    // m of sub-blocks 8 fc .. 8 fc + 7 (lanes fc < 2) for the min term
+                    f5[nf] = bp[1 + 2 * (fc & 1)];
                 }
             }
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const int o = (32 * b2 + 4 * s + fc) ^ fr;
-                const bf16x8 ah = *(const bf16x8 *)(a + fr * 1024 + (o << 4));
-                bf16x8 al;
-                if constexpr (TWO) al = *(const bf16x8 *)(a + C::APLANE + fr * 1024 + (o << 4));
+            for (int h = 0; h < 2; ++h) {
+                uint32_t plo[NF][2], phi[NF][2];
 #pragma unroll
                 for (int nf = 0; nf < NF; ++nf) {
-                    uint32_t ob[4];
                     if constexpr (FMT == FMT_CB2) {
-                        // step s covers sub-block s in every lane: pool {s, 3s} and its
-                        // negation (exact integers); d scales the block's sums
-                        const uint32_t sc32 = (blk[nf][0] >> 16) | (blk[nf][1] << 16);
-                        const float sj = (float)((sc32 >> (4 * s)) & 15u);
-                        const uint32_t lo = pk_bf16(sj, 3.0f * sj), hi = lo ^ 0x80008000u;
-                        const uint32_t dw = hsel ? blk[nf][2 + s] : blk[nf][1 + s];
-                        const uint32_t idx = (dw >> bsh) & 0xffu;
-                        const u32x4 sel = *(const u32x4 *)&tab[(idx * BD_COPIES + copy) * 4];
-                        ob[0] = vperm(hi, lo, sel.x);
-                        ob[1] = vperm(hi, lo, sel.y);
-                        ob[2] = vperm(hi, lo, sel.z);
-                        ob[3] = vperm(hi, lo, sel.w);
+                        const float sj = (float)((f0[nf] >> (8 * (fc & 1) + 4 * h)) & 15u);
+                        plo[nf][0] = pk_bf16(sj, 3.0f * sj);
+                        phi[nf][0] = plo[nf][0] ^ 0x80008000u;
                     } else {
-                        // weights 32 s + 8 fc .. + 7: sub-block 2 s + fc / 2, code bytes
-                        // 20 + 8 s + 2 fc and the next one
-                        // (sub-block byte 4 + j, j = 2 s + f: dword 1 + s / 2, byte 2 (s & 1) + f;
-                        // code dword 5 + 2 s + f; f = fc / 2 picks between static indices)
-                        const int f = fc >> 1;
-                        const uint32_t sm = (blk[nf][1 + (s >> 1)] >> (16 * (s & 1) + 8 * f)) & 0xffu;
-                        const float sc = (float)(sm & 15u), m = (float)(sm >> 4);
-                        const uint32_t lo = pk_bf16(0.0f, sc), hi = pk_bf16(2.0f * sc, 3.0f * sc);
-                        const uint32_t cw = (f ? blk[nf][6 + 2 * s] : blk[nf][5 + 2 * s]) >> (16 * (fc & 1));
-                        const uint2 s0 = *(const uint2 *)&tab[((cw & 0xffu) * BD_COPIES + copy) * 2];
-                        const uint2 s1 = *(const uint2 *)&tab[(((cw >> 8) & 0xffu) * BD_COPIES + copy) * 2];
-                        ob[0] = vperm(hi, lo, s0.x);
-                        ob[1] = vperm(hi, lo, s0.y);
-                        ob[2] = vperm(hi, lo, s1.x);
-                        ob[3] = vperm(hi, lo, s1.y);
-                        (void)m;
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const float sc = (float)((f0[nf] >> (8 * (2 * h + u))) & 15u);
+                            plo[nf][u] = pk_bf16(0.0f, sc);
+                            phi[nf][u] = pk_bf16(2.0f * sc, 3.0f * sc);
+                        }
                     }
-                    const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{ob[0], ob[1], ob[2], ob[3]});
-                    P1[nf] = mfma16x16x32(ah, bq, P1[nf]);
-                    if constexpr (TWO) P1[nf] = mfma16x16x32(al, bq, P1[nf]);
+                }
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const int o = (32 * b2 + 8 * fc + 4 * h + s4) ^ fr;
+                    const bf16x8 ah = *(const bf16x8 *)(a + fr * 1024 + (o << 4));
+                    bf16x8 al;
+                    if constexpr (TWO) al = *(const bf16x8 *)(a + C::APLANE + fr * 1024 + (o << 4));
+#pragma unroll
+                    for (int nf = 0; nf < NF; ++nf) {
+                        uint32_t ob[4];
+                        if constexpr (FMT == FMT_CB2) {
+                            const uint32_t idx = ((h ? f2[nf] : f1[nf]) >> (8 * s4)) & 0xffu;
+                            const u32x4 sel = *(const u32x4 *)&tab[(idx * BD_COPIES + copy) * 4];
+                            ob[0] = vperm(phi[nf][0], plo[nf][0], sel.x);
+                            ob[1] = vperm(phi[nf][0], plo[nf][0], sel.y);
+                            ob[2] = vperm(phi[nf][0], plo[nf][0], sel.z);
+                            ob[3] = vperm(phi[nf][0], plo[nf][0], sel.w);
+                        } else {
+                            const uint32_t cw = h ? (s4 < 2 ? f3[nf] : f4[nf]) : (s4 < 2 ? f1[nf] : f2[nf]);
+                            const uint32_t b0 = (cw >> (16 * (s4 & 1))) & 0xffu, b1 = (cw >> (16 * (s4 & 1) + 8)) & 0xffu;
+                            const uint2 s0 = *(const uint2 *)&tab[(b0 * BD_COPIES + copy) * 2];
+                            const uint2 s1 = *(const uint2 *)&tab[(b1 * BD_COPIES + copy) * 2];
+                            const int u = s4 >> 1;
+                            ob[0] = vperm(phi[nf][u], plo[nf][u], s0.x);
+                            ob[1] = vperm(phi[nf][u], plo[nf][u], s0.y);
+                            ob[2] = vperm(phi[nf][u], plo[nf][u], s1.x);
+                            ob[3] = vperm(phi[nf][u], plo[nf][u], s1.y);
+                        }
+                        const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{ob[0], ob[1], ob[2], ob[3]});
+                        P1[nf] = mfma16x16x32(ah, bq, P1[nf]);
+                        if constexpr (TWO) P1[nf] = mfma16x16x32(al, bq, P1[nf]);
+                    }
                 }
             }
             if constexpr (FMT == FMT_CB2) {
 #pragma unroll
                 for (int nf = 0; nf < NF; ++nf) {
-                    acc[nf] += f16_bits_to_f32(blk[nf][0] & 0xffffu) * P1[nf];
+                    acc[nf] += f16_bits_to_f32(d16[nf]) * P1[nf];
                     P1[nf] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
             } else {
@@ -1407,11 +1414,12 @@ __global__ __launch_bounds__(Bd<GATEUP>::THREADS) void bd_kernel(FfnPass p, int 
                 }
 #pragma unroll
                 for (int nf = 0; nf < NF; ++nf) {
-                    acc[nf] += f16_bits_to_f32(blk[nf][0] & 0xffffu) * P1[nf];
+                    acc[nf] += f16_bits_to_f32(d16[nf] & 0xffffu) * P1[nf];
                     P1[nf] = f32x4{0.f, 0.f, 0.f, 0.f};
                     // m of sub-blocks 8 fc .. 8 fc + 7: high nibbles of bytes 4 + 8 fc ..
-                    const uint32_t m0 = (fc & 1) ? blk[nf][3] : blk[nf][1];
-                    const uint32_t m1 = (fc & 1) ? blk[nf][4] : blk[nf][2];
+                    // (dwords 1 + 2 fc and 2 + 2 fc; the second read here)
+                    const uint32_t m0 = f5[nf];
+                    const uint32_t m1 = w[wrow[nf] * C::WDW + 21 * b2 + 2 + 2 * (fc & 1)];
                     uint32_t mb[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -1422,7 +1430,7 @@ __global__ __launch_bounds__(Bd<GATEUP>::THREADS) void bd_kernel(FfnPass p, int 
                     const bf16x8 bm = __builtin_bit_cast(bf16x8, u32x4{mb[0], mb[1], mb[2], mb[3]});
                     f32x4 Pm = mfma16x16x32(__builtin_bit_cast(bf16x8, xh), bm, f32x4{0.f, 0.f, 0.f, 0.f});
                     Pm = mfma16x16x32(__builtin_bit_cast(bf16x8, xl), bm, Pm);
-                    acc[nf] -= f16_bits_to_f32(blk[nf][0] >> 16) * Pm;
+                    acc[nf] -= f16_bits_to_f32(d16[nf] >> 16) * Pm;
                 }
             }
         }
