@@ -12,7 +12,7 @@ void launch_route_select_small(const double *logits, int T, int E, int k, int32_
                                int32_t *offsets, int32_t *perm, int32_t *inv, hipStream_t s);
 // logits: [route_logits_parts(T, H)][T][E] (partial sums for the fp64 MFMA
 // kernel, which leaves the bias to the top-k kernel)
-constexpr int ROUTE_KPARTS = 2;
+constexpr int ROUTE_KPARTS = 4;
 int route_logits_parts(int T, int H);
 void launch_route_topk(const double *logits, const float *bias, int T, int H, int E, int k, int32_t *topk_idx,
                        float *topk_w, hipStream_t s);

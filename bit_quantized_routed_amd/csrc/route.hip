@@ -115,15 +115,15 @@ __global__ __launch_bounds__(256) void route_logits_tiled(const void *x, const f
 }
 
 // Large T on the fp64 matrix cores: a 64-token x 64-expert tile and one of
-// ROUTE_KPARTS halves of H per work-group, written as partial logits
+// ROUTE_KPARTS parts of H per work-group, written as partial logits
 // [part][T][E] that the top-k kernel adds in part order.  Bigger token tiles
 // read W_r fewer times (T/64 instead of T/32 passes over its 7.34 MB); the K
-// split keeps the work-group count.  H is staged through LDS in chunks of 32
+// split keeps the work-group count up (512 at T = 2048, E = 256).  H is staged through LDS in chunks of 32
 // as fp64 (x and W_r widened exactly); each wave owns 16 experts and the
 // four 16-token quarters (four independent v_mfma_f64_16x16x4f64 chains),
 // and the raw values of chunk c + 1 are loaded into registers while chunk c
 // is computed.  Rows of the LDS tiles are padded to 33 doubles so the 16
-// lanes of one read hit 16 different bank pairs.  Needs H % 64 == 0.
+// lanes of one read hit 16 different bank pairs.  Needs H % (32 * ROUTE_KPARTS) == 0.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 template <bool XBF16>
@@ -420,7 +420,7 @@ void launch_route_topk(const double *logits, const float *bias, int T, int H, in
 #undef MOE_TOPK
 }
 
-int route_logits_parts(int T, int H) { return T > 64 && H % 64 == 0 ? ROUTE_KPARTS : 1; }
+int route_logits_parts(int T, int H) { return T > 64 && H % (32 * ROUTE_KPARTS) == 0 ? ROUTE_KPARTS : 1; }
 
 void launch_route_rank(const int32_t *topk_idx, int T, int E, int k, int32_t *rank, int32_t *tile_counts,
                        hipStream_t s)
