@@ -51,8 +51,8 @@ LAUNCH_SYMBOLS = [
     ("dec_stage2", r"dec1_gateup_kernel<(?:true|false), 2,"),
     ("dec_hform", r"dec1_hform_kernel"),
     ("dec_down_fused", r"dec1_down_fused_kernel"),
-    ("bd_gateup", r"bd_kernel<true,"),
-    ("bd_down", r"bd_kernel<false,"),
+    ("bd_gateup", r"bd_kernel<[17], "),
+    ("bd_down", r"bd_kernel<2, "),
     ("ffn_decode_gateup", r"np_kernel<\d+, true, true,"),
     ("ffn_decode_down", r"np_kernel<\d+, false, true,"),
     ("ffn_prefill_gateup", r"np_kernel<\d+, true, false,"),

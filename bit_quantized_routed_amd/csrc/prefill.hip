@@ -1140,40 +1140,54 @@ hipError_t np_launch(const FfnPass &p, hipStream_t s)
 // per row and pair (84-byte blocks are dword aligned).
 constexpr int BD_COPIES = 4;                       // selector-table copies
 
-template <bool GATEUP> struct Bd {
-    static constexpr int FMT = GATEUP ? FMT_CB2 : FMT_Q2K;
+template <int FMT_> struct Bd {
+    static constexpr int FMT = FMT_;
+    static constexpr bool GATEUP = FMT != FMT_Q2K;             // CB2 / CB2S gate/up, Q2_K down
     static constexpr int WAVES = GATEUP ? 4 : 8;
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int ROWS = 32 * WAVES;                       // weight rows per work-group
     static constexpr int COLS = GATEUP ? 16 * WAVES : 32 * WAVES; // GEMM output columns per work-group
-    static constexpr int WDW = GATEUP ? 20 : 42;                  // dwords per row and block pair
+    // dwords per row and block pair: CB2 two 10-dword block windows, CB2S the
+    // 33 dwords of the pair and one pad dword (never read), Q2_K 42
+    static constexpr int WDW = FMT == FMT_CB2 ? 20 : FMT == FMT_CB2S ? 34 : 42;
+    static constexpr int PB = FMT == FMT_CB2 ? 76 : FMT == FMT_CB2S ? 132 : 168;   // bytes of a block pair in a row
+    static constexpr int COPIES = FMT == FMT_CB2S ? 2 : BD_COPIES;                // lookup-table copies
     static constexpr int WLD = ROWS * WDW / THREADS;              // weight dwords one thread loads per pair
     static constexpr int WSLOT = ROWS * WDW * 4;                  // bytes of one weight stage
     static constexpr int APLANE = BD_BM * 1024;                   // 16 rows x 512 K bf16
     static constexpr int APT = BD_BM * 64 / THREADS;              // 8-K pieces one thread loads per pair
-    static constexpr int TAB = 256 * BD_COPIES * (GATEUP ? 16 : 8);
+    static constexpr int TAB = 256 * COPIES * (GATEUP ? 16 : 8);
     // Q2_K min term: per slot, the 16-K sub-block sums of the staged rows as
     // MFMA A operands, [block][hi, lo][16 rows][16 bf16]
     static constexpr int XSLOT = GATEUP ? 0 : 2 * 2 * BD_BM * 32;
     static_assert(ROWS * WDW % THREADS == 0 && BD_BM * 64 % THREADS == 0, "whole loads per thread");
 };
 
-template <bool GATEUP, bool TWO> constexpr int bd_lds_bytes()
+template <int FMT, bool TWO> constexpr int bd_lds_bytes()
 {
-    return 2 * Bd<GATEUP>::WSLOT + 2 * (TWO ? 2 : 1) * Bd<GATEUP>::APLANE + Bd<GATEUP>::TAB + 2 * Bd<GATEUP>::XSLOT;
+    return 2 * Bd<FMT>::WSLOT + 2 * (TWO ? 2 : 1) * Bd<FMT>::APLANE + Bd<FMT>::TAB + 2 * Bd<FMT>::XSLOT;
 }
 
-// the selector tables of np_build_table, BD_COPIES copies, built by THREADS threads
-template <int FMT, int THREADS>
+// the selector tables of np_build_table, COPIES copies, built by THREADS threads
+template <int FMT, int THREADS, int COPIES>
 __device__ __forceinline__ void bd_build_table(const FfnPass &p, uint32_t *tab)
 {
-    if constexpr (FMT == FMT_CB2) {
+    if constexpr (FMT == FMT_CB2 || FMT == FMT_CB2S) {
         for (int e = threadIdx.x; e < 256 * 4; e += THREADS) {
             const int idx = e >> 2, i = e & 3;
-            const uint32_t b0 = cb2_pos(p.codebook[8 * idx + 2 * i]), b1 = cb2_pos(p.codebook[8 * idx + 2 * i + 1]);
+            uint32_t b0, b1;
+            if constexpr (FMT == FMT_CB2) {
+                b0 = cb2_pos(p.codebook[8 * idx + 2 * i]);
+                b1 = cb2_pos(p.codebook[8 * idx + 2 * i + 1]);
+            } else {
+                // grid magnitudes {1, 3, 5, 7} -> bytes 0, 2, 4, 6 of the pool
+                const uint8_t *grid = (const uint8_t *)p.codebook;
+                b0 = (uint32_t)(grid[8 * idx + 2 * i] - 1);
+                b1 = (uint32_t)(grid[8 * idx + 2 * i + 1] - 1);
+            }
             const uint32_t sel = b0 | ((b0 + 1) << 8) | (b1 << 16) | ((b1 + 1) << 24);
 #pragma unroll
-            for (int c = 0; c < BD_COPIES; ++c) tab[(idx * BD_COPIES + c) * 4 + i] = sel;
+            for (int c = 0; c < COPIES; ++c) tab[(idx * COPIES + c) * 4 + i] = sel;
         }
     } else {
         for (int e = threadIdx.x; e < 256 * 2; e += THREADS) {
@@ -1181,16 +1195,17 @@ __device__ __forceinline__ void bd_build_table(const FfnPass &p, uint32_t *tab)
             const uint32_t q0 = (byte >> (4 * i)) & 3, q1 = (byte >> (4 * i + 2)) & 3;
             const uint32_t sel = (2 * q0) | ((2 * q0 + 1) << 8) | ((2 * q1) << 16) | ((2 * q1 + 1) << 24);
 #pragma unroll
-            for (int c = 0; c < BD_COPIES; ++c) tab[(byte * BD_COPIES + c) * 2 + i] = sel;
+            for (int c = 0; c < COPIES; ++c) tab[(byte * COPIES + c) * 2 + i] = sel;
         }
     }
 }
 
-template <bool GATEUP, bool TWO>
-__global__ __launch_bounds__(Bd<GATEUP>::THREADS) void bd_kernel(FfnPass p, int S)
+template <int FMT_, bool TWO>
+__global__ __launch_bounds__(Bd<FMT_>::THREADS) void bd_kernel(FfnPass p, int S)
 {
-    using C = Bd<GATEUP>;
-    constexpr int FMT = C::FMT, THREADS = C::THREADS, NF = 2;
+    using C = Bd<FMT_>;
+    constexpr int FMT = C::FMT, THREADS = C::THREADS, NF = 2, COPIES = C::COPIES;
+    constexpr bool GATEUP = C::GATEUP;
     extern __shared__ __attribute__((aligned(16))) uint8_t bd_smem[];
     NpTile t;
     if (!np_tile(p, S, C::COLS, BD_BM, NP_BM_DEC, t)) return;
@@ -1199,10 +1214,10 @@ __global__ __launch_bounds__(Bd<GATEUP>::THREADS) void bd_kernel(FfnPass p, int 
     uint8_t *As = bd_smem + 2 * C::WSLOT;                    // [2][hi, lo][16][1024 B]
     uint32_t *tab = (uint32_t *)(As + 2 * (TWO ? 2 : 1) * C::APLANE);
     uint8_t *Xs = (uint8_t *)tab + C::TAB;                   // [2][XSLOT] (Q2_K)
-    bd_build_table<FMT, THREADS>(p, tab);
+    bd_build_table<FMT, THREADS, COPIES>(p, tab);
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int fr = lane & 15, fc = lane >> 4, copy = lane & (BD_COPIES - 1);
+    const int fr = lane & 15, fc = lane >> 4, copy = lane & (COPIES - 1);
     const int npair = t.Kg >> 9;                             // >= 1 (K % 512 == 0, checked on the host)
 
     // ---- this thread's load slots: weight dwords (row, dword) and activation pieces (row, 8-K piece)
@@ -1218,7 +1233,8 @@ __global__ __launch_bounds__(Bd<GATEUP>::THREADS) void bd_kernel(FfnPass p, int 
         if (GATEUP) {
             col = t.n0 + (r & 63);
             base = r < 64 ? wb0 : wb1;
-            off = i < 10 ? 4 * i : 36 + 4 * (i - 10);        // the two 40-byte block windows of the pair
+            if constexpr (FMT == FMT_CB2) off = i < 10 ? 4 * i : 36 + 4 * (i - 10);   // two 40-byte block windows
+            else off = i < 33 ? 4 * i : 0;                   // CB2S: the pair, pad dword re-reads dword 0
         } else {
             col = t.n0 + r;
             base = wb0;
@@ -1228,7 +1244,7 @@ __global__ __launch_bounds__(Bd<GATEUP>::THREADS) void bd_kernel(FfnPass p, int 
         wsrc[j] = base;
         woff[j] = (uint32_t)col * (uint32_t)p.w_row_bytes + (uint32_t)off;
     }
-    constexpr int PB = GATEUP ? 76 : 168;                    // bytes of a block pair in a row
+    constexpr int PB = C::PB;
     int64_t arow[C::APT];
     int akp[C::APT], ar[C::APT];
 #pragma unroll
@@ -1325,7 +1341,17 @@ __global__ __launch_bounds__(Bd<GATEUP>::THREADS) void bd_kernel(FfnPass p, int 
             uint32_t d16[NF], f0[NF], f1[NF], f2[NF], f3[NF] = {}, f4[NF] = {}, f5[NF] = {};
 #pragma unroll
             for (int nf = 0; nf < NF; ++nf) {
-                if constexpr (FMT == FMT_CB2) {
+                if constexpr (FMT == FMT_CB2S) {
+                    // block b2 at byte 66 b2 of the pair; record j = 2 fc + h at byte 2 + 8 j:
+                    // 4 grid indices, then the sign/scale word
+                    const uint16_t *bp = (const uint16_t *)(w + wrow[nf] * C::WDW) + 33 * b2;
+                    d16[nf] = bp[0];
+                    f1[nf] = (uint32_t)bp[1 + 8 * fc] | ((uint32_t)bp[2 + 8 * fc] << 16);
+                    f2[nf] = (uint32_t)bp[3 + 8 * fc] | ((uint32_t)bp[4 + 8 * fc] << 16);
+                    f3[nf] = (uint32_t)bp[5 + 8 * fc] | ((uint32_t)bp[6 + 8 * fc] << 16);
+                    f4[nf] = (uint32_t)bp[7 + 8 * fc] | ((uint32_t)bp[8 + 8 * fc] << 16);
+                    f0[nf] = 0;
+                } else if constexpr (FMT == FMT_CB2) {
                     // odd blocks start 2 bytes into their 10-dword window
                     const uint16_t *bp = (const uint16_t *)(w + wrow[nf] * C::WDW + 10 * b2) + b2;
                     d16[nf] = bp[0];
@@ -1349,7 +1375,12 @@ __global__ __launch_bounds__(Bd<GATEUP>::THREADS) void bd_kernel(FfnPass p, int 
                 uint32_t plo[NF][2], phi[NF][2];
 #pragma unroll
                 for (int nf = 0; nf < NF; ++nf) {
-                    if constexpr (FMT == FMT_CB2) {
+                    if constexpr (FMT == FMT_CB2S) {
+                        // magnitudes {s, 3s, 5s, 7s} (exact); signs per weight below
+                        const float sj = (float)((h ? f4[nf] : f2[nf]) >> 28);
+                        plo[nf][0] = pk_bf16(sj, 3.0f * sj);
+                        phi[nf][0] = pk_bf16(5.0f * sj, 7.0f * sj);
+                    } else if constexpr (FMT == FMT_CB2) {
                         const float sj = (float)((f0[nf] >> (8 * (fc & 1) + 4 * h)) & 15u);
                         plo[nf][0] = pk_bf16(sj, 3.0f * sj);
                         phi[nf][0] = plo[nf][0] ^ 0x80008000u;
@@ -1371,9 +1402,19 @@ __global__ __launch_bounds__(Bd<GATEUP>::THREADS) void bd_kernel(FfnPass p, int 
 #pragma unroll
                     for (int nf = 0; nf < NF; ++nf) {
                         uint32_t ob[4];
-                        if constexpr (FMT == FMT_CB2) {
+                        if constexpr (FMT == FMT_CB2S) {
+                            const uint32_t idx = ((h ? f3[nf] : f1[nf]) >> (8 * s4)) & 0xffu;
+                            const u32x4 sel = *(const u32x4 *)&tab[(idx * COPIES + copy) * 4];
+                            const uint32_t n7 = ((h ? f4[nf] : f2[nf]) >> (7 * s4)) & 0x7fu;
+                            const uint32_t neg = n7 | ((uint32_t)(__builtin_popcount(n7) & 1) << 7);
+                            const uint32_t sv[4] = {sel.x, sel.y, sel.z, sel.w};
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                ob[i] = vperm(phi[nf][0], plo[nf][0], sv[i]) ^
+                                        (((neg >> (2 * i)) & 1u) << 15 | ((neg >> (2 * i + 1)) & 1u) << 31);
+                        } else if constexpr (FMT == FMT_CB2) {
                             const uint32_t idx = ((h ? f2[nf] : f1[nf]) >> (8 * s4)) & 0xffu;
-                            const u32x4 sel = *(const u32x4 *)&tab[(idx * BD_COPIES + copy) * 4];
+                            const u32x4 sel = *(const u32x4 *)&tab[(idx * COPIES + copy) * 4];
                             ob[0] = vperm(phi[nf][0], plo[nf][0], sel.x);
                             ob[1] = vperm(phi[nf][0], plo[nf][0], sel.y);
                             ob[2] = vperm(phi[nf][0], plo[nf][0], sel.z);
@@ -1381,8 +1422,8 @@ __global__ __launch_bounds__(Bd<GATEUP>::THREADS) void bd_kernel(FfnPass p, int 
                         } else {
                             const uint32_t cw = h ? (s4 < 2 ? f3[nf] : f4[nf]) : (s4 < 2 ? f1[nf] : f2[nf]);
                             const uint32_t b0 = (cw >> (16 * (s4 & 1))) & 0xffu, b1 = (cw >> (16 * (s4 & 1) + 8)) & 0xffu;
-                            const uint2 s0 = *(const uint2 *)&tab[(b0 * BD_COPIES + copy) * 2];
-                            const uint2 s1 = *(const uint2 *)&tab[(b1 * BD_COPIES + copy) * 2];
+                            const uint2 s0 = *(const uint2 *)&tab[(b0 * COPIES + copy) * 2];
+                            const uint2 s1 = *(const uint2 *)&tab[(b1 * COPIES + copy) * 2];
                             const int u = s4 >> 1;
                             ob[0] = vperm(phi[nf][u], plo[nf][u], s0.x);
                             ob[1] = vperm(phi[nf][u], plo[nf][u], s0.y);
@@ -1395,7 +1436,7 @@ __global__ __launch_bounds__(Bd<GATEUP>::THREADS) void bd_kernel(FfnPass p, int 
                     }
                 }
             }
-            if constexpr (FMT == FMT_CB2) {
+            if constexpr (FMT != FMT_Q2K) {
 #pragma unroll
                 for (int nf = 0; nf < NF; ++nf) {
                     acc[nf] += f16_bits_to_f32(d16[nf]) * P1[nf];
@@ -1474,17 +1515,17 @@ __global__ __launch_bounds__(Bd<GATEUP>::THREADS) void bd_kernel(FfnPass p, int 
     }
 }
 
-template <bool GATEUP, bool TWO>
+template <int FMT, bool TWO>
 hipError_t bd_launch(const FfnPass &p, hipStream_t s)
 {
-    constexpr int lds = bd_lds_bytes<GATEUP, TWO>();
+    constexpr int lds = bd_lds_bytes<FMT, TWO>();
     static DevSlots attr{};
-    const hipError_t e = lds_limit((const void *)bd_kernel<GATEUP, TWO>, attr, lds);
+    const hipError_t e = lds_limit((const void *)bd_kernel<FMT, TWO>, attr, lds);
     if (e != hipSuccess) return e;
-    const int S = (p.N + Bd<GATEUP>::COLS - 1) / Bd<GATEUP>::COLS;
+    const int S = (p.N + Bd<FMT>::COLS - 1) / Bd<FMT>::COLS;
     const int tiles = ffn_max_tiles(p.T, p.k, p.E, p.Nsh > 0, BD_BM, NP_BM_DEC, std::max(p.sched_parts, 1));
     const int64_t grid = (int64_t)((tiles + 7) / 8) * 8 * S;
-    bd_kernel<GATEUP, TWO><<<dim3((unsigned)grid), Bd<GATEUP>::THREADS, lds, s>>>(p, S);
+    bd_kernel<FMT, TWO><<<dim3((unsigned)grid), Bd<FMT>::THREADS, lds, s>>>(p, S);
     return hipGetLastError();
 }
 
@@ -1548,16 +1589,20 @@ hipError_t np_decode_fmt(const FfnPass &p, bool gateup, hipStream_t s)
 
 bool bd_ok(const FfnPass &up, const FfnPass &dn, int T)
 {
-    // CB2 gate/up, Q2_K down, every K a multiple of 512, at most 64 tokens
-    return up.fmt == FMT_CB2 && dn.fmt == FMT_Q2K && up.K % 512 == 0 && dn.K % 512 == 0 && T <= 64 &&
+    // CB2 or CB2S gate/up, Q2_K down, every K a multiple of 512, at most 64 tokens
+    return (up.fmt == FMT_CB2 || up.fmt == FMT_CB2S) && dn.fmt == FMT_Q2K && up.K % 512 == 0 && dn.K % 512 == 0 && T <= 64 &&
            up.out_f32 && dn.act_f32 && !up.slot == !dn.slot;
 }
 
 hipError_t launch_bd(const FfnPass &p, bool gateup, hipStream_t s)
 {
-    if (gateup) return p.act_f32 ? bd_launch<true, true>(p, s) : bd_launch<true, false>(p, s);
-    if (!p.act_f32) return hipErrorInvalidValue;
-    return bd_launch<false, true>(p, s);
+    if (gateup) {
+        if (p.fmt == FMT_CB2S) return p.act_f32 ? bd_launch<FMT_CB2S, true>(p, s) : bd_launch<FMT_CB2S, false>(p, s);
+        if (p.fmt != FMT_CB2) return hipErrorInvalidValue;
+        return p.act_f32 ? bd_launch<FMT_CB2, true>(p, s) : bd_launch<FMT_CB2, false>(p, s);
+    }
+    if (!p.act_f32 || p.fmt != FMT_Q2K) return hipErrorInvalidValue;
+    return bd_launch<FMT_Q2K, true>(p, s);
 }
 
 hipError_t launch_np_decode(const FfnPass &p, bool gateup, hipStream_t s)
