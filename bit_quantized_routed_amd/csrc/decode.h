@@ -33,7 +33,8 @@ struct DecPass {
     // staged single-token layer (dec_stage1 / dec_stage2, then dec_hform and
     // dec_down_fused with the shared down already done)
     int s1_wg;                                   // stage 1 work-groups (every one takes shared gate/up units)
-    int s2_sd_wg, s2_rt_wg;                      // stage 2 work-groups: shared down role, routed gate/up role
+    int s2_wg;                                   // stage 2 work-groups (routed gate/up units; the shared
+                                                 //    down in their prologue)
     int staged;                                  // 1: the shared down is done in stage 2 (O_sh parts),
                                                  //    so dec_hform forms routed h only and dec_down_fused
                                                  //    adds the O_sh parts to y

@@ -112,11 +112,13 @@ __device__ __forceinline__ int expert_matrix(const DecPass &p, int e) { return p
 //   GU_STAGE1  every work-group first takes router items (fp64 partial logits
 //              of one expert over one H chunk, when p.route), then shared
 //              gate/up units.
-//   GU_STAGE2  work-groups [0, s2_sd_wg) take shared down units (the shared
-//              h is complete after stage 1); the others take routed gate/up
-//              units, first selecting the experts from the partial logits
-//              when p.route (every routed work-group selects, the first also
-//              writes the routing outputs).
+//   GU_STAGE2  every work-group takes routed gate/up units.  Before them,
+//              wave 0 selects the experts from the partial logits when
+//              p.route (every work-group selects, the first also writes the
+//              routing outputs), waves 8..15 build the work-group's table,
+//              and waves 1..15 stream rows of the shared down (the shared h
+//              is complete after stage 1), so the selection's latency is
+//              spent on bytes the step needs anyway.
 enum { GU_SPLIT = 0, GU_STAGE1 = 1, GU_STAGE2 = 2 };
 
 // Whole-row GEMV pieces of the staged layer's shared expert.  A wave streams
@@ -210,11 +212,11 @@ __device__ __forceinline__ void dec1_shared_gateup_rows(const DecPass &p, const 
     }
 }
 
-// Stage 2, shared down: wave n of the role streams output rows n, n + NW, ...
-// (NW = the role's waves) over all of sh_inter, with the shared h for its lanes'
-// K positions (two bf16 terms per value) in registers; the row's sum goes to
-// O_sh[row] (one part).  Two rows are in flight per wave.
-__device__ __forceinline__ void dec1_shared_down_rows(const DecPass &p, int wg, int G)
+// Stage 2, shared down: wave slot n of NW streams output rows n, n + NW, ...
+// over all of sh_inter, with the shared h for its lanes' K positions (two bf16
+// terms per value) in registers; the row's sum goes to O_sh[row] (one part).
+// Two rows are in flight per wave.  Waves need not meet: no barrier.
+__device__ __forceinline__ void dec1_shared_down_rows(const DecPass &p, int n, int NW)
 {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int H = p.H, ns = p.Ish / 512;                          // <= DF_SHSEG segments
@@ -225,7 +227,6 @@ __device__ __forceinline__ void dec1_shared_down_rows(const DecPass &p, int wg, 
         hh[s] = *(const u32x4 *)(p.sh_hi + k);
         hl[s] = *(const u32x4 *)(p.sh_lo + k);
     }
-    const int NW = G * GU_WAVES, n = wg * GU_WAVES + wave;
     u32x4 Wa[DF_SHSEG], Wb[DF_SHSEG];
     auto load = [&](int r, u32x4 (&W4)[DF_SHSEG]) {
         const uint16_t *rw = p.sd + (int64_t)min(r, H - 1) * p.Ish + 8 * lane;
@@ -257,6 +258,20 @@ __device__ __forceinline__ void dec1_shared_down_rows(const DecPass &p, int wg, 
     }
 }
 
+// Work-groups go to the chip's 8 XCDs in turn (work-group b to XCD b % 8),
+// and each XCD has its own L2.  Numbering the G work-groups XCD by XCD (all
+// of XCD 0 first, in launch order, then XCD 1, ...) puts consecutive numbers
+// on one XCD: the K chunks of one row tile, whose 152-byte pieces of a row
+// share cache lines at their edges, then fetch those lines through one L2.
+// A bijection of [0, G) for any G.
+__device__ __forceinline__ int xcd_major(int b, int G)
+{
+    const int x = b & 7;
+    int below = 0;                                                // work-groups on XCDs 0 .. x - 1
+    for (int y = 0; y < x; ++y) below += (G - y + 7) >> 3;
+    return below + (b >> 3);
+}
+
 template <bool XF32, int MODE = GU_SPLIT, int MAXPL = 4>
 __global__ __launch_bounds__(GU_THREADS) void dec1_gateup_kernel(DecPass p)
 {
@@ -280,18 +295,15 @@ __global__ __launch_bounds__(GU_THREADS) void dec1_gateup_kernel(DecPass p)
         shared_role = true;
         G = gridDim.x;
         u = blockIdx.x;
+    } else if constexpr (MODE == GU_STAGE2) {
+        shared_role = false;                                      // the shared down runs inside the routed role
+        G = gridDim.x;
+        u = xcd_major(blockIdx.x, G);
     } else {
-        const int na = MODE == GU_STAGE2 ? p.s2_sd_wg : p.gu_sh_wg;
+        const int na = p.gu_sh_wg;
         shared_role = (int)blockIdx.x < na;
-        G = shared_role ? na : (MODE == GU_STAGE2 ? p.s2_rt_wg : p.gu_rt_wg);
+        G = shared_role ? na : p.gu_rt_wg;
         u = shared_role ? (int)blockIdx.x : (int)blockIdx.x - na;
-    }
-
-    if constexpr (MODE == GU_STAGE2) {
-        if (shared_role) {
-            dec1_shared_down_rows(p, u, G);
-            return;
-        }
     }
     if constexpr (MODE == GU_STAGE1) {
         // x (hi, and lo for fp32 x) into LDS, then whole shared gate/up rows
@@ -404,73 +416,48 @@ __global__ __launch_bounds__(GU_THREADS) void dec1_gateup_kernel(DecPass p)
     // x[8g + v] for its 32 * DEC_LUT_KB groups g and all 256 codewords c, one
     // MFMA per 32 x 32 tile (K = 16: x hi in K 0..7, x lo in K 8..15, the
     // codeword in both); then each 8-weight group of a row costs one 4-byte LDS
-    // read.  Wave w reads block w % 4 of the chunk from the gate (w < 4) or up
-    // rows of features 64 i + lane (i = 0, 1) of the tile, straight into
-    // registers.  The block sums of a row meet in LDS and one fp32 partial per
-    // row and chunk goes to part_rt; the down launch adds them in chunk order.
+    // read.  A row's blocks of the chunk go to four adjacent lanes, straight
+    // into registers; their sums meet in the quad and one fp32 partial per row
+    // and chunk goes to part_rt; the down launch adds them in chunk order.
+    // (stage 2 launches exactly R * nkc work-groups, so none returns here and
+    // every one takes its share of the shared down)
     const int nkc = p.nkc, R = G / nkc;
     const int kc = u % nkc, j0 = u / nkc;
     if (j0 >= R) return;                                          // uniform over the work-group
     const int nbH = H >> 8, rb = p.gu_row_bytes;
     const int kb = min(DEC_LUT_KB, nbH - DEC_LUT_KB * kc);        // blocks in this chunk (2 or 4: H % 512 == 0)
     float *tab = (float *)dsm;                                    // [32 * DEC_LUT_KB groups][256 codewords]
-    float *red = tab + 32 * DEC_LUT_KB * 256;                     // [2][4 blocks][256 rows]
-    if (MODE == GU_STAGE2 && p.route) {
-        // every routed work-group selects the same experts from the partial
-        // logits; the first one also writes the routing outputs
-        if (wave == 0)
-            select_one<MAXPL>(p.rpart, p.bias, p.E, p.k, p.rnc, lane, p.o_idx, p.o_w, p.o_off, p.o_perm, p.o_inv,
-                              u == 0, kid, nullptr);
-    } else if (tid < p.k) {
-        kid[tid] = expert_matrix(p, clamp_expert(p.topk_idx[tid], p.E));
-    }
-    __syncthreads();                                              // expert ids staged
-    // this wave's block of the chunk; waves past a short chunk re-read its
-    // last block and their sums are not added.  Blocks start 2-byte aligned
-    // (rows are 4-byte aligned): the 40-byte window from the aligned address
-    // at or below the block covers it, and stays in the row (a block at a
-    // dword boundary is never the last one, since every row has an even
-    // number of blocks).
-    const int bw = wave & 3, hr = (wave >> 2) & 1, i0 = wave >> 3;
-    const int B = DEC_LUT_KB * kc + min(bw, kb - 1);
-    const int boff = (38 * B) & ~3;
-    const bool odd = __builtin_amdgcn_readfirstlane(B & 1);
-    const float *tb = tab + 32 * 256 * min(bw, kb - 1);
-    const int nft = p.I / 128, ntile = p.k * nft;
-    const uint8_t *wmat = hr ? p.wu : p.wg;
-    auto rowp = [&](int t, int i) -> const uint32_t * {
-        const int s = t / nft, f = 128 * (t - s * nft) + 64 * i + lane;
-        return (const uint32_t *)(wmat + (int64_t)kid[s] * p.gu_expert_bytes + (int64_t)f * rb + boff);
-    };
-    // GU_PF register sets in a ring: while one tile is computed, the next
-    // GU_PF - 1 tiles of this work-group are in flight (a work-group's tiles are
-    // scattered 40-byte row windows, so several must be requested at once to
-    // keep enough bytes moving per CU).  Loads past the last tile re-read the
-    // first one and are never used.
-    uint32_t W[GU_PF][10];
-    auto load = [&](int t, uint32_t (&Wr)[10]) {
-        const uint32_t *src = rowp(t, i0);
-#pragma unroll
-        for (int e = 0; e < 10; ++e) Wr[e] = src[e];
-    };
-    // the first tiles load while the table is built
-    int t = j0;
-#pragma unroll
-    for (int i = 0; i < GU_PF; ++i) load(t + i * R < ntile ? t + i * R : t, W[i]);
-    {
-        // wave w: codewords 32 (w % 8) .. + 31 against the 32-group tiles w / 8, w / 8 + 2, ...
+    // The chunk's table and the expert ids are independent: waves 8..15
+    // build the table (wave w: codewords 32 (w % 8) .. + 31 against every
+    // 32-group tile of the chunk) while wave 0 selects the experts, so the
+    // selection's latency covers the table's
+    if (wave >= 8) {
         const int c = 32 * (wave & 7) + (lane & 31), hl = lane >> 5;
         const uint64_t cw = *(const uint64_t *)(p.codebook + 8 * c);
+        f32x4 xv4[DEC_LUT_KB][2];
+        bf16x8 xa[DEC_LUT_KB];
+#pragma unroll
+        for (int gt = 0; gt < DEC_LUT_KB; ++gt) {
+            // tiles past a short chunk re-read its last one and are not built
+            const int k = 256 * (DEC_LUT_KB * kc + min(gt, kb - 1)) + 8 * (lane & 31);
+            if (XF32) {
+                xv4[gt][0] = *(const f32x4 *)((const float *)p.x + k);
+                xv4[gt][1] = *(const f32x4 *)((const float *)p.x + k + 4);
+            } else {
+                xa[gt] = *(const bf16x8 *)((const uint16_t *)p.x + k);
+            }
+        }
         uint32_t cb[8];
 #pragma unroll
         for (int v = 0; v < 8; ++v) cb[v] = f32_to_bf16_exact((float)(int8_t)(cw >> (8 * v)));
         const bf16x8 Bc = __builtin_bit_cast(bf16x8, pack8(cb));
-        for (int gt = wave >> 3; gt < kb; gt += 2) {
-            const int k = 256 * (DEC_LUT_KB * kc + gt) + 8 * (lane & 31);
+#pragma unroll
+        for (int gt = 0; gt < DEC_LUT_KB; ++gt) {
+            if (gt >= kb) break;                                  // uniform over the work-group
             bf16x8 A = {};
             if (XF32) {
-                const f32x4 v0 = *(const f32x4 *)((const float *)p.x + k), v1 = *(const f32x4 *)((const float *)p.x + k + 4);
-                const float xv[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                const float xv[8] = {xv4[gt][0][0], xv4[gt][0][1], xv4[gt][0][2], xv4[gt][0][3],
+                                     xv4[gt][1][0], xv4[gt][1][1], xv4[gt][1][2], xv4[gt][1][3]};
                 uint32_t h8[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -480,7 +467,7 @@ __global__ __launch_bounds__(GU_THREADS) void dec1_gateup_kernel(DecPass p)
                 }
                 A = __builtin_bit_cast(bf16x8, pack8(h8));
             } else if (hl == 0) {
-                A = *(const bf16x8 *)((const uint16_t *)p.x + k);
+                A = xa[gt];
             }
             f32x16 D = {};
             D = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, Bc, D, 0, 0, 0);
@@ -489,25 +476,61 @@ __global__ __launch_bounds__(GU_THREADS) void dec1_gateup_kernel(DecPass p)
             for (int v = 0; v < 16; ++v) tab[(32 * gt + 8 * (v >> 2) + 4 * hl + (v & 3)) * 256 + c] = D[v];
         }
     }
+    if constexpr (MODE == GU_STAGE2) {
+        // stage 2: waves 1..15 of every work-group stream the shared down's
+        // rows (independent of the selection) while wave 0 selects
+        if (wave > 0 && p.Ish > 0) dec1_shared_down_rows(p, u * (GU_WAVES - 1) + wave - 1, G * (GU_WAVES - 1));
+    }
+    if (MODE == GU_STAGE2 && p.route) {
+        // every routed work-group selects the same experts from the partial
+        // logits; the first one also writes the routing outputs
+        if (wave == 0)
+            select_one<MAXPL>(p.rpart, p.bias, p.E, p.k, p.rnc, lane, p.o_idx, p.o_w, p.o_off, p.o_perm, p.o_inv,
+                              u == 0, kid, nullptr);
+    } else if (tid < p.k) {
+        kid[tid] = expert_matrix(p, clamp_expert(p.topk_idx[tid], p.E));
+    }
+    __syncthreads();                                              // expert ids and table staged
+    // Lane (r, b) of wave w, r = lane / 4, b = lane % 4: block b of the chunk
+    // in row 16 (w / 2) + r of the tile's gate (w even) or up (w odd)
+    // features.  The four blocks of a row sit in adjacent lanes, so one load
+    // instruction reads the row's whole chunk and its cache lines are used
+    // at once; lanes past a short chunk re-read its last block and their
+    // sums are not added.  Blocks start 2-byte aligned (rows are 4-byte
+    // aligned): the 40-byte window from the aligned address at or below the
+    // block covers it, and stays in the row (a block at a dword boundary is
+    // never the last one, since every row has an even number of blocks).
+    const int bl = lane & 3, hr = wave & 1, fo = 16 * (wave >> 1) + (lane >> 2);
+    const int B = DEC_LUT_KB * kc + min(bl, kb - 1);
+    const int boff = (38 * B) & ~3;
+    const bool odd = B & 1;                                       // the block starts 2 bytes into its window
+    const float *tb = tab + 32 * 256 * min(bl, kb - 1);
+    const int nft = p.I / 128, ntile = p.k * nft;
+    const uint8_t *wmat = hr ? p.wu : p.wg;
+    auto rowp = [&](int t) -> const uint32_t * {
+        const int s = t / nft, f = 128 * (t - s * nft) + fo;
+        return (const uint32_t *)(wmat + (int64_t)kid[s] * p.gu_expert_bytes + (int64_t)f * rb + boff);
+    };
+    // GU_PF register sets in a ring: while one tile is computed, the next
+    // GU_PF - 1 tiles of this work-group are in flight.  Loads past the last
+    // tile re-read the first one and are never used.
+    uint32_t W[GU_PF][10];
+    auto load = [&](int t, uint32_t (&Wr)[10]) {
+        const uint32_t *src = rowp(t);
+#pragma unroll
+        for (int e = 0; e < 10; ++e) Wr[e] = src[e];
+    };
+    int t = j0;
+#pragma unroll
+    for (int i = 0; i < GU_PF; ++i) load(t + i * R < ntile ? t + i * R : t, W[i]);
     // one row's block: sum over sub-blocks of s_j * (four table entries), times d
-    auto task = [&](const uint32_t (&W)[10], auto sh2) -> float {
-        constexpr bool SH2 = decltype(sh2)::value;
-        uint32_t d16, sc, ix[8];
-        if constexpr (SH2) {
-            d16 = W[0] >> 16;
-            sc = W[1];
-#pragma unroll
-            for (int m = 0; m < 8; ++m) ix[m] = W[2 + m];
-        } else {
-            d16 = W[0] & 0xffffu;
-            sc = __builtin_amdgcn_alignbyte(W[1], W[0], 2);
-#pragma unroll
-            for (int m = 0; m < 8; ++m) ix[m] = __builtin_amdgcn_alignbyte(W[2 + m], W[1 + m], 2);
-        }
+    auto task = [&](const uint32_t (&W)[10]) -> float {
+        const uint32_t d16 = odd ? W[0] >> 16 : W[0] & 0xffffu;
+        const uint32_t sc = odd ? W[1] : __builtin_amdgcn_alignbyte(W[1], W[0], 2);
         float acc = 0.f;
 #pragma unroll
         for (int sb = 0; sb < 8; ++sb) {
-            const uint32_t w = ix[sb];
+            const uint32_t w = odd ? W[2 + sb] : __builtin_amdgcn_alignbyte(W[2 + sb], W[1 + sb], 2);
             const float *t4 = tb + 4 * sb * 256;
             const float tv = (t4[w & 255u] + t4[256 + ((w >> 8) & 255u)]) + (t4[512 + ((w >> 16) & 255u)] + t4[768 + (w >> 24)]);
             acc += (float)((sc >> (4 * sb)) & 15u) * tv;
@@ -515,30 +538,36 @@ __global__ __launch_bounds__(GU_THREADS) void dec1_gateup_kernel(DecPass p)
         return f16_bits_to_f32(d16) * acc;
     };
     const int64_t cstride = (int64_t)2 * p.k * p.I;               // one K chunk of part_rt
-    auto tile = [&](int tt, int buf, const uint32_t (&W)[10]) {
-        red[(buf * 4 + bw) * 256 + 128 * hr + 64 * i0 + lane] = odd ? task(W, std::true_type{}) : task(W, std::false_type{});
-        __syncthreads();
-        if (tid < 256) {
+    // a row's block sums meet in the quad's first lane (quad_perm moves),
+    // added in block order; that lane writes the row's partial
+    auto quad_get = [](float v, auto j) -> float {
+        constexpr int J = decltype(j)::value;
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), J * 0x55, 0xF, 0xF, false));
+    };
+    auto tile = [&](int tt, const uint32_t (&W)[10]) {
+        const float v = task(W);
+        const float v1 = quad_get(v, std::integral_constant<int, 1>{});
+        const float v2 = quad_get(v, std::integral_constant<int, 2>{});
+        const float v3 = quad_get(v, std::integral_constant<int, 3>{});
+        if (bl == 0) {
+            float sum = v;
+            if (kb > 1) sum += v1;
+            if (kb > 2) sum += v2;
+            if (kb > 3) sum += v3;
             const int s = tt / nft, f0 = 128 * (tt - s * nft);
-            const float *rs = red + buf * 4 * 256 + tid;
-            float sum = rs[0];
-            for (int b = 1; b < kb; ++b) sum += rs[256 * b];
-            p.part_rt[kc * cstride + (int64_t)(2 * s + (tid >> 7)) * p.I + f0 + (tid & 127)] = sum;
+            p.part_rt[kc * cstride + (int64_t)(2 * s + hr) * p.I + f0 + fo] = sum;
         }
     };
-    __syncthreads();                                              // table staged
     // the ring, unrolled so every register set has a fixed name: a tile is
     // computed from its set, which then takes the tile GU_PF steps later (an
-    // unconditional load); the two LDS buffers of block sums alternate, so one
-    // barrier per tile suffices
+    // unconditional load).  Waves do not meet: no barrier per tile.
 #define MOE_GU_STEP(i)                                                             \
     if constexpr ((i) < GU_PF) {                                                   \
-        tile(t, buf, W[i]);                                                        \
-        buf ^= 1;                                                                  \
+        tile(t, W[i]);                                                             \
         load(t + GU_PF * R < ntile ? t + GU_PF * R : t, W[i]);                     \
         if ((t += R) >= ntile) break;                                              \
     }
-    for (int buf = 0;;) {
+    for (;;) {
         MOE_GU_STEP(0)
         MOE_GU_STEP(1)
         MOE_GU_STEP(2)
@@ -1043,11 +1072,11 @@ __global__ __launch_bounds__(DF_THREADS) void dec1_down_fused_kernel(DecPass p, 
 namespace {
 
 // shared role: x (one or two bf16 terms) and the wave sums; routed role: the
-// chunk's table and the two buffers of block sums.  One launch, so the larger.
+// chunk's table.  One launch, so the larger.
 size_t lds_gateup(int H, bool xf32)
 {
     const size_t sh = (size_t)(xf32 ? 4 : 2) * H + 2 * 16 * GU_WAVES * sizeof(float);
-    const size_t rt = (32 * DEC_LUT_KB * 256 + 2 * 4 * 256) * sizeof(float);
+    const size_t rt = (size_t)32 * DEC_LUT_KB * 256 * sizeof(float);
     return std::max(sh, rt);
 }
 
@@ -1096,9 +1125,6 @@ void split_roles(int n_a, double c_a, int n_b, double c_b, int G, int &g_a, int 
 // role work in proportion to these costs.
 constexpr double CB2_COST = 1.5;
 constexpr double Q2K_COST = 2.5;
-// the same for the staged layer's stage 2, against whole-row bf16 streaming
-// (decode1 measured within 1% for weights 2 to 6)
-constexpr double S2_CB2_COST = 3.0;
 
 }  // namespace
 
@@ -1187,7 +1213,7 @@ hipError_t launch_dec_down_fused(const DecPass &p, hipStream_t s)
 namespace {
 
 size_t lds_stage1(int H, bool xf32) { return (size_t)(xf32 ? 4 : 2) * H + 2 * 16 * GU_WAVES * sizeof(float); }
-size_t lds_stage2() { return (32 * DEC_LUT_KB * 256 + 2 * 4 * 256) * sizeof(float); }
+size_t lds_stage2() { return (size_t)32 * DEC_LUT_KB * 256 * sizeof(float); }
 
 // experts per lane of the selection: 4 (E <= 256) or 16 (E <= 1024)
 bool wide_select(const DecPass &p) { return p.route && p.E > 256; }
@@ -1207,8 +1233,8 @@ void dec_plan_staged(DecPass &p)
     int g1 = std::max(1, (p.Ish + 7) / 8);
     if (p.route) g1 = std::max(g1, std::min(ncu, (p.E * p.rnc + GU_WAVES - 1) / GU_WAVES));
     p.s1_wg = std::min(g1, occ1 * ncu);
-    // stage 2: the routed gate/up (one LDS table per work-group) beside the
-    // shared down's rows (16 per work-group and round), split by cost per byte
+    // stage 2: routed gate/up units (one LDS table per work-group) on every
+    // work-group, R per K chunk; the shared down rides in their prologue
     const size_t l2 = lds_stage2();
     const int wide = wide_select(p) ? 1 : 0;
     int occ2;
@@ -1216,13 +1242,9 @@ void dec_plan_staged(DecPass &p)
                              : resident(dec1_gateup_kernel<true, GU_STAGE2, 4>, l2, occ_s2[2], GU_THREADS);
     else occ2 = wide ? resident(dec1_gateup_kernel<false, GU_STAGE2, 16>, l2, occ_s2[1], GU_THREADS)
                      : resident(dec1_gateup_kernel<false, GU_STAGE2, 4>, l2, occ_s2[0], GU_THREADS);
-    const int G = occ2 * ncu, ntile = p.k * p.I / 128;
-    const int n_sd = p.Ish > 0 ? (p.H + GU_WAVES - 1) / GU_WAVES : 0;
-    int g_sd = 0, g_rt = 0;
-    split_roles(n_sd, (double)GU_WAVES * p.Ish * 2, p.nkc * ntile, S2_CB2_COST * 256.0 * DEC_LUT_KB * 38, G, g_sd, g_rt);
-    const int R = std::max(1, std::min(ntile, (g_rt + p.nkc / 2) / p.nkc));
-    p.s2_rt_wg = R * p.nkc;
-    p.s2_sd_wg = n_sd ? std::max(1, std::min(n_sd, G - p.s2_rt_wg)) : 0;
+    const int ntile = p.k * p.I / 128;
+    const int R = std::max(1, std::min(ntile, occ2 * ncu / p.nkc));
+    p.s2_wg = R * p.nkc;
     p.staged = 1;
 }
 
@@ -1237,7 +1259,7 @@ hipError_t launch_dec_stage1(const DecPass &p, hipStream_t s)
 hipError_t launch_dec_stage2(const DecPass &p, hipStream_t s)
 {
     const size_t lds = lds_stage2();
-    const int grid = p.s2_sd_wg + p.s2_rt_wg;
+    const int grid = p.s2_wg;
     const bool wide = wide_select(p);
     if (p.x_f32) {
         if (wide) dec1_gateup_kernel<true, GU_STAGE2, 16><<<grid, GU_THREADS, lds, s>>>(p);

@@ -137,62 +137,39 @@ __device__ __forceinline__ void wave_argmax(double &bv, int &be)
     be = e;
 }
 
-// T == 1: one wave selects and groups.  Lane l holds experts l, l+64, ...;
-// k rounds of a wave-wide arg-max over (logit descending, expert ascending)
-// pick k distinct experts in top-k order.  The grouping of one token is the
-// selection sorted by expert id: offsets come from ballots of the taken
-// flags, and the position of slot j is the number of selected ids below its
-// own.  No LDS, no barriers.
-// With write false only kid / kw (when non-null: the selected experts and
-// their weights in top-k order, e.g. in LDS) are filled.
-template <int MAXPL>                              // experts per lane: E <= 64 * MAXPL
-__device__ __forceinline__ void select_one(const double *part, const float *bias, int E, int k, int NC, int lane,
-                                           int32_t *topk_idx, float *topk_w, int32_t *offsets, int32_t *perm,
-                                           int32_t *inv, bool write, int32_t *kid, float *kw)
+// Candidate logit of expert e at T == 1: its NC (<= 4) partials, all loaded
+// together and added in chunk order, plus the bias; NaN ranks below every
+// number.
+__device__ __forceinline__ double select_logit(const double *part, const float *bias, int E, int NC, int e)
 {
-    double v[MAXPL];
+    double c4[4];
 #pragma unroll
-    for (int i = 0; i < MAXPL; ++i) {
-        const int e = lane + 64 * i;
-        double s = -INFINITY;
-        if (64 * i < E && e < E) {
-            // all chunk loads go out together (NC <= 4), then add in chunk order
-            double c4[4];
+    for (int c = 0; c < 4; ++c) c4[c] = c < NC ? part[(size_t)c * E + e] : 0.0;
+    const double bv = bias ? (double)bias[e] : 0.0;
+    double s = c4[0];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) c4[c] = c < NC ? part[(size_t)c * E + e] : 0.0;
-            const double bv = bias ? (double)bias[e] : 0.0;
-            s = c4[0];
-#pragma unroll
-            for (int c = 1; c < 4; ++c) if (c < NC) s += c4[c];
-            if (bias) s += bv;
-            if (s != s) s = -INFINITY;            // NaN ranks below every number
-        }
-        v[i] = s;
-    }
-    uint32_t taken = 0;
-    int my_e = 0;
-    double my_l = 0.0;
-    for (int j = 0; j < k; ++j) {
-        double bv = -INFINITY;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < MAXPL; ++i) {
-            if (64 * i >= E) break;
-            const int e = lane + 64 * i;
-            // e grows with i, so a strict '>' keeps the lowest expert among equals
-            if (e < E && !((taken >> i) & 1u) && (be == 0x7fffffff || v[i] > bv)) { bv = v[i]; be = e; }
-        }
-        wave_argmax(bv, be);
-        if ((be & 63) == lane && be < E) taken |= 1u << (be >> 6);
-        if (lane == j) { my_e = be; my_l = bv; }
-    }
-    // weights: sigmoid of the selected logits over their sum (fp64)
+    for (int c = 1; c < 4; ++c) if (c < NC) s += c4[c];
+    if (bias) s += bv;
+    return s != s ? -INFINITY : s;
+}
+
+// The end of a T == 1 selection, in one wave: lane j < k holds slot j's
+// expert my_e and logit my_l; bit i of taken says whether expert lane + 64 i
+// was selected.  Weights are the sigmoids of the selected logits over their
+// sum (fp64).  The grouping of one token is the selection sorted by expert
+// id: offsets come from ballots of the taken flags, and the position of slot
+// j is the number of selected ids below its own.  With write false only kid /
+// kw (when non-null: the selected experts and their weights in top-k order,
+// e.g. in LDS) are filled.
+template <int MAXPL>
+__device__ __forceinline__ void select_finish(int E, int k, int lane, int my_e, double my_l, uint32_t taken,
+                                              int32_t *topk_idx, float *topk_w, int32_t *offsets, int32_t *perm,
+                                              int32_t *inv, bool write, int32_t *kid, float *kw)
+{
     double sg = lane < k ? 1.0 / (1.0 + exp(-my_l)) : 0.0;
     double ssum = sg;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ssum += __shfl_xor(ssum, off, 64);
-    // grouping: one ballot of the taken flags per slot gives both the
-    // offsets and, for slot j's expert, the number of selected experts below it
     uint64_t mk[MAXPL];
 #pragma unroll
     for (int i = 0; i < MAXPL; ++i) mk[i] = 64 * i < E ? __ballot((taken >> i) & 1u) : 0ull;
@@ -223,6 +200,40 @@ __device__ __forceinline__ void select_one(const double *part, const float *bias
         base += __popcll(mk[i]);
     }
     if (lane == 0) offsets[E] = base;
+}
+
+// T == 1: one wave selects and groups.  Lane l holds experts l, l+64, ...;
+// k rounds of a wave-wide arg-max over (logit descending, expert ascending)
+// pick k distinct experts in top-k order.  No LDS, no barriers.
+template <int MAXPL>                              // experts per lane: E <= 64 * MAXPL
+__device__ __forceinline__ void select_one(const double *part, const float *bias, int E, int k, int NC, int lane,
+                                           int32_t *topk_idx, float *topk_w, int32_t *offsets, int32_t *perm,
+                                           int32_t *inv, bool write, int32_t *kid, float *kw)
+{
+    double v[MAXPL];
+#pragma unroll
+    for (int i = 0; i < MAXPL; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = 64 * i < E && e < E ? select_logit(part, bias, E, NC, e) : -INFINITY;
+    }
+    uint32_t taken = 0;
+    int my_e = 0;
+    double my_l = 0.0;
+    for (int j = 0; j < k; ++j) {
+        double bv = -INFINITY;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < MAXPL; ++i) {
+            if (64 * i >= E) break;
+            const int e = lane + 64 * i;
+            // e grows with i, so a strict '>' keeps the lowest expert among equals
+            if (e < E && !((taken >> i) & 1u) && (be == 0x7fffffff || v[i] > bv)) { bv = v[i]; be = e; }
+        }
+        wave_argmax(bv, be);
+        if ((be & 63) == lane && be < E) taken |= 1u << (be >> 6);
+        if (lane == j) { my_e = be; my_l = bv; }
+    }
+    select_finish<MAXPL>(E, k, lane, my_e, my_l, taken, topk_idx, topk_w, offsets, perm, inv, write, kid, kw);
 }
 
 }  // namespace moe
