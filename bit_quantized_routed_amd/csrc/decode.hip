@@ -63,6 +63,7 @@ constexpr size_t LDS_MAX = 160 * 1024;
 // slower (63.1 / 65.5 / 67.5 / 69.1 us per step for 2 / 3 / 4 / 5).
 constexpr int GU_PF = 2;
 static_assert(GU_PF >= 2 && GU_PF <= 6, "ring of 2 to 6 register sets");
+static_assert(256 * DEC_LUT_KB * DN_MAXKC / 8 <= GU_THREADS, "stage 1 stages x with one 8-value piece per thread");
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -106,12 +107,14 @@ __device__ __forceinline__ int clamp_expert(int g, int E) { return min(max(g, 0)
 __device__ __forceinline__ int expert_matrix(const DecPass &p, int e) { return p.slot ? max(p.slot[e], 0) : e; }
 
 // ============================================================== gate / up
-// One kernel, three launch modes:
+// One kernel, four launch modes:
 //   GU_SPLIT   work-groups [0, gu_sh_wg) take shared-expert gate/up units
 //              u = wg, wg + gu_sh_wg, ...; the others take routed units.
 //   GU_STAGE1  every work-group first takes router items (fp64 partial logits
 //              of one expert over one H chunk, when p.route), then shared
 //              gate/up units.
+//   GU_STAGE1R the same with bf16 x and at most one item per wave: a wave's
+//              item overlaps its first shared rows.
 //   GU_STAGE2  every work-group takes routed gate/up units.  Before them,
 //              wave 0 selects the experts from the partial logits when
 //              p.route (every work-group selects, the first also writes the
@@ -119,7 +122,7 @@ __device__ __forceinline__ int expert_matrix(const DecPass &p, int e) { return p
 //              and waves 1..15 stream rows of the shared down (the shared h
 //              is complete after stage 1), so the selection's latency is
 //              spent on bytes the step needs anyway.
-enum { GU_SPLIT = 0, GU_STAGE1 = 1, GU_STAGE2 = 2 };
+enum { GU_SPLIT = 0, GU_STAGE1 = 1, GU_STAGE2 = 2, GU_STAGE1R = 3 };
 
 // Whole-row GEMV pieces of the staged layer's shared expert.  A wave streams
 // rows from HBM in 512-wide K segments (64 lanes x 8 bf16, 1 KB contiguous per
@@ -159,45 +162,57 @@ __device__ __forceinline__ float wave_sum(float v)
 // The halves meet in LDS and the first wave writes the feature's
 // h = silu(g) * u as two bf16 terms (sh_hi, sh_lo).  x (one or two bf16 terms)
 // was staged in LDS by the caller.
-template <bool XF32>
+// hook(i), i = 0, 1: called once each per wave, in order, right after the
+// wave's i-th batch of shared loads is requested (at the start or the end when
+// the wave has fewer batches), for work that should run while those loads are
+// in flight; it may use wave-wide operations.  Every load here is
+// unconditional (a wave past sh_inter re-reads the last row and does not use
+// it), so the compiler can wait for exactly the loads a use needs.
+template <bool XF32, typename Hook>
 __device__ __forceinline__ void dec1_shared_gateup_rows(const DecPass &p, const uint16_t *xh, const uint16_t *xl,
-                                                        float *red, int G)
+                                                        float *red, int G, Hook &&hook)
 {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int H = p.H, ns = H / 512, half = wave & 1, nlo = ns / 2;
     const int s0 = half ? nlo : 0, s1 = half ? ns : nlo;
     const int rounds = (p.Ish + 8 * G - 1) / (8 * G);
     constexpr int B = 4;                                          // segments requested together
+    const int nb0 = rounds > 0 ? (s1 - s0 + B - 1) / B : 0;       // round 0's batches (uniform over the wave)
+    if (nb0 == 0) {
+        hook(0);
+        hook(1);
+    }
     for (int rd = 0; rd < rounds; ++rd) {
         const int f = 8 * (rd * G + (int)blockIdx.x) + (wave >> 1);
+        const int fl = min(f, p.Ish - 1);
         float ag = 0.f, au = 0.f;
-        if (f < p.Ish) {                                          // uniform over the wave
-            const uint16_t *rg = p.sg + (int64_t)f * H + 8 * lane, *ru = p.su + (int64_t)f * H + 8 * lane;
-            for (int sb = s0; sb < s1; sb += B) {
-                u32x4 g4[B], u4[B];
+        const uint16_t *rg = p.sg + (int64_t)fl * H + 8 * lane, *ru = p.su + (int64_t)fl * H + 8 * lane;
+        for (int sb = s0; sb < s1; sb += B) {
+            u32x4 g4[B], u4[B];
 #pragma unroll
-                for (int i = 0; i < B; ++i) {
-                    const int sg = min(sb + i, s1 - 1);           // past the half: re-read, not used
-                    g4[i] = *(const u32x4 *)(rg + 512 * sg);
-                    u4[i] = *(const u32x4 *)(ru + 512 * sg);
-                }
+            for (int i = 0; i < B; ++i) {
+                const int sg = min(sb + i, s1 - 1);               // past the half: re-read, not used
+                g4[i] = *(const u32x4 *)(rg + 512 * sg);
+                u4[i] = *(const u32x4 *)(ru + 512 * sg);
+            }
+            if (rd == 0 && sb == s0) hook(0);                     // uniform over the wave
+            if (rd == 0 && sb == s0 + B) hook(1);
 #pragma unroll
-                for (int i = 0; i < B; ++i) {
-                    if (sb + i >= s1) break;
-                    const int k = 512 * (sb + i) + 8 * lane;
-                    const u32x4 a = *(const u32x4 *)&xh[k];
-                    ag = dot8(g4[i], a, ag);
-                    au = dot8(u4[i], a, au);
-                    if (XF32) {
-                        const u32x4 al = *(const u32x4 *)&xl[k];
-                        ag = dot8(g4[i], al, ag);
-                        au = dot8(u4[i], al, au);
-                    }
+            for (int i = 0; i < B; ++i) {
+                if (sb + i >= s1) break;
+                const int k = 512 * (sb + i) + 8 * lane;
+                const u32x4 a = *(const u32x4 *)&xh[k];
+                ag = dot8(g4[i], a, ag);
+                au = dot8(u4[i], a, au);
+                if (XF32) {
+                    const u32x4 al = *(const u32x4 *)&xl[k];
+                    ag = dot8(g4[i], al, ag);
+                    au = dot8(u4[i], al, au);
                 }
             }
-            ag = wave_sum(ag);
-            au = wave_sum(au);
         }
+        ag = wave_sum(ag);
+        au = wave_sum(au);
         if (half && lane == 0) { red[2 * (wave >> 1)] = ag; red[2 * (wave >> 1) + 1] = au; }
         __syncthreads();
         if (!half && lane == 0 && f < p.Ish) {
@@ -210,6 +225,7 @@ __device__ __forceinline__ void dec1_shared_gateup_rows(const DecPass &p, const 
         }
         __syncthreads();
     }
+    if (nb0 == 1) hook(1);
 }
 
 // Stage 2, shared down: wave slot n of NW streams output rows n, n + NW, ...
@@ -283,15 +299,7 @@ __global__ __launch_bounds__(GU_THREADS) void dec1_gateup_kernel(DecPass p)
 
     bool shared_role;
     int G, u;
-    if constexpr (MODE == GU_STAGE1) {
-        if (p.route) {
-            // the router's partial logits, one item per wave, spread over the
-            // whole grid before the shared units (the same items and
-            // arithmetic as the router's own partial-logit launch)
-            const int nitems = p.E * p.rnc, nw = (int)gridDim.x * GU_WAVES;
-            for (int item = (int)blockIdx.x + (int)gridDim.x * wave; item < nitems; item += nw)
-                route_partial_item<1, 1, !XF32>(p.x, p.wr, 1, H, p.E, p.rnc, p.rhc, item, lane, p.rpart);
-        }
+    if constexpr (MODE == GU_STAGE1 || MODE == GU_STAGE1R) {
         shared_role = true;
         G = gridDim.x;
         u = blockIdx.x;
@@ -305,25 +313,66 @@ __global__ __launch_bounds__(GU_THREADS) void dec1_gateup_kernel(DecPass p)
         G = shared_role ? na : p.gu_rt_wg;
         u = shared_role ? (int)blockIdx.x : (int)blockIdx.x - na;
     }
-    if constexpr (MODE == GU_STAGE1) {
-        // x (hi, and lo for fp32 x) into LDS, then whole shared gate/up rows
-        uint16_t *xh = (uint16_t *)dsm;                           // [H]
-        uint16_t *xl = xh + H;                                    // [H] (fp32 x only)
-        float *red = (float *)(dsm + (XF32 ? 4 : 2) * (size_t)H); // [8 features][2]
-        for (int i = tid; i < H / 8; i += GU_THREADS) {
-            if (XF32) {
-                const float *src = (const float *)p.x + 8 * i;
-                uint32_t h[8], l[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) split_bf16(src[e], h[e], l[e]);
-                *(u32x4 *)&xh[8 * i] = pack8(h);
-                *(u32x4 *)&xl[8 * i] = pack8(l);
-            } else {
-                *(u32x4 *)&xh[8 * i] = *(const u32x4 *)((const uint16_t *)p.x + 8 * i);
+    if constexpr (MODE == GU_STAGE1 || MODE == GU_STAGE1R) {
+        // x (hi, and lo for fp32 x) into LDS, the router's partial logits
+        // (the same items and arithmetic as the router's own partial-logit
+        // launch), then whole shared gate/up rows.
+        uint16_t *xh = (uint16_t *)dsm;                           // [H] and a spare 8-value slot
+        uint16_t *xl = xh + H + 8;                                // [H] (fp32 x only)
+        float *red = (float *)(dsm + (XF32 ? 4 : 2) * (size_t)(H + 8));   // [8 features][2]
+        const int nw = (int)gridDim.x * GU_WAVES, item = (int)blockIdx.x + (int)gridDim.x * wave;
+        if constexpr (MODE == GU_STAGE1R) {
+            // bf16 x, one router item per wave at most, in one batch (the
+            // launcher checks): the wave requests x, then its item's router
+            // weights, and does the item's arithmetic (x from LDS) once its
+            // first shared rows are requested too, so the three streams
+            // overlap.  Loads are unconditional (past the end they re-read the
+            // last piece or item), so the compiler waits for exactly the loads
+            // each use needs.  H / 8 <= GU_THREADS: one 8-value piece of x per
+            // thread.
+            static_assert(!XF32, "the overlapped router items read bf16 x from LDS");
+            const int nitems = p.E * p.rnc;
+            const u32x4 xb = *(const u32x4 *)((const uint16_t *)p.x + 8 * min(tid, H / 8 - 1));
+            RouteItem1 ri;
+            route_item1_begin(H, p.rnc, p.rhc, min(item, nitems - 1), lane, ri);
+            route_item1_load(p.wr, H, 0, ri);
+            // every thread stores (those past H / 8 into a spare slot), so the
+            // x load is not moved behind the router loads into a branch
+            *(u32x4 *)&xh[tid < H / 8 ? 8 * tid : H] = xb;
+            __syncthreads();
+            const bool mine = item < nitems;                      // uniform over the wave
+            // first half of the item under the first shared batch, its second
+            // half's loads then, its arithmetic under the second batch
+            dec1_shared_gateup_rows<false>(p, xh, xl, red, G, [&](int i) {
+                if (i == 0) {
+                    if (mine) route_item1_step(xh, 0, ri);
+                    route_item1_load(p.wr, H, 1, ri);
+                } else if (mine) {
+                    route_item1_step(xh, 1, ri);
+                    route_item1_end(ri, p.E, lane, p.rpart);
+                }
+            });
+        } else {
+            // the items first, spread over the whole grid
+            if (p.route) {
+                for (int it = item; it < p.E * p.rnc; it += nw)
+                    route_partial_item<1, 1, !XF32>(p.x, p.wr, 1, H, p.E, p.rnc, p.rhc, it, lane, p.rpart);
             }
+            for (int i = tid; i < H / 8; i += GU_THREADS) {
+                if (XF32) {
+                    const float *src = (const float *)p.x + 8 * i;
+                    uint32_t h[8], l[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) split_bf16(src[e], h[e], l[e]);
+                    *(u32x4 *)&xh[8 * i] = pack8(h);
+                    *(u32x4 *)&xl[8 * i] = pack8(l);
+                } else {
+                    *(u32x4 *)&xh[8 * i] = *(const u32x4 *)((const uint16_t *)p.x + 8 * i);
+                }
+            }
+            __syncthreads();
+            dec1_shared_gateup_rows<XF32>(p, xh, xl, red, G, [](int) {});
         }
-        __syncthreads();
-        if (p.Ish > 0) dec1_shared_gateup_rows<XF32>(p, xh, xl, red, G);
         return;
     }
     if (shared_role) {
@@ -1212,13 +1261,21 @@ hipError_t launch_dec_down_fused(const DecPass &p, hipStream_t s)
 // ------------------------------------------------------------------ staged layer
 namespace {
 
-size_t lds_stage1(int H, bool xf32) { return (size_t)(xf32 ? 4 : 2) * H + 2 * 16 * GU_WAVES * sizeof(float); }
+// x (one or two bf16 terms; a spare 8-value slot after it), the wave sums
+size_t lds_stage1(int H, bool xf32) { return (size_t)(xf32 ? 4 : 2) * (H + 8) + 2 * 16 * GU_WAVES * sizeof(float); }
 size_t lds_stage2() { return (size_t)32 * DEC_LUT_KB * 256 * sizeof(float); }
 
 // experts per lane of the selection: 4 (E <= 256) or 16 (E <= 1024)
 bool wide_select(const DecPass &p) { return p.route && p.E > 256; }
 
-DevSlots occ_s1[2], occ_s2[4];
+// stage 1 with each router item overlapping its wave's first shared rows:
+// bf16 x, at most one item per wave, an item's H chunk in one batch of 8 steps
+bool stage1_overlapped(const DecPass &p)
+{
+    return p.route && !p.x_f32 && p.E * p.rnc <= p.s1_wg * GU_WAVES && p.rhc <= 256 * 8;
+}
+
+DevSlots occ_s1[3], occ_s2[4];
 
 }  // namespace
 
@@ -1233,6 +1290,7 @@ void dec_plan_staged(DecPass &p)
     int g1 = std::max(1, (p.Ish + 7) / 8);
     if (p.route) g1 = std::max(g1, std::min(ncu, (p.E * p.rnc + GU_WAVES - 1) / GU_WAVES));
     p.s1_wg = std::min(g1, occ1 * ncu);
+    if (stage1_overlapped(p)) (void)resident(dec1_gateup_kernel<false, GU_STAGE1R, 4>, l1, occ_s1[2], GU_THREADS);
     // stage 2: routed gate/up units (one LDS table per work-group) on every
     // work-group, R per K chunk; the shared down rides in their prologue
     const size_t l2 = lds_stage2();
@@ -1252,6 +1310,7 @@ hipError_t launch_dec_stage1(const DecPass &p, hipStream_t s)
 {
     const size_t lds = lds_stage1(p.H, p.x_f32);
     if (p.x_f32) dec1_gateup_kernel<true, GU_STAGE1, 4><<<p.s1_wg, GU_THREADS, lds, s>>>(p);
+    else if (stage1_overlapped(p)) dec1_gateup_kernel<false, GU_STAGE1R, 4><<<p.s1_wg, GU_THREADS, lds, s>>>(p);
     else dec1_gateup_kernel<false, GU_STAGE1, 4><<<p.s1_wg, GU_THREADS, lds, s>>>(p);
     return hipGetLastError();
 }

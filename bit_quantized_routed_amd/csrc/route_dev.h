@@ -84,6 +84,62 @@ __device__ __forceinline__ void route_partial_item(const void *x, const float *w
             if (lane == a * TB + b && b < nt) part[((size_t)c * T + t0 + b) * E + eg * EW + a] = acc[a][b];
 }
 
+// A single-token item (T = 1, EW = TB = 1, bf16 x) whose H chunk fits one
+// batch of eight 256-wide steps (HC <= 2048), split into two halves of four
+// steps, each its router-weight loads and then its arithmetic, so that a
+// caller can keep other loads in flight in between (x comes from a copy of its
+// bits, e.g. in LDS).  The arithmetic is route_partial_item's for that case,
+// operation for operation (the fp64 sum runs over the steps in order, across
+// the halves), so both give the same bits.
+struct RouteItem1 {
+    f32x4 w4[4];
+    double acc;
+    int c, e, h0, h_end;
+};
+
+__device__ __forceinline__ void route_item1_begin(int H, int NC, int HC, int item, int lane, RouteItem1 &r)
+{
+    r.c = item % NC;
+    r.e = item / NC;
+    const int h_begin = r.c * HC;
+    r.h_end = min(H, h_begin + HC);
+    r.h0 = h_begin + 4 * lane;
+    r.acc = 0.0;
+}
+
+// loads of half hf (steps 4 hf .. 4 hf + 3); steps past the chunk re-read its
+// last step and are not used, so every load is unconditional
+__device__ __forceinline__ void route_item1_load(const float *wr, int H, int hf, RouteItem1 &r)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int h = min(r.h0 + 256 * (4 * hf + i), r.h_end - 4);
+        r.w4[i] = *(const f32x4 *)&wr[(size_t)r.e * H + h];
+    }
+}
+
+__device__ __forceinline__ void route_item1_step(const uint16_t *xbits, int hf, RouteItem1 &r)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int h = r.h0 + 256 * (4 * hf + i);
+        if (h >= r.h_end) break;
+        const uint2 u = *(const uint2 *)&xbits[h];
+        const double xv[4] = {bf16_bits_to_f32(u.x & 0xffffu), bf16_bits_to_f32(u.x >> 16),
+                              bf16_bits_to_f32(u.y & 0xffffu), bf16_bits_to_f32(u.y >> 16)};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r.acc = fma(xv[q], (double)r.w4[i][q], r.acc);
+    }
+}
+
+__device__ __forceinline__ void route_item1_end(const RouteItem1 &r, int E, int lane, double *part)
+{
+    double acc = r.acc;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0) part[(size_t)r.c * E + r.e] = acc;
+}
+
 // Wave-wide reductions by DPP: four steps (swap neighbours, swap pairs,
 // mirror the half-rows, mirror the rows) leave each 16-lane row's result in
 // every lane of the row; the four row results are read from lanes 0, 16, 32,
