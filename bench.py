@@ -47,7 +47,7 @@ _KERNEL_SOURCES = {"dec_": ["decode.hip", "decode.h", "route_dev.h"], "route_": 
 
 # the library's launch names (moe_profile.name) and the GPU kernel symbols each one runs
 LAUNCH_SYMBOLS = [
-    ("dec_stage1", r"dec1_gateup_kernel<(?:true|false), 1,"),
+    ("dec_stage1", r"dec1_gateup_kernel<(?:true|false), [13],"),
     ("dec_stage2", r"dec1_gateup_kernel<(?:true|false), 2,"),
     ("dec_hform", r"dec1_hform_kernel"),
     ("dec_down_fused", r"dec1_down_fused_kernel"),
