@@ -112,8 +112,11 @@ def machine_ceilings():
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     grid, iters = 4 * n_cu, 4000
     sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    # the 32x32x16 loop: the 16x16x32 probe loop carries compiler-inserted
+    # accumulator moves (about 7 VALU instructions per MFMA) and reads half the
+    # rate that shape reaches in the kernels
     tf = {}
-    for shape, name, fl in ((0, "16x16x32", 16384), (1, "32x32x16", 32768)):
+    for shape, name, fl in ((1, "32x32x16", 32768),):
         M.probe_mfma_loop(shape, grid, 10, sink)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -122,7 +125,7 @@ def machine_ceilings():
         e1.synchronize()
         tf[name] = round(grid * 4 * iters * 8 * fl / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
     return {"stream_read_GBps": round(best_gbs, 1), "stream_read_grid": best_grid,
-            "mfma_bf16_TFLOPs": max(tf.values()), "mfma_bf16_TFLOPs_by_shape": tf,
+            "mfma_bf16_TFLOPs": tf["32x32x16"], "mfma_probe_shape": "v_mfma_f32_32x32x16_bf16",
             "probe": "moe_probe_stream_read / moe_probe_mfma_loop"}
 
 
@@ -519,6 +522,63 @@ def summarize_counters(workload, copy_fetch, copy_write, fetch, write, cmds):
     print("\n".join(out))
 
 
+# counters of one `rocprofv3 --pmc` pass over the compute pipeline (8 SQ and 1 GRBM
+# counter: within one pass's limits)
+SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+               "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def summarize_sq(workload, d, cmd):
+    """Markdown summary of one `rocprofv3 --pmc` run of SQ_COUNTERS: per kernel and
+    dispatch, each counter summed over its instances; derived per kernel: the
+    MFMA busy share (SQ_VALU_MFMA_BUSY_CYCLES, one count per busy SIMD cycle,
+    over the GPU-active cycles of the dispatch -- GRBM_GUI_ACTIVE summed over the
+    8 XCDs, divided by 8 -- times the chip's SIMDs), the bf16 MFMA flops executed
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts them in units of 512) against the
+    kernel's algorithmic flops where defined, VALU instructions per MFMA
+    instruction, LDS bank-conflict cycles per LDS instruction and the share of
+    wave cycles spent waiting on LDS results."""
+    import statistics as st
+    import synthetic as S
+    acc = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        key = (r["Dispatch_Id"], r["Kernel_Name"])
+        acc.setdefault(key, {}).setdefault(r["Counter_Name"], 0.0)
+        acc[key][r["Counter_Name"]] += float(r["Counter_Value"])
+    by = {}
+    for (_, name), v in acc.items():
+        by.setdefault(name, []).append(v)
+    simds = 256 * 4
+    cfg = S.config(workload)
+    T = cfg["T"]
+    out = ["# Compute-pipeline counters: %s" % workload, "",
+           "One `rocprofv3 --pmc` run of %s (per dispatch, summed over" % ", ".join("`%s`" % c for c in SQ_COUNTERS),
+           "instances, averaged over the kernel's dispatches). Command (from the repository root R on the",
+           "MI355X; the summary is the second line's output):", "",
+           "```", _command_text(cmd), "python3 $R/bench.py --summarize-sq %s <the -d folder> '<the first line>'" % workload,
+           "```", "",
+           "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x %d SIMDs); MFMA flops = 512 x" % simds,
+           "SQ_INSTS_VALU_MFMA_MOPS_BF16 (executed, padding and the second bf16 term of fp32 operands",
+           "included); algorithmic flops as the bench defines them for the grouped-GEMM launches.", "",
+           "| kernel | launch | dispatches | MFMA busy | MFMA flops executed | / algorithmic | VALU per MFMA | "
+           "LDS conflict cycles per LDS instr | LDS wait share |",
+           "|---|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for name, runs in sorted(by.items(), key=lambda kv: -st.mean(x.get("SQ_WAVE_CYCLES", 0.0) for x in kv[1])):
+        m = {c: st.mean(x.get(c, 0.0) for x in runs) for c in SQ_COUNTERS}
+        launch = _launch_of(name)
+        cyc = m["GRBM_GUI_ACTIVE"] / 8
+        busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * simds) if cyc else 0.0
+        flops = 512 * m["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+        alg = kernel_flops(cfg, T, launch) if launch and launch.startswith("ffn_prefill_") else None
+        vpm = m["SQ_INSTS_VALU"] / m["SQ_INSTS_MFMA"] if m["SQ_INSTS_MFMA"] else float("nan")
+        cpl = m["SQ_LDS_BANK_CONFLICT"] / m["SQ_INSTS_LDS"] if m["SQ_INSTS_LDS"] else float("nan")
+        wait = m["SQ_WAIT_INST_LDS"] / m["SQ_WAVE_CYCLES"] if m["SQ_WAVE_CYCLES"] else float("nan")
+        out.append("| `%s` | %s | %d | %.1f%% | %.3g | %s | %.1f | %.2f | %.1f%% |" % (
+            name[:110], launch or "", len(runs), 100 * busy, flops, "%.2f" % (flops / alg) if alg else "",
+            vpm, cpl, 100 * wait))
+    print("\n".join(out))
+
+
 SWEEP_T = (1, 2, 4, 8, 16, 24, 32, 48, 64)
 
 
@@ -827,6 +887,9 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar="ARG",
                     help="only print the markdown traffic summary: WORKLOAD COPY_FETCH_DIR COPY_WRITE_DIR "
                          "FETCH_DIR WRITE_DIR COMMAND... (no GPU)")
+    ap.add_argument("--summarize-sq", nargs=3, metavar=("WORKLOAD", "DIR", "COMMAND"),
+                    help="only print the markdown summary of a rocprofv3 --pmc run of the compute-pipeline "
+                         "counters (no GPU)")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
@@ -834,6 +897,9 @@ def main():
     if args.summarize_counters:
         a = args.summarize_counters
         summarize_counters(a[0], a[1], a[2], a[3], a[4], a[5:])
+        return
+    if args.summarize_sq:
+        summarize_sq(*args.summarize_sq)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (the layer's multi-GPU sharding is a design, not "

@@ -17,7 +17,11 @@
  *   v_mfma_f32_16x16x32_bf16 (16384 flop each), shape 1:
  *   v_mfma_f32_32x32x16_bf16 (32768 flop each) -- and writes one float per
  *   thread to sink (device, grid * 256 floats).
- *   flop = grid * 4 * iters * 8 * (16384 or 32768).
+ *   flop = grid * 4 * iters * 8 * (16384 or 32768).  Shape 1 gives the
+ *   chip's MFMA ceiling.  Shape 0 reads about half of it: the compiler keeps
+ *   that loop's accumulators in shifting registers and adds about 7 register
+ *   moves per MFMA (SQ_INSTS_VALU / SQ_INSTS_MFMA), so it measures the loop,
+ *   not the instruction, which runs at the full rate in the kernels.
  *
  * Both are asynchronous on `stream` (time them with events around the call)
  * and return MOE_OK, MOE_ERR_INVALID_ARG for bad sizes or pointers (nothing
