@@ -23,6 +23,7 @@ FMT_CB2, FMT_Q2K, FMT_Q4K, FMT_BF16, FMT_Q5K, FMT_Q6K, FMT_CB2S = 1, 2, 3, 4, 5,
 ACT_F32, ACT_BF16 = 0, 1
 PATH_ROUTE, PATH_DECODE, PATH_PREFILL, PATH_LAYER_DECODE = 0, 1, 2, 3
 LAYER_TOKENWISE_DECODE = 1
+LAYER_ONE_STREAM = 2
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
           -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
 BLOCK_BYTES = {FMT_CB2: 38, FMT_Q2K: 84, FMT_Q4K: 144, FMT_Q5K: 176, FMT_Q6K: 210, FMT_CB2S: 66}

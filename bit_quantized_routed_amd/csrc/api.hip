@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "cache.h"
@@ -110,7 +111,8 @@ int check_layer(const moe_layer *L)
         if ((uintptr_t)ptr % 16) return set_error(MOE_ERR_INVALID_ARG, "layer pointer %p is not 16-byte aligned", ptr);
     if (L->sh_inter < 0) return set_error(MOE_ERR_INVALID_ARG, "sh_inter=%d < 0", L->sh_inter);
     if ((uintptr_t)L->expert_slot % 4) return set_error(MOE_ERR_INVALID_ARG, "expert_slot is not 4-byte aligned");
-    if (L->flags & ~MOE_LAYER_TOKENWISE_DECODE) return set_error(MOE_ERR_INVALID_ARG, "flags=%#x: unknown bits", L->flags);
+    if (L->flags & ~(MOE_LAYER_TOKENWISE_DECODE | MOE_LAYER_ONE_STREAM))
+        return set_error(MOE_ERR_INVALID_ARG, "flags=%#x: unknown bits", L->flags);
     if (L->sh_inter > 0) {
         if (!L->sh_gate || !L->sh_up || !L->sh_down) return set_error(MOE_ERR_INVALID_ARG, "shared expert weights are NULL");
         if (L->sh_inter % 256 || L->hidden % 256)
@@ -293,9 +295,51 @@ DecPass single_pass(const moe_layer *L, const FfnWs &w, int act)
     return d;
 }
 
+// Batched decode with the LDS-staged routed kernels: the shared expert's
+// chain (gate/up, finalize, down) does not depend on the routed one, so it runs
+// on a second stream of the device, forked from and joined back into the
+// caller's stream by two events (the combine waits for both chains; a caller
+// capturing its stream into a graph captures the fork and the join with it).
+// The stream (default priority, non-blocking) and events are created on the
+// first such call on a device and kept until the process ends; enqueues that
+// use them hold a mutex, so each call's join event is its own when host
+// threads call concurrently.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    bool failed = false;
+};
+SideStream g_side[MAX_DEVICES];
+std::mutex g_side_mu;
+
+// this device's side stream (the mutex held), or null: no slot for the device,
+// or creating it failed (the call then runs on the caller's stream alone)
+SideStream *side_stream()
+{
+    const int slot = device_slot();
+    if (slot < 0) return nullptr;
+    SideStream &S = g_side[slot];
+    if (S.failed) return nullptr;
+    if (!S.s) {
+        hipStream_t st = nullptr;
+        hipEvent_t f = nullptr, j = nullptr;
+        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess ||
+            hipEventCreateWithFlags(&f, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&j, hipEventDisableTiming) != hipSuccess) {
+            (void)hipGetLastError();                              // leave no sticky error behind
+            S.failed = true;
+            return nullptr;
+        }
+        S.s = st;
+        S.fork = f;
+        S.join = j;
+    }
+    return &S;
+}
+
 int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t *topk_idx, const float *topk_w,
                const int32_t *offsets, const int32_t *perm, const int32_t *inv, float *y, void *ws,
-               size_t ws_bytes, void *stream, moe_profile *prof, bool prefill)
+               size_t ws_bytes, void *stream, moe_profile *prof, bool prefill, bool side_ok = false)
 {
     int rc = check_layer(L);
     if (rc) return rc;
@@ -426,6 +470,46 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
 
     const char *nm_up = prefill ? "ffn_prefill_gateup" : "ffn_decode_gateup";
     const char *nm_dn = prefill ? "ffn_prefill_down" : "ffn_decode_down";
+    // the shared chain's stream: a second one, forked here, when the routed
+    // tiles run on their own kernels (see SideStream)
+    std::unique_lock<std::mutex> side_lock;
+    SideStream *side = nullptr;
+    if (bd && split && side_ok && !(L->flags & MOE_LAYER_ONE_STREAM)) {
+        side_lock = std::unique_lock<std::mutex>(g_side_mu);
+        side = side_stream();
+        if (side) {
+            if (hipEventRecord(side->fork, s) != hipSuccess) return hip_fail(hipGetLastError(), "fork record");
+            if (hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess) return hip_fail(hipGetLastError(), "fork wait");
+        }
+    }
+    const hipStream_t ss = side ? side->s : s;
+    auto shared_up = [&]() -> int {
+        pr.s = ss;
+        if (!pr.before(nm_up)) return hip_fail(hipGetLastError(), "event record");
+        e = np ? launch_np_prefill(up, true, ss) : npd ? launch_np_decode(up, true, ss)
+               : prefill ? launch_ffn_prefill(up, true, ss) : launch_ffn_decode(up, true, ss);
+        if (e != hipSuccess) return hip_fail(e, nm_up);
+        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+        if (split) {
+            if (!pr.before("sh_finalize")) return hip_fail(hipGetLastError(), "event record");
+            launch_sh_finalize(w.sh_part, w.ks_gu, T, Ish, T * k, nullptr, (float *)w.h, w.hstride, ss);
+            e = hipGetLastError();
+            if (e != hipSuccess) return hip_fail(e, "sh_finalize launch");
+            if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+        }
+        pr.s = s;
+        return MOE_OK;
+    };
+    auto shared_down = [&]() -> int {
+        pr.s = ss;
+        if (!pr.before(nm_dn)) return hip_fail(hipGetLastError(), "event record");
+        e = np ? launch_np_prefill(dn, false, ss) : npd ? launch_np_decode(dn, false, ss)
+               : prefill ? launch_ffn_prefill(dn, false, ss) : launch_ffn_decode(dn, false, ss);
+        if (e != hipSuccess) return hip_fail(e, nm_dn);
+        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+        pr.s = s;
+        return MOE_OK;
+    };
     if (bd) {
         if (!pr.before("bd_gateup")) return hip_fail(hipGetLastError(), "event record");
         e = launch_bd(up, true, s);
@@ -434,20 +518,14 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
         up.skip_routed = dn.skip_routed = 1;
     }
     if (!bd || has_sh) {
-        if (!pr.before(nm_up)) return hip_fail(hipGetLastError(), "event record");
-        e = np ? launch_np_prefill(up, true, s) : npd ? launch_np_decode(up, true, s)
-               : prefill ? launch_ffn_prefill(up, true, s) : launch_ffn_decode(up, true, s);
-        if (e != hipSuccess) return hip_fail(e, nm_up);
-        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+        rc = shared_up();
+        if (rc) return rc;
     }
-    if (split) {
-        if (!pr.before("sh_finalize")) return hip_fail(hipGetLastError(), "event record");
-        launch_sh_finalize(w.sh_part, w.ks_gu, T, Ish, T * k, nullptr, (float *)w.h, w.hstride, s);
-        e = hipGetLastError();
-        if (e != hipSuccess) return hip_fail(e, "sh_finalize launch");
-        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+    if (side && has_sh) {
+        // the shared down follows its gate/up on the side stream
+        rc = shared_down();
+        if (rc) return rc;
     }
-
     if (bd) {
         if (!pr.before("bd_down")) return hip_fail(hipGetLastError(), "event record");
         FfnPass dr = dn;
@@ -456,12 +534,13 @@ int ffn_common(const moe_layer *L, const void *x, int act, int T, const int32_t 
         if (e != hipSuccess) return hip_fail(e, "bd_down");
         if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
     }
-    if (!bd || has_sh) {
-        if (!pr.before(nm_dn)) return hip_fail(hipGetLastError(), "event record");
-        e = np ? launch_np_prefill(dn, false, s) : npd ? launch_np_decode(dn, false, s)
-               : prefill ? launch_ffn_prefill(dn, false, s) : launch_ffn_decode(dn, false, s);
-        if (e != hipSuccess) return hip_fail(e, nm_dn);
-        if (!pr.after()) return hip_fail(hipGetLastError(), "event record");
+    if ((!bd || has_sh) && !side) {
+        rc = shared_down();
+        if (rc) return rc;
+    }
+    if (side) {
+        if (hipEventRecord(side->join, side->s) != hipSuccess) return hip_fail(hipGetLastError(), "join record");
+        if (hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return hip_fail(hipGetLastError(), "join wait");
     }
 
     if (!pr.before("combine")) return hip_fail(hipGetLastError(), "event record");
@@ -602,7 +681,7 @@ int moe_expert_ffn_decode(const moe_layer *L, const void *x, int act, int T, con
                           const float *topk_w, const int32_t *offsets, const int32_t *perm, const int32_t *inv,
                           float *y, void *ws, size_t ws_bytes, void *stream, moe_profile *prof)
 {
-    return ffn_common(L, x, act, T, topk_idx, topk_w, offsets, perm, inv, y, ws, ws_bytes, stream, prof, false);
+    return ffn_common(L, x, act, T, topk_idx, topk_w, offsets, perm, inv, y, ws, ws_bytes, stream, prof, false, true);
 }
 
 int moe_expert_ffn_decode_noalloc(const moe_layer *L, const void *x, int act, int T, const int32_t *topk_idx,
@@ -659,7 +738,7 @@ int moe_layer_decode(const moe_layer *L, const void *x, int act, int T, const fl
             fpp = &fp;
         }
         rc = ffn_common(L, x, act, T, topk_idx, topk_w, offsets, perm, inv, y, fws, ws_bytes - rbytes, stream, fpp,
-                        false);
+                        false, true);
         if (prof) {
             prof->n_launches = nr + fp.n_launches;
             if (fp.kernel >= 0 && fp.kernel < fp.n_launches) prof->name = fp.name;

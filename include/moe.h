@@ -18,8 +18,10 @@
  *
  * Conventions for every entry point:
  *  - Device pointers are HIP device memory owned by the caller.  The library
- *    allocates nothing: scratch comes from the caller's workspace `ws`,
- *    sized with moe_workspace_bytes().  Host pointers are marked "host".
+ *    allocates no device memory: scratch comes from the caller's workspace
+ *    `ws`, sized with moe_workspace_bytes().  Host pointers are marked "host".
+ *    The one object it creates is a second stream with two events per device
+ *    for batched decode (see moe_expert_ffn_decode).
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream) and never synchronise or read device data back to the host.
  *  - Arguments are validated on the host before any HIP call; a bad argument
@@ -39,9 +41,13 @@
  *    address of the no-allocation scratch array -- each computed on first use
  *    on a device, stored atomically and never changed afterwards except
  *    upwards (the LDS limit), so a racing caller at most repeats the query,
- *    and (c) the contents of that scratch array (see
- *    moe_expert_ffn_decode_noalloc).  No entry point allocates, and none holds
- *    a lock.
+ *    (c) the contents of that scratch array (see
+ *    moe_expert_ffn_decode_noalloc), and (d) per device, the second stream
+ *    and two events of batched decode, created on the first call that uses
+ *    them and kept until the process ends; a call enqueues its fork and join
+ *    on them under a mutex (held only while it enqueues), so concurrent
+ *    callers each join their own work.  No entry point allocates device
+ *    memory; no other lock is held.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -138,7 +144,13 @@ enum moe_path { MOE_PATH_ROUTE = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2, M
  *     grouped GEMMs, which agree with the single-token result to about 1e-6
  *     relative, not bit for bit.  It needs a layer the single-token kernels
  *     take (CB2 gate/up, Q2K down; see moe_expert_ffn_decode), otherwise
- *     decode returns MOE_ERR_UNSUPPORTED.  Other bits: MOE_ERR_INVALID_ARG.
+ *     decode returns MOE_ERR_UNSUPPORTED.
+ *     MOE_LAYER_ONE_STREAM (may be combined with the other): every launch of
+ *     a call stays on the caller's stream; batched decode otherwise runs the
+ *     shared expert's chain on a second stream beside the routed kernels (see
+ *     moe_expert_ffn_decode).  For callers that arrange streams themselves
+ *     or time each launch on one stream.  Results are the same bit for bit.
+ *     Other bits: MOE_ERR_INVALID_ARG.
  *   expert_slot: NULL, or a device int32 [n_experts] map from expert to slot:
  *     the FFN calls then read expert e's routed weights at w_* + expert_slot[e]
  *     * (bytes of one expert's matrix) -- the layer view of an expert cache
@@ -151,6 +163,7 @@ enum moe_path { MOE_PATH_ROUTE = 0, MOE_PATH_DECODE = 1, MOE_PATH_PREFILL = 2, M
  *   Every pointer must be 16-byte aligned (device allocations are); the
  *   kernels read weights and the codebook in 8- and 16-byte pieces. */
 #define MOE_LAYER_TOKENWISE_DECODE 1
+#define MOE_LAYER_ONE_STREAM 2
 typedef struct moe_layer {
     int32_t hidden, inter, n_experts, top_k;
     int32_t fmt_gate_up, fmt_down;
@@ -165,7 +178,10 @@ typedef struct moe_layer {
 /* Optional per-kernel timing.  When `prof` is non-NULL and prof->kernel is
  * the 0-based index of one of the kernel launches a call makes, the library
  * records hipEvent_t prof->ev_start immediately before that launch and
- * prof->ev_stop immediately after it, on the call's stream; it always stores
+ * prof->ev_stop immediately after it, on the stream the launch runs on (the
+ * call's stream; the second stream for the shared expert's launches of
+ * batched decode, whose interval then spans the routed kernels beside them
+ * as well); it always stores
  * the number of launches the call made in prof->n_launches and the kernel's
  * name in prof->name.  Events are created and destroyed by the caller. */
 typedef struct moe_profile {
@@ -220,7 +236,15 @@ int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bi
  *   beside the shared down; routed h; the routed down, which adds the shared
  *   output and writes y -- else gate/up, down (SwiGLU as it forms h) and
  *   combine; so such a token's y does not depend on the other tokens of the
- *   call.  Otherwise schedule, gate/up+SwiGLU, down, combine.
+ *   call.  Otherwise schedule, gate/up+SwiGLU, down, combine; for CB2/CB2S
+ *   gate/up with Q2K down, T <= 64, a shared expert and hidden, inter and
+ *   sh_inter multiples of 512, the routed tiles' gate/up and down run on
+ *   `stream` while the shared expert's gate/up, its K-part finalize and its
+ *   down run on the library's second stream of the device, forked from
+ *   `stream` after the schedule and joined back before the combine (events;
+ *   a graph capture of `stream` captures both branches).  The results are
+ *   those of one stream, bit for bit; moe_expert_ffn_decode_noalloc, and a
+ *   layer with MOE_LAYER_ONE_STREAM, keep every launch on `stream`.
  * moe_expert_ffn_prefill -- bf16 MFMA path for any T: x must be bf16;
  *   dequantized weights rounded to bf16 (RNE) in LDS; fp32 accumulation;
  *   h rounded to bf16; down output and combine in fp32.  Relative L2 error

@@ -92,9 +92,12 @@ def test_ffn_validation(kw, code):
 def test_tokenwise_flag_validation():
     dec, pre = M.lib().moe_expert_ffn_decode, M.lib().moe_expert_ffn_prefill
     for fn in (dec, pre):
-        assert _ffn(fn, _layer(flags=2)) == -1                 # unknown bits
+        assert _ffn(fn, _layer(flags=4)) == -1                 # unknown bits
         assert b"flags" in M.lib().moe_last_error()
-    assert _route(_layer(flags=2, w_router=FAKE), ws_bytes=10) == -3   # the router does not read the flags
+        # the one-stream flag (alone or with the token-wise one) passes validation
+        assert _ffn(fn, _layer(flags=M.LAYER_ONE_STREAM), ws_bytes=10) == -3
+    assert _ffn(pre, _layer(flags=M.LAYER_ONE_STREAM | M.LAYER_TOKENWISE_DECODE), ws_bytes=10) == -3
+    assert _route(_layer(flags=4, w_router=FAKE), ws_bytes=10) == -3   # the router does not read the flags
     # token by token needs the single-token kernels; H = 256 is not a multiple of 512
     assert _ffn(dec, _layer(flags=M.LAYER_TOKENWISE_DECODE)) == -2
     assert b"token-by-token" in M.lib().moe_last_error()

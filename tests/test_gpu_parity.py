@@ -427,6 +427,39 @@ def test_full_decode_tokenwise_flag(big):
     assert rel_l2(y[toks], yref) <= DEC_TOL
 
 
+def test_full_decode32_one_stream_flag(big):
+    """Batched decode of the full layer runs the shared expert's chain on a
+    second stream beside the routed kernels; with the one-stream flag every
+    launch stays on the caller's stream, and y is the same bit for bit.  Three
+    calls enqueued back to back on one stream without a host wait between
+    them (each forks and joins on its own) give each call's result too."""
+    cfg = S.config("decode32")
+    x, act, r = run_route(big, cfg)
+    T, k, E, H = x.shape[0], cfg["top_k"], cfg["n_experts"], cfg["hidden"]
+    y2 = run_ffn(big, x, act, r, decode=True)
+    big.layer.c.flags = M.LAYER_ONE_STREAM
+    try:
+        y1 = run_ffn(big, x, act, r, decode=True)
+    finally:
+        big.layer.c.flags = 0
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    parts = [(0, 32), (3, 20), (11, 27)]
+    alone, queued = [], []
+    for a, b in parts:
+        xt = x[a:b].contiguous()
+        rb = M.Routing(b - a, k, E)
+        M.route(big.layer, xt, act, b - a, big.bias(cfg), rb, big.layer.workspace(b - a, M.PATH_ROUTE))
+        alone.append(run_ffn(big, xt, act, rb, decode=True))
+        queued.append((xt, rb, torch.full((b - a, H), float("nan"), device="cuda"),
+                       big.layer.workspace(b - a, M.PATH_DECODE)))
+    torch.cuda.synchronize()
+    for xt, rb, yq, ws in queued:
+        M.ffn_decode(big.layer, xt, act, xt.shape[0], rb, yq, ws)
+    torch.cuda.synchronize()
+    for (xt, rb, yq, ws), ya in zip(queued, alone):
+        assert np.array_equal(yq.cpu().numpy().view(np.uint32), ya.view(np.uint32))
+
+
 def test_full_decode32_q4k(big_q4k):
     assert sampled_check(big_q4k, S.config("decode32_q4k"), True, 8) <= DEC_TOL
 
