@@ -460,6 +460,36 @@ def test_full_decode32_one_stream_flag(big):
         assert np.array_equal(yq.cpu().numpy().view(np.uint32), ya.view(np.uint32))
 
 
+def test_full_decode32_graph_replay(big):
+    """The batched decode call -- routed kernels on the caller's stream, the
+    shared expert's chain forked onto the library's second stream and joined
+    back -- captured into a HIP graph (after an eager call, which creates the
+    second stream): every replay, with eager calls and synchronisations
+    between the replays, gives the eager y bit for bit."""
+    cfg = S.config("decode32")
+    x, act, r = run_route(big, cfg)
+    T, H = x.shape[0], cfg["hidden"]
+    y_eager = run_ffn(big, x, act, r, decode=True)
+    ws = big.layer.workspace(T, M.PATH_DECODE)
+    y = torch.full((T, H), float("nan"), device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        M.ffn_decode(big.layer, x, act, T, r, y, ws, s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        M.ffn_decode(big.layer, x, act, T, r, y, ws, s)
+    torch.cuda.synchronize()
+    for i in range(3):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy().view(np.uint32), y_eager.view(np.uint32)), i
+        assert np.array_equal(run_ffn(big, x, act, r, decode=True).view(np.uint32), y_eager.view(np.uint32)), i
+
+
 def test_full_decode32_q4k(big_q4k):
     assert sampled_check(big_q4k, S.config("decode32_q4k"), True, 8) <= DEC_TOL
 
