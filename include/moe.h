@@ -242,7 +242,9 @@ int moe_route(const moe_layer *L, const void *x, int act, int T, const float *bi
  *   `stream` while the shared expert's gate/up, its K-part finalize and its
  *   down run on the library's second stream of the device, forked from
  *   `stream` after the schedule and joined back before the combine (events;
- *   a graph capture of `stream` captures both branches).  The results are
+ *   a graph capture of `stream` captures both branches; the first such call
+ *   on a device creates the stream, so make one call before capturing).  If
+ *   the stream cannot be created, every launch stays on `stream`.  The results are
  *   those of one stream, bit for bit; moe_expert_ffn_decode_noalloc, and a
  *   layer with MOE_LAYER_ONE_STREAM, keep every launch on `stream`.
  * moe_expert_ffn_prefill -- bf16 MFMA path for any T: x must be bf16;
