@@ -490,6 +490,45 @@ def test_full_decode32_graph_replay(big):
         assert np.array_equal(run_ffn(big, x, act, r, decode=True).view(np.uint32), y_eager.view(np.uint32)), i
 
 
+def test_full_decode32_two_threads(big):
+    """Two host threads each enqueue four batched decode calls on a stream and a
+    workspace of their own; every call forks the shared expert's chain onto
+    the device's one second stream and joins it back (the library serialises
+    those enqueues).  Every output equals the single-threaded one bit for
+    bit."""
+    import threading
+    cfg = S.config("decode32")
+    x, act, r = run_route(big, cfg)
+    T, H = x.shape[0], cfg["hidden"]
+    y_ref = run_ffn(big, x, act, r, decode=True)
+    jobs = []
+    for _ in range(2):
+        st = torch.cuda.Stream()
+        ws = big.layer.workspace(T, M.PATH_DECODE)
+        ys = [torch.full((T, H), float("nan"), device="cuda") for _ in range(4)]
+        jobs.append((st, ws, ys))
+    torch.cuda.synchronize()
+    errs = []
+
+    def worker(st, ws, ys):
+        try:
+            for y in ys:
+                M.ffn_decode(big.layer, x, act, T, r, y, ws, st)
+        except Exception as e:          # reported below, on the main thread
+            errs.append(e)
+
+    th = [threading.Thread(target=worker, args=j) for j in jobs]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errs, errs
+    for st, ws, ys in jobs:
+        for y in ys:
+            assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
+
+
 def test_full_decode32_q4k(big_q4k):
     assert sampled_check(big_q4k, S.config("decode32_q4k"), True, 8) <= DEC_TOL
 
